@@ -1,0 +1,346 @@
+/*
+ * pa_oracle.c -- plain, slow, single-threaded CPU oracle for gate-level
+ * time-based power analysis.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the reference that the HIP path is
+ * checked against.  Only tests/, __graft_entry__.smoke() and the cpu_baseline
+ * leg of bench.py may load or call it.  The product library never links,
+ * loads or calls it, and it shares no source, header, table or helper with
+ * the product library.
+ *
+ * Source of the method: "GPU-Accelerated Gate-Level Time-Based Power
+ * Analysis via Event-Density-Aware Partitioning and Kernel Fusion"
+ * (arXiv 2609.05960), called "the paper" below.  Every step cites the
+ * paper's section, equation or figure it follows.  The paper's display
+ * equations (Eqs. 1-4) are not printed in the available text; where a form
+ * had to be fixed, the reading is stated at the step and listed in the
+ * design notes of the repository.
+ *
+ * What is computed (the plain definition; no blocking, no fusion, no
+ * reordering of the sums beyond what the definition states):
+ *   for every gate, walk the merged per-pin event streams in time order
+ *   (paper, Sec. 2.4.2 and Fig. 3), and at each distinct timestamp
+ *     1. charge the leakage of the interval that ends there at the state the
+ *        gate held during it (Eq. 4), split over the clock-cycle bins it
+ *        overlaps in proportion to the overlap (Sec. 2.4.2);
+ *     2. for every pin with an event there (Fig. 7, the loop over pins with an
+ *        event at t_cur): internal energy from the LUT that the state before
+ *        the event selects, interpolated bilinearly on input slew and output
+ *        load (Sec. 2.4.1, Fig. 2); switching energy 1/2 c v^2 for a 0->1
+ *        event on the output pin (Eq. 1); clock-cycle glitch detection with a
+ *        per-pin event counter (Sec. 2.4.1, Fig. 7 GlitchDetectUpdate) and
+ *        scaling of a glitch's dynamic energy by r_gl (Eq. 2); the event's
+ *        energy goes into the bin of its clock cycle (Sec. 2.4.1);
+ *     3. apply every event at that timestamp to the gate state (Sec. 2.4.2).
+ *   The interval after the last event runs to t_max.  Powers are energies
+ *   over the analysis window (Eq. 3).
+ *
+ * Readings fixed here because the available text does not print them:
+ *   - Eq. 1: E_sw = 0.5 * c * Vdd^2 for each 0->1 event on the output pin;
+ *     a 1->0 output event carries no switching energy.
+ *   - Eq. 2: r_gl = min(1, pw / ((rSlew + fSlew) / 2)) where pw is the time
+ *     since the previous event on the same pin and rSlew, fSlew are the
+ *     slews of that previous event and of the current one (the rise and the
+ *     fall that bound the pulse).  Parity of this form against the paper is
+ *     unpinned: the paper does not print it.
+ *   - Glitch rule: per pin, the m-th event (m >= 2) of that pin inside one
+ *     clock cycle is a glitch; the first event of a pin in a cycle is
+ *     regular (Fig. 7, GlitchDetectUpdate).  A glitch adds r_gl * E to the
+ *     glitch component and to the waveform, and nothing to the internal or
+ *     switching component.
+ *   - Eq. 3: P = E / (t_max * tick_s).  Eq. 4: E_leak = p_leak * dt * tick_s.
+ *   - Gate state S = sum_i v_i 2^i over the input pins (pin 0 is the least
+ *     significant bit); the output pin does not enter the state.
+ *   - Bins are the half-open cycles [c T, (c+1) T); N_cyc = ceil(t_max / T);
+ *     the last bin may be partial.
+ *   - Bilinear interpolation: segment i = clamp(#{axis_j <= x} - 1, 0, n-2),
+ *     fraction (x - x_i) / (x_{i+1} - x_i), extrapolating linearly outside.
+ *   - Units: timestamps, T, t_max and slews in ticks; tick_s seconds per
+ *     tick; cap in F, LUT in J, leakage in W, Vdd in V.  Slews arrive as
+ *     fp32 and are widened to fp64 before any arithmetic.
+ *
+ * Every total and every bin is a Neumaier-compensated fp64 sum.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "pa_oracle.h"
+
+/* ---------------------------------------------------------------- sums -- */
+
+typedef struct {
+  double s, c;
+} nsum;
+
+static void nadd(nsum *a, double x) {
+  double t = a->s + x;
+  if (fabs(a->s) >= fabs(x))
+    a->c += (a->s - t) + x;
+  else
+    a->c += (x - t) + a->s;
+  a->s = t;
+}
+
+static double nval(const nsum *a) { return a->s + a->c; }
+
+/* ------------------------------------------------- bilinear LUT lookup -- */
+
+/* Segment and fraction of x on a strictly increasing axis of n >= 2 points.
+ * NLDM table lookup (paper, Sec. 2.4.1, Fig. 2) read as bilinear
+ * interpolation that extrapolates linearly outside the axis range. */
+static void axis_locate(const double *axis, int n, double x, int *seg, double *frac) {
+  int m = 0;
+  for (int j = 0; j < n; ++j)
+    if (axis[j] <= x) m++;
+  int i = m - 1;
+  if (i < 0) i = 0;
+  if (i > n - 2) i = n - 2;
+  *seg = i;
+  *frac = (x - axis[i]) / (axis[i + 1] - axis[i]);
+}
+
+double pa_oracle_bilerp(int n_slew, int n_cap, const double *slew_axis, const double *cap_axis,
+                        const double *table, double x_slew, double x_cap) {
+  int i, j;
+  double a, b;
+  axis_locate(slew_axis, n_slew, x_slew, &i, &a);
+  axis_locate(cap_axis, n_cap, x_cap, &j, &b);
+  double l00 = table[i * n_cap + j];
+  double l01 = table[i * n_cap + j + 1];
+  double l10 = table[(i + 1) * n_cap + j];
+  double l11 = table[(i + 1) * n_cap + j + 1];
+  return (1.0 - a) * (1.0 - b) * l00 + a * (1.0 - b) * l10 + (1.0 - a) * b * l01 + a * b * l11;
+}
+
+/* ------------------------------------------------------------ validation -- */
+
+int64_t pa_oracle_n_cycles(int64_t t_clk, int64_t t_max) {
+  if (t_clk <= 0 || t_max <= 0) return -1;
+  return (t_max + t_clk - 1) / t_clk;
+}
+
+static int valid_design(int64_t n_gates, const int32_t *gate_cell, const double *gate_cap, int32_t n_cells,
+                        const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap, const double *slew_axis,
+                        const double *cap_axis) {
+  if (n_gates < 0 || n_cells < 1 || n_slew < 2 || n_cap < 2) return PA_ORACLE_EARG;
+  for (int32_t c = 0; c < n_cells; ++c) {
+    if (cell_n_in[c] < 1 || cell_n_in[c] > 8) return PA_ORACLE_EDATA;
+    for (int j = 0; j + 1 < n_slew; ++j)
+      if (!(slew_axis[(int64_t)c * n_slew + j] < slew_axis[(int64_t)c * n_slew + j + 1])) return PA_ORACLE_EDATA;
+    for (int j = 0; j + 1 < n_cap; ++j)
+      if (!(cap_axis[(int64_t)c * n_cap + j] < cap_axis[(int64_t)c * n_cap + j + 1])) return PA_ORACLE_EDATA;
+  }
+  for (int64_t g = 0; g < n_gates; ++g) {
+    if (gate_cell[g] < 0 || gate_cell[g] >= n_cells) return PA_ORACLE_EDATA;
+    if (!isfinite(gate_cap[g])) return PA_ORACLE_EDATA;
+  }
+  return 0;
+}
+
+static int valid_events(int64_t n_pins, const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t,
+                        const uint8_t *evt_val, const float *evt_slew, int64_t t_clk, int64_t t_max,
+                        double tick_s) {
+  if (n_pins < 0 || t_clk <= 0 || t_max <= 0 || !(tick_s > 0.0)) return PA_ORACLE_EARG;
+  if (pin_ptr[0] != 0) return PA_ORACLE_EDATA;
+  for (int64_t p = 0; p < n_pins; ++p) {
+    if (pin_ptr[p + 1] < pin_ptr[p]) return PA_ORACLE_EDATA;
+    if (pin_init[p] > 1) return PA_ORACLE_EDATA;
+    uint8_t v = pin_init[p];
+    for (int64_t e = pin_ptr[p]; e < pin_ptr[p + 1]; ++e) {
+      if (evt_t[e] < 0 || evt_t[e] >= t_max) return PA_ORACLE_EDATA;
+      if (e > pin_ptr[p] && !(evt_t[e] > evt_t[e - 1])) return PA_ORACLE_EDATA;
+      if (evt_val[e] != (uint8_t)(1 - v)) return PA_ORACLE_EDATA;
+      v = evt_val[e];
+      if (!(evt_slew[e] > 0.0f) || !isfinite(evt_slew[e])) return PA_ORACLE_EDATA;
+    }
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------- the run -- */
+
+typedef struct {
+  int32_t n_slew, n_cap;
+  const double *slew_axis, *cap_axis, *lut, *leak;
+  int64_t *lut_base, *leak_base;  /* per cell */
+  double vdd, tick_s;
+  int64_t T, t_max, n_cyc;
+  nsum *wave;
+  nsum e_int, e_sw, e_gl, e_leak;
+  uint64_t *cyc_events, *cyc_glitches;
+  uint64_t n_events, n_glitches;
+} run_ctx;
+
+/* Leakage of the interval [a, b) at constant power p (paper, Sec. 2.4.2,
+ * Eq. 4): energy p * (b - a) * tick_s, added to every overlapped cycle bin in
+ * proportion to the overlap. */
+static void leak_interval(run_ctx *R, double p, int64_t a, int64_t b) {
+  if (b <= a) return;
+  nadd(&R->e_leak, p * (double)(b - a) * R->tick_s);
+  int64_t c_lo = a / R->T;
+  int64_t c_hi = (b + R->T - 1) / R->T; /* exclusive */
+  for (int64_t c = c_lo; c < c_hi; ++c) {
+    int64_t lo = a > c * R->T ? a : c * R->T;
+    int64_t hi = b < (c + 1) * R->T ? b : (c + 1) * R->T;
+    if (hi > lo) nadd(&R->wave[c], p * (double)(hi - lo) * R->tick_s);
+  }
+}
+
+int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_cap_F, int32_t n_cells,
+                  const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap, const double *slew_axis,
+                  const double *cap_axis, const double *lut_J, const double *leak_W, double vdd_V,
+                  int64_t n_pins, const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t,
+                  const uint8_t *evt_val, const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s,
+                  int64_t gate_lo, int64_t gate_hi, pa_oracle_totals *out, double *wave_J,
+                  uint64_t *cyc_events, uint64_t *cyc_glitches, uint8_t *evt_glitch,
+                  uint8_t *evt_state_before) {
+  if (!out || !wave_J || !cyc_events || !cyc_glitches) return PA_ORACLE_EARG;
+  int rc = valid_design(n_gates, gate_cell, gate_cap_F, n_cells, cell_n_in, n_slew, n_cap, slew_axis, cap_axis);
+  if (rc) return rc;
+  rc = valid_events(n_pins, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk, t_max, tick_s);
+  if (rc) return rc;
+  if (gate_lo < 0 || gate_hi > n_gates || gate_lo > gate_hi) return PA_ORACLE_EARG;
+
+  /* gate-major pins: gate g owns k_g input pins followed by one output pin */
+  int64_t *pin_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_gates + 1));
+  int64_t *lut_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_cells);
+  int64_t *leak_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_cells);
+  run_ctx R;
+  memset(&R, 0, sizeof R);
+  R.n_cyc = pa_oracle_n_cycles(t_clk, t_max);
+  R.wave = (nsum *)calloc((size_t)R.n_cyc, sizeof(nsum));
+  if (!pin_base || !lut_base || !leak_base || !R.wave) {
+    free(pin_base); free(lut_base); free(leak_base); free(R.wave);
+    return PA_ORACLE_ENOMEM;
+  }
+  pin_base[0] = 0;
+  for (int64_t g = 0; g < n_gates; ++g) pin_base[g + 1] = pin_base[g] + cell_n_in[gate_cell[g]] + 1;
+  if (pin_base[n_gates] != n_pins) {
+    free(pin_base); free(lut_base); free(leak_base); free(R.wave);
+    return PA_ORACLE_EDATA;
+  }
+  int64_t lb = 0, kb = 0;
+  for (int32_t c = 0; c < n_cells; ++c) {
+    int64_t k = cell_n_in[c];
+    lut_base[c] = lb;
+    leak_base[c] = kb;
+    lb += ((int64_t)1 << k) * k * n_slew * n_cap;
+    kb += (int64_t)1 << k;
+  }
+  R.n_slew = n_slew; R.n_cap = n_cap;
+  R.slew_axis = slew_axis; R.cap_axis = cap_axis; R.lut = lut_J; R.leak = leak_W;
+  R.lut_base = lut_base; R.leak_base = leak_base;
+  R.vdd = vdd_V; R.tick_s = tick_s; R.T = t_clk; R.t_max = t_max;
+  memset(cyc_events, 0, sizeof(uint64_t) * (size_t)R.n_cyc);
+  memset(cyc_glitches, 0, sizeof(uint64_t) * (size_t)R.n_cyc);
+  R.cyc_events = cyc_events;
+  R.cyc_glitches = cyc_glitches;
+
+  for (int64_t g = gate_lo; g < gate_hi; ++g) {
+    const int32_t cell = gate_cell[g];
+    const int k = cell_n_in[cell];
+    const double cap = gate_cap_F[g];
+    const int64_t p0 = pin_base[g];
+    int64_t cur[9], end[9], last_cyc[9], tprev[9];
+    double sprev[9];
+    uint8_t v[9];
+    for (int i = 0; i <= k; ++i) {
+      cur[i] = pin_ptr[p0 + i];
+      end[i] = pin_ptr[p0 + i + 1];
+      v[i] = pin_init[p0 + i];
+      last_cyc[i] = -1;
+      tprev[i] = 0;
+      sprev[i] = 0.0;
+    }
+    unsigned S = 0; /* state over input pins, pin 0 = LSB */
+    for (int i = 0; i < k; ++i) S |= (unsigned)v[i] << i;
+    const double *cell_slew = slew_axis + (int64_t)cell * n_slew;
+    const double *cell_cap = cap_axis + (int64_t)cell * n_cap;
+    int64_t t_last = 0;
+
+    for (;;) {
+      /* next distinct timestamp of the k-way merge (Sec. 2.4.2, Fig. 3) */
+      int64_t t = INT64_MAX;
+      for (int i = 0; i <= k; ++i)
+        if (cur[i] < end[i] && evt_t[cur[i]] < t) t = evt_t[cur[i]];
+      if (t == INT64_MAX) break;
+
+      /* leakage of the interval that ends here, at the state held in it */
+      leak_interval(&R, leak_W[leak_base[cell] + S], t_last, t);
+
+      /* dynamic energy of every pin with an event at t (Fig. 7) */
+      for (int i = 0; i <= k; ++i) {
+        if (!(cur[i] < end[i] && evt_t[cur[i]] == t)) continue;
+        const int64_t e = cur[i];
+        const double slew = (double)evt_slew[e];
+        const int64_t cyc = t / R.T;
+        double E;
+        int is_int;
+        if (i < k) { /* input pin: state-selected internal-power LUT (Fig. 2) */
+          const double *tab = lut_J + lut_base[cell] + ((int64_t)S * k + i) * n_slew * n_cap;
+          E = pa_oracle_bilerp(n_slew, n_cap, cell_slew, cell_cap, tab, slew, cap);
+          is_int = 1;
+        } else { /* output pin: Eq. 1 for a 0->1 event */
+          E = evt_val[e] == 1 ? 0.5 * cap * vdd_V * vdd_V : 0.0;
+          is_int = 0;
+        }
+        cyc_events[cyc] += 1;
+        R.n_events += 1;
+        /* GlitchDetectUpdate: a second or later event of this pin in the
+         * current clock cycle is a glitch (Sec. 2.4.1, Fig. 7) */
+        const int glitch = (last_cyc[i] == cyc);
+        if (glitch) {
+          const double pw = (double)(t - tprev[i]);
+          double r = pw / (0.5 * (slew + sprev[i])); /* Eq. 2 as read above */
+          if (r > 1.0) r = 1.0;
+          nadd(&R.e_gl, r * E);
+          nadd(&R.wave[cyc], r * E);
+          cyc_glitches[cyc] += 1;
+          R.n_glitches += 1;
+        } else {
+          nadd(is_int ? &R.e_int : &R.e_sw, E);
+          nadd(&R.wave[cyc], E);
+        }
+        if (evt_glitch) evt_glitch[e] = (uint8_t)glitch;
+        if (evt_state_before) evt_state_before[e] = (uint8_t)(i < k ? S : 0);
+        last_cyc[i] = cyc;
+        tprev[i] = t;
+        sprev[i] = slew;
+      }
+
+      /* apply every event at t, then rebuild the state (Sec. 2.4.2) */
+      for (int i = 0; i <= k; ++i) {
+        if (cur[i] < end[i] && evt_t[cur[i]] == t) {
+          v[i] = evt_val[cur[i]];
+          cur[i] += 1;
+        }
+      }
+      S = 0;
+      for (int i = 0; i < k; ++i) S |= (unsigned)v[i] << i;
+      t_last = t;
+    }
+    /* leakage is always present: the last interval runs to t_max */
+    leak_interval(&R, leak_W[leak_base[cell] + S], t_last, t_max);
+  }
+
+  for (int64_t c = 0; c < R.n_cyc; ++c) wave_J[c] = nval(&R.wave[c]);
+  const double window_s = (double)t_max * tick_s;
+  out->e_int_J = nval(&R.e_int);
+  out->e_sw_J = nval(&R.e_sw);
+  out->e_gl_J = nval(&R.e_gl);
+  out->e_leak_J = nval(&R.e_leak);
+  out->p_int_W = out->e_int_J / window_s; /* Eq. 3 */
+  out->p_sw_W = out->e_sw_J / window_s;
+  out->p_gl_W = out->e_gl_J / window_s;
+  out->p_leak_W = out->e_leak_J / window_s;
+  out->n_events = R.n_events;
+  out->n_glitches = R.n_glitches;
+  out->n_cycles = R.n_cyc;
+  free(pin_base);
+  free(lut_base);
+  free(leak_base);
+  free(R.wave);
+  return 0;
+}
