@@ -1,0 +1,141 @@
+/*
+ * pa.h -- C ABI of the MI355X (gfx950) gate-level time-based power analysis
+ * library.
+ *
+ * The method is the one of "GPU-Accelerated Gate-Level Time-Based Power
+ * Analysis via Event-Density-Aware Partitioning and Kernel Fusion" (arXiv
+ * 2609.05960), called "the paper" below:
+ *   - per event: reconstruct the gate state before the event (Sec. 2.4.1),
+ *     pick the state's internal-power LUT and interpolate it on input slew
+ *     and output load (Sec. 2.4.1, Fig. 2), add 1/2 c v^2 for a 0->1 event on
+ *     the output pin (Eq. 1), detect glitches by counting a pin's events per
+ *     clock cycle and scale their energy by r_gl (Sec. 2.4.1, Eq. 2, Fig. 7),
+ *     and add the energy to the bin of its clock cycle;
+ *   - per gate: merge the pin streams in time order, apply all events of a
+ *     timestamp together, charge state-dependent leakage over every
+ *     inter-event interval (Eq. 4) and spread it over the cycle bins it
+ *     overlaps in proportion to the overlap (Sec. 2.4.2);
+ *   - powers are energies over the analysis window (Eq. 3).
+ * Readings of what the paper leaves open (its Eqs. 1-4 are not printed in the
+ * available text) are fixed as follows and are part of this contract:
+ *   E_sw = 0.5 * c * Vdd^2 per 0->1 output event (0 J for 1->0);
+ *   r_gl = min(1, pw / ((rSlew + fSlew) / 2)), pw = time since the previous
+ *     event on the same pin, rSlew/fSlew = slews of that event and this one;
+ *   the m-th event (m >= 2) of a pin inside one clock cycle is a glitch and
+ *     adds r_gl * E to the glitch component (only) and to the waveform;
+ *   state S = sum_i v_i 2^i over the input pins (pin 0 = LSB);
+ *   bins are [c T, (c+1) T), N_cyc = ceil(t_max / T), the last may be partial;
+ *   bilinear interpolation extrapolates linearly outside the LUT axes;
+ *   P = E / (t_max * tick_s), E_leak = p_leak * dt * tick_s.
+ *
+ * Conventions for every function:
+ *   - returns PA_OK (0) or a negative PA_E* code; no exception crosses the ABI;
+ *     pa_last_error() gives a message for the calling thread's last failure;
+ *   - array arguments are DEVICE pointers on the context's device (torch
+ *     tensors' data_ptr(), or hipMalloc'd memory), unless stated otherwise;
+ *   - the load calls copy their inputs into library-owned device memory, so
+ *     the caller may free or reuse its arrays once the call returns;
+ *   - a failing load leaves the previously loaded data intact;
+ *   - one context per device; a context is not thread-safe.
+ */
+#ifndef PA_H
+#define PA_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_OK 0
+#define PA_EINVAL (-1) /* bad argument (null pointer, size out of range, call-shape error) */
+#define PA_EDATA (-2)  /* design or event data break the contract above */
+#define PA_ENOMEM (-3) /* device or host allocation failed */
+#define PA_EHIP (-4)   /* HIP runtime error */
+#define PA_ESTATE (-5) /* wrong call order (e.g. pa_run before both loads) */
+
+typedef struct pa_ctx pa_ctx;
+
+/* Speed knobs.  They never change results beyond fp64 summation order; a
+ * zero field means "choose automatically". */
+typedef struct {
+  int32_t chunk_cycles;   /* cycles per time chunk of the event layout (max 1024) */
+  int32_t grid_blocks;    /* blocks of the fused pass (0 = one per compute unit) */
+  int32_t time_kernels;   /* nonzero: record per-kernel device times of pa_run */
+  int32_t reserved;
+} pa_tunables;
+
+/* Create a context on HIP device `hip_device`, launching on `hip_stream`
+ * (a hipStream_t; NULL = the device's null stream).  `t` may be NULL. */
+int pa_create(pa_ctx **out, int hip_device, void *hip_stream, const pa_tunables *t);
+void pa_destroy(pa_ctx *ctx);
+/* Change the stream later calls launch on (a hipStream_t). */
+int pa_set_stream(pa_ctx *ctx, void *hip_stream);
+const char *pa_last_error(void);
+
+/* Load the design (paper Sec. 2.4.1-2.4.2, Figs. 2-3: per-gate cell, state-
+ * indexed internal-power LUTs per input pin, state-indexed leakage).
+ *   gate_cell[G]   int32 cell id in [0, n_cells)
+ *   gate_cap_F[G]  float64 total output load c (pin + wire), farads, finite
+ *   cell_n_in[n_cells] int32 input count k in 1..8 (2^k states; the gate has k
+ *                  input pins then one output pin)
+ *   slew_axis[n_cells][n_slew]  float64 ticks, strictly increasing per cell
+ *   cap_axis[n_cells][n_cap]    float64 farads, strictly increasing per cell
+ *   lut_J   float64, per cell concatenated: [2^k][k][n_slew][n_cap] joules
+ *   leak_W  float64, per cell concatenated: [2^k] watts
+ *   2 <= n_slew, n_cap <= 16.  Loading a design drops any loaded events. */
+int pa_load_design(pa_ctx *ctx, int64_t n_gates, const int32_t *gate_cell, const double *gate_cap_F,
+                   int32_t n_cells, const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap,
+                   const double *slew_axis, const double *cap_axis, const double *lut_J,
+                   const double *leak_W, double vdd_V);
+
+/* Load the activity (paper Sec. 2.4.1-2.4.2: per-pin sorted event streams).
+ *   n_pins  must equal sum_g (k_g + 1); pins are gate-major, inputs 0..k-1,
+ *           output k
+ *   n_events must equal pin_ptr[n_pins]; 0 <= n_events < 2^32
+ *   pin_ptr[P+1]  int64 CSR offsets, pin_ptr[0] = 0, nondecreasing
+ *   pin_init[P]   uint8 value of the pin at t = 0, in {0, 1}
+ *   evt_t[E]      int64 ticks, strictly increasing per pin, 0 <= t < t_max
+ *   evt_val[E]    uint8 new value, alternating per pin starting from !init
+ *   evt_slew[E]   float32 ticks, finite and > 0 (same unit as slew_axis)
+ *   t_clk  clock period in ticks, 1 <= t_clk < 2^32; t_max > 0 analysis end;
+ *   tick_s seconds per tick (> 0).
+ * The events are validated and re-laid out (chunk-major, see the design
+ * notes) into library-owned memory. */
+int pa_load_events(pa_ctx *ctx, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr,
+                   const uint8_t *pin_init, const int64_t *evt_t, const uint8_t *evt_val,
+                   const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s);
+
+typedef struct {
+  double p_int_W, p_sw_W, p_gl_W, p_leak_W; /* Eq. 3 powers */
+  double e_int_J, e_sw_J, e_gl_J, e_leak_J; /* energies over [0, t_max) */
+  uint64_t n_events, n_glitches;
+  int64_t n_cycles;
+} pa_totals;
+
+/* One pass of the power analysis over the loaded design and events.
+ *   out            HOST pointer, filled on return (pa_run synchronizes its stream)
+ *   wave_J[C]      device: energy per cycle bin, J (power = wave_J[c] / (len_c * tick_s))
+ *   cyc_events[C]  device: number of events whose cycle is c
+ *   cyc_glitches[C] device: number of glitch events in cycle c
+ *   evt_glitch[E]  device or NULL: 1 if the event is a glitch (caller's CSR order)
+ *   evt_state_before[E] device or NULL: S(t-) of input-pin events, 0 for output
+ *                  events (caller's CSR order)
+ * C = n_cycles = ceil(t_max / t_clk).  The output arrays must not overlap. */
+int pa_run(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
+           uint8_t *evt_glitch, uint8_t *evt_state_before);
+
+/* Layout and launch facts of the loaded data (HOST struct). */
+typedef struct {
+  int64_t n_gates, n_pins, n_events, n_cycles;
+  int32_t chunk_cycles, n_chunks;
+  int32_t grid_blocks, block_threads;
+  int32_t batch_events, max_segment_events;
+  int64_t device_bytes;       /* library-owned device memory */
+  float kernel_ms[4];         /* last pa_run with time_kernels: fused, finalize, (unused), total */
+} pa_info;
+int pa_get_info(pa_ctx *ctx, pa_info *info);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

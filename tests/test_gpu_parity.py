@@ -1,0 +1,161 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element
+by element on the same seeded inputs.
+
+Cases: the hand circuits; small random designs over every input count 1..8,
+forced same-timestamp collisions and several chunk lengths (results must
+not depend on the layout's chunking or the launch grid); edge cases (no
+events, one gate, partial last bin, events at t = 0 and t = t_max - 1, a
+dense glitch train); and the Tiny, Medium, Skewed and Glitch-heavy workloads
+at full size in the default launch configuration.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import golden_util
+import parity_util as pu
+from workloads import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(d, t, **kw):
+    import oracle
+
+    return oracle.run(d, t, **kw)
+
+
+def _print_case(name):
+    print(f"[case] {name}", flush=True)
+
+
+@pytest.mark.parametrize("path", golden_util.fixtures(), ids=lambda p: p.split("/")[-1])
+def test_hand_circuits(path):
+    spec, d, t = golden_util.load(path)
+    _print_case(path)
+    g = pu.gpu_run(d, t)
+    pu.assert_parity(g, _oracle(d, t), label=path)
+    exp = spec["expect"]
+    for key in ("e_int_J", "e_sw_J", "e_gl_J", "e_leak_J"):
+        assert pu.rel_err(g[key], exp[key]) <= 1e-12 or abs(g[key] - exp[key]) < 1e-30, key
+    assert g["evt_glitch"].tolist() == exp["evt_glitch"]
+    assert g["evt_state_before"].tolist() == exp["evt_state_before"]
+
+
+def _random(seed, G=200, C=40, T=1000, rate=0.3, ks=(1, 2, 3, 4), collide=0, t_max=None):
+    rng = np.random.default_rng(seed)
+    lib = synth.make_library(rng, ks, cells_per_k=2, n_axis=5)
+    k = rng.choice(np.array(ks), size=G)
+    des = synth.assign_gates(rng, lib, k, 1.0, 50.0)
+    P = int(des.pin_base()[-1])
+    tr = synth.poisson_trace(rng, np.full(P, rate), C, T)
+    pin = np.repeat(np.arange(P), np.diff(tr.pin_ptr))
+    tt = tr.evt_t
+    if collide:
+        tt = (tt // collide) * collide
+    if t_max is not None:
+        tt = np.minimum(tt, t_max - 1)
+    tr = synth._finish_trace(rng, P, pin, tt, T, t_max if t_max is not None else C * T)
+    tr = dataclasses.replace(tr, evt_slew=rng.uniform(50, 900, tr.n_events).astype(np.float32))
+    return des, tr
+
+
+RANDOM_CASES = [
+    dict(seed=1),
+    dict(seed=2, ks=(5, 6, 7, 8), G=60, rate=0.2),
+    dict(seed=3, collide=50, rate=0.8, G=120),
+    dict(seed=4, collide=1000, rate=0.6, G=80),  # events on cycle boundaries
+    dict(seed=5, t_max=39 * 1000 + 217),  # partial last bin
+    dict(seed=6, G=3000, C=300, rate=0.05),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+@pytest.mark.parametrize("chunk", [0, 1, 3, 16])
+def test_random_designs_any_chunking(case, chunk):
+    d, t = _random(**case)
+    _print_case(f"random {case} chunk {chunk}")
+    o = _oracle(d, t)
+    g = pu.gpu_run(d, t, chunk_cycles=chunk)
+    pu.assert_parity(g, o, label=f"{case} chunk {chunk}")
+    if chunk:
+        assert g["_info"]["chunk_cycles"] == min(chunk, t.n_cycles)
+
+
+@pytest.mark.parametrize("grid", [1, 3, 64, 256])
+def test_launch_grid_does_not_change_results(grid):
+    d, t = _random(seed=7, G=2000, C=200, rate=0.1)
+    _print_case(f"grid {grid}")
+    pu.assert_parity(pu.gpu_run(d, t, grid_blocks=grid), _oracle(d, t), label=f"grid {grid}")
+
+
+def test_no_events():
+    d, t = _random(seed=8, G=50, rate=0.0)
+    assert t.n_events == 0
+    _print_case("no events")
+    pu.assert_parity(pu.gpu_run(d, t), _oracle(d, t), label="no events")
+
+
+def test_single_gate_and_window_edges():
+    d, t = _random(seed=9, G=1, C=5, T=100, rate=3.0, ks=(3,))
+    # force events at t = 0 and t = t_max - 1 on the first input pin
+    ev = t.evt_t.copy()
+    p0 = slice(t.pin_ptr[0], t.pin_ptr[1])
+    if ev[p0].size >= 2:
+        ev[t.pin_ptr[0]] = 0
+        ev[t.pin_ptr[1] - 1] = t.t_max - 1
+    pin = np.repeat(np.arange(t.n_pins), np.diff(t.pin_ptr))
+    t2 = synth._finish_trace(np.random.default_rng(1), t.n_pins, pin, ev, t.t_clk, t.t_max)
+    _print_case("single gate")
+    pu.assert_parity(pu.gpu_run(d, t2), _oracle(d, t2), label="single gate")
+
+
+def test_dense_glitch_train():
+    """One gate with thousands of events, many inside single cycles."""
+    rng = np.random.default_rng(10)
+    lib = synth.make_library(rng, (2,), cells_per_k=1, n_axis=4)
+    des = synth.assign_gates(rng, lib, np.array([2, 2]), 1.0, 50.0)
+    T, C = 10_000, 30
+    P = 6
+    rates = np.array([60.0, 40.0, 80.0, 0.5, 0.1, 0.2])
+    tr = synth.poisson_trace(rng, rates, C, T)
+    tr = dataclasses.replace(tr, evt_slew=rng.uniform(50, 900, tr.n_events).astype(np.float32))
+    _print_case("dense train")
+    o = _oracle(des, tr)
+    assert o["n_glitches"] > 1000
+    for chunk in (0, 2):
+        pu.assert_parity(pu.gpu_run(des, tr, chunk_cycles=chunk), o, label=f"dense chunk {chunk}")
+
+
+def test_repeated_runs_agree():
+    """Accumulators are reset between passes: two passes give the same integers
+    and the same energies within the fp64 tolerance."""
+    import eda_gate_level_amd as pa
+
+    d, t = _random(seed=11, G=1500, C=120, rate=0.2)
+    _print_case("repeated")
+    an = pa.PowerAnalysis()
+    try:
+        an.load(d, t)
+        outs = [an.run(per_event=True) for _ in range(3)]
+    finally:
+        pass
+    o = _oracle(d, t)
+    for r in outs:
+        g = dict(r["totals"])
+        g.update(wave_J=r["wave_J"].cpu().numpy(), cyc_events=r["cyc_events"].cpu().numpy().astype(np.uint64),
+                 cyc_glitches=r["cyc_glitches"].cpu().numpy().astype(np.uint64),
+                 evt_glitch=r["evt_glitch"][:t.n_events].cpu().numpy(),
+                 evt_state_before=r["evt_state_before"][:t.n_events].cpu().numpy())
+        pu.assert_parity(g, o, label="repeat")
+    an.close()
+
+
+@pytest.mark.parametrize("name", ["tiny", "medium", "skewed", "glitch_heavy"])
+def test_workload_full_size(name):
+    w = synth.make(name)
+    _print_case(f"workload {name} E={w.trace.n_events}")
+    o = _oracle(w.design, w.trace)
+    g = pu.gpu_run(w.design, w.trace)
+    pu.assert_parity(g, o, label=name)
