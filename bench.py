@@ -51,7 +51,21 @@ def main():
     ap.add_argument("--grid-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--quick", action="store_true", help="no 2 s clock warm-up and no CPU baseline (profiling runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB, 5 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+
+        n = args.copy_calibration << 18  # float32 elements
+        x = torch.ones(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        for _ in range(5):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 5}))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding is a design note "
                                    "(one all-reduce of the per-cycle bins), not implemented", "n_gpus": args.gpus}))
@@ -85,7 +99,7 @@ def main():
     clk_before = clocks()
     for _ in range(args.warmup):
         an.run(outs)
-    t_end = time.time() + 2.0
+    t_end = time.time() + (0.0 if args.quick else 2.0)
     while time.time() < t_end:
         an.run(outs)
     # warm (back-to-back, no flush) device times, for reference
@@ -117,7 +131,7 @@ def main():
     value = E / (ms_step * 1e-3)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not (args.no_cpu_baseline or args.quick):
         import oracle
 
         oracle.build()

@@ -68,6 +68,7 @@ uint32_t bits_for(uint64_t v) {  // bits needed to hold 0..v (at least 1)
 struct Design {
   int64_t G = 0, P = 0;
   int32_t n_cells = 0, n_slew = 0, n_cap = 0, kmax = 0;
+  int64_t n_leak = 0;
   double vdd = 0;
   DBuf cell_k, cell_lut_base, cell_leak_base, lut, leak, slew_axis, slew_invw;
   DBuf gate_info, gate_capfrac, gate_esw, gate_k, pin_base, pin_gate, pin_local;
@@ -222,6 +223,7 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   d.n_slew = n_slew;
   d.n_cap = n_cap;
   d.kmax = kmax;
+  d.n_leak = (int64_t)kb;
   d.vdd = vdd_V;
   const int64_t G = n_gates;
   DBuf cap_axis_d, err;
@@ -343,15 +345,14 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   v.t_max = t_max;
   v.tick_s = tick_s;
   v.C = (t_max + t_clk - 1) / t_clk;
-  const uint32_t gb = bits_for(G > 0 ? (uint64_t)(G - 1) : 0);
+  if ((uint64_t)G > pa::kKeyMaxGates - 1)
+    return fail(PA_EINVAL, "pa_load_events: designs of more than 2^23 - 1 gates are not supported");
   const uint32_t pbits = bits_for((uint64_t)d.kmax);
-  const uint32_t sb = (uint32_t)d.kmax;
-  const int tb_avail = 64 - (int)gb - (int)pbits - 1 - (int)sb;
-  if (tb_avail < 1) return fail(PA_EINVAL, "pa_load_events: design too large for the 64-bit event key");
-  const int tb_lim = std::min(tb_avail, 32);
-  const uint64_t max_ticks = std::min<uint64_t>(uint64_t(1) << tb_lim, (uint64_t(1) << 32) - 1);
+  // the pass keeps (pin, t_rel) of an event in one 32-bit word
+  const int tb_lim = 32 - (int)pbits;
+  const uint64_t max_ticks = uint64_t(1) << tb_lim;
   const int64_t cc_cap = (int64_t)(max_ticks / (uint64_t)t_clk);
-  if (cc_cap < 1) return fail(PA_EINVAL, "pa_load_events: clock period too long for the 64-bit event key");
+  if (cc_cap < 1) return fail(PA_EINVAL, "pa_load_events: clock period longer than 2^%d ticks", tb_lim);
   const int ecap = pa::pass_batch_events();
   int64_t Cc = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : 512;
   Cc = std::min<int64_t>({Cc, (int64_t)pa::pass_max_chunk_cycles(), cc_cap, v.C});
@@ -383,15 +384,9 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
     Cc = std::max<int64_t>(1, Cc / 2);
   }
   v.chunk_ticks = (int64_t)v.Cc * t_clk;
-  const uint32_t tbits = bits_for((uint64_t)(v.chunk_ticks - 1));
-  v.kf.s_bits = sb;
-  v.kf.v_sh = sb;
-  v.kf.t_sh = sb + 1;
-  v.kf.p_sh = v.kf.t_sh + tbits;
-  v.kf.g_sh = v.kf.p_sh + pbits;
-  v.kf.p_mask = (1u << pbits) - 1u;
-  v.kf.t_mask = (uint64_t(1) << tbits) - 1u;
-  if (v.kf.g_sh + gb > 64) return fail(PA_EINVAL, "pa_load_events: event key overflow");
+  v.kf.t_bits = bits_for((uint64_t)(v.chunk_ticks - 1));
+  v.kf.p_bits = pbits;
+  if (v.kf.t_bits + pbits > 32) return fail(PA_EINVAL, "pa_load_events: event key overflow");
 
   // ---- layout: offsets of every (chunk, pin) run, chunk-start values, scatter
   const int64_t QP = (int64_t)v.Q * P;
@@ -485,6 +480,8 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   a.slew_invw = d.slew_invw.as<double>();
   a.n_slew = d.n_slew;
   a.n_cap = d.n_cap;
+  a.n_cells = d.n_cells;
+  a.n_leak = d.n_leak;
   a.acc_wave = v.acc_wave.as<double>();
   a.acc_cnt = v.acc_cnt.as<unsigned long long>();
   a.dP = v.dP[cur].as<double>();

@@ -40,24 +40,25 @@ __host__ __device__ inline uint32_t divu32(uint32_t n, const DivU32 &D) {
 }
 
 // ---------------------------------------------------------------------------
-// Packed 64-bit event key of the chunk-major layout.  From the most to the
-// least significant bits:
-//   [gate][pin][t_rel][val][S0]
-// gate  = gate id, pin = local pin index (0..k-1 inputs, k = output),
-// t_rel = timestamp minus the start of the event's time chunk,
-// val   = the pin's value after the event,
-// S0    = input-pin state of the gate at the start of the chunk.
-// Inside one (chunk, gate) segment keys sort by (pin, t_rel), so a binary
-// search over the segment locates any pin's events around a time.
+// Packed 64-bit event key of the chunk-major layout, fixed fields:
+//   bits [41, 64)  gate id (designs up to 2^23 - 1 gates)
+//   bits [ 9, 41)  lk = (pin << t_bits) | t_rel
+//   bit   8        val: the pin's value after the event
+//   bits [ 0,  8)  S0: input-pin state of the gate at the start of the chunk
+// pin = local pin index (0..k-1 inputs, k = output), t_rel = timestamp minus
+// the start of the event's time chunk (t_bits wide, chosen at load so that
+// pin and t_rel share one 32-bit word).  Inside one (chunk, gate) segment the
+// keys, and their lk words, sort by (pin, t_rel), so a search over the
+// segment locates any pin's events around a time.
 // ---------------------------------------------------------------------------
+constexpr uint32_t kKeyGateShift = 41;
+constexpr uint32_t kKeyLkShift = 9;
+constexpr uint32_t kKeyValShift = 8;
+constexpr uint64_t kKeyMaxGates = uint64_t(1) << 23;
+
 struct KeyFmt {
-  uint32_t s_bits;  // width of S0 (= max inputs of any cell)
-  uint32_t v_sh;    // = s_bits
-  uint32_t t_sh;    // = s_bits + 1
-  uint32_t p_sh;    // = t_sh + t_bits
-  uint32_t g_sh;    // = p_sh + p_bits
-  uint32_t p_mask;  // (1 << p_bits) - 1
-  uint64_t t_mask;  // (1 << t_bits) - 1
+  uint32_t t_bits;  // width of t_rel
+  uint32_t p_bits;  // width of the pin index
 };
 
 // Kernel arguments of one pass (passed by value).
@@ -91,6 +92,8 @@ struct PassArgs {
   const double *slew_axis;  // [n_cells][n_slew]
   const double *slew_invw;  // [n_cells][n_slew-1]
   int32_t n_slew, n_cap;
+  int32_t n_cells;
+  int64_t n_leak;             // entries of the leakage table
   // accumulators
   double *acc_wave;                  // [8][C]
   unsigned long long *acc_cnt;       // [8][C]  events | glitches << 32
@@ -130,5 +133,6 @@ hipError_t launch_finalize(const FinalArgs &a, hipStream_t s);
 int pass_block_threads();
 int pass_batch_events();
 int pass_max_chunk_cycles();
+bool pass_cells_fit_lds(int n_cells, int n_slew, int64_t n_leak);
 
 }  // namespace pa

@@ -165,8 +165,9 @@ __global__ void k_scatter(int64_t E, int64_t P, int64_t G, const int64_t *evt_t,
     const uint64_t trel = (uint64_t)(t - q * chunk_ticks);
     const int64_t qp = q * P + p;
     const int64_t dest = (int64_t)pin_off[qp] + (e - (int64_t)first[qp]);
-    const uint64_t k = ((uint64_t)g << kf.g_sh) | (i << kf.p_sh) | (trel << kf.t_sh) |
-                       ((uint64_t)(evt_val[e] & 1u) << kf.v_sh) | (uint64_t)st[q * G + g];
+    const uint64_t lk = (i << kf.t_bits) | trel;
+    const uint64_t k = ((uint64_t)g << kKeyGateShift) | (lk << kKeyLkShift) |
+                       ((uint64_t)(evt_val[e] & 1u) << kKeyValShift) | (uint64_t)st[q * G + g];
     key_out[dest] = k;
     slew_out[dest] = evt_slew[e];
     orig_out[dest] = (uint32_t)e;
