@@ -22,7 +22,6 @@ import argparse
 import json
 import os
 import statistics
-import subprocess
 import sys
 import time
 
@@ -33,12 +32,21 @@ HBM_PEAK_GBS = 8000.0
 
 
 def clocks():
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-        keep = [ln.strip() for ln in out.splitlines() if "sclk" in ln.lower() or "mclk" in ln.lower()]
-        return keep[:4]
-    except Exception as e:  # clocks are informational
-        return [f"unavailable: {e}"]
+    """Current shader and memory clock levels read from the amdgpu sysfs files
+    (no child process: the GPU is already initialised when this runs)."""
+    import glob
+
+    found = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [ln.strip() for ln in f if ln.rstrip().endswith("*")]
+            except OSError:
+                continue
+            if cur:
+                found.append(f"{os.path.basename(os.path.dirname(dev))} {name}: {cur[0]}")
+    return found[:4]
 
 
 def main():

@@ -86,10 +86,13 @@ struct Events {
   uint32_t max_seg = 0;
   pa::KeyFmt kf{};
   DBuf key, slew, orig, chunk_base, pin_init;
+  std::vector<uint32_t> h_chunk_base;
+  DBuf rstart, rchunk;  // block ranges of the pass
+  int32_t n_ranges = 0;
   DBuf acc_wave, acc_cnt, dP[2], tot[2], tot_cnt[2], res;
   int64_t bytes() const {
     int64_t b = (int64_t)(key.bytes + slew.bytes + orig.bytes + chunk_base.bytes + pin_init.bytes + acc_wave.bytes +
-                          acc_cnt.bytes + res.bytes);
+                          acc_cnt.bytes + res.bytes + rstart.bytes + rchunk.bytes);
     for (int s = 0; s < 2; ++s) b += (int64_t)(dP[s].bytes + tot[s].bytes + tot_cnt[s].bytes);
     return b;
   }
@@ -280,6 +283,35 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   return PA_OK;
 }
 
+// Block ranges of the pass: every chunk's events are cut into pieces of about
+// E / target events (never across a chunk, so a block's bins cover one chunk);
+// the kernel moves each nominal cut forward to the next segment head.
+static int build_ranges(pa_ctx *c) {
+  Events &v = c->ev;
+  const int64_t target_blocks = c->tun.grid_blocks > 0 ? c->tun.grid_blocks : 2 * (int64_t)c->n_cu;
+  const int64_t min_events = 4 * (int64_t)pa::pass_wave_batch() * (pa::pass_block_threads() / 64);
+  const int64_t per = std::max<int64_t>(min_events, (v.E + target_blocks - 1) / std::max<int64_t>(1, target_blocks));
+  std::vector<uint32_t> rs, rq;
+  for (int32_t q = 0; q < v.Q; ++q) {
+    const int64_t a = v.h_chunk_base[q], b = v.h_chunk_base[q + 1];
+    if (b <= a) continue;
+    const int64_t n = std::max<int64_t>(1, (b - a + per / 2) / per);
+    for (int64_t i = 0; i < n; ++i) {
+      rs.push_back((uint32_t)(a + (b - a) * i / n));
+      rq.push_back((uint32_t)q);
+    }
+  }
+  v.n_ranges = (int32_t)rs.size();
+  rs.push_back((uint32_t)v.E);
+  rq.push_back(0);
+  HIPCHK(v.rstart.alloc(sizeof(uint32_t) * rs.size()));
+  HIPCHK(v.rchunk.alloc(sizeof(uint32_t) * rq.size()));
+  HIPCHK(hipMemcpyAsync(v.rstart.p, rs.data(), sizeof(uint32_t) * rs.size(), hipMemcpyHostToDevice, c->stream));
+  HIPCHK(hipMemcpyAsync(v.rchunk.p, rq.data(), sizeof(uint32_t) * rq.size(), hipMemcpyHostToDevice, c->stream));
+  HIPCHK(hipStreamSynchronize(c->stream));
+  return PA_OK;
+}
+
 static int zero_accumulators(pa_ctx *c) {
   Events &v = c->ev;
   hipStream_t s = c->stream;
@@ -346,81 +378,103 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   v.tick_s = tick_s;
   v.C = (t_max + t_clk - 1) / t_clk;
   if ((uint64_t)G > pa::kKeyMaxGates - 1)
-    return fail(PA_EINVAL, "pa_load_events: designs of more than 2^23 - 1 gates are not supported");
+    return fail(PA_EINVAL, "pa_load_events: designs of more than 2^22 - 1 gates are not supported");
   const uint32_t pbits = bits_for((uint64_t)d.kmax);
   // the pass keeps (pin, t_rel) of an event in one 32-bit word
   const int tb_lim = 32 - (int)pbits;
   const uint64_t max_ticks = uint64_t(1) << tb_lim;
   const int64_t cc_cap = (int64_t)(max_ticks / (uint64_t)t_clk);
   if (cc_cap < 1) return fail(PA_EINVAL, "pa_load_events: clock period longer than 2^%d ticks", tb_lim);
-  const int ecap = pa::pass_batch_events();
-  int64_t Cc = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : 512;
-  Cc = std::min<int64_t>({Cc, (int64_t)pa::pass_max_chunk_cycles(), cc_cap, v.C});
-  if (Cc < 1) Cc = 1;
-
-  DBuf cnt;
-  size_t tmp_bytes = 0;
-  for (;;) {
-    const int64_t Q = (v.C + Cc - 1) / Cc;
-    if (Q * P >= (int64_t(1) << 31)) return fail(PA_ENOMEM, "pa_load_events: too many (chunk, pin) pairs");
-    HIPCHK(cnt.alloc(sizeof(uint32_t) * (size_t)(Q * P + 1)));
-    HIPCHK(hipMemsetAsync(cnt.p, 0, cnt.bytes, s));
-    if (E > 0) HIPCHK(pa::launch_count(E, P, evt_t, ev_pin.as<uint32_t>(), Cc * t_clk, cnt.as<uint32_t>(), s));
-    HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
-    if (G > 0) HIPCHK(pa::launch_segmax(G, P, (int32_t)Q, d.pin_base.as<int64_t>(), cnt.as<uint32_t>(),
-                                        err.as<uint32_t>(), s));
-    uint32_t mx = 0;
-    HIPCHK(hipMemcpyAsync(&mx, err.p, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-    HIPCHK(hipStreamSynchronize(s));
-    if (mx <= (uint32_t)ecap) {
-      v.Cc = (int32_t)Cc;
-      v.Q = (int32_t)Q;
-      v.max_seg = mx;
-      break;
-    }
-    if (Cc == 1)
-      return fail(PA_EDATA, "pa_load_events: a gate has %u events inside one clock cycle (at most %d supported)", mx,
-                  ecap);
-    Cc = std::max<int64_t>(1, Cc / 2);
-  }
-  v.chunk_ticks = (int64_t)v.Cc * t_clk;
+  // chunk length: a power of two (window lengths halve it), at most the LDS bins
+  int64_t Cc_want = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : 256;
+  Cc_want = std::min<int64_t>({Cc_want, (int64_t)pa::pass_max_chunk_cycles(), cc_cap});
+  int64_t Cc = 1;
+  while (Cc * 2 <= Cc_want) Cc *= 2;
+  int32_t lc = 0;
+  while ((int64_t(1) << lc) < Cc) ++lc;
+  v.Cc = (int32_t)Cc;
+  v.Q = (int32_t)((v.C + Cc - 1) / Cc);
+  v.chunk_ticks = Cc * t_clk;
   v.kf.t_bits = bits_for((uint64_t)(v.chunk_ticks - 1));
   v.kf.p_bits = pbits;
   if (v.kf.t_bits + pbits > 32) return fail(PA_EINVAL, "pa_load_events: event key overflow");
+  const int32_t Q = v.Q;
 
-  // ---- layout: offsets of every (chunk, pin) run, chunk-start values, scatter
-  const int64_t QP = (int64_t)v.Q * P;
-  DBuf pin_off, first, pinval, st, tmp;
-  HIPCHK(pin_off.alloc(sizeof(uint32_t) * (size_t)(QP + 1)));
-  HIPCHK(first.alloc(sizeof(uint32_t) * (size_t)(QP + 1)));
-  HIPCHK(pinval.alloc((size_t)QP + 1));
-  HIPCHK(st.alloc((size_t)((int64_t)v.Q * G + 1)));
-  if (QP > 0) {
-    HIPCHK(pa::scan_exclusive_u32(cnt.as<uint32_t>(), pin_off.as<uint32_t>(), QP, nullptr, &tmp_bytes, s));
-    HIPCHK(tmp.alloc(tmp_bytes));
-    HIPCHK(pa::scan_exclusive_u32(cnt.as<uint32_t>(), pin_off.as<uint32_t>(), QP, tmp.p, &tmp_bytes, s));
-    HIPCHK(pa::launch_pin_chunks(P, v.Q, pin_ptr, pin_init, cnt.as<uint32_t>(), first.as<uint32_t>(),
-                                 pinval.as<uint8_t>(), s));
-  }
+  // ---- density-aware windows: per-gate level s (2^s windows per chunk), refined
+  //      until no (chunk, gate, window) segment holds more than kSegMax events
+  DBuf level, level_next, pw_len, pwbase, cnt, tmp, flags;
+  size_t tmp_bytes = 0;
+  HIPCHK(level.alloc(G));
+  HIPCHK(level_next.alloc(G));
+  HIPCHK(pw_len.alloc(sizeof(int64_t) * (G + 1)));
+  HIPCHK(pwbase.alloc(sizeof(int64_t) * (G + 1)));
+  HIPCHK(flags.alloc(sizeof(uint32_t) * 2));
   if (G > 0)
-    HIPCHK(pa::launch_seg_state(G, P, v.Q, d.pin_base.as<int64_t>(), d.gate_k.as<int32_t>(), pinval.as<uint8_t>(),
-                                st.as<uint8_t>(), s));
+    HIPCHK(pa::launch_gate_levels(G, d.pin_base.as<int64_t>(), pin_ptr, v.C, (int32_t)Cc, lc,
+                                  (double)pa::kSegMax / 4.0, level.as<uint8_t>(), s));
+  int64_t PW = 0;
+  uint32_t hflags[2] = {0, 0};
+  for (int iter = 0;; ++iter) {
+    HIPCHK(hipMemsetAsync(pw_len.p, 0, pw_len.bytes, s));
+    if (G > 0) HIPCHK(pa::launch_pw_len(G, d.gate_k.as<int32_t>(), level.as<uint8_t>(), pw_len.as<int64_t>(), s));
+    tmp_bytes = 0;
+    HIPCHK(pa::scan_exclusive_i64(pw_len.as<int64_t>(), pwbase.as<int64_t>(), G + 1, nullptr, &tmp_bytes, s));
+    HIPCHK(tmp.alloc(tmp_bytes));
+    HIPCHK(pa::scan_exclusive_i64(pw_len.as<int64_t>(), pwbase.as<int64_t>(), G + 1, tmp.p, &tmp_bytes, s));
+    HIPCHK(hipMemcpyAsync(&PW, pwbase.as<int64_t>() + G, sizeof(int64_t), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    if ((int64_t)Q * PW >= (int64_t(1) << 31)) return fail(PA_ENOMEM, "pa_load_events: too many (window, pin) pairs");
+    HIPCHK(cnt.alloc(sizeof(uint32_t) * (size_t)(Q * PW + 1)));
+    HIPCHK(hipMemsetAsync(cnt.p, 0, cnt.bytes, s));
+    if (E > 0)
+      HIPCHK(pa::launch_count_w(E, evt_t, ev_pin.as<uint32_t>(), d.pin_gate.as<int32_t>(), d.pin_local.as<uint8_t>(),
+                                d.gate_k.as<int32_t>(), level.as<uint8_t>(), pwbase.as<int64_t>(), PW, t_clk, lc,
+                                cnt.as<uint32_t>(), s));
+    HIPCHK(hipMemsetAsync(flags.p, 0, flags.bytes, s));
+    HIPCHK(hipMemcpyAsync(level_next.p, level.p, G, hipMemcpyDeviceToDevice, s));
+    if (G > 0)
+      HIPCHK(pa::launch_winmax(G, Q, d.gate_k.as<int32_t>(), level.as<uint8_t>(), pwbase.as<int64_t>(), PW, lc,
+                               cnt.as<uint32_t>(), level_next.as<uint8_t>(), flags.as<uint32_t>(),
+                               flags.as<uint32_t>() + 1, s));
+    HIPCHK(hipMemcpyAsync(hflags, flags.p, sizeof hflags, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    if (hflags[0] & 2u)
+      return fail(PA_EDATA, "pa_load_events: a gate has more than %d events inside one clock cycle", pa::kSegMax);
+    if (!(hflags[0] & 1u)) break;
+    std::swap(level, level_next);
+  }
+  v.max_seg = hflags[1];
+
+  // ---- layout: offsets of every (chunk, gate, window, pin) run, window-start values, scatter
+  const int64_t QPW = (int64_t)Q * PW;
+  DBuf off, first, vstart;
+  HIPCHK(off.alloc(sizeof(uint32_t) * (size_t)(QPW + 1)));
+  HIPCHK(first.alloc(sizeof(uint32_t) * (size_t)(QPW + 1)));
+  HIPCHK(vstart.alloc((size_t)QPW + 1));
+  tmp_bytes = 0;
+  HIPCHK(pa::scan_exclusive_u32(cnt.as<uint32_t>(), off.as<uint32_t>(), QPW + 1, nullptr, &tmp_bytes, s));
+  HIPCHK(tmp.alloc(tmp_bytes));
+  HIPCHK(pa::scan_exclusive_u32(cnt.as<uint32_t>(), off.as<uint32_t>(), QPW + 1, tmp.p, &tmp_bytes, s));
+  if (P > 0)
+    HIPCHK(pa::launch_pin_windows(P, Q, pin_ptr, pin_init, d.pin_gate.as<int32_t>(), d.pin_local.as<uint8_t>(),
+                                  d.gate_k.as<int32_t>(), level.as<uint8_t>(), pwbase.as<int64_t>(), PW,
+                                  cnt.as<uint32_t>(), first.as<uint32_t>(), vstart.as<uint8_t>(), s));
   HIPCHK(v.key.alloc(sizeof(uint64_t) * E));
   HIPCHK(v.slew.alloc(sizeof(float) * E));
   HIPCHK(v.orig.alloc(sizeof(uint32_t) * E));
-  HIPCHK(v.chunk_base.alloc(sizeof(uint32_t) * (v.Q + 1)));
+  HIPCHK(v.chunk_base.alloc(sizeof(uint32_t) * (Q + 1)));
   HIPCHK(v.pin_init.alloc(P));
   if (E > 0)
-    HIPCHK(pa::launch_scatter(E, P, G, evt_t, evt_slew, evt_val, ev_pin.as<uint32_t>(), d.pin_gate.as<int32_t>(),
-                              d.pin_local.as<uint8_t>(), v.chunk_ticks, first.as<uint32_t>(),
-                              pin_off.as<uint32_t>(), st.as<uint8_t>(), v.kf, v.key.as<uint64_t>(),
-                              v.slew.as<float>(), v.orig.as<uint32_t>(), s));
-  if (P > 0) {
-    HIPCHK(pa::launch_chunk_base(v.Q, P, E, pin_off.as<uint32_t>(), v.chunk_base.as<uint32_t>(), s));
-    HIPCHK(hipMemcpyAsync(v.pin_init.p, pin_init, P, hipMemcpyDeviceToDevice, s));
-  } else {
-    HIPCHK(hipMemsetAsync(v.chunk_base.p, 0, v.chunk_base.bytes, s));
-  }
+    HIPCHK(pa::launch_scatter_w(E, evt_t, evt_slew, evt_val, ev_pin.as<uint32_t>(), d.pin_gate.as<int32_t>(),
+                                d.pin_local.as<uint8_t>(), d.gate_k.as<int32_t>(), level.as<uint8_t>(),
+                                pwbase.as<int64_t>(), PW, t_clk, lc, v.chunk_ticks, first.as<uint32_t>(),
+                                off.as<uint32_t>(), vstart.as<uint8_t>(), v.kf, v.key.as<uint64_t>(),
+                                v.slew.as<float>(), v.orig.as<uint32_t>(), s));
+  HIPCHK(pa::launch_chunk_base_w(Q, PW, off.as<uint32_t>(), v.chunk_base.as<uint32_t>(), s));
+  if (P > 0) HIPCHK(hipMemcpyAsync(v.pin_init.p, pin_init, P, hipMemcpyDeviceToDevice, s));
+  v.h_chunk_base.resize(Q + 1);
+  HIPCHK(hipMemcpyAsync(v.h_chunk_base.data(), v.chunk_base.p, sizeof(uint32_t) * (Q + 1), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
 
   // ---- accumulators of the pass
   HIPCHK(v.acc_wave.alloc(sizeof(double) * 8 * v.C));
@@ -435,8 +489,14 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
 
   c->ev = std::move(v);
   c->has_events = true;
-  return zero_accumulators(c) == PA_OK ? (hipStreamSynchronize(s) == hipSuccess ? PA_OK : fail(PA_EHIP, "sync"))
-                                       : PA_EHIP;
+  int rc = build_ranges(c);
+  if (rc == PA_OK) rc = zero_accumulators(c);
+  if (rc == PA_OK && hipStreamSynchronize(s) != hipSuccess) rc = fail(PA_EHIP, "pa_load_events: sync");
+  if (rc != PA_OK) {
+    c->ev = Events();
+    c->has_events = false;
+  }
+  return rc;
 }
 
 int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
@@ -490,11 +550,10 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   a.evt_glitch = evt_glitch;
   a.evt_state = evt_state_before;
 
-  int grid = c->tun.grid_blocks > 0 ? c->tun.grid_blocks : c->n_cu;
-  const int64_t per_block_min = 2 * (int64_t)pa::pass_batch_events();
-  const int64_t by_events = std::max<int64_t>(1, (v.E + per_block_min - 1) / per_block_min);
-  const int64_t by_gates = std::max<int64_t>(1, (d.G + pa::pass_block_threads() - 1) / pa::pass_block_threads());
-  grid = (int)std::max<int64_t>(1, std::min<int64_t>(grid, std::max(by_events, by_gates)));
+  a.rstart = v.rstart.as<uint32_t>();
+  a.rchunk = v.rchunk.as<uint32_t>();
+  a.n_ranges = v.n_ranges;
+  const int grid = std::max(1, v.n_ranges);
   c->last_grid = grid;
 
   pa::FinalArgs f{};
@@ -564,7 +623,7 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
   info->n_chunks = c->ev.Q;
   info->grid_blocks = c->last_grid;
   info->block_threads = pa::pass_block_threads();
-  info->batch_events = pa::pass_batch_events();
+  info->batch_events = pa::pass_wave_batch();
   info->max_segment_events = (int32_t)c->ev.max_seg;
   info->device_bytes = c->d.bytes() + c->ev.bytes();
   for (int k = 0; k < 4; ++k) info->kernel_ms[k] = c->kernel_ms[k];

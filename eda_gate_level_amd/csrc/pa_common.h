@@ -40,25 +40,32 @@ __host__ __device__ inline uint32_t divu32(uint32_t n, const DivU32 &D) {
 }
 
 // ---------------------------------------------------------------------------
-// Packed 64-bit event key of the chunk-major layout, fixed fields:
-//   bits [41, 64)  gate id (designs up to 2^23 - 1 gates)
-//   bits [ 9, 41)  lk = (pin << t_bits) | t_rel
+// Packed 64-bit event key of the event layout, fixed fields:
+//   bits [42, 64)  gate id (designs up to 2^22 - 1 gates)
+//   bit  41        head: first event of its segment
+//   bits [ 9, 41)  lk = (pin code << t_bits) | t_rel
 //   bit   8        val: the pin's value after the event
-//   bits [ 0,  8)  S0: input-pin state of the gate at the start of the chunk
-// pin = local pin index (0..k-1 inputs, k = output), t_rel = timestamp minus
-// the start of the event's time chunk (t_bits wide, chosen at load so that
-// pin and t_rel share one 32-bit word).  Inside one (chunk, gate) segment the
-// keys, and their lk words, sort by (pin, t_rel), so a search over the
-// segment locates any pin's events around a time.
+//   bits [ 0,  8)  S0: input-pin state of the gate at the start of the segment
+// A segment is one (time chunk, gate, time window) triple: chunks are Cc
+// clock cycles long and every gate's chunk is cut into 2^s windows whose
+// length follows the gate's event density, so that no segment holds more
+// than a fixed number of events.  pin code = input pin index 0..k-1, or
+// kOutCode(p_bits) for the output pin; t_rel = timestamp minus the start of
+// the event's chunk.  Inside a segment the lk words increase strictly in
+// (pin code, t_rel) order.
 // ---------------------------------------------------------------------------
-constexpr uint32_t kKeyGateShift = 41;
+constexpr uint32_t kKeyGateShift = 42;
+constexpr uint32_t kKeyHeadShift = 41;
 constexpr uint32_t kKeyLkShift = 9;
 constexpr uint32_t kKeyValShift = 8;
-constexpr uint64_t kKeyMaxGates = uint64_t(1) << 23;
+constexpr uint64_t kKeyMaxGates = uint64_t(1) << 22;
+constexpr int kSegMax = 128;  // most events of one segment
+
+__host__ __device__ inline uint32_t out_code(uint32_t p_bits) { return (1u << p_bits) - 1u; }
 
 struct KeyFmt {
   uint32_t t_bits;  // width of t_rel
-  uint32_t p_bits;  // width of the pin index
+  uint32_t p_bits;  // width of the pin code
 };
 
 // Kernel arguments of one pass (passed by value).
@@ -68,6 +75,9 @@ struct PassArgs {
   const float *slew;
   const uint32_t *orig;        // caller's CSR index of each laid-out event
   const uint32_t *chunk_base;  // [Q+1]
+  const uint32_t *rstart;      // [n_ranges+1] nominal starts of the block ranges (inside one chunk each)
+  const uint32_t *rchunk;      // [n_ranges] chunk of each range
+  int32_t n_ranges;
   int64_t E;
   int32_t Q, Cc;
   int64_t C;
@@ -134,5 +144,6 @@ int pass_block_threads();
 int pass_batch_events();
 int pass_max_chunk_cycles();
 bool pass_cells_fit_lds(int n_cells, int n_slew, int64_t n_leak);
+int pass_wave_batch();
 
 }  // namespace pa

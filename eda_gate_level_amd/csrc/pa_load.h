@@ -31,21 +31,26 @@ hipError_t launch_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pi
 hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init,
                               const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_max,
                               uint32_t *ev_pin, uint32_t *err, hipStream_t s);
-hipError_t launch_count(int64_t E, int64_t P, const int64_t *evt_t, const uint32_t *ev_pin, int64_t chunk_ticks,
-                        uint32_t *cnt, hipStream_t s);
-hipError_t launch_segmax(int64_t G, int64_t P, int32_t Q, const int64_t *pin_base, const uint32_t *cnt,
-                         uint32_t *mx, hipStream_t s);
-hipError_t launch_pin_chunks(int64_t P, int32_t Q, const int64_t *pin_ptr, const uint8_t *pin_init,
-                             const uint32_t *cnt, uint32_t *first, uint8_t *pinval, hipStream_t s);
-hipError_t launch_seg_state(int64_t G, int64_t P, int32_t Q, const int64_t *pin_base, const int32_t *gate_k,
-                            const uint8_t *pinval, uint8_t *st, hipStream_t s);
-hipError_t launch_scatter(int64_t E, int64_t P, int64_t G, const int64_t *evt_t, const float *evt_slew,
-                          const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
-                          const uint8_t *pin_local, int64_t chunk_ticks, const uint32_t *first,
-                          const uint32_t *pin_off, const uint8_t *st, const KeyFmt &kf, uint64_t *key_out,
-                          float *slew_out, uint32_t *orig_out, hipStream_t s);
-hipError_t launch_chunk_base(int32_t Q, int64_t P, int64_t E, const uint32_t *pin_off, uint32_t *cb,
-                             hipStream_t s);
+hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int64_t *pin_ptr, int64_t C, int32_t Cc,
+                              int32_t lc, double target, uint8_t *level, hipStream_t s);
+hipError_t launch_pw_len(int64_t G, const int32_t *gate_k, const uint8_t *level, int64_t *pw_len, hipStream_t s);
+hipError_t launch_count_w(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
+                          const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
+                          const int64_t *pwbase, int64_t PW, int64_t T, int32_t lc, uint32_t *cnt, hipStream_t s);
+hipError_t launch_winmax(int64_t G, int32_t Q, const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase,
+                         int64_t PW, int32_t lc, const uint32_t *cnt, uint8_t *level_next, uint32_t *flags,
+                         uint32_t *max_seg, hipStream_t s);
+hipError_t launch_pin_windows(int64_t P, int32_t Q, const int64_t *pin_ptr, const uint8_t *pin_init,
+                              const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
+                              const uint8_t *level, const int64_t *pwbase, int64_t PW, const uint32_t *cnt,
+                              uint32_t *first, uint8_t *vstart, hipStream_t s);
+hipError_t launch_scatter_w(int64_t E, const int64_t *evt_t, const float *evt_slew, const uint8_t *evt_val,
+                            const uint32_t *ev_pin, const int32_t *pin_gate, const uint8_t *pin_local,
+                            const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase, int64_t PW, int64_t T,
+                            int32_t lc, int64_t chunk_ticks, const uint32_t *first, const uint32_t *off,
+                            const uint8_t *vstart, const KeyFmt &kf, uint64_t *key_out, float *slew_out,
+                            uint32_t *orig_out, hipStream_t s);
+hipError_t launch_chunk_base_w(int32_t Q, int64_t PW, const uint32_t *off, uint32_t *cb, hipStream_t s);
 hipError_t scan_exclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
                               hipStream_t s);
 hipError_t scan_exclusive_i64(const int64_t *in, int64_t *out, int64_t n, void *tmp, size_t *tmp_bytes,

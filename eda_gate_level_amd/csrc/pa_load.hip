@@ -8,12 +8,13 @@
 //
 // The event load validates the per-pin streams (sorted, alternating values,
 // inside the window, positive slews) and lays them out chunk-major: time is
-// cut into chunks of Cc clock cycles, and inside a chunk the events are
-// ordered by gate, pin and time.  Every (chunk, gate) segment is then one
-// contiguous run of packed keys that also carry the gate's input state at the
-// chunk start (the state reconstruction at a window start of Sec. 2.4.2,
-// computed once from per-pin event-count parities).  Chunks start on cycle
-// boundaries, so the per-pin glitch counter never crosses a chunk.
+// cut into chunks of Cc clock cycles, every gate's chunk into density-aware
+// windows, and inside a (chunk, gate, window) segment the events are ordered
+// by pin and time.  Every segment is one contiguous run of packed keys that
+// also carry the gate's input state at the window start (the state
+// reconstruction at a window start of Sec. 2.4.2, from per-pin event-count
+// parities).  Windows start on cycle boundaries, so the per-pin glitch
+// counter never crosses one.
 #include <hip/hip_runtime.h>
 
 #include <hipcub/hipcub.hpp>
@@ -101,82 +102,141 @@ __global__ void k_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
   }
 }
 
-__global__ void k_count(int64_t E, int64_t P, const int64_t *evt_t, const uint32_t *ev_pin, int64_t chunk_ticks,
-                        uint32_t *cnt) {
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t q = evt_t[e] / chunk_ticks;
-    atomicAdd(&cnt[q * P + ev_pin[e]], 1u);
+// ---- density-aware windows (paper Sec. 3, event-density-aware per-gate
+// cycle partitioning): a gate of density rho = N_evt / N_cyc gets windows of
+// about n_evt_tgt / rho cycles; here the window length is Cc / 2^s, the
+// smallest s with rho * Cc / 2^s <= target (the density floor is the chunk
+// itself), refined below until no window holds more than kSegMax events.
+__global__ void k_gate_levels(int64_t G, const int64_t *pin_base, const int64_t *pin_ptr, int64_t C, int32_t Cc,
+                              int32_t lc, double target, uint8_t *level) {
+  for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
+    const double n_evt = (double)(pin_ptr[pin_base[g + 1]] - pin_ptr[pin_base[g]]);
+    const double rho = n_evt / (double)C;
+    int sl = 0;
+    while (sl < lc && rho * (double)(Cc >> sl) > target) ++sl;
+    level[g] = (uint8_t)sl;
   }
 }
 
-// largest (chunk, gate) segment
-__global__ void k_segmax(int64_t G, int64_t P, int32_t Q, const int64_t *pin_base, const uint32_t *cnt,
-                         uint32_t *mx) {
+// (k + 1) << level: (window, pin) pairs of a gate in one chunk
+__global__ void k_pw_len(int64_t G, const int32_t *gate_k, const uint8_t *level, int64_t *pw_len) {
+  for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x)
+    pw_len[g] = (int64_t)(gate_k[g] + 1) << level[g];
+}
+
+struct WinIdx {
+  int64_t pair;  // (chunk, gate, window, pin) pair of the event
+  int64_t base;  // pair of (chunk, gate, window, pin 0)
+  int64_t q;
+};
+
+__device__ __forceinline__ WinIdx win_index(int64_t t, int64_t T, int32_t lc, int32_t sl, int64_t PW, int64_t pwb,
+                                            int32_t k, int32_t i) {
+  const int64_t cyc = t / T;
+  const int64_t q = cyc >> lc;
+  const int64_t cin = cyc & (((int64_t)1 << lc) - 1);
+  const int64_t w = cin >> (lc - sl);
+  WinIdx r;
+  r.q = q;
+  r.base = q * PW + pwb + w * (k + 1);
+  r.pair = r.base + i;
+  return r;
+}
+
+__global__ void k_count_w(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
+                          const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
+                          const int64_t *pwbase, int64_t PW, int64_t T, int32_t lc, uint32_t *cnt) {
+  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t p = ev_pin[e];
+    const int32_t g = pin_gate[p];
+    const WinIdx wi = win_index(evt_t[e], T, lc, level[g], PW, pwbase[g], gate_k[g], pin_local[p]);
+    atomicAdd(&cnt[wi.pair], 1u);
+  }
+}
+
+// flags bit 0: some window exceeds kSegMax and its gate can be refined;
+// bit 1: a one-cycle window exceeds kSegMax (cannot be refined)
+__global__ void k_winmax(int64_t G, int32_t Q, const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase,
+                         int64_t PW, int32_t lc, const uint32_t *cnt, uint8_t *level_next, uint32_t *flags,
+                         uint32_t *max_seg) {
   const int64_t n = G * (int64_t)Q;
   for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < n; u += (int64_t)gridDim.x * blockDim.x) {
     const int64_t q = u / G, g = u - q * G;
-    uint32_t s = 0;
-    for (int64_t p = pin_base[g]; p < pin_base[g + 1]; ++p) s += cnt[q * P + p];
-    atomicMax(mx, s);
-  }
-}
-
-// per pin, walking the chunks in order: the caller's index of its first event
-// in each chunk and its value at each chunk start
-__global__ void k_pin_chunks(int64_t P, int32_t Q, const int64_t *pin_ptr, const uint8_t *pin_init,
-                             const uint32_t *cnt, uint32_t *first, uint8_t *pinval) {
-  for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x) {
-    uint32_t run = (uint32_t)pin_ptr[p];
-    uint8_t v = pin_init[p] & 1u;
-    for (int32_t q = 0; q < Q; ++q) {
-      const uint32_t c = cnt[(int64_t)q * P + p];
-      first[(int64_t)q * P + p] = run;
-      pinval[(int64_t)q * P + p] = v;
-      run += c;
-      v ^= (uint8_t)(c & 1u);
+    const int32_t np = gate_k[g] + 1, sl = level[g];
+    const int64_t b0 = q * PW + pwbase[g];
+    uint32_t mx = 0;
+    for (int64_t w = 0; w < ((int64_t)1 << sl); ++w) {
+      uint32_t sum = 0;
+      for (int32_t i = 0; i < np; ++i) sum += cnt[b0 + w * np + i];
+      mx = sum > mx ? sum : mx;
+    }
+    atomicMax(max_seg, mx);
+    if (mx > (uint32_t)kSegMax) {
+      if (sl < lc) {
+        atomicOr(flags, 1u);
+        level_next[g] = (uint8_t)(sl + 1);  // every writer stores the same value
+      } else {
+        atomicOr(flags, 2u);
+      }
     }
   }
 }
 
-// input-pin state of every gate at every chunk start
-__global__ void k_seg_state(int64_t G, int64_t P, int32_t Q, const int64_t *pin_base, const int32_t *gate_k,
-                            const uint8_t *pinval, uint8_t *st) {
-  const int64_t n = G * (int64_t)Q;
-  for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < n; u += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t q = u / G, g = u - q * G;
-    const int64_t p0 = pin_base[g];
-    uint32_t S = 0;
-    for (int j = 0; j < gate_k[g]; ++j) S |= uint32_t(pinval[q * P + p0 + j]) << j;
-    st[u] = (uint8_t)S;
+// per pin, walking its (chunk, window) pairs in time order: the caller's index
+// of its first event in each window and its value at each window start
+__global__ void k_pin_windows(int64_t P, int32_t Q, const int64_t *pin_ptr, const uint8_t *pin_init,
+                              const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
+                              const uint8_t *level, const int64_t *pwbase, int64_t PW, const uint32_t *cnt,
+                              uint32_t *first, uint8_t *vstart) {
+  for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x) {
+    const int32_t g = pin_gate[p];
+    const int32_t np = gate_k[g] + 1, i = pin_local[p];
+    const int64_t nw = (int64_t)1 << level[g];
+    uint32_t run = (uint32_t)pin_ptr[p];
+    uint8_t v = pin_init[p] & 1u;
+    for (int32_t q = 0; q < Q; ++q) {
+      const int64_t b0 = (int64_t)q * PW + pwbase[g] + i;
+      for (int64_t w = 0; w < nw; ++w) {
+        const int64_t pr = b0 + w * np;
+        const uint32_t c = cnt[pr];
+        first[pr] = run;
+        vstart[pr] = v;
+        run += c;
+        v ^= (uint8_t)(c & 1u);
+      }
+    }
   }
 }
 
-__global__ void k_scatter(int64_t E, int64_t P, int64_t G, const int64_t *evt_t, const float *evt_slew,
-                          const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
-                          const uint8_t *pin_local, int64_t chunk_ticks, const uint32_t *first,
-                          const uint32_t *pin_off, const uint8_t *st, KeyFmt kf, uint64_t *key_out,
-                          float *slew_out, uint32_t *orig_out) {
+__global__ void k_scatter_w(int64_t E, const int64_t *evt_t, const float *evt_slew, const uint8_t *evt_val,
+                            const uint32_t *ev_pin, const int32_t *pin_gate, const uint8_t *pin_local,
+                            const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase, int64_t PW, int64_t T,
+                            int32_t lc, int64_t chunk_ticks, const uint32_t *first, const uint32_t *off,
+                            const uint8_t *vstart, KeyFmt kf, uint64_t *key_out, float *slew_out, uint32_t *orig_out) {
+  const uint32_t outc = out_code(kf.p_bits);
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t p = ev_pin[e];
-    const int64_t g = pin_gate[p];
-    const uint64_t i = pin_local[p];
+    const int32_t g = pin_gate[p];
+    const int32_t k = gate_k[g], i = pin_local[p];
     const int64_t t = evt_t[e];
-    const int64_t q = t / chunk_ticks;
-    const uint64_t trel = (uint64_t)(t - q * chunk_ticks);
-    const int64_t qp = q * P + p;
-    const int64_t dest = (int64_t)pin_off[qp] + (e - (int64_t)first[qp]);
-    const uint64_t lk = (i << kf.t_bits) | trel;
-    const uint64_t k = ((uint64_t)g << kKeyGateShift) | (lk << kKeyLkShift) |
-                       ((uint64_t)(evt_val[e] & 1u) << kKeyValShift) | (uint64_t)st[q * G + g];
-    key_out[dest] = k;
+    const WinIdx wi = win_index(t, T, lc, level[g], PW, pwbase[g], k, i);
+    const int64_t dest = (int64_t)off[wi.pair] + (e - (int64_t)first[wi.pair]);
+    uint32_t S0 = 0;
+    for (int32_t j = 0; j < k; ++j) S0 |= uint32_t(vstart[wi.base + j]) << j;
+    const uint64_t head = dest == (int64_t)off[wi.base] ? 1u : 0u;
+    const uint64_t code = i == k ? outc : (uint32_t)i;
+    const uint64_t trel = (uint64_t)(t - wi.q * chunk_ticks);
+    const uint64_t lk = (code << kf.t_bits) | trel;
+    key_out[dest] = ((uint64_t)g << kKeyGateShift) | (head << kKeyHeadShift) | (lk << kKeyLkShift) |
+                    ((uint64_t)(evt_val[e] & 1u) << kKeyValShift) | (uint64_t)S0;
     slew_out[dest] = evt_slew[e];
     orig_out[dest] = (uint32_t)e;
   }
 }
 
-__global__ void k_chunk_base(int32_t Q, int64_t P, int64_t E, const uint32_t *pin_off, uint32_t *cb) {
+__global__ void k_chunk_base_w(int32_t Q, int64_t PW, const uint32_t *off, uint32_t *cb) {
   for (int32_t q = blockIdx.x * blockDim.x + threadIdx.x; q <= Q; q += gridDim.x * blockDim.x)
-    cb[q] = q < Q ? pin_off[(int64_t)q * P] : (uint32_t)E;
+    cb[q] = off[(int64_t)q * PW];
 }
 
 }  // namespace
@@ -212,44 +272,56 @@ hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
   return hipGetLastError();
 }
 
-hipError_t launch_count(int64_t E, int64_t P, const int64_t *evt_t, const uint32_t *ev_pin, int64_t chunk_ticks,
-                        uint32_t *cnt, hipStream_t s) {
-  hipLaunchKernelGGL(k_count, dim3(grid_for(E)), dim3(kLT), 0, s, E, P, evt_t, ev_pin, chunk_ticks, cnt);
+hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int64_t *pin_ptr, int64_t C, int32_t Cc,
+                              int32_t lc, double target, uint8_t *level, hipStream_t s) {
+  hipLaunchKernelGGL(k_gate_levels, dim3(grid_for(G)), dim3(kLT), 0, s, G, pin_base, pin_ptr, C, Cc, lc, target, level);
   return hipGetLastError();
 }
 
-hipError_t launch_segmax(int64_t G, int64_t P, int32_t Q, const int64_t *pin_base, const uint32_t *cnt,
-                         uint32_t *mx, hipStream_t s) {
-  hipLaunchKernelGGL(k_segmax, dim3(grid_for(G * (int64_t)Q)), dim3(kLT), 0, s, G, P, Q, pin_base, cnt, mx);
+hipError_t launch_pw_len(int64_t G, const int32_t *gate_k, const uint8_t *level, int64_t *pw_len, hipStream_t s) {
+  hipLaunchKernelGGL(k_pw_len, dim3(grid_for(G)), dim3(kLT), 0, s, G, gate_k, level, pw_len);
   return hipGetLastError();
 }
 
-hipError_t launch_pin_chunks(int64_t P, int32_t Q, const int64_t *pin_ptr, const uint8_t *pin_init,
-                             const uint32_t *cnt, uint32_t *first, uint8_t *pinval, hipStream_t s) {
-  hipLaunchKernelGGL(k_pin_chunks, dim3(grid_for(P)), dim3(kLT), 0, s, P, Q, pin_ptr, pin_init, cnt, first, pinval);
+hipError_t launch_count_w(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
+                          const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
+                          const int64_t *pwbase, int64_t PW, int64_t T, int32_t lc, uint32_t *cnt, hipStream_t s) {
+  hipLaunchKernelGGL(k_count_w, dim3(grid_for(E)), dim3(kLT), 0, s, E, evt_t, ev_pin, pin_gate, pin_local, gate_k,
+                     level, pwbase, PW, T, lc, cnt);
   return hipGetLastError();
 }
 
-hipError_t launch_seg_state(int64_t G, int64_t P, int32_t Q, const int64_t *pin_base, const int32_t *gate_k,
-                            const uint8_t *pinval, uint8_t *st, hipStream_t s) {
-  hipLaunchKernelGGL(k_seg_state, dim3(grid_for(G * (int64_t)Q)), dim3(kLT), 0, s, G, P, Q, pin_base, gate_k,
-                     pinval, st);
+hipError_t launch_winmax(int64_t G, int32_t Q, const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase,
+                         int64_t PW, int32_t lc, const uint32_t *cnt, uint8_t *level_next, uint32_t *flags,
+                         uint32_t *max_seg, hipStream_t s) {
+  hipLaunchKernelGGL(k_winmax, dim3(grid_for(G * (int64_t)Q)), dim3(kLT), 0, s, G, Q, gate_k, level, pwbase, PW, lc,
+                     cnt, level_next, flags, max_seg);
   return hipGetLastError();
 }
 
-hipError_t launch_scatter(int64_t E, int64_t P, int64_t G, const int64_t *evt_t, const float *evt_slew,
-                          const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
-                          const uint8_t *pin_local, int64_t chunk_ticks, const uint32_t *first,
-                          const uint32_t *pin_off, const uint8_t *st, const KeyFmt &kf, uint64_t *key_out,
-                          float *slew_out, uint32_t *orig_out, hipStream_t s) {
-  hipLaunchKernelGGL(k_scatter, dim3(grid_for(E)), dim3(kLT), 0, s, E, P, G, evt_t, evt_slew, evt_val, ev_pin,
-                     pin_gate, pin_local, chunk_ticks, first, pin_off, st, kf, key_out, slew_out, orig_out);
+hipError_t launch_pin_windows(int64_t P, int32_t Q, const int64_t *pin_ptr, const uint8_t *pin_init,
+                              const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
+                              const uint8_t *level, const int64_t *pwbase, int64_t PW, const uint32_t *cnt,
+                              uint32_t *first, uint8_t *vstart, hipStream_t s) {
+  hipLaunchKernelGGL(k_pin_windows, dim3(grid_for(P)), dim3(kLT), 0, s, P, Q, pin_ptr, pin_init, pin_gate, pin_local,
+                     gate_k, level, pwbase, PW, cnt, first, vstart);
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_base(int32_t Q, int64_t P, int64_t E, const uint32_t *pin_off, uint32_t *cb,
-                             hipStream_t s) {
-  hipLaunchKernelGGL(k_chunk_base, dim3(grid_for(Q + 1)), dim3(kLT), 0, s, Q, P, E, pin_off, cb);
+hipError_t launch_scatter_w(int64_t E, const int64_t *evt_t, const float *evt_slew, const uint8_t *evt_val,
+                            const uint32_t *ev_pin, const int32_t *pin_gate, const uint8_t *pin_local,
+                            const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase, int64_t PW, int64_t T,
+                            int32_t lc, int64_t chunk_ticks, const uint32_t *first, const uint32_t *off,
+                            const uint8_t *vstart, const KeyFmt &kf, uint64_t *key_out, float *slew_out,
+                            uint32_t *orig_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_scatter_w, dim3(grid_for(E)), dim3(kLT), 0, s, E, evt_t, evt_slew, evt_val, ev_pin, pin_gate,
+                     pin_local, gate_k, level, pwbase, PW, T, lc, chunk_ticks, first, off, vstart, kf, key_out,
+                     slew_out, orig_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_base_w(int32_t Q, int64_t PW, const uint32_t *off, uint32_t *cb, hipStream_t s) {
+  hipLaunchKernelGGL(k_chunk_base_w, dim3(grid_for(Q + 1)), dim3(kLT), 0, s, Q, PW, off, cb);
   return hipGetLastError();
 }
 

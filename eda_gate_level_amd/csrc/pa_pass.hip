@@ -41,52 +41,35 @@ namespace pa {
 namespace {
 
 #ifndef PA_NT
-#define PA_NT 1024
-#endif
-#ifndef PA_R
-#define PA_R 2
+#define PA_NT 512
 #endif
 #ifndef PA_CCMAX
 #define PA_CCMAX 512
 #endif
-#ifndef PA_GATE_LDS
-#define PA_GATE_LDS 2048
-#endif
-constexpr int kNT = PA_NT;        // threads per block
-constexpr int kR = PA_R;          // events per thread per batch
-constexpr int kECAP = kNT * kR;
-constexpr int kCCMAX = PA_CCMAX;  // max cycles per chunk (LDS bins)
-constexpr int kNW = kNT / 64;
+constexpr int kNT = PA_NT;         // threads per block
+constexpr int kNW = kNT / 64;      // waves per block, each working on its own batches
+constexpr int kRW = kSegMax / 64;  // events per lane per wave batch
+constexpr int kWB = 64 * kRW;      // events per wave batch (= the longest segment)
+constexpr int kCCMAX = PA_CCMAX;   // max cycles per chunk (LDS bins)
 constexpr int kXCD = 8;
+constexpr int kMaxCellsLds = 256;
+constexpr int kCellBytesMax = 24 * 1024;
+constexpr uint32_t kInf = 0xFFFFFFFFu;
+static_assert(kWB == kSegMax, "a wave batch holds the longest segment");
 
 __device__ __forceinline__ uint32_t key_gate(uint64_t k) { return uint32_t(k >> kKeyGateShift); }
+__device__ __forceinline__ uint32_t key_head(uint64_t k) { return uint32_t(k >> kKeyHeadShift) & 1u; }
 __device__ __forceinline__ uint32_t key_lk(uint64_t k) { return uint32_t(k >> kKeyLkShift); }
-__device__ __forceinline__ uint32_t key_val(uint64_t k) { return uint32_t(k >> kKeyValShift) & 1u; }
 
-// first segment head at or after position x (a head starts a (chunk, gate)
-// segment); executed by one whole wave
-__device__ int find_head(const PassArgs &a, int64_t x) {
-  if (x >= a.E) return int(a.E);
-  if (x <= 0) return 0;
-  // chunk of x: last q with chunk_base[q] <= x
-  int lo = 0, hi = a.Q;  // answer in [0, Q-1]
-  while (hi - lo > 1) {
-    int mid = (lo + hi) >> 1;
-    if (int64_t(a.chunk_base[mid]) <= x) lo = mid; else hi = mid;
-  }
-  const int64_t cb0 = a.chunk_base[lo], cb1 = a.chunk_base[lo + 1];
-  if (x == cb0) return int(x);
+// first segment head at or after position x (E if none); one whole wave
+__device__ int find_head(const uint64_t *key, int64_t E, int64_t x) {
   const int lane = threadIdx.x & 63;
   for (;;) {
-    int64_t y = x + lane;
-    bool h;
-    if (y >= cb1 || y >= a.E) {
-      h = true;
-    } else {
-      h = key_gate(a.key[y]) != key_gate(a.key[y - 1]);
-    }
-    unsigned long long m = __ballot(h);
-    if (m) return int(x + __ffsll((long long)m) - 1);
+    if (x >= E) return (int)E;
+    const int64_t y = x + lane;
+    const bool h = (y >= E) || key_head(key[y]);
+    const unsigned long long m = __ballot(h);
+    if (m) return (int)(x + __ffsll((long long)m) - 1);
     x += 64;
   }
 }
@@ -96,71 +79,83 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// per-cell tables staged in LDS when the library is small enough
-constexpr int kMaxCellsLds = 256;
-constexpr int kCellDoubles = 2048;
-constexpr int kGateLds = PA_GATE_LDS;             // most distinct gate ids in one batch
-constexpr int kGPT = (kGateLds + kNT - 1) / kNT;
-constexpr int kSeqMax = 64;                       // longest segment merged by one thread
-constexpr int kSeqPins = 4;                       // most input pins merged by one thread
-constexpr uint32_t kInf = 0xFFFFFFFFu;
-static_assert(kR * kNW <= 64, "segment counts of one batch must fit one wave");
+// LDS ordering between the lanes of one wave (no block barrier)
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-// first position in [lo, hi) whose value is >= target (hi if none)
-__device__ __forceinline__ int lower_bound_u32(const uint32_t *s, int lo, int hi, uint32_t target) {
-  int n = hi - lo;
-  while (n > 0) {
-    const int half = n >> 1;
-    const int mid = lo + half;
-    const bool lt = s[mid] < target;
-    lo = lt ? mid + 1 : lo;
-    n = lt ? n - half - 1 : half;
-  }
-  return lo;
+// bytes of the cell tables staged in dynamic LDS
+__host__ __device__ inline int64_t cell_lds_bytes(int n_cells, int n_slew, int64_t n_leak) {
+  return 8 * ((int64_t)n_cells * (2 * n_slew - 1) + n_leak) + 8 * (int64_t)n_cells;
 }
 
 template <bool CELL_LDS, bool DIAG>
 __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
-  // batch staging, decoded from the packed keys
-  __shared__ uint32_t sgl[kECAP];        // gate id
-  __shared__ uint32_t slk[kECAP];        // (pin << t_bits) | t_rel
-  __shared__ uint16_t saux[kECAP];       // S0 | val << 8
-  __shared__ uint16_t scyc[kECAP];       // cycle inside the chunk
-  __shared__ float sslew[kECAP];
-  __shared__ uint32_t ssmo[kECAP];       // state before | switching-pin mask << 8 | owner << 16
-  __shared__ uint16_t sseg[kECAP];       // segment index of each event
-  __shared__ uint16_t ssegst[kECAP + 1]; // segment starts
-  // per-cycle bins of the current chunk
+  extern __shared__ double s_dyn[];  // cell tables: slew axes | inverse widths | leakage | meta | LUT bases
+  // per-wave batch staging
+  __shared__ uint32_t w_lk[kNW][kWB];   // (pin code << t_bits) | t_rel
+  __shared__ uint32_t w_g[kNW][kWB];    // gate id
+  __shared__ uint32_t w_smo[kNW][kWB];  // state before | switching-pin mask << 8 | owner << 16
+  __shared__ float w_slew[kNW][kWB];
+  __shared__ uint16_t w_aux[kNW][kWB];  // S0 | val << 8
+  __shared__ uint16_t w_cyc[kNW][kWB];  // cycle inside the chunk
+  __shared__ uint16_t w_segst[kNW][kWB + 2];
+  __shared__ uint8_t w_seg[kNW][kWB];
+  // per-cycle bins of the block's chunk
   __shared__ double bw[kCCMAX];               // energy: dynamic + partial-bin leakage
   __shared__ double bb[kCCMAX];               // leakage power change
   __shared__ unsigned long long bc[kCCMAX];   // events | glitches << 32
-  // gate data of the batch's gate-id span, cell library
-  __shared__ uint32_t s_ginfo[kGateLds];
-  __shared__ double s_gcf[kGateLds];
-  __shared__ double s_gesw[kGateLds];
-  __shared__ double s_cell[CELL_LDS ? kCellDoubles : 1];     // slew axes, inverse widths, leakage
-  __shared__ uint32_t s_meta[CELL_LDS ? kMaxCellsLds : 1];   // k | leak base << 4
-  __shared__ uint32_t s_lutb[CELL_LDS ? kMaxCellsLds : 1];
-  __shared__ int s_hcnt[kR * kNW];
-  __shared__ int s_hlast[kR * kNW];
-  __shared__ int s_flag;
-  __shared__ int s_range[2];
+  __shared__ int s_bounds[kNW + 1];
   __shared__ double s_red[kNW * 6];
   __shared__ double s_scan[kNW];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const uint32_t tbits = a.kf.t_bits;
   const uint32_t tmask = (1u << tbits) - 1u;
+  const uint32_t outc = out_code(a.kf.p_bits);
   const int nb = gridDim.x, b = blockIdx.x;
   const int xcd = b % kXCD;
   const int ns = a.n_slew, nc = a.n_cap;
-  const int sa_off = 0, iw_off = a.n_cells * ns, lk_off = iw_off + a.n_cells * (ns - 1);
+  const bool has_range = b < a.n_ranges;
 
-  // ---- this block's range of whole segments
-  if (wid < 2) {
-    int64_t nominal = (a.E * (int64_t)(b + wid)) / nb;
-    int h = find_head(a, nominal);
-    if (lane == 0) s_range[wid] = h;
+  // cell tables in dynamic LDS
+  double *c_sa = s_dyn;
+  double *c_iw = c_sa + a.n_cells * ns;
+  double *c_lk = c_iw + a.n_cells * (ns - 1);
+  uint32_t *c_meta = reinterpret_cast<uint32_t *>(c_lk + a.n_leak);  // k | leak base << 4
+  uint32_t *c_lutb = c_meta + a.n_cells;
+  auto cell_k = [&](uint32_t c) -> uint32_t {
+    if constexpr (CELL_LDS) return c_meta[c] & 15u; else return (uint32_t)a.cell_k[c];
+  };
+  auto leak_base = [&](uint32_t c) -> uint32_t {
+    if constexpr (CELL_LDS) return c_meta[c] >> 4; else return a.cell_leak_base[c];
+  };
+  auto lut_base = [&](uint32_t c) -> uint32_t {
+    if constexpr (CELL_LDS) return c_lutb[c]; else return a.cell_lut_base[c];
+  };
+  auto slew_ax = [&](uint32_t c, int j) -> double {
+    if constexpr (CELL_LDS) return c_sa[c * ns + j]; else return a.slew_axis[(size_t)c * ns + j];
+  };
+  auto slew_iw = [&](uint32_t c, int j) -> double {
+    if constexpr (CELL_LDS) return c_iw[c * (ns - 1) + j]; else return a.slew_invw[(size_t)c * (ns - 1) + j];
+  };
+  auto leak_of = [&](uint32_t j) -> double {
+    if constexpr (CELL_LDS) return c_lk[j]; else return a.leak[j];
+  };
+
+  // ---- the block's range (inside one chunk) and its waves' sub-ranges, all cut at segment heads
+  int q = 0;
+  if (has_range) {
+    q = (int)a.rchunk[b];
+    const int64_t r0 = a.rstart[b], r1 = a.rstart[b + 1];
+    for (int w = wid; w <= kNW; w += kNW) {
+      const int h = find_head(a.key, a.E, r0 + (r1 - r0) * w / kNW);
+      if (lane == 0) s_bounds[w] = h;
+    }
+  } else if (tid == 0) {
+    s_bounds[0] = 0;
   }
   for (int c = tid; c < kCCMAX; c += kNT) {
     bw[c] = 0.0;
@@ -169,34 +164,14 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
   }
   if constexpr (CELL_LDS) {
     for (int c = tid; c < a.n_cells; c += kNT) {
-      s_meta[c] = (uint32_t)a.cell_k[c] | (a.cell_leak_base[c] << 4);
-      s_lutb[c] = a.cell_lut_base[c];
+      c_meta[c] = (uint32_t)a.cell_k[c] | (a.cell_leak_base[c] << 4);
+      c_lutb[c] = a.cell_lut_base[c];
     }
-    for (int j = tid; j < a.n_cells * ns; j += kNT) s_cell[sa_off + j] = a.slew_axis[j];
-    for (int j = tid; j < a.n_cells * (ns - 1); j += kNT) s_cell[iw_off + j] = a.slew_invw[j];
-    for (int j = tid; j < a.n_leak; j += kNT) s_cell[lk_off + j] = a.leak[j];
+    for (int j = tid; j < a.n_cells * ns; j += kNT) c_sa[j] = a.slew_axis[j];
+    for (int j = tid; j < a.n_cells * (ns - 1); j += kNT) c_iw[j] = a.slew_invw[j];
+    for (int j = tid; j < a.n_leak; j += kNT) c_lk[j] = a.leak[j];
   }
   __syncthreads();
-  const int s0 = s_range[0], s1 = s_range[1];
-
-  auto cell_k = [&](uint32_t c) -> uint32_t {
-    if constexpr (CELL_LDS) return s_meta[c] & 15u; else return (uint32_t)a.cell_k[c];
-  };
-  auto leak_base = [&](uint32_t c) -> uint32_t {
-    if constexpr (CELL_LDS) return s_meta[c] >> 4; else return a.cell_leak_base[c];
-  };
-  auto lut_base = [&](uint32_t c) -> uint32_t {
-    if constexpr (CELL_LDS) return s_lutb[c]; else return a.cell_lut_base[c];
-  };
-  auto slew_ax = [&](uint32_t c, int j) -> double {
-    if constexpr (CELL_LDS) return s_cell[sa_off + c * ns + j]; else return a.slew_axis[(size_t)c * ns + j];
-  };
-  auto slew_iw = [&](uint32_t c, int j) -> double {
-    if constexpr (CELL_LDS) return s_cell[iw_off + c * (ns - 1) + j]; else return a.slew_invw[(size_t)c * (ns - 1) + j];
-  };
-  auto leak_of = [&](uint32_t j) -> double {
-    if constexpr (CELL_LDS) return s_cell[lk_off + j]; else return a.leak[j];
-  };
 
   double e_int = 0.0, e_sw = 0.0, e_gl = 0.0, e_lk = 0.0, l0 = 0.0;
   unsigned n_gl = 0;
@@ -211,287 +186,221 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
     l0 += leak_of(leak_base(cell) + S);
   }
 
-  // ---- walk the chunks this block's range touches
-  int q = 0;
-  if (s0 < s1) {
-    int lo = 0, hi = a.Q;
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if ((int)a.chunk_base[mid] <= s0) lo = mid; else hi = mid;
-    }
-    q = lo;
-  }
-  int pos = s0;
-  uint64_t pk[kR];
-  float ps[kR];
-  int pf_pos = -1, pf_n = 0;
+  const int64_t cstart = (int64_t)q * a.chunk_ticks;
+  const int64_t clen = min(a.chunk_ticks, a.t_max - cstart);
+  const uint32_t clen32 = (uint32_t)clen;
+  const int ncyc = (int)((clen + a.T - 1) / a.T);
+  const int64_t tail_from_chunk = a.t_max - cstart;  // t_max - t = tail_from_chunk - t_rel
 
-  while (pos < s1) {
-    const int qend = min(s1, (int)a.chunk_base[q + 1]);
-    if (pos >= qend) { ++q; continue; }
-    const int64_t cstart = (int64_t)q * a.chunk_ticks;
-    const int64_t clen = min(a.chunk_ticks, a.t_max - cstart);
-    const uint32_t clen32 = (uint32_t)clen;
-    const int ncyc = (int)((clen + a.T - 1) / a.T);
-    const int64_t tail_from_chunk = a.t_max - cstart;  // t_max - t = tail_from_chunk - t_rel
-
-    while (pos < qend) {
-      const int n = min(kECAP, qend - pos);
-      // ---- stage and decode the batch (from the prefetch registers when they hold it)
-      if (!(pf_pos == pos && pf_n >= n)) {
+  if (has_range) {
+    uint32_t *lk_w = w_lk[wid];
+    uint32_t *g_w = w_g[wid];
+    uint32_t *smo_w = w_smo[wid];
+    float *sl_w = w_slew[wid];
+    uint16_t *aux_w = w_aux[wid];
+    uint16_t *cyc_w = w_cyc[wid];
+    uint16_t *segst_w = w_segst[wid];
+    uint8_t *seg_w = w_seg[wid];
+    const int wb = s_bounds[wid + 1];
+    int pos = s_bounds[wid];
+    uint64_t pk[kRW];
+    float ps[kRW];
+    {
+      const int n0 = min(kWB, wb - pos);
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
-          const int x = r * kNT + tid;
-          if (x < n) { pk[r] = a.key[pos + x]; ps[r] = a.slew[pos + x]; }
+      for (int r = 0; r < kRW; ++r) {
+        const int x = r * 64 + lane;
+        if (x < n0) {
+          pk[r] = __builtin_nontemporal_load(a.key + pos + x);
+          ps[r] = __builtin_nontemporal_load(a.slew + pos + x);
         }
       }
+    }
+    while (pos < wb) {
+      const int n = min(kWB, wb - pos);
+      // ---- segments of the batch: head bits, the last (maybe incomplete) one deferred
+      unsigned long long hm[kRW];
+      int last = -1;
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const int x = r * kNT + tid;
-        if (x < n) {
+      for (int r = 0; r < kRW; ++r) {
+        const int x = r * 64 + lane;
+        hm[r] = __ballot(x < n && key_head(pk[r]));
+        if (hm[r]) last = r * 64 + 63 - __clzll((long long)hm[r]);
+      }
+      const int nproc = (pos + n < wb && last > 0) ? last : n;
+      int nseg = 0;
+      int sidx[kRW];
+#pragma unroll
+      for (int r = 0; r < kRW; ++r) {
+        const int lim = nproc - r * 64;  // lanes below lim are in [0, nproc)
+        const unsigned long long valid = lim >= 64 ? ~0ull : (lim <= 0 ? 0ull : ((1ull << lim) - 1ull));
+        const unsigned long long upto = (lane == 63) ? hm[r] : (hm[r] & ((2ull << lane) - 1ull));
+        sidx[r] = nseg + __popcll(upto) - 1;
+        nseg += __popcll(hm[r] & valid);
+      }
+      // ---- decode into the wave's LDS region; issue the gate-data loads
+      uint32_t gi[kRW];
+      double gcf[kRW], gesw[kRW];
+#pragma unroll
+      for (int r = 0; r < kRW; ++r) {
+        const int x = r * 64 + lane;
+        gi[r] = 0;
+        if (x < nproc) {
           const uint64_t k = pk[r];
           const uint32_t lk = key_lk(k);
-          sgl[x] = key_gate(k);
-          slk[x] = lk;
-          saux[x] = (uint16_t)(uint32_t(k) & 0x1FFu);  // S0 | val << 8
-          scyc[x] = (uint16_t)divu32(lk & tmask, a.divT);
-          sslew[x] = ps[r];
+          const uint32_t g = key_gate(k);
+          lk_w[x] = lk;
+          g_w[x] = g;
+          aux_w[x] = (uint16_t)(uint32_t(k) & 0x1FFu);  // S0 | val << 8
+          cyc_w[x] = (uint16_t)divu32(lk & tmask, a.divT);
+          sl_w[x] = ps[r];
+          seg_w[x] = (uint8_t)sidx[r];
+          if ((hm[r] >> lane) & 1ull) segst_w[sidx[r]] = (uint16_t)x;
+          gi[r] = a.gate_info[g];
+          gcf[r] = a.gate_capfrac[g];
+          gesw[r] = a.gate_esw[g];
         }
       }
-      if (tid == 0) s_flag = 0;
-      __syncthreads();
-
-      // ---- cut the batch so that its gate ids span at most kGateLds, then load their data
-      const uint32_t g_lo = sgl[0];
-      int n_eff = n;
-      if (sgl[n - 1] - g_lo >= (uint32_t)kGateLds) n_eff = lower_bound_u32(sgl, 0, n, g_lo + kGateLds);
-      const uint32_t g_span = sgl[n_eff - 1] - g_lo + 1;
-      uint32_t pgi[kGPT];
-      double pgc[kGPT], pge[kGPT];
-#pragma unroll
-      for (int u = 0; u < kGPT; ++u) {
-        const uint32_t j = u * kNT + tid;
-        if (j < g_span) {
-          pgi[u] = a.gate_info[g_lo + j];
-          pgc[u] = a.gate_capfrac[g_lo + j];
-          pge[u] = a.gate_esw[g_lo + j];
-        }
-      }
-
-      // ---- number the (chunk, gate) segments of the batch
-#pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const int x = r * kNT + tid;
-        const bool h = (x < n_eff) && (x == 0 || sgl[x] != sgl[x - 1]);
-        const unsigned long long hm = __ballot(h);
-        if (lane == 0) {
-          s_hcnt[r * kNW + wid] = __popcll(hm);
-          s_hlast[r * kNW + wid] = hm ? (r * kNT + wid * 64 + 63 - __clzll((long long)hm)) : -1;
-        }
-      }
-      __syncthreads();
-      // prefix of the per-(round, wave) head counts, one lane per entry
-      const int hc = lane < kR * kNW ? s_hcnt[lane] : 0;
-      int hincl = hc;
-      for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(hincl, o, 64);
-        if (lane >= o) hincl += v;
-      }
-      int hl = lane < kR * kNW ? s_hlast[lane] : -1;
-      for (int o = 32; o > 0; o >>= 1) hl = max(hl, __shfl_xor(hl, o, 64));
-      const int nseg_all = __shfl(hincl, 63, 64);
-      const int last_head = hl;
-      const bool defer = (n_eff == n) && (pos + n < qend) && last_head > 0;
-      const int nproc = defer ? last_head : n_eff;
-      const int nseg = defer ? nseg_all - 1 : nseg_all;
-#pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const int x = r * kNT + tid;
-        const int ent = r * kNW + wid;
-        const int sbase = __shfl(hincl, ent, 64) - __shfl(hc, ent, 64);
-        const bool h = (x < n_eff) && (x == 0 || sgl[x] != sgl[x - 1]);
-        const unsigned long long hm = __ballot(h);
-        if (x < nproc) {
-          const unsigned long long upto = (lane == 63) ? hm : (hm & ((2ull << lane) - 1ull));
-          const int sidx = sbase + __popcll(upto) - 1;
-          sseg[x] = (uint16_t)sidx;
-          if (h) ssegst[sidx] = (uint16_t)x;
-        }
-      }
-      if (tid == 0) ssegst[nseg] = (uint16_t)nproc;
-
-      // ---- prefetch the next batch while this one is computed
+      if (lane == 0) segst_w[nseg] = (uint16_t)nproc;
+      // ---- prefetch the next batch
+      const int npos = pos + nproc;
       {
-        const int npos = pos + nproc;
-        int nend = qend;
-        if (npos >= qend) nend = min(s1, (int)a.chunk_base[min(q + 2, a.Q)]);
-        const int nn = min(kECAP, nend - npos);
-        pf_pos = npos;
-        pf_n = nn > 0 ? nn : 0;
+        const int nn = min(kWB, wb - npos);
 #pragma unroll
-        for (int r = 0; r < kR; ++r) {
-          const int x = r * kNT + tid;
-          if (x < pf_n) { pk[r] = a.key[npos + x]; ps[r] = a.slew[npos + x]; }
+        for (int r = 0; r < kRW; ++r) {
+          const int x = r * 64 + lane;
+          if (x < nn) {
+            pk[r] = __builtin_nontemporal_load(a.key + npos + x);
+            ps[r] = __builtin_nontemporal_load(a.slew + npos + x);
+          }
         }
       }
-#pragma unroll
-      for (int u = 0; u < kGPT; ++u) {
-        const uint32_t j = u * kNT + tid;
-        if (j < g_span) {
-          s_ginfo[j] = pgi[u];
-          s_gcf[j] = pgc[u];
-          s_gesw[j] = pge[u];
-        }
-      }
-      __syncthreads();
+      wave_sync();
 
       // ---- k-way merge of each segment's input-pin streams in time order
-      //      (Sec. 2.4.2, Fig. 3): one thread per (chunk, gate) segment walks the
-      //      distinct timestamps; every input event gets the state before it, the
-      //      set of input pins switching at its timestamp, and whether it is the
-      //      lowest of them (that one charges the leakage change).
-      for (int sg = tid; sg < nseg; sg += kNT) {
-        const int st = ssegst[sg], en = ssegst[sg + 1];
-        const uint32_t kk = cell_k(s_ginfo[sgl[st] - g_lo] & 0xFFFFFFu);
-        if (kk > (uint32_t)kSeqPins || en - st > kSeqMax) {
-          s_flag = 1;
-          continue;
-        }
-        int n0 = 0, n1 = 0, n2 = 0, n3 = 0;
+      //      (Sec. 2.4.2, Fig. 3): one lane per segment walks the distinct
+      //      timestamps; every input event gets the state before it, the set of
+      //      input pins switching at its timestamp, and whether it is the lowest
+      //      of them (that one charges the leakage change).
+      for (int sg = lane; sg < nseg; sg += 64) {
+        const int st = segst_w[sg], en = segst_w[sg + 1];
+        int n0 = 0, n1 = 0, n2 = 0, n3 = 0, nhi = 0;
         for (int m = st; m < en; ++m) {
-          const uint32_t p = slk[m] >> tbits;
+          const uint32_t p = lk_w[m] >> tbits;
+          // the output pin's code is not an input pin (it may equal 1 or 3)
           n0 += p == 0u;
-          n1 += p == 1u;
+          n1 += (p == 1u && p != outc);
           n2 += p == 2u;
-          n3 += p == 3u;
+          n3 += (p == 3u && p != outc);
+          nhi += (p >= 4u && p != outc);
         }
-        // pins at or above kk are the output pin: no state, not merged
-        if (kk < 4u) n3 = 0;
-        if (kk < 3u) n2 = 0;
-        if (kk < 2u) n1 = 0;
-        int c0 = st, c1 = st + n0, c2 = c1 + n1, c3 = c2 + n2;
-        const int e0 = c1, e1 = c2, e2 = c3, e3 = c3 + n3;
-        uint32_t S = saux[st] & 0xFFu;
-        uint32_t h0 = c0 < e0 ? (slk[c0] & tmask) : kInf;
-        uint32_t h1 = c1 < e1 ? (slk[c1] & tmask) : kInf;
-        uint32_t h2 = c2 < e2 ? (slk[c2] & tmask) : kInf;
-        uint32_t h3 = c3 < e3 ? (slk[c3] & tmask) : kInf;
-        for (;;) {
-          const uint32_t t = min(min(h0, h1), min(h2, h3));
-          if (t == kInf) break;
-          const uint32_t mask = (h0 == t ? 1u : 0u) | (h1 == t ? 2u : 0u) | (h2 == t ? 4u : 0u) | (h3 == t ? 8u : 0u);
-          const uint32_t own = __ffs((int)mask) - 1;
-          const uint32_t w = S | (mask << 8);
-          if (h0 == t) { ssmo[c0] = w | ((own == 0u) << 16); ++c0; h0 = c0 < e0 ? (slk[c0] & tmask) : kInf; }
-          if (h1 == t) { ssmo[c1] = w | ((own == 1u) << 16); ++c1; h1 = c1 < e1 ? (slk[c1] & tmask) : kInf; }
-          if (h2 == t) { ssmo[c2] = w | ((own == 2u) << 16); ++c2; h2 = c2 < e2 ? (slk[c2] & tmask) : kInf; }
-          if (h3 == t) { ssmo[c3] = w | ((own == 3u) << 16); ++c3; h3 = c3 < e3 ? (slk[c3] & tmask) : kInf; }
-          S ^= mask;
-        }
-      }
-      __syncthreads();
-
-      // ---- long or wide segments: each other input pin's value just before t by
-      //      binary search inside the segment (run only when a batch has one)
-      if (s_flag) {
-#pragma unroll
-        for (int r = 0; r < kR; ++r) {
-          const int x = r * kNT + tid;
-          if (x >= nproc) continue;
-          const uint32_t lk = slk[x];
-          const uint32_t i = lk >> tbits;
-          const uint32_t kk = cell_k(s_ginfo[sgl[x] - g_lo] & 0xFFFFFFu);
-          const int sg = sseg[x];
-          const int st = ssegst[sg], en = ssegst[sg + 1];
-          if (i >= kk || (kk <= (uint32_t)kSeqPins && en - st <= kSeqMax)) continue;
-          const uint32_t trel = lk & tmask;
-          const uint32_t au = saux[x];
-          uint32_t Sm = ((au & 0xFFu) & ~(1u << i)) | ((((au >> 8) & 1u) ^ 1u) << i);
-          uint32_t mask = 1u << i;
-          uint32_t owner = 1u;
-          for (uint32_t j = 0; j < kk; ++j) {
-            if (j == i) continue;
-            const uint32_t target = (j << tbits) | trel;
-            const int lo = j < i ? st : x + 1;
-            const int hi = j < i ? x : en;
-            const int p = lower_bound_u32(slk, lo, hi, target);
-            if (p > st && (slk[p - 1] >> tbits) == j) Sm = (Sm & ~(1u << j)) | (((saux[p - 1] >> 8) & 1u) << j);
-            if (p < en && slk[p] == target) {
-              mask |= 1u << j;
-              if (j < i) owner = 0u;
-            }
+        const uint32_t S0 = aux_w[st] & 0xFFu;
+        if (nhi == 0) {
+          int c0 = st, c1 = st + n0, c2 = c1 + n1, c3 = c2 + n2;
+          const int e0 = c1, e1 = c2, e2 = c3, e3 = c3 + n3;
+          uint32_t S = S0;
+          uint32_t h0 = c0 < e0 ? (lk_w[c0] & tmask) : kInf;
+          uint32_t h1 = c1 < e1 ? (lk_w[c1] & tmask) : kInf;
+          uint32_t h2 = c2 < e2 ? (lk_w[c2] & tmask) : kInf;
+          uint32_t h3 = c3 < e3 ? (lk_w[c3] & tmask) : kInf;
+          for (;;) {
+            const uint32_t t = min(min(h0, h1), min(h2, h3));
+            if (t == kInf) break;
+            const uint32_t mask = (h0 == t ? 1u : 0u) | (h1 == t ? 2u : 0u) | (h2 == t ? 4u : 0u) | (h3 == t ? 8u : 0u);
+            const uint32_t own = __ffs((int)mask) - 1;
+            const uint32_t wv = S | (mask << 8);
+            if (h0 == t) { smo_w[c0] = wv | ((own == 0u) << 16); ++c0; h0 = c0 < e0 ? (lk_w[c0] & tmask) : kInf; }
+            if (h1 == t) { smo_w[c1] = wv | ((own == 1u) << 16); ++c1; h1 = c1 < e1 ? (lk_w[c1] & tmask) : kInf; }
+            if (h2 == t) { smo_w[c2] = wv | ((own == 2u) << 16); ++c2; h2 = c2 < e2 ? (lk_w[c2] & tmask) : kInf; }
+            if (h3 == t) { smo_w[c3] = wv | ((own == 3u) << 16); ++c3; h3 = c3 < e3 ? (lk_w[c3] & tmask) : kInf; }
+            S ^= mask;
           }
-          ssmo[x] = Sm | (mask << 8) | (owner << 16);
+        } else {
+          // gates with more than four inputs: every input event scans its segment
+          for (int x = st; x < en; ++x) {
+            const uint32_t lx = lk_w[x];
+            const uint32_t ix = lx >> tbits;
+            if (ix == outc) continue;
+            const uint32_t tx = lx & tmask;
+            uint32_t Sm = (S0 & ~(1u << ix)) | ((((aux_w[x] >> 8) & 1u) ^ 1u) << ix);
+            uint32_t mask = 1u << ix, owner = 1u;
+            for (int m = st; m < en; ++m) {
+              const uint32_t lm = lk_w[m];
+              const uint32_t im = lm >> tbits;
+              if (im == outc || im == ix) continue;
+              const uint32_t tm = lm & tmask;
+              if (tm < tx) Sm = (Sm & ~(1u << im)) | (((aux_w[m] >> 8) & 1u) << im);
+              else if (tm == tx) {
+                mask |= 1u << im;
+                if (im < ix) owner = 0u;
+              }
+            }
+            smo_w[x] = Sm | (mask << 8) | (owner << 16);
+          }
         }
-        __syncthreads();
       }
+      wave_sync();
 
       // ---- one event per lane: energies, glitches, leakage changes, bins
-      double L[kR][4];  // input event: 2x2 LUT corners; output event: L[r][0] = 0.5 c Vdd^2
-      double fa[kR], fb[kR];
-      uint32_t smo[kR];  // state before | mask << 8 | owner << 16 | input << 17
-      uint32_t gi_r[kR];
+      double L[kRW][4];  // input event: 2x2 LUT corners; output event: L[r][0] = 0.5 c Vdd^2
+      double fa[kRW];
+      uint32_t smo[kRW];  // state before | mask << 8 | owner << 16 | input << 17
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const int x = r * kNT + tid;
+      for (int r = 0; r < kRW; ++r) {
+        const int x = r * 64 + lane;
         smo[r] = 0;
-        gi_r[r] = 0;
         if (x >= nproc) continue;
-        const uint32_t i = slk[x] >> tbits;
-        const uint32_t gl = sgl[x] - g_lo;
-        const uint32_t ginfo = s_ginfo[gl];
-        gi_r[r] = ginfo;
-        const uint32_t cell = ginfo & 0xFFFFFFu;
-        const uint32_t kk = cell_k(cell);
-        if (i >= kk) {  // output pin: no LUT, no state
-          L[r][0] = s_gesw[gl];
+        const uint32_t code = lk_w[x] >> tbits;
+        if (code == outc) {  // output pin: no LUT, no state
+          L[r][0] = gesw[r];
           continue;
         }
-        fb[r] = s_gcf[gl];
-        const uint32_t so = ssmo[x];
+        const uint32_t cell = gi[r] & 0xFFFFFFu;
+        const uint32_t kk = cell_k(cell);
+        const uint32_t so = smo_w[x];
         smo[r] = so | (1u << 17);
-        const uint32_t Sm = so & 0xFFu;
+        const uint32_t Sm = so & ((1u << kk) - 1u);  // no-op for valid states; keeps the LUT row inside the cell
         // slew segment on the cell's axis (Sec. 2.4.1, Fig. 2)
-        const double sl = (double)sslew[x];
+        const double sl = (double)sl_w[x];
         int si = 0;
         for (int j = 1; j < ns - 1; ++j) si += (sl >= slew_ax(cell, j)) ? 1 : 0;
         fa[r] = (sl - slew_ax(cell, si)) * slew_iw(cell, si);
-        const double *Lp = a.lut + lut_base(cell) + ((Sm * kk + i) * (uint32_t)ns + si) * (uint32_t)nc + (ginfo >> 24);
+        const double *Lp = a.lut + lut_base(cell) + ((Sm * kk + code) * (uint32_t)ns + si) * (uint32_t)nc + (gi[r] >> 24);
         L[r][0] = Lp[0];
         L[r][1] = Lp[1];
         L[r][2] = Lp[nc];
         L[r][3] = Lp[nc + 1];
       }
 #pragma unroll
-      for (int r = 0; r < kR; ++r) {
-        const int x = r * kNT + tid;
+      for (int r = 0; r < kRW; ++r) {
+        const int x = r * 64 + lane;
         if (x >= nproc) continue;
-        const uint32_t lk = slk[x];
-        const uint32_t i = lk >> tbits;
+        const uint32_t lk = lk_w[x];
+        const uint32_t code = lk >> tbits;
         const uint32_t trel = lk & tmask;
-        const uint32_t cyc = scyc[x];
-        const uint32_t val = (saux[x] >> 8) & 1u;
-        const int sst = ssegst[sseg[x]];
+        const uint32_t cyc = cyc_w[x];
+        const uint32_t val = (aux_w[x] >> 8) & 1u;
+        const int sst = segst_w[seg_w[x]];
         // glitch: previous event of the same pin inside the same cycle (Fig. 7)
         bool glitch = false;
         double r_gl = 0.0;
-        if (x > sst && (slk[x - 1] >> tbits) == i && scyc[x - 1] == cyc) {
+        if (x > sst && (lk_w[x - 1] >> tbits) == code && cyc_w[x - 1] == cyc) {
           glitch = true;
-          const double pw = (double)(trel - (slk[x - 1] & tmask));
-          const double rr = pw / (0.5 * ((double)sslew[x] + (double)sslew[x - 1]));  // Eq. 2 (reading)
+          const double pw = (double)(trel - (lk_w[x - 1] & tmask));
+          const double rr = pw / (0.5 * ((double)sl_w[x] + (double)sl_w[x - 1]));  // Eq. 2 (reading)
           r_gl = rr > 1.0 ? 1.0 : rr;
         }
         const uint32_t so = smo[r];
         double E, extra = 0.0;
         if (so & (1u << 17)) {
           // bilinear internal energy
-          const double v0 = L[r][0] + fb[r] * (L[r][1] - L[r][0]);
-          const double v1 = L[r][2] + fb[r] * (L[r][3] - L[r][2]);
+          const double v0 = L[r][0] + gcf[r] * (L[r][1] - L[r][0]);
+          const double v1 = L[r][2] + gcf[r] * (L[r][3] - L[r][2]);
           E = v0 + fa[r] * (v1 - v0);
           if (so & (1u << 16)) {
             // leakage power change at this timestamp (owner = lowest switching input pin)
             const uint32_t Sm = so & 0xFFu, mask = (so >> 8) & 0xFFu;
-            const uint32_t lb = leak_base(gi_r[r] & 0xFFFFFFu);
+            const uint32_t lb = leak_base(gi[r] & 0xFFFFFFu);
             const double dp = leak_of(lb + (Sm ^ mask)) - leak_of(lb + Sm);
             if (dp != 0.0) {
               const uint32_t bend = min((cyc + 1u) * a.T, clen32);
@@ -521,60 +430,52 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
           if (a.evt_state) a.evt_state[o] = (uint8_t)(so & 0xFFu);
         }
       }
-      pos += nproc;
-      __syncthreads();
+      wave_sync();
+      pos = npos;
     }
+  }
+  __syncthreads();
 
-    // ---- flush this chunk's bins: in-chunk prefix of leakage changes, then atomics
-    {
-      constexpr int PER = kCCMAX / kNT > 0 ? kCCMAX / kNT : 1;
-      double loc[PER];
-      double s = 0.0;
+  // ---- flush the chunk's bins: in-chunk prefix of leakage changes, then atomics
+  if (has_range) {
+    constexpr int PER = kCCMAX / kNT > 0 ? kCCMAX / kNT : 1;
+    double loc[PER];
+    double s = 0.0;
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int c = tid * PER + u;
-        loc[u] = (c < ncyc) ? bb[c] : 0.0;
-        s += loc[u];
-      }
-      // exclusive scan of per-thread sums across the block
-      double incl = s;
-      for (int o = 1; o < 64; o <<= 1) {
-        const double v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-      }
-      if (lane == 63) s_scan[wid] = incl;
-      __syncthreads();
-      double wbase = 0.0, total = 0.0;
-      for (int w = 0; w < kNW; ++w) {
-        const double v = s_scan[w];
-        if (w < wid) wbase += v;
-        total += v;
-      }
-      double run = wbase + incl - s;
-      const int64_t cg0 = (int64_t)q * a.Cc;
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int c = tid * PER + u;
-        if (c < ncyc) {
-          const int64_t cg = cg0 + c;
-          const double len = (cg == a.C - 1) ? (double)(a.t_max - cg * (int64_t)a.T) : (double)a.T;
-          const double v = bw[c] + run * len * a.tick_s;
-          if (v != 0.0) atomicAdd(&a.acc_wave[(size_t)xcd * a.C + cg], v);
-          const unsigned long long cn = bc[c];
-          if (cn) atomicAdd(&a.acc_cnt[(size_t)xcd * a.C + cg], cn);
-          run += loc[u];
-        }
-      }
-      if (tid == 0 && total != 0.0) atomicAdd(&a.dP[q], total);
-      __syncthreads();
-      for (int c = tid; c < kCCMAX; c += kNT) {
-        bw[c] = 0.0;
-        bb[c] = 0.0;
-        bc[c] = 0ull;
-      }
-      __syncthreads();
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid * PER + u;
+      loc[u] = (c < ncyc) ? bb[c] : 0.0;
+      s += loc[u];
     }
-    ++q;
+    double incl = s;
+    for (int o = 1; o < 64; o <<= 1) {
+      const double v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_scan[wid] = incl;
+    __syncthreads();
+    double wbase = 0.0, total = 0.0;
+    for (int w = 0; w < kNW; ++w) {
+      const double v = s_scan[w];
+      if (w < wid) wbase += v;
+      total += v;
+    }
+    double run = wbase + incl - s;
+    const int64_t cg0 = (int64_t)q * a.Cc;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid * PER + u;
+      if (c < ncyc) {
+        const int64_t cg = cg0 + c;
+        const double len = (cg == a.C - 1) ? (double)(a.t_max - cg * (int64_t)a.T) : (double)a.T;
+        const double v = bw[c] + run * len * a.tick_s;
+        if (v != 0.0) atomicAdd(&a.acc_wave[(size_t)xcd * a.C + cg], v);
+        const unsigned long long cn = bc[c];
+        if (cn) atomicAdd(&a.acc_cnt[(size_t)xcd * a.C + cg], cn);
+        run += loc[u];
+      }
+    }
+    if (tid == 0 && total != 0.0) atomicAdd(&a.dP[q], total);
   }
 
   // ---- block totals
@@ -659,20 +560,22 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
 }  // namespace
 
 int pass_block_threads() { return kNT; }
-int pass_batch_events() { return kECAP; }
+int pass_batch_events() { return kWB; }
+int pass_wave_batch() { return kWB; }
 int pass_max_chunk_cycles() { return kCCMAX; }
 
 bool pass_cells_fit_lds(int n_cells, int n_slew, int64_t n_leak) {
-  return n_cells <= kMaxCellsLds && (int64_t)n_cells * (2 * n_slew - 1) + n_leak <= kCellDoubles;
+  return n_cells <= kMaxCellsLds && cell_lds_bytes(n_cells, n_slew, n_leak) <= kCellBytesMax;
 }
 
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
   const bool cells = pass_cells_fit_lds(a.n_cells, a.n_slew, a.n_leak);
   const bool diag = a.evt_glitch || a.evt_state;
+  const size_t dyn = cells ? (size_t)cell_lds_bytes(a.n_cells, a.n_slew, a.n_leak) : 0;
   if (cells && !diag)
-    hipLaunchKernelGGL((k_fused<true, false>), dim3(grid_blocks), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((k_fused<true, false>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
   else if (cells)
-    hipLaunchKernelGGL((k_fused<true, true>), dim3(grid_blocks), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((k_fused<true, true>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
   else if (!diag)
     hipLaunchKernelGGL((k_fused<false, false>), dim3(grid_blocks), dim3(kNT), 0, s, a);
   else

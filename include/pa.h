@@ -58,8 +58,10 @@ typedef struct pa_ctx pa_ctx;
 /* Speed knobs.  They never change results beyond fp64 summation order; a
  * zero field means "choose automatically". */
 typedef struct {
-  int32_t chunk_cycles;   /* cycles per time chunk of the event layout (max 1024) */
-  int32_t grid_blocks;    /* blocks of the fused pass (0 = one per compute unit) */
+  int32_t chunk_cycles;   /* cycles per time chunk of the event layout; rounded down to a
+                             power of two, at most 512 (0 = 256) */
+  int32_t grid_blocks;    /* target block count of the fused pass (0 = two per compute unit);
+                             the pass cuts the events into about this many ranges */
   int32_t time_kernels;   /* nonzero: record per-kernel device times of pa_run */
   int32_t reserved;
 } pa_tunables;
@@ -90,17 +92,27 @@ int pa_load_design(pa_ctx *ctx, int64_t n_gates, const int32_t *gate_cell, const
 
 /* Load the activity (paper Sec. 2.4.1-2.4.2: per-pin sorted event streams).
  *   n_pins  must equal sum_g (k_g + 1); pins are gate-major, inputs 0..k-1,
- *           output k
- *   n_events must equal pin_ptr[n_pins]; 0 <= n_events < 2^32
+ *           output k; the design may hold at most 2^22 - 1 gates here
+ *   n_events must equal pin_ptr[n_pins]; 0 <= n_events < 2^31
  *   pin_ptr[P+1]  int64 CSR offsets, pin_ptr[0] = 0, nondecreasing
  *   pin_init[P]   uint8 value of the pin at t = 0, in {0, 1}
  *   evt_t[E]      int64 ticks, strictly increasing per pin, 0 <= t < t_max
  *   evt_val[E]    uint8 new value, alternating per pin starting from !init
  *   evt_slew[E]   float32 ticks, finite and > 0 (same unit as slew_axis)
- *   t_clk  clock period in ticks, 1 <= t_clk < 2^32; t_max > 0 analysis end;
- *   tick_s seconds per tick (> 0).
- * The events are validated and re-laid out (chunk-major, see the design
- * notes) into library-owned memory. */
+ *   t_clk  clock period in ticks, 1 <= t_clk <= 2^(32 - b) where b is the
+ *          bit count of the largest input count k of the design (b = 1 for
+ *          k = 1, 2 for k = 2..3, 3 for k = 4..7, 4 for k = 8);
+ *   t_max > 0 analysis end, at most 2^28 clock cycles; tick_s seconds per
+ *   tick (> 0).
+ * Limit: at most 128 events of one gate (all its pins together) inside one
+ * clock cycle; more is reported as PA_EDATA.
+ * The events are validated (PA_EDATA for a broken rule above; the
+ * previously loaded events stay usable) and re-laid out into library-owned
+ * memory: time chunks of chunk_cycles cycles, inside a chunk gate-major
+ * segments of one gate and one time window (windows split a dense gate's
+ * chunk into 2^s equal parts so that no segment exceeds 128 events; the
+ * paper's event-density-aware per-gate cycle partitioning), each segment
+ * pin-major and time-sorted per pin. */
 int pa_load_events(pa_ctx *ctx, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr,
                    const uint8_t *pin_init, const int64_t *evt_t, const uint8_t *evt_val,
                    const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s);
