@@ -10,28 +10,37 @@
 // cycle bin.  Per gate (Sec. 2.4.2, Fig. 3, Eq. 4): state-dependent leakage
 // over every inter-event interval, spread over the cycle bins it overlaps.
 // The paper fuses both parts into one thread per (gate, cycle window)
-// (Fig. 7); this pass instead gives each lane one event and lets a block
-// share its events through LDS:
-//   * events are laid out chunk-major (time chunks of Cc cycles), then by
-//     gate, pin, time; each 64-bit key also carries the gate's input state at
-//     the chunk start, so a (chunk, gate) segment is self-contained;
-//   * a block streams a contiguous range of segments through LDS in batches
-//     (coalesced key/slew loads, next batch prefetched into registers while
-//     the current one is computed);
-//   * the state before an event comes from one binary search per other input
-//     pin inside the segment (value of that pin's last event before t, or the
-//     chunk-start state), which is the k-way merge of Sec. 2.4.2 done by
-//     search instead of by a sequential walk;
+// (Fig. 7).  This pass keeps the fusion and maps it onto 64-lane waves:
+//   * events are laid out chunk-major (time chunks of Cc cycles); inside a
+//     chunk, gate-major segments of one gate and one time window (a power-
+//     of-two part of the chunk picked per gate from its event density when
+//     the events are loaded, so that no segment holds more than 128 events:
+//     the event-density-aware per-gate partitioning of the paper), each
+//     segment pin-major and time-sorted per pin.  Every 64-bit key carries
+//     gate, segment-head bit, pin code, time in the chunk, value and the
+//     gate's input state at the segment start, so a segment is
+//     self-contained;
+//   * a block owns a range of whole segments inside one chunk; each of its
+//     waves streams a share of them in batches of 128 events (two per lane)
+//     with coalesced nontemporal key/slew loads, the next batch prefetched
+//     into registers, and no block barrier inside the loop;
+//   * per batch one lane per segment walks its input-pin streams in time
+//     order (the k-way merge of Sec. 2.4.2, Fig. 3), giving every input
+//     event the state before it, the set of input pins switching at its
+//     timestamp and whether it is the lowest of them;
+//   * then one lane per event: state-selected LUT, bilinear on slew and load
+//     (Sec. 2.4.1, Fig. 2), switching energy (Eq. 1), glitch test against the
+//     previous event of the same pin (Fig. 7, Eq. 2), energies added to
+//     per-cycle bins in LDS;
 //   * leakage is charged as power changes: at every distinct input timestamp
-//     one event (the lowest input pin switching there) adds
-//     dP = leak[S+] - leak[S-]; its partial bin gets dP * (bin end - t) and
-//     all later bins get dP * their length through an in-LDS prefix sum per
-//     chunk and a per-chunk carry; the leakage at t = 0 is the sum over gates
-//     of leak[S0].  This is the same sum as the paper's per-interval,
-//     per-overlapped-bin split (Sec. 2.4.2), reordered;
-//   * per-cycle bins live in LDS and are flushed once per (block, chunk) with
-//     fp64/u64 atomics into one of 8 copies (one per XCD), which the
-//     finalize kernel adds up.
+//     the lowest switching input pin adds dP = leak[S+] - leak[S-]; its
+//     partial bin gets dP * (bin end - t) and all later bins get dP * their
+//     length through an in-LDS prefix sum per chunk and a per-chunk carry;
+//     the leakage at t = 0 is the sum over gates of leak[S0].  This is the
+//     paper's per-interval, per-overlapped-bin split (Sec. 2.4.2, Eq. 4)
+//     summed in another order;
+//   * the bins are flushed once per block with fp64/u64 atomics into one of 8
+//     copies (one per XCD), which the finalize kernel adds up.
 #include <hip/hip_runtime.h>
 
 #include "pa_common.h"
