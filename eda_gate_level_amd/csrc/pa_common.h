@@ -4,112 +4,84 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
-#include <string>
 
 #include "pa.h"
 
 namespace pa {
 
 // ---------------------------------------------------------------------------
-// Exact unsigned 32-bit division by a divisor fixed at load time, by a
-// multiply-high and two shifts (Granlund & Montgomery, "Division by invariant
-// integers using multiplication", PLDI 1994, Fig. 4.1):
-//   l = ceil(log2 d), m = floor(2^32 (2^l - d) / d) + 1,
-//   t = mulhi(m, n), q = (t + ((n - t) >> min(l,1))) >> max(l-1,0).
-// Exact for every 1 <= d < 2^32 and 0 <= n < 2^32.  Cycle indices of events
-// (t / T) are integer decisions and must match plain division bit for bit.
-// ---------------------------------------------------------------------------
-struct DivU32 {
-  uint32_t m, sh1, sh2, d;
-};
-
-inline DivU32 make_divu32(uint32_t d) {
-  uint32_t l = 0;
-  while (l < 32 && (uint64_t(1) << l) < d) ++l;
-  DivU32 D;
-  D.m = uint32_t(((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1);
-  D.sh1 = l < 1 ? l : 1;
-  D.sh2 = l > 0 ? l - 1 : 0;
-  D.d = d;
-  return D;
-}
-
-__host__ __device__ inline uint32_t divu32(uint32_t n, const DivU32 &D) {
-  uint32_t t = uint32_t((uint64_t(n) * D.m) >> 32);
-  return (t + ((n - t) >> D.sh1)) >> D.sh2;
-}
-
-// ---------------------------------------------------------------------------
-// Packed 64-bit event key of the event layout, fixed fields:
+// Event layout.  Time is cut into chunks of Cc clock cycles (a power of two);
+// inside a chunk every gate's cycles are cut into 2^s equal windows, s chosen
+// per gate from its event density (the paper's event-density-aware per-gate
+// cycle partitioning).  The events are ordered by
+//   (chunk, gate, cycle, pin code, time),
+// so a window is one contiguous run, and inside a window the events of one
+// clock cycle form one run ordered by pin, then time.
+//
+// Packed 64-bit key of an event:
 //   bits [42, 64)  gate id (designs up to 2^22 - 1 gates)
-//   bit  41        head: first event of its segment
-//   bits [ 9, 41)  lk = (pin code << t_bits) | t_rel
-//   bit   8        val: the pin's value after the event
-//   bits [ 0,  8)  S0: input-pin state of the gate at the start of the segment
-// A segment is one (time chunk, gate, time window) triple: chunks are Cc
-// clock cycles long and every gate's chunk is cut into 2^s windows whose
-// length follows the gate's event density, so that no segment holds more
-// than a fixed number of events.  pin code = input pin index 0..k-1, or
-// kOutCode(p_bits) for the output pin; t_rel = timestamp minus the start of
-// the event's chunk.  Inside a segment the lk words increase strictly in
-// (pin code, t_rel) order.
+//   bit  41        window head: first event of its (chunk, gate, window)
+//   bit  40        val: the pin's value after the event
+//   bits [32, 40)  S0: the gate's input-pin state at the window start (on
+//                  window heads; zero elsewhere)
+//   bits [ 0, 32)  lk = (cycle in chunk << (pb + tb)) | (pin code << tb) | tic
+// tic = time minus the start of the event's clock cycle (tb bits); pin code =
+// input pin index 0..k-1, or out_code(pb) for the output pin.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kKeyGateShift = 42;
 constexpr uint32_t kKeyHeadShift = 41;
-constexpr uint32_t kKeyLkShift = 9;
-constexpr uint32_t kKeyValShift = 8;
+constexpr uint32_t kKeyValShift = 40;
+constexpr uint32_t kKeyS0Shift = 32;
 constexpr uint64_t kKeyMaxGates = uint64_t(1) << 22;
-constexpr int kSegMax = 128;  // most events of one segment
+constexpr int kGroupMax = 127;  // most events of one gate inside one clock cycle
 
-__host__ __device__ inline uint32_t out_code(uint32_t p_bits) { return (1u << p_bits) - 1u; }
+__host__ __device__ inline uint32_t out_code(uint32_t pb) { return (1u << pb) - 1u; }
 
-struct KeyFmt {
-  uint32_t t_bits;  // width of t_rel
-  uint32_t p_bits;  // width of the pin code
-};
+// Smallest float at or above x.  The slew-axis segment of an event is found
+// by comparing its fp32 slew with the axis points; for every float s,
+// s >= float_at_or_above(x) holds exactly when (double)s >= x, so comparing
+// in fp32 against these thresholds picks the same segment as fp64 compares.
+inline float float_at_or_above(double x) {
+  float f = (float)x;
+  if ((double)f < x) f = __builtin_nextafterf(f, __builtin_inff());
+  return f;
+}
 
 // Kernel arguments of one pass (passed by value).
 struct PassArgs {
-  // events, chunk-major layout
+  // events
   const uint64_t *key;
   const float *slew;
-  const uint32_t *orig;        // caller's CSR index of each laid-out event
-  const uint32_t *chunk_base;  // [Q+1]
-  const uint32_t *rstart;      // [n_ranges+1] nominal starts of the block ranges (inside one chunk each)
-  const uint32_t *rchunk;      // [n_ranges] chunk of each range
+  const uint32_t *orig;    // caller's CSR index of each laid-out event
+  const uint32_t *rstart;  // [n_ranges+1] nominal starts of the block ranges (inside one chunk each)
+  const uint32_t *rchunk;  // [n_ranges] chunk of each range
   int32_t n_ranges;
   int64_t E;
   int32_t Q, Cc;
   int64_t C;
   uint32_t T;
-  DivU32 divT;
+  uint32_t tb, pb;         // bit widths of tic and of the pin code in lk
+  uint32_t last_len;       // ticks of the last cycle bin
   int64_t chunk_ticks;
   int64_t t_max;
   double tick_s;
-  KeyFmt kf;
   // design
   int64_t G;
   const uint32_t *gate_info;  // cell | (cap segment << 24)
-  const double *gate_capfrac;
-  const double *gate_esw;     // 0.5 * c * Vdd^2
+  const double2 *gate_cw;     // (fraction along the cap segment, 0.5 c Vdd^2)
   const int64_t *pin_base;    // [G+1]
   const uint8_t *pin_init;    // [P]
-  const int32_t *cell_k;
-  const uint32_t *cell_lut_base;
-  const uint32_t *cell_leak_base;
+  const uint2 *cell_meta;     // x = k | leak base << 4, y = LUT base
+  const float *cell_thr;      // [n_cells][n_thr] inner slew-axis points as float, rounded up
+  const double2 *cell_axw;    // [n_cells][n_slew-1] (slew-axis point, 1 / segment width)
   const double *lut;
   const double *leak;
-  const double *slew_axis;  // [n_cells][n_slew]
-  const double *slew_invw;  // [n_cells][n_slew-1]
-  int32_t n_slew, n_cap;
-  int32_t n_cells;
-  int64_t n_leak;             // entries of the leakage table
-  // accumulators
-  double *acc_wave;                  // [8][C]
-  unsigned long long *acc_cnt;       // [8][C]  events | glitches << 32
-  double *dP;                        // [Q]   leakage power change inside each chunk
-  double *tot;                       // [8]   e_int, e_sw, e_gl, e_leak_changes, L0, -, -, -
-  unsigned long long *tot_cnt;       // [2]   n_glitches, -
+  int32_t n_slew, n_cap, n_cells, n_thr;
+  int64_t n_leak;
+  // per-block results, reduced by the finalize kernel
+  double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
+  unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32
+  double *blk_part;              // [grid][8] e_int, e_sw, e_gl, e_leak changes, L0 part, dP sum, n_gl, -
   // diagnostics (may be null)
   uint8_t *evt_glitch;
   uint8_t *evt_state;
@@ -119,31 +91,28 @@ struct FinalArgs {
   int64_t C;
   int32_t Cc, Q;
   uint32_t T;
+  uint32_t last_len;
   int64_t t_max;
   double tick_s;
-  int64_t E;
-  double *acc_wave;
-  unsigned long long *acc_cnt;
-  const double *dP;
-  const double *tot;
-  const unsigned long long *tot_cnt;
-  double *dP_next;                   // other parity set, zeroed here
-  double *tot_next;
-  unsigned long long *tot_cnt_next;
-  int32_t Q_next;
+  int32_t grid;
+  const uint32_t *chunk_blk;  // [Q+1] first block of every chunk (blocks are in chunk order)
+  const double *blk_wave;
+  const unsigned long long *blk_cnt;
+  const double *blk_part;
   double *wave_out;
   uint64_t *cyc_events;
   uint64_t *cyc_glitches;
-  double *res;                       // [16] results for the host
+  double *res;                // [16] results for the host
 };
 
 // Launchers (defined in pa_pass.hip).
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s);
 hipError_t launch_finalize(const FinalArgs &a, hipStream_t s);
 int pass_block_threads();
-int pass_batch_events();
-int pass_max_chunk_cycles();
-bool pass_cells_fit_lds(int n_cells, int n_slew, int64_t n_leak);
 int pass_wave_batch();
+int pass_max_chunk_cycles();
+// dynamic LDS bytes of the pass, and whether the cell tables fit in it
+size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_leak, bool cells);
+bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_leak);
 
 }  // namespace pa

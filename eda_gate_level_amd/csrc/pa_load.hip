@@ -7,14 +7,14 @@
 // Sec. 2.4.1) and the switching energy 0.5 c Vdd^2 of its output (Eq. 1).
 //
 // The event load validates the per-pin streams (sorted, alternating values,
-// inside the window, positive slews) and lays them out chunk-major: time is
-// cut into chunks of Cc clock cycles, every gate's chunk into density-aware
-// windows, and inside a (chunk, gate, window) segment the events are ordered
-// by pin and time.  Every segment is one contiguous run of packed keys that
-// also carry the gate's input state at the window start (the state
-// reconstruction at a window start of Sec. 2.4.2, from per-pin event-count
-// parities).  Windows start on cycle boundaries, so the per-pin glitch
-// counter never crosses one.
+// inside the window, positive slews) and lays them out: a radix sort puts
+// the events in (time chunk, gate, clock cycle, pin, time) order, and every
+// gate's part of a chunk is cut into windows whose length follows the gate's
+// event density (the paper's event-density-aware per-gate cycle
+// partitioning).  The first event of a window carries the gate's input state
+// at the window start, found from per-pin event-count parities (the state
+// reconstruction at a window start of Sec. 2.4.2).  Windows start on cycle
+// boundaries, so the per-pin glitch counter never crosses one.
 #include <hip/hip_runtime.h>
 
 #include <hipcub/hipcub.hpp>
@@ -38,7 +38,7 @@ inline int grid_for(int64_t n) {
 
 __global__ void k_gate_tables(int64_t G, const int32_t *gate_cell, const double *gate_cap, int32_t n_cells,
                               const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
-                              uint32_t *gate_info, double *capfrac, double *esw, int32_t *gate_k, uint32_t *err) {
+                              uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err) {
   for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
     const int32_t cell = gate_cell[g];
     const double cap = gate_cap[g];
@@ -52,8 +52,7 @@ __global__ void k_gate_tables(int64_t G, const int32_t *gate_cell, const double 
     int seg = 0;
     for (int j = 1; j < n_cap - 1; ++j) seg += (cap >= ca[j]) ? 1 : 0;
     gate_info[g] = (uint32_t)cell | ((uint32_t)seg << 24);
-    capfrac[g] = (cap - ca[seg]) / (ca[seg + 1] - ca[seg]);
-    esw[g] = 0.5 * cap * vdd * vdd;
+    gate_cw[g] = make_double2((cap - ca[seg]) / (ca[seg + 1] - ca[seg]), 0.5 * cap * vdd * vdd);
     gate_k[g] = cell_k[cell];
   }
 }
@@ -102,11 +101,11 @@ __global__ void k_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
   }
 }
 
-// ---- density-aware windows (paper Sec. 3, event-density-aware per-gate
-// cycle partitioning): a gate of density rho = N_evt / N_cyc gets windows of
-// about n_evt_tgt / rho cycles; here the window length is Cc / 2^s, the
-// smallest s with rho * Cc / 2^s <= target (the density floor is the chunk
-// itself), refined below until no window holds more than kSegMax events.
+// Window level of every gate: a gate of density rho = N_evt / N_cyc gets
+// windows of Cc / 2^s cycles, the smallest s with rho * Cc / 2^s <= target
+// (the paper sizes its per-gate windows to a target event count per thread;
+// here the chunk is the upper bound on a window, which plays the part of its
+// parallelism floor).
 __global__ void k_gate_levels(int64_t G, const int64_t *pin_base, const int64_t *pin_ptr, int64_t C, int32_t Cc,
                               int32_t lc, double target, uint8_t *level) {
   for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
@@ -118,125 +117,111 @@ __global__ void k_gate_levels(int64_t G, const int64_t *pin_base, const int64_t 
   }
 }
 
-// (k + 1) << level: (window, pin) pairs of a gate in one chunk
-__global__ void k_pw_len(int64_t G, const int32_t *gate_k, const uint8_t *level, int64_t *pw_len) {
-  for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x)
-    pw_len[g] = (int64_t)(gate_k[g] + 1) << level[g];
-}
-
-struct WinIdx {
-  int64_t pair;  // (chunk, gate, window, pin) pair of the event
-  int64_t base;  // pair of (chunk, gate, window, pin 0)
-  int64_t q;
+// Fields of an event in the layout order.
+struct EvPos {
+  uint64_t q;     // chunk
+  uint32_t g;     // gate
+  uint32_t cyc;   // cycle inside the chunk
+  uint32_t code;  // pin code
+  uint32_t tic;   // time inside the cycle
 };
 
-__device__ __forceinline__ WinIdx win_index(int64_t t, int64_t T, int32_t lc, int32_t sl, int64_t PW, int64_t pwb,
-                                            int32_t k, int32_t i) {
-  const int64_t cyc = t / T;
-  const int64_t q = cyc >> lc;
-  const int64_t cin = cyc & (((int64_t)1 << lc) - 1);
-  const int64_t w = cin >> (lc - sl);
-  WinIdx r;
-  r.q = q;
-  r.base = q * PW + pwb + w * (k + 1);
-  r.pair = r.base + i;
+__device__ __forceinline__ EvPos ev_pos(int64_t e, const int64_t *evt_t, const uint32_t *ev_pin,
+                                        const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
+                                        const LayoutFmt &f) {
+  EvPos r;
+  const int64_t t = evt_t[e];
+  const uint32_t p = ev_pin[e];
+  r.g = (uint32_t)pin_gate[p];
+  const uint32_t i = pin_local[p];
+  const int64_t cg = t / f.T;
+  r.q = (uint64_t)(cg >> f.lc);
+  r.cyc = (uint32_t)(cg & ((int64_t(1) << f.lc) - 1));
+  r.tic = (uint32_t)(t - cg * f.T);
+  r.code = i == (uint32_t)gate_k[r.g] ? out_code(f.pb) : i;
   return r;
 }
 
-__global__ void k_count_w(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
-                          const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
-                          const int64_t *pwbase, int64_t PW, int64_t T, int32_t lc, uint32_t *cnt) {
+__device__ __forceinline__ uint32_t lk_of(const EvPos &p, const LayoutFmt &f) {
+  return (p.cyc << (f.pb + f.tb)) | (p.code << f.tb) | p.tic;
+}
+
+// sort keys: (chunk, gate, lk) in one word, or (gate, lk) with the chunk apart
+__global__ void k_sort_keys(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
+                            const uint8_t *pin_local, const int32_t *gate_k, LayoutFmt f, uint64_t *key,
+                            uint32_t *chunk, uint32_t *idx) {
+  const uint32_t lkb = f.lc + f.pb + f.tb;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t p = ev_pin[e];
-    const int32_t g = pin_gate[p];
-    const WinIdx wi = win_index(evt_t[e], T, lc, level[g], PW, pwbase[g], gate_k[g], pin_local[p]);
-    atomicAdd(&cnt[wi.pair], 1u);
+    const EvPos p = ev_pos(e, evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
+    const uint64_t low = ((uint64_t)p.g << lkb) | lk_of(p, f);
+    if (chunk) {
+      key[e] = low;
+      chunk[e] = (uint32_t)p.q;
+    } else {
+      key[e] = (p.q << (f.gb + lkb)) | low;
+    }
+    idx[e] = (uint32_t)e;
   }
 }
 
-// flags bit 0: some window exceeds kSegMax and its gate can be refined;
-// bit 1: a one-cycle window exceeds kSegMax (cannot be refined)
-__global__ void k_winmax(int64_t G, int32_t Q, const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase,
-                         int64_t PW, int32_t lc, const uint32_t *cnt, uint8_t *level_next, uint32_t *flags,
-                         uint32_t *max_seg) {
-  const int64_t n = G * (int64_t)Q;
-  for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < n; u += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t q = u / G, g = u - q * G;
-    const int32_t np = gate_k[g] + 1, sl = level[g];
-    const int64_t b0 = q * PW + pwbase[g];
-    uint32_t mx = 0;
-    for (int64_t w = 0; w < ((int64_t)1 << sl); ++w) {
-      uint32_t sum = 0;
-      for (int32_t i = 0; i < np; ++i) sum += cnt[b0 + w * np + i];
-      mx = sum > mx ? sum : mx;
+// chunk of every event in the order of perm (input of the second sort stage)
+__global__ void k_chunk_of(int64_t E, const uint32_t *perm, const uint32_t *chunk, uint32_t *chunk_sorted) {
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x)
+    chunk_sorted[x] = chunk[perm[x]];
+}
+
+// Packed keys of the sorted events, window heads and their start states, and
+// the per-(gate, cycle) size limit.
+__global__ void k_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, const float *evt_slew,
+                         const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
+                         const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
+                         const int64_t *pin_base, const int64_t *pin_ptr, const uint8_t *pin_init, LayoutFmt f,
+                         uint64_t *key_out, float *slew_out, uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err) {
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = perm[x];
+    const EvPos p = ev_pos(e, evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
+    const uint32_t sl = level[p.g];
+    const uint32_t w = p.cyc >> (f.lc - sl);
+    bool head = true;
+    if (x > 0) {
+      const EvPos pp = ev_pos(perm[x - 1], evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
+      head = !(pp.q == p.q && pp.g == p.g && (pp.cyc >> (f.lc - sl)) == w);
     }
-    atomicMax(max_seg, mx);
-    if (mx > (uint32_t)kSegMax) {
-      if (sl < lc) {
-        atomicOr(flags, 1u);
-        level_next[g] = (uint8_t)(sl + 1);  // every writer stores the same value
-      } else {
-        atomicOr(flags, 2u);
+    if (x >= kGroupMax) {
+      const EvPos pf = ev_pos(perm[x - kGroupMax], evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
+      if (pf.q == p.q && pf.g == p.g && pf.cyc == p.cyc) atomicOr(err, ERR_GROUP);
+    }
+    uint64_t S0 = 0;
+    if (head) {
+      // input state at the window start: pin value = init XOR parity of its earlier events
+      const int64_t tw = ((int64_t)p.q * f.Cc + ((int64_t)w << (f.lc - sl))) * f.T;
+      const int64_t pb = pin_base[p.g];
+      const int32_t k = gate_k[p.g];
+      for (int32_t j = 0; j < k; ++j) {
+        int64_t lo = pin_ptr[pb + j], hi = pin_ptr[pb + j + 1];
+        const int64_t base = lo;
+        while (lo < hi) {  // first event at or after tw
+          const int64_t mid = (lo + hi) >> 1;
+          if (evt_t[mid] < tw) lo = mid + 1; else hi = mid;
+        }
+        S0 |= (uint64_t)((pin_init[pb + j] ^ (uint8_t)((lo - base) & 1)) & 1u) << j;
       }
     }
+    key_out[x] = ((uint64_t)p.g << kKeyGateShift) | ((uint64_t)head << kKeyHeadShift) |
+                 ((uint64_t)(evt_val[e] & 1u) << kKeyValShift) | (S0 << kKeyS0Shift) | (uint64_t)lk_of(p, f);
+    slew_out[x] = evt_slew[e];
+    orig_out[x] = (uint32_t)e;
+    chunk_out[x] = (uint32_t)p.q;
   }
 }
 
-// per pin, walking its (chunk, window) pairs in time order: the caller's index
-// of its first event in each window and its value at each window start
-__global__ void k_pin_windows(int64_t P, int32_t Q, const int64_t *pin_ptr, const uint8_t *pin_init,
-                              const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
-                              const uint8_t *level, const int64_t *pwbase, int64_t PW, const uint32_t *cnt,
-                              uint32_t *first, uint8_t *vstart) {
-  for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t g = pin_gate[p];
-    const int32_t np = gate_k[g] + 1, i = pin_local[p];
-    const int64_t nw = (int64_t)1 << level[g];
-    uint32_t run = (uint32_t)pin_ptr[p];
-    uint8_t v = pin_init[p] & 1u;
-    for (int32_t q = 0; q < Q; ++q) {
-      const int64_t b0 = (int64_t)q * PW + pwbase[g] + i;
-      for (int64_t w = 0; w < nw; ++w) {
-        const int64_t pr = b0 + w * np;
-        const uint32_t c = cnt[pr];
-        first[pr] = run;
-        vstart[pr] = v;
-        run += c;
-        v ^= (uint8_t)(c & 1u);
-      }
-    }
+// first sorted event of every chunk: cb[q] = first x with chunk(x) >= q
+__global__ void k_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted, uint32_t *cb) {
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x <= E; x += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t qa = x > 0 ? (int64_t)chunk_sorted[x - 1] : -1;
+    const int64_t qb = x < E ? (int64_t)chunk_sorted[x] : (int64_t)Q;
+    for (int64_t q = qa + 1; q <= qb; ++q) cb[q] = (uint32_t)x;
   }
-}
-
-__global__ void k_scatter_w(int64_t E, const int64_t *evt_t, const float *evt_slew, const uint8_t *evt_val,
-                            const uint32_t *ev_pin, const int32_t *pin_gate, const uint8_t *pin_local,
-                            const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase, int64_t PW, int64_t T,
-                            int32_t lc, int64_t chunk_ticks, const uint32_t *first, const uint32_t *off,
-                            const uint8_t *vstart, KeyFmt kf, uint64_t *key_out, float *slew_out, uint32_t *orig_out) {
-  const uint32_t outc = out_code(kf.p_bits);
-  for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t p = ev_pin[e];
-    const int32_t g = pin_gate[p];
-    const int32_t k = gate_k[g], i = pin_local[p];
-    const int64_t t = evt_t[e];
-    const WinIdx wi = win_index(t, T, lc, level[g], PW, pwbase[g], k, i);
-    const int64_t dest = (int64_t)off[wi.pair] + (e - (int64_t)first[wi.pair]);
-    uint32_t S0 = 0;
-    for (int32_t j = 0; j < k; ++j) S0 |= uint32_t(vstart[wi.base + j]) << j;
-    const uint64_t head = dest == (int64_t)off[wi.base] ? 1u : 0u;
-    const uint64_t code = i == k ? outc : (uint32_t)i;
-    const uint64_t trel = (uint64_t)(t - wi.q * chunk_ticks);
-    const uint64_t lk = (code << kf.t_bits) | trel;
-    key_out[dest] = ((uint64_t)g << kKeyGateShift) | (head << kKeyHeadShift) | (lk << kKeyLkShift) |
-                    ((uint64_t)(evt_val[e] & 1u) << kKeyValShift) | (uint64_t)S0;
-    slew_out[dest] = evt_slew[e];
-    orig_out[dest] = (uint32_t)e;
-  }
-}
-
-__global__ void k_chunk_base_w(int32_t Q, int64_t PW, const uint32_t *off, uint32_t *cb) {
-  for (int32_t q = blockIdx.x * blockDim.x + threadIdx.x; q <= Q; q += gridDim.x * blockDim.x)
-    cb[q] = off[(int64_t)q * PW];
 }
 
 }  // namespace
@@ -245,10 +230,9 @@ __global__ void k_chunk_base_w(int32_t Q, int64_t PW, const uint32_t *off, uint3
 
 hipError_t launch_gate_tables(int64_t G, const int32_t *gate_cell, const double *gate_cap, int32_t n_cells,
                               const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
-                              uint32_t *gate_info, double *capfrac, double *esw, int32_t *gate_k, uint32_t *err,
-                              hipStream_t s) {
+                              uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err, hipStream_t s) {
   hipLaunchKernelGGL(k_gate_tables, dim3(grid_for(G)), dim3(kLT), 0, s, G, gate_cell, gate_cap, n_cells, cell_k,
-                     cap_axis, n_cap, vdd, gate_info, capfrac, esw, gate_k, err);
+                     cap_axis, n_cap, vdd, gate_info, gate_cw, gate_k, err);
   return hipGetLastError();
 }
 
@@ -278,61 +262,45 @@ hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_pw_len(int64_t G, const int32_t *gate_k, const uint8_t *level, int64_t *pw_len, hipStream_t s) {
-  hipLaunchKernelGGL(k_pw_len, dim3(grid_for(G)), dim3(kLT), 0, s, G, gate_k, level, pw_len);
+hipError_t launch_sort_keys(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
+                            const uint8_t *pin_local, const int32_t *gate_k, const LayoutFmt &f, uint64_t *key,
+                            uint32_t *chunk, uint32_t *idx, hipStream_t s) {
+  hipLaunchKernelGGL(k_sort_keys, dim3(grid_for(E)), dim3(kLT), 0, s, E, evt_t, ev_pin, pin_gate, pin_local, gate_k, f,
+                     key, chunk, idx);
   return hipGetLastError();
 }
 
-hipError_t launch_count_w(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
-                          const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
-                          const int64_t *pwbase, int64_t PW, int64_t T, int32_t lc, uint32_t *cnt, hipStream_t s) {
-  hipLaunchKernelGGL(k_count_w, dim3(grid_for(E)), dim3(kLT), 0, s, E, evt_t, ev_pin, pin_gate, pin_local, gate_k,
-                     level, pwbase, PW, T, lc, cnt);
+hipError_t launch_chunk_of(int64_t E, const uint32_t *perm, const uint32_t *chunk, uint32_t *chunk_sorted,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(k_chunk_of, dim3(grid_for(E)), dim3(kLT), 0, s, E, perm, chunk, chunk_sorted);
   return hipGetLastError();
 }
 
-hipError_t launch_winmax(int64_t G, int32_t Q, const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase,
-                         int64_t PW, int32_t lc, const uint32_t *cnt, uint8_t *level_next, uint32_t *flags,
-                         uint32_t *max_seg, hipStream_t s) {
-  hipLaunchKernelGGL(k_winmax, dim3(grid_for(G * (int64_t)Q)), dim3(kLT), 0, s, G, Q, gate_k, level, pwbase, PW, lc,
-                     cnt, level_next, flags, max_seg);
+hipError_t launch_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, const float *evt_slew,
+                         const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
+                         const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
+                         const int64_t *pin_base, const int64_t *pin_ptr, const uint8_t *pin_init, const LayoutFmt &f,
+                         uint64_t *key_out, float *slew_out, uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err,
+                         hipStream_t s) {
+  hipLaunchKernelGGL(k_layout, dim3(grid_for(E)), dim3(kLT), 0, s, E, perm, evt_t, evt_slew, evt_val, ev_pin, pin_gate,
+                     pin_local, gate_k, level, pin_base, pin_ptr, pin_init, f, key_out, slew_out, orig_out, chunk_out,
+                     err);
   return hipGetLastError();
 }
 
-hipError_t launch_pin_windows(int64_t P, int32_t Q, const int64_t *pin_ptr, const uint8_t *pin_init,
-                              const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
-                              const uint8_t *level, const int64_t *pwbase, int64_t PW, const uint32_t *cnt,
-                              uint32_t *first, uint8_t *vstart, hipStream_t s) {
-  hipLaunchKernelGGL(k_pin_windows, dim3(grid_for(P)), dim3(kLT), 0, s, P, Q, pin_ptr, pin_init, pin_gate, pin_local,
-                     gate_k, level, pwbase, PW, cnt, first, vstart);
+hipError_t launch_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted, uint32_t *cb, hipStream_t s) {
+  hipLaunchKernelGGL(k_chunk_base, dim3(grid_for(E + 1)), dim3(kLT), 0, s, E, Q, chunk_sorted, cb);
   return hipGetLastError();
 }
 
-hipError_t launch_scatter_w(int64_t E, const int64_t *evt_t, const float *evt_slew, const uint8_t *evt_val,
-                            const uint32_t *ev_pin, const int32_t *pin_gate, const uint8_t *pin_local,
-                            const int32_t *gate_k, const uint8_t *level, const int64_t *pwbase, int64_t PW, int64_t T,
-                            int32_t lc, int64_t chunk_ticks, const uint32_t *first, const uint32_t *off,
-                            const uint8_t *vstart, const KeyFmt &kf, uint64_t *key_out, float *slew_out,
-                            uint32_t *orig_out, hipStream_t s) {
-  hipLaunchKernelGGL(k_scatter_w, dim3(grid_for(E)), dim3(kLT), 0, s, E, evt_t, evt_slew, evt_val, ev_pin, pin_gate,
-                     pin_local, gate_k, level, pwbase, PW, T, lc, chunk_ticks, first, off, vstart, kf, key_out,
-                     slew_out, orig_out);
-  return hipGetLastError();
+hipError_t sort_pairs_u64(const uint64_t *kin, uint64_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,
+                          int end_bit, void *tmp, size_t *tmp_bytes, hipStream_t s) {
+  return hipcub::DeviceRadixSort::SortPairs(tmp, *tmp_bytes, kin, kout, vin, vout, (int)n, 0, end_bit, s);
 }
 
-hipError_t launch_chunk_base_w(int32_t Q, int64_t PW, const uint32_t *off, uint32_t *cb, hipStream_t s) {
-  hipLaunchKernelGGL(k_chunk_base_w, dim3(grid_for(Q + 1)), dim3(kLT), 0, s, Q, PW, off, cb);
-  return hipGetLastError();
-}
-
-hipError_t scan_exclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
-                              hipStream_t s) {
-  return hipcub::DeviceScan::ExclusiveSum(tmp, *tmp_bytes, in, out, (size_t)n, s);
-}
-
-hipError_t scan_exclusive_i64(const int64_t *in, int64_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
-                              hipStream_t s) {
-  return hipcub::DeviceScan::ExclusiveSum(tmp, *tmp_bytes, in, out, (size_t)n, s);
+hipError_t sort_pairs_u32(const uint32_t *kin, uint32_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,
+                          int end_bit, void *tmp, size_t *tmp_bytes, hipStream_t s) {
+  return hipcub::DeviceRadixSort::SortPairs(tmp, *tmp_bytes, kin, kout, vin, vout, (int)n, 0, end_bit, s);
 }
 
 }  // namespace pa

@@ -1,5 +1,5 @@
 // pa_pass.hip -- the hot path of gate-level time-based power analysis on
-// gfx950: one fused pass over the chunk-major event layout plus a finalize.
+// gfx950: one fused pass over the event layout plus a finalize.
 //
 // Method: "GPU-Accelerated Gate-Level Time-Based Power Analysis via
 // Event-Density-Aware Partitioning and Kernel Fusion" (arXiv 2609.05960).
@@ -11,26 +11,23 @@
 // over every inter-event interval, spread over the cycle bins it overlaps.
 // The paper fuses both parts into one thread per (gate, cycle window)
 // (Fig. 7).  This pass keeps the fusion and maps it onto 64-lane waves:
-//   * events are laid out chunk-major (time chunks of Cc cycles); inside a
-//     chunk, gate-major segments of one gate and one time window (a power-
-//     of-two part of the chunk picked per gate from its event density when
-//     the events are loaded, so that no segment holds more than 128 events:
-//     the event-density-aware per-gate partitioning of the paper), each
-//     segment pin-major and time-sorted per pin.  Every 64-bit key carries
-//     gate, segment-head bit, pin code, time in the chunk, value and the
-//     gate's input state at the segment start, so a segment is
-//     self-contained;
-//   * a block owns a range of whole segments inside one chunk; each of its
-//     waves streams a share of them in batches of 128 events (two per lane)
-//     with coalesced nontemporal key/slew loads, the next batch prefetched
-//     into registers, and no block barrier inside the loop;
-//   * per batch one lane per segment walks its input-pin streams in time
-//     order (the k-way merge of Sec. 2.4.2, Fig. 3), giving every input
-//     event the state before it, the set of input pins switching at its
-//     timestamp and whether it is the lowest of them;
-//   * then one lane per event: state-selected LUT, bilinear on slew and load
-//     (Sec. 2.4.1, Fig. 2), switching energy (Eq. 1), glitch test against the
-//     previous event of the same pin (Fig. 7, Eq. 2), energies added to
+//   * the events are laid out by (time chunk, gate, clock cycle, pin, time);
+//     every gate's part of a chunk is cut into density-aware windows whose
+//     first event carries the gate's input state at the window start;
+//   * a block owns a range of whole windows inside one chunk and each of its
+//     waves streams a share of them, 128 consecutive events per batch (two
+//     per lane, 16-byte loads), the next batch prefetched into registers;
+//   * the state before every event is a segmented XOR scan of the input
+//     events' pin bits across the wave (DPP row shifts and broadcasts), the
+//     segments being the windows: the k-way merge of Sec. 2.4.2 at cycle
+//     granularity.  Inside one (gate, cycle) run the events are pin-major,
+//     so where a run holds several pins their time order is fixed up by a
+//     short walk over the run, which also finds the input pins switching at
+//     the same timestamp (all of them see the state before it);
+//   * a glitch is an event whose previous event in the layout is on the same
+//     pin in the same cycle (Fig. 7, Eq. 2);
+//   * one lane per event: state-selected LUT, bilinear on slew and load
+//     (Sec. 2.4.1, Fig. 2), switching energy (Eq. 1), energies added to
 //     per-cycle bins in LDS;
 //   * leakage is charged as power changes: at every distinct input timestamp
 //     the lowest switching input pin adds dP = leak[S+] - leak[S-]; its
@@ -39,8 +36,8 @@
 //     the leakage at t = 0 is the sum over gates of leak[S0].  This is the
 //     paper's per-interval, per-overlapped-bin split (Sec. 2.4.2, Eq. 4)
 //     summed in another order;
-//   * the bins are flushed once per block with fp64/u64 atomics into one of 8
-//     copies (one per XCD), which the finalize kernel adds up.
+//   * every block writes its bins and totals to its own slots; the finalize
+//     kernel adds them up in a fixed order (no global atomics).
 #include <hip/hip_runtime.h>
 
 #include "pa_common.h"
@@ -50,27 +47,22 @@ namespace pa {
 namespace {
 
 #ifndef PA_NT
-#define PA_NT 512
+#define PA_NT 256
 #endif
-#ifndef PA_CCMAX
-#define PA_CCMAX 512
-#endif
-constexpr int kNT = PA_NT;         // threads per block
-constexpr int kNW = kNT / 64;      // waves per block, each working on its own batches
-constexpr int kRW = kSegMax / 64;  // events per lane per wave batch
-constexpr int kWB = 64 * kRW;      // events per wave batch (= the longest segment)
-constexpr int kCCMAX = PA_CCMAX;   // max cycles per chunk (LDS bins)
-constexpr int kXCD = 8;
-constexpr int kMaxCellsLds = 256;
-constexpr int kCellBytesMax = 24 * 1024;
-constexpr uint32_t kInf = 0xFFFFFFFFu;
-static_assert(kWB == kSegMax, "a wave batch holds the longest segment");
+constexpr int kNT = PA_NT;           // threads per block
+constexpr int kNW = kNT / 64;        // waves per block, each working on its own batches
+constexpr int kB = 128;              // events per wave batch, two consecutive ones per lane
+constexpr int kCCMAX = 512;          // max cycles per chunk (LDS bins)
+constexpr uint32_t kFlag = 0x100u;   // segment start flag of the state scan
+constexpr size_t kLdsMax = 64 * 1024;
+static_assert(kB - 1 >= kGroupMax, "a (gate, cycle) run fits in one batch after an odd start");
 
-__device__ __forceinline__ uint32_t key_gate(uint64_t k) { return uint32_t(k >> kKeyGateShift); }
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t key_head(uint64_t k) { return uint32_t(k >> kKeyHeadShift) & 1u; }
-__device__ __forceinline__ uint32_t key_lk(uint64_t k) { return uint32_t(k >> kKeyLkShift); }
 
-// first segment head at or after position x (E if none); one whole wave
+// first window head at or after position x (E if none); one whole wave
 __device__ int find_head(const uint64_t *key, int64_t E, int64_t x) {
   const int lane = threadIdx.x & 63;
   for (;;) {
@@ -95,66 +87,86 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// bytes of the cell tables staged in dynamic LDS
-__host__ __device__ inline int64_t cell_lds_bytes(int n_cells, int n_slew, int64_t n_leak) {
-  return 8 * ((int64_t)n_cells * (2 * n_slew - 1) + n_leak) + 8 * (int64_t)n_cells;
+// value of another lane by a DPP move; lanes without a source read 0
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+}
+
+// State-scan element: low 8 bits = XOR of input-pin bits, kFlag = a window
+// starts here (its value then also holds the window's start state).
+// a then b: b restarts the segment, or the bits add up.
+__device__ __forceinline__ uint32_t seg_combine(uint32_t a, uint32_t b) { return (b & kFlag) ? b : (a ^ b); }
+
+// inclusive segmented scan over the 64 lanes (row shifts 1, 2, 4, 8, then
+// row broadcasts 15 and 31; 0 is the identity)
+__device__ __forceinline__ uint32_t seg_scan(uint32_t w) {
+  w = seg_combine(dpp_mov<0x111>(w), w);
+  w = seg_combine(dpp_mov<0x112>(w), w);
+  w = seg_combine(dpp_mov<0x114>(w), w);
+  w = seg_combine(dpp_mov<0x118>(w), w);
+  w = seg_combine(dpp_mov<0x142, 0xA>(w), w);
+  w = seg_combine(dpp_mov<0x143, 0xC>(w), w);
+  return w;
+}
+
+struct CellLds {
+  double2 *axw;
+  float *thr;
+  double *bw, *bb;
+  unsigned long long *bc;
+  double *leak;
+  uint2 *meta;
+};
+
+__host__ __device__ inline size_t cell_bytes(int n_cells, int n_slew, int n_thr, int64_t n_leak) {
+  return 16 * (size_t)n_cells * (n_slew - 1) + 4 * (size_t)n_cells * n_thr + 8 * (size_t)n_leak + 8 * (size_t)n_cells;
+}
+
+// dynamic LDS: [slew (axis, 1/width) pairs][slew thresholds][bins: wave, leakage change, counts][leakage][cell meta]
+__device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, int n_slew, int n_thr,
+                                         int64_t n_leak, bool cells) {
+  CellLds L;
+  L.axw = reinterpret_cast<double2 *>(s);
+  L.thr = reinterpret_cast<float *>(L.axw + (cells ? n_cells * (n_slew - 1) : 0));
+  L.bw = reinterpret_cast<double *>(L.thr + (cells ? n_cells * n_thr : 0));
+  L.bb = L.bw + Cc;
+  L.bc = reinterpret_cast<unsigned long long *>(L.bb + Cc);
+  L.leak = reinterpret_cast<double *>(L.bc + Cc);
+  L.meta = reinterpret_cast<uint2 *>(L.leak + (cells ? n_leak : 0));
+  return L;
 }
 
 template <bool CELL_LDS, bool DIAG>
 __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
-  extern __shared__ double s_dyn[];  // cell tables: slew axes | inverse widths | leakage | meta | LUT bases
-  // per-wave batch staging
-  __shared__ uint32_t w_lk[kNW][kWB];   // (pin code << t_bits) | t_rel
-  __shared__ uint32_t w_g[kNW][kWB];    // gate id
-  __shared__ uint32_t w_smo[kNW][kWB];  // state before | switching-pin mask << 8 | owner << 16
-  __shared__ float w_slew[kNW][kWB];
-  __shared__ uint16_t w_aux[kNW][kWB];  // S0 | val << 8
-  __shared__ uint16_t w_cyc[kNW][kWB];  // cycle inside the chunk
-  __shared__ uint16_t w_segst[kNW][kWB + 2];
-  __shared__ uint8_t w_seg[kNW][kWB];
-  // per-cycle bins of the block's chunk
-  __shared__ double bw[kCCMAX];               // energy: dynamic + partial-bin leakage
-  __shared__ double bb[kCCMAX];               // leakage power change
-  __shared__ unsigned long long bc[kCCMAX];   // events | glitches << 32
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  __shared__ uint32_t st_lk[kNW][kB];  // batch events (lk) for the in-cycle walk
+  __shared__ uint8_t st_gh[kNW][kB];   // run-start flags of the batch events
   __shared__ int s_bounds[kNW + 1];
-  __shared__ double s_red[kNW * 6];
+  __shared__ double s_red[kNW][8];
   __shared__ double s_scan[kNW];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const uint32_t tbits = a.kf.t_bits;
-  const uint32_t tmask = (1u << tbits) - 1u;
-  const uint32_t outc = out_code(a.kf.p_bits);
-  const int nb = gridDim.x, b = blockIdx.x;
-  const int xcd = b % kXCD;
-  const int ns = a.n_slew, nc = a.n_cap;
+  const int b = blockIdx.x, nb = gridDim.x;
+  const int Cc = a.Cc, ns = a.n_slew, nc = a.n_cap, nthr = a.n_thr;
+  const CellLds L = carve(s_dyn, Cc, a.n_cells, ns, nthr, a.n_leak, CELL_LDS);
   const bool has_range = b < a.n_ranges;
 
-  // cell tables in dynamic LDS
-  double *c_sa = s_dyn;
-  double *c_iw = c_sa + a.n_cells * ns;
-  double *c_lk = c_iw + a.n_cells * (ns - 1);
-  uint32_t *c_meta = reinterpret_cast<uint32_t *>(c_lk + a.n_leak);  // k | leak base << 4
-  uint32_t *c_lutb = c_meta + a.n_cells;
-  auto cell_k = [&](uint32_t c) -> uint32_t {
-    if constexpr (CELL_LDS) return c_meta[c] & 15u; else return (uint32_t)a.cell_k[c];
+  auto meta_of = [&](uint32_t c) -> uint2 {
+    if constexpr (CELL_LDS) return L.meta[c]; else return a.cell_meta[c];
   };
-  auto leak_base = [&](uint32_t c) -> uint32_t {
-    if constexpr (CELL_LDS) return c_meta[c] >> 4; else return a.cell_leak_base[c];
+  auto thr_of = [&](uint32_t c, int j) -> float4 {
+    if constexpr (CELL_LDS) return *reinterpret_cast<const float4 *>(L.thr + (size_t)c * nthr + j);
+    else return *reinterpret_cast<const float4 *>(a.cell_thr + (size_t)c * nthr + j);
   };
-  auto lut_base = [&](uint32_t c) -> uint32_t {
-    if constexpr (CELL_LDS) return c_lutb[c]; else return a.cell_lut_base[c];
-  };
-  auto slew_ax = [&](uint32_t c, int j) -> double {
-    if constexpr (CELL_LDS) return c_sa[c * ns + j]; else return a.slew_axis[(size_t)c * ns + j];
-  };
-  auto slew_iw = [&](uint32_t c, int j) -> double {
-    if constexpr (CELL_LDS) return c_iw[c * (ns - 1) + j]; else return a.slew_invw[(size_t)c * (ns - 1) + j];
+  auto axw_of = [&](uint32_t c, uint32_t j) -> double2 {
+    if constexpr (CELL_LDS) return L.axw[c * (uint32_t)(ns - 1) + j]; else return a.cell_axw[(size_t)c * (ns - 1) + j];
   };
   auto leak_of = [&](uint32_t j) -> double {
-    if constexpr (CELL_LDS) return c_lk[j]; else return a.leak[j];
+    if constexpr (CELL_LDS) return L.leak[j]; else return a.leak[j];
   };
 
-  // ---- the block's range (inside one chunk) and its waves' sub-ranges, all cut at segment heads
+  // ---- the block's range (inside one chunk) and its waves' sub-ranges, all cut at window heads
   int q = 0;
   if (has_range) {
     q = (int)a.rchunk[b];
@@ -163,22 +175,19 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
       const int h = find_head(a.key, a.E, r0 + (r1 - r0) * w / kNW);
       if (lane == 0) s_bounds[w] = h;
     }
-  } else if (tid == 0) {
-    s_bounds[0] = 0;
+  } else if (tid <= kNW) {
+    s_bounds[tid] = 0;
   }
-  for (int c = tid; c < kCCMAX; c += kNT) {
-    bw[c] = 0.0;
-    bb[c] = 0.0;
-    bc[c] = 0ull;
+  for (int c = tid; c < Cc; c += kNT) {
+    L.bw[c] = 0.0;
+    L.bb[c] = 0.0;
+    L.bc[c] = 0ull;
   }
   if constexpr (CELL_LDS) {
-    for (int c = tid; c < a.n_cells; c += kNT) {
-      c_meta[c] = (uint32_t)a.cell_k[c] | (a.cell_leak_base[c] << 4);
-      c_lutb[c] = a.cell_lut_base[c];
-    }
-    for (int j = tid; j < a.n_cells * ns; j += kNT) c_sa[j] = a.slew_axis[j];
-    for (int j = tid; j < a.n_cells * (ns - 1); j += kNT) c_iw[j] = a.slew_invw[j];
-    for (int j = tid; j < a.n_leak; j += kNT) c_lk[j] = a.leak[j];
+    for (int j = tid; j < a.n_cells * (ns - 1); j += kNT) L.axw[j] = a.cell_axw[j];
+    for (int j = tid; j < a.n_cells * nthr; j += kNT) L.thr[j] = a.cell_thr[j];
+    for (int j = tid; j < a.n_leak; j += kNT) L.leak[j] = a.leak[j];
+    for (int j = tid; j < a.n_cells; j += kNT) L.meta[j] = a.cell_meta[j];
   }
   __syncthreads();
 
@@ -187,273 +196,229 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
 
   // ---- leakage at t = 0: sum over gates of leak[S0] (Sec. 2.4.2, Fig. 3)
   for (int64_t g = (int64_t)b * kNT + tid; g < a.G; g += (int64_t)nb * kNT) {
-    const uint32_t cell = a.gate_info[g] & 0xFFFFFFu;
-    const int kk = (int)cell_k(cell);
+    const uint2 m = meta_of(a.gate_info[g] & 0xFFFFFFu);
+    const int kk = (int)(m.x & 15u);
     const int64_t p0 = a.pin_base[g];
     uint32_t S = 0;
     for (int j = 0; j < kk; ++j) S |= uint32_t(a.pin_init[p0 + j]) << j;
-    l0 += leak_of(leak_base(cell) + S);
+    l0 += leak_of((m.x >> 4) + S);
   }
 
   const int64_t cstart = (int64_t)q * a.chunk_ticks;
   const int64_t clen = min(a.chunk_ticks, a.t_max - cstart);
-  const uint32_t clen32 = (uint32_t)clen;
   const int ncyc = (int)((clen + a.T - 1) / a.T);
-  const int64_t tail_from_chunk = a.t_max - cstart;  // t_max - t = tail_from_chunk - t_rel
+  const bool last_chunk = (q == a.Q - 1);
+  const uint32_t lastc = (uint32_t)(ncyc - 1);
+  const uint32_t T = a.T;
+  const double Td = (double)T;
+  const double tail = (double)(a.t_max - cstart);  // t_max - t = tail - (cyc T + tic)
+  const double tick = a.tick_s;
+  const uint32_t tb = a.tb, pb = a.pb, cs = tb + pb;
+  const uint32_t tmask = (1u << tb) - 1u;
+  const uint32_t outc = (1u << pb) - 1u;
 
   if (has_range) {
-    uint32_t *lk_w = w_lk[wid];
-    uint32_t *g_w = w_g[wid];
-    uint32_t *smo_w = w_smo[wid];
-    float *sl_w = w_slew[wid];
-    uint16_t *aux_w = w_aux[wid];
-    uint16_t *cyc_w = w_cyc[wid];
-    uint16_t *segst_w = w_segst[wid];
-    uint8_t *seg_w = w_seg[wid];
-    const int wb = s_bounds[wid + 1];
+    const int wend = s_bounds[wid + 1];
     int pos = s_bounds[wid];
-    uint64_t pk[kRW];
-    float ps[kRW];
-    {
-      const int n0 = min(kWB, wb - pos);
-#pragma unroll
-      for (int r = 0; r < kRW; ++r) {
-        const int x = r * 64 + lane;
-        if (x < n0) {
-          pk[r] = __builtin_nontemporal_load(a.key + pos + x);
-          ps[r] = __builtin_nontemporal_load(a.slew + pos + x);
-        }
+    uint32_t carry = 0;
+    u64x2 kp = {0ull, 0ull};
+    f32x2 sp = {0.f, 0.f};
+    auto load_batch = [&](int p) {
+      const int x0 = (p & ~1) + 2 * lane;
+      if (x0 + 1 < wend) {
+        kp = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x0));
+        sp = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x0));
+      } else if (x0 < wend) {
+        kp = u64x2{__builtin_nontemporal_load(a.key + x0), 0ull};
+        sp = f32x2{__builtin_nontemporal_load(a.slew + x0), 0.f};
       }
-    }
-    while (pos < wb) {
-      const int n = min(kWB, wb - pos);
-      // ---- segments of the batch: head bits, the last (maybe incomplete) one deferred
-      unsigned long long hm[kRW];
-      int last = -1;
-#pragma unroll
-      for (int r = 0; r < kRW; ++r) {
-        const int x = r * 64 + lane;
-        hm[r] = __ballot(x < n && key_head(pk[r]));
-        if (hm[r]) last = r * 64 + 63 - __clzll((long long)hm[r]);
-      }
-      const int nproc = (pos + n < wb && last > 0) ? last : n;
-      int nseg = 0;
-      int sidx[kRW];
-#pragma unroll
-      for (int r = 0; r < kRW; ++r) {
-        const int lim = nproc - r * 64;  // lanes below lim are in [0, nproc)
-        const unsigned long long valid = lim >= 64 ? ~0ull : (lim <= 0 ? 0ull : ((1ull << lim) - 1ull));
-        const unsigned long long upto = (lane == 63) ? hm[r] : (hm[r] & ((2ull << lane) - 1ull));
-        sidx[r] = nseg + __popcll(upto) - 1;
-        nseg += __popcll(hm[r] & valid);
-      }
-      // ---- decode into the wave's LDS region; issue the gate-data loads
-      uint32_t gi[kRW];
-      double gcf[kRW], gesw[kRW];
-#pragma unroll
-      for (int r = 0; r < kRW; ++r) {
-        const int x = r * 64 + lane;
-        gi[r] = 0;
-        if (x < nproc) {
-          const uint64_t k = pk[r];
-          const uint32_t lk = key_lk(k);
-          const uint32_t g = key_gate(k);
-          lk_w[x] = lk;
-          g_w[x] = g;
-          aux_w[x] = (uint16_t)(uint32_t(k) & 0x1FFu);  // S0 | val << 8
-          cyc_w[x] = (uint16_t)divu32(lk & tmask, a.divT);
-          sl_w[x] = ps[r];
-          seg_w[x] = (uint8_t)sidx[r];
-          if ((hm[r] >> lane) & 1ull) segst_w[sidx[r]] = (uint16_t)x;
-          gi[r] = a.gate_info[g];
-          gcf[r] = a.gate_capfrac[g];
-          gesw[r] = a.gate_esw[g];
-        }
-      }
-      if (lane == 0) segst_w[nseg] = (uint16_t)nproc;
-      // ---- prefetch the next batch
-      const int npos = pos + nproc;
-      {
-        const int nn = min(kWB, wb - npos);
-#pragma unroll
-        for (int r = 0; r < kRW; ++r) {
-          const int x = r * 64 + lane;
-          if (x < nn) {
-            pk[r] = __builtin_nontemporal_load(a.key + npos + x);
-            ps[r] = __builtin_nontemporal_load(a.slew + npos + x);
-          }
-        }
-      }
-      wave_sync();
+    };
+    if (pos < wend) load_batch(pos);
+    uint32_t *slk = st_lk[wid];
+    uint8_t *sgh = st_gh[wid];
 
-      // ---- k-way merge of each segment's input-pin streams in time order
-      //      (Sec. 2.4.2, Fig. 3): one lane per segment walks the distinct
-      //      timestamps; every input event gets the state before it, the set of
-      //      input pins switching at its timestamp, and whether it is the lowest
-      //      of them (that one charges the leakage change).
-      for (int sg = lane; sg < nseg; sg += 64) {
-        const int st = segst_w[sg], en = segst_w[sg + 1];
-        int n0 = 0, n1 = 0, n2 = 0, n3 = 0, nhi = 0;
-        for (int m = st; m < en; ++m) {
-          const uint32_t p = lk_w[m] >> tbits;
-          // the output pin's code is not an input pin (it may equal 1 or 3)
-          n0 += p == 0u;
-          n1 += (p == 1u && p != outc);
-          n2 += p == 2u;
-          n3 += (p == 3u && p != outc);
-          nhi += (p >= 4u && p != outc);
-        }
-        const uint32_t S0 = aux_w[st] & 0xFFu;
-        if (nhi == 0) {
-          int c0 = st, c1 = st + n0, c2 = c1 + n1, c3 = c2 + n2;
-          const int e0 = c1, e1 = c2, e2 = c3, e3 = c3 + n3;
-          uint32_t S = S0;
-          uint32_t h0 = c0 < e0 ? (lk_w[c0] & tmask) : kInf;
-          uint32_t h1 = c1 < e1 ? (lk_w[c1] & tmask) : kInf;
-          uint32_t h2 = c2 < e2 ? (lk_w[c2] & tmask) : kInf;
-          uint32_t h3 = c3 < e3 ? (lk_w[c3] & tmask) : kInf;
-          for (;;) {
-            const uint32_t t = min(min(h0, h1), min(h2, h3));
-            if (t == kInf) break;
-            const uint32_t mask = (h0 == t ? 1u : 0u) | (h1 == t ? 2u : 0u) | (h2 == t ? 4u : 0u) | (h3 == t ? 8u : 0u);
-            const uint32_t own = __ffs((int)mask) - 1;
-            const uint32_t wv = S | (mask << 8);
-            if (h0 == t) { smo_w[c0] = wv | ((own == 0u) << 16); ++c0; h0 = c0 < e0 ? (lk_w[c0] & tmask) : kInf; }
-            if (h1 == t) { smo_w[c1] = wv | ((own == 1u) << 16); ++c1; h1 = c1 < e1 ? (lk_w[c1] & tmask) : kInf; }
-            if (h2 == t) { smo_w[c2] = wv | ((own == 2u) << 16); ++c2; h2 = c2 < e2 ? (lk_w[c2] & tmask) : kInf; }
-            if (h3 == t) { smo_w[c3] = wv | ((own == 3u) << 16); ++c3; h3 = c3 < e3 ? (lk_w[c3] & tmask) : kInf; }
-            S ^= mask;
-          }
-        } else {
-          // gates with more than four inputs: every input event scans its segment
-          for (int x = st; x < en; ++x) {
-            const uint32_t lx = lk_w[x];
-            const uint32_t ix = lx >> tbits;
-            if (ix == outc) continue;
-            const uint32_t tx = lx & tmask;
-            uint32_t Sm = (S0 & ~(1u << ix)) | ((((aux_w[x] >> 8) & 1u) ^ 1u) << ix);
-            uint32_t mask = 1u << ix, owner = 1u;
-            for (int m = st; m < en; ++m) {
-              const uint32_t lm = lk_w[m];
-              const uint32_t im = lm >> tbits;
-              if (im == outc || im == ix) continue;
-              const uint32_t tm = lm & tmask;
-              if (tm < tx) Sm = (Sm & ~(1u << im)) | (((aux_w[m] >> 8) & 1u) << im);
-              else if (tm == tx) {
-                mask |= 1u << im;
-                if (im < ix) owner = 0u;
+    while (pos < wend) {
+      const int base = pos & ~1;
+      const int first = pos - base;  // 0, or 1 when the batch starts on an odd event
+      const int navail = min(kB, wend - base);
+      const uint64_t K0 = kp.x, K1 = kp.y;
+      const float s0 = sp.x, s1 = sp.y;
+      const int i0 = 2 * lane, i1 = i0 + 1;
+      const bool v0 = i0 >= first && i0 < navail;
+      const bool v1 = i1 < navail;
+      const uint32_t lk0 = (uint32_t)K0, lk1 = (uint32_t)K1;
+      const uint32_t h0 = (uint32_t)(K0 >> 32), h1 = (uint32_t)(K1 >> 32);
+      const bool hd0 = (h0 >> 9) & 1u, hd1 = (h1 >> 9) & 1u;
+      // the event before slot i0 is the previous lane's second one
+      const uint32_t lkp0 = dpp_mov<0x138>(lk1);
+      // run starts: a window head, the batch start, or a new clock cycle
+      const bool gh0 = hd0 || i0 == first || ((lk0 ^ lkp0) >> cs) != 0u;
+      const bool gh1 = hd1 || i1 == first || ((lk1 ^ lk0) >> cs) != 0u;
+      // process up to the last run start, so that no (gate, cycle) run is split
+      const unsigned long long M0 = __ballot(v0 && gh0), M1 = __ballot(v1 && gh1);
+      int last = -1;
+      if (M0) last = 2 * (63 - __clzll((long long)M0));
+      if (M1) last = max(last, 2 * (63 - __clzll((long long)M1)) + 1);
+      const int end = (base + navail < wend && last > first) ? last : navail;
+      const bool a0 = v0 && i0 < end, a1 = v1 && i1 < end;
+      const int npos = base + end;
+      if (npos < wend) load_batch(npos);
+
+      const uint32_t c0 = (lk0 >> tb) & outc, c1 = (lk1 >> tb) & outc;  // pin codes
+      const uint32_t y0 = lk0 >> cs, y1 = lk1 >> cs;                      // cycles in the chunk
+      const uint32_t t0 = lk0 & tmask, t1 = lk1 & tmask;                  // time inside the cycle
+      const bool in0 = c0 != outc, in1 = c1 != outc;
+      const uint32_t g0 = h0 >> 10, g1 = h1 >> 10;
+      uint32_t gi0 = 0, gi1 = 0;
+      double2 cw0 = make_double2(0.0, 0.0), cw1 = make_double2(0.0, 0.0);
+      if (a0) { gi0 = a.gate_info[g0]; cw0 = a.gate_cw[g0]; }
+      if (a1) { gi1 = a.gate_info[g1]; cw1 = a.gate_cw[g1]; }
+
+      // ---- state before every event: segmented XOR scan over the batch (Sec. 2.4.2)
+      const uint32_t tg0 = (a0 && in0) ? (1u << c0) : 0u;
+      const uint32_t tg1 = (a1 && in1) ? (1u << c1) : 0u;
+      const uint32_t e0 = !a0 ? 0u : (hd0 ? (kFlag | ((h0 & 0xFFu) ^ tg0)) : tg0);
+      const uint32_t e1 = !a1 ? 0u : (hd1 ? (kFlag | ((h1 & 0xFFu) ^ tg1)) : tg1);
+      uint32_t wv = seg_combine(e0, e1);
+      if (lane == 0) wv = seg_combine(carry, wv);
+      const uint32_t I = seg_scan(wv);
+      uint32_t X = dpp_mov<0x138>(I);
+      if (lane == 0) X = carry;
+      const uint32_t I0 = seg_combine(X, e0);
+      uint32_t S0s = hd0 ? (h0 & 0xFFu) : (X & 0xFFu);
+      uint32_t S1s = hd1 ? (h1 & 0xFFu) : (I0 & 0xFFu);
+      carry = (uint32_t)__builtin_amdgcn_readlane((int)I, (end - 1) >> 1);
+
+      // ---- runs of one gate in one cycle with several events: time order across pins
+      uint32_t mk0 = 1u << c0, mk1 = 1u << c1;  // input pins switching at the event's timestamp
+      bool ow0 = true, ow1 = true;              // lowest of them: charges the leakage change
+      if ((__ballot(a0 && !gh0) | __ballot(a1 && !gh1)) != 0ull) {
+        slk[i0] = lk0;
+        slk[i1] = lk1;
+        sgh[i0] = (uint8_t)(gh0 || i0 >= end);
+        sgh[i1] = (uint8_t)(gh1 || i1 >= end);
+        wave_sync();
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int p = r ? i1 : i0;
+          const bool act = (r ? (a1 && in1) : (a0 && in0));
+          const uint32_t cx = r ? c1 : c0, tx = r ? t1 : t0;
+          const bool ghx = r ? gh1 : gh0;
+          uint32_t corr = 0, mk = 1u << cx;
+          bool ow = true;
+          bool bk = act && !ghx;
+          bool fw = act && p + 1 < end && !sgh[p + 1];
+          auto visit = [&](uint32_t ly) {
+            const uint32_t j = (ly >> tb) & outc;
+            if (j != outc && j != cx) {
+              const uint32_t ty = ly & tmask;
+              if (j < cx ? ty >= tx : ty < tx) corr ^= 1u << j;
+              if (ty == tx) {
+                mk |= 1u << j;
+                if (j < cx) ow = false;
               }
             }
-            smo_w[x] = Sm | (mask << 8) | (owner << 16);
-          }
-        }
-      }
-      wave_sync();
-
-      // ---- one event per lane: energies, glitches, leakage changes, bins
-      double L[kRW][4];  // input event: 2x2 LUT corners; output event: L[r][0] = 0.5 c Vdd^2
-      double fa[kRW];
-      uint32_t smo[kRW];  // state before | mask << 8 | owner << 16 | input << 17
-#pragma unroll
-      for (int r = 0; r < kRW; ++r) {
-        const int x = r * 64 + lane;
-        smo[r] = 0;
-        if (x >= nproc) continue;
-        const uint32_t code = lk_w[x] >> tbits;
-        if (code == outc) {  // output pin: no LUT, no state
-          L[r][0] = gesw[r];
-          continue;
-        }
-        const uint32_t cell = gi[r] & 0xFFFFFFu;
-        const uint32_t kk = cell_k(cell);
-        const uint32_t so = smo_w[x];
-        smo[r] = so | (1u << 17);
-        const uint32_t Sm = so & ((1u << kk) - 1u);  // no-op for valid states; keeps the LUT row inside the cell
-        // slew segment on the cell's axis (Sec. 2.4.1, Fig. 2)
-        const double sl = (double)sl_w[x];
-        int si = 0;
-        for (int j = 1; j < ns - 1; ++j) si += (sl >= slew_ax(cell, j)) ? 1 : 0;
-        fa[r] = (sl - slew_ax(cell, si)) * slew_iw(cell, si);
-        const double *Lp = a.lut + lut_base(cell) + ((Sm * kk + code) * (uint32_t)ns + si) * (uint32_t)nc + (gi[r] >> 24);
-        L[r][0] = Lp[0];
-        L[r][1] = Lp[1];
-        L[r][2] = Lp[nc];
-        L[r][3] = Lp[nc + 1];
-      }
-#pragma unroll
-      for (int r = 0; r < kRW; ++r) {
-        const int x = r * 64 + lane;
-        if (x >= nproc) continue;
-        const uint32_t lk = lk_w[x];
-        const uint32_t code = lk >> tbits;
-        const uint32_t trel = lk & tmask;
-        const uint32_t cyc = cyc_w[x];
-        const uint32_t val = (aux_w[x] >> 8) & 1u;
-        const int sst = segst_w[seg_w[x]];
-        // glitch: previous event of the same pin inside the same cycle (Fig. 7)
-        bool glitch = false;
-        double r_gl = 0.0;
-        if (x > sst && (lk_w[x - 1] >> tbits) == code && cyc_w[x - 1] == cyc) {
-          glitch = true;
-          const double pw = (double)(trel - (lk_w[x - 1] & tmask));
-          const double rr = pw / (0.5 * ((double)sl_w[x] + (double)sl_w[x - 1]));  // Eq. 2 (reading)
-          r_gl = rr > 1.0 ? 1.0 : rr;
-        }
-        const uint32_t so = smo[r];
-        double E, extra = 0.0;
-        if (so & (1u << 17)) {
-          // bilinear internal energy
-          const double v0 = L[r][0] + gcf[r] * (L[r][1] - L[r][0]);
-          const double v1 = L[r][2] + gcf[r] * (L[r][3] - L[r][2]);
-          E = v0 + fa[r] * (v1 - v0);
-          if (so & (1u << 16)) {
-            // leakage power change at this timestamp (owner = lowest switching input pin)
-            const uint32_t Sm = so & 0xFFu, mask = (so >> 8) & 0xFFu;
-            const uint32_t lb = leak_base(gi[r] & 0xFFFFFFu);
-            const double dp = leak_of(lb + (Sm ^ mask)) - leak_of(lb + Sm);
-            if (dp != 0.0) {
-              const uint32_t bend = min((cyc + 1u) * a.T, clen32);
-              extra = dp * (double)(bend - trel) * a.tick_s;
-              atomicAdd(&bb[cyc], dp);
-              e_lk += dp * (double)(tail_from_chunk - (int64_t)trel) * a.tick_s;
+          };
+          for (int d = 1; __ballot(bk || fw) != 0ull; ++d) {
+            if (bk) {
+              const int y = p - d;
+              visit(slk[y]);
+              bk = !sgh[y];
+            }
+            if (fw) {
+              const int y = p + d;
+              visit(slk[y]);
+              fw = y + 1 < end && !sgh[y + 1];
             }
           }
-          if (!glitch) e_int += E;
-        } else {
-          // switching energy of a 0->1 output event (Eq. 1)
-          E = val ? L[r][0] : 0.0;
-          if (!glitch) e_sw += E;
+          if (r) { S1s ^= corr; mk1 = mk; ow1 = ow; } else { S0s ^= corr; mk0 = mk; ow0 = ow; }
         }
+        wave_sync();
+      }
+
+      // ---- one event per lane slot: energy, glitch, leakage change, bins
+      const float sp0 = __int_as_float((int)dpp_mov<0x138>((uint32_t)__float_as_int(s1)));
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const bool act = r ? a1 : a0;
+        if (!act) continue;
+        const uint32_t lk = r ? lk1 : lk0, hw = r ? h1 : h0;
+        const uint32_t code = r ? c1 : c0, cyc = r ? y1 : y0, tic = r ? t1 : t0;
+        const bool input = r ? in1 : in0;
+        const bool gh = r ? gh1 : gh0;
+        const uint32_t info = r ? gi1 : gi0;
+        const double2 cw = r ? cw1 : cw0;
+        const float sl = r ? s1 : s0;
+        const uint32_t lkp = r ? lk0 : lkp0;
+        const float slp = r ? s0 : sp0;
+        const uint32_t cell = info & 0xFFFFFFu;
+        const uint2 m = meta_of(cell);
+        const uint32_t kk = m.x & 15u, lb = m.x >> 4;
+        const uint32_t smask = (1u << kk) - 1u;
+        const uint32_t Sm = (r ? S1s : S0s) & smask;
+        // slew segment on the cell's axis: inner points at or below the slew (Sec. 2.4.1, Fig. 2)
+        uint32_t si = 0;
+        for (int j = 0; j < nthr; j += 4) {
+          const float4 th = thr_of(cell, j);
+          si += (sl >= th.x ? 1u : 0u) + (sl >= th.y ? 1u : 0u) + (sl >= th.z ? 1u : 0u) + (sl >= th.w ? 1u : 0u);
+        }
+        const double2 aw = axw_of(cell, si);
+        const double fa = ((double)sl - aw.x) * aw.y;
+        const uint32_t cl = input ? code : 0u;
+        const double *Lp = a.lut + (m.y + ((Sm * kk + cl) * (uint32_t)ns + si) * (uint32_t)nc + (info >> 24));
+        const double L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
+        const double v0 = L00 + cw.x * (L01 - L00);
+        const double v1 = L10 + cw.x * (L11 - L10);
+        const double Eint = v0 + fa * (v1 - v0);
+        const double E = input ? Eint : (((hw >> 8) & 1u) ? cw.y : 0.0);  // Eq. 1: 0->1 output events only
+        // glitch: the previous event of the same pin lies in the same cycle (Fig. 7)
+        const bool glitch = !gh && ((lk ^ lkp) >> tb) == 0u;
         double contrib = E;
         if (glitch) {
-          contrib = r_gl * E;
+          const double pw = (double)(tic - (lkp & tmask));
+          const double rr = pw / (0.5 * ((double)sl + (double)slp));  // Eq. 2 (reading)
+          contrib = (rr > 1.0 ? 1.0 : rr) * E;
           e_gl += contrib;
           ++n_gl;
+        } else if (input) {
+          e_int += E;
+        } else {
+          e_sw += E;
         }
-        contrib += extra;
-        if (contrib != 0.0) atomicAdd(&bw[cyc], contrib);
-        atomicAdd(&bc[cyc], 1ull | ((unsigned long long)glitch << 32));
+        // leakage power change at this timestamp (owner = lowest switching input pin)
+        if (input && (r ? ow1 : ow0)) {
+          const double dp = leak_of(lb + (Sm ^ ((r ? mk1 : mk0) & smask))) - leak_of(lb + Sm);
+          if (dp != 0.0) {
+            const uint32_t blen = (last_chunk && cyc == lastc) ? a.last_len : T;
+            const double dpt = dp * tick;
+            contrib += dpt * (double)(blen - tic);
+            atomicAdd(&L.bb[cyc], dp);
+            e_lk += dpt * (tail - fma((double)cyc, Td, (double)tic));
+          }
+        }
+        if (contrib != 0.0) atomicAdd(&L.bw[cyc], contrib);
+        atomicAdd(&L.bc[cyc], 1ull | ((unsigned long long)glitch << 32));
         if constexpr (DIAG) {
-          const uint32_t o = a.orig[pos + x];
+          const uint32_t o = a.orig[base + (r ? i1 : i0)];
           if (a.evt_glitch) a.evt_glitch[o] = glitch ? 1 : 0;
-          if (a.evt_state) a.evt_state[o] = (uint8_t)(so & 0xFFu);
+          if (a.evt_state) a.evt_state[o] = (uint8_t)(input ? Sm : 0u);
         }
       }
-      wave_sync();
       pos = npos;
     }
   }
   __syncthreads();
 
-  // ---- flush the chunk's bins: in-chunk prefix of leakage changes, then atomics
-  if (has_range) {
+  // ---- the block's bins: in-chunk prefix of the leakage changes, then its own slots
+  double dsum = 0.0;
+  {
     constexpr int PER = kCCMAX / kNT > 0 ? kCCMAX / kNT : 1;
     double loc[PER];
     double s = 0.0;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid * PER + u;
-      loc[u] = (c < ncyc) ? bb[c] : 0.0;
+      loc[u] = (has_range && c < ncyc) ? L.bb[c] : 0.0;
       s += loc[u];
     }
     double incl = s;
@@ -463,105 +428,144 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
     }
     if (lane == 63) s_scan[wid] = incl;
     __syncthreads();
-    double wbase = 0.0, total = 0.0;
+    double wbase = 0.0;
     for (int w = 0; w < kNW; ++w) {
       const double v = s_scan[w];
       if (w < wid) wbase += v;
-      total += v;
+      dsum += v;
     }
     double run = wbase + incl - s;
-    const int64_t cg0 = (int64_t)q * a.Cc;
+    double *ow = a.blk_wave + (size_t)b * Cc;
+    unsigned long long *oc = a.blk_cnt + (size_t)b * Cc;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid * PER + u;
-      if (c < ncyc) {
-        const int64_t cg = cg0 + c;
-        const double len = (cg == a.C - 1) ? (double)(a.t_max - cg * (int64_t)a.T) : (double)a.T;
-        const double v = bw[c] + run * len * a.tick_s;
-        if (v != 0.0) atomicAdd(&a.acc_wave[(size_t)xcd * a.C + cg], v);
-        const unsigned long long cn = bc[c];
-        if (cn) atomicAdd(&a.acc_cnt[(size_t)xcd * a.C + cg], cn);
-        run += loc[u];
+      if (c < Cc) {
+        double v = 0.0;
+        unsigned long long cn = 0ull;
+        if (has_range && c < ncyc) {
+          const double len = (last_chunk && c == (int)lastc) ? (double)a.last_len : Td;
+          v = L.bw[c] + run * len * tick;
+          cn = L.bc[c];
+          run += loc[u];
+        }
+        ow[c] = v;
+        oc[c] = cn;
       }
     }
-    if (tid == 0 && total != 0.0) atomicAdd(&a.dP[q], total);
   }
 
   // ---- block totals
   {
-    double v[5] = {e_int, e_sw, e_gl, e_lk, l0};
+    double v[6] = {e_int, e_sw, e_gl, e_lk, l0, (double)n_gl};
 #pragma unroll
-    for (int u = 0; u < 5; ++u) v[u] = wave_sum(v[u]);
-    unsigned long long ng = n_gl;
-    for (int o = 32; o > 0; o >>= 1) ng += __shfl_xor(ng, o, 64);
+    for (int u = 0; u < 6; ++u) v[u] = wave_sum(v[u]);
     if (lane == 0) {
 #pragma unroll
-      for (int u = 0; u < 5; ++u) s_red[wid * 6 + u] = v[u];
-      s_red[wid * 6 + 5] = (double)ng;
+      for (int u = 0; u < 6; ++u) s_red[wid][u] = v[u];
     }
     __syncthreads();
-    if (tid < 6) {
+    if (tid < 8) {
       double t = 0.0;
-      for (int w = 0; w < kNW; ++w) t += s_red[w * 6 + tid];
       if (tid < 5) {
-        if (t != 0.0) atomicAdd(&a.tot[tid], t);
-      } else {
-        if (t != 0.0) atomicAdd(&a.tot_cnt[0], (unsigned long long)t);
+        for (int w = 0; w < kNW; ++w) t += s_red[w][tid];
+      } else if (tid == 5) {
+        t = dsum;
+      } else if (tid == 6) {
+        for (int w = 0; w < kNW; ++w) t += s_red[w][5];
       }
+      a.blk_part[(size_t)b * 8 + tid] = t;
     }
   }
 }
 
 constexpr int kFT = 256;
 
+__device__ double block_sum(double v, double *s_red) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) s_red[wid] = v;
+  __syncthreads();
+  double t = 0.0;
+  for (int w = 0; w < kFT / 64; ++w) t += s_red[w];
+  return t;
+}
+
+// One thread per cycle: adds up the blocks' bins of the cycle's chunk and the
+// leakage carried into the chunk (L0 plus the changes of earlier chunks);
+// block 0 also adds up the totals (Eq. 3).
 __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
-  __shared__ double s_base[kFT / 64];
+  __shared__ double s_red[kFT / 64];
+  __shared__ double s_P[kFT];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kFT;
-  const int qa = (int)(c0 / f.Cc);
-  // leakage power at the start of chunk qa: L0 + sum of earlier chunks' changes
-  double part = 0.0;
-  for (int j = tid; j < qa; j += kFT) part += f.dP[j];
-  part = wave_sum(part);
-  if (lane == 0) s_base[wid] = part;
+  const int64_t chi = min(c0 + kFT, f.C) - 1;
+  const int qa = (int)(c0 / f.Cc), qb = (int)(chi / f.Cc);
+  const uint32_t ba = f.chunk_blk[qa];
+  double l0 = 0.0, pre = 0.0;
+  for (int bb = tid; bb < f.grid; bb += kFT) {
+    l0 += f.blk_part[(size_t)bb * 8 + 4];
+    if ((uint32_t)bb < ba) pre += f.blk_part[(size_t)bb * 8 + 5];
+  }
+  l0 = block_sum(l0, s_red);
+  pre = block_sum(pre, s_red);
+  // leakage change inside every covered chunk, then their exclusive prefix
+  double dq = 0.0;
+  if (tid <= qb - qa) {
+    const uint32_t b0 = f.chunk_blk[qa + tid], b1 = f.chunk_blk[qa + tid + 1];
+    for (uint32_t bb = b0; bb < b1; ++bb) dq += f.blk_part[(size_t)bb * 8 + 5];
+  }
+  double incl = dq;
+  for (int o = 1; o < 64; o <<= 1) {
+    const double v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
   __syncthreads();
-  double base = f.tot[4];
-  for (int w = 0; w < kFT / 64; ++w) base += s_base[w];
+  if (lane == 63) s_red[wid] = incl;
+  __syncthreads();
+  double wb = 0.0;
+  for (int w = 0; w < wid; ++w) wb += s_red[w];
+  s_P[tid] = l0 + pre + wb + incl - dq;
+  __syncthreads();
   const int64_t c = c0 + tid;
   if (c < f.C) {
-    const int qc = (int)(c / f.Cc);
-    double P = base;
-    for (int j = qa; j < qc; ++j) P += f.dP[j];
-    const double len = (c == f.C - 1) ? (double)(f.t_max - c * (int64_t)f.T) : (double)f.T;
-    double w = P * len * f.tick_s;
+    const int q = (int)(c / f.Cc);
+    const int cin = (int)(c - (int64_t)q * f.Cc);
+    const double len = (c == f.C - 1) ? (double)f.last_len : (double)f.T;
+    double w = s_P[q - qa] * len * f.tick_s;
     unsigned long long cnt = 0;
-#pragma unroll
-    for (int x = 0; x < kXCD; ++x) {
-      w += f.acc_wave[(size_t)x * f.C + c];
-      cnt += f.acc_cnt[(size_t)x * f.C + c];
-      f.acc_wave[(size_t)x * f.C + c] = 0.0;
-      f.acc_cnt[(size_t)x * f.C + c] = 0ull;
+    const uint32_t b0 = f.chunk_blk[q], b1 = f.chunk_blk[q + 1];
+    for (uint32_t bb = b0; bb < b1; ++bb) {
+      w += f.blk_wave[(size_t)bb * f.Cc + cin];
+      cnt += f.blk_cnt[(size_t)bb * f.Cc + cin];
     }
     f.wave_out[c] = w;
     f.cyc_events[c] = cnt & 0xFFFFFFFFull;
     f.cyc_glitches[c] = cnt >> 32;
   }
   if (blockIdx.x == 0) {
-    for (int j = tid; j < f.Q_next; j += kFT) f.dP_next[j] = 0.0;
-    if (tid < 8) f.tot_next[tid] = 0.0;
-    if (tid < 2) f.tot_cnt_next[tid] = 0ull;
+    double t[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int bb = tid; bb < f.grid; bb += kFT) {
+      t[0] += f.blk_part[(size_t)bb * 8 + 0];
+      t[1] += f.blk_part[(size_t)bb * 8 + 1];
+      t[2] += f.blk_part[(size_t)bb * 8 + 2];
+      t[3] += f.blk_part[(size_t)bb * 8 + 3];
+      t[4] += f.blk_part[(size_t)bb * 8 + 6];
+    }
+    for (int u = 0; u < 5; ++u) t[u] = block_sum(t[u], s_red);
     if (tid == 0) {
       const double window = (double)f.t_max * f.tick_s;
-      const double e_leak = f.tot[4] * window + f.tot[3];
-      f.res[0] = f.tot[0];
-      f.res[1] = f.tot[1];
-      f.res[2] = f.tot[2];
+      const double e_leak = l0 * window + t[3];
+      f.res[0] = t[0];
+      f.res[1] = t[1];
+      f.res[2] = t[2];
       f.res[3] = e_leak;
-      f.res[4] = f.tot[0] / window;  // Eq. 3
-      f.res[5] = f.tot[1] / window;
-      f.res[6] = f.tot[2] / window;
+      f.res[4] = t[0] / window;  // Eq. 3
+      f.res[5] = t[1] / window;
+      f.res[6] = t[2] / window;
       f.res[7] = e_leak / window;
-      f.res[8] = (double)f.tot_cnt[0];
+      f.res[8] = t[4];
     }
   }
 }
@@ -569,26 +573,30 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
 }  // namespace
 
 int pass_block_threads() { return kNT; }
-int pass_batch_events() { return kWB; }
-int pass_wave_batch() { return kWB; }
+int pass_wave_batch() { return kB; }
 int pass_max_chunk_cycles() { return kCCMAX; }
 
-bool pass_cells_fit_lds(int n_cells, int n_slew, int64_t n_leak) {
-  return n_cells <= kMaxCellsLds && cell_lds_bytes(n_cells, n_slew, n_leak) <= kCellBytesMax;
+size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_leak, bool cells) {
+  return 24 * (size_t)Cc + (cells ? cell_bytes(n_cells, n_slew, n_thr, n_leak) : 0);
+}
+
+bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_leak) {
+  return pass_lds_bytes(Cc, n_cells, n_slew, n_thr, n_leak, true) <= 48 * 1024;
 }
 
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
-  const bool cells = pass_cells_fit_lds(a.n_cells, a.n_slew, a.n_leak);
+  const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_thr, a.n_leak);
   const bool diag = a.evt_glitch || a.evt_state;
-  const size_t dyn = cells ? (size_t)cell_lds_bytes(a.n_cells, a.n_slew, a.n_leak) : 0;
+  const size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_thr, a.n_leak, cells);
+  if (dyn > kLdsMax) return hipErrorInvalidValue;
   if (cells && !diag)
     hipLaunchKernelGGL((k_fused<true, false>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
   else if (cells)
     hipLaunchKernelGGL((k_fused<true, true>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
   else if (!diag)
-    hipLaunchKernelGGL((k_fused<false, false>), dim3(grid_blocks), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((k_fused<false, false>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
   else
-    hipLaunchKernelGGL((k_fused<false, true>), dim3(grid_blocks), dim3(kNT), 0, s, a);
+    hipLaunchKernelGGL((k_fused<false, true>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
   return hipGetLastError();
 }
 

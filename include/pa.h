@@ -59,8 +59,8 @@ typedef struct pa_ctx pa_ctx;
  * zero field means "choose automatically". */
 typedef struct {
   int32_t chunk_cycles;   /* cycles per time chunk of the event layout; rounded down to a
-                             power of two, at most 512 (0 = 256) */
-  int32_t grid_blocks;    /* target block count of the fused pass (0 = two per compute unit);
+                             power of two, at most 512 (0 = 512) */
+  int32_t grid_blocks;    /* target block count of the fused pass (0 = four per compute unit);
                              the pass cuts the events into about this many ranges */
   int32_t time_kernels;   /* nonzero: record per-kernel device times of pa_run */
   int32_t reserved;
@@ -104,15 +104,14 @@ int pa_load_design(pa_ctx *ctx, int64_t n_gates, const int32_t *gate_cell, const
  *          k = 1, 2 for k = 2..3, 3 for k = 4..7, 4 for k = 8);
  *   t_max > 0 analysis end, at most 2^28 clock cycles; tick_s seconds per
  *   tick (> 0).
- * Limit: at most 128 events of one gate (all its pins together) inside one
+ * Limit: at most 127 events of one gate (all its pins together) inside one
  * clock cycle; more is reported as PA_EDATA.
  * The events are validated (PA_EDATA for a broken rule above; the
  * previously loaded events stay usable) and re-laid out into library-owned
- * memory: time chunks of chunk_cycles cycles, inside a chunk gate-major
- * segments of one gate and one time window (windows split a dense gate's
- * chunk into 2^s equal parts so that no segment exceeds 128 events; the
- * paper's event-density-aware per-gate cycle partitioning), each segment
- * pin-major and time-sorted per pin. */
+ * memory: time chunks of chunk_cycles cycles; inside a chunk the events are
+ * ordered by gate, clock cycle, pin and time, and every gate's part of a
+ * chunk is cut into 2^s equal windows sized from the gate's event density
+ * (the paper's event-density-aware per-gate cycle partitioning). */
 int pa_load_events(pa_ctx *ctx, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr,
                    const uint8_t *pin_init, const int64_t *evt_t, const uint8_t *evt_val,
                    const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s);
@@ -141,7 +140,8 @@ typedef struct {
   int64_t n_gates, n_pins, n_events, n_cycles;
   int32_t chunk_cycles, n_chunks;
   int32_t grid_blocks, block_threads;
-  int32_t batch_events, max_segment_events;
+  int32_t batch_events;       /* events one wave takes per step of the pass */
+  int32_t max_segment_events; /* most events of one gate in one clock cycle (the load limit) */
   int64_t device_bytes;       /* library-owned device memory */
   float kernel_ms[4];         /* last pa_run with time_kernels: fused, finalize, (unused), total */
 } pa_info;

@@ -58,32 +58,35 @@ def test_create_without_gpu_fails_cleanly(libpa):
     assert ei.value.code in (_pa.PA_EINVAL, _pa.PA_EHIP)
 
 
-DIV_TEST = r"""
+THR_TEST = r"""
 #include "pa_common.h"
+#include <cmath>
 #include <cstdio>
 #include <cstdint>
+#include <cstring>
 #include <random>
+static float bits_f(uint32_t u) { float f; std::memcpy(&f, &u, 4); return f; }
 int main() {
-  std::mt19937_64 rng(12345);
-  const uint32_t ds[] = {1u, 2u, 3u, 5u, 7u, 10u, 997u, 1000u, 4096u, 65535u, 65536u, 100000u, 500000u,
-                         1000000u, 999983u, 1u << 31, (1u << 31) + 1u, 4294967291u, 4294967295u};
+  std::mt19937_64 rng(777);
+  std::uniform_real_distribution<double> mant(1.0, 2.0);
   long bad = 0, n = 0;
-  for (uint32_t d : ds) {
-    pa::DivU32 D = pa::make_divu32(d);
-    for (uint64_t x = 0; x < 200000; ++x) { uint32_t v = (uint32_t)x; bad += pa::divu32(v, D) != v / d; ++n; }
-    for (int k = 0; k < 200000; ++k) { uint32_t v = (uint32_t)rng(); bad += pa::divu32(v, D) != v / d; ++n; }
-    for (uint64_t m = 1; m * d <= 0xFFFFFFFFull && m < 5000; ++m) {
-      for (int o = -1; o <= 1; ++o) {
-        uint64_t v = m * d + o; if (v > 0xFFFFFFFFull) continue;
-        bad += pa::divu32((uint32_t)v, D) != (uint32_t)v / d; ++n;
-      }
+  for (int k = 0; k < 200000; ++k) {
+    // axis points of every magnitude, also exactly representable ones and negatives
+    double x = std::ldexp(mant(rng), (int)(rng() % 80) - 40);
+    if (k % 7 == 0) x = (double)(float)x;
+    if (k % 11 == 0) x = -x;
+    const float t = pa::float_at_or_above(x);
+    if (!((double)t >= x)) ++bad;
+    // floats around x: the fp32 compare must agree with the fp64 one
+    const float c = (float)x;
+    uint32_t u;
+    std::memcpy(&u, &c, 4);
+    for (int d = -3; d <= 3; ++d) {
+      const float s = bits_f(u + (uint32_t)d);
+      if (!std::isfinite(s)) continue;
+      bad += (s >= t) != ((double)s >= x);
+      ++n;
     }
-    uint32_t top = 0xFFFFFFFFu; bad += pa::divu32(top, D) != top / d; ++n;
-  }
-  for (int k = 0; k < 300000; ++k) {
-    uint32_t d = (uint32_t)rng() | 1u; if ((k & 1) == 0) d = (uint32_t)(rng() % 2000000) + 1u;
-    uint32_t v = (uint32_t)rng();
-    pa::DivU32 D = pa::make_divu32(d); bad += pa::divu32(v, D) != v / d; ++n;
   }
   printf("%ld %ld\n", bad, n);
   return bad != 0;
@@ -91,10 +94,10 @@ int main() {
 """
 
 
-def test_cycle_division_is_exact(tmp_path):
-    src = tmp_path / "div.cpp"
-    src.write_text(DIV_TEST)
-    exe = tmp_path / "div"
+def test_fp32_slew_thresholds_match_fp64_compares(tmp_path):
+    src = tmp_path / "thr.cpp"
+    src.write_text(THR_TEST)
+    exe = tmp_path / "thr"
     hipcc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
     r = subprocess.run([hipcc, "-O2", "-std=c++17", "-x", "hip", "--offload-arch=gfx950", f"-I{ROOT}/include",
                         f"-I{ROOT}/eda_gate_level_amd/csrc", "-o", str(exe), str(src)], capture_output=True, text=True)
