@@ -297,7 +297,7 @@ static int build_ranges(pa_ctx *c, Events &v) {
     cb[q] = (uint32_t)rs.size();
     const int64_t a = v.h_chunk_base[q], b = v.h_chunk_base[q + 1];
     if (b <= a) continue;
-    const int64_t n = std::max<int64_t>(1, (b - a + per / 2) / per);
+    const int64_t n = std::max<int64_t>(1, (b - a) / per);  // never more blocks than the target
     for (int64_t i = 0; i < n; ++i) {
       rs.push_back((uint32_t)(a + (b - a) * i / n));
       rq.push_back((uint32_t)q);

@@ -49,6 +49,9 @@ namespace {
 #ifndef PA_NT
 #define PA_NT 256
 #endif
+#ifndef PA_FUSED_ATTR
+#define PA_FUSED_ATTR
+#endif
 constexpr int kNT = PA_NT;           // threads per block
 constexpr int kNW = kNT / 64;        // waves per block, each working on its own batches
 constexpr int kB = 128;              // events per wave batch, two consecutive ones per lane
@@ -98,15 +101,23 @@ __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
 // a then b: b restarts the segment, or the bits add up.
 __device__ __forceinline__ uint32_t seg_combine(uint32_t a, uint32_t b) { return (b & kFlag) ? b : (a ^ b); }
 
+// one step of the scan: w picks up the value of another lane unless a
+// window starts at or before w's own lane (its flag is set)
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t seg_step(uint32_t w) {
+  const uint32_t t = dpp_mov<CTRL, ROWS>(w) ^ w;
+  return w > 0xFFu ? w : t;
+}
+
 // inclusive segmented scan over the 64 lanes (row shifts 1, 2, 4, 8, then
 // row broadcasts 15 and 31; 0 is the identity)
 __device__ __forceinline__ uint32_t seg_scan(uint32_t w) {
-  w = seg_combine(dpp_mov<0x111>(w), w);
-  w = seg_combine(dpp_mov<0x112>(w), w);
-  w = seg_combine(dpp_mov<0x114>(w), w);
-  w = seg_combine(dpp_mov<0x118>(w), w);
-  w = seg_combine(dpp_mov<0x142, 0xA>(w), w);
-  w = seg_combine(dpp_mov<0x143, 0xC>(w), w);
+  w = seg_step<0x111>(w);
+  w = seg_step<0x112>(w);
+  w = seg_step<0x114>(w);
+  w = seg_step<0x118>(w);
+  w = seg_step<0x142, 0xA>(w);
+  w = seg_step<0x143, 0xC>(w);
   return w;
 }
 
@@ -137,8 +148,9 @@ __device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, 
   return L;
 }
 
-template <bool CELL_LDS, bool DIAG>
-__global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
+// NIN: number of inner slew-axis points when fixed at compile time (-1: any)
+template <bool CELL_LDS, bool DIAG, int NIN>
+__global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   extern __shared__ __align__(16) unsigned char s_dyn[];
   __shared__ uint32_t st_lk[kNW][kB];  // batch events (lk) for the in-cycle walk
   __shared__ uint8_t st_gh[kNW][kB];   // run-start flags of the batch events
@@ -358,9 +370,22 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
         const uint32_t Sm = (r ? S1s : S0s) & smask;
         // slew segment on the cell's axis: inner points at or below the slew (Sec. 2.4.1, Fig. 2)
         uint32_t si = 0;
-        for (int j = 0; j < nthr; j += 4) {
-          const float4 th = thr_of(cell, j);
-          si += (sl >= th.x ? 1u : 0u) + (sl >= th.y ? 1u : 0u) + (sl >= th.z ? 1u : 0u) + (sl >= th.w ? 1u : 0u);
+        if constexpr (NIN >= 0) {
+          // NIN inner points, fully unrolled
+#pragma unroll
+          for (int j = 0; j < NIN; j += 4) {
+            const float4 th = thr_of(cell, j);
+            si += sl >= th.x ? 1u : 0u;
+            if (j + 1 < NIN) si += sl >= th.y ? 1u : 0u;
+            if (j + 2 < NIN) si += sl >= th.z ? 1u : 0u;
+            if (j + 3 < NIN) si += sl >= th.w ? 1u : 0u;
+          }
+        } else {
+          // padding points are +inf and never counted
+          for (int j = 0; j < nthr; j += 4) {
+            const float4 th = thr_of(cell, j);
+            si += (sl >= th.x ? 1u : 0u) + (sl >= th.y ? 1u : 0u) + (sl >= th.z ? 1u : 0u) + (sl >= th.w ? 1u : 0u);
+          }
         }
         const double2 aw = axw_of(cell, si);
         const double fa = ((double)sl - aw.x) * aw.y;
@@ -389,11 +414,11 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
         if (input && (r ? ow1 : ow0)) {
           const double dp = leak_of(lb + (Sm ^ ((r ? mk1 : mk0) & smask))) - leak_of(lb + Sm);
           if (dp != 0.0) {
-            const uint32_t blen = (last_chunk && cyc == lastc) ? a.last_len : T;
-            const double dpt = dp * tick;
-            contrib += dpt * (double)(blen - tic);
+            // rest of the event's bin (the flush corrects a partial last bin)
+            const double part = dp * tick * (double)(T - tic);
+            contrib += part;
+            e_lk += part;
             atomicAdd(&L.bb[cyc], dp);
-            e_lk += dpt * (tail - fma((double)cyc, Td, (double)tic));
           }
         }
         if (contrib != 0.0) atomicAdd(&L.bw[cyc], contrib);
@@ -444,8 +469,18 @@ __global__ __launch_bounds__(kNT) void k_fused(PassArgs a) {
         double v = 0.0;
         unsigned long long cn = 0ull;
         if (has_range && c < ncyc) {
-          const double len = (last_chunk && c == (int)lastc) ? (double)a.last_len : Td;
+          // leakage changes of earlier bins of the chunk; the changes of this
+          // bin reach t_max from the bin end on (its own part is in bw)
+          const bool partial = last_chunk && c == (int)lastc;
+          const double len = partial ? (double)a.last_len : Td;
           v = L.bw[c] + run * len * tick;
+          if (partial) {
+            const double fix = loc[u] * tick * (Td - (double)a.last_len);
+            v -= fix;
+            e_lk -= fix;
+          } else {
+            e_lk += loc[u] * tick * (tail - Td * (double)(c + 1));
+          }
           cn = L.bc[c];
           run += loc[u];
         }
@@ -589,14 +624,18 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
   const bool diag = a.evt_glitch || a.evt_state;
   const size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_thr, a.n_leak, cells);
   if (dyn > kLdsMax) return hipErrorInvalidValue;
-  if (cells && !diag)
-    hipLaunchKernelGGL((k_fused<true, false>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
-  else if (cells)
-    hipLaunchKernelGGL((k_fused<true, true>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
-  else if (!diag)
-    hipLaunchKernelGGL((k_fused<false, false>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
-  else
-    hipLaunchKernelGGL((k_fused<false, true>), dim3(grid_blocks), dim3(kNT), dyn, s, a);
+  const dim3 g(grid_blocks), t(kNT);
+  if (cells && !diag) {
+    if (a.n_slew == 7) hipLaunchKernelGGL((k_fused<true, false, 5>), g, t, dyn, s, a);
+    else if (a.n_slew == 8) hipLaunchKernelGGL((k_fused<true, false, 6>), g, t, dyn, s, a);
+    else hipLaunchKernelGGL((k_fused<true, false, -1>), g, t, dyn, s, a);
+  } else if (cells) {
+    hipLaunchKernelGGL((k_fused<true, true, -1>), g, t, dyn, s, a);
+  } else if (!diag) {
+    hipLaunchKernelGGL((k_fused<false, false, -1>), g, t, dyn, s, a);
+  } else {
+    hipLaunchKernelGGL((k_fused<false, true, -1>), g, t, dyn, s, a);
+  }
   return hipGetLastError();
 }
 
