@@ -254,27 +254,45 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   HIPCHK(hipMemcpyAsync(d.lut.p, lut_J, sizeof(double) * lb, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipMemcpyAsync(d.leak.p, leak_W, sizeof(double) * kb, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipMemcpyAsync(cap_axis_d.p, hca.data(), sizeof(double) * hca.size(), hipMemcpyHostToDevice, s));
+  // internal gate order: sorted by cell (stable), so that the gates of a
+  // wave's events mostly share a cell and their LUT rows share cache lines;
+  // pins keep the caller's numbering
+  std::vector<int32_t> gcell(G);
+  if (G > 0) HIPCHK(hipMemcpyAsync(gcell.data(), gate_cell, sizeof(int32_t) * G, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  std::vector<int64_t> cstart(n_cells + 1, 0);
+  for (int64_t g = 0; g < G; ++g) {
+    if (gcell[g] < 0 || gcell[g] >= n_cells) return fail(PA_EDATA, "pa_load_design: gate cell id out of range");
+    ++cstart[gcell[g] + 1];
+  }
+  for (int32_t i = 0; i < n_cells; ++i) cstart[i + 1] += cstart[i];
+  std::vector<int32_t> perm(G);  // internal gate -> caller gate
+  for (int64_t g = 0; g < G; ++g) perm[cstart[gcell[g]]++] = (int32_t)g;
+  std::vector<int64_t> pbc(G + 1), pb(G + 1);  // first caller pin of every caller / internal gate
+  pbc[0] = 0;
+  for (int64_t g = 0; g < G; ++g) pbc[g + 1] = pbc[g] + hk[gcell[g]] + 1;
+  for (int64_t i = 0; i < G; ++i) pb[i] = pbc[perm[i]];
+  pb[G] = pbc[G];
+  d.P = pbc[G];
+  DBuf perm_d;
+  HIPCHK(perm_d.alloc(sizeof(int32_t) * G));
+  if (G > 0) HIPCHK(hipMemcpyAsync(perm_d.p, perm.data(), sizeof(int32_t) * G, hipMemcpyHostToDevice, s));
   HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
   if (G > 0)
-    HIPCHK(pa::launch_gate_tables(G, gate_cell, gate_cap_F, n_cells, d.cell_k.as<int32_t>(), cap_axis_d.as<double>(),
-                                  n_cap, vdd_V, d.gate_info.as<uint32_t>(), d.gate_cw.as<double2>(),
-                                  d.gate_k.as<int32_t>(), err.as<uint32_t>(), s));
-  std::vector<int32_t> gk(G);
+    HIPCHK(pa::launch_gate_tables(G, perm_d.as<int32_t>(), gate_cell, gate_cap_F, n_cells, d.cell_k.as<int32_t>(),
+                                  cap_axis_d.as<double>(), n_cap, vdd_V, d.gate_info.as<uint32_t>(),
+                                  d.gate_cw.as<double2>(), d.gate_k.as<int32_t>(), err.as<uint32_t>(), s));
   uint32_t herr = 0;
-  if (G > 0) HIPCHK(hipMemcpyAsync(gk.data(), d.gate_k.p, sizeof(int32_t) * G, hipMemcpyDeviceToHost, s));
   HIPCHK(hipMemcpyAsync(&herr, err.p, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
   if (herr & pa::ERR_CELL_ID) return fail(PA_EDATA, "pa_load_design: gate cell id out of range");
   if (herr & pa::ERR_CAP) return fail(PA_EDATA, "pa_load_design: gate load not finite");
-  std::vector<int64_t> pb(G + 1);
-  pb[0] = 0;
-  for (int64_t g = 0; g < G; ++g) pb[g + 1] = pb[g] + gk[g] + 1;
-  d.P = pb[G];
   HIPCHK(hipMemcpyAsync(d.pin_base.p, pb.data(), sizeof(int64_t) * (G + 1), hipMemcpyHostToDevice, s));
   HIPCHK(d.pin_gate.alloc(sizeof(int32_t) * d.P));
   HIPCHK(d.pin_local.alloc(sizeof(uint8_t) * d.P));
   if (G > 0)
-    HIPCHK(pa::launch_pin_owner(G, d.pin_base.as<int64_t>(), d.pin_gate.as<int32_t>(), d.pin_local.as<uint8_t>(), s));
+    HIPCHK(pa::launch_pin_owner(G, d.pin_base.as<int64_t>(), d.gate_k.as<int32_t>(), d.pin_gate.as<int32_t>(),
+                                d.pin_local.as<uint8_t>(), s));
   HIPCHK(hipStreamSynchronize(s));
 
   c->d = std::move(d);
@@ -414,8 +432,8 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
     // ---- density-aware window level per gate
     DBuf level;
     HIPCHK(level.alloc(G));
-    HIPCHK(pa::launch_gate_levels(G, d.pin_base.as<int64_t>(), pin_ptr, v.C, (int32_t)Cc, (int32_t)lc, 32.0,
-                                  level.as<uint8_t>(), s));
+    HIPCHK(pa::launch_gate_levels(G, d.pin_base.as<int64_t>(), d.gate_k.as<int32_t>(), pin_ptr, v.C, (int32_t)Cc,
+                                  (int32_t)lc, 32.0, level.as<uint8_t>(), s));
     // ---- order (chunk, gate, cycle, pin, time) by radix sort
     DBuf k0, k1, idx, perm, tmp;
     size_t tmp_bytes = 0;

@@ -31,18 +31,18 @@ struct LayoutFmt {
   uint32_t gb;   // gate-id bits of the sort key
 };
 
-hipError_t launch_gate_tables(int64_t G, const int32_t *gate_cell, const double *gate_cap, int32_t n_cells,
-                              const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
+hipError_t launch_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,
+                              int32_t n_cells, const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
                               uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err, hipStream_t s);
-hipError_t launch_pin_owner(int64_t G, const int64_t *pin_base, int32_t *pin_gate, uint8_t *pin_local,
-                            hipStream_t s);
+hipError_t launch_pin_owner(int64_t G, const int64_t *pin_base, const int32_t *gate_k, int32_t *pin_gate,
+                            uint8_t *pin_local, hipStream_t s);
 hipError_t launch_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err,
                             hipStream_t s);
 hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init,
                               const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_max,
                               uint32_t *ev_pin, uint32_t *err, hipStream_t s);
-hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int64_t *pin_ptr, int64_t C, int32_t Cc,
-                              int32_t lc, double target, uint8_t *level, hipStream_t s);
+hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int32_t *gate_k, const int64_t *pin_ptr,
+                              int64_t C, int32_t Cc, int32_t lc, double target, uint8_t *level, hipStream_t s);
 // chunk == nullptr: one 64-bit key (chunk, gate, lk); else key = (gate, lk) and chunk[e] apart
 hipError_t launch_sort_keys(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
                             const uint8_t *pin_local, const int32_t *gate_k, const LayoutFmt &f, uint64_t *key,

@@ -36,12 +36,13 @@ inline int grid_for(int64_t n) {
 
 // ------------------------------------------------------------------ design
 
-__global__ void k_gate_tables(int64_t G, const int32_t *gate_cell, const double *gate_cap, int32_t n_cells,
-                              const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
+// per internal gate g (caller gate perm[g])
+__global__ void k_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,
+                              int32_t n_cells, const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
                               uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err) {
   for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
-    const int32_t cell = gate_cell[g];
-    const double cap = gate_cap[g];
+    const int32_t cell = gate_cell[perm[g]];
+    const double cap = gate_cap[perm[g]];
     if (cell < 0 || cell >= n_cells) {
       atomicOr(err, ERR_CELL_ID);
       gate_k[g] = 0;
@@ -57,10 +58,11 @@ __global__ void k_gate_tables(int64_t G, const int32_t *gate_cell, const double 
   }
 }
 
-// pin -> (gate, local index) from the gate pin bases
-__global__ void k_pin_owner(int64_t G, const int64_t *pin_base, int32_t *pin_gate, uint8_t *pin_local) {
+// pin -> (internal gate, local index) from the gates' first pins
+__global__ void k_pin_owner(int64_t G, const int64_t *pin_base, const int32_t *gate_k, int32_t *pin_gate,
+                            uint8_t *pin_local) {
   for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t p0 = pin_base[g], p1 = pin_base[g + 1];
+    const int64_t p0 = pin_base[g], p1 = p0 + gate_k[g] + 1;
     for (int64_t p = p0; p < p1; ++p) {
       pin_gate[p] = (int32_t)g;
       pin_local[p] = (uint8_t)(p - p0);
@@ -106,10 +108,10 @@ __global__ void k_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
 // (the paper sizes its per-gate windows to a target event count per thread;
 // here the chunk is the upper bound on a window, which plays the part of its
 // parallelism floor).
-__global__ void k_gate_levels(int64_t G, const int64_t *pin_base, const int64_t *pin_ptr, int64_t C, int32_t Cc,
-                              int32_t lc, double target, uint8_t *level) {
+__global__ void k_gate_levels(int64_t G, const int64_t *pin_base, const int32_t *gate_k, const int64_t *pin_ptr,
+                              int64_t C, int32_t Cc, int32_t lc, double target, uint8_t *level) {
   for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
-    const double n_evt = (double)(pin_ptr[pin_base[g + 1]] - pin_ptr[pin_base[g]]);
+    const double n_evt = (double)(pin_ptr[pin_base[g] + gate_k[g] + 1] - pin_ptr[pin_base[g]]);
     const double rho = n_evt / (double)C;
     int sl = 0;
     while (sl < lc && rho * (double)(Cc >> sl) > target) ++sl;
@@ -228,17 +230,17 @@ __global__ void k_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted,
 
 // ------------------------------------------------------------- launchers
 
-hipError_t launch_gate_tables(int64_t G, const int32_t *gate_cell, const double *gate_cap, int32_t n_cells,
-                              const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
+hipError_t launch_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,
+                              int32_t n_cells, const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
                               uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err, hipStream_t s) {
-  hipLaunchKernelGGL(k_gate_tables, dim3(grid_for(G)), dim3(kLT), 0, s, G, gate_cell, gate_cap, n_cells, cell_k,
+  hipLaunchKernelGGL(k_gate_tables, dim3(grid_for(G)), dim3(kLT), 0, s, G, perm, gate_cell, gate_cap, n_cells, cell_k,
                      cap_axis, n_cap, vdd, gate_info, gate_cw, gate_k, err);
   return hipGetLastError();
 }
 
-hipError_t launch_pin_owner(int64_t G, const int64_t *pin_base, int32_t *pin_gate, uint8_t *pin_local,
-                            hipStream_t s) {
-  hipLaunchKernelGGL(k_pin_owner, dim3(grid_for(G)), dim3(kLT), 0, s, G, pin_base, pin_gate, pin_local);
+hipError_t launch_pin_owner(int64_t G, const int64_t *pin_base, const int32_t *gate_k, int32_t *pin_gate,
+                            uint8_t *pin_local, hipStream_t s) {
+  hipLaunchKernelGGL(k_pin_owner, dim3(grid_for(G)), dim3(kLT), 0, s, G, pin_base, gate_k, pin_gate, pin_local);
   return hipGetLastError();
 }
 
@@ -256,9 +258,10 @@ hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
   return hipGetLastError();
 }
 
-hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int64_t *pin_ptr, int64_t C, int32_t Cc,
-                              int32_t lc, double target, uint8_t *level, hipStream_t s) {
-  hipLaunchKernelGGL(k_gate_levels, dim3(grid_for(G)), dim3(kLT), 0, s, G, pin_base, pin_ptr, C, Cc, lc, target, level);
+hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int32_t *gate_k, const int64_t *pin_ptr,
+                              int64_t C, int32_t Cc, int32_t lc, double target, uint8_t *level, hipStream_t s) {
+  hipLaunchKernelGGL(k_gate_levels, dim3(grid_for(G)), dim3(kLT), 0, s, G, pin_base, gate_k, pin_ptr, C, Cc, lc, target,
+                     level);
   return hipGetLastError();
 }
 
