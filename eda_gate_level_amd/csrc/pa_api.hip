@@ -421,8 +421,13 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   const uint32_t qbits = bits_for((uint64_t)std::max<int32_t>(v.Q - 1, 0));
   const int32_t Q = v.Q;
 
-  HIPCHK(v.key.alloc(sizeof(uint64_t) * E));
-  HIPCHK(v.slew.alloc(sizeof(float) * E));
+  // two zeroed entries past the events (even count): the pass fetches event
+  // pairs without a bounds branch
+  const int64_t Ea = (E + 2) & ~int64_t(1);
+  HIPCHK(v.key.alloc(sizeof(uint64_t) * Ea));
+  HIPCHK(v.slew.alloc(sizeof(float) * Ea));
+  HIPCHK(hipMemsetAsync(v.key.as<uint64_t>() + E, 0, sizeof(uint64_t) * (Ea - E), s));
+  HIPCHK(hipMemsetAsync(v.slew.as<float>() + E, 0, sizeof(float) * (Ea - E), s));
   HIPCHK(v.orig.alloc(sizeof(uint32_t) * E));
   HIPCHK(v.pin_init.alloc(P));
   DBuf chunk_sorted, cbase;

@@ -168,11 +168,12 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
     if constexpr (CELL_LDS) return L.meta[c]; else return a.cell_meta[c];
   };
   auto thr_of = [&](uint32_t c, int j) -> float4 {
-    if constexpr (CELL_LDS) return *reinterpret_cast<const float4 *>(L.thr + (size_t)c * nthr + j);
-    else return *reinterpret_cast<const float4 *>(a.cell_thr + (size_t)c * nthr + j);
+    // cells < 2^24 and short axes: every offset here is a full-rate 24-bit product
+    if constexpr (CELL_LDS) return *reinterpret_cast<const float4 *>(L.thr + __umul24(c, nthr) + j);
+    else return *reinterpret_cast<const float4 *>(a.cell_thr + __umul24(c, nthr) + j);
   };
   auto axw_of = [&](uint32_t c, uint32_t j) -> double2 {
-    if constexpr (CELL_LDS) return L.axw[c * (uint32_t)(ns - 1) + j]; else return a.cell_axw[(size_t)c * (ns - 1) + j];
+    if constexpr (CELL_LDS) return L.axw[__umul24(c, ns - 1) + j]; else return a.cell_axw[__umul24(c, ns - 1) + j];
   };
   auto leak_of = [&](uint32_t j) -> double {
     if constexpr (CELL_LDS) return L.leak[j]; else return a.leak[j];
@@ -390,7 +391,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         const double2 aw = axw_of(cell, si);
         const double fa = ((double)sl - aw.x) * aw.y;
         const uint32_t cl = input ? code : 0u;
-        const double *Lp = a.lut + (m.y + ((Sm * kk + cl) * (uint32_t)ns + si) * (uint32_t)nc + (info >> 24));
+        const double *Lp = a.lut + (m.y + __umul24(__umul24(__umul24(Sm, kk) + cl, ns) + si, nc) + (info >> 24));
         const double L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
         const double v0 = L00 + cw.x * (L01 - L00);
         const double v1 = L10 + cw.x * (L11 - L10);
@@ -437,7 +438,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   // ---- the block's bins: in-chunk prefix of the leakage changes, then its own slots
   double dsum = 0.0;
   {
-    constexpr int PER = kCCMAX / kNT > 0 ? kCCMAX / kNT : 1;
+    constexpr int PER = (kCCMAX + kNT - 1) / kNT;
     double loc[PER];
     double s = 0.0;
 #pragma unroll
@@ -514,41 +515,91 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   }
 }
 
-constexpr int kFT = 256;
+constexpr int kFC = 64;             // finalize: cycles per block (one per lane)
+constexpr int kFP = 8;              // finalize: waves per block, each adding up a share of the blocks
+constexpr int kFT = kFC * kFP;
 
-__device__ double block_sum(double v, double *s_red) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  v = wave_sum(v);
-  __syncthreads();
-  if (lane == 0) s_red[wid] = v;
-  __syncthreads();
-  double t = 0.0;
-  for (int w = 0; w < kFT / 64; ++w) t += s_red[w];
-  return t;
-}
-
-// One thread per cycle: adds up the blocks' bins of the cycle's chunk and the
-// leakage carried into the chunk (L0 plus the changes of earlier chunks);
-// block 0 also adds up the totals (Eq. 3).
+// Lane l of wave p adds up, for cycle l of the block's 64, the bins of the
+// p-th share of the cycle's chunk's blocks; the waves also share the sums over
+// all blocks' totals.  Wave 0 then adds the shares in order after the leakage
+// carried into the chunk (L0 plus the changes of earlier chunks); block 0 also
+// writes the totals (Eq. 3).  Every sum runs in a fixed order, and every loop
+// keeps eight independent loads in flight.
 __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
-  __shared__ double s_red[kFT / 64];
-  __shared__ double s_P[kFT];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int64_t c0 = (int64_t)blockIdx.x * kFT;
-  const int64_t chi = min(c0 + kFT, f.C) - 1;
+  __shared__ double s_w[kFP][kFC];
+  __shared__ unsigned long long s_n[kFP][kFC];
+  __shared__ double s_t[kFP][8];
+  const int lane = threadIdx.x & 63, wp = threadIdx.x >> 6;
+  const int64_t c0 = (int64_t)blockIdx.x * kFC;
+  const int64_t chi = min(c0 + kFC, f.C) - 1;
+  const int64_t c = c0 + lane;
   const int qa = (int)(c0 / f.Cc), qb = (int)(chi / f.Cc);
+  const int q = (int)(min(c, chi) / f.Cc);
   const uint32_t ba = f.chunk_blk[qa];
-  double l0 = 0.0, pre = 0.0;
-  for (int bb = tid; bb < f.grid; bb += kFT) {
-    l0 += f.blk_part[(size_t)bb * 8 + 4];
-    if ((uint32_t)bb < ba) pre += f.blk_part[(size_t)bb * 8 + 5];
+  const bool totals = blockIdx.x == 0;
+  {
+    // this wave's share of the cycle's chunk's blocks
+    const uint32_t b0 = f.chunk_blk[q], b1 = f.chunk_blk[q + 1];
+    const uint32_t n = b1 - b0, s0 = b0 + n * wp / kFP, s1 = b0 + n * (wp + 1) / kFP;
+    const int cin = (int)(min(c, chi) - (int64_t)q * f.Cc);
+    double w = 0.0;
+    unsigned long long cnt = 0;
+    for (uint32_t bb = s0; bb < s1; bb += 8) {
+      double v[8];
+      unsigned long long m[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool ok = bb + u < s1;
+        v[u] = ok ? f.blk_wave[(size_t)(bb + u) * f.Cc + cin] : 0.0;
+        m[u] = ok ? f.blk_cnt[(size_t)(bb + u) * f.Cc + cin] : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        w += v[u];
+        cnt += m[u];
+      }
+    }
+    s_w[wp][lane] = w;
+    s_n[wp][lane] = cnt;
+    // this wave's share of the blocks' totals: L0, the changes before chunk qa, and (block 0) the energies
+    double t[7] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    for (int b8 = wp * 64 * 8; b8 < f.grid; b8 += kFT * 8) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int bb = b8 + u * 64 + lane;
+        if (bb < f.grid) {
+          const double *pp = f.blk_part + (size_t)bb * 8;
+          t[0] += pp[4];
+          if ((uint32_t)bb < ba) t[1] += pp[5];
+          if (totals) {
+            t[2] += pp[0];
+            t[3] += pp[1];
+            t[4] += pp[2];
+            t[5] += pp[3];
+            t[6] += pp[6];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 7; ++u) t[u] = wave_sum(t[u]);
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < 7; ++u) s_t[wp][u] = t[u];
+    }
   }
-  l0 = block_sum(l0, s_red);
-  pre = block_sum(pre, s_red);
-  // leakage change inside every covered chunk, then their exclusive prefix
+  __syncthreads();
+  if (wp != 0) return;
+  double l0 = 0.0, pre = 0.0;
+#pragma unroll
+  for (int p = 0; p < kFP; ++p) {
+    l0 += s_t[p][0];
+    pre += s_t[p][1];
+  }
+  // the changes inside chunks qa .. qb-1 (qb - qa < 64), then their exclusive prefix
   double dq = 0.0;
-  if (tid <= qb - qa) {
-    const uint32_t b0 = f.chunk_blk[qa + tid], b1 = f.chunk_blk[qa + tid + 1];
+  if (lane < qb - qa) {
+    const uint32_t b0 = f.chunk_blk[qa + lane], b1 = f.chunk_blk[qa + lane + 1];
     for (uint32_t bb = b0; bb < b1; ++bb) dq += f.blk_part[(size_t)bb * 8 + 5];
   }
   double incl = dq;
@@ -556,52 +607,36 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
     const double v = __shfl_up(incl, o, 64);
     if (lane >= o) incl += v;
   }
-  __syncthreads();
-  if (lane == 63) s_red[wid] = incl;
-  __syncthreads();
-  double wb = 0.0;
-  for (int w = 0; w < wid; ++w) wb += s_red[w];
-  s_P[tid] = l0 + pre + wb + incl - dq;
-  __syncthreads();
-  const int64_t c = c0 + tid;
+  const double Pj = l0 + pre + (incl - dq);  // power carried into chunk qa + lane
+  const double Pq = __shfl(Pj, q - qa, 64);
   if (c < f.C) {
-    const int q = (int)(c / f.Cc);
-    const int cin = (int)(c - (int64_t)q * f.Cc);
     const double len = (c == f.C - 1) ? (double)f.last_len : (double)f.T;
-    double w = s_P[q - qa] * len * f.tick_s;
+    double w = Pq * len * f.tick_s;
     unsigned long long cnt = 0;
-    const uint32_t b0 = f.chunk_blk[q], b1 = f.chunk_blk[q + 1];
-    for (uint32_t bb = b0; bb < b1; ++bb) {
-      w += f.blk_wave[(size_t)bb * f.Cc + cin];
-      cnt += f.blk_cnt[(size_t)bb * f.Cc + cin];
+#pragma unroll
+    for (int p = 0; p < kFP; ++p) {
+      w += s_w[p][lane];
+      cnt += s_n[p][lane];
     }
     f.wave_out[c] = w;
     f.cyc_events[c] = cnt & 0xFFFFFFFFull;
     f.cyc_glitches[c] = cnt >> 32;
   }
-  if (blockIdx.x == 0) {
+  if (totals && lane == 0) {
     double t[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-    for (int bb = tid; bb < f.grid; bb += kFT) {
-      t[0] += f.blk_part[(size_t)bb * 8 + 0];
-      t[1] += f.blk_part[(size_t)bb * 8 + 1];
-      t[2] += f.blk_part[(size_t)bb * 8 + 2];
-      t[3] += f.blk_part[(size_t)bb * 8 + 3];
-      t[4] += f.blk_part[(size_t)bb * 8 + 6];
-    }
-    for (int u = 0; u < 5; ++u) t[u] = block_sum(t[u], s_red);
-    if (tid == 0) {
-      const double window = (double)f.t_max * f.tick_s;
-      const double e_leak = l0 * window + t[3];
-      f.res[0] = t[0];
-      f.res[1] = t[1];
-      f.res[2] = t[2];
-      f.res[3] = e_leak;
-      f.res[4] = t[0] / window;  // Eq. 3
-      f.res[5] = t[1] / window;
-      f.res[6] = t[2] / window;
-      f.res[7] = e_leak / window;
-      f.res[8] = t[4];
-    }
+    for (int p = 0; p < kFP; ++p)
+      for (int u = 0; u < 5; ++u) t[u] += s_t[p][2 + u];
+    const double window = (double)f.t_max * f.tick_s;
+    const double e_leak = l0 * window + t[3];
+    f.res[0] = t[0];
+    f.res[1] = t[1];
+    f.res[2] = t[2];
+    f.res[3] = e_leak;
+    f.res[4] = t[0] / window;  // Eq. 3
+    f.res[5] = t[1] / window;
+    f.res[6] = t[2] / window;
+    f.res[7] = e_leak / window;
+    f.res[8] = t[4];
   }
 }
 
@@ -640,7 +675,7 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
 }
 
 hipError_t launch_finalize(const FinalArgs &f, hipStream_t s) {
-  const int grid = (int)((f.C + kFT - 1) / kFT);
+  const int grid = (int)((f.C + kFC - 1) / kFC);
   hipLaunchKernelGGL(k_finalize, dim3(grid), dim3(kFT), 0, s, f);
   return hipGetLastError();
 }
