@@ -302,10 +302,16 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       uint32_t S1s = hd1 ? (h1 & 0xFFu) : (I0 & 0xFFu);
       carry = (uint32_t)__builtin_amdgcn_readlane((int)I, (end - 1) >> 1);
 
-      // ---- runs of one gate in one cycle with several events: time order across pins
+      // ---- runs of one gate in one cycle with input events on several pins:
+      // time order across pins.  Runs are pin-major with the output last, so
+      // such a run has two adjacent input events on different pins; without
+      // one the defaults below hold for every event of the batch.
       uint32_t mk0 = 1u << c0, mk1 = 1u << c1;  // input pins switching at the event's timestamp
       bool ow0 = true, ow1 = true;              // lowest of them: charges the leakage change
-      if ((__ballot(a0 && !gh0) | __ballot(a1 && !gh1)) != 0ull) {
+      const uint32_t cp0 = (lkp0 >> tb) & outc;  // pin code of the event before slot i0
+      const bool dw0 = a0 && in0 && !gh0 && cp0 != outc && cp0 != c0;
+      const bool dw1 = a1 && in1 && !gh1 && in0 && c0 != c1;
+      if (__ballot(dw0 || dw1) != 0ull) {
         slk[i0] = lk0;
         slk[i1] = lk1;
         sgh[i0] = (uint8_t)(gh0 || i0 >= end);
