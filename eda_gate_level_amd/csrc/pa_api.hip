@@ -87,11 +87,13 @@ struct Events {
   DBuf key, slew, orig, pin_init;
   std::vector<uint32_t> h_chunk_base;
   DBuf rstart, rchunk, chunk_blk;  // block ranges of the pass, first block of every chunk
+  DBuf wbound, l0;                 // the waves' ranges of every block; leakage power at t = 0
   int32_t n_ranges = 0, grid = 1;
   DBuf blk_wave, blk_cnt, blk_part, res;
   int64_t bytes() const {
     return (int64_t)(key.bytes + slew.bytes + orig.bytes + pin_init.bytes + rstart.bytes + rchunk.bytes +
-                     chunk_blk.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes + res.bytes);
+                     chunk_blk.bytes + wbound.bytes + l0.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
+                     res.bytes);
   }
 };
 
@@ -336,6 +338,18 @@ static int build_ranges(pa_ctx *c, Events &v) {
   HIPCHK(hipMemcpyAsync(v.rstart.p, rs.data(), sizeof(uint32_t) * rs.size(), hipMemcpyHostToDevice, c->stream));
   HIPCHK(hipMemcpyAsync(v.rchunk.p, rq.data(), sizeof(uint32_t) * rq.size(), hipMemcpyHostToDevice, c->stream));
   HIPCHK(hipMemcpyAsync(v.chunk_blk.p, cb.data(), sizeof(uint32_t) * cb.size(), hipMemcpyHostToDevice, c->stream));
+  // the cuts between every block's waves, moved to window heads
+  HIPCHK(v.wbound.alloc(sizeof(int32_t) * (size_t)v.grid * pa::pass_wave_bounds_per_block()));
+  HIPCHK(pa::launch_wave_bounds(v.key.as<uint64_t>(), v.E, v.rstart.as<uint32_t>(), v.n_ranges,
+                                v.wbound.as<int32_t>(), c->stream));
+  // leakage power at t = 0, from the initial pin values
+  const Design &d = c->d;
+  DBuf part;
+  HIPCHK(part.alloc(sizeof(double) * pa::leak0_parts()));
+  HIPCHK(v.l0.alloc(sizeof(double)));
+  HIPCHK(pa::launch_leak0(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
+                          d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), part.as<double>(), v.l0.as<double>(),
+                          c->stream));
   HIPCHK(hipStreamSynchronize(c->stream));
   return PA_OK;
 }
@@ -506,7 +520,7 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   a.key = v.key.as<uint64_t>();
   a.slew = v.slew.as<float>();
   a.orig = v.orig.as<uint32_t>();
-  a.rstart = v.rstart.as<uint32_t>();
+  a.wbound = v.wbound.as<int32_t>();
   a.rchunk = v.rchunk.as<uint32_t>();
   a.n_ranges = v.n_ranges;
   a.E = v.E;
@@ -551,6 +565,7 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   f.tick_s = v.tick_s;
   f.grid = v.grid;
   f.chunk_blk = v.chunk_blk.as<uint32_t>();
+  f.l0 = v.l0.as<double>();
   f.blk_wave = a.blk_wave;
   f.blk_cnt = a.blk_cnt;
   f.blk_part = a.blk_part;

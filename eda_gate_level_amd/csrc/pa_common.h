@@ -53,7 +53,7 @@ struct PassArgs {
   const uint64_t *key;
   const float *slew;
   const uint32_t *orig;    // caller's CSR index of each laid-out event
-  const uint32_t *rstart;  // [n_ranges+1] nominal starts of the block ranges (inside one chunk each)
+  const int32_t *wbound;   // [n_ranges][waves+1] the waves' ranges of every block, cut at window heads
   const uint32_t *rchunk;  // [n_ranges] chunk of each range
   int32_t n_ranges;
   int64_t E;
@@ -99,6 +99,7 @@ struct FinalArgs {
   const double *blk_wave;
   const unsigned long long *blk_cnt;
   const double *blk_part;
+  const double *l0;           // leakage power at t = 0, summed at load
   double *wave_out;
   uint64_t *cyc_events;
   uint64_t *cyc_glitches;
@@ -108,6 +109,11 @@ struct FinalArgs {
 // Launchers (defined in pa_pass.hip).
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s);
 hipError_t launch_finalize(const FinalArgs &a, hipStream_t s);
+// the waves' ranges of every block: nominal cuts rstart[b] + (rstart[b+1] - rstart[b]) * w / waves
+// moved to the next window head; wb holds pass_wave_bounds_per_block() entries per block
+hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rstart, int32_t n_ranges, int32_t *wb,
+                              hipStream_t s);
+int pass_wave_bounds_per_block();
 int pass_block_threads();
 int pass_wave_batch();
 int pass_max_chunk_cycles();

@@ -230,6 +230,50 @@ __global__ void k_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted,
 
 // ------------------------------------------------------------- launchers
 
+// Leakage power at t = 0 (every gate in its initial input state), in two
+// fixed-order steps: kL0B partial sums, then their sum.
+constexpr int kL0B = 256;
+
+__global__ __launch_bounds__(kLT) void k_leak0_part(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta,
+                                                     const double *leak, const int64_t *pin_base,
+                                                     const uint8_t *pin_init, double *part) {
+  __shared__ double s_w[kLT / 64];
+  double l = 0.0;
+  for (int64_t g = blockIdx.x * (int64_t)kLT + threadIdx.x; g < G; g += (int64_t)kL0B * kLT) {
+    const uint2 m = cell_meta[gate_info[g] & 0xFFFFFFu];
+    const int k = (int)(m.x & 15u);
+    const int64_t p0 = pin_base[g];
+    uint32_t S = 0;
+    for (int j = 0; j < k; ++j) S |= uint32_t(pin_init[p0 + j]) << j;
+    l += leak[(m.x >> 4) + S];
+  }
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+  if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = l;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int w = 0; w < kLT / 64; ++w) t += s_w[w];
+    part[blockIdx.x] = t;
+  }
+}
+
+__global__ void k_leak0_sum(const double *part, double *l0) {
+  if (threadIdx.x == 0 && blockIdx.x == 0) {
+    double t = 0.0;
+    for (int i = 0; i < kL0B; ++i) t += part[i];
+    *l0 = t;
+  }
+}
+
+hipError_t launch_leak0(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
+                        const int64_t *pin_base, const uint8_t *pin_init, double *part, double *l0, hipStream_t s) {
+  hipLaunchKernelGGL(k_leak0_part, dim3(kL0B), dim3(kLT), 0, s, G, gate_info, cell_meta, leak, pin_base, pin_init,
+                     part);
+  hipLaunchKernelGGL(k_leak0_sum, dim3(1), dim3(64), 0, s, part, l0);
+  return hipGetLastError();
+}
+int leak0_parts() { return kL0B; }
+
 hipError_t launch_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,
                               int32_t n_cells, const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
                               uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err, hipStream_t s) {

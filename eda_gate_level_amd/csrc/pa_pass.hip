@@ -154,7 +154,6 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   extern __shared__ __align__(16) unsigned char s_dyn[];
   __shared__ uint32_t st_lk[kNW][kB];  // batch events (lk) for the in-cycle walk
   __shared__ uint8_t st_gh[kNW][kB];   // run-start flags of the batch events
-  __shared__ int s_bounds[kNW + 1];
   __shared__ double s_red[kNW][8];
   __shared__ double s_scan[kNW];
 
@@ -179,18 +178,27 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
     if constexpr (CELL_LDS) return L.leak[j]; else return a.leak[j];
   };
 
-  // ---- the block's range (inside one chunk) and its waves' sub-ranges, all cut at window heads
-  int q = 0;
+  // ---- the block's chunk and this wave's range (cut at window heads at load);
+  // the first batch is fetched before the tables are staged
+  int q = 0, pos = 0, wend = 0;
   if (has_range) {
     q = (int)a.rchunk[b];
-    const int64_t r0 = a.rstart[b], r1 = a.rstart[b + 1];
-    for (int w = wid; w <= kNW; w += kNW) {
-      const int h = find_head(a.key, a.E, r0 + (r1 - r0) * w / kNW);
-      if (lane == 0) s_bounds[w] = h;
-    }
-  } else if (tid <= kNW) {
-    s_bounds[tid] = 0;
+    pos = a.wbound[b * (kNW + 1) + wid];
+    wend = a.wbound[b * (kNW + 1) + wid + 1];
   }
+  u64x2 kp = {0ull, 0ull};
+  f32x2 sp = {0.f, 0.f};
+  auto load_batch = [&](int p) {
+    const int x0 = (p & ~1) + 2 * lane;
+    if (x0 + 1 < wend) {
+      kp = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x0));
+      sp = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x0));
+    } else if (x0 < wend) {
+      kp = u64x2{__builtin_nontemporal_load(a.key + x0), 0ull};
+      sp = f32x2{__builtin_nontemporal_load(a.slew + x0), 0.f};
+    }
+  };
+  if (pos < wend) load_batch(pos);
   for (int c = tid; c < Cc; c += kNT) {
     L.bw[c] = 0.0;
     L.bb[c] = 0.0;
@@ -204,18 +212,8 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   }
   __syncthreads();
 
-  double e_int = 0.0, e_sw = 0.0, e_gl = 0.0, e_lk = 0.0, l0 = 0.0;
+  double e_int = 0.0, e_sw = 0.0, e_gl = 0.0, e_lk = 0.0;
   unsigned n_gl = 0;
-
-  // ---- leakage at t = 0: sum over gates of leak[S0] (Sec. 2.4.2, Fig. 3)
-  for (int64_t g = (int64_t)b * kNT + tid; g < a.G; g += (int64_t)nb * kNT) {
-    const uint2 m = meta_of(a.gate_info[g] & 0xFFFFFFu);
-    const int kk = (int)(m.x & 15u);
-    const int64_t p0 = a.pin_base[g];
-    uint32_t S = 0;
-    for (int j = 0; j < kk; ++j) S |= uint32_t(a.pin_init[p0 + j]) << j;
-    l0 += leak_of((m.x >> 4) + S);
-  }
 
   const int64_t cstart = (int64_t)q * a.chunk_ticks;
   const int64_t clen = min(a.chunk_ticks, a.t_max - cstart);
@@ -231,22 +229,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   const uint32_t outc = (1u << pb) - 1u;
 
   if (has_range) {
-    const int wend = s_bounds[wid + 1];
-    int pos = s_bounds[wid];
     uint32_t carry = 0;
-    u64x2 kp = {0ull, 0ull};
-    f32x2 sp = {0.f, 0.f};
-    auto load_batch = [&](int p) {
-      const int x0 = (p & ~1) + 2 * lane;
-      if (x0 + 1 < wend) {
-        kp = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x0));
-        sp = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x0));
-      } else if (x0 < wend) {
-        kp = u64x2{__builtin_nontemporal_load(a.key + x0), 0ull};
-        sp = f32x2{__builtin_nontemporal_load(a.slew + x0), 0.f};
-      }
-    };
-    if (pos < wend) load_batch(pos);
     uint32_t *slk = st_lk[wid];
     uint8_t *sgh = st_gh[wid];
 
@@ -499,7 +482,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
 
   // ---- block totals
   {
-    double v[6] = {e_int, e_sw, e_gl, e_lk, l0, (double)n_gl};
+    double v[6] = {e_int, e_sw, e_gl, e_lk, 0.0, (double)n_gl};
 #pragma unroll
     for (int u = 0; u < 6; ++u) v[u] = wave_sum(v[u]);
     if (lane == 0) {
@@ -518,6 +501,16 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       }
       a.blk_part[(size_t)b * 8 + tid] = t;
     }
+  }
+}
+
+// One wave per block range: the cuts between the block's waves, moved to window heads.
+__global__ __launch_bounds__(64) void k_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rstart,
+                                                     int32_t *wb) {
+  const int64_t r0 = rstart[blockIdx.x], r1 = rstart[blockIdx.x + 1];
+  for (int w = 0; w <= kNW; ++w) {
+    const int h = find_head(key, E, r0 + (r1 - r0) * w / kNW);
+    if (threadIdx.x == 0) wb[(size_t)blockIdx.x * (kNW + 1) + w] = h;
   }
 }
 
@@ -575,7 +568,6 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
         const int bb = b8 + u * 64 + lane;
         if (bb < f.grid) {
           const double *pp = f.blk_part + (size_t)bb * 8;
-          t[0] += pp[4];
           if ((uint32_t)bb < ba) t[1] += pp[5];
           if (totals) {
             t[2] += pp[0];
@@ -596,12 +588,10 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
   }
   __syncthreads();
   if (wp != 0) return;
-  double l0 = 0.0, pre = 0.0;
+  const double l0 = *f.l0;
+  double pre = 0.0;
 #pragma unroll
-  for (int p = 0; p < kFP; ++p) {
-    l0 += s_t[p][0];
-    pre += s_t[p][1];
-  }
+  for (int p = 0; p < kFP; ++p) pre += s_t[p][1];
   // the changes inside chunks qa .. qb-1 (qb - qa < 64), then their exclusive prefix
   double dq = 0.0;
   if (lane < qb - qa) {
@@ -649,6 +639,14 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
 }  // namespace
 
 int pass_block_threads() { return kNT; }
+int pass_wave_bounds_per_block() { return kNW + 1; }
+
+hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rstart, int32_t n_ranges, int32_t *wb,
+                              hipStream_t s) {
+  if (n_ranges <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_wave_bounds, dim3(n_ranges), dim3(64), 0, s, key, E, rstart, wb);
+  return hipGetLastError();
+}
 int pass_wave_batch() { return kB; }
 int pass_max_chunk_cycles() { return kCCMAX; }
 
