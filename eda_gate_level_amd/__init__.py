@@ -12,10 +12,11 @@ from __future__ import annotations
 from typing import Optional
 
 from ._pa import (EXPORTS, PA_EDATA, PA_EHIP, PA_EINVAL, PA_ENOMEM, PA_ESTATE, PA_OK, PaError, lib, pa_create,
-                  pa_destroy, pa_get_info, pa_last_error, pa_load_design, pa_load_events, pa_run, pa_set_stream)
+                  pa_destroy, pa_get_info, pa_last_error, pa_load_design, pa_load_events, pa_run, pa_set_stream,
+                  pa_set_timing)
 
-__all__ = ["PowerAnalysis", "PaError", "pa_create", "pa_destroy", "pa_set_stream", "pa_last_error", "pa_load_design",
-           "pa_load_events", "pa_run", "pa_get_info", "lib", "EXPORTS", "PA_OK", "PA_EINVAL", "PA_EDATA",
+__all__ = ["PowerAnalysis", "PaError", "pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error",
+           "pa_load_design", "pa_load_events", "pa_run", "pa_get_info", "lib", "EXPORTS", "PA_OK", "PA_EINVAL", "PA_EDATA",
            "PA_ENOMEM", "PA_EHIP", "PA_ESTATE"]
 
 
@@ -32,7 +33,7 @@ class PowerAnalysis:
     output tensors."""
 
     def __init__(self, device: int = 0, stream=None, chunk_cycles: int = 0, grid_blocks: int = 0,
-                 time_kernels: bool = False):
+                 time_kernels=0):
         import torch
 
         self.device = torch.device("cuda", device)
@@ -41,6 +42,10 @@ class PowerAnalysis:
         self.ctx = pa_create(device, stream, chunk_cycles, grid_blocks, time_kernels)
         self.n_cycles = 0
         self.n_events = 0
+
+    def set_timing(self, time_kernels: int) -> None:
+        """0: none; 1: fused, finalize and pass device times; 2: the pass only."""
+        pa_set_timing(self.ctx, time_kernels)
 
     def close(self):
         if getattr(self, "ctx", None):

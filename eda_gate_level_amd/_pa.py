@@ -19,8 +19,8 @@ PA_OK, PA_EINVAL, PA_EDATA, PA_ENOMEM, PA_EHIP, PA_ESTATE = 0, -1, -2, -3, -4, -
 _NAMES = {PA_EINVAL: "PA_EINVAL", PA_EDATA: "PA_EDATA", PA_ENOMEM: "PA_ENOMEM", PA_EHIP: "PA_EHIP",
           PA_ESTATE: "PA_ESTATE"}
 
-EXPORTS = ("pa_create", "pa_destroy", "pa_set_stream", "pa_last_error", "pa_load_design", "pa_load_events",
-           "pa_run", "pa_get_info")
+EXPORTS = ("pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error", "pa_load_design",
+           "pa_load_events", "pa_run", "pa_get_info")
 
 
 class PaError(RuntimeError):
@@ -66,13 +66,15 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.pa_destroy.argtypes = [P]
     L.pa_destroy.restype = None
     L.pa_set_stream.argtypes = [P, P]
+    L.pa_set_timing.argtypes = [P, i32]
     L.pa_last_error.restype = C.c_char_p
     L.pa_last_error.argtypes = []
     L.pa_load_design.argtypes = [P, i64, P, P, i32, P, i32, i32, P, P, P, P, dbl]
     L.pa_load_events.argtypes = [P, i64, i64, P, P, P, P, P, i64, i64, dbl]
     L.pa_run.argtypes = [P, C.POINTER(pa_totals), P, P, P, P, P]
     L.pa_get_info.argtypes = [P, C.POINTER(pa_info)]
-    for name in ("pa_create", "pa_set_stream", "pa_load_design", "pa_load_events", "pa_run", "pa_get_info"):
+    for name in ("pa_create", "pa_set_stream", "pa_set_timing", "pa_load_design", "pa_load_events", "pa_run",
+                 "pa_get_info"):
         getattr(L, name).restype = C.c_int
     return L
 
@@ -119,8 +121,8 @@ def _stream_handle(stream) -> C.c_void_p:
 
 
 def pa_create(device: int = 0, stream=None, chunk_cycles: int = 0, grid_blocks: int = 0,
-              time_kernels: bool = False) -> C.c_void_p:
-    t = pa_tunables(chunk_cycles, grid_blocks, 1 if time_kernels else 0, 0)
+              time_kernels=0) -> C.c_void_p:
+    t = pa_tunables(chunk_cycles, grid_blocks, int(time_kernels), 0)
     h = C.c_void_p()
     _check(lib().pa_create(C.byref(h), int(device), _stream_handle(stream), C.byref(t)))
     return h
@@ -133,6 +135,10 @@ def pa_destroy(ctx) -> None:
 
 def pa_set_stream(ctx, stream) -> None:
     _check(lib().pa_set_stream(ctx, _stream_handle(stream)))
+
+
+def pa_set_timing(ctx, time_kernels: int) -> None:
+    _check(lib().pa_set_timing(ctx, int(time_kernels)))
 
 
 def pa_last_error() -> str:

@@ -129,6 +129,8 @@ const char *pa_last_error(void) { return g_err.c_str(); }
 int pa_create(pa_ctx **out, int hip_device, void *hip_stream, const pa_tunables *t) {
   if (!out) return fail(PA_EINVAL, "pa_create: out is NULL");
   *out = nullptr;
+  if (t && (t->time_kernels < 0 || t->time_kernels > 2))
+    return fail(PA_EINVAL, "pa_create: time_kernels must be 0, 1 or 2");
   int ndev = 0;
   HIPCHK(hipGetDeviceCount(&ndev));
   if (hip_device < 0 || hip_device >= ndev) return fail(PA_EINVAL, "pa_create: device %d of %d", hip_device, ndev);
@@ -163,6 +165,13 @@ void pa_destroy(pa_ctx *c) {
     if (e) (void)hipEventDestroy(e);
   if (c->h_res) (void)hipHostFree(c->h_res);
   delete c;
+}
+
+int pa_set_timing(pa_ctx *c, int32_t time_kernels) {
+  if (!c) return fail(PA_EINVAL, "pa_set_timing: NULL context");
+  if (time_kernels < 0 || time_kernels > 2) return fail(PA_EINVAL, "pa_set_timing: mode must be 0, 1 or 2");
+  c->tun.time_kernels = time_kernels;
+  return PA_OK;
 }
 
 int pa_set_stream(pa_ctx *c, void *hip_stream) {
@@ -574,10 +583,10 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   f.cyc_glitches = cyc_glitches;
   f.res = v.res.as<double>();
 
-  const bool timed = c->tun.time_kernels != 0;
+  const bool timed = c->tun.time_kernels != 0, per_kernel = c->tun.time_kernels == 1;
   if (timed) HIPCHK(hipEventRecord(c->tev[0], s));
   hipError_t e1 = pa::launch_pass(a, v.grid, s);
-  if (timed && e1 == hipSuccess) e1 = hipEventRecord(c->tev[1], s);
+  if (per_kernel && e1 == hipSuccess) e1 = hipEventRecord(c->tev[1], s);
   if (e1 == hipSuccess) e1 = pa::launch_finalize(f, s);
   if (timed && e1 == hipSuccess) e1 = hipEventRecord(c->tev[2], s);
   if (e1 == hipSuccess) e1 = hipMemcpyAsync(c->h_res, f.res, sizeof(double) * 16, hipMemcpyDeviceToHost, s);
@@ -586,10 +595,13 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
     (void)hipStreamSynchronize(s);
     return fail(PA_EHIP, "pa_run: HIP error %s", hipGetErrorString(e1));
   }
-  if (timed) {
+  if (per_kernel) {
     (void)hipEventElapsedTime(&c->kernel_ms[0], c->tev[0], c->tev[1]);
     (void)hipEventElapsedTime(&c->kernel_ms[1], c->tev[1], c->tev[2]);
     c->kernel_ms[3] = c->kernel_ms[0] + c->kernel_ms[1];
+  } else if (timed) {
+    c->kernel_ms[0] = c->kernel_ms[1] = 0.0f;
+    (void)hipEventElapsedTime(&c->kernel_ms[3], c->tev[0], c->tev[2]);
   }
   const double *r = c->h_res;
   out->e_int_J = r[0];

@@ -62,7 +62,9 @@ typedef struct {
                              power of two, at most 512 (0 = 512) */
   int32_t grid_blocks;    /* target block count of the fused pass (0 = four per compute unit);
                              the pass cuts the events into about this many ranges */
-  int32_t time_kernels;   /* nonzero: record per-kernel device times of pa_run */
+  int32_t time_kernels;   /* 0: no timing; 1: device times of the fused kernel, the finalize
+                             kernel and the whole pass (three events on the stream);
+                             2: the whole pass only (two events, none between the kernels) */
   int32_t reserved;
 } pa_tunables;
 
@@ -73,6 +75,9 @@ void pa_destroy(pa_ctx *ctx);
 /* Change the stream later calls launch on (a hipStream_t). */
 int pa_set_stream(pa_ctx *ctx, void *hip_stream);
 const char *pa_last_error(void);
+/* Change the timing mode of later pa_run calls (the time_kernels field:
+ * 0, 1 or 2; PA_EINVAL otherwise). */
+int pa_set_timing(pa_ctx *ctx, int32_t time_kernels);
 
 /* Load the design (paper Sec. 2.4.1-2.4.2, Figs. 2-3: per-gate cell, state-
  * indexed internal-power LUTs per input pin, state-indexed leakage).
@@ -143,7 +148,7 @@ typedef struct {
   int32_t batch_events;       /* events one wave takes per step of the pass */
   int32_t max_segment_events; /* most events of one gate in one clock cycle (the load limit) */
   int64_t device_bytes;       /* library-owned device memory */
-  float kernel_ms[4];         /* last pa_run with time_kernels: fused, finalize, (unused), total */
+  float kernel_ms[4];         /* last timed pa_run: fused, finalize, (unused), whole pass; mode 2 fills only the last */
 } pa_info;
 int pa_get_info(pa_ctx *ctx, pa_info *info);
 
