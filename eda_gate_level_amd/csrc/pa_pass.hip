@@ -183,8 +183,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   int q = 0, pos = 0, wend = 0;
   if (has_range) {
     q = (int)a.rchunk[b];
-    pos = a.wbound[b * (kNW + 1) + wid];
-    wend = a.wbound[b * (kNW + 1) + wid + 1];
+    // wave-uniform, so the batch loop is steered by scalar branches
+    pos = __builtin_amdgcn_readfirstlane(a.wbound[b * (kNW + 1) + wid]);
+    wend = __builtin_amdgcn_readfirstlane(a.wbound[b * (kNW + 1) + wid + 1]);
   }
   u64x2 kp = {0ull, 0ull};
   f32x2 sp = {0.f, 0.f};
