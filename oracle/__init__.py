@@ -51,7 +51,7 @@ def lib():
         L.pa_oracle_run.restype = C.c_int
         L.pa_oracle_run.argtypes = [C.c_int64, P, P, C.c_int32, P, C.c_int32, C.c_int32, P, P, P, P,
                                     C.c_double, C.c_int64, P, P, P, P, P, C.c_int64, C.c_int64,
-                                    C.c_double, C.c_int64, C.c_int64, C.POINTER(Totals), P, P, P, P, P]
+                                    C.c_double, C.c_int64, C.c_int64, C.POINTER(Totals), P, P, P, P, P, P]
         L.pa_oracle_bilerp.restype = C.c_double
         L.pa_oracle_bilerp.argtypes = [C.c_int, C.c_int, P, P, P, C.c_double, C.c_double]
         L.pa_oracle_n_cycles.restype = C.c_int64
@@ -78,10 +78,12 @@ class OracleError(RuntimeError):
     pass
 
 
-def run(design, trace, gate_lo: int = 0, gate_hi: Optional[int] = None, per_event: bool = True) -> dict:
+def run(design, trace, gate_lo: int = 0, gate_hi: Optional[int] = None, per_event: bool = True,
+        per_gate: bool = False) -> dict:
     """Run the oracle over gates [gate_lo, gate_hi).  Returns the totals, the
-    per-cycle waveform/counts and (if per_event) the per-event glitch flags and
-    states before each event."""
+    per-cycle waveform/counts, (if per_event) the per-event glitch flags and
+    states before each event, and (if per_gate) gate_J[G][4]: every gate's
+    internal, switching, glitch and leakage energy (zero outside the range)."""
     d, t = design, trace
     if gate_hi is None:
         gate_hi = d.n_gates
@@ -98,17 +100,20 @@ def run(design, trace, gate_lo: int = 0, gate_hi: Optional[int] = None, per_even
     E = t.evt_t.shape[0]
     fl = np.zeros(E, np.uint8) if per_event else None
     st = np.zeros(E, np.uint8) if per_event else None
+    gj = np.zeros((d.n_gates, 4), np.float64) if per_gate else None
     tot = Totals()
     a = arrs
     rc = lib().pa_oracle_run(d.n_gates, _p(a["gc"]), _p(a["cap"]), d.n_cells, _p(a["k"]), d.n_slew, d.n_cap,
                              _p(a["sa"]), _p(a["ca"]), _p(a["lut"]), _p(a["leak"]), float(d.vdd_V),
                              t.pin_init.shape[0], _p(a["pp"]), _p(a["pi"]), _p(a["et"]), _p(a["ev"]),
                              _p(a["es"]), int(t.t_clk), int(t.t_max), float(t.tick_s), int(gate_lo),
-                             int(gate_hi), C.byref(tot), _p(wave), _p(ce), _p(cg), _p(fl), _p(st))
+                             int(gate_hi), C.byref(tot), _p(wave), _p(ce), _p(cg), _p(fl), _p(st), _p(gj))
     if rc != 0:
         raise OracleError(f"oracle rejected the input (code {rc})")
     out = {f: getattr(tot, f) for f, _ in Totals._fields_}
     out.update(wave_J=wave, cyc_events=ce, cyc_glitches=cg)
     if per_event:
         out.update(evt_glitch=fl, evt_state_before=st)
+    if per_gate:
+        out.update(gate_J=gj)
     return out

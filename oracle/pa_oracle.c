@@ -171,6 +171,7 @@ typedef struct {
   nsum e_int, e_sw, e_gl, e_leak;
   uint64_t *cyc_events, *cyc_glitches;
   uint64_t n_events, n_glitches;
+  nsum g_int, g_sw, g_gl, g_leak; /* the current gate's share */
 } run_ctx;
 
 /* Leakage of the interval [a, b) at constant power p (paper, Sec. 2.4.2,
@@ -179,6 +180,7 @@ typedef struct {
 static void leak_interval(run_ctx *R, double p, int64_t a, int64_t b) {
   if (b <= a) return;
   nadd(&R->e_leak, p * (double)(b - a) * R->tick_s);
+  nadd(&R->g_leak, p * (double)(b - a) * R->tick_s);
   int64_t c_lo = a / R->T;
   int64_t c_hi = (b + R->T - 1) / R->T; /* exclusive */
   for (int64_t c = c_lo; c < c_hi; ++c) {
@@ -195,7 +197,7 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
                   const uint8_t *evt_val, const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s,
                   int64_t gate_lo, int64_t gate_hi, pa_oracle_totals *out, double *wave_J,
                   uint64_t *cyc_events, uint64_t *cyc_glitches, uint8_t *evt_glitch,
-                  uint8_t *evt_state_before) {
+                  uint8_t *evt_state_before, double *gate_J) {
   if (!out || !wave_J || !cyc_events || !cyc_glitches) return PA_ORACLE_EARG;
   int rc = valid_design(n_gates, gate_cell, gate_cap_F, n_cells, cell_n_in, n_slew, n_cap, slew_axis, cap_axis);
   if (rc) return rc;
@@ -259,6 +261,10 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
     const double *cell_slew = slew_axis + (int64_t)cell * n_slew;
     const double *cell_cap = cap_axis + (int64_t)cell * n_cap;
     int64_t t_last = 0;
+    memset(&R.g_int, 0, sizeof R.g_int);
+    memset(&R.g_sw, 0, sizeof R.g_sw);
+    memset(&R.g_gl, 0, sizeof R.g_gl);
+    memset(&R.g_leak, 0, sizeof R.g_leak);
 
     for (;;) {
       /* next distinct timestamp of the k-way merge (Sec. 2.4.2, Fig. 3) */
@@ -296,11 +302,13 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
           double r = pw / (0.5 * (slew + sprev[i])); /* Eq. 2 as read above */
           if (r > 1.0) r = 1.0;
           nadd(&R.e_gl, r * E);
+          nadd(&R.g_gl, r * E);
           nadd(&R.wave[cyc], r * E);
           cyc_glitches[cyc] += 1;
           R.n_glitches += 1;
         } else {
           nadd(is_int ? &R.e_int : &R.e_sw, E);
+          nadd(is_int ? &R.g_int : &R.g_sw, E);
           nadd(&R.wave[cyc], E);
         }
         if (evt_glitch) evt_glitch[e] = (uint8_t)glitch;
@@ -323,6 +331,13 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
     }
     /* leakage is always present: the last interval runs to t_max */
     leak_interval(&R, leak_W[leak_base[cell] + S], t_last, t_max);
+    /* the gate's own energies (the per-gate output the paper ranks hotspots by, Sec. 5) */
+    if (gate_J) {
+      gate_J[4 * g + 0] = nval(&R.g_int);
+      gate_J[4 * g + 1] = nval(&R.g_sw);
+      gate_J[4 * g + 2] = nval(&R.g_gl);
+      gate_J[4 * g + 3] = nval(&R.g_leak);
+    }
   }
 
   for (int64_t c = 0; c < R.n_cyc; ++c) wave_J[c] = nval(&R.wave[c]);

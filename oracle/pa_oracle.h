@@ -15,7 +15,9 @@
  *   pins are gate-major: gate g owns k_g input pins then 1 output pin
  *   pin_ptr[P+1] CSR offsets into evt_t / evt_val / evt_slew
  * Outputs: wave_J, cyc_events, cyc_glitches have ceil(t_max/t_clk) entries;
- * evt_glitch and evt_state_before have pin_ptr[P] entries or are NULL.
+ * evt_glitch and evt_state_before have pin_ptr[P] entries or are NULL;
+ * gate_J[G][4] (NULL = not wanted) receives every processed gate's internal,
+ * switching, glitch and leakage energy in J.
  * Only gates [gate_lo, gate_hi) are processed; outputs hold their share.
  */
 #ifndef PA_ORACLE_H
@@ -49,7 +51,7 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
                   const uint8_t *evt_val, const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s,
                   int64_t gate_lo, int64_t gate_hi, pa_oracle_totals *out, double *wave_J,
                   uint64_t *cyc_events, uint64_t *cyc_glitches, uint8_t *evt_glitch,
-                  uint8_t *evt_state_before);
+                  uint8_t *evt_state_before, double *gate_J);
 
 #ifdef __cplusplus
 }

@@ -119,14 +119,19 @@ def dynamic(design, trace):
     contrib = np.where(flag, r * E, E)
     cyc = trace.evt_t // trace.t_clk
     wave = np.bincount(cyc, weights=contrib, minlength=trace.n_cycles)
+    G = design.n_gates
+    gate_dyn = np.stack([np.bincount(g, weights=np.where(~out & ~flag, E, 0.0), minlength=G),
+                         np.bincount(g, weights=np.where(out & ~flag, E, 0.0), minlength=G),
+                         np.bincount(g, weights=np.where(flag, r * E, 0.0), minlength=G)], axis=1)
     return dict(E=E, e_int=float(E[~out & ~flag].sum()), e_sw=float(E[out & ~flag].sum()),
-                e_gl=float((r * E)[flag].sum()), wave_dyn=wave, _kk=kk)
+                e_gl=float((r * E)[flag].sum()), wave_dyn=wave, gate_dyn=gate_dyn, _kk=kk)
 
 
-def leakage_per_tick(design, trace):
+def leakage_per_tick(design, trace, per_gate=False):
     """Leakage by brute force over every tick of a tiny window: the energy of
     tick x is leak[cell][S(x)] * tick_s where S(x) holds after all events at
-    times <= x.  Returns (e_leak, per-cycle leakage bins)."""
+    times <= x.  Returns (e_leak, per-cycle leakage bins), plus every gate's
+    leakage energy when per_gate."""
     assert trace.t_max <= 200_000, "per-tick brute force is for tiny windows"
     ticks = np.arange(trace.t_max, dtype=np.int64)
     k = design.gate_k()
@@ -135,6 +140,7 @@ def leakage_per_tick(design, trace):
     ncyc = trace.n_cycles
     bins_ticks = np.zeros(ncyc)
     total = 0.0
+    gate_total = np.zeros(design.n_gates)
     cyc_of_tick = ticks // trace.t_clk
     for g in range(design.n_gates):
         S = np.zeros(trace.t_max, np.int64)
@@ -147,5 +153,8 @@ def leakage_per_tick(design, trace):
         # integer tick counts per (bin, state) times the power, i.e. one multiply per term
         per_bin = np.bincount(cyc_of_tick, weights=p_tick, minlength=ncyc)
         bins_ticks += per_bin
-        total += p_tick.sum()
+        gate_total[g] = p_tick.sum()
+        total += gate_total[g]
+    if per_gate:
+        return total * trace.tick_s, bins_ticks * trace.tick_s, gate_total * trace.tick_s
     return total * trace.tick_s, bins_ticks * trace.tick_s

@@ -164,6 +164,21 @@ def test_small_random_dynamic_and_states(oracle_lib, seed):
     assert r["n_glitches"] == bf.glitch_count(tr) > 0
 
 
+@pytest.mark.parametrize("seed", [31, 32])
+def test_per_gate_energies_bruteforce(oracle_lib, seed):
+    """Every gate's internal, switching, glitch and leakage energy (the
+    per-gate output that hotspot ranking uses) against the brute-force
+    per-event energies (scipy interpolation) and per-tick leakage, gate by gate."""
+    des, tr = _small_random(seed, G=40, C=25, T=800, rate=0.5)
+    r = oracle_lib.run(des, tr, per_gate=True)
+    gj = r["gate_J"]
+    dyn = bf.dynamic(des, tr)
+    _, _, leak_g = bf.leakage_per_tick(des, tr, per_gate=True)
+    ref = np.concatenate([dyn["gate_dyn"], leak_g[:, None]], axis=1)
+    np.testing.assert_allclose(gj, ref, rtol=1e-11, atol=1e-30)
+    assert np.all(gj[:, 3] > 0) and np.count_nonzero(gj[:, 2]) > 0
+
+
 @pytest.fixture(scope="module")
 def tiny_run(oracle_lib):
     w = synth.tiny()
@@ -208,6 +223,15 @@ def test_gate_subsets_add_up(oracle_lib, tiny_run):
         assert _close(a[key] + b[key], r[key], rel=1e-12)
     np.testing.assert_allclose(a["wave_J"] + b["wave_J"], r["wave_J"], rtol=1e-12)
     assert a["n_glitches"] + b["n_glitches"] == r["n_glitches"]
+
+
+def test_per_gate_sums_to_totals(oracle_lib, tiny_run):
+    w, r = tiny_run
+    gj = oracle_lib.run(w.design, w.trace, per_event=False, per_gate=True)["gate_J"]
+    for c, key in enumerate(("e_int_J", "e_sw_J", "e_gl_J", "e_leak_J")):
+        assert _close(float(gj[:, c].sum()), r[key], rel=1e-12), key
+    sub = oracle_lib.run(w.design, w.trace, 100, 101, per_event=False)
+    assert [sub[k] for k in ("e_int_J", "e_sw_J", "e_gl_J", "e_leak_J")] == gj[100].tolist()
 
 
 def test_tiny_generator_statistics(tiny_run):
