@@ -12,11 +12,12 @@ from __future__ import annotations
 from typing import Optional
 
 from ._pa import (EXPORTS, PA_EDATA, PA_EHIP, PA_EINVAL, PA_ENOMEM, PA_ESTATE, PA_OK, PaError, lib, pa_create,
-                  pa_destroy, pa_get_info, pa_last_error, pa_load_design, pa_load_events, pa_run, pa_set_stream,
-                  pa_set_timing)
+                  pa_destroy, pa_get_info, pa_last_error, pa_load_design, pa_load_events, pa_run, pa_run_gates,
+                  pa_set_stream, pa_set_timing)
 
 __all__ = ["PowerAnalysis", "PaError", "pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error",
-           "pa_load_design", "pa_load_events", "pa_run", "pa_get_info", "lib", "EXPORTS", "PA_OK", "PA_EINVAL", "PA_EDATA",
+           "pa_load_design", "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info", "lib", "EXPORTS", "PA_OK",
+           "PA_EINVAL", "PA_EDATA",
            "PA_ENOMEM", "PA_EHIP", "PA_ESTATE"]
 
 
@@ -42,6 +43,7 @@ class PowerAnalysis:
         self.ctx = pa_create(device, stream, chunk_cycles, grid_blocks, time_kernels)
         self.n_cycles = 0
         self.n_events = 0
+        self.n_gates = 0
 
     def set_timing(self, time_kernels: int) -> None:
         """0: none; 1: fused, finalize and pass device times; 2: the pass only."""
@@ -66,6 +68,7 @@ class PowerAnalysis:
                        _dev(d.cell_n_in, torch.int32, dev), d.n_slew, d.n_cap,
                        _dev(d.slew_axis, torch.float64, dev), _dev(d.cap_axis, torch.float64, dev),
                        _dev(d.lut_J, torch.float64, dev), _dev(d.leak_W, torch.float64, dev), d.vdd_V)
+        self.n_gates = int(d.gate_cell.shape[0])
 
     def load_events(self, t) -> None:
         import torch
@@ -81,7 +84,7 @@ class PowerAnalysis:
         self.load_design(design)
         self.load_events(trace)
 
-    def alloc_outputs(self, per_event: bool = False) -> dict:
+    def alloc_outputs(self, per_event: bool = False, per_gate: bool = False) -> dict:
         import torch
 
         C, E, dev = self.n_cycles, self.n_events, self.device
@@ -91,13 +94,20 @@ class PowerAnalysis:
         if per_event:
             out["evt_glitch"] = torch.empty(max(E, 1), dtype=torch.uint8, device=dev)
             out["evt_state_before"] = torch.empty(max(E, 1), dtype=torch.uint8, device=dev)
+        if per_gate:
+            out["gate_J"] = torch.empty((max(self.n_gates, 1), 4), dtype=torch.float64, device=dev)
         return out
 
     def run(self, outputs: Optional[dict] = None, per_event: bool = False) -> dict:
         if outputs is None:
             outputs = self.alloc_outputs(per_event)
-        tot = pa_run(self.ctx, outputs["wave_J"], outputs["cyc_events"], outputs["cyc_glitches"],
-                     outputs.get("evt_glitch"), outputs.get("evt_state_before"))
+        if "gate_J" in outputs:
+            # per-gate energies (internal, switching, glitch, leakage) in a pass of their own
+            tot = pa_run_gates(self.ctx, outputs["wave_J"], outputs["cyc_events"], outputs["cyc_glitches"],
+                               outputs["gate_J"])
+        else:
+            tot = pa_run(self.ctx, outputs["wave_J"], outputs["cyc_events"], outputs["cyc_glitches"],
+                         outputs.get("evt_glitch"), outputs.get("evt_state_before"))
         return dict(totals=tot, **outputs)
 
     def info(self) -> dict:

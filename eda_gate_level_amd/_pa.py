@@ -20,7 +20,7 @@ _NAMES = {PA_EINVAL: "PA_EINVAL", PA_EDATA: "PA_EDATA", PA_ENOMEM: "PA_ENOMEM", 
           PA_ESTATE: "PA_ESTATE"}
 
 EXPORTS = ("pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error", "pa_load_design",
-           "pa_load_events", "pa_run", "pa_get_info")
+           "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info")
 
 
 class PaError(RuntimeError):
@@ -72,9 +72,10 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.pa_load_design.argtypes = [P, i64, P, P, i32, P, i32, i32, P, P, P, P, dbl]
     L.pa_load_events.argtypes = [P, i64, i64, P, P, P, P, P, i64, i64, dbl]
     L.pa_run.argtypes = [P, C.POINTER(pa_totals), P, P, P, P, P]
+    L.pa_run_gates.argtypes = [P, C.POINTER(pa_totals), P, P, P, P]
     L.pa_get_info.argtypes = [P, C.POINTER(pa_info)]
     for name in ("pa_create", "pa_set_stream", "pa_set_timing", "pa_load_design", "pa_load_events", "pa_run",
-                 "pa_get_info"):
+                 "pa_run_gates", "pa_get_info"):
         getattr(L, name).restype = C.c_int
     return L
 
@@ -178,6 +179,17 @@ def pa_run(ctx, wave_J, cyc_events, cyc_glitches, evt_glitch=None, evt_state_bef
                         _ptr(cyc_glitches, torch.uint64, name="cyc_glitches"),
                         _ptr(evt_glitch, torch.uint8, name="evt_glitch"),
                         _ptr(evt_state_before, torch.uint8, name="evt_state_before")))
+    return tot.as_dict()
+
+
+def pa_run_gates(ctx, wave_J, cyc_events, cyc_glitches, gate_J) -> dict:
+    import torch
+
+    tot = pa_totals()
+    _check(lib().pa_run_gates(ctx, C.byref(tot), _ptr(wave_J, torch.float64, name="wave_J"),
+                              _ptr(cyc_events, torch.uint64, name="cyc_events"),
+                              _ptr(cyc_glitches, torch.uint64, name="cyc_glitches"),
+                              _ptr(gate_J, torch.float64, name="gate_J")))
     return tot.as_dict()
 
 

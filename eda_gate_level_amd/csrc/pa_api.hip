@@ -72,10 +72,11 @@ struct Design {
   double vdd = 0;
   DBuf cell_k, cell_meta, cell_thr, cell_axw, lut, leak;
   DBuf gate_info, gate_cw, gate_k, pin_base, pin_gate, pin_local;
+  DBuf perm;  // internal gate -> caller gate
   int64_t bytes() const {
     return (int64_t)(cell_k.bytes + cell_meta.bytes + cell_thr.bytes + cell_axw.bytes + lut.bytes + leak.bytes +
                      gate_info.bytes + gate_cw.bytes + gate_k.bytes + pin_base.bytes + pin_gate.bytes +
-                     pin_local.bytes);
+                     pin_local.bytes + perm.bytes);
   }
 };
 
@@ -285,7 +286,7 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   for (int64_t i = 0; i < G; ++i) pb[i] = pbc[perm[i]];
   pb[G] = pbc[G];
   d.P = pbc[G];
-  DBuf perm_d;
+  DBuf &perm_d = d.perm;
   HIPCHK(perm_d.alloc(sizeof(int32_t) * G));
   if (G > 0) HIPCHK(hipMemcpyAsync(perm_d.p, perm.data(), sizeof(int32_t) * G, hipMemcpyHostToDevice, s));
   HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
@@ -515,15 +516,15 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   return PA_OK;
 }
 
-int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
-           uint8_t *evt_glitch, uint8_t *evt_state_before) {
-  if (!c) return fail(PA_EINVAL, "pa_run: NULL context");
-  if (!c->has_design || !c->has_events) return fail(PA_ESTATE, "pa_run: design and events must be loaded first");
-  if (!out || !wave_J || !cyc_events || !cyc_glitches) return fail(PA_EINVAL, "pa_run: NULL output");
-  HIPCHK(hipSetDevice(c->device));
+static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
+                    uint8_t *evt_glitch, uint8_t *evt_state_before, double *gate_J) {
   const Design &d = c->d;
   Events &v = c->ev;
   hipStream_t s = c->stream;
+  if (gate_J)
+    HIPCHK(pa::launch_gate_rows(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
+                                d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), d.perm.as<int32_t>(),
+                                (double)v.t_max * v.tick_s, gate_J, s));
 
   pa::PassArgs a{};
   a.key = v.key.as<uint64_t>();
@@ -562,6 +563,8 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   a.blk_cnt = v.blk_cnt.as<unsigned long long>();
   a.blk_part = v.blk_part.as<double>();
   a.evt_glitch = evt_glitch;
+  a.gate_J = gate_J;
+  a.gate_perm = d.perm.as<int32_t>();
   a.evt_state = evt_state_before;
 
   pa::FinalArgs f{};
@@ -616,6 +619,26 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   out->n_events = (uint64_t)v.E;
   out->n_cycles = v.C;
   return PA_OK;
+}
+
+int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
+           uint8_t *evt_glitch, uint8_t *evt_state_before) {
+  if (!c) return fail(PA_EINVAL, "pa_run: NULL context");
+  if (!c->has_design || !c->has_events) return fail(PA_ESTATE, "pa_run: design and events must be loaded first");
+  if (!out || !wave_J || !cyc_events || !cyc_glitches) return fail(PA_EINVAL, "pa_run: NULL output");
+  HIPCHK(hipSetDevice(c->device));
+  return run_pass(c, out, wave_J, cyc_events, cyc_glitches, evt_glitch, evt_state_before, nullptr);
+}
+
+int pa_run_gates(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
+                 double *gate_J) {
+  if (!c) return fail(PA_EINVAL, "pa_run_gates: NULL context");
+  if (!c->has_design || !c->has_events)
+    return fail(PA_ESTATE, "pa_run_gates: design and events must be loaded first");
+  if (!out || !wave_J || !cyc_events || !cyc_glitches || (!gate_J && c->d.G > 0))
+    return fail(PA_EINVAL, "pa_run_gates: NULL output");
+  HIPCHK(hipSetDevice(c->device));
+  return run_pass(c, out, wave_J, cyc_events, cyc_glitches, nullptr, nullptr, gate_J);
 }
 
 int pa_get_info(pa_ctx *c, pa_info *info) {

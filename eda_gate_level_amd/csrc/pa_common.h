@@ -85,6 +85,8 @@ struct PassArgs {
   // diagnostics (may be null)
   uint8_t *evt_glitch;
   uint8_t *evt_state;
+  double *gate_J;             // [G][4] per-gate energies, caller's gate order (added to)
+  const int32_t *gate_perm;   // internal gate -> caller gate
 };
 
 struct FinalArgs {

@@ -38,6 +38,10 @@ hipError_t launch_gate_tables(int64_t G, const int32_t *perm, const int32_t *gat
 hipError_t launch_leak0(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
                         const int64_t *pin_base, const uint8_t *pin_init, double *part, double *l0, hipStream_t s);
 int leak0_parts();
+// per-gate output rows (caller's gate order): zero dynamic parts, leakage at the initial state over the window
+hipError_t launch_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
+                            const int64_t *pin_base, const uint8_t *pin_init, const int32_t *perm, double window,
+                            double *gate_J, hipStream_t s);
 hipError_t launch_pin_owner(int64_t G, const int64_t *pin_base, const int32_t *gate_k, int32_t *pin_gate,
                             uint8_t *pin_local, hipStream_t s);
 hipError_t launch_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err,

@@ -274,6 +274,34 @@ hipError_t launch_leak0(int64_t G, const uint32_t *gate_info, const uint2 *cell_
 }
 int leak0_parts() { return kL0B; }
 
+// Per-gate output start: row perm[g] = (0, 0, 0, leak[S0] * window), the
+// gate's leakage before any power change.
+__global__ void k_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
+                            const int64_t *pin_base, const uint8_t *pin_init, const int32_t *perm, double window,
+                            double *gate_J) {
+  for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
+    const uint2 m = cell_meta[gate_info[g] & 0xFFFFFFu];
+    const int k = (int)(m.x & 15u);
+    const int64_t p0 = pin_base[g];
+    uint32_t S = 0;
+    for (int j = 0; j < k; ++j) S |= uint32_t(pin_init[p0 + j]) << j;
+    double *row = gate_J + 4 * (size_t)perm[g];
+    row[0] = 0.0;
+    row[1] = 0.0;
+    row[2] = 0.0;
+    row[3] = leak[(m.x >> 4) + S] * window;
+  }
+}
+
+hipError_t launch_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
+                            const int64_t *pin_base, const uint8_t *pin_init, const int32_t *perm, double window,
+                            double *gate_J, hipStream_t s) {
+  if (G <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gate_rows, dim3(grid_for(G)), dim3(kLT), 0, s, G, gate_info, cell_meta, leak, pin_base,
+                     pin_init, perm, window, gate_J);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,
                               int32_t n_cells, const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
                               uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err, hipStream_t s) {

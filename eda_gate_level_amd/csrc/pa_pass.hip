@@ -390,6 +390,8 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         // glitch: the previous event of the same pin lies in the same cycle (Fig. 7)
         const bool glitch = !gh && ((lk ^ lkp) >> tb) == 0u;
         double contrib = E;
+        double lk_gate = 0.0;  // leakage of this power change up to t_max (per-gate output)
+        double dyn = 0.0;      // this event's dynamic energy after the glitch scale
         if (glitch) {
           const double pw = (double)(tic - (lkp & tmask));
           const double rr = pw / (0.5 * ((double)sl + (double)slp));  // Eq. 2 (reading)
@@ -401,12 +403,19 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         } else {
           e_sw += E;
         }
+        dyn = contrib;
         // leakage power change at this timestamp (owner = lowest switching input pin)
         if (input && (r ? ow1 : ow0)) {
           const double dp = leak_of(lb + (Sm ^ ((r ? mk1 : mk0) & smask))) - leak_of(lb + Sm);
           if (dp != 0.0) {
             // rest of the event's bin (the flush corrects a partial last bin)
             const double part = dp * tick * (double)(T - tic);
+            if constexpr (DIAG) {
+              if (a.gate_J) {
+                lk_gate = dp * tick * (double)(a.t_max - cstart - ((int64_t)cyc * T + tic));
+                atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[hw >> 10] + 3, lk_gate);
+              }
+            }
             contrib += part;
             e_lk += part;
             atomicAdd(&L.bb[cyc], dp);
@@ -418,6 +427,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
           const uint32_t o = a.orig[base + (r ? i1 : i0)];
           if (a.evt_glitch) a.evt_glitch[o] = glitch ? 1 : 0;
           if (a.evt_state) a.evt_state[o] = (uint8_t)(input ? Sm : 0u);
+          // the gate's own energy: internal, switching or glitch (device atomics)
+          if (a.gate_J && dyn != 0.0)
+            atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[hw >> 10] + (glitch ? 2 : (input ? 0 : 1)), dyn);
         }
       }
       pos = npos;
@@ -661,7 +673,7 @@ bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_le
 
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
   const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_thr, a.n_leak);
-  const bool diag = a.evt_glitch || a.evt_state;
+  const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
   const size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_thr, a.n_leak, cells);
   if (dyn > kLdsMax) return hipErrorInvalidValue;
   const dim3 g(grid_blocks), t(kNT);

@@ -140,6 +140,17 @@ typedef struct {
 int pa_run(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
            uint8_t *evt_glitch, uint8_t *evt_state_before);
 
+/* pa_run plus every gate's own energies, the per-gate power the paper ranks
+ * hotspots by (its spatial-accuracy evaluation, Sec. 5):
+ *   gate_J[G][4]   device: per gate (caller's order) the internal, switching,
+ *                  glitch and leakage energy over [0, t_max), J; overwritten.
+ * The gate rows add up to the totals (up to fp64 summation order).  This
+ * pass takes the diagnostic kernel variant and adds the per-gate energies
+ * with device atomics, so its row sums may differ between runs in the last
+ * bits; the totals and the waveform do not. */
+int pa_run_gates(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
+                 double *gate_J);
+
 /* Layout and launch facts of the loaded data (HOST struct). */
 typedef struct {
   int64_t n_gates, n_pins, n_events, n_cycles;
