@@ -222,8 +222,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {G} gates (1-4 inputs, 7x7 fp64 LUTs), {C} cycles of "
-                               f"{tr.t_clk} fs, {E} events, seed 0",
+        "config": {"workload": f"{w.name}: {G} gates (inputs {int(d.cell_n_in.min())}-{int(d.cell_n_in.max())}, "
+                               f"{d.n_slew}x{d.n_cap} fp64 LUTs), {C} cycles of {tr.t_clk} fs, {E} events, seed 0",
                    "gates": G, "pins": P, "events": E, "cycles": C,
                    "chunk_cycles": info["chunk_cycles"], "grid_blocks": info["grid_blocks"],
                    "block_threads": info["block_threads"]},

@@ -156,6 +156,15 @@ def test_repeated_runs_agree():
     an.close()
 
 
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_contention_small(m):
+    """Every pin toggling m times per cycle: all events of a cycle share one
+    waveform bin and most are glitches (the stress workload, reduced)."""
+    w = synth.contention(m, G=12, C=700)
+    _print_case(f"contention m={m}")
+    pu.assert_parity(pu.gpu_run(w.design, w.trace), _oracle(w.design, w.trace), label=f"contention {m}")
+
+
 @pytest.mark.parametrize("name", ["tiny", "medium", "skewed", "glitch_heavy"])
 def test_workload_full_size(name):
     w = synth.make(name)

@@ -234,6 +234,28 @@ def test_per_gate_sums_to_totals(oracle_lib, tiny_run):
     assert [sub[k] for k in ("e_int_J", "e_sw_J", "e_gl_J", "e_leak_J")] == gj[100].tolist()
 
 
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_contention_generator_and_glitch_count(oracle_lib, m):
+    """The waveform-bin stress trace: every pin toggles exactly m times in
+    every cycle, times strictly increasing, values alternating; so every bin
+    holds P*m events of which P*(m-1) are glitches, in closed form."""
+    w = synth.contention(m, G=5, C=40)
+    d, t = w.design, w.trace
+    P = t.n_pins
+    cyc = t.evt_t // t.t_clk
+    pin = bf.event_pins(t)
+    assert t.n_events == P * 40 * m
+    assert np.all(np.bincount(pin * 40 + cyc, minlength=P * 40) == m)
+    for p in range(P):
+        tt = t.evt_t[t.pin_ptr[p]:t.pin_ptr[p + 1]]
+        assert np.all(np.diff(tt) > 0)
+        vv = t.evt_val[t.pin_ptr[p]:t.pin_ptr[p + 1]].astype(int)
+        assert vv[0] == 1 - int(t.pin_init[p]) and np.all(vv[1:] != vv[:-1])
+    r = oracle_lib.run(d, t, per_event=False)
+    assert np.all(r["cyc_events"] == P * m) and np.all(r["cyc_glitches"] == P * (m - 1))
+    assert r["n_glitches"] == P * 40 * (m - 1)
+
+
 def test_tiny_generator_statistics(tiny_run):
     """Tiny draws Poisson(0.1) events per pin-cycle: expected glitches =
     N_pin_cycles * (lambda - 1 + e^-lambda) ~ 2,902, expected events 60,000."""

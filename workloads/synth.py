@@ -294,7 +294,47 @@ def large(seed: int = 0) -> Workload:
     return Workload("large", des, tr, {"lognormal_sigma": sigma})
 
 
-CONFIGS = {"tiny": tiny, "medium": medium, "skewed": skewed, "glitch_heavy": glitch_heavy, "large": large}
+def toggle_trace(rng: np.random.Generator, n_pins: int, n_cycles: int, t_clk: int, m: int) -> Trace:
+    """Every pin toggles m times in every clock cycle: the cycle is cut into m
+    equal slots and toggle j falls uniformly inside slot j, so the times of a
+    pin are strictly increasing.  Values alternate from a random initial
+    value; slews ~ U(5, 100) ps."""
+    slot = t_clk // m
+    per_pin = n_cycles * m
+    grid = (np.arange(n_cycles, dtype=np.int64)[:, None] * t_clk
+            + np.arange(m, dtype=np.int64)[None, :] * slot).reshape(-1)
+    evt_t = rng.integers(0, slot, size=(n_pins, per_pin), dtype=np.int64)
+    evt_t += grid[None, :]
+    evt_t = evt_t.reshape(-1)
+    pin_ptr = np.arange(n_pins + 1, dtype=np.int64) * per_pin
+    pin_init = rng.integers(0, 2, size=n_pins, dtype=np.uint8)
+    alt = np.resize(np.array([1, 0], dtype=np.uint8), per_pin)  # toggle i gives !init for even i
+    evt_val = (np.tile(alt, n_pins) ^ np.repeat(pin_init, per_pin)).astype(np.uint8)
+    evt_slew = rng.random(evt_t.shape[0], dtype=np.float32)
+    evt_slew *= np.float32(95 * PS)
+    evt_slew += np.float32(5 * PS)
+    return Trace(pin_ptr=pin_ptr, pin_init=pin_init, evt_t=evt_t, evt_val=evt_val, evt_slew=evt_slew,
+                 t_clk=int(t_clk), t_max=int(n_cycles) * int(t_clk))
+
+
+def contention(m: int, seed: int = 0, G: int = 32, C: int = 100_000) -> Workload:
+    """Waveform-bin stress: 32 two-input gates (96 pins), 100,000 cycles of
+    1 ns, every pin toggling m times per cycle (m = 1, 2, 4, 8: 9.6M to
+    76.8M events, 96 m events in every waveform bin).  Every event of a cycle lands in the same waveform bin and
+    every toggle after a pin's first in a cycle is a glitch, so this is the
+    worst case for the per-bin accumulation (the paper's atomic stress test
+    on high-activity synthetic waveforms, Sec. 5)."""
+    rng = np.random.default_rng(seed)
+    lib = make_library(rng, [2])
+    des = assign_gates(rng, lib, np.full(G, 2, np.int64), 1.0, 50.0)
+    P = int(des.pin_base()[-1])
+    tr = toggle_trace(rng, P, C, NS, m)
+    return Workload(f"contention{m}", des, tr, {"toggles_per_cycle": m})
+
+
+CONFIGS = {"tiny": tiny, "medium": medium, "skewed": skewed, "glitch_heavy": glitch_heavy, "large": large,
+           "contention1": lambda seed=0: contention(1, seed), "contention2": lambda seed=0: contention(2, seed),
+           "contention4": lambda seed=0: contention(4, seed), "contention8": lambda seed=0: contention(8, seed)}
 
 
 def make(name: str, seed: int = 0) -> Workload:
