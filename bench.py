@@ -81,6 +81,33 @@ def profiled_traffic(workload):
     return int(m_tr.group(1))
 
 
+def window_ablation(args, w, dev):
+    """The paper's fixed-window comparison on this layout: the same pass with
+    density-aware windows and with every gate's windows fixed at n cycles."""
+    import torch
+
+    import eda_gate_level_amd as pa
+
+    d, tr = w.design, w.trace
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for n_fix in (0, 1, 2, 4, 8, 16, 32):
+        an = pa.PowerAnalysis(0, torch.cuda.current_stream(dev), chunk_cycles=args.chunk_cycles,
+                              grid_blocks=args.grid_blocks, time_kernels=1, fixed_window_cycles=n_fix)
+        an.load(d, tr)
+        outs = an.alloc_outputs()
+        for _ in range(max(3, args.warmup // 4)):
+            an.run(outs)
+        fused = []
+        for _ in range(max(5, args.steps // 2)):
+            flush.fill_(1.0)
+            an.run(outs)
+            fused.append(an.info()["kernel_ms"][0])
+        st = an.window_stats()
+        print(json.dumps({"workload": w.name, "windows": "density-aware" if n_fix == 0 else f"fixed {n_fix} cycles",
+                          "fused_ms": statistics.median(fused), "events_per_window": st}), flush=True)
+        an.close()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +119,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--quick", action="store_true", help="no 2 s clock warm-up and no CPU baseline (profiling runs)")
+    ap.add_argument("--window-ablation", action="store_true",
+                    help="time the pass with density-aware windows and with fixed windows of 1..32 cycles "
+                         "(one JSON line each, with the events-per-window distribution)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB, 5 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -121,6 +151,9 @@ def main():
     torch.cuda.set_device(dev)
     t0 = time.time()
     w = synth.make(args.workload)
+    if args.window_ablation:
+        window_ablation(args, w, dev)
+        return
     d, tr = w.design, w.trace
     gen_s = time.time() - t0
     E, G, P, C = tr.n_events, d.n_gates, tr.n_pins, tr.n_cycles

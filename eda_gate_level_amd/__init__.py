@@ -12,11 +12,12 @@ from __future__ import annotations
 from typing import Optional
 
 from ._pa import (EXPORTS, PA_EDATA, PA_EHIP, PA_EINVAL, PA_ENOMEM, PA_ESTATE, PA_OK, PaError, lib, pa_create,
-                  pa_destroy, pa_get_info, pa_last_error, pa_load_design, pa_load_events, pa_run, pa_run_gates,
-                  pa_set_stream, pa_set_timing)
+                  pa_destroy, pa_get_info, pa_get_window_stats, pa_last_error, pa_load_design, pa_load_events,
+                  pa_run, pa_run_gates, pa_set_stream, pa_set_timing)
 
 __all__ = ["PowerAnalysis", "PaError", "pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error",
-           "pa_load_design", "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info", "lib", "EXPORTS", "PA_OK",
+           "pa_load_design", "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info", "pa_get_window_stats",
+           "lib", "EXPORTS", "PA_OK",
            "PA_EINVAL", "PA_EDATA",
            "PA_ENOMEM", "PA_EHIP", "PA_ESTATE"]
 
@@ -34,13 +35,13 @@ class PowerAnalysis:
     output tensors."""
 
     def __init__(self, device: int = 0, stream=None, chunk_cycles: int = 0, grid_blocks: int = 0,
-                 time_kernels=0):
+                 time_kernels=0, fixed_window_cycles: int = 0):
         import torch
 
         self.device = torch.device("cuda", device)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
-        self.ctx = pa_create(device, stream, chunk_cycles, grid_blocks, time_kernels)
+        self.ctx = pa_create(device, stream, chunk_cycles, grid_blocks, time_kernels, fixed_window_cycles)
         self.n_cycles = 0
         self.n_events = 0
         self.n_gates = 0
@@ -109,6 +110,10 @@ class PowerAnalysis:
             tot = pa_run(self.ctx, outputs["wave_J"], outputs["cyc_events"], outputs["cyc_glitches"],
                          outputs.get("evt_glitch"), outputs.get("evt_state_before"))
         return dict(totals=tot, **outputs)
+
+    def window_stats(self) -> dict:
+        """Events per (chunk, gate, window) of the loaded layout: count, mean, p50/p90/p99, max."""
+        return pa_get_window_stats(self.ctx)
 
     def info(self) -> dict:
         return pa_get_info(self.ctx)

@@ -20,7 +20,7 @@ _NAMES = {PA_EINVAL: "PA_EINVAL", PA_EDATA: "PA_EDATA", PA_ENOMEM: "PA_ENOMEM", 
           PA_ESTATE: "PA_ESTATE"}
 
 EXPORTS = ("pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error", "pa_load_design",
-           "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info")
+           "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info", "pa_get_window_stats")
 
 
 class PaError(RuntimeError):
@@ -31,13 +31,21 @@ class PaError(RuntimeError):
 
 class pa_tunables(C.Structure):
     _fields_ = [("chunk_cycles", C.c_int32), ("grid_blocks", C.c_int32), ("time_kernels", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("fixed_window_cycles", C.c_int32)]
 
 
 class pa_totals(C.Structure):
     _fields_ = [("p_int_W", C.c_double), ("p_sw_W", C.c_double), ("p_gl_W", C.c_double), ("p_leak_W", C.c_double),
                 ("e_int_J", C.c_double), ("e_sw_J", C.c_double), ("e_gl_J", C.c_double), ("e_leak_J", C.c_double),
                 ("n_events", C.c_uint64), ("n_glitches", C.c_uint64), ("n_cycles", C.c_int64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class pa_window_stats(C.Structure):
+    _fields_ = [("n_windows", C.c_int64), ("mean", C.c_double), ("p50", C.c_int64), ("p90", C.c_int64),
+                ("p99", C.c_int64), ("max", C.c_int64)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -74,8 +82,9 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.pa_run.argtypes = [P, C.POINTER(pa_totals), P, P, P, P, P]
     L.pa_run_gates.argtypes = [P, C.POINTER(pa_totals), P, P, P, P]
     L.pa_get_info.argtypes = [P, C.POINTER(pa_info)]
+    L.pa_get_window_stats.argtypes = [P, C.POINTER(pa_window_stats)]
     for name in ("pa_create", "pa_set_stream", "pa_set_timing", "pa_load_design", "pa_load_events", "pa_run",
-                 "pa_run_gates", "pa_get_info"):
+                 "pa_run_gates", "pa_get_info", "pa_get_window_stats"):
         getattr(L, name).restype = C.c_int
     return L
 
@@ -122,8 +131,8 @@ def _stream_handle(stream) -> C.c_void_p:
 
 
 def pa_create(device: int = 0, stream=None, chunk_cycles: int = 0, grid_blocks: int = 0,
-              time_kernels=0) -> C.c_void_p:
-    t = pa_tunables(chunk_cycles, grid_blocks, int(time_kernels), 0)
+              time_kernels=0, fixed_window_cycles: int = 0) -> C.c_void_p:
+    t = pa_tunables(chunk_cycles, grid_blocks, int(time_kernels), int(fixed_window_cycles))
     h = C.c_void_p()
     _check(lib().pa_create(C.byref(h), int(device), _stream_handle(stream), C.byref(t)))
     return h
@@ -191,6 +200,12 @@ def pa_run_gates(ctx, wave_J, cyc_events, cyc_glitches, gate_J) -> dict:
                               _ptr(cyc_glitches, torch.uint64, name="cyc_glitches"),
                               _ptr(gate_J, torch.float64, name="gate_J")))
     return tot.as_dict()
+
+
+def pa_get_window_stats(ctx) -> dict:
+    st = pa_window_stats()
+    _check(lib().pa_get_window_stats(ctx, C.byref(st)))
+    return st.as_dict()
 
 
 def pa_get_info(ctx) -> dict:

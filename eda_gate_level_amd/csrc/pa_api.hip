@@ -461,8 +461,15 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
     // ---- density-aware window level per gate
     DBuf level;
     HIPCHK(level.alloc(G));
+    int32_t fixed_level = -1;
+    if (c->tun.fixed_window_cycles > 0) {
+      int64_t n = 1;
+      while (n * 2 <= c->tun.fixed_window_cycles && n * 2 <= Cc) n *= 2;
+      fixed_level = 0;
+      while ((Cc >> fixed_level) > n) ++fixed_level;
+    }
     HIPCHK(pa::launch_gate_levels(G, d.pin_base.as<int64_t>(), d.gate_k.as<int32_t>(), pin_ptr, v.C, (int32_t)Cc,
-                                  (int32_t)lc, 32.0, level.as<uint8_t>(), s));
+                                  (int32_t)lc, 32.0, fixed_level, level.as<uint8_t>(), s));
     // ---- order (chunk, gate, cycle, pin, time) by radix sort
     DBuf k0, k1, idx, perm, tmp;
     size_t tmp_bytes = 0;
@@ -639,6 +646,40 @@ int pa_run_gates(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events
     return fail(PA_EINVAL, "pa_run_gates: NULL output");
   HIPCHK(hipSetDevice(c->device));
   return run_pass(c, out, wave_J, cyc_events, cyc_glitches, nullptr, nullptr, gate_J);
+}
+
+int pa_get_window_stats(pa_ctx *c, pa_window_stats *out) {
+  if (!c || !out) return fail(PA_EINVAL, "pa_get_window_stats: NULL argument");
+  if (!c->has_events) return fail(PA_ESTATE, "pa_get_window_stats: no events loaded");
+  HIPCHK(hipSetDevice(c->device));
+  const Events &v = c->ev;
+  hipStream_t s = c->stream;
+  *out = pa_window_stats{};
+  if (v.E == 0) return PA_OK;
+  DBuf sizes, n;
+  HIPCHK(sizes.alloc(sizeof(uint32_t) * v.E));
+  HIPCHK(n.alloc(sizeof(unsigned long long)));
+  HIPCHK(hipMemsetAsync(n.p, 0, sizeof(unsigned long long), s));
+  HIPCHK(pa::launch_window_sizes(v.E, v.key.as<uint64_t>(), sizes.as<uint32_t>(), n.as<unsigned long long>(), s));
+  unsigned long long hn = 0;
+  HIPCHK(hipMemcpyAsync(&hn, n.p, sizeof(hn), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  std::vector<uint32_t> h(hn);
+  if (hn) HIPCHK(hipMemcpyAsync(h.data(), sizes.p, sizeof(uint32_t) * hn, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  std::sort(h.begin(), h.end());
+  out->n_windows = (int64_t)hn;
+  if (hn) {
+    double sum = 0.0;
+    for (uint32_t x : h) sum += x;
+    out->mean = sum / (double)hn;
+    auto pct = [&](double q) { return (int64_t)h[std::min<size_t>(hn - 1, (size_t)(q * (double)(hn - 1) + 0.5))]; };
+    out->p50 = pct(0.50);
+    out->p90 = pct(0.90);
+    out->p99 = pct(0.99);
+    out->max = (int64_t)h.back();
+  }
+  return PA_OK;
 }
 
 int pa_get_info(pa_ctx *c, pa_info *info) {

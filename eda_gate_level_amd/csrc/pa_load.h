@@ -49,8 +49,13 @@ hipError_t launch_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pi
 hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init,
                               const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_max,
                               uint32_t *ev_pin, uint32_t *err, hipStream_t s);
+// per-gate window level: fixed_level >= 0 gives every gate that level, else density-aware
 hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int32_t *gate_k, const int64_t *pin_ptr,
-                              int64_t C, int32_t Cc, int32_t lc, double target, uint8_t *level, hipStream_t s);
+                              int64_t C, int32_t Cc, int32_t lc, double target, int32_t fixed_level,
+                              uint8_t *level, hipStream_t s);
+// events of every window of the layout, appended in any order to sizes (*n counts them; zero it first)
+hipError_t launch_window_sizes(int64_t E, const uint64_t *key, uint32_t *sizes, unsigned long long *n,
+                               hipStream_t s);
 // chunk == nullptr: one 64-bit key (chunk, gate, lk); else key = (gate, lk) and chunk[e] apart
 hipError_t launch_sort_keys(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
                             const uint8_t *pin_local, const int32_t *gate_k, const LayoutFmt &f, uint64_t *key,

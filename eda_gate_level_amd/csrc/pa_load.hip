@@ -109,8 +109,13 @@ __global__ void k_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
 // here the chunk is the upper bound on a window, which plays the part of its
 // parallelism floor).
 __global__ void k_gate_levels(int64_t G, const int64_t *pin_base, const int32_t *gate_k, const int64_t *pin_ptr,
-                              int64_t C, int32_t Cc, int32_t lc, double target, uint8_t *level) {
+                              int64_t C, int32_t Cc, int32_t lc, double target, int32_t fixed_level,
+                              uint8_t *level) {
   for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
+    if (fixed_level >= 0) {  // the same window length for every gate
+      level[g] = (uint8_t)fixed_level;
+      continue;
+    }
     const double n_evt = (double)(pin_ptr[pin_base[g] + gate_k[g] + 1] - pin_ptr[pin_base[g]]);
     const double rho = n_evt / (double)C;
     int sl = 0;
@@ -331,9 +336,29 @@ hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
 }
 
 hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int32_t *gate_k, const int64_t *pin_ptr,
-                              int64_t C, int32_t Cc, int32_t lc, double target, uint8_t *level, hipStream_t s) {
+                              int64_t C, int32_t Cc, int32_t lc, double target, int32_t fixed_level,
+                              uint8_t *level, hipStream_t s) {
   hipLaunchKernelGGL(k_gate_levels, dim3(grid_for(G)), dim3(kLT), 0, s, G, pin_base, gate_k, pin_ptr, C, Cc, lc, target,
-                     level);
+                     fixed_level, level);
+  return hipGetLastError();
+}
+
+// Events per window: every window head finds the next head (or the end) and
+// appends the distance.
+__global__ void k_window_sizes(int64_t E, const uint64_t *key, uint32_t *sizes, unsigned long long *n) {
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
+    if (!((key[x] >> kKeyHeadShift) & 1ull)) continue;
+    int64_t y = x + 1;
+    while (y < E && !((key[y] >> kKeyHeadShift) & 1ull)) ++y;
+    const unsigned long long i = atomicAdd(n, 1ull);
+    sizes[i] = (uint32_t)(y - x);
+  }
+}
+
+hipError_t launch_window_sizes(int64_t E, const uint64_t *key, uint32_t *sizes, unsigned long long *n,
+                               hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_window_sizes, dim3(grid_for(E)), dim3(kLT), 0, s, E, key, sizes, n);
   return hipGetLastError();
 }
 

@@ -65,7 +65,9 @@ typedef struct {
   int32_t time_kernels;   /* 0: no timing; 1: device times of the fused kernel, the finalize
                              kernel and the whole pass (three events on the stream);
                              2: the whole pass only (two events, none between the kernels) */
-  int32_t reserved;
+  int32_t fixed_window_cycles; /* 0: density-aware windows (below); n > 0: every gate's
+                             windows are n cycles (rounded down to a power of two, at most the
+                             chunk) -- the fixed-window layout the paper compares against */
 } pa_tunables;
 
 /* Create a context on HIP device `hip_device`, launching on `hip_stream`
@@ -150,6 +152,15 @@ int pa_run(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, ui
  * bits; the totals and the waveform do not. */
 int pa_run_gates(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
                  double *gate_J);
+
+/* Events per window of the loaded layout (HOST struct): the windows are the
+ * (chunk, gate, window) pieces whose first event carries the gate's state. */
+typedef struct {
+  int64_t n_windows;
+  double mean;
+  int64_t p50, p90, p99, max;
+} pa_window_stats;
+int pa_get_window_stats(pa_ctx *ctx, pa_window_stats *out);
 
 /* Layout and launch facts of the loaded data (HOST struct). */
 typedef struct {

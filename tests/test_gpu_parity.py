@@ -93,6 +93,32 @@ def test_launch_grid_does_not_change_results(grid):
     pu.assert_parity(pu.gpu_run(d, t, grid_blocks=grid), _oracle(d, t), label=f"grid {grid}")
 
 
+@pytest.mark.parametrize("n_fix", [1, 4, 32])
+def test_fixed_windows_do_not_change_results(n_fix):
+    """Fixed-length windows (the layout the paper's density-aware windows
+    replace) give the same results; with one-cycle windows every (gate,
+    cycle) run is a window, so the window count is the number of such runs."""
+    import eda_gate_level_amd as pa
+
+    d, t = _random(seed=9, G=400, C=120, rate=0.3)
+    _print_case(f"fixed windows {n_fix}")
+    pu.assert_parity(pu.gpu_run(d, t, fixed_window_cycles=n_fix), _oracle(d, t), label=f"fixed {n_fix}")
+    an = pa.PowerAnalysis(fixed_window_cycles=n_fix)
+    try:
+        an.load(d, t)
+        st = an.window_stats()
+    finally:
+        an.close()
+    pb = d.pin_base()
+    gate = np.repeat(np.repeat(np.arange(d.n_gates), np.diff(pb)), np.diff(t.pin_ptr))
+    run = gate.astype(np.int64) * t.n_cycles + t.evt_t // t.t_clk
+    if n_fix == 1:
+        assert st["n_windows"] == np.unique(run).shape[0]
+        assert st["max"] == np.bincount(np.unique(run, return_inverse=True)[1]).max()
+    assert st["p50"] <= st["p90"] <= st["p99"] <= st["max"]
+    assert abs(st["mean"] * st["n_windows"] - t.n_events) < 1e-6 * t.n_events
+
+
 def test_no_events():
     d, t = _random(seed=8, G=50, rate=0.0)
     assert t.n_events == 0
