@@ -14,9 +14,9 @@ namespace pa {
 // inside a chunk every gate's cycles are cut into 2^s equal windows, s chosen
 // per gate from its event density (the paper's event-density-aware per-gate
 // cycle partitioning).  The events are ordered by
-//   (chunk, gate, cycle, pin code, time),
+//   (chunk, gate, cycle, time, pin code),
 // so a window is one contiguous run, and inside a window the events of one
-// clock cycle form one run ordered by pin, then time.
+// clock cycle form one run in time order (events of one timestamp by pin).
 //
 // Packed 64-bit key of an event:
 //   bits [42, 64)  gate id (designs up to 2^22 - 1 gates)
@@ -24,7 +24,7 @@ namespace pa {
 //   bit  40        val: the pin's value after the event
 //   bits [32, 40)  S0: the gate's input-pin state at the window start (on
 //                  window heads; zero elsewhere)
-//   bits [ 0, 32)  lk = (cycle in chunk << (pb + tb)) | (pin code << tb) | tic
+//   bits [ 0, 32)  lk = (cycle in chunk << (pb + tb)) | (tic << pb) | pin code
 // tic = time minus the start of the event's clock cycle (tb bits); pin code =
 // input pin index 0..k-1, or out_code(pb) for the output pin.
 // ---------------------------------------------------------------------------

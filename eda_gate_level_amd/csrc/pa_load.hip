@@ -150,7 +150,7 @@ __device__ __forceinline__ EvPos ev_pos(int64_t e, const int64_t *evt_t, const u
 }
 
 __device__ __forceinline__ uint32_t lk_of(const EvPos &p, const LayoutFmt &f) {
-  return (p.cyc << (f.pb + f.tb)) | (p.code << f.tb) | p.tic;
+  return (p.cyc << (f.pb + f.tb)) | (p.tic << f.pb) | p.code;
 }
 
 // sort keys: (chunk, gate, lk) in one word, or (gate, lk) with the chunk apart

@@ -11,7 +11,7 @@
 // over every inter-event interval, spread over the cycle bins it overlaps.
 // The paper fuses both parts into one thread per (gate, cycle window)
 // (Fig. 7).  This pass keeps the fusion and maps it onto 64-lane waves:
-//   * the events are laid out by (time chunk, gate, clock cycle, pin, time);
+//   * the events are laid out by (time chunk, gate, clock cycle, time, pin);
 //     every gate's part of a chunk is cut into density-aware windows whose
 //     first event carries the gate's input state at the window start;
 //   * a block owns a range of whole windows inside one chunk and each of its
@@ -19,13 +19,14 @@
 //     per lane, 16-byte loads), the next batch prefetched into registers;
 //   * the state before every event is a segmented XOR scan of the input
 //     events' pin bits across the wave (DPP row shifts and broadcasts), the
-//     segments being the windows: the k-way merge of Sec. 2.4.2 at cycle
-//     granularity.  Inside one (gate, cycle) run the events are pin-major,
-//     so where a run holds several pins their time order is fixed up by a
-//     short walk over the run, which also finds the input pins switching at
-//     the same timestamp (all of them see the state before it);
-//   * a glitch is an event whose previous event in the layout is on the same
-//     pin in the same cycle (Fig. 7, Eq. 2);
+//     segments being the windows: the k-way merge of Sec. 2.4.2, since the
+//     layout is already in time order.  Events of one timestamp are
+//     adjacent; each sees the state before the first of them, and the lowest
+//     input pin among them charges the leakage change of the whole set;
+//   * a glitch is an event whose pin has an earlier event in the same
+//     (gate, cycle) run: a segmented OR scan of pin bits over the runs
+//     (Fig. 7); its pulse width and the previous slew come from that earlier
+//     event, found by a short step back over the run (Eq. 2);
 //   * one lane per event: state-selected LUT, bilinear on slew and load
 //     (Sec. 2.4.1, Fig. 2), switching energy (Eq. 1), energies added to
 //     per-cycle bins in LDS;
@@ -121,6 +122,27 @@ __device__ __forceinline__ uint32_t seg_scan(uint32_t w) {
   return w;
 }
 
+// Glitch-scan element: low 16 bits = pins with an event so far in the run,
+// kRun = a (gate, cycle) run starts here.  a then b: b restarts or the sets join.
+constexpr uint32_t kRun = 0x10000u;
+__device__ __forceinline__ uint32_t or_combine(uint32_t a, uint32_t b) { return (b & kRun) ? b : (a | b); }
+
+template <int CTRL, int ROWS = 0xF>
+__device__ __forceinline__ uint32_t or_step(uint32_t w) {
+  const uint32_t t = dpp_mov<CTRL, ROWS>(w) | w;
+  return (w & kRun) ? w : t;
+}
+
+__device__ __forceinline__ uint32_t or_scan(uint32_t w) {
+  w = or_step<0x111>(w);
+  w = or_step<0x112>(w);
+  w = or_step<0x114>(w);
+  w = or_step<0x118>(w);
+  w = or_step<0x142, 0xA>(w);
+  w = or_step<0x143, 0xC>(w);
+  return w;
+}
+
 struct CellLds {
   double2 *axw;
   float *thr;
@@ -153,7 +175,8 @@ template <bool CELL_LDS, bool DIAG, int NIN>
 __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   extern __shared__ __align__(16) unsigned char s_dyn[];
   __shared__ uint32_t st_lk[kNW][kB];  // batch events (lk) for the in-cycle walk
-  __shared__ uint8_t st_gh[kNW][kB];   // run-start flags of the batch events
+  __shared__ uint8_t st_gh[kNW][kB];   // tie flags of the batch events (same run, same time as the one before)
+  __shared__ float st_sl[kNW][kB];     // slews of the batch events
   __shared__ double s_red[kNW][8];
   __shared__ double s_scan[kNW];
 
@@ -261,9 +284,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       const int npos = base + end;
       if (npos < wend) load_batch(npos);
 
-      const uint32_t c0 = (lk0 >> tb) & outc, c1 = (lk1 >> tb) & outc;  // pin codes
+      const uint32_t c0 = lk0 & outc, c1 = lk1 & outc;                    // pin codes
       const uint32_t y0 = lk0 >> cs, y1 = lk1 >> cs;                      // cycles in the chunk
-      const uint32_t t0 = lk0 & tmask, t1 = lk1 & tmask;                  // time inside the cycle
+      const uint32_t t0 = (lk0 >> pb) & tmask, t1 = (lk1 >> pb) & tmask;  // time inside the cycle
       const bool in0 = c0 != outc, in1 = c1 != outc;
       const uint32_t g0 = h0 >> 10, g1 = h1 >> 10;
       uint32_t gi0 = 0, gi1 = 0;
@@ -286,61 +309,87 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       uint32_t S1s = hd1 ? (h1 & 0xFFu) : (I0 & 0xFFu);
       carry = (uint32_t)__builtin_amdgcn_readlane((int)I, (end - 1) >> 1);
 
-      // ---- runs of one gate in one cycle with input events on several pins:
-      // time order across pins.  Runs are pin-major with the output last, so
-      // such a run has two adjacent input events on different pins; without
-      // one the defaults below hold for every event of the batch.
+      // ---- glitches: the pin already has an event in this (gate, cycle) run
+      // (Sec. 2.4.1, Fig. 7); runs never cross a batch, so no carry
+      // (only batches with a run of two or more events can hold one)
+      bool gl0 = false, gl1 = false;
+      if ((__ballot(a0 && !gh0) | __ballot(a1 && !gh1)) != 0ull) {
+        const uint32_t u0 = a0 ? (1u << c0) : 0u, u1 = a1 ? (1u << c1) : 0u;
+        const uint32_t Io = or_scan(or_combine(gh0 ? (kRun | u0) : u0, gh1 ? (kRun | u1) : u1));
+        // (the lane move runs in every lane: a lane whose value is not taken
+        // must still provide its own to the next one)
+        const uint32_t Xo = dpp_mov<0x138>(Io) & 0xFFFFu;  // lane 0 reads 0: a batch starts a run
+        const uint32_t seen0 = gh0 ? 0u : Xo;
+        const uint32_t seen1 = gh1 ? 0u : (seen0 | u0);
+        gl0 = a0 && ((seen0 >> c0) & 1u);
+        gl1 = a1 && ((seen1 >> c1) & 1u);
+      }
+
+      // ---- events of one gate at one timestamp (ties), adjacent in the
+      // layout: each sees the state before the first of them (the scan
+      // counted the earlier ones, which are inputs: the output code is the
+      // highest), and the first, the lowest input pin, charges the leakage
+      // change of all their input pins together
+      const uint32_t tp0 = (lkp0 >> pb) & tmask;  // time of the event before slot i0
+      const bool tie0 = a0 && !gh0 && t0 == tp0;
+      const bool tie1 = a1 && !gh1 && t1 == t0;
       uint32_t mk0 = 1u << c0, mk1 = 1u << c1;  // input pins switching at the event's timestamp
-      bool ow0 = true, ow1 = true;              // lowest of them: charges the leakage change
-      const uint32_t cp0 = (lkp0 >> tb) & outc;  // pin code of the event before slot i0
-      const bool dw0 = a0 && in0 && !gh0 && cp0 != outc && cp0 != c0;
-      const bool dw1 = a1 && in1 && !gh1 && in0 && c0 != c1;
-      if (__ballot(dw0 || dw1) != 0ull) {
+      const bool ow0 = !tie0, ow1 = !tie1;      // first of its timestamp
+      uint32_t tq0 = 0, tq1 = 0;                // time of the pin's previous event (glitches)
+      float sq0 = 0.f, sq1 = 0.f;               // its slew
+      if ((__ballot(tie0 || tie1) | __ballot(gl0 || gl1)) != 0ull) {
         slk[i0] = lk0;
         slk[i1] = lk1;
-        sgh[i0] = (uint8_t)(gh0 || i0 >= end);
-        sgh[i1] = (uint8_t)(gh1 || i1 >= end);
+        sgh[i0] = (uint8_t)tie0;
+        sgh[i1] = (uint8_t)tie1;
+        st_sl[wid][i0] = s0;
+        st_sl[wid][i1] = s1;
         wave_sync();
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int p = r ? i1 : i0;
-          const bool act = (r ? (a1 && in1) : (a0 && in0));
-          const uint32_t cx = r ? c1 : c0, tx = r ? t1 : t0;
-          const bool ghx = r ? gh1 : gh0;
-          uint32_t corr = 0, mk = 1u << cx;
-          bool ow = true;
-          bool bk = act && !ghx;
-          bool fw = act && p + 1 < end && !sgh[p + 1];
-          auto visit = [&](uint32_t ly) {
-            const uint32_t j = (ly >> tb) & outc;
-            if (j != outc && j != cx) {
-              const uint32_t ty = ly & tmask;
-              if (j < cx ? ty >= tx : ty < tx) corr ^= 1u << j;
-              if (ty == tx) {
-                mk |= 1u << j;
-                if (j < cx) ow = false;
-              }
-            }
-          };
-          for (int d = 1; __ballot(bk || fw) != 0ull; ++d) {
+          const uint32_t cx = r ? c1 : c0;
+          // back over the earlier events of the same timestamp: undo their toggles
+          uint32_t corr = 0;
+          bool bk = r ? tie1 : tie0;
+          for (int y = p - 1; __ballot(bk) != 0ull; --y) {
             if (bk) {
-              const int y = p - d;
-              visit(slk[y]);
-              bk = !sgh[y];
-            }
-            if (fw) {
-              const int y = p + d;
-              visit(slk[y]);
-              fw = y + 1 < end && !sgh[y + 1];
+              corr ^= 1u << (slk[y] & outc);
+              bk = sgh[y] != 0;
             }
           }
-          if (r) { S1s ^= corr; mk1 = mk; ow1 = ow; } else { S0s ^= corr; mk0 = mk; ow0 = ow; }
+          // forward over the later ones: the input pins switching with this event
+          uint32_t mk = 1u << cx;
+          bool fw = (r ? (a1 && in1) : (a0 && in0)) && p + 1 < end && sgh[p + 1];
+          for (int y = p + 1; __ballot(fw) != 0ull; ++y) {
+            if (fw) {
+              const uint32_t j = slk[y] & outc;
+              if (j != outc) mk |= 1u << j;
+              fw = y + 1 < end && sgh[y + 1];
+            }
+          }
+          // glitch: back to the pin's previous event of the run (it exists, so
+          // the step stops there; the batch start bounds it all the same)
+          bool sr = r ? gl1 : gl0;
+          uint32_t tq = 0;
+          float sq = 0.f;
+          for (int y = p - 1; __ballot(sr) != 0ull; --y) {
+            if (sr) {
+              if (y < first) {
+                sr = false;
+              } else if ((slk[y] & outc) == cx) {
+                tq = (slk[y] >> pb) & tmask;
+                sq = st_sl[wid][y];
+                sr = false;
+              }
+            }
+          }
+          if (r) { S1s ^= corr; mk1 = mk; tq1 = tq; sq1 = sq; } else { S0s ^= corr; mk0 = mk; tq0 = tq; sq0 = sq; }
         }
         wave_sync();
       }
 
       // ---- one event per lane slot: energy, glitch, leakage change, bins
-      const float sp0 = __int_as_float((int)dpp_mov<0x138>((uint32_t)__float_as_int(s1)));
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const bool act = r ? a1 : a0;
@@ -348,12 +397,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         const uint32_t lk = r ? lk1 : lk0, hw = r ? h1 : h0;
         const uint32_t code = r ? c1 : c0, cyc = r ? y1 : y0, tic = r ? t1 : t0;
         const bool input = r ? in1 : in0;
-        const bool gh = r ? gh1 : gh0;
         const uint32_t info = r ? gi1 : gi0;
         const double2 cw = r ? cw1 : cw0;
         const float sl = r ? s1 : s0;
-        const uint32_t lkp = r ? lk0 : lkp0;
-        const float slp = r ? s0 : sp0;
         const uint32_t cell = info & 0xFFFFFFu;
         const uint2 m = meta_of(cell);
         const uint32_t kk = m.x & 15u, lb = m.x >> 4;
@@ -387,14 +433,13 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         const double v1 = L10 + cw.x * (L11 - L10);
         const double Eint = v0 + fa * (v1 - v0);
         const double E = input ? Eint : (((hw >> 8) & 1u) ? cw.y : 0.0);  // Eq. 1: 0->1 output events only
-        // glitch: the previous event of the same pin lies in the same cycle (Fig. 7)
-        const bool glitch = !gh && ((lk ^ lkp) >> tb) == 0u;
+        const bool glitch = r ? gl1 : gl0;
         double contrib = E;
         double lk_gate = 0.0;  // leakage of this power change up to t_max (per-gate output)
         double dyn = 0.0;      // this event's dynamic energy after the glitch scale
         if (glitch) {
-          const double pw = (double)(tic - (lkp & tmask));
-          const double rr = pw / (0.5 * ((double)sl + (double)slp));  // Eq. 2 (reading)
+          const double pw = (double)(tic - (r ? tq1 : tq0));
+          const double rr = pw / (0.5 * ((double)sl + (double)(r ? sq1 : sq0)));  // Eq. 2 (reading)
           contrib = (rr > 1.0 ? 1.0 : rr) * E;
           e_gl += contrib;
           ++n_gl;

@@ -116,7 +116,7 @@ int pa_load_design(pa_ctx *ctx, int64_t n_gates, const int32_t *gate_cell, const
  * The events are validated (PA_EDATA for a broken rule above; the
  * previously loaded events stay usable) and re-laid out into library-owned
  * memory: time chunks of chunk_cycles cycles; inside a chunk the events are
- * ordered by gate, clock cycle, pin and time, and every gate's part of a
+ * ordered by gate, clock cycle, time and pin, and every gate's part of a
  * chunk is cut into 2^s equal windows sized from the gate's event density
  * (the paper's event-density-aware per-gate cycle partitioning). */
 int pa_load_events(pa_ctx *ctx, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr,
