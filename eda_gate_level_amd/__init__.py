@@ -13,10 +13,11 @@ from typing import Optional
 
 from ._pa import (EXPORTS, PA_EDATA, PA_EHIP, PA_EINVAL, PA_ENOMEM, PA_ESTATE, PA_OK, PaError, lib, pa_create,
                   pa_destroy, pa_get_info, pa_get_window_stats, pa_last_error, pa_load_design, pa_load_events,
-                  pa_run, pa_run_gates, pa_set_stream, pa_set_timing)
+                  pa_pack_text, pa_run, pa_run_gates, pa_run_text, pa_set_stream, pa_set_timing)
 
 __all__ = ["PowerAnalysis", "PaError", "pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error",
            "pa_load_design", "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info", "pa_get_window_stats",
+           "pa_pack_text", "pa_run_text",
            "lib", "EXPORTS", "PA_OK",
            "PA_EINVAL", "PA_EDATA",
            "PA_ENOMEM", "PA_EHIP", "PA_ESTATE"]
@@ -110,6 +111,22 @@ class PowerAnalysis:
             tot = pa_run(self.ctx, outputs["wave_J"], outputs["cyc_events"], outputs["cyc_glitches"],
                          outputs.get("evt_glitch"), outputs.get("evt_state_before"))
         return dict(totals=tot, **outputs)
+
+    def run_text(self, text, t_clk: int, t_max: int, tick_s: float = 1e-15, segment_cycles: int = 0,
+                 n_threads: int = 0, serial: bool = False) -> dict:
+        """Power analysis of VCD-like activity text (host bytes), packed on host
+        threads segment by segment while the GPU computes the previous one.
+        Needs a loaded design; leaves no events loaded."""
+        import torch
+
+        C, dev = -(-int(t_max) // int(t_clk)), self.device
+        outs = dict(wave_J=torch.empty(C, dtype=torch.float64, device=dev),
+                    cyc_events=torch.empty(C, dtype=torch.uint64, device=dev),
+                    cyc_glitches=torch.empty(C, dtype=torch.uint64, device=dev))
+        tot, st = pa_run_text(self.ctx, text, t_clk, t_max, tick_s, outs["wave_J"], outs["cyc_events"],
+                              outs["cyc_glitches"], segment_cycles, n_threads, serial)
+        self.n_cycles, self.n_events = 0, 0
+        return dict(totals=tot, stats=st, **outs)
 
     def window_stats(self) -> dict:
         """Events per (chunk, gate, window) of the loaded layout: count, mean, p50/p90/p99, max."""

@@ -20,7 +20,8 @@ _NAMES = {PA_EINVAL: "PA_EINVAL", PA_EDATA: "PA_EDATA", PA_ENOMEM: "PA_ENOMEM", 
           PA_ESTATE: "PA_ESTATE"}
 
 EXPORTS = ("pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error", "pa_load_design",
-           "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info", "pa_get_window_stats")
+           "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info", "pa_get_window_stats", "pa_pack_text",
+           "pa_run_text")
 
 
 class PaError(RuntimeError):
@@ -63,6 +64,20 @@ class pa_info(C.Structure):
         return d
 
 
+class pa_text_opts(C.Structure):
+    _fields_ = [("segment_cycles", C.c_int32), ("n_threads", C.c_int32), ("serial", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class pa_text_stats(C.Structure):
+    _fields_ = [("n_segments", C.c_int64), ("n_events", C.c_int64), ("max_segment_events", C.c_int64),
+                ("text_bytes", C.c_int64), ("header_s", C.c_double), ("index_s", C.c_double),
+                ("parse_s", C.c_double), ("gpu_s", C.c_double), ("wall_s", C.c_double)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 def load_library(path: str = LIB_PATH) -> C.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"libpa.so not built ({path}); run __graft_entry__.build() or python -m "
@@ -83,8 +98,11 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.pa_run_gates.argtypes = [P, C.POINTER(pa_totals), P, P, P, P]
     L.pa_get_info.argtypes = [P, C.POINTER(pa_info)]
     L.pa_get_window_stats.argtypes = [P, C.POINTER(pa_window_stats)]
+    L.pa_pack_text.argtypes = [P, i64, i64, i32, i64, C.POINTER(i64), P, P, P, P, P]
+    L.pa_run_text.argtypes = [P, P, i64, i64, i64, dbl, C.POINTER(pa_text_opts), C.POINTER(pa_totals), P, P, P,
+                              C.POINTER(pa_text_stats)]
     for name in ("pa_create", "pa_set_stream", "pa_set_timing", "pa_load_design", "pa_load_events", "pa_run",
-                 "pa_run_gates", "pa_get_info", "pa_get_window_stats"):
+                 "pa_run_gates", "pa_get_info", "pa_get_window_stats", "pa_pack_text", "pa_run_text"):
         getattr(L, name).restype = C.c_int
     return L
 
@@ -212,3 +230,52 @@ def pa_get_info(ctx) -> dict:
     info = pa_info()
     _check(lib().pa_get_info(ctx, C.byref(info)))
     return info.as_dict()
+
+
+def _text_ptr(text):
+    """Host address and length of activity text given as bytes, bytearray or a uint8 numpy array."""
+    import numpy as np
+
+    if isinstance(text, bytes):
+        return C.c_void_p(C.cast(C.c_char_p(text), C.c_void_p).value), len(text), text
+    if isinstance(text, bytearray):
+        buf = (C.c_char * len(text)).from_buffer(text)
+        return C.c_void_p(C.addressof(buf)), len(text), buf
+    a = np.ascontiguousarray(text, dtype=np.uint8)
+    return C.c_void_p(a.ctypes.data), int(a.size), a
+
+
+def pa_pack_text(text, n_pins: int, n_threads: int = 0) -> dict:
+    """Host CSR of the text's events (numpy arrays): pin_ptr, pin_init, evt_t, evt_val, evt_slew."""
+    import numpy as np
+
+    ptr, n, keep = _text_ptr(text)
+    ne = C.c_int64(0)
+    _check(lib().pa_pack_text(ptr, n, int(n_pins), int(n_threads), 0, C.byref(ne), None, None, None, None, None))
+    E = int(ne.value)
+    out = dict(pin_ptr=np.empty(n_pins + 1, np.int64), pin_init=np.empty(n_pins, np.uint8),
+               evt_t=np.empty(max(E, 1), np.int64), evt_val=np.empty(max(E, 1), np.uint8),
+               evt_slew=np.empty(max(E, 1), np.float32))
+    _check(lib().pa_pack_text(ptr, n, int(n_pins), int(n_threads), max(E, 1), C.byref(ne),
+                              *(C.c_void_p(out[k].ctypes.data) for k in ("pin_ptr", "pin_init", "evt_t", "evt_val",
+                                                                          "evt_slew"))))
+    del keep
+    for k in ("evt_t", "evt_val", "evt_slew"):
+        out[k] = out[k][:E]
+    return out
+
+
+def pa_run_text(ctx, text, t_clk: int, t_max: int, tick_s: float, wave_J, cyc_events, cyc_glitches,
+                segment_cycles: int = 0, n_threads: int = 0, serial: bool = False):
+    """Totals and packing statistics of the text's power analysis (outputs written to the device tensors)."""
+    import torch
+
+    ptr, n, keep = _text_ptr(text)
+    opts = pa_text_opts(int(segment_cycles), int(n_threads), int(bool(serial)), 0)
+    tot, st = pa_totals(), pa_text_stats()
+    _check(lib().pa_run_text(ctx, ptr, n, int(t_clk), int(t_max), float(tick_s), C.byref(opts), C.byref(tot),
+                             _ptr(wave_J, torch.float64, name="wave_J"),
+                             _ptr(cyc_events, torch.uint64, name="cyc_events"),
+                             _ptr(cyc_glitches, torch.uint64, name="cyc_glitches"), C.byref(st)))
+    del keep
+    return tot.as_dict(), st.as_dict()

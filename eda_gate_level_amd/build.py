@@ -10,6 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
 SOURCES = ["pa_api.hip", "pa_load.hip", "pa_pass.hip"]
+HOST_SOURCES = ["pa_text.cpp"]  # plain C++ (the activity-text packer), built with the host compiler
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -35,6 +36,12 @@ def build(verbose: bool = False) -> str:
         cmd = [hipcc(), *HIPCC_FLAGS, "-c", "-o", obj, os.path.join(CSRC, src)]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
+    for src in HOST_SOURCES:
+        obj = os.path.join(CSRC, src.replace(".cpp", ".o"))
+        cmd = ["g++", "-O3", "-std=c++17", "-fPIC", "-pthread", f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+               "-c", "-o", obj, os.path.join(CSRC, src)]
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
+        objs.append(obj)
     for cmd, p in procs:
         out, _ = p.communicate()
         if p.returncode != 0:
@@ -43,7 +50,7 @@ def build(verbose: bool = False) -> str:
         if verbose and out:
             sys.stderr.write(out)
     tmp = LIB + ".tmp"
-    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs]
     subprocess.run(link, check=True)
     os.replace(tmp, LIB)
     for o in objs:

@@ -5,16 +5,23 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <chrono>
 #include <cmath>
+#include <condition_variable>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
+#include <limits>
+#include <mutex>
 #include <string>
+#include <thread>
 #include <vector>
 
 #include "pa.h"
 #include "pa_common.h"
 #include "pa_load.h"
+#include "pa_text.h"
 
 namespace {
 
@@ -697,6 +704,296 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
   info->max_segment_events = pa::kGroupMax;
   info->device_bytes = c->d.bytes() + c->ev.bytes();
   for (int k = 0; k < 4; ++k) info->kernel_ms[k] = c->kernel_ms[k];
+  return PA_OK;
+}
+
+
+}  // extern "C"
+
+// ------------------------------------------------------------ activity text --
+
+namespace {
+
+double now_s() {
+  return std::chrono::duration<double>(std::chrono::steady_clock::now().time_since_epoch()).count();
+}
+
+int text_threads(int32_t n) {
+  if (n > 0) return std::min<int32_t>(n, 256);
+  const unsigned h = std::thread::hardware_concurrency();
+  return (int)std::max(1u, std::min(16u, h ? h : 1u));
+}
+
+// one packed segment: pin_ptr, pin_init and the three event arrays in one block
+struct SegLayout {
+  size_t o_ptr = 0, o_init = 0, o_t = 0, o_val = 0, o_slew = 0, bytes = 0;
+};
+
+SegLayout seg_layout(int64_t P, int64_t E) {
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  SegLayout L;
+  size_t o = 0;
+  L.o_ptr = o;
+  o += al(sizeof(int64_t) * (size_t)(P + 1));
+  L.o_init = o;
+  o += al((size_t)P);
+  L.o_t = o;
+  o += al(sizeof(int64_t) * (size_t)E);
+  L.o_val = o;
+  o += al((size_t)E);
+  L.o_slew = o;
+  o += al(sizeof(float) * (size_t)E);
+  L.bytes = std::max<size_t>(o, 256);
+  return L;
+}
+
+pa::text::Csr carve(void *base, const SegLayout &L) {
+  char *b = static_cast<char *>(base);
+  return pa::text::Csr{reinterpret_cast<int64_t *>(b + L.o_ptr), reinterpret_cast<uint8_t *>(b + L.o_init),
+                       reinterpret_cast<int64_t *>(b + L.o_t), reinterpret_cast<uint8_t *>(b + L.o_val),
+                       reinterpret_cast<float *>(b + L.o_slew)};
+}
+
+struct PinnedBuf {
+  void *p = nullptr;
+  ~PinnedBuf() {
+    if (p) (void)hipHostFree(p);
+  }
+};
+
+}  // namespace
+
+extern "C" {
+
+int pa_pack_text(const char *text, int64_t text_len, int64_t n_pins, int32_t n_threads, int64_t max_events,
+                 int64_t *n_events, int64_t *pin_ptr, uint8_t *pin_init, int64_t *evt_t, uint8_t *evt_val,
+                 float *evt_slew) {
+  if (text_len < 0 || (!text && text_len > 0)) return fail(PA_EINVAL, "pa_pack_text: bad text");
+  if (!n_events) return fail(PA_EINVAL, "pa_pack_text: n_events is NULL");
+  if (n_threads < 0) return fail(PA_EINVAL, "pa_pack_text: n_threads < 0");
+  const bool query = !pin_ptr && !pin_init && !evt_t && !evt_val && !evt_slew;
+  if (!query && (!pin_ptr || !pin_init || !evt_t || !evt_val || !evt_slew))
+    return fail(PA_EINVAL, "pa_pack_text: give all output arrays or none");
+  *n_events = 0;
+  std::string err;
+  pa::text::Header h;
+  if (pa::text::parse_header(text, (size_t)text_len, h, err) != 0) return fail(PA_EDATA, "pa_pack_text: %s", err.c_str());
+  if (h.n_pins != n_pins)
+    return fail(PA_EDATA, "pa_pack_text: the text declares %lld variables, n_pins is %lld", (long long)h.n_pins,
+                (long long)n_pins);
+  pa::text::Pool pool(text_threads(n_threads));
+  pa::text::SegmentIndex ix;
+  const int64_t big = std::numeric_limits<int64_t>::max();
+  if (pa::text::index_segments(text, (size_t)text_len, h, big, 1, big, pool, ix, err) != 0)
+    return fail(PA_EDATA, "pa_pack_text: %s", err.c_str());
+  *n_events = ix.events[0];
+  if (query) return PA_OK;
+  if (max_events < ix.events[0])
+    return fail(PA_EINVAL, "pa_pack_text: %lld value changes, max_events is %lld", (long long)ix.events[0],
+                (long long)max_events);
+  pa::text::Packer pk(pool);
+  std::vector<uint8_t> init_end((size_t)n_pins);
+  const pa::text::Csr out{pin_ptr, pin_init, evt_t, evt_val, evt_slew};
+  if (pk.pack(text, ix.begin[0], ix.begin[1], h, ix.events[0], 0, h.init.data(), out, init_end.data(), err) != 0)
+    return fail(PA_EDATA, "pa_pack_text: %s", err.c_str());
+  return PA_OK;
+}
+
+int pa_run_text(pa_ctx *c, const char *text, int64_t text_len, int64_t t_clk, int64_t t_max, double tick_s,
+                const pa_text_opts *o, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
+                pa_text_stats *st) {
+  const double w0 = now_s();
+  if (!c) return fail(PA_EINVAL, "pa_run_text: NULL context");
+  if (!c->has_design) return fail(PA_ESTATE, "pa_run_text: no design loaded");
+  if (text_len < 0 || (!text && text_len > 0)) return fail(PA_EINVAL, "pa_run_text: bad text");
+  if (!out || !wave_J || !cyc_events || !cyc_glitches) return fail(PA_EINVAL, "pa_run_text: NULL output");
+  if (t_clk < 1 || t_clk >= (int64_t(1) << 32)) return fail(PA_EINVAL, "pa_run_text: t_clk out of range");
+  if (t_max < 1) return fail(PA_EINVAL, "pa_run_text: t_max must be > 0");
+  const int64_t C = (t_max + t_clk - 1) / t_clk;
+  if (C > (int64_t(1) << 28)) return fail(PA_EINVAL, "pa_run_text: more than 2^28 clock cycles");
+  if (!(tick_s > 0.0) || !std::isfinite(tick_s)) return fail(PA_EINVAL, "pa_run_text: tick_s must be > 0");
+  if (o && (o->segment_cycles < 0 || o->n_threads < 0 || o->serial < 0 || o->serial > 1 || o->reserved != 0))
+    return fail(PA_EINVAL, "pa_run_text: bad options");
+  const int64_t S = o && o->segment_cycles > 0 ? o->segment_cycles : 1024;
+  const bool serial = o && o->serial == 1;
+  HIPCHK(hipSetDevice(c->device));
+  const int64_t P = c->d.P;
+  hipStream_t s = c->stream;
+
+  std::string err;
+  double t0 = now_s();
+  pa::text::Header h;
+  if (pa::text::parse_header(text, (size_t)text_len, h, err) != 0) return fail(PA_EDATA, "pa_run_text: %s", err.c_str());
+  if (h.n_pins != P)
+    return fail(PA_EDATA, "pa_run_text: the text declares %lld variables, the design has %lld pins",
+                (long long)h.n_pins, (long long)P);
+  const double header_s = now_s() - t0;
+  pa::text::Pool pool(text_threads(o ? o->n_threads : 0));
+  const int64_t n_seg = (C + S - 1) / S, seg_ticks = S * t_clk;
+  t0 = now_s();
+  pa::text::SegmentIndex ix;
+  if (pa::text::index_segments(text, (size_t)text_len, h, seg_ticks, n_seg, t_max, pool, ix, err) != 0)
+    return fail(PA_EDATA, "pa_run_text: %s", err.c_str());
+  const double index_s = now_s() - t0;
+  int64_t e_max = 0, e_all = 0;
+  for (int64_t k = 0; k < n_seg; ++k) {
+    e_max = std::max(e_max, ix.events[(size_t)k]);
+    e_all += ix.events[(size_t)k];
+  }
+
+  const SegLayout L = seg_layout(P, e_max);
+  PinnedBuf host[2];
+  pa::text::Csr hcsr[2];
+  for (int i = 0; i < (serial ? 1 : 2); ++i) {
+    HIPCHK(hipHostMalloc(&host[i].p, L.bytes, hipHostMallocDefault));
+    hcsr[i] = carve(host[i].p, L);
+  }
+  DBuf dev;
+  HIPCHK(dev.alloc(L.bytes));
+  const pa::text::Csr dcsr = carve(dev.p, L);
+  std::vector<uint8_t> cur(h.init), nxt((size_t)P);
+  pa::text::Packer pk(pool);
+
+  // every segment's load replaces the context's events; none stay loaded
+  struct DropEvents {
+    pa_ctx *c;
+    ~DropEvents() { c->has_events = false; }
+  } drop{c};
+  double acc[4] = {0, 0, 0, 0}, parse_s = 0.0, gpu_s = 0.0;
+  uint64_t n_gl = 0;
+
+  // copy, load and run segment k from host slot `slot`; release() once the slot's copies are done
+  auto gpu_segment = [&](int slot, int64_t k, const std::function<void()> &release) -> int {
+    const int64_t c0 = k * S, ts = c0 * t_clk, te = std::min(t_max, ts + seg_ticks);
+    const int64_t E = ix.events[(size_t)k];
+    const pa::text::Csr &hc = hcsr[slot];
+    HIPCHK(hipMemcpyAsync(dcsr.pin_ptr, hc.pin_ptr, sizeof(int64_t) * (size_t)(P + 1), hipMemcpyHostToDevice, s));
+    if (P > 0) HIPCHK(hipMemcpyAsync(dcsr.pin_init, hc.pin_init, (size_t)P, hipMemcpyHostToDevice, s));
+    if (E > 0) {
+      HIPCHK(hipMemcpyAsync(dcsr.t, hc.t, sizeof(int64_t) * (size_t)E, hipMemcpyHostToDevice, s));
+      HIPCHK(hipMemcpyAsync(dcsr.val, hc.val, (size_t)E, hipMemcpyHostToDevice, s));
+      HIPCHK(hipMemcpyAsync(dcsr.slew, hc.slew, sizeof(float) * (size_t)E, hipMemcpyHostToDevice, s));
+    }
+    int rc = pa_load_events(c, P, E, dcsr.pin_ptr, dcsr.pin_init, dcsr.t, dcsr.val, dcsr.slew, t_clk, te - ts, tick_s);
+    const hipError_t se = hipStreamSynchronize(s);
+    release();
+    if (rc != PA_OK) return rc;
+    if (se != hipSuccess) return fail(PA_EHIP, "pa_run_text: HIP error %s", hipGetErrorString(se));
+    pa_totals t{};
+    rc = run_pass(c, &t, wave_J + c0, cyc_events + c0, cyc_glitches + c0, nullptr, nullptr, nullptr);
+    if (rc != PA_OK) return rc;
+    acc[0] += t.e_int_J;
+    acc[1] += t.e_sw_J;
+    acc[2] += t.e_gl_J;
+    acc[3] += t.e_leak_J;
+    n_gl += t.n_glitches;
+    return PA_OK;
+  };
+  auto pack = [&](int slot, int64_t k) -> int {
+    const double p0 = now_s();
+    const int rc = pk.pack(text, ix.begin[(size_t)k], ix.begin[(size_t)k + 1], h, ix.events[(size_t)k],
+                           k * seg_ticks, cur.data(), hcsr[slot], nxt.data(), err);
+    parse_s += now_s() - p0;
+    if (rc == 0) cur.swap(nxt);
+    return rc;
+  };
+
+  if (serial) {
+    for (int64_t k = 0; k < n_seg; ++k) {
+      if (pack(0, k) != 0) return fail(PA_EDATA, "pa_run_text: %s", err.c_str());
+      const double g0 = now_s();
+      const int rc = gpu_segment(0, k, [] {});
+      gpu_s += now_s() - g0;
+      if (rc != PA_OK) return rc;
+    }
+  } else {
+    std::mutex mu;
+    std::condition_variable cv;
+    int64_t packed = -1;
+    bool slot_free[2] = {true, true}, stop = false;
+    int grc = PA_OK;
+    std::string gmsg;
+    std::thread gpu([&] {
+      if (hipSetDevice(c->device) != hipSuccess) {
+        std::lock_guard<std::mutex> g(mu);
+        stop = true;
+        grc = PA_EHIP;
+        gmsg = "pa_run_text: hipSetDevice failed on the copy thread";
+        cv.notify_all();
+        return;
+      }
+      for (int64_t k = 0; k < n_seg; ++k) {
+        {
+          std::unique_lock<std::mutex> lk(mu);
+          cv.wait(lk, [&] { return stop || packed >= k; });
+          if (stop) return;
+        }
+        const int slot = (int)(k & 1);
+        const double g0 = now_s();
+        const int rc = gpu_segment(slot, k, [&] {
+          std::lock_guard<std::mutex> g(mu);
+          slot_free[slot] = true;
+          cv.notify_all();
+        });
+        gpu_s += now_s() - g0;
+        if (rc != PA_OK) {
+          std::lock_guard<std::mutex> g(mu);
+          stop = true;
+          grc = rc;
+          gmsg = g_err;
+          cv.notify_all();
+          return;
+        }
+      }
+    });
+    int prc = 0;
+    for (int64_t k = 0; k < n_seg; ++k) {
+      const int slot = (int)(k & 1);
+      {
+        std::unique_lock<std::mutex> lk(mu);
+        cv.wait(lk, [&] { return stop || slot_free[slot]; });
+        if (stop) break;
+        slot_free[slot] = false;
+      }
+      prc = pack(slot, k);
+      std::lock_guard<std::mutex> g(mu);
+      if (prc != 0) {
+        stop = true;
+        cv.notify_all();
+        break;
+      }
+      packed = k;
+      cv.notify_all();
+    }
+    gpu.join();
+    // the copy thread works on earlier segments than the parser: its error comes first
+    if (grc != PA_OK) return fail(grc, "%s", gmsg.c_str());
+    if (prc != 0) return fail(PA_EDATA, "pa_run_text: %s", err.c_str());
+  }
+
+  const double window = (double)t_max * tick_s;
+  out->e_int_J = acc[0];
+  out->e_sw_J = acc[1];
+  out->e_gl_J = acc[2];
+  out->e_leak_J = acc[3];
+  out->p_int_W = acc[0] / window;
+  out->p_sw_W = acc[1] / window;
+  out->p_gl_W = acc[2] / window;
+  out->p_leak_W = acc[3] / window;
+  out->n_events = (uint64_t)e_all;
+  out->n_glitches = n_gl;
+  out->n_cycles = C;
+  if (st) {
+    st->n_segments = n_seg;
+    st->n_events = e_all;
+    st->max_segment_events = e_max;
+    st->text_bytes = text_len;
+    st->header_s = header_s;
+    st->index_s = index_s;
+    st->parse_s = parse_s;
+    st->gpu_s = gpu_s;
+    st->wall_s = now_s() - w0;
+  }
   return PA_OK;
 }
 

@@ -174,6 +174,81 @@ typedef struct {
 } pa_info;
 int pa_get_info(pa_ctx *ctx, pa_info *info);
 
+/* ---- Activity text: host-side event packing, overlapped with the GPU ----
+ * The paper's GPU flow packs the events of its activity files on host
+ * threads while the GPU computes, so that packing hides behind the power
+ * computation (its Sec. 5, end-to-end runtime breakdown, Fig. 13).  The text
+ * read here is a subset of VCD with one slew per value change (the paper
+ * does not print its input format; slews come from timing analysis there):
+ *   - "$var <type> 1 <id> <name> [<more>] $end" declares one variable per
+ *     pin, in the pin order of pa_load_events; other "$<keyword> ... $end"
+ *     sections of the definitions are skipped; "$enddefinitions $end" ends
+ *     them;
+ *   - optionally "#0", then "$dumpvars <v><id> ... $end": the value of every
+ *     pin at t = 0 (each pin at least once; the last entry counts);
+ *   - then lines "#<t>" (a timestamp in ticks, nondecreasing, at most 18
+ *     digits) and "<v><id> <slew>" (a value change at the current time; the
+ *     slew in ticks as a decimal number, read as the nearest float32); the
+ *     value changes before the first "#<t>" of the body are at t = 0; blank
+ *     lines are allowed;
+ *   <v> is 0 or 1; <id> is 1..8 characters in '!'..'~'.  Anything else
+ *   (x/z values, vectors, unknown identifiers, other sections after
+ *   $dumpvars, decreasing timestamps) is PA_EDATA, with the byte offset in
+ *   pa_last_error().  The rules of pa_load_events (strictly increasing
+ *   times per pin, values alternating from the initial value, slews finite
+ *   and > 0) are checked where the events are loaded.
+ *
+ * pa_pack_text: the whole text as one CSR, in HOST memory (no device, no
+ * context).  text[text_len] is host memory; n_pins must equal the declared
+ * variables (PA_EDATA otherwise).  n_threads host threads (0 = min(16,
+ * hardware threads), at most 256).  *n_events receives the number of value
+ * changes.  With pin_ptr, pin_init, evt_t, evt_val and evt_slew all NULL
+ * nothing else is written (a size query); otherwise all must be given,
+ * pin_ptr[n_pins + 1], pin_init[n_pins], and the event arrays of max_events
+ * entries (PA_EINVAL if fewer than *n_events).  At most 2^31 - 1 events. */
+int pa_pack_text(const char *text, int64_t text_len, int64_t n_pins, int32_t n_threads, int64_t max_events,
+                 int64_t *n_events, int64_t *pin_ptr, uint8_t *pin_init, int64_t *evt_t, uint8_t *evt_val,
+                 float *evt_slew);
+
+typedef struct {
+  int32_t segment_cycles; /* clock cycles per segment (0 = 1024) */
+  int32_t n_threads;      /* host threads that parse (0 = min(16, hardware threads)), at most 256 */
+  int32_t serial;         /* 0: parse segment k + 1 while the GPU loads and computes segment k;
+                             1: one after the other (to measure what the overlap hides) */
+  int32_t reserved;       /* 0 */
+} pa_text_opts;
+
+typedef struct {
+  int64_t n_segments, n_events, max_segment_events, text_bytes;
+  double header_s; /* definitions and initial values (one thread) */
+  double index_s;  /* cutting the value changes into segments (all threads) */
+  double parse_s;  /* parsing and packing the segments, summed */
+  double gpu_s;    /* copies, event loads and passes of the segments, summed */
+  double wall_s;   /* the whole call */
+} pa_text_stats;
+
+/* The power analysis of an activity text: pa_load_events + pa_run over the
+ * text's events, computed segment by segment.  Segment k holds clock cycles
+ * [k S, (k + 1) S) (S = segment_cycles; the last may be shorter); host
+ * threads parse and pack segment k + 1 into pinned host memory while a
+ * second host thread copies segment k to the device, loads it (the load's
+ * validation, layout and windows) and runs the pass into wave_J[k S ...],
+ * cyc_events[k S ...] and cyc_glitches[k S ...].  Every quantity the paper
+ * defines stays inside a clock cycle, given the pin values at the cycle
+ * start, so the segments are independent: the waveform and counts equal
+ * those of one pa_load_events + pa_run of the whole trace, and the totals
+ * equal them up to fp64 summation order.
+ *   text[text_len]  HOST memory (the format above)
+ *   t_clk, t_max, tick_s  as for pa_load_events
+ *   opts    may be NULL (all defaults); stats (HOST) may be NULL
+ *   out     HOST totals over [0, t_max)
+ *   wave_J, cyc_events, cyc_glitches  device, C = ceil(t_max / t_clk) entries
+ * Needs a loaded design (PA_ESTATE).  The context holds no events afterwards
+ * (pa_run then reports PA_ESTATE until the next pa_load_events). */
+int pa_run_text(pa_ctx *ctx, const char *text, int64_t text_len, int64_t t_clk, int64_t t_max, double tick_s,
+                const pa_text_opts *opts, pa_totals *out, double *wave_J, uint64_t *cyc_events,
+                uint64_t *cyc_glitches, pa_text_stats *stats);
+
 #ifdef __cplusplus
 }
 #endif

@@ -1,0 +1,254 @@
+"""Activity text: the oracle's plain reader pinned, and the library's host
+packer (pa_pack_text, host code only, no GPU) against it.
+
+The paper packs the events of its activity files on host threads while the
+GPU computes ("GPU-Accelerated Gate-Level Time-Based Power Analysis via
+Event-Density-Aware Partitioning and Kernel Fusion", Sec. 5, Fig. 13).  The
+text here is the library's reading of such files: a VCD subset with one slew
+per value change.  What pins the oracle reader:
+  - a hand-worked golden text (tests/golden/text_small.*);
+  - the float32 rounding against values built from the float32 bit
+    patterns (exact values, midpoints with ties to even, the values next to
+    midpoints, the smallest and largest magnitudes);
+  - round trips: the text written from a seeded trace reads back as that
+    trace, for one-, two- and three-character identifiers;
+  - rejection of text outside the format.
+The packer must then give the oracle's arrays bit for bit.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import vcd_text as ov
+from workloads import synth, vcd_text
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+KEYS = ("pin_ptr", "pin_init", "evt_t", "evt_val", "evt_slew")
+
+
+def _lib_pack(text, n_pins, n_threads=0):
+    import eda_gate_level_amd as pa
+
+    return pa.pa_pack_text(text, n_pins, n_threads)
+
+
+def _same(a, b, label=""):
+    for k in KEYS:
+        x, y = np.asarray(a[k]), np.asarray(b[k])
+        assert x.shape == y.shape, f"{label} {k}: shapes {x.shape} {y.shape}"
+        if k == "evt_slew":
+            assert np.array_equal(x.view(np.uint32), y.astype(np.float32).view(np.uint32)), f"{label} {k}"
+        else:
+            assert np.array_equal(x, y), f"{label} {k}"
+
+
+def _trace_dict(t):
+    return {k: getattr(t, k) for k in KEYS}
+
+
+def _small_trace(seed, P, rate=2.0, C=30, T=1000):
+    rng = np.random.default_rng(seed)
+    return synth.poisson_trace(rng, np.full(P, rate), C, T)
+
+
+# ------------------------------------------------------------ oracle pins --
+
+def test_golden_text_oracle():
+    g = json.load(open(os.path.join(GOLDEN, "text_small.json")))
+    text = open(os.path.join(GOLDEN, g["text"]), "rb").read()
+    o = ov.parse(text, g["n_pins"])
+    _same(o, {k: np.array(g[k]) for k in KEYS}, "golden")
+
+
+def _f32(bits):
+    return np.array([bits], dtype=np.uint32).view(np.float32)[0]
+
+
+def test_nearest_float32_from_bit_patterns():
+    from fractions import Fraction
+
+    rng = np.random.default_rng(7)
+    bits = np.concatenate([rng.integers(1, 0x7F7FFFFF, size=300, dtype=np.uint32),
+                           np.array([1, 2, 0x007FFFFF, 0x00800000, 0x3F800000, 0x4B800000, 0x7F7FFFFE],
+                                    dtype=np.uint32)])
+    for b in bits.tolist():
+        f, g = _f32(b), _f32(b + 1)
+        qf, qg = Fraction(float(f)), Fraction(float(g))
+        mid = (qf + qg) / 2
+        tiny = (qg - qf) / 1000
+        assert ov.nearest_float32(qf) == f
+        assert ov.nearest_float32(qg) == g
+        # ties go to the even bit pattern
+        assert ov.nearest_float32(mid) == (f if b % 2 == 0 else g)
+        assert ov.nearest_float32(mid - tiny) == f
+        assert ov.nearest_float32(mid + tiny) == g
+    # beyond the largest float, halfway and above round to infinity
+    big = Fraction(float(_f32(0x7F7FFFFF)))
+    ulp = big - Fraction(float(_f32(0x7F7FFFFE)))
+    assert ov.nearest_float32(big + ulp / 2 - ulp / 1000) == _f32(0x7F7FFFFF)
+    assert np.isinf(ov.nearest_float32(big + ulp / 2))
+    assert ov.nearest_float32(Fraction(0)) == 0.0
+
+
+def test_read_decimal_forms():
+    assert ov.read_decimal("12") == 12.0
+    assert ov.read_decimal("12.") == 12.0
+    assert ov.read_decimal(".5") == 0.5
+    assert ov.read_decimal("0.000125e3") == 0.125
+    assert ov.read_decimal("185878398e-4") == np.float32(18587.8398)
+    assert ov.read_decimal("16777217") == 16777216.0  # halfway, to even
+    assert ov.read_decimal("16777219") == 16777220.0  # halfway, to even
+    assert ov.read_decimal("16777217.000000001") == 16777218.0  # just above halfway
+    for bad in ("", ".", "e5", "1e", "1e+", "+1", "-1", "1.2.3", "0x10", "inf", "nan", "1_0"):
+        with pytest.raises(ValueError):
+            ov.read_decimal(bad)
+
+
+@pytest.mark.parametrize("P", [5, 94, 95, 9000])
+def test_round_trip_oracle(P):
+    t = _small_trace(P, P, rate=1.0 if P < 1000 else 0.05)
+    text = vcd_text.write(t)
+    assert vcd_text.id_length(P) == (1 if P <= 94 else 2 if P <= 94 ** 2 else 3)
+    _same(ov.parse(text, P), _trace_dict(t), f"P={P}")
+
+
+def test_empty_body_and_zero_pins():
+    t = _small_trace(1, 7, rate=0.0)
+    assert t.n_events == 0
+    text = vcd_text.write(t)
+    _same(ov.parse(text, 7), _trace_dict(t), "no events")
+    text0 = b"$enddefinitions $end\n$dumpvars\n$end\n"
+    o = ov.parse(text0, 0)
+    assert o["pin_ptr"].tolist() == [0] and o["evt_t"].size == 0
+
+
+_HEAD = b"$var wire 1 ! a $end\n$var wire 1 % b $end\n$enddefinitions $end\n#0\n$dumpvars\n0!\n1%\n$end\n"
+BAD_TEXTS = {
+    "x value": _HEAD + b"#3\nx! 1.0\n",
+    "unknown id": _HEAD + b"#3\n1? 1.0\n",
+    "no slew": _HEAD + b"#3\n1!\n",
+    "bad slew": _HEAD + b"#3\n1! 1.0q\n",
+    "signed slew": _HEAD + b"#3\n1! +1.0\n",
+    "extra token": _HEAD + b"#3\n1! 1.0 7\n",
+    "time decreases": _HEAD + b"#3\n1! 1.0\n#2\n0% 1.0\n",
+    "bad time": _HEAD + b"#3a\n1! 1.0\n",
+    "section in body": _HEAD + b"#3\n$comment hi $end\n",
+    "vector var": b"$var wire 2 ! a $end\n$enddefinitions $end\n$dumpvars\n0!\n$end\n",
+    "duplicate id": b"$var wire 1 ! a $end\n$var wire 1 ! b $end\n$enddefinitions $end\n$dumpvars\n0!\n$end\n",
+    "missing init": b"$var wire 1 ! a $end\n$var wire 1 % b $end\n$enddefinitions $end\n$dumpvars\n0!\n$end\n",
+    "no dumpvars": b"$var wire 1 ! a $end\n$enddefinitions $end\n#0\n1! 2.0\n",
+    "late dumpvars": b"$var wire 1 ! a $end\n$enddefinitions $end\n#5\n$dumpvars\n0!\n$end\n",
+    "no enddefinitions": b"$var wire 1 ! a $end\n",
+    "long id": b"$var wire 1 !!!!!!!!! a $end\n$enddefinitions $end\n$dumpvars\n0!!!!!!!!!\n$end\n",
+}
+
+
+@pytest.mark.parametrize("name", sorted(BAD_TEXTS))
+def test_oracle_rejects(name):
+    P = 1 if name in ("vector var", "no dumpvars", "late dumpvars", "no enddefinitions", "long id") else 2
+    with pytest.raises(ValueError):
+        ov.parse(BAD_TEXTS[name], P)
+
+
+# ------------------------------------------------ library packer vs oracle --
+
+def test_golden_text_library():
+    g = json.load(open(os.path.join(GOLDEN, "text_small.json")))
+    text = open(os.path.join(GOLDEN, g["text"]), "rb").read()
+    for nt in (1, 4):
+        _same(_lib_pack(text, g["n_pins"], nt), ov.parse(text, g["n_pins"]), f"golden threads {nt}")
+
+
+@pytest.mark.parametrize("P", [5, 95, 9000])
+def test_library_matches_oracle(P):
+    t = _small_trace(P + 1, P, rate=1.0 if P < 1000 else 0.05)
+    text = vcd_text.write(t)
+    o = ov.parse(text, P)
+    for nt in (1, 3):
+        _same(_lib_pack(text, P, nt), o, f"P={P} threads {nt}")
+
+
+@pytest.mark.parametrize("name", sorted(BAD_TEXTS))
+def test_library_rejects(name):
+    import eda_gate_level_amd as pa
+
+    P = 1 if name in ("vector var", "no dumpvars", "late dumpvars", "no enddefinitions", "long id") else 2
+    with pytest.raises(pa.PaError) as e:
+        _lib_pack(BAD_TEXTS[name], P)
+    assert e.value.code == pa.PA_EDATA
+
+
+def test_library_pin_count_and_query():
+    import eda_gate_level_amd as pa
+
+    t = _small_trace(3, 6)
+    text = vcd_text.write(t)
+    with pytest.raises(pa.PaError) as e:
+        _lib_pack(text, 7)
+    assert e.value.code == pa.PA_EDATA
+    import ctypes as C
+
+    n = C.c_int64(-1)
+    rc = pa.lib().pa_pack_text(C.c_char_p(text), len(text), 6, 2, 0, C.byref(n), None, None, None, None, None)
+    assert rc == 0 and n.value == t.n_events
+    rc = pa.lib().pa_pack_text(C.c_char_p(text), len(text), 6, 2, 0, None, None, None, None, None, None)
+    assert rc == pa.PA_EINVAL
+
+
+def _decimal_tokens(rng, n):
+    """Decimal slew tokens of every shape the grammar allows: 1-25 significant
+    digits, leading and trailing zeros, with and without a point and an
+    exponent, plus exact float32 midpoints."""
+    out = []
+    for _ in range(n):
+        nd = int(rng.integers(1, 26))
+        digits = "".join(str(int(d)) for d in rng.integers(0, 10, size=nd))
+        digits = str(int(rng.integers(1, 10))) + digits[1:]
+        point = int(rng.integers(0, nd + 1))
+        lead = "0" * int(rng.integers(0, 3))
+        tok = lead + digits[:point] + ("." + digits[point:] if point < nd or rng.random() < 0.3 else "")
+        if rng.random() < 0.5:
+            tok += "eE"[int(rng.integers(0, 2))] + ["", "+", "-"][int(rng.integers(0, 3))] + str(int(rng.integers(0, 30)))
+        out.append(tok)
+    # midpoints between neighbouring float32 values, written out exactly
+    from fractions import Fraction
+
+    for b in rng.integers(0x30000000, 0x5F000000, size=n // 4, dtype=np.uint32).tolist():
+        q = (Fraction(float(_f32(b))) + Fraction(float(_f32(b + 1)))) / 2
+        k = 0
+        while q.denominator != 1:
+            q *= 10
+            k += 1
+        out.append(f"{q.numerator}e-{k}")
+    out += ["16777217", "16777219", "33554434", "33554438", "1e-45", "7e-46", "3.4028235e38"]
+    return out
+
+
+def test_library_slew_rounding_matches_oracle():
+    """Every token through the packer (one pin, one event per timestamp)
+    against the oracle's exact rational rounding, bit for bit."""
+    rng = np.random.default_rng(11)
+    toks = _decimal_tokens(rng, 4000)
+    lines = [b"$var wire 1 ! a $end\n$enddefinitions $end\n$dumpvars\n0!\n$end\n"]
+    for i, tok in enumerate(toks):
+        lines.append(f"#{i + 1}\n{(i + 1) % 2}! {tok}\n".encode())
+    text = b"".join(lines)
+    lib = _lib_pack(text, 1)
+    want = np.array([ov.read_decimal(t) for t in toks], dtype=np.float32)
+    got = lib["evt_slew"]
+    bad = np.flatnonzero(got.view(np.uint32) != want.view(np.uint32))
+    assert bad.size == 0, [(toks[i], float(got[i]), float(want[i])) for i in bad[:5]]
+
+
+@pytest.mark.slow
+def test_library_many_pieces_and_threads():
+    """A text of a few MB (many parser pieces per thread count) against the
+    trace it was written from."""
+    rng = np.random.default_rng(5)
+    t = synth.poisson_trace(rng, np.full(4000, 0.5), 1000, 1000)
+    text = vcd_text.write(t)
+    assert len(text) > 2 << 20
+    for nt in (1, 2, 7, 16):
+        _same(_lib_pack(text, 4000, nt), _trace_dict(t), f"threads {nt}")
