@@ -57,7 +57,6 @@ constexpr int kNT = PA_NT;           // threads per block
 constexpr int kNW = kNT / 64;        // waves per block, each working on its own batches
 constexpr int kB = 128;              // events per wave batch, two consecutive ones per lane
 constexpr int kCCMAX = 512;          // max cycles per chunk (LDS bins)
-constexpr uint32_t kFlag = 0x100u;   // segment start flag of the state scan
 constexpr size_t kLdsMax = 64 * 1024;
 static_assert(kB - 1 >= kGroupMax, "a (gate, cycle) run fits in one batch after an odd start");
 
@@ -97,28 +96,32 @@ __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
 }
 
-// State-scan element: low 8 bits = XOR of input-pin bits, kFlag = a window
-// starts here (its value then also holds the window's start state).
-// a then b: b restarts the segment, or the bits add up.
-__device__ __forceinline__ uint32_t seg_combine(uint32_t a, uint32_t b) { return (b & kFlag) ? b : (a ^ b); }
-
-// one step of the scan: w picks up the value of another lane unless a
-// window starts at or before w's own lane (its flag is set)
+// another lane's value by a DPP move inside a scan step: lanes without a
+// source (outside the row, or rows the broadcast does not write) read 0
 template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ uint32_t seg_step(uint32_t w) {
-  const uint32_t t = dpp_mov<CTRL, ROWS>(w) ^ w;
-  return w > 0xFFu ? w : t;
+__device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
 }
 
-// inclusive segmented scan over the 64 lanes (row shifts 1, 2, 4, 8, then
-// row broadcasts 15 and 31; 0 is the identity)
-__device__ __forceinline__ uint32_t seg_scan(uint32_t w) {
-  w = seg_step<0x111>(w);
-  w = seg_step<0x112>(w);
-  w = seg_step<0x114>(w);
-  w = seg_step<0x118>(w);
-  w = seg_step<0x142, 0xA>(w);
-  w = seg_step<0x143, 0xC>(w);
+// inclusive XOR and max scans over the 64 lanes (row shifts 1, 2, 4, 8, then
+// row broadcasts 15 and 31); 0 is the identity of both
+__device__ __forceinline__ uint32_t xor_scan(uint32_t w) {
+  w ^= dpp_src<0x111>(w);
+  w ^= dpp_src<0x112>(w);
+  w ^= dpp_src<0x114>(w);
+  w ^= dpp_src<0x118>(w);
+  w ^= dpp_src<0x142, 0xA>(w);
+  w ^= dpp_src<0x143, 0xC>(w);
+  return w;
+}
+
+__device__ __forceinline__ uint32_t max_scan(uint32_t w) {
+  w = max(w, dpp_src<0x111>(w));
+  w = max(w, dpp_src<0x112>(w));
+  w = max(w, dpp_src<0x114>(w));
+  w = max(w, dpp_src<0x118>(w));
+  w = max(w, dpp_src<0x142, 0xA>(w));
+  w = max(w, dpp_src<0x143, 0xC>(w));
   return w;
 }
 
@@ -212,15 +215,13 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   }
   u64x2 kp = {0ull, 0ull};
   f32x2 sp = {0.f, 0.f};
+  // pairs past the wave's range belong to other waves (or to the two zeroed
+  // entries after the last event); the batch ignores them
+  const int xmax = (int)(((a.E + 2) & ~int64_t(1)) - 2);
   auto load_batch = [&](int p) {
-    const int x0 = (p & ~1) + 2 * lane;
-    if (x0 + 1 < wend) {
-      kp = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x0));
-      sp = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x0));
-    } else if (x0 < wend) {
-      kp = u64x2{__builtin_nontemporal_load(a.key + x0), 0ull};
-      sp = f32x2{__builtin_nontemporal_load(a.slew + x0), 0.f};
-    }
+    const int x0 = min((p & ~1) + 2 * lane, xmax);
+    kp = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x0));
+    sp = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x0));
   };
   if (pos < wend) load_batch(pos);
   for (int c = tid; c < Cc; c += kNT) {
@@ -294,26 +295,45 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       if (a0) { gi0 = a.gate_info[g0]; cw0 = a.gate_cw[g0]; }
       if (a1) { gi1 = a.gate_info[g1]; cw1 = a.gate_cw[g1]; }
 
-      // ---- state before every event: segmented XOR scan over the batch (Sec. 2.4.2)
+      // ---- state before every event (Sec. 2.4.2): the toggles of the input
+      // events before it in the batch (an XOR scan, Q) on top of the state at
+      // the last window head at or before it.  A head h carries
+      // (h + 1) << 8 | (S0 ^ Q[h]), so a max scan finds the last one, and the
+      // state before event i is that low byte ^ Q[i]; the state carried
+      // from the previous batch acts as a head at position 0.
       const uint32_t tg0 = (a0 && in0) ? (1u << c0) : 0u;
       const uint32_t tg1 = (a1 && in1) ? (1u << c1) : 0u;
-      const uint32_t e0 = !a0 ? 0u : (hd0 ? (kFlag | ((h0 & 0xFFu) ^ tg0)) : tg0);
-      const uint32_t e1 = !a1 ? 0u : (hd1 ? (kFlag | ((h1 & 0xFFu) ^ tg1)) : tg1);
-      uint32_t wv = seg_combine(e0, e1);
-      if (lane == 0) wv = seg_combine(carry, wv);
-      const uint32_t I = seg_scan(wv);
-      uint32_t X = dpp_mov<0x138>(I);
-      if (lane == 0) X = carry;
-      const uint32_t I0 = seg_combine(X, e0);
-      uint32_t S0s = hd0 ? (h0 & 0xFFu) : (X & 0xFFu);
-      uint32_t S1s = hd1 ? (h1 & 0xFFu) : (I0 & 0xFFu);
-      carry = (uint32_t)__builtin_amdgcn_readlane((int)I, (end - 1) >> 1);
+      const uint32_t Q0 = xor_scan(tg0 ^ tg1) ^ tg0 ^ tg1;  // toggles before slot i0
+      const uint32_t Q1 = Q0 ^ tg0;
+      const uint32_t V0 = (a0 && hd0) ? (((uint32_t)(i0 + 1) << 8) | ((h0 ^ Q0) & 0xFFu)) : 0u;
+      const uint32_t V1 = (a1 && hd1) ? (((uint32_t)(i1 + 1) << 8) | ((h1 ^ Q1) & 0xFFu)) : 0u;
+      uint32_t vm = max(V0, V1);
+      if (lane == 0) vm = max(vm, carry);
+      const uint32_t M = max_scan(vm);
+      uint32_t Mx = dpp_mov<0x138>(M);
+      if (lane == 0) Mx = carry;
+      const uint32_t B0 = max(Mx, V0), B1 = max(B0, V1);
+      uint32_t S0s = (B0 ^ Q0) & 0xFFu;
+      uint32_t S1s = (B1 ^ Q1) & 0xFFu;
+      // state after event end - 1 (a lane's slot 1 past the end adds nothing)
+      carry = (uint32_t)__builtin_amdgcn_readlane((int)((B1 ^ Q1 ^ tg1) & 0xFFu), (end - 1) >> 1);
 
       // ---- glitches: the pin already has an event in this (gate, cycle) run
-      // (Sec. 2.4.1, Fig. 7); runs never cross a batch, so no carry
-      // (only batches with a run of two or more events can hold one)
+      // (Sec. 2.4.1, Fig. 7); runs never cross a batch, so no carry.  When no
+      // run of the batch holds three or more events, the only earlier event
+      // of a run is the one just before; otherwise an OR scan of pin bits
+      // over the runs gives every event the pins seen before it.
+      const uint32_t tp0 = (lkp0 >> pb) & tmask;  // time of the event before slot i0
+      const uint32_t ghp = dpp_mov<0x138>((uint32_t)gh1);  // the event before slot i0 starts a run
+      const float sp0 = __uint_as_float(dpp_mov<0x138>(__float_as_uint(s1)));  // its slew
+      const bool slowgl = (__ballot(a0 && !gh0 && !ghp) | __ballot(a1 && !gh1 && !gh0)) != 0ull;
       bool gl0 = false, gl1 = false;
-      if ((__ballot(a0 && !gh0) | __ballot(a1 && !gh1)) != 0ull) {
+      uint32_t tq0 = tp0, tq1 = t0;  // time of the pin's previous event (glitches)
+      float sq0 = sp0, sq1 = s0;     // its slew
+      if (!slowgl) {
+        gl0 = a0 && !gh0 && (c0 == (lkp0 & outc));
+        gl1 = a1 && !gh1 && (c1 == c0);
+      } else {
         const uint32_t u0 = a0 ? (1u << c0) : 0u, u1 = a1 ? (1u << c1) : 0u;
         const uint32_t Io = or_scan(or_combine(gh0 ? (kRun | u0) : u0, gh1 ? (kRun | u1) : u1));
         // (the lane move runs in every lane: a lane whose value is not taken
@@ -330,14 +350,11 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       // counted the earlier ones, which are inputs: the output code is the
       // highest), and the first, the lowest input pin, charges the leakage
       // change of all their input pins together
-      const uint32_t tp0 = (lkp0 >> pb) & tmask;  // time of the event before slot i0
       const bool tie0 = a0 && !gh0 && t0 == tp0;
       const bool tie1 = a1 && !gh1 && t1 == t0;
       uint32_t mk0 = 1u << c0, mk1 = 1u << c1;  // input pins switching at the event's timestamp
       const bool ow0 = !tie0, ow1 = !tie1;      // first of its timestamp
-      uint32_t tq0 = 0, tq1 = 0;                // time of the pin's previous event (glitches)
-      float sq0 = 0.f, sq1 = 0.f;               // its slew
-      if ((__ballot(tie0 || tie1) | __ballot(gl0 || gl1)) != 0ull) {
+      if ((__ballot(tie0 || tie1) | (slowgl ? __ballot(gl0 || gl1) : 0ull)) != 0ull) {
         slk[i0] = lk0;
         slk[i1] = lk1;
         sgh[i0] = (uint8_t)tie0;
@@ -368,11 +385,12 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
               fw = y + 1 < end && sgh[y + 1];
             }
           }
-          // glitch: back to the pin's previous event of the run (it exists, so
-          // the step stops there; the batch start bounds it all the same)
-          bool sr = r ? gl1 : gl0;
-          uint32_t tq = 0;
-          float sq = 0.f;
+          // glitch in a long run: back to the pin's previous event of the run
+          // (it exists, so the step stops there; the batch start bounds it
+          // all the same)
+          bool sr = slowgl && (r ? gl1 : gl0);
+          uint32_t tq = r ? tq1 : tq0;
+          float sq = r ? sq1 : sq0;
           for (int y = p - 1; __ballot(sr) != 0ull; --y) {
             if (sr) {
               if (y < first) {
