@@ -77,12 +77,12 @@ struct Design {
   int32_t n_cells = 0, n_slew = 0, n_cap = 0, kmax = 0, n_thr = 0;
   int64_t n_leak = 0;
   double vdd = 0;
-  DBuf cell_k, cell_meta, cell_thr, cell_axw, lut, leak;
-  DBuf gate_info, gate_cw, gate_k, pin_base, pin_gate, pin_local;
+  DBuf cell_k, cell_meta, cell_thr, cell_axw, cell_caxw, lut, leak;
+  DBuf gate_info, gate_rec, gate_k, pin_base, pin_gate, pin_local;
   DBuf perm;  // internal gate -> caller gate
   int64_t bytes() const {
-    return (int64_t)(cell_k.bytes + cell_meta.bytes + cell_thr.bytes + cell_axw.bytes + lut.bytes + leak.bytes +
-                     gate_info.bytes + gate_cw.bytes + gate_k.bytes + pin_base.bytes + pin_gate.bytes +
+    return (int64_t)(cell_k.bytes + cell_meta.bytes + cell_thr.bytes + cell_axw.bytes + cell_caxw.bytes + lut.bytes +
+                     leak.bytes + gate_info.bytes + gate_rec.bytes + gate_k.bytes + pin_base.bytes + pin_gate.bytes +
                      pin_local.bytes + perm.bytes);
   }
 };
@@ -215,7 +215,7 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   const int32_t n_thr = ((n_slew - 2) + 3) / 4 * 4;
   std::vector<uint32_t> meta(2 * (size_t)n_cells);
   std::vector<float> thr((size_t)n_cells * n_thr, INFINITY);
-  std::vector<double> axw(2 * (size_t)n_cells * (n_slew - 1));
+  std::vector<double> axw(2 * (size_t)n_cells * (n_slew - 1)), caxw(2 * (size_t)n_cells * (n_cap - 1));
   uint64_t lb = 0, kb = 0;
   int32_t kmax = 0;
   for (int32_t i = 0; i < n_cells; ++i) {
@@ -240,6 +240,11 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
       axw[2 * ((size_t)i * (n_slew - 1) + j)] = sa[j];
       axw[2 * ((size_t)i * (n_slew - 1) + j) + 1] = 1.0 / (sa[j + 1] - sa[j]);
     }
+    const double *ca = &hca[(size_t)i * n_cap];
+    for (int j = 0; j + 1 < n_cap; ++j) {
+      caxw[2 * ((size_t)i * (n_cap - 1) + j)] = ca[j];
+      caxw[2 * ((size_t)i * (n_cap - 1) + j) + 1] = 1.0 / (ca[j + 1] - ca[j]);
+    }
   }
 
   Design d;
@@ -257,11 +262,12 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   HIPCHK(d.cell_meta.alloc(sizeof(uint32_t) * meta.size()));
   HIPCHK(d.cell_thr.alloc(sizeof(float) * thr.size()));
   HIPCHK(d.cell_axw.alloc(sizeof(double) * axw.size()));
+  HIPCHK(d.cell_caxw.alloc(sizeof(double) * caxw.size()));
   HIPCHK(d.lut.alloc(sizeof(double) * lb));
   HIPCHK(d.leak.alloc(sizeof(double) * kb));
   HIPCHK(cap_axis_d.alloc(sizeof(double) * hca.size()));
   HIPCHK(d.gate_info.alloc(sizeof(uint32_t) * G));
-  HIPCHK(d.gate_cw.alloc(2 * sizeof(double) * G));
+  HIPCHK(d.gate_rec.alloc(4 * sizeof(uint32_t) * G));
   HIPCHK(d.gate_k.alloc(sizeof(int32_t) * G));
   HIPCHK(d.pin_base.alloc(sizeof(int64_t) * (G + 1)));
   HIPCHK(err.alloc(sizeof(uint32_t)));
@@ -270,6 +276,7 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   if (!thr.empty())
     HIPCHK(hipMemcpyAsync(d.cell_thr.p, thr.data(), sizeof(float) * thr.size(), hipMemcpyHostToDevice, s));
   HIPCHK(hipMemcpyAsync(d.cell_axw.p, axw.data(), sizeof(double) * axw.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(d.cell_caxw.p, caxw.data(), sizeof(double) * caxw.size(), hipMemcpyHostToDevice, s));
   HIPCHK(hipMemcpyAsync(d.lut.p, lut_J, sizeof(double) * lb, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipMemcpyAsync(d.leak.p, leak_W, sizeof(double) * kb, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipMemcpyAsync(cap_axis_d.p, hca.data(), sizeof(double) * hca.size(), hipMemcpyHostToDevice, s));
@@ -300,7 +307,7 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   if (G > 0)
     HIPCHK(pa::launch_gate_tables(G, perm_d.as<int32_t>(), gate_cell, gate_cap_F, n_cells, d.cell_k.as<int32_t>(),
                                   cap_axis_d.as<double>(), n_cap, vdd_V, d.gate_info.as<uint32_t>(),
-                                  d.gate_cw.as<double2>(), d.gate_k.as<int32_t>(), err.as<uint32_t>(), s));
+                                  d.gate_rec.as<uint4>(), d.gate_k.as<int32_t>(), err.as<uint32_t>(), s));
   uint32_t herr = 0;
   HIPCHK(hipMemcpyAsync(&herr, err.p, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
@@ -559,13 +566,14 @@ static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_eve
   a.t_max = v.t_max;
   a.tick_s = v.tick_s;
   a.G = d.G;
-  a.gate_info = d.gate_info.as<uint32_t>();
-  a.gate_cw = d.gate_cw.as<double2>();
+  a.gate_rec = d.gate_rec.as<uint4>();
+  a.hv2 = 0.5 * d.vdd * d.vdd;
   a.pin_base = d.pin_base.as<int64_t>();
   a.pin_init = v.pin_init.as<uint8_t>();
   a.cell_meta = d.cell_meta.as<uint2>();
   a.cell_thr = d.cell_thr.as<float>();
   a.cell_axw = d.cell_axw.as<double2>();
+  a.cell_caxw = d.cell_caxw.as<double2>();
   a.lut = d.lut.as<double>();
   a.leak = d.leak.as<double>();
   a.n_slew = d.n_slew;

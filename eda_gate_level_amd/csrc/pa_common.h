@@ -67,13 +67,14 @@ struct PassArgs {
   double tick_s;
   // design
   int64_t G;
-  const uint32_t *gate_info;  // cell | (cap segment << 24)
-  const double2 *gate_cw;     // (fraction along the cap segment, 0.5 c Vdd^2)
+  const uint4 *gate_rec;      // (load c as fp64 bits lo, hi; cell | (cap segment << 24); 0)
   const int64_t *pin_base;    // [G+1]
   const uint8_t *pin_init;    // [P]
   const uint2 *cell_meta;     // x = k | leak base << 4, y = LUT base
   const float *cell_thr;      // [n_cells][n_thr] inner slew-axis points as float, rounded up
   const double2 *cell_axw;    // [n_cells][n_slew-1] (slew-axis point, 1 / segment width)
+  const double2 *cell_caxw;   // [n_cells][n_cap-1] (cap-axis point, 1 / segment width)
+  double hv2;                 // 0.5 Vdd^2
   const double *lut;
   const double *leak;
   int32_t n_slew, n_cap, n_cells, n_thr;
@@ -120,7 +121,7 @@ int pass_block_threads();
 int pass_wave_batch();
 int pass_max_chunk_cycles();
 // dynamic LDS bytes of the pass, and whether the cell tables fit in it
-size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_leak, bool cells);
-bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_leak);
+size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, bool cells);
+bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak);
 
 }  // namespace pa

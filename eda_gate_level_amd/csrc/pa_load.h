@@ -33,7 +33,7 @@ struct LayoutFmt {
 
 hipError_t launch_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,
                               int32_t n_cells, const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
-                              uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err, hipStream_t s);
+                              uint32_t *gate_info, uint4 *gate_rec, int32_t *gate_k, uint32_t *err, hipStream_t s);
 // leakage power at t = 0 into *l0 (part: leak0_parts() doubles of scratch)
 hipError_t launch_leak0(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
                         const int64_t *pin_base, const uint8_t *pin_init, double *part, double *l0, hipStream_t s);

@@ -39,7 +39,7 @@ inline int grid_for(int64_t n) {
 // per internal gate g (caller gate perm[g])
 __global__ void k_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,
                               int32_t n_cells, const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
-                              uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err) {
+                              uint32_t *gate_info, uint4 *gate_rec, int32_t *gate_k, uint32_t *err) {
   for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
     const int32_t cell = gate_cell[perm[g]];
     const double cap = gate_cap[perm[g]];
@@ -53,7 +53,8 @@ __global__ void k_gate_tables(int64_t G, const int32_t *perm, const int32_t *gat
     int seg = 0;
     for (int j = 1; j < n_cap - 1; ++j) seg += (cap >= ca[j]) ? 1 : 0;
     gate_info[g] = (uint32_t)cell | ((uint32_t)seg << 24);
-    gate_cw[g] = make_double2((cap - ca[seg]) / (ca[seg + 1] - ca[seg]), 0.5 * cap * vdd * vdd);
+    const uint64_t cb = (uint64_t)__double_as_longlong(cap);
+    gate_rec[g] = make_uint4((uint32_t)cb, (uint32_t)(cb >> 32), gate_info[g], 0u);
     gate_k[g] = cell_k[cell];
   }
 }
@@ -309,9 +310,9 @@ hipError_t launch_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *c
 
 hipError_t launch_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,
                               int32_t n_cells, const int32_t *cell_k, const double *cap_axis, int32_t n_cap, double vdd,
-                              uint32_t *gate_info, double2 *gate_cw, int32_t *gate_k, uint32_t *err, hipStream_t s) {
+                              uint32_t *gate_info, uint4 *gate_rec, int32_t *gate_k, uint32_t *err, hipStream_t s) {
   hipLaunchKernelGGL(k_gate_tables, dim3(grid_for(G)), dim3(kLT), 0, s, G, perm, gate_cell, gate_cap, n_cells, cell_k,
-                     cap_axis, n_cap, vdd, gate_info, gate_cw, gate_k, err);
+                     cap_axis, n_cap, vdd, gate_info, gate_rec, gate_k, err);
   return hipGetLastError();
 }
 

@@ -147,7 +147,7 @@ __device__ __forceinline__ uint32_t or_scan(uint32_t w) {
 }
 
 struct CellLds {
-  double2 *axw;
+  double2 *axw, *caxw;
   float *thr;
   double *bw, *bb;
   unsigned long long *bc;
@@ -155,16 +155,19 @@ struct CellLds {
   uint2 *meta;
 };
 
-__host__ __device__ inline size_t cell_bytes(int n_cells, int n_slew, int n_thr, int64_t n_leak) {
-  return 16 * (size_t)n_cells * (n_slew - 1) + 4 * (size_t)n_cells * n_thr + 8 * (size_t)n_leak + 8 * (size_t)n_cells;
+__host__ __device__ inline size_t cell_bytes(int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
+  return 16 * (size_t)n_cells * (n_slew - 1 + n_cap - 1) + 4 * (size_t)n_cells * n_thr + 8 * (size_t)n_leak +
+         8 * (size_t)n_cells;
 }
 
-// dynamic LDS: [slew (axis, 1/width) pairs][slew thresholds][bins: wave, leakage change, counts][leakage][cell meta]
-__device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, int n_slew, int n_thr,
+// dynamic LDS: [slew (axis, 1/width) pairs][cap (axis, 1/width) pairs][slew thresholds][bins: wave,
+// leakage change, counts][leakage][cell meta]
+__device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, int n_slew, int n_cap, int n_thr,
                                          int64_t n_leak, bool cells) {
   CellLds L;
   L.axw = reinterpret_cast<double2 *>(s);
-  L.thr = reinterpret_cast<float *>(L.axw + (cells ? n_cells * (n_slew - 1) : 0));
+  L.caxw = L.axw + (cells ? n_cells * (n_slew - 1) : 0);
+  L.thr = reinterpret_cast<float *>(L.caxw + (cells ? n_cells * (n_cap - 1) : 0));
   L.bw = reinterpret_cast<double *>(L.thr + (cells ? n_cells * n_thr : 0));
   L.bb = L.bw + Cc;
   L.bc = reinterpret_cast<unsigned long long *>(L.bb + Cc);
@@ -186,7 +189,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x, nb = gridDim.x;
   const int Cc = a.Cc, ns = a.n_slew, nc = a.n_cap, nthr = a.n_thr;
-  const CellLds L = carve(s_dyn, Cc, a.n_cells, ns, nthr, a.n_leak, CELL_LDS);
+  const CellLds L = carve(s_dyn, Cc, a.n_cells, ns, nc, nthr, a.n_leak, CELL_LDS);
   const bool has_range = b < a.n_ranges;
 
   auto meta_of = [&](uint32_t c) -> uint2 {
@@ -199,6 +202,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   };
   auto axw_of = [&](uint32_t c, uint32_t j) -> double2 {
     if constexpr (CELL_LDS) return L.axw[__umul24(c, ns - 1) + j]; else return a.cell_axw[__umul24(c, ns - 1) + j];
+  };
+  auto caxw_of = [&](uint32_t c, uint32_t j) -> double2 {
+    if constexpr (CELL_LDS) return L.caxw[__umul24(c, nc - 1) + j]; else return a.cell_caxw[__umul24(c, nc - 1) + j];
   };
   auto leak_of = [&](uint32_t j) -> double {
     if constexpr (CELL_LDS) return L.leak[j]; else return a.leak[j];
@@ -231,6 +237,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   }
   if constexpr (CELL_LDS) {
     for (int j = tid; j < a.n_cells * (ns - 1); j += kNT) L.axw[j] = a.cell_axw[j];
+    for (int j = tid; j < a.n_cells * (nc - 1); j += kNT) L.caxw[j] = a.cell_caxw[j];
     for (int j = tid; j < a.n_cells * nthr; j += kNT) L.thr[j] = a.cell_thr[j];
     for (int j = tid; j < a.n_leak; j += kNT) L.leak[j] = a.leak[j];
     for (int j = tid; j < a.n_cells; j += kNT) L.meta[j] = a.cell_meta[j];
@@ -289,11 +296,12 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       const uint32_t y0 = lk0 >> cs, y1 = lk1 >> cs;                      // cycles in the chunk
       const uint32_t t0 = (lk0 >> pb) & tmask, t1 = (lk1 >> pb) & tmask;  // time inside the cycle
       const bool in0 = c0 != outc, in1 = c1 != outc;
+      // the gates' records; slot 1 reuses slot 0's when both events are of one gate
       const uint32_t g0 = h0 >> 10, g1 = h1 >> 10;
-      uint32_t gi0 = 0, gi1 = 0;
-      double2 cw0 = make_double2(0.0, 0.0), cw1 = make_double2(0.0, 0.0);
-      if (a0) { gi0 = a.gate_info[g0]; cw0 = a.gate_cw[g0]; }
-      if (a1) { gi1 = a.gate_info[g1]; cw1 = a.gate_cw[g1]; }
+      const bool same_gate = a0 && g1 == g0;
+      uint4 rec0 = make_uint4(0u, 0u, 0u, 0u), rec1 = make_uint4(0u, 0u, 0u, 0u);
+      if (a0) rec0 = a.gate_rec[g0];
+      if (a1 && !same_gate) rec1 = a.gate_rec[g1];
 
       // ---- state before every event (Sec. 2.4.2): the toggles of the input
       // events before it in the batch (an XOR scan, Q) on top of the state at
@@ -415,8 +423,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         const uint32_t lk = r ? lk1 : lk0, hw = r ? h1 : h0;
         const uint32_t code = r ? c1 : c0, cyc = r ? y1 : y0, tic = r ? t1 : t0;
         const bool input = r ? in1 : in0;
-        const uint32_t info = r ? gi1 : gi0;
-        const double2 cw = r ? cw1 : cw0;
+        const uint4 rec = (r && !same_gate) ? rec1 : rec0;
+        const uint32_t info = rec.z;
+        const double cap = __hiloint2double((int)rec.y, (int)rec.x);
         const float sl = r ? s1 : s0;
         const uint32_t cell = info & 0xFFFFFFu;
         const uint2 m = meta_of(cell);
@@ -447,10 +456,12 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         const uint32_t cl = input ? code : 0u;
         const double *Lp = a.lut + (m.y + __umul24(__umul24(__umul24(Sm, kk) + cl, ns) + si, nc) + (info >> 24));
         const double L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
-        const double v0 = L00 + cw.x * (L01 - L00);
-        const double v1 = L10 + cw.x * (L11 - L10);
+        const double2 cx = caxw_of(cell, info >> 24);
+        const double fc = (cap - cx.x) * cx.y;  // position on the gate's cap segment (Sec. 2.4.1, Fig. 2)
+        const double v0 = L00 + fc * (L01 - L00);
+        const double v1 = L10 + fc * (L11 - L10);
         const double Eint = v0 + fa * (v1 - v0);
-        const double E = input ? Eint : (((hw >> 8) & 1u) ? cw.y : 0.0);  // Eq. 1: 0->1 output events only
+        const double E = input ? Eint : (((hw >> 8) & 1u) ? a.hv2 * cap : 0.0);  // Eq. 1: 0->1 output events only
         const bool glitch = r ? gl1 : gl0;
         double contrib = E;
         double lk_gate = 0.0;  // leakage of this power change up to t_max (per-gate output)
@@ -726,18 +737,18 @@ hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rs
 int pass_wave_batch() { return kB; }
 int pass_max_chunk_cycles() { return kCCMAX; }
 
-size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_leak, bool cells) {
-  return 24 * (size_t)Cc + (cells ? cell_bytes(n_cells, n_slew, n_thr, n_leak) : 0);
+size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, bool cells) {
+  return 24 * (size_t)Cc + (cells ? cell_bytes(n_cells, n_slew, n_cap, n_thr, n_leak) : 0);
 }
 
-bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_thr, int64_t n_leak) {
-  return pass_lds_bytes(Cc, n_cells, n_slew, n_thr, n_leak, true) <= 48 * 1024;
+bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
+  return pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, true) <= 48 * 1024;
 }
 
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
-  const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_thr, a.n_leak);
+  const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak);
   const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
-  const size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_thr, a.n_leak, cells);
+  const size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, cells);
   if (dyn > kLdsMax) return hipErrorInvalidValue;
   const dim3 g(grid_blocks), t(kNT);
   if (cells && !diag) {
