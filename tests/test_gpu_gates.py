@@ -101,3 +101,45 @@ def test_hotspot_ranking_full_size(name):
     tau, overlap = _ranking(p_gpu, p_ref)
     print(f"[hotspots] {name}: kendall tau {tau:.9f}, overlap@1% {overlap:.4f}", flush=True)
     assert tau >= 0.99999 and overlap == 1.0
+
+
+def test_large_full_size_sampled():
+    """The 200M-event, 2M-gate workload at full size, in the pass the bench
+    times, checked where a full oracle run would take too long:
+      - per-cycle event counts against a histogram of the event cycles;
+      - glitch flags per cycle against the definition (an event whose pin has
+        an earlier event in the same clock cycle);
+      - the waveform adds up to the totals;
+      - 256 random gates and the 16 busiest: their per-gate energies from the
+        full run against the oracle run on just those gates (gates are
+        independent, so the sub-design's rows are the same rows)."""
+    import oracle
+
+    w = synth.make("large")
+    d, t = w.design, w.trace
+    print(f"[case] large full size E={t.n_events}", flush=True)
+    g = _gpu_gates(d, t)
+    assert int(g["n_events"]) == t.n_events
+    cyc = t.evt_t // t.t_clk
+    C = t.n_cycles
+    np.testing.assert_array_equal(g["cyc_events"], np.bincount(cyc, minlength=C).astype(np.uint64))
+    first = np.zeros(t.n_events, dtype=bool)
+    first[t.pin_ptr[:-1][np.diff(t.pin_ptr) > 0]] = True
+    gl = np.zeros(t.n_events, dtype=bool)
+    gl[1:] = ~first[1:] & (cyc[1:] == cyc[:-1])
+    assert int(g["n_glitches"]) == int(gl.sum())
+    np.testing.assert_array_equal(g["cyc_glitches"], np.bincount(cyc[gl], minlength=C).astype(np.uint64))
+    total = sum(g[k] for k in COMPONENTS)
+    assert pu.rel_err(g["wave_J"].sum(), total) <= REL_GATE
+    rng = np.random.default_rng(3)
+    counts = np.diff(t.pin_ptr)
+    per_gate = np.add.reduceat(counts, d.pin_base()[:-1]) if d.n_gates else counts
+    pick = np.unique(np.concatenate([rng.choice(d.n_gates, size=256, replace=False),
+                                     np.argsort(-per_gate, kind="stable")[:16]]))
+    sub = synth.select_gates(w, pick)
+    o = oracle.run(sub.design, sub.trace, per_event=False, per_gate=True)
+    gj, oj = g["gate_J"][pick], o["gate_J"]
+    den = np.maximum(np.abs(gj), np.abs(oj))
+    bad = np.abs(gj - oj) > REL_GATE * den
+    assert not bad.any(), f"{int(bad.sum())} sampled gate entries off"
+    print(f"[large] {t.n_events} events, {int(gl.sum())} glitches, {pick.size} gates checked", flush=True)

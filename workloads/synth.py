@@ -353,3 +353,21 @@ def subset_gates(w: Workload, g_lo: int, g_hi: int) -> Workload:
                              pin_init=t.pin_init[p_lo:p_hi].copy(), evt_t=t.evt_t[e_lo:e_hi].copy(),
                              evt_val=t.evt_val[e_lo:e_hi].copy(), evt_slew=t.evt_slew[e_lo:e_hi].copy())
     return Workload(f"{w.name}[{g_lo}:{g_hi}]", des, tr, dict(w.info))
+
+
+def select_gates(w: Workload, gates) -> Workload:
+    """The sub-design made of the given gates (in increasing order) with their
+    pins and events (same library, clock and window)."""
+    d, t = w.design, w.trace
+    gates = np.unique(np.asarray(gates, dtype=np.int64))
+    pb = d.pin_base()
+    npin = pb[gates + 1] - pb[gates]
+    pins = np.repeat(pb[gates], npin) + (np.arange(int(npin.sum())) - np.repeat(np.cumsum(npin) - npin, npin))
+    cnt = t.pin_ptr[pins + 1] - t.pin_ptr[pins]
+    ptr = np.zeros(pins.shape[0] + 1, dtype=np.int64)
+    np.cumsum(cnt, out=ptr[1:])
+    ev = np.repeat(t.pin_ptr[pins], cnt) + (np.arange(int(cnt.sum())) - np.repeat(ptr[:-1], cnt))
+    des = dataclasses.replace(d, gate_cell=d.gate_cell[gates].copy(), gate_cap_F=d.gate_cap_F[gates].copy())
+    tr = dataclasses.replace(t, pin_ptr=ptr, pin_init=t.pin_init[pins].copy(), evt_t=t.evt_t[ev].copy(),
+                             evt_val=t.evt_val[ev].copy(), evt_slew=t.evt_slew[ev].copy())
+    return Workload(f"{w.name}[{gates.shape[0]} gates]", des, tr, dict(w.info))
