@@ -91,7 +91,7 @@ struct Events {
   int64_t E = 0, C = 0, T = 0, t_max = 0, chunk_ticks = 0;
   double tick_s = 0;
   int32_t Cc = 0, Q = 0;
-  uint32_t tb = 0, pb = 0, last_len = 0;
+  uint32_t tb = 0, pb = 0, gb = 1, last_len = 0;
   DBuf key, slew, orig, pin_init;
   std::vector<uint32_t> h_chunk_base;
   DBuf rstart, rchunk, chunk_blk;  // block ranges of the pass, first block of every chunk
@@ -437,8 +437,11 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   if (v.pb + v.tb > 32)
     return fail(PA_EINVAL, "pa_load_events: clock period longer than 2^%d ticks", 32 - (int)v.pb);
   // chunk length: a power of two (window lengths halve it), at most the LDS bins
-  const uint32_t lc_max = 32 - v.pb - v.tb;
-  int64_t Cc_want = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : 512;
+  // the cycle in the chunk has the low word's bits above pin code and tic, and
+  // the bits the gate id leaves free in the high word
+  const uint32_t gb = bits_for((uint64_t)std::max<int64_t>(G - 1, 0));
+  const uint32_t lc_max = (32 - v.pb - v.tb) + (22 - gb);
+  int64_t Cc_want = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : 1024;
   Cc_want = std::min<int64_t>(Cc_want, (int64_t)pa::pass_max_chunk_cycles());
   if (lc_max < 31) Cc_want = std::min<int64_t>(Cc_want, int64_t(1) << lc_max);
   int64_t Cc = 1;
@@ -454,7 +457,8 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   f.lc = lc;
   f.pb = v.pb;
   f.tb = v.tb;
-  f.gb = bits_for((uint64_t)std::max<int64_t>(G - 1, 0));
+  f.gb = gb;
+  v.gb = gb;
   const uint32_t lkb = lc + v.pb + v.tb;
   const uint32_t qbits = bits_for((uint64_t)std::max<int32_t>(v.Q - 1, 0));
   const int32_t Q = v.Q;
@@ -561,6 +565,7 @@ static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_eve
   a.T = (uint32_t)v.T;
   a.tb = v.tb;
   a.pb = v.pb;
+  a.gb = v.gb;
   a.last_len = v.last_len;
   a.chunk_ticks = v.chunk_ticks;
   a.t_max = v.t_max;

@@ -18,15 +18,18 @@ namespace pa {
 // so a window is one contiguous run, and inside a window the events of one
 // clock cycle form one run in time order (events of one timestamp by pin).
 //
-// Packed 64-bit key of an event:
-//   bits [42, 64)  gate id (designs up to 2^22 - 1 gates)
-//   bit  41        window head: first event of its (chunk, gate, window)
-//   bit  40        val: the pin's value after the event
-//   bits [32, 40)  S0: the gate's input-pin state at the window start (on
-//                  window heads; zero elsewhere)
-//   bits [ 0, 32)  lk = (cycle in chunk << (pb + tb)) | (tic << pb) | pin code
-// tic = time minus the start of the event's clock cycle (tb bits); pin code =
-// input pin index 0..k-1, or out_code(pb) for the output pin.
+// Packed 64-bit key of an event (gb = bits of the largest gate id, cs = pb + tb):
+//   bits [42 + gb, 64)  the high bits of the cycle in the chunk (22 - gb of them)
+//   bits [42, 42 + gb)  gate id (designs up to 2^22 - 1 gates)
+//   bit  41             window head: first event of its (chunk, gate, window)
+//   bit  40             val: the pin's value after the event
+//   bits [32, 40)       S0: the gate's input-pin state at the window start (on
+//                       window heads; zero elsewhere)
+//   bits [ 0, 32)       (low bits of the cycle in the chunk << cs) | (tic << pb) | pin code
+// so the cycle in the chunk, (key >> 32 >> (10 + gb)) << (32 - cs) | low word >> cs,
+// has 32 - cs + 22 - gb bits.  tic = time minus the start of the event's clock
+// cycle (tb bits); pin code = input pin index 0..k-1, or out_code(pb) for the
+// output pin.
 // ---------------------------------------------------------------------------
 constexpr uint32_t kKeyGateShift = 42;
 constexpr uint32_t kKeyHeadShift = 41;
@@ -60,7 +63,8 @@ struct PassArgs {
   int32_t Q, Cc;
   int64_t C;
   uint32_t T;
-  uint32_t tb, pb;         // bit widths of tic and of the pin code in lk
+  uint32_t tb, pb;         // bit widths of tic and of the pin code in the key's low word
+  uint32_t gb;             // bit width of the gate id
   uint32_t last_len;       // ticks of the last cycle bin
   int64_t chunk_ticks;
   int64_t t_max;

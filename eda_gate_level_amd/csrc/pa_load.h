@@ -28,7 +28,7 @@ struct LayoutFmt {
   uint32_t lc;   // log2 Cc
   uint32_t pb;   // pin-code bits
   uint32_t tb;   // tic bits
-  uint32_t gb;   // gate-id bits of the sort key
+  uint32_t gb;   // gate-id bits of the sort key and of the packed key
 };
 
 hipError_t launch_gate_tables(int64_t G, const int32_t *perm, const int32_t *gate_cell, const double *gate_cap,

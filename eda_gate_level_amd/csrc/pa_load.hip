@@ -150,8 +150,9 @@ __device__ __forceinline__ EvPos ev_pos(int64_t e, const int64_t *evt_t, const u
   return r;
 }
 
-__device__ __forceinline__ uint32_t lk_of(const EvPos &p, const LayoutFmt &f) {
-  return (p.cyc << (f.pb + f.tb)) | (p.tic << f.pb) | p.code;
+// (cycle, time, pin code) as one integer of lc + pb + tb bits
+__device__ __forceinline__ uint64_t lk_of(const EvPos &p, const LayoutFmt &f) {
+  return ((uint64_t)p.cyc << (f.pb + f.tb)) | ((uint64_t)p.tic << f.pb) | p.code;
 }
 
 // sort keys: (chunk, gate, lk) in one word, or (gate, lk) with the chunk apart
@@ -215,8 +216,10 @@ __global__ void k_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, 
         S0 |= (uint64_t)((pin_init[pb + j] ^ (uint8_t)((lo - base) & 1)) & 1u) << j;
       }
     }
-    key_out[x] = ((uint64_t)p.g << kKeyGateShift) | ((uint64_t)head << kKeyHeadShift) |
-                 ((uint64_t)(evt_val[e] & 1u) << kKeyValShift) | (S0 << kKeyS0Shift) | (uint64_t)lk_of(p, f);
+    const uint64_t lk = lk_of(p, f);
+    key_out[x] = ((lk >> 32) << (kKeyGateShift + f.gb)) | ((uint64_t)p.g << kKeyGateShift) |
+                 ((uint64_t)head << kKeyHeadShift) | ((uint64_t)(evt_val[e] & 1u) << kKeyValShift) |
+                 (S0 << kKeyS0Shift) | (lk & 0xFFFFFFFFull);
     slew_out[x] = evt_slew[e];
     orig_out[x] = (uint32_t)e;
     chunk_out[x] = (uint32_t)p.q;

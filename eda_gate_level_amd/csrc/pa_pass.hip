@@ -56,7 +56,7 @@ namespace {
 constexpr int kNT = PA_NT;           // threads per block
 constexpr int kNW = kNT / 64;        // waves per block, each working on its own batches
 constexpr int kB = 128;              // events per wave batch, two consecutive ones per lane
-constexpr int kCCMAX = 512;          // max cycles per chunk (LDS bins)
+constexpr int kCCMAX = 1024;         // max cycles per chunk (LDS bins)
 constexpr size_t kLdsMax = 64 * 1024;
 static_assert(kB - 1 >= kGroupMax, "a (gate, cycle) run fits in one batch after an odd start");
 
@@ -257,6 +257,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   const double tail = (double)(a.t_max - cstart);  // t_max - t = tail - (cyc T + tic)
   const double tick = a.tick_s;
   const uint32_t tb = a.tb, pb = a.pb, cs = tb + pb;
+  const uint32_t gmask = (1u << a.gb) - 1u, ysh = 10u + a.gb;  // gate id and high cycle bits in the key's high word
   const uint32_t tmask = (1u << tb) - 1u;
   const uint32_t outc = (1u << pb) - 1u;
 
@@ -277,11 +278,15 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       const uint32_t lk0 = (uint32_t)K0, lk1 = (uint32_t)K1;
       const uint32_t h0 = (uint32_t)(K0 >> 32), h1 = (uint32_t)(K1 >> 32);
       const bool hd0 = (h0 >> 9) & 1u, hd1 = (h1 >> 9) & 1u;
+      // cycles in the chunk
+      const uint32_t y0 = (uint32_t)((((uint64_t)h0 >> ysh) << 32 | lk0) >> cs);
+      const uint32_t y1 = (uint32_t)((((uint64_t)h1 >> ysh) << 32 | lk1) >> cs);
       // the event before slot i0 is the previous lane's second one
       const uint32_t lkp0 = dpp_mov<0x138>(lk1);
+      const uint32_t yp0 = dpp_mov<0x138>(y1);
       // run starts: a window head, the batch start, or a new clock cycle
-      const bool gh0 = hd0 || i0 == first || ((lk0 ^ lkp0) >> cs) != 0u;
-      const bool gh1 = hd1 || i1 == first || ((lk1 ^ lk0) >> cs) != 0u;
+      const bool gh0 = hd0 || i0 == first || y0 != yp0;
+      const bool gh1 = hd1 || i1 == first || y1 != y0;
       // process up to the last run start, so that no (gate, cycle) run is split
       const unsigned long long M0 = __ballot(v0 && gh0), M1 = __ballot(v1 && gh1);
       int last = -1;
@@ -293,11 +298,10 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       if (npos < wend) load_batch(npos);
 
       const uint32_t c0 = lk0 & outc, c1 = lk1 & outc;                    // pin codes
-      const uint32_t y0 = lk0 >> cs, y1 = lk1 >> cs;                      // cycles in the chunk
       const uint32_t t0 = (lk0 >> pb) & tmask, t1 = (lk1 >> pb) & tmask;  // time inside the cycle
       const bool in0 = c0 != outc, in1 = c1 != outc;
       // the gates' records; slot 1 reuses slot 0's when both events are of one gate
-      const uint32_t g0 = h0 >> 10, g1 = h1 >> 10;
+      const uint32_t g0 = (h0 >> 10) & gmask, g1 = (h1 >> 10) & gmask;
       const bool same_gate = a0 && g1 == g0;
       uint4 rec0 = make_uint4(0u, 0u, 0u, 0u), rec1 = make_uint4(0u, 0u, 0u, 0u);
       if (a0) rec0 = a.gate_rec[g0];
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
             if constexpr (DIAG) {
               if (a.gate_J) {
                 lk_gate = dp * tick * (double)(a.t_max - cstart - ((int64_t)cyc * T + tic));
-                atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[hw >> 10] + 3, lk_gate);
+                atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[(hw >> 10) & gmask] + 3, lk_gate);
               }
             }
             contrib += part;
@@ -503,7 +507,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
           if (a.evt_state) a.evt_state[o] = (uint8_t)(input ? Sm : 0u);
           // the gate's own energy: internal, switching or glitch (device atomics)
           if (a.gate_J && dyn != 0.0)
-            atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[hw >> 10] + (glitch ? 2 : (input ? 0 : 1)), dyn);
+            atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[(hw >> 10) & gmask] + (glitch ? 2 : (input ? 0 : 1)), dyn);
         }
       }
       pos = npos;
