@@ -45,10 +45,30 @@ inline bool pack_id(const char *p, size_t n, uint64_t &key) {
   return true;
 }
 
+// the value of eight decimal digits c[0..8) (c[0] most significant), or
+// false if any of them is not a digit: every byte of w - '0' must be below 10
+inline bool eight_digits(const char *c, uint64_t &v) {
+  uint64_t w;
+  std::memcpy(&w, c, 8);
+  const uint64_t d = w - 0x3030303030303030ull;
+  if (((w | (w + 0x4646464646464646ull)) & 0x8080808080808080ull) != 0 || (d & 0xF0F0F0F0F0F0F0F0ull) != 0)
+    return false;
+  // pairs, quads, then all eight (the first character is the low byte)
+  uint64_t x = (d * 10 + (d >> 8)) & 0x00FF00FF00FF00FFull;
+  x = (x * 100 + (x >> 16)) & 0x0000FFFF0000FFFFull;
+  v = (x * 10000 + (x >> 32)) & 0xFFFFFFFFull;
+  return true;
+}
+
 // nonnegative decimal integer [p, e) (at most 18 digits)
 inline bool parse_time(const char *p, const char *e, int64_t &v) {
   if (p == e || e - p > 18) return false;
   int64_t x = 0;
+  uint64_t v8;
+  while (e - p >= 8 && eight_digits(p, v8)) {
+    x = x * 100000000 + (int64_t)v8;
+    p += 8;
+  }
   for (; p < e; ++p) {
     if (!is_digit(*p)) return false;
     x = x * 10 + (*p - '0');
@@ -122,11 +142,17 @@ bool parse_float_slow(const char *a, const char *b, float &out) {
 bool parse_float(const char *a, const char *b, float &out) {
   const char *p = a;
   uint64_t m = 0;
-  int nd = 0, q = 0;
+  int nd = 0, q = 0;  // digits taken into m (leading zeros included), power of ten
   bool any = false, lost = false;
+  uint64_t v8;
+  if (b - p >= 8 && eight_digits(p, v8)) {  // the first eight digits at once
+    m = v8;
+    nd = 8;
+    p += 8;
+    any = true;
+  }
   for (; p < b && is_digit(*p); ++p) {
     any = true;
-    if (m == 0 && *p == '0') continue;
     if (nd < 19) {
       m = m * 10 + (uint64_t)(*p - '0');
       ++nd;
@@ -138,10 +164,6 @@ bool parse_float(const char *a, const char *b, float &out) {
   if (p < b && *p == '.') {
     for (++p; p < b && is_digit(*p); ++p) {
       any = true;
-      if (m == 0 && *p == '0') {
-        --q;
-        continue;
-      }
       if (nd < 19) {
         m = m * 10 + (uint64_t)(*p - '0');
         ++nd;
@@ -169,13 +191,15 @@ bool parse_float(const char *a, const char *b, float &out) {
   }
   if (m >= (uint64_t(1) << 53) || q < -22 || q > 22) return parse_float_slow(a, b, out);
   const double d = q >= 0 ? (double)m * kPow10[q] : (double)m / kPow10[-q];
-  const float f = (float)d;
-  if ((double)f != d) {
-    const float g = std::nextafter(f, (double)f < d ? std::numeric_limits<float>::infinity()
-                                                     : -std::numeric_limits<float>::infinity());
-    if ((double)f + (double)g == 2.0 * d) return parse_float_slow(a, b, out);
-  }
-  out = f;
+  // a double in the range of normal floats lies halfway between two floats
+  // exactly when its 29 significand bits below float precision are 1000...0;
+  // outside that range (and for those) the slow path decides
+  uint64_t bits;
+  std::memcpy(&bits, &d, sizeof bits);
+  const uint64_t ex = (bits >> 52) & 0x7FF;
+  if (ex < 1023 - 125 || ex > 1023 + 127 || (bits & ((uint64_t(1) << 29) - 1)) == (uint64_t(1) << 28))
+    return parse_float_slow(a, b, out);
+  out = (float)d;
   return true;
 }
 
@@ -360,6 +384,21 @@ struct PieceIndex {
   size_t err_at = 0;
 };
 
+// the first '\n' in [p, e), or e: eight bytes at a time (a byte of w ^ '\n'
+// that is zero gives the lowest flag of the borrow trick exactly)
+inline const char *find_nl(const char *p, const char *e) {
+  while (e - p >= 8) {
+    uint64_t w;
+    std::memcpy(&w, p, 8);
+    const uint64_t x = w ^ 0x0A0A0A0A0A0A0A0Aull;
+    const uint64_t t = (x - 0x0101010101010101ull) & ~x & 0x8080808080808080ull;
+    if (t) return p + (__builtin_ctzll(t) >> 3);
+    p += 8;
+  }
+  while (p < e && *p != '\n') ++p;
+  return p;
+}
+
 // the first byte at or after c (and after b0) that starts a line
 size_t line_start_at_or_after(const char *s, size_t b0, size_t b1, size_t c) {
   if (c <= b0) return b0;
@@ -392,12 +431,11 @@ int index_segments(const char *s, size_t n, const Header &h, int64_t seg_ticks, 
   pool.run(np, [&](int i) {
     PieceIndex &X = pc[i];
     const char *p = s + cut[i], *e = s + cut[i + 1];
-    int64_t seg = -1, cnt = 0;
+    int64_t seg = -1, cnt = 0, sg = -1, seg_lo = 0, seg_hi = -1;
     while (p < e) {
       const char *line = p;
-      const char *nl = (const char *)std::memchr(p, '\n', (size_t)(e - p));
-      const char *le = nl ? nl : e;
-      p = nl ? nl + 1 : e;
+      const char *le = find_nl(p, e);
+      p = le < e ? le + 1 : e;
       const char *q = line;
       while (q < le && is_blank(*q)) ++q;
       if (q == le) continue;
@@ -422,7 +460,13 @@ int index_segments(const char *s, size_t n, const Header &h, int64_t seg_ticks, 
       }
       if (X.first_t < 0) X.first_t = tv;
       X.last_t = tv;
-      const int64_t sg = tv >= t_end ? n_seg : std::min(tv / seg_ticks, n_seg);
+      // the segment of tv (a division only when tv leaves the current one)
+      if (tv < seg_lo || tv >= seg_hi) {
+        const int64_t k = tv >= t_end ? n_seg : std::min(tv / seg_ticks, n_seg);
+        seg_lo = k < n_seg ? k * seg_ticks : t_end;
+        seg_hi = k < n_seg - 1 ? seg_lo + seg_ticks : (k < n_seg ? t_end : std::numeric_limits<int64_t>::max());
+        sg = k;
+      }
       if (sg != seg) {
         if (seg < 0)
           X.pre = cnt;
