@@ -125,7 +125,7 @@ def text_pipeline(args, w, dev):
     print(f"[bench] text of {w.name}: {len(text)} bytes, written in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
     pack = []
-    for _ in range(3):
+    for _ in range(5):
         t0 = time.time()
         r = pa.pa_pack_text(text, tr.n_pins, args.text_threads)
         pack.append(time.time() - t0)
@@ -143,7 +143,7 @@ def text_pipeline(args, w, dev):
     runs = {}
     for serial in (True, False):
         walls, st, tot = [], None, None
-        for i in range(4):
+        for i in range(6):
             r = an.run_text(text, tr.t_clk, tr.t_max, tr.tick_s, segment_cycles=args.segment_cycles,
                             n_threads=args.text_threads, serial=serial)
             if i:
@@ -157,8 +157,6 @@ def text_pipeline(args, w, dev):
     an.close()
     E = tr.n_events
     ser, ovl = runs[True], runs[False]
-    saved = ser["wall_s"] - ovl["wall_s"]
-    hideable = min(ovl["stats"]["parse_s"], ovl["stats"]["gpu_s"])
     print(json.dumps({
         "workload": w.name, "mode": "activity text", "events": E, "text_bytes": len(text),
         "segment_cycles": args.segment_cycles or 1024, "threads": args.text_threads or "default",
@@ -168,7 +166,7 @@ def text_pipeline(args, w, dev):
         "overlapped_events_per_s": E / ovl["wall_s"],
         "overlapped_parse_s": ovl["stats"]["parse_s"], "overlapped_gpu_s": ovl["stats"]["gpu_s"],
         "index_s": ovl["stats"]["index_s"], "header_s": ovl["stats"]["header_s"],
-        "hidden_fraction": saved / hideable if hideable > 0 else None,
+        "overlap_saving": 1.0 - ovl["wall_s"] / ser["wall_s"],
         "arrays_load_and_pass_s": arrays_s,
         "rel_err_totals": max(ser["rel_err_totals"], ovl["rel_err_totals"]),
         "rel_err_bins": max(ser["rel_err_bins"], ovl["rel_err_bins"])}), flush=True)

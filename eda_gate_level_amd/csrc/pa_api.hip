@@ -63,6 +63,8 @@ struct DBuf {
     bytes = n;
     return hipSuccess;
   }
+  // at least n bytes, keeping the allocation when it is large enough
+  hipError_t ensure(size_t n) { return (p && bytes >= n) ? hipSuccess : alloc(n); }
   template <class T> T *as() const { return static_cast<T *>(p); }
 };
 
@@ -105,6 +107,38 @@ struct Events {
   }
 };
 
+// owning pinned host buffer (grow-only)
+struct PinnedBuf {
+  void *p = nullptr;
+  size_t bytes = 0;
+  PinnedBuf() = default;
+  PinnedBuf(const PinnedBuf &) = delete;
+  PinnedBuf &operator=(const PinnedBuf &) = delete;
+  ~PinnedBuf() {
+    if (p) (void)hipHostFree(p);
+  }
+  hipError_t ensure(size_t n) {
+    if (p && bytes >= n) return hipSuccess;
+    if (p) (void)hipHostFree(p);
+    p = nullptr;
+    bytes = 0;
+    const hipError_t e = hipHostMalloc(&p, n, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      p = nullptr;
+      return e;
+    }
+    bytes = n;
+    return hipSuccess;
+  }
+};
+
+// device buffers of the event load that live only during it; kept (grow-only)
+// so that repeated loads, e.g. the segments of an activity text, allocate
+// and free nothing
+struct LoadScratch {
+  DBuf err, ev_pin, chunk_sorted, cbase, level, k0, k1, idx, perm, chunk, tmp, part;
+};
+
 }  // namespace
 
 struct pa_ctx {
@@ -115,6 +149,10 @@ struct pa_ctx {
   bool has_design = false, has_events = false;
   Design d;
   Events ev;
+  Events ev_spare;  // the events before the current ones: their buffers serve the next load
+  LoadScratch ls;
+  PinnedBuf text_host[2];  // pa_run_text: packed segments on the host, and their device copy
+  DBuf text_dev;
   double *h_res = nullptr;
   hipEvent_t tev[3] = {nullptr, nullptr, nullptr};
   float kernel_ms[4] = {0, 0, 0, 0};
@@ -352,25 +390,25 @@ static int build_ranges(pa_ctx *c, Events &v) {
   v.grid = std::max(1, v.n_ranges);
   rs.push_back((uint32_t)v.E);
   rq.push_back(0);
-  HIPCHK(v.rstart.alloc(sizeof(uint32_t) * rs.size()));
-  HIPCHK(v.rchunk.alloc(sizeof(uint32_t) * rq.size()));
-  HIPCHK(v.chunk_blk.alloc(sizeof(uint32_t) * cb.size()));
-  HIPCHK(v.blk_wave.alloc(sizeof(double) * (size_t)v.grid * v.Cc));
-  HIPCHK(v.blk_cnt.alloc(sizeof(unsigned long long) * (size_t)v.grid * v.Cc));
-  HIPCHK(v.blk_part.alloc(sizeof(double) * 8 * (size_t)v.grid));
-  HIPCHK(v.res.alloc(sizeof(double) * 16));
+  HIPCHK(v.rstart.ensure(sizeof(uint32_t) * rs.size()));
+  HIPCHK(v.rchunk.ensure(sizeof(uint32_t) * rq.size()));
+  HIPCHK(v.chunk_blk.ensure(sizeof(uint32_t) * cb.size()));
+  HIPCHK(v.blk_wave.ensure(sizeof(double) * (size_t)v.grid * v.Cc));
+  HIPCHK(v.blk_cnt.ensure(sizeof(unsigned long long) * (size_t)v.grid * v.Cc));
+  HIPCHK(v.blk_part.ensure(sizeof(double) * 8 * (size_t)v.grid));
+  HIPCHK(v.res.ensure(sizeof(double) * 16));
   HIPCHK(hipMemcpyAsync(v.rstart.p, rs.data(), sizeof(uint32_t) * rs.size(), hipMemcpyHostToDevice, c->stream));
   HIPCHK(hipMemcpyAsync(v.rchunk.p, rq.data(), sizeof(uint32_t) * rq.size(), hipMemcpyHostToDevice, c->stream));
   HIPCHK(hipMemcpyAsync(v.chunk_blk.p, cb.data(), sizeof(uint32_t) * cb.size(), hipMemcpyHostToDevice, c->stream));
   // the cuts between every block's waves, moved to window heads
-  HIPCHK(v.wbound.alloc(sizeof(int32_t) * (size_t)v.grid * pa::pass_wave_bounds_per_block()));
+  HIPCHK(v.wbound.ensure(sizeof(int32_t) * (size_t)v.grid * pa::pass_wave_bounds_per_block()));
   HIPCHK(pa::launch_wave_bounds(v.key.as<uint64_t>(), v.E, v.rstart.as<uint32_t>(), v.n_ranges,
                                 v.wbound.as<int32_t>(), c->stream));
   // leakage power at t = 0, from the initial pin values
   const Design &d = c->d;
-  DBuf part;
-  HIPCHK(part.alloc(sizeof(double) * pa::leak0_parts()));
-  HIPCHK(v.l0.alloc(sizeof(double)));
+  DBuf &part = c->ls.part;
+  HIPCHK(part.ensure(sizeof(double) * pa::leak0_parts()));
+  HIPCHK(v.l0.ensure(sizeof(double)));
   HIPCHK(pa::launch_leak0(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
                           d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), part.as<double>(), v.l0.as<double>(),
                           c->stream));
@@ -403,9 +441,9 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   if (ends[0] != 0 || ends[1] != E) return fail(PA_EDATA, "pa_load_events: pin_ptr[0] must be 0 and pin_ptr[P] = n_events");
 
   // ---- validation
-  DBuf err, ev_pin;
-  HIPCHK(err.alloc(sizeof(uint32_t)));
-  HIPCHK(ev_pin.alloc(sizeof(uint32_t) * E));
+  DBuf &err = c->ls.err, &ev_pin = c->ls.ev_pin;
+  HIPCHK(err.ensure(sizeof(uint32_t)));
+  HIPCHK(ev_pin.ensure(sizeof(uint32_t) * std::max<int64_t>(E, 1)));
   HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
   if (P > 0) HIPCHK(pa::launch_pin_check(P, pin_ptr, pin_init, err.as<uint32_t>(), s));
   uint32_t herr = 0;
@@ -423,7 +461,10 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   if (herr & pa::ERR_SLEW) return fail(PA_EDATA, "pa_load_events: slew not finite and > 0");
 
   // ---- bit widths of the layout: lk = (cycle in chunk | pin code | time in cycle) in 32 bits
-  Events v;
+  // the new layout goes into the buffers of the events before the current
+  // ones; the current events stay usable until the load succeeds
+  Events v = std::move(c->ev_spare);
+  c->ev_spare = Events();
   v.E = E;
   v.T = t_clk;
   v.t_max = t_max;
@@ -466,19 +507,19 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   // two zeroed entries past the events (even count): the pass fetches event
   // pairs without a bounds branch
   const int64_t Ea = (E + 2) & ~int64_t(1);
-  HIPCHK(v.key.alloc(sizeof(uint64_t) * Ea));
-  HIPCHK(v.slew.alloc(sizeof(float) * Ea));
+  HIPCHK(v.key.ensure(sizeof(uint64_t) * Ea));
+  HIPCHK(v.slew.ensure(sizeof(float) * Ea));
   HIPCHK(hipMemsetAsync(v.key.as<uint64_t>() + E, 0, sizeof(uint64_t) * (Ea - E), s));
   HIPCHK(hipMemsetAsync(v.slew.as<float>() + E, 0, sizeof(float) * (Ea - E), s));
-  HIPCHK(v.orig.alloc(sizeof(uint32_t) * E));
-  HIPCHK(v.pin_init.alloc(P));
-  DBuf chunk_sorted, cbase;
-  HIPCHK(chunk_sorted.alloc(sizeof(uint32_t) * E));
-  HIPCHK(cbase.alloc(sizeof(uint32_t) * (Q + 1)));
+  HIPCHK(v.orig.ensure(sizeof(uint32_t) * E));
+  HIPCHK(v.pin_init.ensure(P));
+  DBuf &chunk_sorted = c->ls.chunk_sorted, &cbase = c->ls.cbase;
+  HIPCHK(chunk_sorted.ensure(sizeof(uint32_t) * E));
+  HIPCHK(cbase.ensure(sizeof(uint32_t) * (Q + 1)));
   if (E > 0) {
     // ---- density-aware window level per gate
-    DBuf level;
-    HIPCHK(level.alloc(G));
+    DBuf &level = c->ls.level;
+    HIPCHK(level.ensure(G));
     int32_t fixed_level = -1;
     if (c->tun.fixed_window_cycles > 0) {
       int64_t n = 1;
@@ -489,22 +530,22 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
     HIPCHK(pa::launch_gate_levels(G, d.pin_base.as<int64_t>(), d.gate_k.as<int32_t>(), pin_ptr, v.C, (int32_t)Cc,
                                   (int32_t)lc, 32.0, fixed_level, level.as<uint8_t>(), s));
     // ---- order (chunk, gate, cycle, pin, time) by radix sort
-    DBuf k0, k1, idx, perm, tmp;
+    DBuf &k0 = c->ls.k0, &k1 = c->ls.k1, &idx = c->ls.idx, &perm = c->ls.perm, &tmp = c->ls.tmp;
     size_t tmp_bytes = 0;
-    HIPCHK(k0.alloc(sizeof(uint64_t) * E));
-    HIPCHK(k1.alloc(sizeof(uint64_t) * E));
-    HIPCHK(idx.alloc(sizeof(uint32_t) * E));
-    HIPCHK(perm.alloc(sizeof(uint32_t) * E));
+    HIPCHK(k0.ensure(sizeof(uint64_t) * E));
+    HIPCHK(k1.ensure(sizeof(uint64_t) * E));
+    HIPCHK(idx.ensure(sizeof(uint32_t) * E));
+    HIPCHK(perm.ensure(sizeof(uint32_t) * E));
     const bool one_key = qbits + f.gb + lkb <= 64;
-    DBuf chunk;
-    if (!one_key) HIPCHK(chunk.alloc(sizeof(uint32_t) * E));
+    DBuf &chunk = c->ls.chunk;
+    if (!one_key) HIPCHK(chunk.ensure(sizeof(uint32_t) * E));
     HIPCHK(pa::launch_sort_keys(E, evt_t, ev_pin.as<uint32_t>(), d.pin_gate.as<int32_t>(), d.pin_local.as<uint8_t>(),
                                 d.gate_k.as<int32_t>(), f, k0.as<uint64_t>(),
                                 one_key ? nullptr : chunk.as<uint32_t>(), idx.as<uint32_t>(), s));
     const int end_bit = (int)(one_key ? qbits + f.gb + lkb : f.gb + lkb);
     HIPCHK(pa::sort_pairs_u64(k0.as<uint64_t>(), k1.as<uint64_t>(), idx.as<uint32_t>(), perm.as<uint32_t>(), E,
                               end_bit, nullptr, &tmp_bytes, s));
-    HIPCHK(tmp.alloc(tmp_bytes));
+    HIPCHK(tmp.ensure(tmp_bytes));
     HIPCHK(pa::sort_pairs_u64(k0.as<uint64_t>(), k1.as<uint64_t>(), idx.as<uint32_t>(), perm.as<uint32_t>(), E,
                               end_bit, tmp.p, &tmp_bytes, s));
     if (!one_key) {
@@ -513,9 +554,10 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
       HIPCHK(pa::launch_chunk_of(E, perm.as<uint32_t>(), chunk.as<uint32_t>(), qk, s));
       tmp_bytes = 0;
       HIPCHK(pa::sort_pairs_u32(qk, qs, perm.as<uint32_t>(), idx.as<uint32_t>(), E, (int)qbits, nullptr, &tmp_bytes, s));
-      HIPCHK(tmp.alloc(tmp_bytes));
+      HIPCHK(tmp.ensure(tmp_bytes));
       HIPCHK(pa::sort_pairs_u32(qk, qs, perm.as<uint32_t>(), idx.as<uint32_t>(), E, (int)qbits, tmp.p, &tmp_bytes, s));
-      std::swap(perm, idx);
+      std::swap(perm.p, idx.p);
+      std::swap(perm.bytes, idx.bytes);
     }
     // ---- packed keys, window heads and start states
     HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
@@ -536,6 +578,7 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   HIPCHK(hipStreamSynchronize(s));
   int rc = build_ranges(c, v);
   if (rc != PA_OK) return rc;
+  c->ev_spare = std::move(c->ev);
   c->ev = std::move(v);
   c->has_events = true;
   return PA_OK;
@@ -715,7 +758,11 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
   info->block_threads = pa::pass_block_threads();
   info->batch_events = pa::pass_wave_batch();
   info->max_segment_events = pa::kGroupMax;
-  info->device_bytes = c->d.bytes() + c->ev.bytes();
+  const LoadScratch &ls = c->ls;
+  info->device_bytes = c->d.bytes() + c->ev.bytes() + c->ev_spare.bytes() + (int64_t)c->text_dev.bytes +
+                       (int64_t)(ls.err.bytes + ls.ev_pin.bytes + ls.chunk_sorted.bytes + ls.cbase.bytes +
+                                 ls.level.bytes + ls.k0.bytes + ls.k1.bytes + ls.idx.bytes + ls.perm.bytes +
+                                 ls.chunk.bytes + ls.tmp.bytes + ls.part.bytes);
   for (int k = 0; k < 4; ++k) info->kernel_ms[k] = c->kernel_ms[k];
   return PA_OK;
 }
@@ -766,13 +813,6 @@ pa::text::Csr carve(void *base, const SegLayout &L) {
                        reinterpret_cast<int64_t *>(b + L.o_t), reinterpret_cast<uint8_t *>(b + L.o_val),
                        reinterpret_cast<float *>(b + L.o_slew)};
 }
-
-struct PinnedBuf {
-  void *p = nullptr;
-  ~PinnedBuf() {
-    if (p) (void)hipHostFree(p);
-  }
-};
 
 }  // namespace
 
@@ -855,15 +895,14 @@ int pa_run_text(pa_ctx *c, const char *text, int64_t text_len, int64_t t_clk, in
   }
 
   const SegLayout L = seg_layout(P, e_max);
-  PinnedBuf host[2];
+  // pinned host slots and the device staging area, kept by the context for later calls
   pa::text::Csr hcsr[2];
   for (int i = 0; i < (serial ? 1 : 2); ++i) {
-    HIPCHK(hipHostMalloc(&host[i].p, L.bytes, hipHostMallocDefault));
-    hcsr[i] = carve(host[i].p, L);
+    HIPCHK(c->text_host[i].ensure(L.bytes));
+    hcsr[i] = carve(c->text_host[i].p, L);
   }
-  DBuf dev;
-  HIPCHK(dev.alloc(L.bytes));
-  const pa::text::Csr dcsr = carve(dev.p, L);
+  HIPCHK(c->text_dev.ensure(L.bytes));
+  const pa::text::Csr dcsr = carve(c->text_dev.p, L);
   std::vector<uint8_t> cur(h.init), nxt((size_t)P);
   pa::text::Packer pk(pool);
 
