@@ -90,10 +90,11 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// value of another lane by a DPP move; lanes without a source read 0
+// value of another lane by a DPP move; lanes without a source read 0 (the
+// bound control writes 0 there, so no zeroed old value is needed)
 template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
 }
 
 // another lane's value by a DPP move inside a scan step: lanes without a
