@@ -140,6 +140,42 @@ def test_single_gate_and_window_edges():
     pu.assert_parity(pu.gpu_run(d, t2), _oracle(d, t2), label="single gate")
 
 
+def test_cycle_bits_above_the_gate_id():
+    """A 1 ns clock in 1 fs ticks leaves 9 bits of the low key word for the
+    cycle in the chunk: 1024-cycle chunks (and the 2048-cycle window) need the
+    cycle bits the gate id leaves free in the high word."""
+    d, t = _random(seed=12, G=300, C=2500, T=1_000_000, rate=0.01)
+    _print_case("cycle high bits")
+    o = _oracle(d, t)
+    for chunk in (0, 512, 1024):
+        g = pu.gpu_run(d, t, chunk_cycles=chunk)
+        pu.assert_parity(g, o, label=f"high cycle bits chunk {chunk}")
+        assert g["_info"]["chunk_cycles"] == (chunk or 1024)
+
+
+def test_widest_gate_ids_and_clock():
+    """2^21 + 5 gates (22-bit gate ids, no free bits in the high word) and a
+    clock of 2^31 - 5 ticks for one-input cells (the pin code and the time
+    in the cycle fill the low word): every chunk is one cycle."""
+    rng = np.random.default_rng(13)
+    lib = synth.make_library(rng, (1,), cells_per_k=2, n_axis=4)
+    G = (1 << 21) + 5
+    des = synth.assign_gates(rng, lib, np.ones(G, dtype=np.int64), 1.0, 50.0)
+    P = 2 * G
+    T, C = (1 << 31) - 5, 6
+    rates = np.zeros(P)
+    hot = rng.choice(P, size=400, replace=False)
+    rates[hot] = 2.0
+    rates[-2:] = 3.0  # the last gate, the largest id
+    tr = synth.poisson_trace(rng, rates, C, T)
+    tr = dataclasses.replace(tr, evt_slew=rng.uniform(50, 900, tr.n_events).astype(np.float32))
+    _print_case(f"widest ids E={tr.n_events}")
+    o = _oracle(des, tr)
+    g = pu.gpu_run(des, tr)
+    pu.assert_parity(g, o, label="widest ids")
+    assert g["_info"]["chunk_cycles"] == 1
+
+
 def test_dense_glitch_train():
     """One gate with thousands of events, about 70 of them per clock cycle
     (time windows of single cycles), many inside single cycles."""
