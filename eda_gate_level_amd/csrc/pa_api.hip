@@ -371,7 +371,8 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
 // the kernel moves each nominal cut forward to the next window head.  Also the
 // first block of every chunk, for the finalize kernel.
 static int build_ranges(pa_ctx *c, Events &v) {
-  const int64_t target_blocks = c->tun.grid_blocks > 0 ? c->tun.grid_blocks : 4 * (int64_t)c->n_cu;
+  const int64_t target_blocks =
+      c->tun.grid_blocks > 0 ? c->tun.grid_blocks : (int64_t)pa::pass_blocks_per_cu() * c->n_cu;
   const int64_t min_events = 4 * (int64_t)pa::pass_wave_batch() * (pa::pass_block_threads() / 64);
   const int64_t per = std::max<int64_t>(min_events, (v.E + target_blocks - 1) / std::max<int64_t>(1, target_blocks));
   std::vector<uint32_t> rs, rq, cb(v.Q + 1);
@@ -482,7 +483,7 @@ int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *p
   // the bits the gate id leaves free in the high word
   const uint32_t gb = bits_for((uint64_t)std::max<int64_t>(G - 1, 0));
   const uint32_t lc_max = (32 - v.pb - v.tb) + (22 - gb);
-  int64_t Cc_want = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : 1024;
+  int64_t Cc_want = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : pa::pass_max_chunk_cycles();
   Cc_want = std::min<int64_t>(Cc_want, (int64_t)pa::pass_max_chunk_cycles());
   if (lc_max < 31) Cc_want = std::min<int64_t>(Cc_want, int64_t(1) << lc_max);
   int64_t Cc = 1;

@@ -122,6 +122,8 @@ hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rs
                               hipStream_t s);
 int pass_wave_bounds_per_block();
 int pass_block_threads();
+int pass_blocks_per_cu();       // blocks of the pass resident on one compute unit
+size_t pass_static_lds_bytes();  // static LDS of a block of the pass
 int pass_wave_batch();
 int pass_max_chunk_cycles();
 // dynamic LDS bytes of the pass, and whether the cell tables fit in it

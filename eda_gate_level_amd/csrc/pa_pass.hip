@@ -48,16 +48,17 @@ namespace pa {
 namespace {
 
 #ifndef PA_NT
-#define PA_NT 256
+#define PA_NT 1024
 #endif
 #ifndef PA_FUSED_ATTR
 #define PA_FUSED_ATTR
 #endif
 constexpr int kNT = PA_NT;           // threads per block
 constexpr int kNW = kNT / 64;        // waves per block, each working on its own batches
+constexpr int kBPC = 1024 / kNT;     // blocks per compute unit (16 waves each)
 constexpr int kB = 128;              // events per wave batch, two consecutive ones per lane
-constexpr int kCCMAX = 1024;         // max cycles per chunk (LDS bins)
-constexpr size_t kLdsMax = 64 * 1024;
+constexpr int kCCMAX = 2048;         // max cycles per chunk (LDS bins)
+constexpr size_t kLdsMax = 160 * 1024 / kBPC;  // LDS of a block (gfx950: 160 KB per compute unit)
 static_assert(kB - 1 >= kGroupMax, "a (gate, cycle) run fits in one batch after an odd start");
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
@@ -375,6 +376,41 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         st_sl[wid][i0] = s0;
         st_sl[wid][i1] = s1;
         wave_sync();
+        // glitches in runs of three or more events: the pin's previous event
+        // in the run (it exists: the glitch's pin has an earlier event in the
+        // run).  In pulse trains it is mostly the event just before; for the
+        // rest it is the pin's last event before this one, found for every
+        // pin left by a max scan of positions.
+        if (slowgl) {
+          bool need0 = gl0, need1 = gl1;
+          int pp0 = 0, pp1 = 0;
+          if (need0 && (lkp0 & outc) == c0) {  // (the event before a glitch is in its run)
+            pp0 = i0 - 1;
+            need0 = false;
+          }
+          if (need1 && c0 == c1) {
+            pp1 = i0;
+            need1 = false;
+          }
+          if ((__ballot(need0) | __ballot(need1)) != 0ull) {
+            for (uint32_t c = 0; c <= outc; ++c) {
+              if ((__ballot(need0 && c0 == c) | __ballot(need1 && c1 == c)) == 0ull) continue;
+              const uint32_t v0 = (a0 && c0 == c) ? (uint32_t)(i0 + 1) : 0u;
+              const uint32_t v1 = (a1 && c1 == c) ? (uint32_t)(i1 + 1) : 0u;
+              const uint32_t Mx = dpp_mov<0x138>(max_scan(max(v0, v1)));  // last before slot i0
+              if (need0 && c0 == c) pp0 = (int)Mx - 1;
+              if (need1 && c1 == c) pp1 = (int)max(Mx, v0) - 1;
+            }
+          }
+          if (gl0) {
+            tq0 = (slk[pp0] >> pb) & tmask;
+            sq0 = st_sl[wid][pp0];
+          }
+          if (gl1) {
+            tq1 = (slk[pp1] >> pb) & tmask;
+            sq1 = st_sl[wid][pp1];
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int p = r ? i1 : i0;
@@ -398,24 +434,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
               fw = y + 1 < end && sgh[y + 1];
             }
           }
-          // glitch in a long run: back to the pin's previous event of the run
-          // (it exists, so the step stops there; the batch start bounds it
-          // all the same)
-          bool sr = slowgl && (r ? gl1 : gl0);
-          uint32_t tq = r ? tq1 : tq0;
-          float sq = r ? sq1 : sq0;
-          for (int y = p - 1; __ballot(sr) != 0ull; --y) {
-            if (sr) {
-              if (y < first) {
-                sr = false;
-              } else if ((slk[y] & outc) == cx) {
-                tq = (slk[y] >> pb) & tmask;
-                sq = st_sl[wid][y];
-                sr = false;
-              }
-            }
-          }
-          if (r) { S1s ^= corr; mk1 = mk; tq1 = tq; sq1 = sq; } else { S0s ^= corr; mk0 = mk; tq0 = tq; sq0 = sq; }
+          if (r) { S1s ^= corr; mk1 = mk; } else { S0s ^= corr; mk0 = mk; }
         }
         wave_sync();
       }
@@ -731,6 +750,10 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
 }  // namespace
 
 int pass_block_threads() { return kNT; }
+int pass_blocks_per_cu() { return kBPC; }
+size_t pass_static_lds_bytes() {
+  return (size_t)kNW * kB * (sizeof(uint32_t) + sizeof(uint8_t) + sizeof(float)) + (size_t)kNW * 9 * sizeof(double);
+}
 int pass_wave_bounds_per_block() { return kNW + 1; }
 
 hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rstart, int32_t n_ranges, int32_t *wb,
@@ -747,14 +770,14 @@ size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int
 }
 
 bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
-  return pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, true) <= 48 * 1024;
+  return pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, true) + pass_static_lds_bytes() <= kLdsMax;
 }
 
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
   const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak);
   const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
   const size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, cells);
-  if (dyn > kLdsMax) return hipErrorInvalidValue;
+  if (dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
   const dim3 g(grid_blocks), t(kNT);
   if (cells && !diag) {
     if (a.n_slew == 7) hipLaunchKernelGGL((k_fused<true, false, 5>), g, t, dyn, s, a);

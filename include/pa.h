@@ -59,9 +59,10 @@ typedef struct pa_ctx pa_ctx;
  * zero field means "choose automatically". */
 typedef struct {
   int32_t chunk_cycles;   /* cycles per time chunk of the event layout; rounded down to a
-                             power of two, at most 1024 and at most what the key's bits
-                             allow for the clock period and gate count (0 = 1024) */
-  int32_t grid_blocks;    /* target block count of the fused pass (0 = four per compute unit);
+                             power of two, at most 2048 and at most what the key's bits
+                             allow for the clock period and gate count (0 = 2048) */
+  int32_t grid_blocks;    /* target block count of the fused pass (0 = one 1024-thread block
+                             per compute unit);
                              the pass cuts the events into about this many ranges */
   int32_t time_kernels;   /* 0: no timing; 1: device times of the fused kernel, the finalize
                              kernel and the whole pass (three events on the stream);

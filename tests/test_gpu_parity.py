@@ -142,15 +142,15 @@ def test_single_gate_and_window_edges():
 
 def test_cycle_bits_above_the_gate_id():
     """A 1 ns clock in 1 fs ticks leaves 9 bits of the low key word for the
-    cycle in the chunk: 1024-cycle chunks (and the 2048-cycle window) need the
-    cycle bits the gate id leaves free in the high word."""
-    d, t = _random(seed=12, G=300, C=2500, T=1_000_000, rate=0.01)
+    cycle in the chunk: 1024- and 2048-cycle chunks need the cycle bits the
+    gate id leaves free in the high word (2048 is the default)."""
+    d, t = _random(seed=12, G=300, C=4500, T=1_000_000, rate=0.01)
     _print_case("cycle high bits")
     o = _oracle(d, t)
-    for chunk in (0, 512, 1024):
+    for chunk in (0, 512, 1024, 2048):
         g = pu.gpu_run(d, t, chunk_cycles=chunk)
         pu.assert_parity(g, o, label=f"high cycle bits chunk {chunk}")
-        assert g["_info"]["chunk_cycles"] == (chunk or 1024)
+        assert g["_info"]["chunk_cycles"] == (chunk or 2048)
 
 
 def test_widest_gate_ids_and_clock():
