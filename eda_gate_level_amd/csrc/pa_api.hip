@@ -98,11 +98,13 @@ struct Events {
   std::vector<uint32_t> h_chunk_base;
   DBuf rstart, rchunk, chunk_blk;  // block ranges of the pass, first block of every chunk
   DBuf wbound, l0;                 // the waves' ranges of every block; leakage power at t = 0
+  DBuf lplan;                      // per block, the cells whose LUTs it copies into LDS
+  int32_t lut_lds = 0;             // LDS doubles of a block for those copies (0: none)
   int32_t n_ranges = 0, grid = 1;
   DBuf blk_wave, blk_cnt, blk_part, res;
   int64_t bytes() const {
     return (int64_t)(key.bytes + slew.bytes + orig.bytes + pin_init.bytes + rstart.bytes + rchunk.bytes +
-                     chunk_blk.bytes + wbound.bytes + l0.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
+                     chunk_blk.bytes + wbound.bytes + l0.bytes + lplan.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
                      res.bytes);
   }
 };
@@ -264,8 +266,8 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
     meta[2 * i + 1] = (uint32_t)lb;
     lb += (uint64_t(1) << k) * (uint64_t)k * n_slew * n_cap;
     kb += uint64_t(1) << k;
-    if (lb >= (uint64_t(1) << 32) || kb >= (uint64_t(1) << 28))
-      return fail(PA_EINVAL, "pa_load_design: LUT tables exceed 2^32 entries or leakage tables 2^28");
+    if (lb >= (uint64_t(1) << 31) || kb >= (uint64_t(1) << 28))
+      return fail(PA_EINVAL, "pa_load_design: LUT tables reach 2^31 entries or leakage tables 2^28");
     const double *sa = &hsa[(size_t)i * n_slew];
     for (int j = 0; j + 1 < n_slew; ++j)
       if (!(sa[j] < sa[j + 1]))
@@ -405,8 +407,20 @@ static int build_ranges(pa_ctx *c, Events &v) {
   HIPCHK(v.wbound.ensure(sizeof(int32_t) * (size_t)v.grid * pa::pass_wave_bounds_per_block()));
   HIPCHK(pa::launch_wave_bounds(v.key.as<uint64_t>(), v.E, v.rstart.as<uint32_t>(), v.n_ranges,
                                 v.wbound.as<int32_t>(), c->stream));
-  // leakage power at t = 0, from the initial pin values
   const Design &d = c->d;
+  // the cells whose LUTs every block copies into its spare LDS
+  v.lut_lds = pa::pass_lut_lds_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak);
+  if (c->tun.lut_lds_kib < 0) v.lut_lds = 0;
+  else if (c->tun.lut_lds_kib > 0) v.lut_lds = std::min<int32_t>(v.lut_lds, c->tun.lut_lds_kib * 128);
+  if (v.lut_lds > 0 && v.n_ranges > 0) {
+    HIPCHK(v.lplan.ensure(sizeof(uint2) * (size_t)v.n_ranges * pa::pass_lut_plan_slots()));
+    HIPCHK(pa::launch_lut_plan(v.key.as<uint64_t>(), v.wbound.as<int32_t>(), v.n_ranges, d.gate_rec.as<uint4>(),
+                               d.cell_meta.as<uint2>(), v.gb, d.n_slew, d.n_cap, v.lut_lds, v.lplan.as<uint2>(),
+                               c->stream));
+  } else {
+    v.lut_lds = 0;
+  }
+  // leakage power at t = 0, from the initial pin values
   DBuf &part = c->ls.part;
   HIPCHK(part.ensure(sizeof(double) * pa::leak0_parts()));
   HIPCHK(v.l0.ensure(sizeof(double)));
@@ -630,6 +644,8 @@ static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_eve
   a.n_cells = d.n_cells;
   a.n_thr = d.n_thr;
   a.n_leak = d.n_leak;
+  a.lut_plan = v.lut_lds > 0 ? v.lplan.as<uint2>() : nullptr;
+  a.lut_lds = v.lut_lds;
   a.blk_wave = v.blk_wave.as<double>();
   a.blk_cnt = v.blk_cnt.as<unsigned long long>();
   a.blk_part = v.blk_part.as<double>();

@@ -83,6 +83,9 @@ struct PassArgs {
   const double *leak;
   int32_t n_slew, n_cap, n_cells, n_thr;
   int64_t n_leak;
+  // cells whose LUTs every block copies into LDS (see launch_lut_plan)
+  const uint2 *lut_plan;      // [n_ranges][pass_lut_plan_slots()] (cell, LDS offset in doubles), cell ~0 = none
+  int32_t lut_lds;            // LDS reserved for them, doubles (0: none)
   // per-block results, reduced by the finalize kernel
   double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
   unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32
@@ -121,6 +124,17 @@ hipError_t launch_finalize(const FinalArgs &a, hipStream_t s);
 hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rstart, int32_t n_ranges, int32_t *wb,
                               hipStream_t s);
 int pass_wave_bounds_per_block();
+// Per block, the cells whose LUTs it copies into the LDS left over by its bins
+// and cell tables (lut_lds doubles, from pass_lut_lds_doubles): 64 events
+// sampled evenly over the block's range give each cell present a weight, and
+// the heaviest cells that still fit are taken, at most
+// pass_lut_plan_slots() of them.  plan holds that many (cell, LDS offset)
+// pairs per block; unused slots have cell ~0.
+hipError_t launch_lut_plan(const uint64_t *key, const int32_t *wb, int32_t n_ranges, const uint4 *gate_rec,
+                           const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap, int32_t lut_lds, uint2 *plan,
+                           hipStream_t s);
+int pass_lut_plan_slots();
+int32_t pass_lut_lds_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak);
 int pass_block_threads();
 int pass_blocks_per_cu();       // blocks of the pass resident on one compute unit
 size_t pass_static_lds_bytes();  // static LDS of a block of the pass

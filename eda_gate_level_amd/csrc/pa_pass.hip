@@ -25,11 +25,15 @@
 //     input pin among them charges the leakage change of the whole set;
 //   * a glitch is an event whose pin has an earlier event in the same
 //     (gate, cycle) run: a segmented OR scan of pin bits over the runs
-//     (Fig. 7); its pulse width and the previous slew come from that earlier
-//     event, found by a short step back over the run (Eq. 2);
+//     (Fig. 7); its pulse width and the previous slew come from the pin's
+//     previous event in the run: the event just before, or the one a max
+//     scan of positions per pin finds (Eq. 2);
 //   * one lane per event: state-selected LUT, bilinear on slew and load
 //     (Sec. 2.4.1, Fig. 2), switching energy (Eq. 1), energies added to
-//     per-cycle bins in LDS;
+//     per-cycle bins in LDS.  The LUTs of the cells most of a block's events
+//     use are copied into the block's spare LDS at its start (chosen at load
+//     from a sample of its events); the other cells are read through the
+//     caches;
 //   * leakage is charged as power changes: at every distinct input timestamp
 //     the lowest switching input pin adds dP = leak[S+] - leak[S-]; its
 //     partial bin gets dP * (bin end - t) and all later bins get dP * their
@@ -58,6 +62,9 @@ constexpr int kNW = kNT / 64;        // waves per block, each working on its own
 constexpr int kBPC = 1024 / kNT;     // blocks per compute unit (16 waves each)
 constexpr int kB = 128;              // events per wave batch, two consecutive ones per lane
 constexpr int kCCMAX = 2048;         // max cycles per chunk (LDS bins)
+constexpr int kPlan = 8;             // cells per block whose LUTs may sit in LDS
+constexpr uint32_t kLutLds = 0x80000000u;  // LUT base flag in a block's cell table: offset into its LDS copy
+typedef __attribute__((address_space(3))) double lds_f64;
 constexpr size_t kLdsMax = 160 * 1024 / kBPC;  // LDS of a block (gfx950: 160 KB per compute unit)
 static_assert(kB - 1 >= kGroupMax, "a (gate, cycle) run fits in one batch after an odd start");
 
@@ -155,6 +162,7 @@ struct CellLds {
   unsigned long long *bc;
   double *leak;
   uint2 *meta;
+  double *lut;  // the block's LUT copies, 16-byte aligned after the cell meta
 };
 
 __host__ __device__ inline size_t cell_bytes(int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
@@ -163,7 +171,7 @@ __host__ __device__ inline size_t cell_bytes(int n_cells, int n_slew, int n_cap,
 }
 
 // dynamic LDS: [slew (axis, 1/width) pairs][cap (axis, 1/width) pairs][slew thresholds][bins: wave,
-// leakage change, counts][leakage][cell meta]
+// leakage change, counts][leakage][cell meta][LUT copies]
 __device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, int n_slew, int n_cap, int n_thr,
                                          int64_t n_leak, bool cells) {
   CellLds L;
@@ -175,6 +183,8 @@ __device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, 
   L.bc = reinterpret_cast<unsigned long long *>(L.bb + Cc);
   L.leak = reinterpret_cast<double *>(L.bc + Cc);
   L.meta = reinterpret_cast<uint2 *>(L.leak + (cells ? n_leak : 0));
+  const size_t end = (size_t)(reinterpret_cast<unsigned char *>(L.meta + (cells ? n_cells : 0)) - s);
+  L.lut = reinterpret_cast<double *>(s + ((end + 15) & ~size_t(15)));
   return L;
 }
 
@@ -242,7 +252,34 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
     for (int j = tid; j < a.n_cells * (nc - 1); j += kNT) L.caxw[j] = a.cell_caxw[j];
     for (int j = tid; j < a.n_cells * nthr; j += kNT) L.thr[j] = a.cell_thr[j];
     for (int j = tid; j < a.n_leak; j += kNT) L.leak[j] = a.leak[j];
-    for (int j = tid; j < a.n_cells; j += kNT) L.meta[j] = a.cell_meta[j];
+    // the cells whose LUTs this block reads from LDS: their table entries
+    // point into the copy instead of the global LUT
+    uint32_t pc[kPlan], po[kPlan];
+#pragma unroll
+    for (int e = 0; e < kPlan; ++e) {
+      const uint2 v = (has_range && a.lut_lds > 0) ? a.lut_plan[(size_t)b * kPlan + e] : make_uint2(~0u, 0u);
+      pc[e] = v.x;
+      po[e] = v.y;
+    }
+    for (int j = tid; j < a.n_cells; j += kNT) {
+      uint2 mv = a.cell_meta[j];
+#pragma unroll
+      for (int e = 0; e < kPlan; ++e)
+        if (pc[e] == (uint32_t)j) mv.y = kLutLds | po[e];
+      L.meta[j] = mv;
+    }
+    // LUT sizes 2^k k ns nc are even, so every table starts 16-byte aligned
+#pragma unroll 1
+    for (int e = 0; e < kPlan; ++e) {
+      if (pc[e] == ~0u) break;
+      const uint2 gm = a.cell_meta[pc[e]];
+      const uint32_t k = gm.x & 15u;
+      const int n2 = (int)((((1u << k) * k) * (uint32_t)(ns * nc)) >> 1);
+      const double2 *src = reinterpret_cast<const double2 *>(a.lut + gm.y);
+      double2 *dst = reinterpret_cast<double2 *>(L.lut + po[e]);
+#pragma unroll 4
+      for (int j = tid; j < n2; j += kNT) dst[j] = src[j];
+    }
   }
   __syncthreads();
 
@@ -478,8 +515,17 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         const double2 aw = axw_of(cell, si);
         const double fa = ((double)sl - aw.x) * aw.y;
         const uint32_t cl = input ? code : 0u;
-        const double *Lp = a.lut + (m.y + __umul24(__umul24(__umul24(Sm, kk) + cl, ns) + si, nc) + (info >> 24));
-        const double L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
+        const uint32_t lo = __umul24(__umul24(__umul24(Sm, kk) + cl, ns) + si, nc) + (info >> 24);
+        double L00, L01, L10, L11;
+        if (CELL_LDS && (m.y & kLutLds) != 0u) {
+          // an LDS-typed pointer, so the two branches' loads stay ds reads and
+          // global loads instead of merging into flat loads
+          const lds_f64 *Lp = (const lds_f64 *)(L.lut) + ((m.y & ~kLutLds) + lo);
+          L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
+        } else {
+          const double *Lp = a.lut + (m.y + lo);
+          L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
+        }
         const double2 cx = caxw_of(cell, info >> 24);
         const double fc = (cap - cx.x) * cx.y;  // position on the gate's cap segment (Sec. 2.4.1, Fig. 2)
         const double v0 = L00 + fc * (L01 - L00);
@@ -625,6 +671,51 @@ __global__ __launch_bounds__(64) void k_wave_bounds(const uint64_t *key, int64_t
   }
 }
 
+// One wave per block range: 64 events sampled at the midpoints of 64 equal
+// slices of the range give the cells present (nondecreasing, since gates
+// are numbered in cell order) and each cell's share; the heaviest cells whose
+// LUTs still fit in `budget` doubles are taken, heaviest first.
+__global__ __launch_bounds__(64) void k_lut_plan(const uint64_t *key, const int32_t *wb, const uint4 *gate_rec,
+                                                 const uint2 *cell_meta, uint32_t gb, int ns, int nc,
+                                                 uint32_t budget, uint2 *plan) {
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int r0 = wb[(size_t)b * (kNW + 1)], r1 = wb[(size_t)b * (kNW + 1) + kNW];
+  const uint32_t gmask = (1u << gb) - 1u;
+  uint32_t cell = ~0u;
+  if (r1 > r0) {
+    const int p = r0 + (int)((int64_t)(r1 - r0) * (2 * lane + 1) / 128);
+    const uint32_t g = (uint32_t)(key[p] >> (32 + 10)) & gmask;
+    cell = gate_rec[g].z & 0xFFFFFFu;
+  }
+  const uint32_t prev = __shfl_up(cell, 1);
+  const bool start = cell != ~0u && (lane == 0 || prev != cell);
+  const unsigned long long st = __ballot(start);
+  uint32_t len = 0, sz = 0;
+  if (start) {
+    const unsigned long long after = lane < 63 ? (st >> (lane + 1)) << (lane + 1) : 0ull;
+    len = (after ? (uint32_t)(__ffsll((long long)after) - 1) : 64u) - (uint32_t)lane;
+    const uint32_t k = cell_meta[cell].x & 15u;
+    sz = ((1u << k) * k) * (uint32_t)(ns * nc);
+  }
+  bool cand = start && sz <= budget;
+  uint32_t used = 0;
+  int ne = 0;
+  while (ne < kPlan) {
+    uint32_t v = cand ? (len << 6 | (63u - (uint32_t)lane)) : 0u;
+    for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+    if (v == 0u) break;
+    const int bl = 63 - (int)(v & 63u);
+    const uint32_t bsz = (uint32_t)__shfl((int)sz, bl), bcell = (uint32_t)__shfl((int)cell, bl);
+    if (lane == bl) cand = false;
+    if (used + bsz <= budget) {
+      if (lane == 0) plan[(size_t)b * kPlan + ne] = make_uint2(bcell, used);
+      used += bsz;
+      ++ne;
+    }
+  }
+  if (lane >= ne && lane < kPlan) plan[(size_t)b * kPlan + lane] = make_uint2(~0u, 0u);
+}
+
 constexpr int kFC = 64;             // finalize: cycles per block (one per lane)
 constexpr int kFP = 8;              // finalize: waves per block, each adding up a share of the blocks
 constexpr int kFT = kFC * kFP;
@@ -762,6 +853,15 @@ hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rs
   hipLaunchKernelGGL(k_wave_bounds, dim3(n_ranges), dim3(64), 0, s, key, E, rstart, wb);
   return hipGetLastError();
 }
+hipError_t launch_lut_plan(const uint64_t *key, const int32_t *wb, int32_t n_ranges, const uint4 *gate_rec,
+                           const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap, int32_t lut_lds, uint2 *plan,
+                           hipStream_t s) {
+  if (n_ranges <= 0 || lut_lds <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lut_plan, dim3(n_ranges), dim3(64), 0, s, key, wb, gate_rec, cell_meta, gb, n_slew, n_cap,
+                     (uint32_t)lut_lds, plan);
+  return hipGetLastError();
+}
+int pass_lut_plan_slots() { return kPlan; }
 int pass_wave_batch() { return kB; }
 int pass_max_chunk_cycles() { return kCCMAX; }
 
@@ -773,10 +873,24 @@ bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, i
   return pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, true) + pass_static_lds_bytes() <= kLdsMax;
 }
 
+static size_t lut_lds_offset(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
+  return (pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, true) + 15) & ~size_t(15);
+}
+
+int32_t pass_lut_lds_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
+  if (!pass_cells_fit_lds(Cc, n_cells, n_slew, n_cap, n_thr, n_leak)) return 0;
+  const size_t used = lut_lds_offset(Cc, n_cells, n_slew, n_cap, n_thr, n_leak) + pass_static_lds_bytes();
+  return used < kLdsMax ? (int32_t)((kLdsMax - used) / 16 * 2) : 0;
+}
+
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
   const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak);
   const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
-  const size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, cells);
+  size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, cells);
+  if (cells && a.lut_lds > 0) {
+    if (!a.lut_plan) return hipErrorInvalidValue;
+    dyn = lut_lds_offset(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak) + 8 * (size_t)a.lut_lds;
+  }
   if (dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
   const dim3 g(grid_blocks), t(kNT);
   if (cells && !diag) {

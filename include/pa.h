@@ -70,6 +70,10 @@ typedef struct {
   int32_t fixed_window_cycles; /* 0: density-aware windows (below); n > 0: every gate's
                              windows are n cycles (rounded down to a power of two, at most the
                              chunk) -- the fixed-window layout the paper compares against */
+  int32_t lut_lds_kib;    /* LDS each block of the pass may fill with copies of the LUTs its
+                             events use most: 0 = all the LDS its bins and cell tables leave;
+                             n > 0 = at most n KiB; negative = none (every LUT read goes
+                             through the caches) */
 } pa_tunables;
 
 /* Create a context on HIP device `hip_device`, launching on `hip_stream`
@@ -93,7 +97,9 @@ int pa_set_timing(pa_ctx *ctx, int32_t time_kernels);
  *   cap_axis[n_cells][n_cap]    float64 farads, strictly increasing per cell
  *   lut_J   float64, per cell concatenated: [2^k][k][n_slew][n_cap] joules
  *   leak_W  float64, per cell concatenated: [2^k] watts
- *   2 <= n_slew, n_cap <= 16.  Loading a design drops any loaded events. */
+ *   2 <= n_slew, n_cap <= 16; the LUTs of all cells together hold fewer than
+ *   2^31 entries and the leakage tables fewer than 2^28 (PA_EINVAL otherwise).
+ *   Loading a design drops any loaded events. */
 int pa_load_design(pa_ctx *ctx, int64_t n_gates, const int32_t *gate_cell, const double *gate_cap_F,
                    int32_t n_cells, const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap,
                    const double *slew_axis, const double *cap_axis, const double *lut_J,

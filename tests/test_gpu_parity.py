@@ -119,6 +119,51 @@ def test_fixed_windows_do_not_change_results(n_fix):
     assert abs(st["mean"] * st["n_windows"] - t.n_events) < 1e-6 * t.n_events
 
 
+def _many_cells(seed, cells_per_k, ks, G, C, rate, n_axis=5):
+    rng = np.random.default_rng(seed)
+    lib = synth.make_library(rng, ks, cells_per_k=cells_per_k, n_axis=n_axis)
+    k = rng.choice(np.array(ks), size=G)
+    des = synth.assign_gates(rng, lib, k, 1.0, 50.0)
+    tr = synth.poisson_trace(rng, np.full(int(des.pin_base()[-1]), rate), C, 1000)
+    return des, dataclasses.replace(tr, evt_slew=rng.uniform(50, 900, tr.n_events).astype(np.float32))
+
+
+LUT_CASES = {
+    "eight-cells": lambda: _random(seed=1),
+    "wide-cells": lambda: _random(seed=2, ks=(5, 6, 7, 8), G=60, rate=0.2),  # 8-input LUTs never fit
+    "eighty-cells": lambda: _many_cells(11, 40, (1, 2), G=600, C=50, rate=0.3),  # > 8 cells per block
+    "tiny-7x7": lambda: (lambda w: (w.design, w.trace))(synth.make("tiny")),
+}
+
+
+@pytest.mark.parametrize("name", list(LUT_CASES))
+def test_lut_copies_in_lds(name):
+    """Each block copies the LUTs of the cells most of its events use into
+    LDS and reads the rest through the caches.  With no copies, with room for
+    the smallest tables only, and with all the spare LDS, the results must
+    meet the parity bar, in both the plain and the per-event kernels, and the
+    event energies must be bit for bit the same (same arithmetic on the same
+    table values, summed in a fixed order).  The bins and the leakage built
+    from them are LDS atomics, whose order between waves is free, so they
+    match to rounding."""
+    d, t = LUT_CASES[name]()
+    _print_case(f"lut copies {name}")
+    o = _oracle(d, t)
+    for per_event in (False, True):
+        ref = None
+        for kib in (-1, 1, 0):
+            g = pu.gpu_run(d, t, per_event=per_event, lut_lds_kib=kib)
+            pu.assert_parity(g, o, per_event=per_event, label=f"lut {name} {kib} {per_event}")
+            if ref is None:
+                ref = g
+                continue
+            for key in ("e_int_J", "e_sw_J", "e_gl_J", "n_glitches"):
+                assert g[key] == ref[key], (key, kib, per_event)
+            assert pu.rel_err(g["e_leak_J"], ref["e_leak_J"]) <= 1e-13, (kib, per_event)
+            np.testing.assert_allclose(g["wave_J"], ref["wave_J"], rtol=1e-13, atol=0)
+            assert np.array_equal(g["cyc_events"], ref["cyc_events"])
+
+
 def test_no_events():
     d, t = _random(seed=8, G=50, rate=0.0)
     assert t.n_events == 0
