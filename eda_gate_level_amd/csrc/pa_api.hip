@@ -153,6 +153,7 @@ struct pa_ctx {
   Events ev;
   Events ev_spare;  // the events before the current ones: their buffers serve the next load
   LoadScratch ls;
+  bool keep_load_buffers = false;  // pa_run_text: ev_spare and ls live until the text is done
   PinnedBuf text_host[2];  // pa_run_text: packed segments on the host, and their device copy
   DBuf text_dev;
   double *h_res = nullptr;
@@ -431,9 +432,32 @@ static int build_ranges(pa_ctx *c, Events &v) {
   return PA_OK;
 }
 
+// the buffers of the previous event load and the load's scratch: kept across
+// the many loads of one activity text, dropped after a load of the caller's own
+static void release_load_buffers(pa_ctx *c) {
+  c->ls = LoadScratch();
+  c->ev_spare = Events();
+}
+
+static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr, const uint8_t *pin_init,
+                       const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_clk,
+                       int64_t t_max, double tick_s);
+
 int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr, const uint8_t *pin_init,
                    const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_clk,
                    int64_t t_max, double tick_s) {
+  const int rc = load_events(c, n_pins, n_events, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk, t_max, tick_s);
+  if (c && !c->keep_load_buffers) {
+    (void)hipSetDevice(c->device);
+    if (c->stream) (void)hipStreamSynchronize(c->stream);
+    release_load_buffers(c);
+  }
+  return rc;
+}
+
+static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr, const uint8_t *pin_init,
+                       const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_clk,
+                       int64_t t_max, double tick_s) {
   if (!c) return fail(PA_EINVAL, "pa_load_events: NULL context");
   if (!c->has_design) return fail(PA_ESTATE, "pa_load_events: no design loaded");
   const Design &d = c->d;
@@ -887,6 +911,16 @@ int pa_run_text(pa_ctx *c, const char *text, int64_t text_len, int64_t t_clk, in
   const int64_t S = o && o->segment_cycles > 0 ? o->segment_cycles : 1024;
   const bool serial = o && o->serial == 1;
   HIPCHK(hipSetDevice(c->device));
+  // the segments' loads reuse one another's buffers; they go when the text is done
+  struct HoldLoadBuffers {
+    pa_ctx *c;
+    explicit HoldLoadBuffers(pa_ctx *x) : c(x) { c->keep_load_buffers = true; }
+    ~HoldLoadBuffers() {
+      c->keep_load_buffers = false;
+      if (c->stream) (void)hipStreamSynchronize(c->stream);
+      release_load_buffers(c);
+    }
+  } hold(c);
   const int64_t P = c->d.P;
   hipStream_t s = c->stream;
 

@@ -177,8 +177,9 @@ typedef struct {
   int32_t grid_blocks, block_threads;
   int32_t batch_events;       /* events one wave takes per step of the pass */
   int32_t max_segment_events; /* most events of one gate in one clock cycle (the load limit) */
-  int64_t device_bytes;       /* library-owned device memory (the loaded data, the buffers of the
-                                 previous event load and the load's scratch, which later loads reuse) */
+  int64_t device_bytes;       /* library-owned device memory: the loaded design and events, the
+                                 per-pass scratch, and the staging of pa_run_text (the load's own
+                                 scratch is freed when pa_load_events returns) */
   float kernel_ms[4];         /* last timed pa_run: fused, finalize, (unused), whole pass; mode 2 fills only the last */
 } pa_info;
 int pa_get_info(pa_ctx *ctx, pa_info *info);
