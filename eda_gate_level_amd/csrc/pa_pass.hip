@@ -549,8 +549,11 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         }
         dyn = contrib;
         // leakage power change at this timestamp (owner = lowest switching input pin)
-        if (input && (r ? ow1 : ow0)) {
-          const double dp = leak_of(lb + (Sm ^ ((r ? mk1 : mk0) & smask))) - leak_of(lb + Sm);
+        // (read for every event, so that the reads can start early; output
+        // events and later events of a timestamp keep dp = 0)
+        const double lk1v = leak_of(lb + (Sm ^ ((r ? mk1 : mk0) & smask))), lk0v = leak_of(lb + Sm);
+        {
+          const double dp = (input && (r ? ow1 : ow0)) ? lk1v - lk0v : 0.0;
           if (dp != 0.0) {
             // rest of the event's bin (the flush corrects a partial last bin)
             const double part = dp * tick * (double)(T - tic);
