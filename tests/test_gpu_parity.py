@@ -164,6 +164,32 @@ def test_lut_copies_in_lds(name):
             assert np.array_equal(g["cyc_events"], ref["cyc_events"])
 
 
+def test_load_frees_its_scratch():
+    """The event load's scratch (sort keys, indexes, the radix sort's storage)
+    and the previous load's buffers are freed when the load returns: loading
+    the same events again keeps the footprint, and it stays within the
+    events' own arrays (key, slew, caller index: 16 B per event), the
+    per-block bins and the design."""
+    import eda_gate_level_amd as pa
+
+    d, t = _random(seed=12, G=3000, C=300, rate=0.05)
+    _print_case("load scratch")
+    an = pa.PowerAnalysis()
+    try:
+        an.load(d, t)
+        i1 = an.info()
+        an.load(d, t)
+        i2 = an.info()
+        an.run(per_event=False)
+        i3 = an.info()
+    finally:
+        an.close()
+    assert i2["device_bytes"] == i1["device_bytes"] == i3["device_bytes"]
+    bound = (24 * t.n_events + 16 * i1["grid_blocks"] * i1["chunk_cycles"] + 64 * d.n_gates
+             + 16 * int(d.pin_base()[-1]) + d.lut_J.nbytes + (1 << 20))
+    assert i1["device_bytes"] <= bound, (i1["device_bytes"], bound)
+
+
 def test_no_events():
     d, t = _random(seed=8, G=50, rate=0.0)
     assert t.n_events == 0
