@@ -96,15 +96,16 @@ struct Events {
   uint32_t tb = 0, pb = 0, gb = 1, last_len = 0;
   DBuf key, slew, orig, pin_init;
   std::vector<uint32_t> h_chunk_base;
+  int64_t n_windows = 0, slots = 0;  // windows; slots of the lane streams (events and empty slots)
   DBuf rstart, rchunk, chunk_blk;  // block ranges of the pass, first block of every chunk
-  DBuf wbound, l0;                 // the waves' ranges of every block; leakage power at t = 0
+  DBuf wdesc, wlen, l0;            // every wave's (first slot, events per lane); events per window; leakage at t = 0
   DBuf lplan;                      // per block, the cells whose LUTs it copies into LDS
   int32_t lut_lds = 0;             // LDS doubles of a block for those copies (0: none)
   int32_t n_ranges = 0, grid = 1;
   DBuf blk_wave, blk_cnt, blk_part, res;
   int64_t bytes() const {
     return (int64_t)(key.bytes + slew.bytes + orig.bytes + pin_init.bytes + rstart.bytes + rchunk.bytes +
-                     chunk_blk.bytes + wbound.bytes + l0.bytes + lplan.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
+                     chunk_blk.bytes + wdesc.bytes + wlen.bytes + l0.bytes + lplan.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
                      res.bytes);
   }
 };
@@ -139,6 +140,8 @@ struct PinnedBuf {
 // and free nothing
 struct LoadScratch {
   DBuf err, ev_pin, chunk_sorted, cbase, level, k0, k1, idx, perm, chunk, tmp, part;
+  DBuf skey, sslew, sorig;            // the events in window order
+  DBuf winc, ws, bwin, wkey0, wkey1, widx, worder, wlane, lane_len, wave_len;  // lane streams
 };
 
 }  // namespace
@@ -369,14 +372,22 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   return PA_OK;
 }
 
-// Block ranges of the pass: every chunk's events are cut into pieces of about
-// E / target events (never across a chunk, so a block's bins cover one chunk);
-// the kernel moves each nominal cut forward to the next window head.  Also the
-// first block of every chunk, for the finalize kernel.
+// Block ranges of the pass and the lane streams.  Every chunk's events are cut
+// into pieces of about E / target events (never across a chunk, so a block's
+// bins cover one chunk), each cut moved to the next window start; a block's
+// windows are then dealt to its lanes (pa_load.hip) and scattered into the
+// interleaved streams.  Also the first block of every chunk, for the
+// finalize kernel.  The sorted events are in c->ls.skey / sslew / sorig.
 static int build_ranges(pa_ctx *c, Events &v) {
+  const Design &d = c->d;
+  hipStream_t s = c->stream;
+  LoadScratch &ls = c->ls;
+  if (pa::pass_block_threads() != pa::lane_plan_lanes())
+    return fail(PA_EINVAL, "pa_load_events: lane plan and pass disagree on the block size");
+  const int NW = pa::pass_waves_per_block();
   const int64_t target_blocks =
       c->tun.grid_blocks > 0 ? c->tun.grid_blocks : (int64_t)pa::pass_blocks_per_cu() * c->n_cu;
-  const int64_t min_events = 4 * (int64_t)pa::pass_wave_batch() * (pa::pass_block_threads() / 64);
+  const int64_t min_events = 4 * (int64_t)pa::pass_wave_batch() * NW;
   const int64_t per = std::max<int64_t>(min_events, (v.E + target_blocks - 1) / std::max<int64_t>(1, target_blocks));
   std::vector<uint32_t> rs, rq, cb(v.Q + 1);
   for (int32_t q = 0; q < v.Q; ++q) {
@@ -390,8 +401,9 @@ static int build_ranges(pa_ctx *c, Events &v) {
     }
   }
   cb[v.Q] = (uint32_t)rs.size();
-  v.n_ranges = (int32_t)rs.size();
-  v.grid = std::max(1, v.n_ranges);
+  const int32_t nr = (int32_t)rs.size();
+  v.n_ranges = nr;
+  v.grid = std::max(1, nr);
   rs.push_back((uint32_t)v.E);
   rq.push_back(0);
   HIPCHK(v.rstart.ensure(sizeof(uint32_t) * rs.size()));
@@ -401,34 +413,102 @@ static int build_ranges(pa_ctx *c, Events &v) {
   HIPCHK(v.blk_cnt.ensure(sizeof(unsigned long long) * (size_t)v.grid * v.Cc));
   HIPCHK(v.blk_part.ensure(sizeof(double) * 8 * (size_t)v.grid));
   HIPCHK(v.res.ensure(sizeof(double) * 16));
-  HIPCHK(hipMemcpyAsync(v.rstart.p, rs.data(), sizeof(uint32_t) * rs.size(), hipMemcpyHostToDevice, c->stream));
-  HIPCHK(hipMemcpyAsync(v.rchunk.p, rq.data(), sizeof(uint32_t) * rq.size(), hipMemcpyHostToDevice, c->stream));
-  HIPCHK(hipMemcpyAsync(v.chunk_blk.p, cb.data(), sizeof(uint32_t) * cb.size(), hipMemcpyHostToDevice, c->stream));
-  // the cuts between every block's waves, moved to window heads
-  HIPCHK(v.wbound.ensure(sizeof(int32_t) * (size_t)v.grid * pa::pass_wave_bounds_per_block()));
-  HIPCHK(pa::launch_wave_bounds(v.key.as<uint64_t>(), v.E, v.rstart.as<uint32_t>(), v.n_ranges,
-                                v.wbound.as<int32_t>(), c->stream));
-  const Design &d = c->d;
+  HIPCHK(hipMemcpyAsync(v.rstart.p, rs.data(), sizeof(uint32_t) * rs.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(v.rchunk.p, rq.data(), sizeof(uint32_t) * rq.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(v.chunk_blk.p, cb.data(), sizeof(uint32_t) * cb.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(v.wdesc.ensure(sizeof(uint2) * (size_t)v.grid * NW));
+  HIPCHK(hipMemsetAsync(v.wdesc.p, 0, sizeof(uint2) * (size_t)v.grid * NW, s));
+
+  // ---- windows: starts, each block's first window, lengths
+  const int64_t E = v.E;
+  uint32_t W = 0;
+  if (E > 0) {
+    HIPCHK(ls.winc.ensure(sizeof(uint32_t) * E));
+    HIPCHK(ls.widx.ensure(sizeof(uint32_t) * E));  // head flags first, window indices later
+    HIPCHK(pa::launch_head_flags(E, ls.skey.as<uint64_t>(), ls.widx.as<uint32_t>(), s));
+    size_t tb = 0;
+    HIPCHK(pa::scan_inclusive_u32(ls.widx.as<uint32_t>(), ls.winc.as<uint32_t>(), E, nullptr, &tb, s));
+    HIPCHK(ls.tmp.ensure(tb));
+    HIPCHK(pa::scan_inclusive_u32(ls.widx.as<uint32_t>(), ls.winc.as<uint32_t>(), E, ls.tmp.p, &tb, s));
+    HIPCHK(hipMemcpyAsync(&W, ls.winc.as<uint32_t>() + (E - 1), sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+  }
+  v.n_windows = W;
+  HIPCHK(ls.ws.ensure(sizeof(uint32_t) * ((size_t)W + 1)));
+  HIPCHK(ls.bwin.ensure(sizeof(uint32_t) * ((size_t)nr + 1)));
+  HIPCHK(v.wlen.ensure(sizeof(uint32_t) * std::max<size_t>(W, 1)));
+  std::vector<uint32_t> wave_len((size_t)nr * NW, 0);
+  if (W > 0) {
+    HIPCHK(pa::launch_win_starts(E, ls.skey.as<uint64_t>(), ls.winc.as<uint32_t>(), ls.ws.as<uint32_t>(), s));
+    HIPCHK(pa::launch_block_windows(nr, E, v.rstart.as<uint32_t>(), ls.skey.as<uint64_t>(), ls.winc.as<uint32_t>(), W,
+                                    ls.bwin.as<uint32_t>(), s));
+    // ---- every block's windows, longest first (a stable sort keeps gate order among equals)
+    HIPCHK(ls.wkey0.ensure(sizeof(uint64_t) * W));
+    HIPCHK(ls.wkey1.ensure(sizeof(uint64_t) * W));
+    HIPCHK(ls.worder.ensure(sizeof(uint32_t) * W));
+    HIPCHK(pa::launch_win_keys(W, ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(), nr, ls.wkey0.as<uint64_t>(),
+                               ls.widx.as<uint32_t>(), v.wlen.as<uint32_t>(), s));
+    const int end_bit = 32 + (int)bits_for((uint64_t)std::max(nr - 1, 0));
+    size_t tb = 0;
+    HIPCHK(pa::sort_pairs_u64(ls.wkey0.as<uint64_t>(), ls.wkey1.as<uint64_t>(), ls.widx.as<uint32_t>(),
+                              ls.worder.as<uint32_t>(), W, end_bit, nullptr, &tb, s));
+    HIPCHK(ls.tmp.ensure(tb));
+    HIPCHK(pa::sort_pairs_u64(ls.wkey0.as<uint64_t>(), ls.wkey1.as<uint64_t>(), ls.widx.as<uint32_t>(),
+                              ls.worder.as<uint32_t>(), W, end_bit, ls.tmp.p, &tb, s));
+    // ---- lanes: every window's place in its lane's stream, every wave's longest stream
+    HIPCHK(ls.wlane.ensure(sizeof(uint2) * W));
+    HIPCHK(ls.lane_len.ensure(sizeof(uint32_t) * (size_t)nr * pa::lane_plan_lanes()));
+    HIPCHK(ls.wave_len.ensure(sizeof(uint32_t) * (size_t)nr * NW));
+    HIPCHK(pa::launch_lane_plan(nr, ls.bwin.as<uint32_t>(), ls.worder.as<uint32_t>(), v.wlen.as<uint32_t>(),
+                                ls.wlane.as<uint2>(), ls.lane_len.as<uint32_t>(), s));
+    HIPCHK(pa::launch_wave_len((int64_t)nr * NW, ls.lane_len.as<uint32_t>(), ls.wave_len.as<uint32_t>(), s));
+    HIPCHK(hipMemcpyAsync(wave_len.data(), ls.wave_len.p, sizeof(uint32_t) * wave_len.size(), hipMemcpyDeviceToHost,
+                          s));
+    HIPCHK(hipStreamSynchronize(s));
+  }
+  // ---- every wave's first slot: 64 lane streams of its longest stream's length each
+  std::vector<uint2> wd((size_t)v.grid * NW, make_uint2(0u, 0u));
+  uint64_t slots = 0;
+  for (size_t w = 0; w < wave_len.size(); ++w) {
+    wd[w] = make_uint2((uint32_t)slots, wave_len[w]);
+    slots += 64 * (uint64_t)wave_len[w];
+  }
+  if (slots >= (uint64_t(1) << 31))
+    return fail(PA_EINVAL, "pa_load_events: the lane streams need %llu slots (2^31 allowed)",
+                (unsigned long long)slots);
+  v.slots = (int64_t)slots;
+  HIPCHK(hipMemcpyAsync(v.wdesc.p, wd.data(), sizeof(uint2) * wd.size(), hipMemcpyHostToDevice, s));
+  // ---- the streams: keys and slews, the caller's index of every event; empty slots hold key 0
+  const int64_t Sa = (int64_t)slots + 2;  // two zeroed entries past the streams
+  HIPCHK(v.key.ensure(sizeof(uint64_t) * Sa));
+  HIPCHK(v.slew.ensure(sizeof(float) * Sa));
+  HIPCHK(v.orig.ensure(sizeof(uint32_t) * Sa));
+  HIPCHK(hipMemsetAsync(v.key.p, 0, sizeof(uint64_t) * Sa, s));
+  HIPCHK(hipMemsetAsync(v.slew.p, 0, sizeof(float) * Sa, s));
+  HIPCHK(hipMemsetAsync(v.orig.p, 0xFF, sizeof(uint32_t) * Sa, s));
+  if (W > 0)
+    HIPCHK(pa::launch_scatter(E, ls.skey.as<uint64_t>(), ls.sslew.as<float>(), ls.sorig.as<uint32_t>(),
+                              ls.winc.as<uint32_t>(), ls.ws.as<uint32_t>(), ls.wlane.as<uint2>(), v.wdesc.as<uint2>(),
+                              v.key.as<uint64_t>(), v.slew.as<float>(), v.orig.as<uint32_t>(), s));
   // the cells whose LUTs every block copies into its spare LDS
-  v.lut_lds = pa::pass_lut_lds_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak);
+  v.lut_lds = pa::pass_lut_lds_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax);
   if (c->tun.lut_lds_kib < 0) v.lut_lds = 0;
   else if (c->tun.lut_lds_kib > 0) v.lut_lds = std::min<int32_t>(v.lut_lds, c->tun.lut_lds_kib * 128);
-  if (v.lut_lds > 0 && v.n_ranges > 0) {
-    HIPCHK(v.lplan.ensure(sizeof(uint2) * (size_t)v.n_ranges * pa::pass_lut_plan_slots()));
-    HIPCHK(pa::launch_lut_plan(v.key.as<uint64_t>(), v.wbound.as<int32_t>(), v.n_ranges, d.gate_rec.as<uint4>(),
-                               d.cell_meta.as<uint2>(), v.gb, d.n_slew, d.n_cap, v.lut_lds, v.lplan.as<uint2>(),
-                               c->stream));
+  if (v.lut_lds > 0 && nr > 0 && W > 0) {
+    HIPCHK(v.lplan.ensure(sizeof(uint2) * (size_t)nr * pa::pass_lut_plan_slots()));
+    HIPCHK(pa::launch_lut_plan(ls.skey.as<uint64_t>(), ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(), nr,
+                               d.gate_rec.as<uint4>(), d.cell_meta.as<uint2>(), v.gb, d.n_slew, d.n_cap, v.lut_lds,
+                               v.lplan.as<uint2>(), s));
   } else {
     v.lut_lds = 0;
   }
   // leakage power at t = 0, from the initial pin values
-  DBuf &part = c->ls.part;
+  DBuf &part = ls.part;
   HIPCHK(part.ensure(sizeof(double) * pa::leak0_parts()));
   HIPCHK(v.l0.ensure(sizeof(double)));
   HIPCHK(pa::launch_leak0(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
-                          d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), part.as<double>(), v.l0.as<double>(),
-                          c->stream));
-  HIPCHK(hipStreamSynchronize(c->stream));
+                          d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), part.as<double>(), v.l0.as<double>(), s));
+  HIPCHK(hipStreamSynchronize(s));
   return PA_OK;
 }
 
@@ -543,14 +623,11 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   const uint32_t qbits = bits_for((uint64_t)std::max<int32_t>(v.Q - 1, 0));
   const int32_t Q = v.Q;
 
-  // two zeroed entries past the events (even count): the pass fetches event
-  // pairs without a bounds branch
-  const int64_t Ea = (E + 2) & ~int64_t(1);
-  HIPCHK(v.key.ensure(sizeof(uint64_t) * Ea));
-  HIPCHK(v.slew.ensure(sizeof(float) * Ea));
-  HIPCHK(hipMemsetAsync(v.key.as<uint64_t>() + E, 0, sizeof(uint64_t) * (Ea - E), s));
-  HIPCHK(hipMemsetAsync(v.slew.as<float>() + E, 0, sizeof(float) * (Ea - E), s));
-  HIPCHK(v.orig.ensure(sizeof(uint32_t) * E));
+  // the events in window order (scratch); build_ranges lays them out for the pass
+  DBuf &skey = c->ls.skey, &sslew = c->ls.sslew, &sorig = c->ls.sorig;
+  HIPCHK(skey.ensure(sizeof(uint64_t) * std::max<int64_t>(E, 1)));
+  HIPCHK(sslew.ensure(sizeof(float) * std::max<int64_t>(E, 1)));
+  HIPCHK(sorig.ensure(sizeof(uint32_t) * std::max<int64_t>(E, 1)));
   HIPCHK(v.pin_init.ensure(P));
   DBuf &chunk_sorted = c->ls.chunk_sorted, &cbase = c->ls.cbase;
   HIPCHK(chunk_sorted.ensure(sizeof(uint32_t) * E));
@@ -602,13 +679,9 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
     HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
     HIPCHK(pa::launch_layout(E, perm.as<uint32_t>(), evt_t, evt_slew, evt_val, ev_pin.as<uint32_t>(),
                              d.pin_gate.as<int32_t>(), d.pin_local.as<uint8_t>(), d.gate_k.as<int32_t>(),
-                             level.as<uint8_t>(), d.pin_base.as<int64_t>(), pin_ptr, pin_init, f, v.key.as<uint64_t>(),
-                             v.slew.as<float>(), v.orig.as<uint32_t>(), chunk_sorted.as<uint32_t>(),
-                             err.as<uint32_t>(), s));
-    HIPCHK(hipMemcpyAsync(&herr, err.p, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-    HIPCHK(hipStreamSynchronize(s));
-    if (herr & pa::ERR_GROUP)
-      return fail(PA_EDATA, "pa_load_events: a gate has more than %d events inside one clock cycle", pa::kGroupMax);
+                             level.as<uint8_t>(), d.pin_base.as<int64_t>(), pin_ptr, pin_init, f, skey.as<uint64_t>(),
+                             sslew.as<float>(), sorig.as<uint32_t>(), chunk_sorted.as<uint32_t>(), err.as<uint32_t>(),
+                             s));
   }
   HIPCHK(pa::launch_chunk_base(E, Q, chunk_sorted.as<uint32_t>(), cbase.as<uint32_t>(), s));
   if (P > 0) HIPCHK(hipMemcpyAsync(v.pin_init.p, pin_init, P, hipMemcpyDeviceToDevice, s));
@@ -637,7 +710,7 @@ static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_eve
   a.key = v.key.as<uint64_t>();
   a.slew = v.slew.as<float>();
   a.orig = v.orig.as<uint32_t>();
-  a.wbound = v.wbound.as<int32_t>();
+  a.wdesc = v.wdesc.as<uint2>();
   a.rchunk = v.rchunk.as<uint32_t>();
   a.n_ranges = v.n_ranges;
   a.E = v.E;
@@ -668,6 +741,7 @@ static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_eve
   a.n_cells = d.n_cells;
   a.n_thr = d.n_thr;
   a.n_leak = d.n_leak;
+  a.kmax = d.kmax;
   a.lut_plan = v.lut_lds > 0 ? v.lplan.as<uint2>() : nullptr;
   a.lut_lds = v.lut_lds;
   a.blk_wave = v.blk_wave.as<double>();
@@ -760,16 +834,9 @@ int pa_get_window_stats(pa_ctx *c, pa_window_stats *out) {
   hipStream_t s = c->stream;
   *out = pa_window_stats{};
   if (v.E == 0) return PA_OK;
-  DBuf sizes, n;
-  HIPCHK(sizes.alloc(sizeof(uint32_t) * v.E));
-  HIPCHK(n.alloc(sizeof(unsigned long long)));
-  HIPCHK(hipMemsetAsync(n.p, 0, sizeof(unsigned long long), s));
-  HIPCHK(pa::launch_window_sizes(v.E, v.key.as<uint64_t>(), sizes.as<uint32_t>(), n.as<unsigned long long>(), s));
-  unsigned long long hn = 0;
-  HIPCHK(hipMemcpyAsync(&hn, n.p, sizeof(hn), hipMemcpyDeviceToHost, s));
-  HIPCHK(hipStreamSynchronize(s));
+  const uint64_t hn = (uint64_t)v.n_windows;
   std::vector<uint32_t> h(hn);
-  if (hn) HIPCHK(hipMemcpyAsync(h.data(), sizes.p, sizeof(uint32_t) * hn, hipMemcpyDeviceToHost, s));
+  if (hn) HIPCHK(hipMemcpyAsync(h.data(), v.wlen.p, sizeof(uint32_t) * hn, hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
   std::sort(h.begin(), h.end());
   out->n_windows = (int64_t)hn;
@@ -798,13 +865,18 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
   info->grid_blocks = c->has_events ? c->ev.grid : 0;
   info->block_threads = pa::pass_block_threads();
   info->batch_events = pa::pass_wave_batch();
-  info->max_segment_events = pa::kGroupMax;
+  info->max_segment_events = 0;  // no limit
   const LoadScratch &ls = c->ls;
   info->device_bytes = c->d.bytes() + c->ev.bytes() + c->ev_spare.bytes() + (int64_t)c->text_dev.bytes +
                        (int64_t)(ls.err.bytes + ls.ev_pin.bytes + ls.chunk_sorted.bytes + ls.cbase.bytes +
                                  ls.level.bytes + ls.k0.bytes + ls.k1.bytes + ls.idx.bytes + ls.perm.bytes +
-                                 ls.chunk.bytes + ls.tmp.bytes + ls.part.bytes);
+                                 ls.chunk.bytes + ls.tmp.bytes + ls.part.bytes + ls.skey.bytes + ls.sslew.bytes +
+                                 ls.sorig.bytes + ls.winc.bytes + ls.ws.bytes + ls.bwin.bytes + ls.wkey0.bytes +
+                                 ls.wkey1.bytes + ls.widx.bytes + ls.worder.bytes + ls.wlane.bytes +
+                                 ls.lane_len.bytes + ls.wave_len.bytes);
   for (int k = 0; k < 4; ++k) info->kernel_ms[k] = c->kernel_ms[k];
+  info->n_windows = c->has_events ? c->ev.n_windows : 0;
+  info->n_slots = c->has_events ? c->ev.slots : 0;
   return PA_OK;
 }
 

@@ -13,10 +13,15 @@ namespace pa {
 // Event layout.  Time is cut into chunks of Cc clock cycles (a power of two);
 // inside a chunk every gate's cycles are cut into 2^s equal windows, s chosen
 // per gate from its event density (the paper's event-density-aware per-gate
-// cycle partitioning).  The events are ordered by
-//   (chunk, gate, cycle, time, pin code),
-// so a window is one contiguous run, and inside a window the events of one
-// clock cycle form one run in time order (events of one timestamp by pin).
+// cycle partitioning).  Inside a window the events are in
+//   (cycle, time, pin code)
+// order: the events of one clock cycle form one run in time order, events of
+// one timestamp ordered by pin code.  Every block of the pass owns a range of
+// whole windows of one chunk; its windows are dealt to its lanes, and each
+// lane walks its windows one after the other (each padded to an even length).
+// A wave's 64 lane streams are interleaved in pairs: event j of lane l sits at
+// slot base + (j / 2) * 128 + 2 l + j % 2.  Empty slots hold key 0, which no
+// event has (an event at the start of a window is a head, so bit 41 is set).
 //
 // Packed 64-bit key of an event (gb = bits of the largest gate id, cs = pb + tb):
 //   bits [42 + gb, 64)  the high bits of the cycle in the chunk (22 - gb of them)
@@ -36,7 +41,6 @@ constexpr uint32_t kKeyHeadShift = 41;
 constexpr uint32_t kKeyValShift = 40;
 constexpr uint32_t kKeyS0Shift = 32;
 constexpr uint64_t kKeyMaxGates = uint64_t(1) << 22;
-constexpr int kGroupMax = 127;  // most events of one gate inside one clock cycle
 
 __host__ __device__ inline uint32_t out_code(uint32_t pb) { return (1u << pb) - 1u; }
 
@@ -55,8 +59,8 @@ struct PassArgs {
   // events
   const uint64_t *key;
   const float *slew;
-  const uint32_t *orig;    // caller's CSR index of each laid-out event
-  const int32_t *wbound;   // [n_ranges][waves+1] the waves' ranges of every block, cut at window heads
+  const uint32_t *orig;    // caller's CSR index of each laid-out event (~0 in empty slots)
+  const uint2 *wdesc;      // [n_ranges][waves] every wave's (first slot, events per lane)
   const uint32_t *rchunk;  // [n_ranges] chunk of each range
   int32_t n_ranges;
   int64_t E;
@@ -83,6 +87,7 @@ struct PassArgs {
   const double *leak;
   int32_t n_slew, n_cap, n_cells, n_thr;
   int64_t n_leak;
+  int32_t kmax;               // most inputs of a cell (pin slots per lane: kmax + 1)
   // cells whose LUTs every block copies into LDS (see launch_lut_plan)
   const uint2 *lut_plan;      // [n_ranges][pass_lut_plan_slots()] (cell, LDS offset in doubles), cell ~0 = none
   int32_t lut_lds;            // LDS reserved for them, doubles (0: none)
@@ -119,29 +124,26 @@ struct FinalArgs {
 // Launchers (defined in pa_pass.hip).
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s);
 hipError_t launch_finalize(const FinalArgs &a, hipStream_t s);
-// the waves' ranges of every block: nominal cuts rstart[b] + (rstart[b+1] - rstart[b]) * w / waves
-// moved to the next window head; wb holds pass_wave_bounds_per_block() entries per block
-hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rstart, int32_t n_ranges, int32_t *wb,
-                              hipStream_t s);
-int pass_wave_bounds_per_block();
-// Per block, the cells whose LUTs it copies into the LDS left over by its bins
-// and cell tables (lut_lds doubles, from pass_lut_lds_doubles): 64 events
-// sampled evenly over the block's range give each cell present a weight, and
-// the heaviest cells that still fit are taken, at most
-// pass_lut_plan_slots() of them.  plan holds that many (cell, LDS offset)
-// pairs per block; unused slots have cell ~0.
-hipError_t launch_lut_plan(const uint64_t *key, const int32_t *wb, int32_t n_ranges, const uint4 *gate_rec,
-                           const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap, int32_t lut_lds, uint2 *plan,
-                           hipStream_t s);
+// Per block, the cells whose LUTs it copies into the LDS left over by its bins,
+// pin records and cell tables (lut_lds doubles, from pass_lut_lds_doubles): 64
+// windows sampled evenly over the block's window range [bwin[b], bwin[b+1])
+// (window w starts at sorted event ws[w], skey holds the sorted keys) give
+// each cell present a weight, and the heaviest cells that still fit are
+// taken, at most pass_lut_plan_slots() of them.  plan holds that many
+// (cell, LDS offset) pairs per block; unused slots have cell ~0.
+hipError_t launch_lut_plan(const uint64_t *skey, const uint32_t *ws, const uint32_t *bwin, int32_t n_ranges,
+                           const uint4 *gate_rec, const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap,
+                           int32_t lut_lds, uint2 *plan, hipStream_t s);
 int pass_lut_plan_slots();
-int32_t pass_lut_lds_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak);
+int32_t pass_lut_lds_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax);
 int pass_block_threads();
 int pass_blocks_per_cu();       // blocks of the pass resident on one compute unit
+int pass_waves_per_block();
 size_t pass_static_lds_bytes();  // static LDS of a block of the pass
 int pass_wave_batch();
 int pass_max_chunk_cycles();
 // dynamic LDS bytes of the pass, and whether the cell tables fit in it
-size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, bool cells);
-bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak);
+size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax, bool cells);
+bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax);
 
 }  // namespace pa

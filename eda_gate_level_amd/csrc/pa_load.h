@@ -18,7 +18,6 @@ enum : uint32_t {
   ERR_TIME_ORDER = 1u << 5,  // timestamps not strictly increasing on a pin
   ERR_VALUE = 1u << 6,       // values do not alternate starting from !init
   ERR_SLEW = 1u << 7,        // slew not finite and > 0
-  ERR_GROUP = 1u << 8,       // more than kGroupMax events of one gate in one clock cycle
 };
 
 // bit widths of the event layout
@@ -53,9 +52,6 @@ hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
 hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int32_t *gate_k, const int64_t *pin_ptr,
                               int64_t C, int32_t Cc, int32_t lc, double target, int32_t fixed_level,
                               uint8_t *level, hipStream_t s);
-// events of every window of the layout, appended in any order to sizes (*n counts them; zero it first)
-hipError_t launch_window_sizes(int64_t E, const uint64_t *key, uint32_t *sizes, unsigned long long *n,
-                               hipStream_t s);
 // chunk == nullptr: one 64-bit key (chunk, gate, lk); else key = (gate, lk) and chunk[e] apart
 hipError_t launch_sort_keys(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
                             const uint8_t *pin_local, const int32_t *gate_k, const LayoutFmt &f, uint64_t *key,
@@ -69,6 +65,25 @@ hipError_t launch_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, 
                          uint64_t *key_out, float *slew_out, uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err,
                          hipStream_t s);
 hipError_t launch_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted, uint32_t *cb, hipStream_t s);
+// lane streams of the pass (see pa_load.hip): head flags; window starts
+// (ws[W] = E); every block's first window; window sort keys, indices and
+// lengths; per (block, lane) the windows' places and the stream length; per
+// wave the longest stream; the scatter of the sorted events into the streams
+hipError_t launch_head_flags(int64_t E, const uint64_t *skey, uint32_t *flag, hipStream_t s);
+hipError_t launch_win_starts(int64_t E, const uint64_t *skey, const uint32_t *winc, uint32_t *ws, hipStream_t s);
+hipError_t launch_block_windows(int32_t nr, int64_t E, const uint32_t *rstart, const uint64_t *skey,
+                                const uint32_t *winc, uint32_t W, uint32_t *bwin, hipStream_t s);
+hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, uint64_t *wkey,
+                           uint32_t *widx, uint32_t *wlen, hipStream_t s);
+hipError_t launch_lane_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint32_t *wlen,
+                            uint2 *wlane, uint32_t *lane_len, hipStream_t s);
+hipError_t launch_wave_len(int64_t n_waves, const uint32_t *lane_len, uint32_t *wave_len, hipStream_t s);
+hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
+                          const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
+                          uint64_t *key, float *slew, uint32_t *orig, hipStream_t s);
+int lane_plan_lanes();  // lanes of a block of the pass
+hipError_t scan_inclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
+                              hipStream_t s);
 hipError_t sort_pairs_u64(const uint64_t *kin, uint64_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,
                           int end_bit, void *tmp, size_t *tmp_bytes, hipStream_t s);
 hipError_t sort_pairs_u32(const uint32_t *kin, uint32_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,

@@ -179,8 +179,7 @@ __global__ void k_chunk_of(int64_t E, const uint32_t *perm, const uint32_t *chun
     chunk_sorted[x] = chunk[perm[x]];
 }
 
-// Packed keys of the sorted events, window heads and their start states, and
-// the per-(gate, cycle) size limit.
+// Packed keys of the sorted events, window heads and their start states.
 __global__ void k_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, const float *evt_slew,
                          const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
                          const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
@@ -195,10 +194,6 @@ __global__ void k_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, 
     if (x > 0) {
       const EvPos pp = ev_pos(perm[x - 1], evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
       head = !(pp.q == p.q && pp.g == p.g && (pp.cyc >> (f.lc - sl)) == w);
-    }
-    if (x >= kGroupMax) {
-      const EvPos pf = ev_pos(perm[x - kGroupMax], evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
-      if (pf.q == p.q && pf.g == p.g && pf.cyc == p.cyc) atomicOr(err, ERR_GROUP);
     }
     uint64_t S0 = 0;
     if (head) {
@@ -232,6 +227,105 @@ __global__ void k_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted,
     const int64_t qa = x > 0 ? (int64_t)chunk_sorted[x - 1] : -1;
     const int64_t qb = x < E ? (int64_t)chunk_sorted[x] : (int64_t)Q;
     for (int64_t q = qa + 1; q <= qb; ++q) cb[q] = (uint32_t)x;
+  }
+}
+
+
+// ------------------------------------------------------ lane streams of the pass
+//
+// The sorted events (window order) are dealt to the pass's lanes: every block
+// owns a range of whole windows of one chunk; its windows, longest first, go
+// to its 1024 lanes in snake order (ranks 0..1023 to lanes 0..1023, the next
+// 1024 to lanes 1023..0, and so on), so that the lanes' event counts come out
+// nearly equal.  A lane's windows follow one another in its stream, each
+// padded to an even length, and a wave's 64 streams are interleaved in pairs.
+
+constexpr int kLaneNT = 1024;  // lanes of a block of the pass
+constexpr int kLaneNW = kLaneNT / 64;
+
+__global__ void k_head_flags(int64_t E, const uint64_t *skey, uint32_t *flag) {
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x)
+    flag[x] = (uint32_t)(skey[x] >> kKeyHeadShift) & 1u;
+}
+
+// ws[w] = first sorted event of window w (winc = inclusive count of heads); ws[W] = E
+__global__ void k_win_starts(int64_t E, const uint64_t *skey, const uint32_t *winc, uint32_t *ws) {
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
+    if ((skey[x] >> kKeyHeadShift) & 1ull) ws[winc[x] - 1] = (uint32_t)x;
+    if (x == E - 1) ws[winc[x]] = (uint32_t)E;
+  }
+}
+
+// first window of every block: the first window starting at or after the
+// block's nominal first event (E: none)
+__global__ void k_block_windows(int32_t nr, int64_t E, const uint32_t *rstart, const uint64_t *skey,
+                                const uint32_t *winc, uint32_t W, uint32_t *bwin) {
+  for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b <= nr; b += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t x = rstart[b];
+    bwin[b] = x < E ? winc[x] - (uint32_t)((skey[x] >> kKeyHeadShift) & 1ull) : W;
+  }
+}
+
+// per window: (block << 32 | ~(even length)), so a stable sort orders every
+// block's windows longest first; wlen = the window's event count
+__global__ void k_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, uint64_t *wkey,
+                           uint32_t *widx, uint32_t *wlen) {
+  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < W; w += (int64_t)gridDim.x * blockDim.x) {
+    int lo = 0, hi = nr;  // last block with bwin[b] <= w
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (bwin[mid] <= (uint32_t)w) lo = mid; else hi = mid;
+    }
+    const uint32_t n = ws[w + 1] - ws[w];
+    wlen[w] = n;
+    wkey[w] = ((uint64_t)lo << 32) | (uint64_t)(0xFFFFFFFFu - ((n + 1u) & ~1u));
+    widx[w] = (uint32_t)w;
+  }
+}
+
+// one thread per (block, lane): its windows in snake order, their offsets in
+// the lane's stream (wlane[w] = (global wave << 6 | lane, first event)), and
+// the stream's length
+__global__ void k_lane_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint32_t *wlen,
+                            uint2 *wlane, uint32_t *lane_len) {
+  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t >= (int64_t)nr * kLaneNT) return;
+  const int b = (int)(t / kLaneNT), u = (int)(t % kLaneNT);
+  const uint32_t w0 = bwin[b], nb = bwin[b + 1] - w0;
+  const uint32_t lane_id = ((uint32_t)(b * kLaneNW + u / 64) << 6) | (uint32_t)(u % 64);
+  uint32_t off = 0;
+  for (uint32_t round = 0;; ++round) {
+    const uint32_t r = round * kLaneNT + ((round & 1u) ? (uint32_t)(kLaneNT - 1 - u) : (uint32_t)u);
+    if (r >= nb) break;
+    const uint32_t w = worder[w0 + r];
+    wlane[w] = make_uint2(lane_id, off);
+    off += (wlen[w] + 1u) & ~1u;
+  }
+  lane_len[t] = off;
+}
+
+// events per lane of every wave: the longest of its 64 lane streams
+__global__ void k_wave_len(int64_t n_waves, const uint32_t *lane_len, uint32_t *wave_len) {
+  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < n_waves;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    uint32_t m = 0;
+    for (int l = 0; l < 64; ++l) m = max(m, lane_len[w * 64 + l]);
+    wave_len[w] = m;
+  }
+}
+
+// every sorted event to its slot in its lane's stream
+__global__ void k_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
+                          const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
+                          uint64_t *key, float *slew, uint32_t *orig) {
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t w = winc[x] - 1u;
+    const uint2 wl = wlane[w];
+    const uint32_t j = wl.y + ((uint32_t)x - ws[w]);
+    const uint32_t y = wdesc[wl.x >> 6].x + (j >> 1) * 128u + 2u * (wl.x & 63u) + (j & 1u);
+    key[y] = skey[x];
+    slew[y] = sslew[x];
+    orig[y] = sorig[x];
   }
 }
 
@@ -347,25 +441,6 @@ hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int32_t 
   return hipGetLastError();
 }
 
-// Events per window: every window head finds the next head (or the end) and
-// appends the distance.
-__global__ void k_window_sizes(int64_t E, const uint64_t *key, uint32_t *sizes, unsigned long long *n) {
-  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
-    if (!((key[x] >> kKeyHeadShift) & 1ull)) continue;
-    int64_t y = x + 1;
-    while (y < E && !((key[y] >> kKeyHeadShift) & 1ull)) ++y;
-    const unsigned long long i = atomicAdd(n, 1ull);
-    sizes[i] = (uint32_t)(y - x);
-  }
-}
-
-hipError_t launch_window_sizes(int64_t E, const uint64_t *key, uint32_t *sizes, unsigned long long *n,
-                               hipStream_t s) {
-  if (E <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_window_sizes, dim3(grid_for(E)), dim3(kLT), 0, s, E, key, sizes, n);
-  return hipGetLastError();
-}
-
 hipError_t launch_sort_keys(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
                             const uint8_t *pin_local, const int32_t *gate_k, const LayoutFmt &f, uint64_t *key,
                             uint32_t *chunk, uint32_t *idx, hipStream_t s) {
@@ -395,6 +470,52 @@ hipError_t launch_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, 
 hipError_t launch_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted, uint32_t *cb, hipStream_t s) {
   hipLaunchKernelGGL(k_chunk_base, dim3(grid_for(E + 1)), dim3(kLT), 0, s, E, Q, chunk_sorted, cb);
   return hipGetLastError();
+}
+
+hipError_t launch_head_flags(int64_t E, const uint64_t *skey, uint32_t *flag, hipStream_t s) {
+  hipLaunchKernelGGL(k_head_flags, dim3(grid_for(E)), dim3(kLT), 0, s, E, skey, flag);
+  return hipGetLastError();
+}
+hipError_t launch_win_starts(int64_t E, const uint64_t *skey, const uint32_t *winc, uint32_t *ws, hipStream_t s) {
+  hipLaunchKernelGGL(k_win_starts, dim3(grid_for(E)), dim3(kLT), 0, s, E, skey, winc, ws);
+  return hipGetLastError();
+}
+hipError_t launch_block_windows(int32_t nr, int64_t E, const uint32_t *rstart, const uint64_t *skey,
+                                const uint32_t *winc, uint32_t W, uint32_t *bwin, hipStream_t s) {
+  hipLaunchKernelGGL(k_block_windows, dim3(grid_for(nr + 1)), dim3(kLT), 0, s, nr, E, rstart, skey, winc, W, bwin);
+  return hipGetLastError();
+}
+hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, uint64_t *wkey,
+                           uint32_t *widx, uint32_t *wlen, hipStream_t s) {
+  if (W == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_win_keys, dim3(grid_for(W)), dim3(kLT), 0, s, W, ws, bwin, nr, wkey, widx, wlen);
+  return hipGetLastError();
+}
+hipError_t launch_lane_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint32_t *wlen,
+                            uint2 *wlane, uint32_t *lane_len, hipStream_t s) {
+  const int64_t n = (int64_t)nr * kLaneNT;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lane_plan, dim3((unsigned)((n + kLT - 1) / kLT)), dim3(kLT), 0, s, nr, bwin, worder, wlen,
+                     wlane, lane_len);
+  return hipGetLastError();
+}
+hipError_t launch_wave_len(int64_t n_waves, const uint32_t *lane_len, uint32_t *wave_len, hipStream_t s) {
+  if (n_waves == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_wave_len, dim3(grid_for(n_waves)), dim3(kLT), 0, s, n_waves, lane_len, wave_len);
+  return hipGetLastError();
+}
+hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
+                          const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
+                          uint64_t *key, float *slew, uint32_t *orig, hipStream_t s) {
+  hipLaunchKernelGGL(k_scatter, dim3(grid_for(E)), dim3(kLT), 0, s, E, skey, sslew, sorig, winc, ws, wlane, wdesc,
+                     key, slew, orig);
+  return hipGetLastError();
+}
+int lane_plan_lanes() { return kLaneNT; }
+
+hipError_t scan_inclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
+                              hipStream_t s) {
+  return hipcub::DeviceScan::InclusiveSum(tmp, *tmp_bytes, in, out, (int)n, s);
 }
 
 hipError_t sort_pairs_u64(const uint64_t *kin, uint64_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,

@@ -10,37 +10,36 @@
 // cycle bin.  Per gate (Sec. 2.4.2, Fig. 3, Eq. 4): state-dependent leakage
 // over every inter-event interval, spread over the cycle bins it overlaps.
 // The paper fuses both parts into one thread per (gate, cycle window)
-// (Fig. 7).  This pass keeps the fusion and maps it onto 64-lane waves:
-//   * the events are laid out by (time chunk, gate, clock cycle, time, pin);
-//     every gate's part of a chunk is cut into density-aware windows whose
-//     first event carries the gate's input state at the window start;
-//   * a block owns a range of whole windows inside one chunk and each of its
-//     waves streams a share of them, 128 consecutive events per batch (two
-//     per lane, 16-byte loads), the next batch prefetched into registers;
-//   * the state before every event is a segmented XOR scan of the input
-//     events' pin bits across the wave (DPP row shifts and broadcasts), the
-//     segments being the windows: the k-way merge of Sec. 2.4.2, since the
-//     layout is already in time order.  Events of one timestamp are
-//     adjacent; each sees the state before the first of them, and the lowest
-//     input pin among them charges the leakage change of the whole set;
-//   * a glitch is an event whose pin has an earlier event in the same
-//     (gate, cycle) run: a segmented OR scan of pin bits over the runs
-//     (Fig. 7); its pulse width and the previous slew come from the pin's
-//     previous event in the run: the event just before, or the one a max
-//     scan of positions per pin finds (Eq. 2);
-//   * one lane per event: state-selected LUT, bilinear on slew and load
-//     (Sec. 2.4.1, Fig. 2), switching energy (Eq. 1), energies added to
-//     per-cycle bins in LDS.  The LUTs of the cells most of a block's events
-//     use are copied into the block's spare LDS at its start (chosen at load
-//     from a sample of its events); the other cells are read through the
-//     caches;
-//   * leakage is charged as power changes: at every distinct input timestamp
-//     the lowest switching input pin adds dP = leak[S+] - leak[S-]; its
-//     partial bin gets dP * (bin end - t) and all later bins get dP * their
-//     length through an in-LDS prefix sum per chunk and a per-chunk carry;
-//     the leakage at t = 0 is the sum over gates of leak[S0].  This is the
-//     paper's per-interval, per-overlapped-bin split (Sec. 2.4.2, Eq. 4)
-//     summed in another order;
+// (Fig. 7).  This pass keeps that mapping and lays the data out for 64-lane
+// waves:
+//   * every gate's part of a time chunk is cut into density-aware windows
+//     whose first event (the head) carries the gate's input state at the
+//     window start; a lane walks whole windows, one event after the other,
+//     in time order: the k-way merge of Sec. 2.4.2 is the layout's order;
+//   * at load, a block's windows are sorted by length and dealt to its 1024
+//     lanes in snake order, so the lanes' event counts come out nearly equal;
+//     a wave's 64 lane streams are interleaved two events at a time, so that
+//     step i of the wave reads events 2i and 2i+1 of every lane with one
+//     coalesced 16-byte load per lane (the next step's pair prefetched);
+//   * per lane, in registers: the input state, the state at the start of the
+//     current timestamp (all events of one timestamp see it), the pins that
+//     already switched in the current cycle (the per-pin counter of Fig. 7:
+//     an event whose pin is in that set is a glitch), and the gate's leakage
+//     power; the gate record, cell entry, cap position and slew thresholds
+//     are read once per window, at its head.  Every pin's last time and slew
+//     in the current cycle sit in LDS for the pulse width of Eq. 2;
+//   * per event: state-selected LUT, bilinear on slew and load (Sec. 2.4.1,
+//     Fig. 2), switching energy (Eq. 1), energies added to per-cycle bins in
+//     LDS.  The LUTs of the cells most of a block's events use are copied into
+//     the block's spare LDS at its start (chosen at load from a sample of its
+//     windows); the other cells are read through the caches;
+//   * leakage is charged as power changes: every input event adds
+//     dP = leak[S after] - leak[S before] (the events of one timestamp add up
+//     to the change of the whole set); its partial bin gets dP * (bin end - t)
+//     and all later bins get dP * their length through an in-LDS prefix sum
+//     per chunk and a per-chunk carry; the leakage at t = 0 is the sum over
+//     gates of leak[S0].  This is the paper's per-interval, per-overlapped-bin
+//     split (Sec. 2.4.2, Eq. 4) summed in another order;
 //   * every block writes its bins and totals to its own slots; the finalize
 //     kernel adds them up in a fixed order (no global atomics).
 #include <hip/hip_runtime.h>
@@ -58,101 +57,21 @@ namespace {
 #define PA_FUSED_ATTR
 #endif
 constexpr int kNT = PA_NT;           // threads per block
-constexpr int kNW = kNT / 64;        // waves per block, each working on its own batches
+constexpr int kNW = kNT / 64;        // waves per block, each walking its own 64 lane streams
 constexpr int kBPC = 1024 / kNT;     // blocks per compute unit (16 waves each)
-constexpr int kB = 128;              // events per wave batch, two consecutive ones per lane
+constexpr int kB = 128;              // events per wave step, two consecutive ones per lane
 constexpr int kCCMAX = 2048;         // max cycles per chunk (LDS bins)
 constexpr int kPlan = 8;             // cells per block whose LUTs may sit in LDS
 constexpr uint32_t kLutLds = 0x80000000u;  // LUT base flag in a block's cell table: offset into its LDS copy
 typedef __attribute__((address_space(3))) double lds_f64;
 constexpr size_t kLdsMax = 160 * 1024 / kBPC;  // LDS of a block (gfx950: 160 KB per compute unit)
-static_assert(kB - 1 >= kGroupMax, "a (gate, cycle) run fits in one batch after an odd start");
 
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t key_head(uint64_t k) { return uint32_t(k >> kKeyHeadShift) & 1u; }
-
-// first window head at or after position x (E if none); one whole wave
-__device__ int find_head(const uint64_t *key, int64_t E, int64_t x) {
-  const int lane = threadIdx.x & 63;
-  for (;;) {
-    if (x >= E) return (int)E;
-    const int64_t y = x + lane;
-    const bool h = (y >= E) || key_head(key[y]);
-    const unsigned long long m = __ballot(h);
-    if (m) return (int)(x + __ffsll((long long)m) - 1);
-    x += 64;
-  }
-}
-
 __device__ __forceinline__ double wave_sum(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
-}
-
-// LDS ordering between the lanes of one wave (no block barrier)
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// value of another lane by a DPP move; lanes without a source read 0 (the
-// bound control writes 0 there, so no zeroed old value is needed)
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ uint32_t dpp_mov(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
-}
-
-// another lane's value by a DPP move inside a scan step: lanes without a
-// source (outside the row, or rows the broadcast does not write) read 0
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ uint32_t dpp_src(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, true);
-}
-
-// inclusive XOR and max scans over the 64 lanes (row shifts 1, 2, 4, 8, then
-// row broadcasts 15 and 31); 0 is the identity of both
-__device__ __forceinline__ uint32_t xor_scan(uint32_t w) {
-  w ^= dpp_src<0x111>(w);
-  w ^= dpp_src<0x112>(w);
-  w ^= dpp_src<0x114>(w);
-  w ^= dpp_src<0x118>(w);
-  w ^= dpp_src<0x142, 0xA>(w);
-  w ^= dpp_src<0x143, 0xC>(w);
-  return w;
-}
-
-__device__ __forceinline__ uint32_t max_scan(uint32_t w) {
-  w = max(w, dpp_src<0x111>(w));
-  w = max(w, dpp_src<0x112>(w));
-  w = max(w, dpp_src<0x114>(w));
-  w = max(w, dpp_src<0x118>(w));
-  w = max(w, dpp_src<0x142, 0xA>(w));
-  w = max(w, dpp_src<0x143, 0xC>(w));
-  return w;
-}
-
-// Glitch-scan element: low 16 bits = pins with an event so far in the run,
-// kRun = a (gate, cycle) run starts here.  a then b: b restarts or the sets join.
-constexpr uint32_t kRun = 0x10000u;
-__device__ __forceinline__ uint32_t or_combine(uint32_t a, uint32_t b) { return (b & kRun) ? b : (a | b); }
-
-template <int CTRL, int ROWS = 0xF>
-__device__ __forceinline__ uint32_t or_step(uint32_t w) {
-  const uint32_t t = dpp_mov<CTRL, ROWS>(w) | w;
-  return (w & kRun) ? w : t;
-}
-
-__device__ __forceinline__ uint32_t or_scan(uint32_t w) {
-  w = or_step<0x111>(w);
-  w = or_step<0x112>(w);
-  w = or_step<0x114>(w);
-  w = or_step<0x118>(w);
-  w = or_step<0x142, 0xA>(w);
-  w = or_step<0x143, 0xC>(w);
-  return w;
 }
 
 struct CellLds {
@@ -160,6 +79,7 @@ struct CellLds {
   float *thr;
   double *bw, *bb;
   unsigned long long *bc;
+  uint2 *prec;  // [waves][pin slots][64]: a pin's last (time in cycle, slew) per lane
   double *leak;
   uint2 *meta;
   double *lut;  // the block's LUT copies, 16-byte aligned after the cell meta
@@ -170,10 +90,13 @@ __host__ __device__ inline size_t cell_bytes(int n_cells, int n_slew, int n_cap,
          8 * (size_t)n_cells;
 }
 
+// pin slots of a lane: the input pins 0..kmax-1 and the output pin (slot kmax)
+__host__ __device__ inline size_t prec_bytes(int kmax) { return (size_t)kNW * (kmax + 1) * 64 * 8; }
+
 // dynamic LDS: [slew (axis, 1/width) pairs][cap (axis, 1/width) pairs][slew thresholds][bins: wave,
-// leakage change, counts][leakage][cell meta][LUT copies]
+// leakage change, counts][pin records][leakage][cell meta][LUT copies]
 __device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, int n_slew, int n_cap, int n_thr,
-                                         int64_t n_leak, bool cells) {
+                                         int64_t n_leak, int kmax, bool cells) {
   CellLds L;
   L.axw = reinterpret_cast<double2 *>(s);
   L.caxw = L.axw + (cells ? n_cells * (n_slew - 1) : 0);
@@ -181,7 +104,8 @@ __device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, 
   L.bw = reinterpret_cast<double *>(L.thr + (cells ? n_cells * n_thr : 0));
   L.bb = L.bw + Cc;
   L.bc = reinterpret_cast<unsigned long long *>(L.bb + Cc);
-  L.leak = reinterpret_cast<double *>(L.bc + Cc);
+  L.prec = reinterpret_cast<uint2 *>(L.bc + Cc);
+  L.leak = reinterpret_cast<double *>(L.prec + (size_t)kNW * (kmax + 1) * 64);
   L.meta = reinterpret_cast<uint2 *>(L.leak + (cells ? n_leak : 0));
   const size_t end = (size_t)(reinterpret_cast<unsigned char *>(L.meta + (cells ? n_cells : 0)) - s);
   L.lut = reinterpret_cast<double *>(s + ((end + 15) & ~size_t(15)));
@@ -192,16 +116,12 @@ __device__ __forceinline__ CellLds carve(unsigned char *s, int Cc, int n_cells, 
 template <bool CELL_LDS, bool DIAG, int NIN>
 __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   extern __shared__ __align__(16) unsigned char s_dyn[];
-  __shared__ uint32_t st_lk[kNW][kB];  // batch events (lk) for the in-cycle walk
-  __shared__ uint8_t st_gh[kNW][kB];   // tie flags of the batch events (same run, same time as the one before)
-  __shared__ float st_sl[kNW][kB];     // slews of the batch events
   __shared__ double s_red[kNW][8];
   __shared__ double s_scan[kNW];
-
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int b = blockIdx.x, nb = gridDim.x;
+  const int b = blockIdx.x;
   const int Cc = a.Cc, ns = a.n_slew, nc = a.n_cap, nthr = a.n_thr;
-  const CellLds L = carve(s_dyn, Cc, a.n_cells, ns, nc, nthr, a.n_leak, CELL_LDS);
+  const CellLds L = carve(s_dyn, Cc, a.n_cells, ns, nc, nthr, a.n_leak, a.kmax, CELL_LDS);
   const bool has_range = b < a.n_ranges;
 
   auto meta_of = [&](uint32_t c) -> uint2 {
@@ -222,26 +142,25 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
     if constexpr (CELL_LDS) return L.leak[j]; else return a.leak[j];
   };
 
-  // ---- the block's chunk and this wave's range (cut at window heads at load);
-  // the first batch is fetched before the tables are staged
-  int q = 0, pos = 0, wend = 0;
+  // ---- this wave's 64 lane streams: slots [base, base + 64 len), lane l's
+  // event j at base + (j / 2) * 128 + 2 l + j % 2; the first pair is fetched
+  // before the tables are staged
+  int base = 0, len = 0, q = 0;
   if (has_range) {
     q = (int)a.rchunk[b];
-    // wave-uniform, so the batch loop is steered by scalar branches
-    pos = __builtin_amdgcn_readfirstlane(a.wbound[b * (kNW + 1) + wid]);
-    wend = __builtin_amdgcn_readfirstlane(a.wbound[b * (kNW + 1) + wid + 1]);
+    const uint2 d = a.wdesc[b * kNW + wid];
+    // wave-uniform, so the step loop is steered by scalar branches
+    base = __builtin_amdgcn_readfirstlane((int)d.x);
+    len = __builtin_amdgcn_readfirstlane((int)d.y);
   }
   u64x2 kp = {0ull, 0ull};
   f32x2 sp = {0.f, 0.f};
-  // pairs past the wave's range belong to other waves (or to the two zeroed
-  // entries after the last event); the batch ignores them
-  const int xmax = (int)(((a.E + 2) & ~int64_t(1)) - 2);
-  auto load_batch = [&](int p) {
-    const int x0 = min((p & ~1) + 2 * lane, xmax);
-    kp = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x0));
-    sp = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x0));
+  auto load_pair = [&](int j) {
+    const int x = base + j * 64 + 2 * lane;
+    kp = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x));
+    sp = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x));
   };
-  if (pos < wend) load_batch(pos);
+  if (len > 0) load_pair(0);
   for (int c = tid; c < Cc; c += kNT) {
     L.bw[c] = 0.0;
     L.bb[c] = 0.0;
@@ -299,246 +218,121 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   const uint32_t gmask = (1u << a.gb) - 1u, ysh = 10u + a.gb;  // gate id and high cycle bits in the key's high word
   const uint32_t tmask = (1u << tb) - 1u;
   const uint32_t outc = (1u << pb) - 1u;
+  const uint32_t kmax = (uint32_t)a.kmax;
 
-  if (has_range) {
-    uint32_t carry = 0;
-    uint32_t *slk = st_lk[wid];
-    uint8_t *sgh = st_gh[wid];
+  if (len > 0) {
+    // the lane's window: its gate and cell entry, the load's position on
+    // the cell's cap segment, the switching energy, the slew thresholds
+    uint32_t gate = 0, cell = 0, kk = 0, lb = 0, lutb = 0, cseg = 0;
+    double fc = 0.0, esw = 0.0;
+    constexpr int NTH = NIN > 0 ? NIN : 1;
+    float th[NTH];
+#pragma unroll
+    for (int j = 0; j < NTH; ++j) th[j] = __builtin_inff();
+    // the lane's running state: input pins after the last event, at the start
+    // of the current timestamp, pins switched in the current cycle, the time
+    // of the last event, the leakage power of the current state
+    uint32_t S = 0, St = 0, seen = 0, pcyc = ~0u, ptic = 0;
+    double lkS = 0.0;
+    uint2 *prec = L.prec + (size_t)wid * (kmax + 1) * 64 + lane;
 
-    while (pos < wend) {
-      const int base = pos & ~1;
-      const int first = pos - base;  // 0, or 1 when the batch starts on an odd event
-      const int navail = min(kB, wend - base);
+#pragma unroll 1
+    for (int j = 0; j < len; j += 2) {
       const uint64_t K0 = kp.x, K1 = kp.y;
       const float s0 = sp.x, s1 = sp.y;
-      const int i0 = 2 * lane, i1 = i0 + 1;
-      const bool v0 = i0 >= first && i0 < navail;
-      const bool v1 = i1 < navail;
-      const uint32_t lk0 = (uint32_t)K0, lk1 = (uint32_t)K1;
-      const uint32_t h0 = (uint32_t)(K0 >> 32), h1 = (uint32_t)(K1 >> 32);
-      const bool hd0 = (h0 >> 9) & 1u, hd1 = (h1 >> 9) & 1u;
-      // cycles in the chunk
-      const uint32_t y0 = (uint32_t)((((uint64_t)h0 >> ysh) << 32 | lk0) >> cs);
-      const uint32_t y1 = (uint32_t)((((uint64_t)h1 >> ysh) << 32 | lk1) >> cs);
-      // the event before slot i0 is the previous lane's second one
-      const uint32_t lkp0 = dpp_mov<0x138>(lk1);
-      const uint32_t yp0 = dpp_mov<0x138>(y1);
-      // run starts: a window head, the batch start, or a new clock cycle
-      const bool gh0 = hd0 || i0 == first || y0 != yp0;
-      const bool gh1 = hd1 || i1 == first || y1 != y0;
-      // process up to the last run start, so that no (gate, cycle) run is split
-      const unsigned long long M0 = __ballot(v0 && gh0), M1 = __ballot(v1 && gh1);
-      int last = -1;
-      if (M0) last = 2 * (63 - __clzll((long long)M0));
-      if (M1) last = max(last, 2 * (63 - __clzll((long long)M1)) + 1);
-      const int end = (base + navail < wend && last > first) ? last : navail;
-      const bool a0 = v0 && i0 < end, a1 = v1 && i1 < end;
-      const int npos = base + end;
-      if (npos < wend) load_batch(npos);
-
-      const uint32_t c0 = lk0 & outc, c1 = lk1 & outc;                    // pin codes
-      const uint32_t t0 = (lk0 >> pb) & tmask, t1 = (lk1 >> pb) & tmask;  // time inside the cycle
-      const bool in0 = c0 != outc, in1 = c1 != outc;
-      // the gates' records; slot 1 reuses slot 0's when both events are of one gate
-      const uint32_t g0 = (h0 >> 10) & gmask, g1 = (h1 >> 10) & gmask;
-      const bool same_gate = a0 && g1 == g0;
-      uint4 rec0 = make_uint4(0u, 0u, 0u, 0u), rec1 = make_uint4(0u, 0u, 0u, 0u);
-      if (a0) rec0 = a.gate_rec[g0];
-      if (a1 && !same_gate) rec1 = a.gate_rec[g1];
-
-      // ---- state before every event (Sec. 2.4.2): the toggles of the input
-      // events before it in the batch (an XOR scan, Q) on top of the state at
-      // the last window head at or before it.  A head h carries
-      // (h + 1) << 8 | (S0 ^ Q[h]), so a max scan finds the last one, and the
-      // state before event i is that low byte ^ Q[i]; the state carried
-      // from the previous batch acts as a head at position 0.
-      const uint32_t tg0 = (a0 && in0) ? (1u << c0) : 0u;
-      const uint32_t tg1 = (a1 && in1) ? (1u << c1) : 0u;
-      const uint32_t Q0 = xor_scan(tg0 ^ tg1) ^ tg0 ^ tg1;  // toggles before slot i0
-      const uint32_t Q1 = Q0 ^ tg0;
-      const uint32_t V0 = (a0 && hd0) ? (((uint32_t)(i0 + 1) << 8) | ((h0 ^ Q0) & 0xFFu)) : 0u;
-      const uint32_t V1 = (a1 && hd1) ? (((uint32_t)(i1 + 1) << 8) | ((h1 ^ Q1) & 0xFFu)) : 0u;
-      uint32_t vm = max(V0, V1);
-      if (lane == 0) vm = max(vm, carry);
-      const uint32_t M = max_scan(vm);
-      uint32_t Mx = dpp_mov<0x138>(M);
-      if (lane == 0) Mx = carry;
-      const uint32_t B0 = max(Mx, V0), B1 = max(B0, V1);
-      uint32_t S0s = (B0 ^ Q0) & 0xFFu;
-      uint32_t S1s = (B1 ^ Q1) & 0xFFu;
-      // state after event end - 1 (a lane's slot 1 past the end adds nothing)
-      carry = (uint32_t)__builtin_amdgcn_readlane((int)((B1 ^ Q1 ^ tg1) & 0xFFu), (end - 1) >> 1);
-
-      // ---- glitches: the pin already has an event in this (gate, cycle) run
-      // (Sec. 2.4.1, Fig. 7); runs never cross a batch, so no carry.  When no
-      // run of the batch holds three or more events, the only earlier event
-      // of a run is the one just before; otherwise an OR scan of pin bits
-      // over the runs gives every event the pins seen before it.
-      const uint32_t tp0 = (lkp0 >> pb) & tmask;  // time of the event before slot i0
-      const uint32_t ghp = dpp_mov<0x138>((uint32_t)gh1);  // the event before slot i0 starts a run
-      const float sp0 = __uint_as_float(dpp_mov<0x138>(__float_as_uint(s1)));  // its slew
-      const bool slowgl = (__ballot(a0 && !gh0 && !ghp) | __ballot(a1 && !gh1 && !gh0)) != 0ull;
-      bool gl0 = false, gl1 = false;
-      uint32_t tq0 = tp0, tq1 = t0;  // time of the pin's previous event (glitches)
-      float sq0 = sp0, sq1 = s0;     // its slew
-      if (!slowgl) {
-        gl0 = a0 && !gh0 && (c0 == (lkp0 & outc));
-        gl1 = a1 && !gh1 && (c1 == c0);
-      } else {
-        const uint32_t u0 = a0 ? (1u << c0) : 0u, u1 = a1 ? (1u << c1) : 0u;
-        const uint32_t Io = or_scan(or_combine(gh0 ? (kRun | u0) : u0, gh1 ? (kRun | u1) : u1));
-        // (the lane move runs in every lane: a lane whose value is not taken
-        // must still provide its own to the next one)
-        const uint32_t Xo = dpp_mov<0x138>(Io) & 0xFFFFu;  // lane 0 reads 0: a batch starts a run
-        const uint32_t seen0 = gh0 ? 0u : Xo;
-        const uint32_t seen1 = gh1 ? 0u : (seen0 | u0);
-        gl0 = a0 && ((seen0 >> c0) & 1u);
-        gl1 = a1 && ((seen1 >> c1) & 1u);
-      }
-
-      // ---- events of one gate at one timestamp (ties), adjacent in the
-      // layout: each sees the state before the first of them (the scan
-      // counted the earlier ones, which are inputs: the output code is the
-      // highest), and the first, the lowest input pin, charges the leakage
-      // change of all their input pins together
-      const bool tie0 = a0 && !gh0 && t0 == tp0;
-      const bool tie1 = a1 && !gh1 && t1 == t0;
-      uint32_t mk0 = 1u << c0, mk1 = 1u << c1;  // input pins switching at the event's timestamp
-      const bool ow0 = !tie0, ow1 = !tie1;      // first of its timestamp
-      if ((__ballot(tie0 || tie1) | (slowgl ? __ballot(gl0 || gl1) : 0ull)) != 0ull) {
-        slk[i0] = lk0;
-        slk[i1] = lk1;
-        sgh[i0] = (uint8_t)tie0;
-        sgh[i1] = (uint8_t)tie1;
-        st_sl[wid][i0] = s0;
-        st_sl[wid][i1] = s1;
-        wave_sync();
-        // glitches in runs of three or more events: the pin's previous event
-        // in the run (it exists: the glitch's pin has an earlier event in the
-        // run).  In pulse trains it is mostly the event just before; for the
-        // rest it is the pin's last event before this one, found for every
-        // pin left by a max scan of positions.
-        if (slowgl) {
-          bool need0 = gl0, need1 = gl1;
-          int pp0 = 0, pp1 = 0;
-          if (need0 && (lkp0 & outc) == c0) {  // (the event before a glitch is in its run)
-            pp0 = i0 - 1;
-            need0 = false;
-          }
-          if (need1 && c0 == c1) {
-            pp1 = i0;
-            need1 = false;
-          }
-          if ((__ballot(need0) | __ballot(need1)) != 0ull) {
-            for (uint32_t c = 0; c <= outc; ++c) {
-              if ((__ballot(need0 && c0 == c) | __ballot(need1 && c1 == c)) == 0ull) continue;
-              const uint32_t v0 = (a0 && c0 == c) ? (uint32_t)(i0 + 1) : 0u;
-              const uint32_t v1 = (a1 && c1 == c) ? (uint32_t)(i1 + 1) : 0u;
-              const uint32_t Mx = dpp_mov<0x138>(max_scan(max(v0, v1)));  // last before slot i0
-              if (need0 && c0 == c) pp0 = (int)Mx - 1;
-              if (need1 && c1 == c) pp1 = (int)max(Mx, v0) - 1;
-            }
-          }
-          if (gl0) {
-            tq0 = (slk[pp0] >> pb) & tmask;
-            sq0 = st_sl[wid][pp0];
-          }
-          if (gl1) {
-            tq1 = (slk[pp1] >> pb) & tmask;
-            sq1 = st_sl[wid][pp1];
-          }
-        }
+      if (j + 2 < len) load_pair(j + 2);
+      const uint32_t h0 = (uint32_t)(K0 >> 32);
+      // a window head: windows have even lengths in the lane's stream, so a
+      // head is always the first of a pair (an empty slot has key 0)
+      if (K0 != 0ull && ((h0 >> 9) & 1u)) {
+        gate = (h0 >> 10) & gmask;
+        const uint4 rec = a.gate_rec[gate];
+        const double cap = __hiloint2double((int)rec.y, (int)rec.x);
+        cell = rec.z & 0xFFFFFFu;
+        cseg = rec.z >> 24;
+        const uint2 m = meta_of(cell);
+        kk = m.x & 15u;
+        lb = m.x >> 4;
+        lutb = m.y;
+        const double2 cx = caxw_of(cell, cseg);
+        fc = (cap - cx.x) * cx.y;  // position on the gate's cap segment (Sec. 2.4.1, Fig. 2)
+        esw = a.hv2 * cap;         // Eq. 1
+        if constexpr (NIN > 0) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int p = r ? i1 : i0;
-          const uint32_t cx = r ? c1 : c0;
-          // back over the earlier events of the same timestamp: undo their toggles
-          uint32_t corr = 0;
-          bool bk = r ? tie1 : tie0;
-          for (int y = p - 1; __ballot(bk) != 0ull; --y) {
-            if (bk) {
-              corr ^= 1u << (slk[y] & outc);
-              bk = sgh[y] != 0;
-            }
+          for (int i = 0; i < NIN; i += 4) {
+            const float4 t4 = thr_of(cell, i);
+            th[i] = t4.x;
+            if (i + 1 < NIN) th[i + 1] = t4.y;
+            if (i + 2 < NIN) th[i + 2] = t4.z;
+            if (i + 3 < NIN) th[i + 3] = t4.w;
           }
-          // forward over the later ones: the input pins switching with this event
-          uint32_t mk = 1u << cx;
-          bool fw = (r ? (a1 && in1) : (a0 && in0)) && p + 1 < end && sgh[p + 1];
-          for (int y = p + 1; __ballot(fw) != 0ull; ++y) {
-            if (fw) {
-              const uint32_t j = slk[y] & outc;
-              if (j != outc) mk |= 1u << j;
-              fw = y + 1 < end && sgh[y + 1];
-            }
-          }
-          if (r) { S1s ^= corr; mk1 = mk; } else { S0s ^= corr; mk0 = mk; }
         }
-        wave_sync();
+        S = h0 & 0xFFu;  // input state at the window start
+        St = S;
+        seen = 0;
+        pcyc = ~0u;
+        lkS = leak_of(lb + S);
       }
 
-      // ---- one event per lane slot: energy, glitch, leakage change, bins
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const bool act = r ? a1 : a0;
-        if (!act) continue;
-        const uint32_t lk = r ? lk1 : lk0, hw = r ? h1 : h0;
-        const uint32_t code = r ? c1 : c0, cyc = r ? y1 : y0, tic = r ? t1 : t0;
-        const bool input = r ? in1 : in0;
-        const uint4 rec = (r && !same_gate) ? rec1 : rec0;
-        const uint32_t info = rec.z;
-        const double cap = __hiloint2double((int)rec.y, (int)rec.x);
+        const uint64_t K = r ? K1 : K0;
+        if (K == 0ull) continue;  // an empty slot of a short lane stream or an odd window
+        const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
         const float sl = r ? s1 : s0;
-        const uint32_t cell = info & 0xFFFFFFu;
-        const uint2 m = meta_of(cell);
-        const uint32_t kk = m.x & 15u, lb = m.x >> 4;
-        const uint32_t smask = (1u << kk) - 1u;
-        const uint32_t Sm = (r ? S1s : S0s) & smask;
+        const uint32_t code = lk & outc;                   // pin code
+        const uint32_t tic = (lk >> pb) & tmask;           // time inside the cycle
+        const uint32_t cyc = (uint32_t)((((uint64_t)hw >> ysh) << 32 | lk) >> cs);  // cycle in the chunk
+        const bool input = code != outc;
+        // all events of one timestamp see the state before the first of them
+        // (Sec. 2.4.2); a new timestamp starts from the state after the last
+        if (cyc != pcyc || tic != ptic) St = S;
+        const uint32_t Sm = St;
+        // glitch: the pin already switched in this clock cycle (Sec. 2.4.1, Fig. 7)
+        if (cyc != pcyc) seen = 0;
+        const bool glitch = (seen >> code) & 1u;
+        seen |= 1u << code;
+        pcyc = cyc;
+        ptic = tic;
+        uint2 *pr = prec + (size_t)min(code, kmax) * 64;
+        uint2 prev = make_uint2(0u, 0u);
+        if (glitch) prev = *pr;  // the pin's previous event in this cycle
+        *pr = make_uint2(tic, __float_as_uint(sl));
+
         // slew segment on the cell's axis: inner points at or below the slew (Sec. 2.4.1, Fig. 2)
         uint32_t si = 0;
-        if constexpr (NIN >= 0) {
-          // NIN inner points, fully unrolled
+        if constexpr (NIN > 0) {
 #pragma unroll
-          for (int j = 0; j < NIN; j += 4) {
-            const float4 th = thr_of(cell, j);
-            si += sl >= th.x ? 1u : 0u;
-            if (j + 1 < NIN) si += sl >= th.y ? 1u : 0u;
-            if (j + 2 < NIN) si += sl >= th.z ? 1u : 0u;
-            if (j + 3 < NIN) si += sl >= th.w ? 1u : 0u;
-          }
+          for (int i = 0; i < NIN; ++i) si += sl >= th[i] ? 1u : 0u;
         } else {
           // padding points are +inf and never counted
-          for (int j = 0; j < nthr; j += 4) {
-            const float4 th = thr_of(cell, j);
-            si += (sl >= th.x ? 1u : 0u) + (sl >= th.y ? 1u : 0u) + (sl >= th.z ? 1u : 0u) + (sl >= th.w ? 1u : 0u);
+          for (int i = 0; i < nthr; i += 4) {
+            const float4 t4 = thr_of(cell, i);
+            si += (sl >= t4.x ? 1u : 0u) + (sl >= t4.y ? 1u : 0u) + (sl >= t4.z ? 1u : 0u) + (sl >= t4.w ? 1u : 0u);
           }
         }
         const double2 aw = axw_of(cell, si);
         const double fa = ((double)sl - aw.x) * aw.y;
         const uint32_t cl = input ? code : 0u;
-        const uint32_t lo = __umul24(__umul24(__umul24(Sm, kk) + cl, ns) + si, nc) + (info >> 24);
+        const uint32_t lo = __umul24(__umul24(__umul24(Sm, kk) + cl, ns) + si, nc) + cseg;
         double L00, L01, L10, L11;
-        if (CELL_LDS && (m.y & kLutLds) != 0u) {
+        if (CELL_LDS && (lutb & kLutLds) != 0u) {
           // an LDS-typed pointer, so the two branches' loads stay ds reads and
           // global loads instead of merging into flat loads
-          const lds_f64 *Lp = (const lds_f64 *)(L.lut) + ((m.y & ~kLutLds) + lo);
+          const lds_f64 *Lp = (const lds_f64 *)(L.lut) + ((lutb & ~kLutLds) + lo);
           L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
         } else {
-          const double *Lp = a.lut + (m.y + lo);
+          const double *Lp = a.lut + (lutb + lo);
           L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
         }
-        const double2 cx = caxw_of(cell, info >> 24);
-        const double fc = (cap - cx.x) * cx.y;  // position on the gate's cap segment (Sec. 2.4.1, Fig. 2)
         const double v0 = L00 + fc * (L01 - L00);
         const double v1 = L10 + fc * (L11 - L10);
         const double Eint = v0 + fa * (v1 - v0);
-        const double E = input ? Eint : (((hw >> 8) & 1u) ? a.hv2 * cap : 0.0);  // Eq. 1: 0->1 output events only
-        const bool glitch = r ? gl1 : gl0;
+        const double E = input ? Eint : (((hw >> 8) & 1u) ? esw : 0.0);  // Eq. 1: 0->1 output events only
         double contrib = E;
-        double lk_gate = 0.0;  // leakage of this power change up to t_max (per-gate output)
-        double dyn = 0.0;      // this event's dynamic energy after the glitch scale
         if (glitch) {
-          const double pw = (double)(tic - (r ? tq1 : tq0));
-          const double rr = pw / (0.5 * ((double)sl + (double)(r ? sq1 : sq0)));  // Eq. 2 (reading)
+          const double pw = (double)(tic - prev.x);
+          const double rr = pw / (0.5 * ((double)sl + (double)__uint_as_float(prev.y)));  // Eq. 2 (reading)
           contrib = (rr > 1.0 ? 1.0 : rr) * E;
           e_gl += contrib;
           ++n_gl;
@@ -547,21 +341,20 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         } else {
           e_sw += E;
         }
-        dyn = contrib;
-        // leakage power change at this timestamp (owner = lowest switching input pin)
-        // (read for every event, so that the reads can start early; output
-        // events and later events of a timestamp keep dp = 0)
-        const double lk1v = leak_of(lb + (Sm ^ ((r ? mk1 : mk0) & smask))), lk0v = leak_of(lb + Sm);
-        {
-          const double dp = (input && (r ? ow1 : ow0)) ? lk1v - lk0v : 0.0;
+        const double dyn = contrib;  // this event's dynamic energy after the glitch scale
+        if (input) {
+          // leakage power change of this input's toggle (Sec. 2.4.2, Eq. 4)
+          S ^= 1u << code;
+          const double lkn = leak_of(lb + S);
+          const double dp = lkn - lkS;
+          lkS = lkn;
           if (dp != 0.0) {
             // rest of the event's bin (the flush corrects a partial last bin)
             const double part = dp * tick * (double)(T - tic);
             if constexpr (DIAG) {
-              if (a.gate_J) {
-                lk_gate = dp * tick * (double)(a.t_max - cstart - ((int64_t)cyc * T + tic));
-                atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[(hw >> 10) & gmask] + 3, lk_gate);
-              }
+              if (a.gate_J)
+                atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[gate] + 3,
+                          dp * tick * (double)(a.t_max - cstart - ((int64_t)cyc * T + tic)));
             }
             contrib += part;
             e_lk += part;
@@ -571,19 +364,17 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         if (contrib != 0.0) atomicAdd(&L.bw[cyc], contrib);
         atomicAdd(&L.bc[cyc], 1ull | ((unsigned long long)glitch << 32));
         if constexpr (DIAG) {
-          const uint32_t o = a.orig[base + (r ? i1 : i0)];
+          const uint32_t o = a.orig[base + j * 64 + 2 * lane + r];
           if (a.evt_glitch) a.evt_glitch[o] = glitch ? 1 : 0;
           if (a.evt_state) a.evt_state[o] = (uint8_t)(input ? Sm : 0u);
           // the gate's own energy: internal, switching or glitch (device atomics)
           if (a.gate_J && dyn != 0.0)
-            atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[(hw >> 10) & gmask] + (glitch ? 2 : (input ? 0 : 1)), dyn);
+            atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[gate] + (glitch ? 2 : (input ? 0 : 1)), dyn);
         }
       }
-      pos = npos;
     }
   }
   __syncthreads();
-
   // ---- the block's bins: in-chunk prefix of the leakage changes, then its own slots
   double dsum = 0.0;
   {
@@ -664,30 +455,22 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
   }
 }
 
-// One wave per block range: the cuts between the block's waves, moved to window heads.
-__global__ __launch_bounds__(64) void k_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rstart,
-                                                     int32_t *wb) {
-  const int64_t r0 = rstart[blockIdx.x], r1 = rstart[blockIdx.x + 1];
-  for (int w = 0; w <= kNW; ++w) {
-    const int h = find_head(key, E, r0 + (r1 - r0) * w / kNW);
-    if (threadIdx.x == 0) wb[(size_t)blockIdx.x * (kNW + 1) + w] = h;
-  }
-}
 
-// One wave per block range: 64 events sampled at the midpoints of 64 equal
-// slices of the range give the cells present (nondecreasing, since gates
-// are numbered in cell order) and each cell's share; the heaviest cells whose
-// LUTs still fit in `budget` doubles are taken, heaviest first.
-__global__ __launch_bounds__(64) void k_lut_plan(const uint64_t *key, const int32_t *wb, const uint4 *gate_rec,
-                                                 const uint2 *cell_meta, uint32_t gb, int ns, int nc,
-                                                 uint32_t budget, uint2 *plan) {
+// One wave per block: 64 windows sampled at the midpoints of 64 equal slices
+// of the block's window range (windows in gate order, gates numbered in cell
+// order, so the cells come out nondecreasing) give the cells present and each
+// cell's share; the heaviest cells whose LUTs still fit in `budget` doubles
+// are taken, heaviest first.
+__global__ __launch_bounds__(64) void k_lut_plan(const uint64_t *skey, const uint32_t *ws, const uint32_t *bwin,
+                                                 const uint4 *gate_rec, const uint2 *cell_meta, uint32_t gb, int ns,
+                                                 int nc, uint32_t budget, uint2 *plan) {
   const int b = blockIdx.x, lane = threadIdx.x;
-  const int r0 = wb[(size_t)b * (kNW + 1)], r1 = wb[(size_t)b * (kNW + 1) + kNW];
+  const uint32_t w0 = bwin[b], w1 = bwin[b + 1];
   const uint32_t gmask = (1u << gb) - 1u;
   uint32_t cell = ~0u;
-  if (r1 > r0) {
-    const int p = r0 + (int)((int64_t)(r1 - r0) * (2 * lane + 1) / 128);
-    const uint32_t g = (uint32_t)(key[p] >> (32 + 10)) & gmask;
+  if (w1 > w0) {
+    const uint32_t w = w0 + (uint32_t)((uint64_t)(w1 - w0) * (2 * lane + 1) / 128);
+    const uint32_t g = (uint32_t)(skey[ws[w]] >> (32 + 10)) & gmask;
     cell = gate_rec[g].z & 0xFFFFFFu;
   }
   const uint32_t prev = __shfl_up(cell, 1);
@@ -845,54 +628,46 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
 
 int pass_block_threads() { return kNT; }
 int pass_blocks_per_cu() { return kBPC; }
-size_t pass_static_lds_bytes() {
-  return (size_t)kNW * kB * (sizeof(uint32_t) + sizeof(uint8_t) + sizeof(float)) + (size_t)kNW * 9 * sizeof(double);
-}
-int pass_wave_bounds_per_block() { return kNW + 1; }
+int pass_waves_per_block() { return kNW; }
+size_t pass_static_lds_bytes() { return (size_t)kNW * 9 * sizeof(double); }
 
-hipError_t launch_wave_bounds(const uint64_t *key, int64_t E, const uint32_t *rstart, int32_t n_ranges, int32_t *wb,
-                              hipStream_t s) {
-  if (n_ranges <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_wave_bounds, dim3(n_ranges), dim3(64), 0, s, key, E, rstart, wb);
-  return hipGetLastError();
-}
-hipError_t launch_lut_plan(const uint64_t *key, const int32_t *wb, int32_t n_ranges, const uint4 *gate_rec,
-                           const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap, int32_t lut_lds, uint2 *plan,
-                           hipStream_t s) {
+hipError_t launch_lut_plan(const uint64_t *skey, const uint32_t *ws, const uint32_t *bwin, int32_t n_ranges,
+                           const uint4 *gate_rec, const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap,
+                           int32_t lut_lds, uint2 *plan, hipStream_t s) {
   if (n_ranges <= 0 || lut_lds <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lut_plan, dim3(n_ranges), dim3(64), 0, s, key, wb, gate_rec, cell_meta, gb, n_slew, n_cap,
-                     (uint32_t)lut_lds, plan);
+  hipLaunchKernelGGL(k_lut_plan, dim3(n_ranges), dim3(64), 0, s, skey, ws, bwin, gate_rec, cell_meta, gb, n_slew,
+                     n_cap, (uint32_t)lut_lds, plan);
   return hipGetLastError();
 }
 int pass_lut_plan_slots() { return kPlan; }
 int pass_wave_batch() { return kB; }
 int pass_max_chunk_cycles() { return kCCMAX; }
 
-size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, bool cells) {
-  return 24 * (size_t)Cc + (cells ? cell_bytes(n_cells, n_slew, n_cap, n_thr, n_leak) : 0);
+size_t pass_lds_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax, bool cells) {
+  return 24 * (size_t)Cc + prec_bytes(kmax) + (cells ? cell_bytes(n_cells, n_slew, n_cap, n_thr, n_leak) : 0);
 }
 
-bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
-  return pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, true) + pass_static_lds_bytes() <= kLdsMax;
+bool pass_cells_fit_lds(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax) {
+  return pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, kmax, true) + pass_static_lds_bytes() <= kLdsMax;
 }
 
-static size_t lut_lds_offset(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
-  return (pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, true) + 15) & ~size_t(15);
+static size_t lut_lds_offset(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax) {
+  return (pass_lds_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, kmax, true) + 15) & ~size_t(15);
 }
 
-int32_t pass_lut_lds_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak) {
-  if (!pass_cells_fit_lds(Cc, n_cells, n_slew, n_cap, n_thr, n_leak)) return 0;
-  const size_t used = lut_lds_offset(Cc, n_cells, n_slew, n_cap, n_thr, n_leak) + pass_static_lds_bytes();
+int32_t pass_lut_lds_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax) {
+  if (!pass_cells_fit_lds(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, kmax)) return 0;
+  const size_t used = lut_lds_offset(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, kmax) + pass_static_lds_bytes();
   return used < kLdsMax ? (int32_t)((kLdsMax - used) / 16 * 2) : 0;
 }
 
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
-  const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak);
+  const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax);
   const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
-  size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, cells);
+  size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax, cells);
   if (cells && a.lut_lds > 0) {
     if (!a.lut_plan) return hipErrorInvalidValue;
-    dyn = lut_lds_offset(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak) + 8 * (size_t)a.lut_lds;
+    dyn = lut_lds_offset(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax) + 8 * (size_t)a.lut_lds;
   }
   if (dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
   const dim3 g(grid_blocks), t(kNT);

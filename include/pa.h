@@ -119,14 +119,14 @@ int pa_load_design(pa_ctx *ctx, int64_t n_gates, const int32_t *gate_cell, const
  *          k = 1, 2 for k = 2..3, 3 for k = 4..7, 4 for k = 8);
  *   t_max > 0 analysis end, at most 2^28 clock cycles; tick_s seconds per
  *   tick (> 0).
- * Limit: at most 127 events of one gate (all its pins together) inside one
- * clock cycle; more is reported as PA_EDATA.
  * The events are validated (PA_EDATA for a broken rule above; the
  * previously loaded events stay usable) and re-laid out into library-owned
- * memory: time chunks of chunk_cycles cycles; inside a chunk the events are
- * ordered by gate, clock cycle, time and pin, and every gate's part of a
- * chunk is cut into 2^s equal windows sized from the gate's event density
- * (the paper's event-density-aware per-gate cycle partitioning). */
+ * memory: time chunks of chunk_cycles cycles; every gate's part of a chunk
+ * is cut into 2^s equal windows sized from the gate's event density (the
+ * paper's event-density-aware per-gate cycle partitioning), the events of a
+ * window in clock cycle, time and pin order; the windows of a block of the
+ * pass are dealt to its lanes by length, and every lane walks its windows
+ * event by event. */
 int pa_load_events(pa_ctx *ctx, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr,
                    const uint8_t *pin_init, const int64_t *evt_t, const uint8_t *evt_val,
                    const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s);
@@ -176,11 +176,14 @@ typedef struct {
   int32_t chunk_cycles, n_chunks;
   int32_t grid_blocks, block_threads;
   int32_t batch_events;       /* events one wave takes per step of the pass */
-  int32_t max_segment_events; /* most events of one gate in one clock cycle (the load limit) */
+  int32_t max_segment_events; /* 0: no limit on the events of one gate in one clock cycle */
   int64_t device_bytes;       /* library-owned device memory: the loaded design and events, the
                                  per-pass scratch, and the staging of pa_run_text (the load's own
                                  scratch is freed when pa_load_events returns) */
   float kernel_ms[4];         /* last timed pa_run: fused, finalize, (unused), whole pass; mode 2 fills only the last */
+  int64_t n_windows;          /* density-aware windows of the layout */
+  int64_t n_slots;            /* slots of the pass's lane streams: the events plus the empty slots
+                                 that pad windows to even lengths and lanes to their wave's longest */
 } pa_info;
 int pa_get_info(pa_ctx *ctx, pa_info *info);
 

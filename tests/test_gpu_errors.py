@@ -156,22 +156,3 @@ def test_bad_design_rejected(kind):
         assert ei.value.code == pa.PA_EDATA
     finally:
         an.close()
-
-
-def test_too_many_events_of_one_gate_in_one_cycle():
-    """The layout holds at most 128 events of one gate inside one clock cycle;
-    more is reported as PA_EDATA (a documented limit of this library)."""
-    import eda_gate_level_amd as pa
-
-    rng = np.random.default_rng(3)
-    lib = synth.make_library(rng, (1,), cells_per_k=1, n_axis=3)
-    des = synth.assign_gates(rng, lib, np.array([1]), 1.0, 5.0)
-    tr = synth.poisson_trace(rng, np.array([100.0, 100.0]), 4, 100_000)
-    an = pa.PowerAnalysis()
-    try:
-        an.load_design(des)
-        with pytest.raises(pa.PaError) as ei:
-            an.load_events(tr)
-        assert ei.value.code == pa.PA_EDATA
-    finally:
-        an.close()

@@ -168,8 +168,8 @@ def test_load_frees_its_scratch():
     """The event load's scratch (sort keys, indexes, the radix sort's storage)
     and the previous load's buffers are freed when the load returns: loading
     the same events again keeps the footprint, and it stays within the
-    events' own arrays (key, slew, caller index: 16 B per event), the
-    per-block bins and the design."""
+    events' own arrays (key, slew, caller index: 16 B per slot of the lane
+    streams, 4 B per window), the per-block bins and the design."""
     import eda_gate_level_amd as pa
 
     d, t = _random(seed=12, G=3000, C=300, rate=0.05)
@@ -185,7 +185,9 @@ def test_load_frees_its_scratch():
     finally:
         an.close()
     assert i2["device_bytes"] == i1["device_bytes"] == i3["device_bytes"]
-    bound = (24 * t.n_events + 16 * i1["grid_blocks"] * i1["chunk_cycles"] + 64 * d.n_gates
+    print(f"events {t.n_events} windows {i1['n_windows']} slots {i1['n_slots']}", flush=True)
+    assert t.n_events <= i1["n_slots"] <= 2 * t.n_events + 128 * i1["n_windows"]
+    bound = (16 * i1["n_slots"] + 4 * i1["n_windows"] + 16 * i1["grid_blocks"] * i1["chunk_cycles"] + 64 * d.n_gates
              + 16 * int(d.pin_base()[-1]) + d.lut_J.nbytes + (1 << 20))
     assert i1["device_bytes"] <= bound, (i1["device_bytes"], bound)
 
@@ -263,6 +265,21 @@ def test_dense_glitch_train():
     assert o["n_glitches"] > 1000
     for chunk in (0, 2):
         pu.assert_parity(pu.gpu_run(des, tr, chunk_cycles=chunk), o, label=f"dense chunk {chunk}")
+
+
+def test_hundreds_of_events_of_one_gate_in_one_cycle():
+    """A gate with about 200 events inside single clock cycles (two pins at
+    100 events per cycle each): a lane walks the whole run, with no limit on
+    its length."""
+    rng = np.random.default_rng(3)
+    lib = synth.make_library(rng, (1,), cells_per_k=1, n_axis=3)
+    des = synth.assign_gates(rng, lib, np.array([1]), 1.0, 5.0)
+    tr = synth.poisson_trace(rng, np.array([100.0, 100.0]), 4, 100_000)
+    _print_case("200 events per gate-cycle")
+    o = _oracle(des, tr)
+    assert tr.n_events > 600 and o["n_glitches"] > 500
+    for chunk in (0, 1):
+        pu.assert_parity(pu.gpu_run(des, tr, chunk_cycles=chunk), o, label=f"dense cycle chunk {chunk}")
 
 
 def test_repeated_runs_agree():
