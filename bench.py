@@ -331,7 +331,9 @@ def main():
                                f"{d.n_slew}x{d.n_cap} fp64 LUTs), {C} cycles of {tr.t_clk} fs, {E} events, seed 0",
                    "gates": G, "pins": P, "events": E, "cycles": C,
                    "chunk_cycles": info["chunk_cycles"], "grid_blocks": info["grid_blocks"],
-                   "block_threads": info["block_threads"]},
+                   "block_threads": info["block_threads"], "windows": info["n_windows"],
+                   "stream_slots": info["n_slots"], "wave_steps_max": info["wave_steps_max"],
+                   "wave_steps_mean": round(info["wave_steps_mean"], 2)},
         "gate_cycles_per_s": G * C / (ms_step * 1e-3),
         "fused_ms": ms_fused,
         "pass_ms_p10_p90": [float(np.percentile(pass_ms, 10)), float(np.percentile(pass_ms, 90))],

@@ -97,6 +97,8 @@ struct Events {
   DBuf key, slew, orig, pin_init;
   std::vector<uint32_t> h_chunk_base;
   int64_t n_windows = 0, slots = 0;  // windows; slots of the lane streams (events and empty slots)
+  int32_t wave_steps_max = 0;       // steps of the longest wave, and the mean over waves with work
+  float wave_steps_mean = 0.f;
   DBuf rstart, rchunk, chunk_blk;  // block ranges of the pass, first block of every chunk
   DBuf wdesc, wlen, l0;            // every wave's (first slot, events per lane); events per window; leakage at t = 0
   DBuf lplan;                      // per block, the cells whose LUTs it copies into LDS
@@ -372,6 +374,14 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   return PA_OK;
 }
 
+// Density-aware windows: a gate's windows are the longest power-of-two parts
+// of a chunk whose expected event count is at most this.  A lane walks whole
+// windows, so the longest window bounds the longest lane.
+#ifndef PA_WINDOW_EVENTS
+#define PA_WINDOW_EVENTS 32.0
+#endif
+static constexpr double kWindowEvents = PA_WINDOW_EVENTS;
+
 // Block ranges of the pass and the lane streams.  Every chunk's events are cut
 // into pieces of about E / target events (never across a chunk, so a block's
 // bins cover one chunk), each cut moved to the next window start; a block's
@@ -468,11 +478,16 @@ static int build_ranges(pa_ctx *c, Events &v) {
   }
   // ---- every wave's first slot: 64 lane streams of its longest stream's length each
   std::vector<uint2> wd((size_t)v.grid * NW, make_uint2(0u, 0u));
-  uint64_t slots = 0;
+  uint64_t slots = 0, busy = 0;
+  uint32_t longest = 0;
   for (size_t w = 0; w < wave_len.size(); ++w) {
     wd[w] = make_uint2((uint32_t)slots, wave_len[w]);
     slots += 64 * (uint64_t)wave_len[w];
+    longest = std::max(longest, wave_len[w]);
+    busy += wave_len[w] > 0 ? 1 : 0;
   }
+  v.wave_steps_max = (int32_t)(longest / 2);
+  v.wave_steps_mean = busy ? (float)((double)slots / 128.0 / (double)busy) : 0.f;
   if (slots >= (uint64_t(1) << 31))
     return fail(PA_EINVAL, "pa_load_events: the lane streams need %llu slots (2^31 allowed)",
                 (unsigned long long)slots);
@@ -644,7 +659,7 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
       while ((Cc >> fixed_level) > n) ++fixed_level;
     }
     HIPCHK(pa::launch_gate_levels(G, d.pin_base.as<int64_t>(), d.gate_k.as<int32_t>(), pin_ptr, v.C, (int32_t)Cc,
-                                  (int32_t)lc, 32.0, fixed_level, level.as<uint8_t>(), s));
+                                  (int32_t)lc, kWindowEvents, fixed_level, level.as<uint8_t>(), s));
     // ---- order (chunk, gate, cycle, pin, time) by radix sort
     DBuf &k0 = c->ls.k0, &k1 = c->ls.k1, &idx = c->ls.idx, &perm = c->ls.perm, &tmp = c->ls.tmp;
     size_t tmp_bytes = 0;
@@ -877,6 +892,8 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
   for (int k = 0; k < 4; ++k) info->kernel_ms[k] = c->kernel_ms[k];
   info->n_windows = c->has_events ? c->ev.n_windows : 0;
   info->n_slots = c->has_events ? c->ev.slots : 0;
+  info->wave_steps_max = c->has_events ? c->ev.wave_steps_max : 0;
+  info->wave_steps_mean = c->has_events ? c->ev.wave_steps_mean : 0.f;
   return PA_OK;
 }
 

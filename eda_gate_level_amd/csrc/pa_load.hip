@@ -234,11 +234,11 @@ __global__ void k_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted,
 // ------------------------------------------------------ lane streams of the pass
 //
 // The sorted events (window order) are dealt to the pass's lanes: every block
-// owns a range of whole windows of one chunk; its windows, longest first, go
-// to its 1024 lanes in snake order (ranks 0..1023 to lanes 0..1023, the next
-// 1024 to lanes 1023..0, and so on), so that the lanes' event counts come out
-// nearly equal.  A lane's windows follow one another in its stream, each
-// padded to an even length, and a wave's 64 streams are interleaved in pairs.
+// owns a range of whole windows of one chunk; its windows, longest first, are
+// dealt to its 1024 lanes, each to one of the lanes with the shortest stream
+// so far (k_lane_plan), so that the lanes' event counts come out nearly equal.
+// A lane's windows follow one another in its stream, each padded to an even
+// length, and a wave's 64 streams are interleaved in pairs.
 
 constexpr int kLaneNT = 1024;  // lanes of a block of the pass
 constexpr int kLaneNW = kLaneNT / 64;
@@ -283,25 +283,52 @@ __global__ void k_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin,
   }
 }
 
-// one thread per (block, lane): its windows in snake order, their offsets in
-// the lane's stream (wlane[w] = (global wave << 6 | lane, first event)), and
-// the stream's length
-__global__ void k_lane_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint32_t *wlen,
-                            uint2 *wlane, uint32_t *lane_len) {
-  const int64_t t = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t >= (int64_t)nr * kLaneNT) return;
-  const int b = (int)(t / kLaneNT), u = (int)(t % kLaneNT);
+// One block of kLaneNT threads per block of the pass, one thread per lane:
+// the block's windows, longest first, are dealt in rounds of kLaneNT, each
+// round giving its windows to the lanes in order of their current length,
+// shortest first (the longest-processing-time rule, applied a round at a
+// time), so that the lanes' stream lengths come out nearly equal.  Every
+// window's place in its lane's stream goes to wlane[w] = (global wave << 6 |
+// lane, first slot), and every lane's stream length to lane_len.
+__global__ __launch_bounds__(kLaneNT) void k_lane_plan(const uint32_t *bwin, const uint32_t *worder,
+                                                       const uint32_t *wlen, uint2 *wlane, uint32_t *lane_len) {
+  __shared__ unsigned long long sk[kLaneNT];
+  __shared__ uint32_t snew[kLaneNT];
+  const int b = blockIdx.x, u = threadIdx.x;
   const uint32_t w0 = bwin[b], nb = bwin[b + 1] - w0;
-  const uint32_t lane_id = ((uint32_t)(b * kLaneNW + u / 64) << 6) | (uint32_t)(u % 64);
-  uint32_t off = 0;
-  for (uint32_t round = 0;; ++round) {
-    const uint32_t r = round * kLaneNT + ((round & 1u) ? (uint32_t)(kLaneNT - 1 - u) : (uint32_t)u);
-    if (r >= nb) break;
-    const uint32_t w = worder[w0 + r];
-    wlane[w] = make_uint2(lane_id, off);
-    off += (wlen[w] + 1u) & ~1u;
+  uint32_t len = 0;  // this lane's stream so far
+  for (uint32_t r0 = 0; r0 < nb; r0 += kLaneNT) {
+    // the lanes sorted by (length, lane): a bitonic sort over the block
+    sk[u] = ((unsigned long long)len << 16) | (unsigned)u;
+    __syncthreads();
+    for (int k = 2; k <= kLaneNT; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        const int ixj = u ^ j;
+        if (ixj > u) {
+          const unsigned long long x = sk[u], y = sk[ixj];
+          if (((u & k) == 0) ? (x > y) : (x < y)) {
+            sk[u] = y;
+            sk[ixj] = x;
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // the round's window of rank r0 + u goes to the u-th shortest lane
+    const unsigned long long e = sk[u];
+    const uint32_t lane = (uint32_t)(e & 0xFFFFu), off = (uint32_t)(e >> 16);
+    uint32_t nl = off;
+    if (r0 + u < nb) {
+      const uint32_t w = worder[w0 + r0 + u];
+      wlane[w] = make_uint2(((uint32_t)(b * kLaneNW) + lane / 64u) << 6 | (lane % 64u), off);
+      nl = off + ((wlen[w] + 1u) & ~1u);  // the window's events padded to an even count
+    }
+    snew[lane] = nl;
+    __syncthreads();
+    len = snew[u];
+    __syncthreads();
   }
-  lane_len[t] = off;
+  lane_len[(size_t)b * kLaneNT + u] = len;
 }
 
 // events per lane of every wave: the longest of its 64 lane streams
@@ -493,10 +520,8 @@ hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin,
 }
 hipError_t launch_lane_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint32_t *wlen,
                             uint2 *wlane, uint32_t *lane_len, hipStream_t s) {
-  const int64_t n = (int64_t)nr * kLaneNT;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lane_plan, dim3((unsigned)((n + kLT - 1) / kLT)), dim3(kLT), 0, s, nr, bwin, worder, wlen,
-                     wlane, lane_len);
+  if (nr <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lane_plan, dim3((unsigned)nr), dim3(kLaneNT), 0, s, bwin, worder, wlen, wlane, lane_len);
   return hipGetLastError();
 }
 hipError_t launch_wave_len(int64_t n_waves, const uint32_t *lane_len, uint32_t *wave_len, hipStream_t s) {

@@ -16,8 +16,9 @@
 //     whose first event (the head) carries the gate's input state at the
 //     window start; a lane walks whole windows, one event after the other,
 //     in time order: the k-way merge of Sec. 2.4.2 is the layout's order;
-//   * at load, a block's windows are sorted by length and dealt to its 1024
-//     lanes in snake order, so the lanes' event counts come out nearly equal;
+//   * at load, a block's windows are dealt to its 1024 lanes longest first,
+//     each to a lane whose stream is shortest so far, so the lanes' event
+//     counts come out nearly equal;
 //     a wave's 64 lane streams are interleaved two events at a time, so that
 //     step i of the wave reads events 2i and 2i+1 of every lane with one
 //     coalesced 16-byte load per lane (the next step's pair prefetched);
@@ -274,102 +275,150 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
         lkS = leak_of(lb + S);
       }
 
+      // ---- the pair's two events, in phases so that both events' LDS reads
+      // are in flight together.  Phase 1, integer and branch-free: the fields,
+      // the state before each event (all events of one timestamp see the
+      // state before the first of them, Sec. 2.4.2), the glitch flags (the pin
+      // already switched in this clock cycle, Sec. 2.4.1, Fig. 7), the slew
+      // segment and the LUT row.  An empty slot (key 0, a short lane stream
+      // or an odd window) changes no state and adds nothing.
+      uint32_t code[2], tic[2], cyc[2], Sm[2], Sa[2], si[2], lo[2];
+      bool act[2], input[2], glitch[2], rise[2];
+      float sl[2] = {s0, s1};
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const uint64_t K = r ? K1 : K0;
-        if (K == 0ull) continue;  // an empty slot of a short lane stream or an odd window
+        act[r] = K != 0ull;
         const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
-        const float sl = r ? s1 : s0;
-        const uint32_t code = lk & outc;                   // pin code
-        const uint32_t tic = (lk >> pb) & tmask;           // time inside the cycle
-        const uint32_t cyc = (uint32_t)((((uint64_t)hw >> ysh) << 32 | lk) >> cs);  // cycle in the chunk
-        const bool input = code != outc;
-        // all events of one timestamp see the state before the first of them
-        // (Sec. 2.4.2); a new timestamp starts from the state after the last
-        if (cyc != pcyc || tic != ptic) St = S;
-        const uint32_t Sm = St;
-        // glitch: the pin already switched in this clock cycle (Sec. 2.4.1, Fig. 7)
-        if (cyc != pcyc) seen = 0;
-        const bool glitch = (seen >> code) & 1u;
-        seen |= 1u << code;
-        pcyc = cyc;
-        ptic = tic;
-        uint2 *pr = prec + (size_t)min(code, kmax) * 64;
-        uint2 prev = make_uint2(0u, 0u);
-        if (glitch) prev = *pr;  // the pin's previous event in this cycle
-        *pr = make_uint2(tic, __float_as_uint(sl));
-
+        code[r] = lk & outc;                   // pin code
+        tic[r] = (lk >> pb) & tmask;           // time inside the cycle
+        cyc[r] = (uint32_t)((((uint64_t)hw >> ysh) << 32 | lk) >> cs);  // cycle in the chunk
+        rise[r] = (hw >> 8) & 1u;              // the pin's value after the event
+        input[r] = act[r] && code[r] != outc;
+        const bool newcyc = cyc[r] != pcyc;
+        if (act[r] && (newcyc || tic[r] != ptic)) St = S;
+        Sm[r] = St;
+        if (act[r] && newcyc) seen = 0;
+        const uint32_t bit = 1u << code[r];
+        glitch[r] = act[r] && ((seen & bit) != 0u);
+        if (act[r]) {
+          seen |= bit;
+          pcyc = cyc[r];
+          ptic = tic[r];
+        }
+        if (input[r]) S ^= bit;
+        Sa[r] = S;  // state after the event (leakage)
         // slew segment on the cell's axis: inner points at or below the slew (Sec. 2.4.1, Fig. 2)
-        uint32_t si = 0;
+        uint32_t n = 0;
         if constexpr (NIN > 0) {
 #pragma unroll
-          for (int i = 0; i < NIN; ++i) si += sl >= th[i] ? 1u : 0u;
+          for (int i = 0; i < NIN; ++i) n += sl[r] >= th[i] ? 1u : 0u;
         } else {
           // padding points are +inf and never counted
           for (int i = 0; i < nthr; i += 4) {
             const float4 t4 = thr_of(cell, i);
-            si += (sl >= t4.x ? 1u : 0u) + (sl >= t4.y ? 1u : 0u) + (sl >= t4.z ? 1u : 0u) + (sl >= t4.w ? 1u : 0u);
+            n += (sl[r] >= t4.x ? 1u : 0u) + (sl[r] >= t4.y ? 1u : 0u) + (sl[r] >= t4.z ? 1u : 0u) +
+                 (sl[r] >= t4.w ? 1u : 0u);
           }
         }
-        const double2 aw = axw_of(cell, si);
-        const double fa = ((double)sl - aw.x) * aw.y;
-        const uint32_t cl = input ? code : 0u;
-        const uint32_t lo = __umul24(__umul24(__umul24(Sm, kk) + cl, ns) + si, nc) + cseg;
-        double L00, L01, L10, L11;
-        if (CELL_LDS && (lutb & kLutLds) != 0u) {
-          // an LDS-typed pointer, so the two branches' loads stay ds reads and
-          // global loads instead of merging into flat loads
-          const lds_f64 *Lp = (const lds_f64 *)(L.lut) + ((lutb & ~kLutLds) + lo);
-          L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
-        } else {
-          const double *Lp = a.lut + (lutb + lo);
-          L00 = Lp[0], L01 = Lp[1], L10 = Lp[nc], L11 = Lp[nc + 1];
+        si[r] = n;
+        const uint32_t cl = input[r] ? code[r] : 0u;
+        lo[r] = __umul24(__umul24(__umul24(Sm[r], kk) + cl, ns) + n, nc) + cseg;
+      }
+      // ---- phase 2: every table read of both events
+      double2 aw[2];
+      double L00[2], L01[2], L10[2], L11[2], lkn[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        aw[r] = axw_of(cell, si[r]);
+        lkn[r] = leak_of(lb + Sa[r]);
+      }
+      if (CELL_LDS && (lutb & kLutLds) != 0u) {
+        // an LDS-typed pointer, so the two branches' loads stay ds reads and
+        // global loads instead of merging into flat loads
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const lds_f64 *Lp = (const lds_f64 *)(L.lut) + ((lutb & ~kLutLds) + lo[r]);
+          L00[r] = Lp[0], L01[r] = Lp[1], L10[r] = Lp[nc], L11[r] = Lp[nc + 1];
         }
-        const double v0 = L00 + fc * (L01 - L00);
-        const double v1 = L10 + fc * (L11 - L10);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const double *Lp = a.lut + (lutb + lo[r]);
+          L00[r] = Lp[0], L01[r] = Lp[1], L10[r] = Lp[nc], L11[r] = Lp[nc + 1];
+        }
+      }
+      // ---- phase 3: energies (Sec. 2.4.1, Fig. 2; Eq. 1) and leakage changes (Sec. 2.4.2, Eq. 4)
+      double E[2], dp[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const double fa = ((double)sl[r] - aw[r].x) * aw[r].y;
+        const double v0 = L00[r] + fc * (L01[r] - L00[r]);
+        const double v1 = L10[r] + fc * (L11[r] - L10[r]);
         const double Eint = v0 + fa * (v1 - v0);
-        const double E = input ? Eint : (((hw >> 8) & 1u) ? esw : 0.0);  // Eq. 1: 0->1 output events only
-        double contrib = E;
-        if (glitch) {
-          const double pw = (double)(tic - prev.x);
-          const double rr = pw / (0.5 * ((double)sl + (double)__uint_as_float(prev.y)));  // Eq. 2 (reading)
-          contrib = (rr > 1.0 ? 1.0 : rr) * E;
+        E[r] = input[r] ? Eint : ((act[r] && rise[r]) ? esw : 0.0);  // Eq. 1: 0->1 output events only
+        // the toggle of an input moves the gate's leakage power from lkS to lkn
+        const double lprev = r ? (input[0] ? lkn[0] : lkS) : lkS;
+        dp[r] = input[r] ? lkn[r] - lprev : 0.0;
+      }
+      if (input[0]) lkS = lkn[0];
+      if (input[1]) lkS = lkn[1];
+      // ---- phase 4 (rare): a glitch's energy scaled by r_gl, from the pulse
+      // width and the slews of the pin's previous event in the cycle and this one (Eq. 2)
+      double scale[2] = {1.0, 1.0};
+      if (glitch[0] || glitch[1]) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          uint2 *pr = prec + (size_t)min(code[r], kmax) * 64;
+          if (glitch[r]) {
+            const uint2 prev = *pr;  // the pin's previous event in this cycle
+            const double pw = (double)(tic[r] - prev.x);
+            const double rr = pw / (0.5 * ((double)sl[r] + (double)__uint_as_float(prev.y)));  // Eq. 2 (reading)
+            scale[r] = rr > 1.0 ? 1.0 : rr;
+          }
+          if (act[r]) *pr = make_uint2(tic[r], __float_as_uint(sl[r]));
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+          if (act[r]) prec[(size_t)min(code[r], kmax) * 64] = make_uint2(tic[r], __float_as_uint(sl[r]));
+      }
+      // ---- phase 5: totals and bins
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (!act[r]) continue;
+        double contrib = E[r];
+        if (glitch[r]) {
+          contrib = scale[r] * E[r];
           e_gl += contrib;
           ++n_gl;
-        } else if (input) {
-          e_int += E;
+        } else if (input[r]) {
+          e_int += E[r];
         } else {
-          e_sw += E;
+          e_sw += E[r];
         }
         const double dyn = contrib;  // this event's dynamic energy after the glitch scale
-        if (input) {
-          // leakage power change of this input's toggle (Sec. 2.4.2, Eq. 4)
-          S ^= 1u << code;
-          const double lkn = leak_of(lb + S);
-          const double dp = lkn - lkS;
-          lkS = lkn;
-          if (dp != 0.0) {
-            // rest of the event's bin (the flush corrects a partial last bin)
-            const double part = dp * tick * (double)(T - tic);
-            if constexpr (DIAG) {
-              if (a.gate_J)
-                atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[gate] + 3,
-                          dp * tick * (double)(a.t_max - cstart - ((int64_t)cyc * T + tic)));
-            }
-            contrib += part;
-            e_lk += part;
-            atomicAdd(&L.bb[cyc], dp);
+        if (dp[r] != 0.0) {
+          // rest of the event's bin (the flush corrects a partial last bin)
+          const double part = dp[r] * tick * (double)(T - tic[r]);
+          if constexpr (DIAG) {
+            if (a.gate_J)
+              atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[gate] + 3,
+                        dp[r] * tick * (double)(a.t_max - cstart - ((int64_t)cyc[r] * T + tic[r])));
           }
+          contrib += part;
+          e_lk += part;
+          atomicAdd(&L.bb[cyc[r]], dp[r]);
         }
-        if (contrib != 0.0) atomicAdd(&L.bw[cyc], contrib);
-        atomicAdd(&L.bc[cyc], 1ull | ((unsigned long long)glitch << 32));
+        if (contrib != 0.0) atomicAdd(&L.bw[cyc[r]], contrib);
+        atomicAdd(&L.bc[cyc[r]], 1ull | ((unsigned long long)glitch[r] << 32));
         if constexpr (DIAG) {
           const uint32_t o = a.orig[base + j * 64 + 2 * lane + r];
-          if (a.evt_glitch) a.evt_glitch[o] = glitch ? 1 : 0;
-          if (a.evt_state) a.evt_state[o] = (uint8_t)(input ? Sm : 0u);
+          if (a.evt_glitch) a.evt_glitch[o] = glitch[r] ? 1 : 0;
+          if (a.evt_state) a.evt_state[o] = (uint8_t)(input[r] ? Sm[r] : 0u);
           // the gate's own energy: internal, switching or glitch (device atomics)
           if (a.gate_J && dyn != 0.0)
-            atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[gate] + (glitch ? 2 : (input ? 0 : 1)), dyn);
+            atomicAdd(a.gate_J + 4 * (size_t)a.gate_perm[gate] + (glitch[r] ? 2 : (input[r] ? 0 : 1)), dyn);
         }
       }
     }

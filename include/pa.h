@@ -184,6 +184,8 @@ typedef struct {
   int64_t n_windows;          /* density-aware windows of the layout */
   int64_t n_slots;            /* slots of the pass's lane streams: the events plus the empty slots
                                  that pad windows to even lengths and lanes to their wave's longest */
+  int32_t wave_steps_max;     /* steps (event pairs) of the pass's longest wave */
+  float wave_steps_mean;      /* steps of a wave, averaged over the waves with work */
 } pa_info;
 int pa_get_info(pa_ctx *ctx, pa_info *info);
 
