@@ -22,13 +22,36 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "pa_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra"]
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off", "-fno-fast-math", "-Wall",
+          "-Wextra"]
 
 
-def build(extra_flags=()) -> str:
-    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", LIB, SRC, "-lm"]
+def build(extra_flags=(), out=LIB) -> str:
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", out, SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    return LIB
+    return out
+
+
+def host_threads(cap: int = 16) -> int:
+    """Host cores this process may use, at most `cap` (the CPU share a GPU
+    box gives one GPU is 16 cores, whatever the machine has)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(cap, n))
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" if absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 class Totals(C.Structure):
@@ -52,6 +75,11 @@ def lib():
         L.pa_oracle_run.argtypes = [C.c_int64, P, P, C.c_int32, P, C.c_int32, C.c_int32, P, P, P, P,
                                     C.c_double, C.c_int64, P, P, P, P, P, C.c_int64, C.c_int64,
                                     C.c_double, C.c_int64, C.c_int64, C.POINTER(Totals), P, P, P, P, P, P]
+        L.pa_oracle_run_mt.restype = C.c_int
+        L.pa_oracle_run_mt.argtypes = [C.c_int64, P, P, C.c_int32, P, C.c_int32, C.c_int32, P, P, P, P,
+                                       C.c_double, C.c_int64, P, P, P, P, P, C.c_int64, C.c_int64,
+                                       C.c_double, C.c_int64, C.c_int64, C.c_int32, C.POINTER(Totals), P, P, P,
+                                       P, P, P]
         L.pa_oracle_bilerp.restype = C.c_double
         L.pa_oracle_bilerp.argtypes = [C.c_int, C.c_int, P, P, P, C.c_double, C.c_double]
         L.pa_oracle_n_cycles.restype = C.c_int64
@@ -79,11 +107,13 @@ class OracleError(RuntimeError):
 
 
 def run(design, trace, gate_lo: int = 0, gate_hi: Optional[int] = None, per_event: bool = True,
-        per_gate: bool = False) -> dict:
+        per_gate: bool = False, threads: int = 1) -> dict:
     """Run the oracle over gates [gate_lo, gate_hi).  Returns the totals, the
     per-cycle waveform/counts, (if per_event) the per-event glitch flags and
     states before each event, and (if per_gate) gate_J[G][4]: every gate's
-    internal, switching, glitch and leakage energy (zero outside the range)."""
+    internal, switching, glitch and leakage energy (zero outside the range).
+    threads > 1 walks contiguous gate ranges on that many host threads and
+    merges their sums in range order (pa_oracle_run_mt)."""
     d, t = design, trace
     if gate_hi is None:
         gate_hi = d.n_gates
@@ -103,11 +133,15 @@ def run(design, trace, gate_lo: int = 0, gate_hi: Optional[int] = None, per_even
     gj = np.zeros((d.n_gates, 4), np.float64) if per_gate else None
     tot = Totals()
     a = arrs
-    rc = lib().pa_oracle_run(d.n_gates, _p(a["gc"]), _p(a["cap"]), d.n_cells, _p(a["k"]), d.n_slew, d.n_cap,
-                             _p(a["sa"]), _p(a["ca"]), _p(a["lut"]), _p(a["leak"]), float(d.vdd_V),
-                             t.pin_init.shape[0], _p(a["pp"]), _p(a["pi"]), _p(a["et"]), _p(a["ev"]),
-                             _p(a["es"]), int(t.t_clk), int(t.t_max), float(t.tick_s), int(gate_lo),
-                             int(gate_hi), C.byref(tot), _p(wave), _p(ce), _p(cg), _p(fl), _p(st), _p(gj))
+    common = (d.n_gates, _p(a["gc"]), _p(a["cap"]), d.n_cells, _p(a["k"]), d.n_slew, d.n_cap, _p(a["sa"]),
+              _p(a["ca"]), _p(a["lut"]), _p(a["leak"]), float(d.vdd_V), t.pin_init.shape[0], _p(a["pp"]),
+              _p(a["pi"]), _p(a["et"]), _p(a["ev"]), _p(a["es"]), int(t.t_clk), int(t.t_max), float(t.tick_s),
+              int(gate_lo), int(gate_hi))
+    if threads > 1:
+        rc = lib().pa_oracle_run_mt(*common, int(threads), C.byref(tot), _p(wave), _p(ce), _p(cg), _p(fl), _p(st),
+                                    _p(gj))
+    else:
+        rc = lib().pa_oracle_run(*common, C.byref(tot), _p(wave), _p(ce), _p(cg), _p(fl), _p(st), _p(gj))
     if rc != 0:
         raise OracleError(f"oracle rejected the input (code {rc})")
     out = {f: getattr(tot, f) for f, _ in Totals._fields_}

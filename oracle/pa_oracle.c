@@ -60,8 +60,16 @@
  *     fp32 and are widened to fp64 before any arithmetic.
  *
  * Every total and every bin is a Neumaier-compensated fp64 sum.
+ *
+ * pa_oracle_run_mt walks the same gates with the same per-gate code on host
+ * threads: each thread takes a contiguous gate range with its own bins,
+ * totals and counts, and the ranges are merged in order afterwards (again
+ * with compensated sums).  Gates are independent apart from these shared
+ * sums, so the result is the single-threaded one up to the order of fp64
+ * additions; integer outputs are identical.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -161,90 +169,59 @@ static int valid_events(int64_t n_pins, const int64_t *pin_ptr, const uint8_t *p
 
 /* ------------------------------------------------------------- the run -- */
 
+/* What every gate walk reads (shared, read-only). */
 typedef struct {
   int32_t n_slew, n_cap;
-  const double *slew_axis, *cap_axis, *lut, *leak;
-  int64_t *lut_base, *leak_base;  /* per cell */
+  const int32_t *gate_cell, *cell_n_in;
+  const double *gate_cap, *slew_axis, *cap_axis, *lut, *leak;
+  const int64_t *pin_base, *lut_base, *leak_base; /* per gate / per cell */
+  const int64_t *pin_ptr, *evt_t;
+  const uint8_t *pin_init, *evt_val;
+  const float *evt_slew;
   double vdd, tick_s;
   int64_t T, t_max, n_cyc;
+} run_in;
+
+/* What a gate walk adds to: the waveform bins, the totals and the per-cycle
+ * counts of the gates it walks (one set per thread), plus the current gate's
+ * own share. */
+typedef struct {
   nsum *wave;
   nsum e_int, e_sw, e_gl, e_leak;
   uint64_t *cyc_events, *cyc_glitches;
   uint64_t n_events, n_glitches;
-  nsum g_int, g_sw, g_gl, g_leak; /* the current gate's share */
-} run_ctx;
+  nsum g_int, g_sw, g_gl, g_leak;
+} run_acc;
 
 /* Leakage of the interval [a, b) at constant power p (paper, Sec. 2.4.2,
  * Eq. 4): energy p * (b - a) * tick_s, added to every overlapped cycle bin in
  * proportion to the overlap. */
-static void leak_interval(run_ctx *R, double p, int64_t a, int64_t b) {
+static void leak_interval(const run_in *I, run_acc *R, double p, int64_t a, int64_t b) {
   if (b <= a) return;
-  nadd(&R->e_leak, p * (double)(b - a) * R->tick_s);
-  nadd(&R->g_leak, p * (double)(b - a) * R->tick_s);
-  int64_t c_lo = a / R->T;
-  int64_t c_hi = (b + R->T - 1) / R->T; /* exclusive */
+  nadd(&R->e_leak, p * (double)(b - a) * I->tick_s);
+  nadd(&R->g_leak, p * (double)(b - a) * I->tick_s);
+  int64_t c_lo = a / I->T;
+  int64_t c_hi = (b + I->T - 1) / I->T; /* exclusive */
   for (int64_t c = c_lo; c < c_hi; ++c) {
-    int64_t lo = a > c * R->T ? a : c * R->T;
-    int64_t hi = b < (c + 1) * R->T ? b : (c + 1) * R->T;
-    if (hi > lo) nadd(&R->wave[c], p * (double)(hi - lo) * R->tick_s);
+    int64_t lo = a > c * I->T ? a : c * I->T;
+    int64_t hi = b < (c + 1) * I->T ? b : (c + 1) * I->T;
+    if (hi > lo) nadd(&R->wave[c], p * (double)(hi - lo) * I->tick_s);
   }
 }
 
-int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_cap_F, int32_t n_cells,
-                  const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap, const double *slew_axis,
-                  const double *cap_axis, const double *lut_J, const double *leak_W, double vdd_V,
-                  int64_t n_pins, const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t,
-                  const uint8_t *evt_val, const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s,
-                  int64_t gate_lo, int64_t gate_hi, pa_oracle_totals *out, double *wave_J,
-                  uint64_t *cyc_events, uint64_t *cyc_glitches, uint8_t *evt_glitch,
-                  uint8_t *evt_state_before, double *gate_J) {
-  if (!out || !wave_J || !cyc_events || !cyc_glitches) return PA_ORACLE_EARG;
-  int rc = valid_design(n_gates, gate_cell, gate_cap_F, n_cells, cell_n_in, n_slew, n_cap, slew_axis, cap_axis);
-  if (rc) return rc;
-  rc = valid_events(n_pins, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk, t_max, tick_s);
-  if (rc) return rc;
-  if (gate_lo < 0 || gate_hi > n_gates || gate_lo > gate_hi) return PA_ORACLE_EARG;
-
-  /* gate-major pins: gate g owns k_g input pins followed by one output pin */
-  int64_t *pin_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_gates + 1));
-  int64_t *lut_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_cells);
-  int64_t *leak_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_cells);
-  run_ctx R;
-  memset(&R, 0, sizeof R);
-  R.n_cyc = pa_oracle_n_cycles(t_clk, t_max);
-  R.wave = (nsum *)calloc((size_t)R.n_cyc, sizeof(nsum));
-  if (!pin_base || !lut_base || !leak_base || !R.wave) {
-    free(pin_base); free(lut_base); free(leak_base); free(R.wave);
-    return PA_ORACLE_ENOMEM;
-  }
-  pin_base[0] = 0;
-  for (int64_t g = 0; g < n_gates; ++g) pin_base[g + 1] = pin_base[g] + cell_n_in[gate_cell[g]] + 1;
-  if (pin_base[n_gates] != n_pins) {
-    free(pin_base); free(lut_base); free(leak_base); free(R.wave);
-    return PA_ORACLE_EDATA;
-  }
-  int64_t lb = 0, kb = 0;
-  for (int32_t c = 0; c < n_cells; ++c) {
-    int64_t k = cell_n_in[c];
-    lut_base[c] = lb;
-    leak_base[c] = kb;
-    lb += ((int64_t)1 << k) * k * n_slew * n_cap;
-    kb += (int64_t)1 << k;
-  }
-  R.n_slew = n_slew; R.n_cap = n_cap;
-  R.slew_axis = slew_axis; R.cap_axis = cap_axis; R.lut = lut_J; R.leak = leak_W;
-  R.lut_base = lut_base; R.leak_base = leak_base;
-  R.vdd = vdd_V; R.tick_s = tick_s; R.T = t_clk; R.t_max = t_max;
-  memset(cyc_events, 0, sizeof(uint64_t) * (size_t)R.n_cyc);
-  memset(cyc_glitches, 0, sizeof(uint64_t) * (size_t)R.n_cyc);
-  R.cyc_events = cyc_events;
-  R.cyc_glitches = cyc_glitches;
-
-  for (int64_t g = gate_lo; g < gate_hi; ++g) {
-    const int32_t cell = gate_cell[g];
-    const int k = cell_n_in[cell];
-    const double cap = gate_cap_F[g];
-    const int64_t p0 = pin_base[g];
+/* Walk gates [g_lo, g_hi) one after the other, each in time order. */
+static void walk_gates(const run_in *I, run_acc *R, int64_t g_lo, int64_t g_hi, uint8_t *evt_glitch,
+                       uint8_t *evt_state_before, double *gate_J) {
+  const int64_t *pin_ptr = I->pin_ptr, *evt_t = I->evt_t;
+  const uint8_t *pin_init = I->pin_init, *evt_val = I->evt_val;
+  const float *evt_slew = I->evt_slew;
+  const int32_t n_slew = I->n_slew, n_cap = I->n_cap;
+  const double vdd_V = I->vdd;
+  for (int64_t g = g_lo; g < g_hi; ++g) {
+    const int32_t cell = I->gate_cell[g];
+    const int k = I->cell_n_in[cell];
+    const double cap = I->gate_cap[g];
+    const int64_t p0 = I->pin_base[g];
     int64_t cur[9], end[9], last_cyc[9], tprev[9];
     double sprev[9];
     uint8_t v[9];
@@ -258,13 +235,13 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
     }
     unsigned S = 0; /* state over input pins, pin 0 = LSB */
     for (int i = 0; i < k; ++i) S |= (unsigned)v[i] << i;
-    const double *cell_slew = slew_axis + (int64_t)cell * n_slew;
-    const double *cell_cap = cap_axis + (int64_t)cell * n_cap;
+    const double *cell_slew = I->slew_axis + (int64_t)cell * n_slew;
+    const double *cell_cap = I->cap_axis + (int64_t)cell * n_cap;
     int64_t t_last = 0;
-    memset(&R.g_int, 0, sizeof R.g_int);
-    memset(&R.g_sw, 0, sizeof R.g_sw);
-    memset(&R.g_gl, 0, sizeof R.g_gl);
-    memset(&R.g_leak, 0, sizeof R.g_leak);
+    memset(&R->g_int, 0, sizeof R->g_int);
+    memset(&R->g_sw, 0, sizeof R->g_sw);
+    memset(&R->g_gl, 0, sizeof R->g_gl);
+    memset(&R->g_leak, 0, sizeof R->g_leak);
 
     for (;;) {
       /* next distinct timestamp of the k-way merge (Sec. 2.4.2, Fig. 3) */
@@ -274,26 +251,26 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
       if (t == INT64_MAX) break;
 
       /* leakage of the interval that ends here, at the state held in it */
-      leak_interval(&R, leak_W[leak_base[cell] + S], t_last, t);
+      leak_interval(I, R, I->leak[I->leak_base[cell] + S], t_last, t);
 
       /* dynamic energy of every pin with an event at t (Fig. 7) */
       for (int i = 0; i <= k; ++i) {
         if (!(cur[i] < end[i] && evt_t[cur[i]] == t)) continue;
         const int64_t e = cur[i];
         const double slew = (double)evt_slew[e];
-        const int64_t cyc = t / R.T;
+        const int64_t cyc = t / I->T;
         double E;
         int is_int;
         if (i < k) { /* input pin: state-selected internal-power LUT (Fig. 2) */
-          const double *tab = lut_J + lut_base[cell] + ((int64_t)S * k + i) * n_slew * n_cap;
+          const double *tab = I->lut + I->lut_base[cell] + ((int64_t)S * k + i) * n_slew * n_cap;
           E = pa_oracle_bilerp(n_slew, n_cap, cell_slew, cell_cap, tab, slew, cap);
           is_int = 1;
         } else { /* output pin: Eq. 1 for a 0->1 event */
           E = evt_val[e] == 1 ? 0.5 * cap * vdd_V * vdd_V : 0.0;
           is_int = 0;
         }
-        cyc_events[cyc] += 1;
-        R.n_events += 1;
+        R->cyc_events[cyc] += 1;
+        R->n_events += 1;
         /* GlitchDetectUpdate: a second or later event of this pin in the
          * current clock cycle is a glitch (Sec. 2.4.1, Fig. 7) */
         const int glitch = (last_cyc[i] == cyc);
@@ -301,15 +278,15 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
           const double pw = (double)(t - tprev[i]);
           double r = pw / (0.5 * (slew + sprev[i])); /* Eq. 2 as read above */
           if (r > 1.0) r = 1.0;
-          nadd(&R.e_gl, r * E);
-          nadd(&R.g_gl, r * E);
-          nadd(&R.wave[cyc], r * E);
-          cyc_glitches[cyc] += 1;
-          R.n_glitches += 1;
+          nadd(&R->e_gl, r * E);
+          nadd(&R->g_gl, r * E);
+          nadd(&R->wave[cyc], r * E);
+          R->cyc_glitches[cyc] += 1;
+          R->n_glitches += 1;
         } else {
-          nadd(is_int ? &R.e_int : &R.e_sw, E);
-          nadd(is_int ? &R.g_int : &R.g_sw, E);
-          nadd(&R.wave[cyc], E);
+          nadd(is_int ? &R->e_int : &R->e_sw, E);
+          nadd(is_int ? &R->g_int : &R->g_sw, E);
+          nadd(&R->wave[cyc], E);
         }
         if (evt_glitch) evt_glitch[e] = (uint8_t)glitch;
         if (evt_state_before) evt_state_before[e] = (uint8_t)(i < k ? S : 0);
@@ -330,32 +307,218 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
       t_last = t;
     }
     /* leakage is always present: the last interval runs to t_max */
-    leak_interval(&R, leak_W[leak_base[cell] + S], t_last, t_max);
-    /* the gate's own energies (the per-gate output the paper ranks hotspots by, Sec. 5) */
+    leak_interval(I, R, I->leak[I->leak_base[cell] + S], t_last, I->t_max);
+    /* the gate's own energies (the per-gate output the paper ranks hotspots by,
+     * its spatial-accuracy evaluation: Table 3, Figs. 10-11) */
     if (gate_J) {
-      gate_J[4 * g + 0] = nval(&R.g_int);
-      gate_J[4 * g + 1] = nval(&R.g_sw);
-      gate_J[4 * g + 2] = nval(&R.g_gl);
-      gate_J[4 * g + 3] = nval(&R.g_leak);
+      gate_J[4 * g + 0] = nval(&R->g_int);
+      gate_J[4 * g + 1] = nval(&R->g_sw);
+      gate_J[4 * g + 2] = nval(&R->g_gl);
+      gate_J[4 * g + 3] = nval(&R->g_leak);
     }
   }
+}
 
-  for (int64_t c = 0; c < R.n_cyc; ++c) wave_J[c] = nval(&R.wave[c]);
-  const double window_s = (double)t_max * tick_s;
-  out->e_int_J = nval(&R.e_int);
-  out->e_sw_J = nval(&R.e_sw);
-  out->e_gl_J = nval(&R.e_gl);
-  out->e_leak_J = nval(&R.e_leak);
+/* Shared set-up of both entry points: validation and the per-gate / per-cell
+ * bases.  On success the caller owns the three arrays in *I. */
+static int set_up(run_in *I, int64_t n_gates, const int32_t *gate_cell, const double *gate_cap_F, int32_t n_cells,
+                  const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap, const double *slew_axis,
+                  const double *cap_axis, const double *lut_J, const double *leak_W, double vdd_V, int64_t n_pins,
+                  const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t, const uint8_t *evt_val,
+                  const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s, int64_t gate_lo,
+                  int64_t gate_hi) {
+  int rc = valid_design(n_gates, gate_cell, gate_cap_F, n_cells, cell_n_in, n_slew, n_cap, slew_axis, cap_axis);
+  if (rc) return rc;
+  rc = valid_events(n_pins, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk, t_max, tick_s);
+  if (rc) return rc;
+  if (gate_lo < 0 || gate_hi > n_gates || gate_lo > gate_hi) return PA_ORACLE_EARG;
+  memset(I, 0, sizeof *I);
+  /* gate-major pins: gate g owns k_g input pins followed by one output pin */
+  int64_t *pin_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)(n_gates + 1));
+  int64_t *lut_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_cells);
+  int64_t *leak_base = (int64_t *)malloc(sizeof(int64_t) * (size_t)n_cells);
+  if (!pin_base || !lut_base || !leak_base) {
+    free(pin_base); free(lut_base); free(leak_base);
+    return PA_ORACLE_ENOMEM;
+  }
+  pin_base[0] = 0;
+  for (int64_t g = 0; g < n_gates; ++g) pin_base[g + 1] = pin_base[g] + cell_n_in[gate_cell[g]] + 1;
+  if (pin_base[n_gates] != n_pins) {
+    free(pin_base); free(lut_base); free(leak_base);
+    return PA_ORACLE_EDATA;
+  }
+  int64_t lb = 0, kb = 0;
+  for (int32_t c = 0; c < n_cells; ++c) {
+    int64_t k = cell_n_in[c];
+    lut_base[c] = lb;
+    leak_base[c] = kb;
+    lb += ((int64_t)1 << k) * k * n_slew * n_cap;
+    kb += (int64_t)1 << k;
+  }
+  I->n_slew = n_slew; I->n_cap = n_cap;
+  I->gate_cell = gate_cell; I->cell_n_in = cell_n_in; I->gate_cap = gate_cap_F;
+  I->slew_axis = slew_axis; I->cap_axis = cap_axis; I->lut = lut_J; I->leak = leak_W;
+  I->pin_base = pin_base; I->lut_base = lut_base; I->leak_base = leak_base;
+  I->pin_ptr = pin_ptr; I->evt_t = evt_t; I->pin_init = pin_init; I->evt_val = evt_val; I->evt_slew = evt_slew;
+  I->vdd = vdd_V; I->tick_s = tick_s; I->T = t_clk; I->t_max = t_max;
+  I->n_cyc = pa_oracle_n_cycles(t_clk, t_max);
+  return 0;
+}
+
+static void free_in(run_in *I) {
+  free((void *)I->pin_base);
+  free((void *)I->lut_base);
+  free((void *)I->leak_base);
+}
+
+static void write_totals(const run_in *I, const run_acc *R, pa_oracle_totals *out) {
+  const double window_s = (double)I->t_max * I->tick_s;
+  out->e_int_J = nval(&R->e_int);
+  out->e_sw_J = nval(&R->e_sw);
+  out->e_gl_J = nval(&R->e_gl);
+  out->e_leak_J = nval(&R->e_leak);
   out->p_int_W = out->e_int_J / window_s; /* Eq. 3 */
   out->p_sw_W = out->e_sw_J / window_s;
   out->p_gl_W = out->e_gl_J / window_s;
   out->p_leak_W = out->e_leak_J / window_s;
-  out->n_events = R.n_events;
-  out->n_glitches = R.n_glitches;
-  out->n_cycles = R.n_cyc;
-  free(pin_base);
-  free(lut_base);
-  free(leak_base);
+  out->n_events = R->n_events;
+  out->n_glitches = R->n_glitches;
+  out->n_cycles = I->n_cyc;
+}
+
+int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_cap_F, int32_t n_cells,
+                  const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap, const double *slew_axis,
+                  const double *cap_axis, const double *lut_J, const double *leak_W, double vdd_V,
+                  int64_t n_pins, const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t,
+                  const uint8_t *evt_val, const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s,
+                  int64_t gate_lo, int64_t gate_hi, pa_oracle_totals *out, double *wave_J,
+                  uint64_t *cyc_events, uint64_t *cyc_glitches, uint8_t *evt_glitch,
+                  uint8_t *evt_state_before, double *gate_J) {
+  if (!out || !wave_J || !cyc_events || !cyc_glitches) return PA_ORACLE_EARG;
+  run_in I;
+  int rc = set_up(&I, n_gates, gate_cell, gate_cap_F, n_cells, cell_n_in, n_slew, n_cap, slew_axis, cap_axis, lut_J,
+                  leak_W, vdd_V, n_pins, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk, t_max, tick_s, gate_lo,
+                  gate_hi);
+  if (rc) return rc;
+  run_acc R;
+  memset(&R, 0, sizeof R);
+  R.wave = (nsum *)calloc((size_t)I.n_cyc, sizeof(nsum));
+  if (!R.wave) {
+    free_in(&I);
+    return PA_ORACLE_ENOMEM;
+  }
+  memset(cyc_events, 0, sizeof(uint64_t) * (size_t)I.n_cyc);
+  memset(cyc_glitches, 0, sizeof(uint64_t) * (size_t)I.n_cyc);
+  R.cyc_events = cyc_events;
+  R.cyc_glitches = cyc_glitches;
+  walk_gates(&I, &R, gate_lo, gate_hi, evt_glitch, evt_state_before, gate_J);
+  for (int64_t c = 0; c < I.n_cyc; ++c) wave_J[c] = nval(&R.wave[c]);
+  write_totals(&I, &R, out);
   free(R.wave);
+  free_in(&I);
   return 0;
+}
+
+/* ------------------------------------------------ the run on host threads -- */
+
+typedef struct {
+  const run_in *I;
+  run_acc R;
+  int64_t g_lo, g_hi;
+  uint8_t *evt_glitch, *evt_state_before;
+  double *gate_J;
+} shard;
+
+static void *shard_main(void *arg) {
+  shard *s = (shard *)arg;
+  walk_gates(s->I, &s->R, s->g_lo, s->g_hi, s->evt_glitch, s->evt_state_before, s->gate_J);
+  return NULL;
+}
+
+int pa_oracle_run_mt(int64_t n_gates, const int32_t *gate_cell, const double *gate_cap_F, int32_t n_cells,
+                     const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap, const double *slew_axis,
+                     const double *cap_axis, const double *lut_J, const double *leak_W, double vdd_V,
+                     int64_t n_pins, const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t,
+                     const uint8_t *evt_val, const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s,
+                     int64_t gate_lo, int64_t gate_hi, int32_t n_threads, pa_oracle_totals *out, double *wave_J,
+                     uint64_t *cyc_events, uint64_t *cyc_glitches, uint8_t *evt_glitch,
+                     uint8_t *evt_state_before, double *gate_J) {
+  if (!out || !wave_J || !cyc_events || !cyc_glitches || n_threads < 1 || n_threads > 1024) return PA_ORACLE_EARG;
+  run_in I;
+  int rc = set_up(&I, n_gates, gate_cell, gate_cap_F, n_cells, cell_n_in, n_slew, n_cap, slew_axis, cap_axis, lut_J,
+                  leak_W, vdd_V, n_pins, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk, t_max, tick_s, gate_lo,
+                  gate_hi);
+  if (rc) return rc;
+  const int64_t n = gate_hi - gate_lo;
+  if (n_threads > n) n_threads = n > 0 ? (int32_t)n : 1;
+  shard *sh = (shard *)calloc((size_t)n_threads, sizeof(shard));
+  pthread_t *th = (pthread_t *)calloc((size_t)n_threads, sizeof(pthread_t));
+  int ok = sh && th;
+  for (int32_t i = 0; ok && i < n_threads; ++i) {
+    sh[i].R.wave = (nsum *)calloc((size_t)I.n_cyc, sizeof(nsum));
+    sh[i].R.cyc_events = (uint64_t *)calloc((size_t)I.n_cyc, sizeof(uint64_t));
+    sh[i].R.cyc_glitches = (uint64_t *)calloc((size_t)I.n_cyc, sizeof(uint64_t));
+    ok = sh[i].R.wave && sh[i].R.cyc_events && sh[i].R.cyc_glitches;
+  }
+  if (ok) {
+    /* contiguous gate ranges of about equal work: a gate costs its events
+     * and, through its leakage intervals, every cycle of the window */
+    const int64_t *pb = I.pin_base;
+    double total = 0.0;
+    for (int64_t g = gate_lo; g < gate_hi; ++g) total += 32.0 * (double)(pin_ptr[pb[g + 1]] - pin_ptr[pb[g]]) + (double)I.n_cyc;
+    double acc = 0.0;
+    int64_t g = gate_lo;
+    for (int32_t i = 0; i < n_threads; ++i) {
+      sh[i].I = &I;
+      sh[i].evt_glitch = evt_glitch;
+      sh[i].evt_state_before = evt_state_before;
+      sh[i].gate_J = gate_J;
+      sh[i].g_lo = g;
+      const double goal = total * (double)(i + 1) / (double)n_threads;
+      while (g < gate_hi && (i == n_threads - 1 || acc < goal)) {
+        acc += 32.0 * (double)(pin_ptr[pb[g + 1]] - pin_ptr[pb[g]]) + (double)I.n_cyc;
+        ++g;
+      }
+      sh[i].g_hi = g;
+    }
+    int32_t started = 0;
+    for (; started < n_threads; ++started)
+      if (pthread_create(&th[started], NULL, shard_main, &sh[started]) != 0) break;
+    for (int32_t i = 0; i < started; ++i) pthread_join(th[i], NULL);
+    /* a thread that could not start: its gates run here */
+    for (int32_t i = started; i < n_threads; ++i) shard_main(&sh[i]);
+    /* merge in shard order: compensated sums of the shards' bins and totals */
+    run_acc M;
+    memset(&M, 0, sizeof M);
+    for (int64_t c = 0; c < I.n_cyc; ++c) {
+      nsum w = {0.0, 0.0};
+      uint64_t ne = 0, ng = 0;
+      for (int32_t i = 0; i < n_threads; ++i) {
+        nadd(&w, nval(&sh[i].R.wave[c]));
+        ne += sh[i].R.cyc_events[c];
+        ng += sh[i].R.cyc_glitches[c];
+      }
+      wave_J[c] = nval(&w);
+      cyc_events[c] = ne;
+      cyc_glitches[c] = ng;
+    }
+    for (int32_t i = 0; i < n_threads; ++i) {
+      nadd(&M.e_int, nval(&sh[i].R.e_int));
+      nadd(&M.e_sw, nval(&sh[i].R.e_sw));
+      nadd(&M.e_gl, nval(&sh[i].R.e_gl));
+      nadd(&M.e_leak, nval(&sh[i].R.e_leak));
+      M.n_events += sh[i].R.n_events;
+      M.n_glitches += sh[i].R.n_glitches;
+    }
+    write_totals(&I, &M, out);
+  }
+  for (int32_t i = 0; sh && i < n_threads; ++i) {
+    free(sh[i].R.wave);
+    free(sh[i].R.cyc_events);
+    free(sh[i].R.cyc_glitches);
+  }
+  free(sh);
+  free(th);
+  free_in(&I);
+  return ok ? 0 : PA_ORACLE_ENOMEM;
 }

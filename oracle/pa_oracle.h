@@ -53,6 +53,18 @@ int pa_oracle_run(int64_t n_gates, const int32_t *gate_cell, const double *gate_
                   uint64_t *cyc_events, uint64_t *cyc_glitches, uint8_t *evt_glitch,
                   uint8_t *evt_state_before, double *gate_J);
 
+/* The same run on n_threads host threads (1..1024): gates [gate_lo, gate_hi)
+ * are cut into contiguous ranges of about equal work, each walked by one
+ * thread into private bins, totals and counts, merged in range order. */
+int pa_oracle_run_mt(int64_t n_gates, const int32_t *gate_cell, const double *gate_cap_F, int32_t n_cells,
+                     const int32_t *cell_n_in, int32_t n_slew, int32_t n_cap, const double *slew_axis,
+                     const double *cap_axis, const double *lut_J, const double *leak_W, double vdd_V,
+                     int64_t n_pins, const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t,
+                     const uint8_t *evt_val, const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s,
+                     int64_t gate_lo, int64_t gate_hi, int32_t n_threads, pa_oracle_totals *out, double *wave_J,
+                     uint64_t *cyc_events, uint64_t *cyc_glitches, uint8_t *evt_glitch,
+                     uint8_t *evt_state_before, double *gate_J);
+
 #ifdef __cplusplus
 }
 #endif

@@ -234,6 +234,44 @@ def test_per_gate_sums_to_totals(oracle_lib, tiny_run):
     assert [sub[k] for k in ("e_int_J", "e_sw_J", "e_gl_J", "e_leak_J")] == gj[100].tolist()
 
 
+@pytest.mark.parametrize("threads", [1, 2, 7, 64])
+def test_threaded_oracle_equals_single_thread(oracle_lib, tiny_run, threads):
+    """The threaded driver (contiguous gate ranges on host threads, merged in
+    order) against the single-threaded walk: integer outputs, per-event
+    outputs and per-gate rows identical; totals and bins equal up to the
+    order of the fp64 additions.  Also on a gate sub-range, and with more
+    threads than gates."""
+    w, r = tiny_run
+    m = oracle_lib.run(w.design, w.trace, per_gate=True, threads=threads)
+    g1 = oracle_lib.run(w.design, w.trace, per_event=False, per_gate=True)["gate_J"]
+    for key in ("e_int_J", "e_sw_J", "e_gl_J", "e_leak_J", "p_int_W", "p_sw_W", "p_gl_W", "p_leak_W"):
+        assert _close(m[key], r[key], rel=1e-14), key
+    for key in ("n_events", "n_glitches", "n_cycles"):
+        assert m[key] == r[key], key
+    for key in ("cyc_events", "cyc_glitches", "evt_glitch", "evt_state_before"):
+        np.testing.assert_array_equal(m[key], r[key], err_msg=key)
+    np.testing.assert_allclose(m["wave_J"], r["wave_J"], rtol=1e-14, atol=0)
+    np.testing.assert_array_equal(m["gate_J"], g1)
+    a = oracle_lib.run(w.design, w.trace, 123, 321, per_event=False)
+    b = oracle_lib.run(w.design, w.trace, 123, 321, per_event=False, threads=threads)
+    np.testing.assert_array_equal(a["cyc_events"], b["cyc_events"])
+    np.testing.assert_allclose(a["wave_J"], b["wave_J"], rtol=1e-14, atol=0)
+    assert _close(a["e_leak_J"], b["e_leak_J"], rel=1e-14) and a["n_glitches"] == b["n_glitches"]
+    few = synth.subset_gates(w, 0, 3)
+    c = oracle_lib.run(few.design, few.trace, per_event=False)
+    d = oracle_lib.run(few.design, few.trace, per_event=False, threads=threads)
+    assert _close(c["e_int_J"], d["e_int_J"], rel=1e-14)
+    np.testing.assert_array_equal(c["cyc_glitches"], d["cyc_glitches"])
+
+
+def test_threaded_oracle_rejects_bad_input(oracle_lib):
+    des, tr = _small_random(31)
+    tt = tr.evt_t.copy()
+    tt[-1] = tr.t_max
+    with pytest.raises(Exception):
+        oracle_lib.run(des, dataclasses.replace(tr, evt_t=tt), threads=4)
+
+
 @pytest.mark.parametrize("m", [1, 3, 8])
 def test_contention_generator_and_glitch_count(oracle_lib, m):
     """The waveform-bin stress trace: every pin toggles exactly m times in
