@@ -36,14 +36,14 @@ class PowerAnalysis:
     output tensors."""
 
     def __init__(self, device: int = 0, stream=None, chunk_cycles: int = 0, grid_blocks: int = 0,
-                 time_kernels=0, fixed_window_cycles: int = 0, lut_lds_kib: int = 0):
+                 time_kernels=0, fixed_window_cycles: int = 0, lut_lds_kib: int = 0, device_mib_cap: int = 0):
         import torch
 
         self.device = torch.device("cuda", device)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         self.ctx = pa_create(device, stream, chunk_cycles, grid_blocks, time_kernels, fixed_window_cycles,
-                             lut_lds_kib)
+                             lut_lds_kib, device_mib_cap)
         self.n_cycles = 0
         self.n_events = 0
         self.n_gates = 0
@@ -104,6 +104,7 @@ class PowerAnalysis:
     def run(self, outputs: Optional[dict] = None, per_event: bool = False) -> dict:
         if outputs is None:
             outputs = self.alloc_outputs(per_event)
+        self._check_outputs(outputs)
         if "gate_J" in outputs:
             # per-gate energies (internal, switching, glitch, leakage) in a pass of their own
             tot = pa_run_gates(self.ctx, outputs["wave_J"], outputs["cyc_events"], outputs["cyc_glitches"],
@@ -112,6 +113,17 @@ class PowerAnalysis:
             tot = pa_run(self.ctx, outputs["wave_J"], outputs["cyc_events"], outputs["cyc_glitches"],
                          outputs.get("evt_glitch"), outputs.get("evt_state_before"))
         return dict(totals=tot, **outputs)
+
+    def _check_outputs(self, outputs: dict) -> None:
+        """Every output the pass writes must hold what the loaded data imply:
+        C cycles, E events, G x 4 gate rows (ValueError before any launch)."""
+        need = dict(wave_J=self.n_cycles, cyc_events=self.n_cycles, cyc_glitches=self.n_cycles,
+                    evt_glitch=self.n_events, evt_state_before=self.n_events, gate_J=4 * self.n_gates)
+        for key, t in outputs.items():
+            if key not in need:
+                raise ValueError(f"unknown output {key!r}")
+            if t is not None and int(t.numel()) < need[key]:
+                raise ValueError(f"{key}: {int(t.numel())} elements, needs at least {need[key]}")
 
     def run_text(self, text, t_clk: int, t_max: int, tick_s: float = 1e-15, segment_cycles: int = 0,
                  n_threads: int = 0, serial: bool = False) -> dict:

@@ -32,7 +32,7 @@ class PaError(RuntimeError):
 
 class pa_tunables(C.Structure):
     _fields_ = [("chunk_cycles", C.c_int32), ("grid_blocks", C.c_int32), ("time_kernels", C.c_int32),
-                ("fixed_window_cycles", C.c_int32), ("lut_lds_kib", C.c_int32)]
+                ("fixed_window_cycles", C.c_int32), ("lut_lds_kib", C.c_int32), ("device_mib_cap", C.c_int32)]
 
 
 class pa_totals(C.Structure):
@@ -57,7 +57,8 @@ class pa_info(C.Structure):
                 ("chunk_cycles", C.c_int32), ("n_chunks", C.c_int32), ("grid_blocks", C.c_int32),
                 ("block_threads", C.c_int32), ("batch_events", C.c_int32), ("max_segment_events", C.c_int32),
                 ("device_bytes", C.c_int64), ("kernel_ms", C.c_float * 4), ("n_windows", C.c_int64),
-                ("n_slots", C.c_int64), ("wave_steps_max", C.c_int32), ("wave_steps_mean", C.c_float)]
+                ("n_slots", C.c_int64), ("wave_steps_max", C.c_int32), ("wave_steps_mean", C.c_float),
+                ("tables_in_lds", C.c_int32)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_ if f != "kernel_ms"}
@@ -141,6 +142,41 @@ def _ptr(t, dtype, device=None, name="array"):
     return C.c_void_p(t.data_ptr())
 
 
+def _numel(t, name):
+    import torch
+
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    return int(t.numel())
+
+
+def _need(t, n: int, name: str, exact: bool = True) -> None:
+    """Size check before any pointer crosses the ABI: the library reads and
+    writes these arrays by the sizes the loaded design and events imply, so a
+    short array would be read or written out of bounds on the device."""
+    if t is None:
+        return
+    m = _numel(t, name)
+    if (m != n) if exact else (m < n):
+        raise ValueError(f"{name}: {m} elements, {'expected' if exact else 'needs at least'} {n}")
+
+
+def _design_sizes(cell_n_in, n_slew: int, n_cap: int):
+    """LUT and leakage entries the cell library needs: sum over cells of
+    2^k * k * n_slew * n_cap and of 2^k (k = input count, 1..8)."""
+    k = cell_n_in.detach().to("cpu").to(dtype=cell_n_in.dtype).tolist()
+    if any((not isinstance(x, int)) or x < 1 or x > 8 for x in k):
+        raise ValueError("cell_n_in: input counts must be 1..8")
+    return sum((1 << x) * x * n_slew * n_cap for x in k), sum(1 << x for x in k)
+
+
+def _outputs_for(ctx):
+    """(cycles, events, gates) of the context's loaded data."""
+    info = pa_info()
+    _check(lib().pa_get_info(ctx, C.byref(info)))
+    return int(info.n_cycles), int(info.n_events), int(info.n_gates)
+
+
 def _stream_handle(stream) -> C.c_void_p:
     if stream is None:
         return C.c_void_p(None)
@@ -150,8 +186,10 @@ def _stream_handle(stream) -> C.c_void_p:
 
 
 def pa_create(device: int = 0, stream=None, chunk_cycles: int = 0, grid_blocks: int = 0,
-              time_kernels=0, fixed_window_cycles: int = 0, lut_lds_kib: int = 0) -> C.c_void_p:
-    t = pa_tunables(chunk_cycles, grid_blocks, int(time_kernels), int(fixed_window_cycles), int(lut_lds_kib))
+              time_kernels=0, fixed_window_cycles: int = 0, lut_lds_kib: int = 0,
+              device_mib_cap: int = 0) -> C.c_void_p:
+    t = pa_tunables(chunk_cycles, grid_blocks, int(time_kernels), int(fixed_window_cycles), int(lut_lds_kib),
+                    int(device_mib_cap))
     h = C.c_void_p()
     _check(lib().pa_create(C.byref(h), int(device), _stream_handle(stream), C.byref(t)))
     return h
@@ -178,6 +216,14 @@ def pa_load_design(ctx, gate_cell, gate_cap_F, cell_n_in, n_slew: int, n_cap: in
                    leak_W, vdd_V: float) -> None:
     import torch
 
+    G, nc = _numel(gate_cell, "gate_cell"), _numel(cell_n_in, "cell_n_in")
+    _need(gate_cap_F, G, "gate_cap_F")
+    _need(slew_axis, nc * int(n_slew), "slew_axis")
+    _need(cap_axis, nc * int(n_cap), "cap_axis")
+    if nc and 2 <= int(n_slew) <= 16 and 2 <= int(n_cap) <= 16:
+        n_lut, n_leak = _design_sizes(cell_n_in, int(n_slew), int(n_cap))
+        _need(lut_J, n_lut, "lut_J")
+        _need(leak_W, n_leak, "leak_W")
     _check(lib().pa_load_design(ctx, int(gate_cell.numel()), _ptr(gate_cell, torch.int32, name="gate_cell"),
                                 _ptr(gate_cap_F, torch.float64, name="gate_cap_F"), int(cell_n_in.numel()),
                                 _ptr(cell_n_in, torch.int32, name="cell_n_in"), int(n_slew), int(n_cap),
@@ -191,6 +237,10 @@ def pa_load_events(ctx, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk: int,
                    tick_s: float) -> None:
     import torch
 
+    P, E = _numel(pin_init, "pin_init"), _numel(evt_t, "evt_t")
+    _need(pin_ptr, P + 1, "pin_ptr")
+    _need(evt_val, E, "evt_val")
+    _need(evt_slew, E, "evt_slew")
     _check(lib().pa_load_events(ctx, int(pin_init.numel()), int(evt_t.numel()),
                                 _ptr(pin_ptr, torch.int64, name="pin_ptr"), _ptr(pin_init, torch.uint8, name="pin_init"),
                                 _ptr(evt_t, torch.int64, name="evt_t"), _ptr(evt_val, torch.uint8, name="evt_val"),
@@ -201,6 +251,11 @@ def pa_load_events(ctx, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk: int,
 def pa_run(ctx, wave_J, cyc_events, cyc_glitches, evt_glitch=None, evt_state_before=None) -> dict:
     import torch
 
+    Cn, E, _ = _outputs_for(ctx)
+    for t, name in ((wave_J, "wave_J"), (cyc_events, "cyc_events"), (cyc_glitches, "cyc_glitches")):
+        _need(t, Cn, name, exact=False)
+    for t, name in ((evt_glitch, "evt_glitch"), (evt_state_before, "evt_state_before")):
+        _need(t, E, name, exact=False)
     tot = pa_totals()
     _check(lib().pa_run(ctx, C.byref(tot), _ptr(wave_J, torch.float64, name="wave_J"),
                         _ptr(cyc_events, torch.uint64, name="cyc_events"),
@@ -213,6 +268,10 @@ def pa_run(ctx, wave_J, cyc_events, cyc_glitches, evt_glitch=None, evt_state_bef
 def pa_run_gates(ctx, wave_J, cyc_events, cyc_glitches, gate_J) -> dict:
     import torch
 
+    Cn, _, G = _outputs_for(ctx)
+    for t, name in ((wave_J, "wave_J"), (cyc_events, "cyc_events"), (cyc_glitches, "cyc_glitches")):
+        _need(t, Cn, name, exact=False)
+    _need(gate_J, 4 * G, "gate_J", exact=False)
     tot = pa_totals()
     _check(lib().pa_run_gates(ctx, C.byref(tot), _ptr(wave_J, torch.float64, name="wave_J"),
                               _ptr(cyc_events, torch.uint64, name="cyc_events"),
@@ -271,6 +330,10 @@ def pa_run_text(ctx, text, t_clk: int, t_max: int, tick_s: float, wave_J, cyc_ev
     """Totals and packing statistics of the text's power analysis (outputs written to the device tensors)."""
     import torch
 
+    if int(t_clk) >= 1 and int(t_max) >= 1:
+        Cn = -(-int(t_max) // int(t_clk))
+        for t, name in ((wave_J, "wave_J"), (cyc_events, "cyc_events"), (cyc_glitches, "cyc_glitches")):
+            _need(t, Cn, name, exact=False)
     ptr, n, keep = _text_ptr(text)
     opts = pa_text_opts(int(segment_cycles), int(n_threads), int(bool(serial)), 0)
     tot, st = pa_totals(), pa_text_stats()

@@ -27,6 +27,22 @@ namespace {
 
 thread_local std::string g_err;
 
+// Device-memory accounting of the context whose call this thread is serving:
+// every library buffer adds its bytes while it lives; with a cap set
+// (pa_tunables.device_mib_cap, a debug knob), an allocation that would take
+// the live total past it fails as if the device were out of memory.
+struct MemBudget {
+  int64_t live = 0;
+  int64_t cap = 0;  // 0 = none
+};
+thread_local MemBudget *g_budget = nullptr;
+
+struct BudgetScope {  // RAII: the calls of one API entry are charged to its context
+  MemBudget *prev;
+  explicit BudgetScope(MemBudget *b) : prev(g_budget) { g_budget = b; }
+  ~BudgetScope() { g_budget = prev; }
+};
+
 int fail(int code, const char *fmt, ...) {
   char buf[512];
   va_list ap;
@@ -41,26 +57,45 @@ int fail(int code, const char *fmt, ...) {
 struct DBuf {
   void *p = nullptr;
   size_t bytes = 0;
+  MemBudget *budget = nullptr;  // the context charged for this buffer
   DBuf() = default;
   DBuf(const DBuf &) = delete;
   DBuf &operator=(const DBuf &) = delete;
-  DBuf(DBuf &&o) noexcept : p(o.p), bytes(o.bytes) { o.p = nullptr; o.bytes = 0; }
+  DBuf(DBuf &&o) noexcept : p(o.p), bytes(o.bytes), budget(o.budget) {
+    o.p = nullptr;
+    o.bytes = 0;
+    o.budget = nullptr;
+  }
   DBuf &operator=(DBuf &&o) noexcept {
-    if (this != &o) { reset(); p = o.p; bytes = o.bytes; o.p = nullptr; o.bytes = 0; }
+    if (this != &o) {
+      reset();
+      p = o.p;
+      bytes = o.bytes;
+      budget = o.budget;
+      o.p = nullptr;
+      o.bytes = 0;
+      o.budget = nullptr;
+    }
     return *this;
   }
   ~DBuf() { reset(); }
   void reset() {
     if (p) (void)hipFree(p);
+    if (budget) budget->live -= (int64_t)bytes;
     p = nullptr;
     bytes = 0;
+    budget = nullptr;
   }
   hipError_t alloc(size_t n) {
     reset();
     if (n == 0) n = 16;
+    MemBudget *b = g_budget;
+    if (b && b->cap > 0 && b->live + (int64_t)n > b->cap) return hipErrorOutOfMemory;
     hipError_t e = hipMalloc(&p, n);
     if (e != hipSuccess) { p = nullptr; return e; }
     bytes = n;
+    budget = b;
+    if (b) b->live += (int64_t)n;
     return hipSuccess;
   }
   // at least n bytes, keeping the allocation when it is large enough
@@ -149,6 +184,7 @@ struct LoadScratch {
 }  // namespace
 
 struct pa_ctx {
+  MemBudget mem;  // declared first: destroyed after every buffer below
   int device = 0;
   hipStream_t stream = nullptr;
   pa_tunables tun{};
@@ -185,6 +221,7 @@ int pa_create(pa_ctx **out, int hip_device, void *hip_stream, const pa_tunables 
   *out = nullptr;
   if (t && (t->time_kernels < 0 || t->time_kernels > 2))
     return fail(PA_EINVAL, "pa_create: time_kernels must be 0, 1 or 2");
+  if (t && t->device_mib_cap < 0) return fail(PA_EINVAL, "pa_create: device_mib_cap must be >= 0");
   int ndev = 0;
   HIPCHK(hipGetDeviceCount(&ndev));
   if (hip_device < 0 || hip_device >= ndev) return fail(PA_EINVAL, "pa_create: device %d of %d", hip_device, ndev);
@@ -196,6 +233,7 @@ int pa_create(pa_ctx **out, int hip_device, void *hip_stream, const pa_tunables 
   c->device = hip_device;
   c->stream = (hipStream_t)hip_stream;
   if (t) c->tun = *t;
+  c->mem.cap = (int64_t)c->tun.device_mib_cap << 20;
   c->n_cu = prop.multiProcessorCount;
   if (hipHostMalloc((void **)&c->h_res, 16 * sizeof(double), hipHostMallocDefault) != hipSuccess) {
     delete c;
@@ -246,6 +284,7 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   if (!cell_n_in || !slew_axis || !cap_axis || !lut_J || !leak_W || (n_gates > 0 && (!gate_cell || !gate_cap_F)))
     return fail(PA_EINVAL, "pa_load_design: NULL array");
   if (!std::isfinite(vdd_V)) return fail(PA_EINVAL, "pa_load_design: Vdd not finite");
+  BudgetScope bs(&c->mem);
   HIPCHK(hipSetDevice(c->device));
   hipStream_t s = c->stream;
 
@@ -541,6 +580,7 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
 int pa_load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr, const uint8_t *pin_init,
                    const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_clk,
                    int64_t t_max, double tick_s) {
+  BudgetScope bs(c ? &c->mem : nullptr);
   const int rc = load_events(c, n_pins, n_events, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_clk, t_max, tick_s);
   if (c && !c->keep_load_buffers) {
     (void)hipSetDevice(c->device);
@@ -826,6 +866,7 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   if (!c) return fail(PA_EINVAL, "pa_run: NULL context");
   if (!c->has_design || !c->has_events) return fail(PA_ESTATE, "pa_run: design and events must be loaded first");
   if (!out || !wave_J || !cyc_events || !cyc_glitches) return fail(PA_EINVAL, "pa_run: NULL output");
+  BudgetScope bs(&c->mem);
   HIPCHK(hipSetDevice(c->device));
   return run_pass(c, out, wave_J, cyc_events, cyc_glitches, evt_glitch, evt_state_before, nullptr);
 }
@@ -837,6 +878,7 @@ int pa_run_gates(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events
     return fail(PA_ESTATE, "pa_run_gates: design and events must be loaded first");
   if (!out || !wave_J || !cyc_events || !cyc_glitches || (!gate_J && c->d.G > 0))
     return fail(PA_EINVAL, "pa_run_gates: NULL output");
+  BudgetScope bs(&c->mem);
   HIPCHK(hipSetDevice(c->device));
   return run_pass(c, out, wave_J, cyc_events, cyc_glitches, nullptr, nullptr, gate_J);
 }
@@ -894,6 +936,11 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
   info->n_slots = c->has_events ? c->ev.slots : 0;
   info->wave_steps_max = c->has_events ? c->ev.wave_steps_max : 0;
   info->wave_steps_mean = c->has_events ? c->ev.wave_steps_mean : 0.f;
+  info->tables_in_lds = (c->has_design && c->has_events &&
+                         pa::pass_cells_fit_lds(c->ev.Cc, c->d.n_cells, c->d.n_slew, c->d.n_cap, c->d.n_thr,
+                                                c->d.n_leak, c->d.kmax))
+                            ? 1
+                            : 0;
   return PA_OK;
 }
 
@@ -999,6 +1046,7 @@ int pa_run_text(pa_ctx *c, const char *text, int64_t text_len, int64_t t_clk, in
     return fail(PA_EINVAL, "pa_run_text: bad options");
   const int64_t S = o && o->segment_cycles > 0 ? o->segment_cycles : 1024;
   const bool serial = o && o->serial == 1;
+  BudgetScope bs(&c->mem);
   HIPCHK(hipSetDevice(c->device));
   // the segments' loads reuse one another's buffers; they go when the text is done
   struct HoldLoadBuffers {
@@ -1106,6 +1154,7 @@ int pa_run_text(pa_ctx *c, const char *text, int64_t text_len, int64_t t_clk, in
     int grc = PA_OK;
     std::string gmsg;
     std::thread gpu([&] {
+      BudgetScope gbs(&c->mem);
       if (hipSetDevice(c->device) != hipSuccess) {
         std::lock_guard<std::mutex> g(mu);
         stop = true;

@@ -3,7 +3,7 @@
 //
 // The paper's GPU flow packs events on the CPU and overlaps that with the
 // GPU's power computation ("GPU-Accelerated Gate-Level Time-Based Power
-// Analysis via Event-Density-Aware Partitioning and Kernel Fusion", Sec. 5,
+// Analysis via Event-Density-Aware Partitioning and Kernel Fusion",
 // end-to-end runtime breakdown, Fig. 13).  The text format is described in
 // include/pa.h (pa_pack_text).  Everything here is plain C++ (no HIP).
 #pragma once

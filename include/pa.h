@@ -74,6 +74,10 @@ typedef struct {
                              events use most: 0 = all the LDS its bins and cell tables leave;
                              n > 0 = at most n KiB; negative = none (every LUT read goes
                              through the caches) */
+  int32_t device_mib_cap; /* debug: 0 = no cap; n > 0 = the context's device buffers may hold
+                             at most n MiB together, and an allocation past that fails with
+                             PA_ENOMEM as a real out-of-memory would (for testing the
+                             out-of-memory paths; a failed load keeps the loaded data) */
 } pa_tunables;
 
 /* Create a context on HIP device `hip_device`, launching on `hip_stream`
@@ -151,7 +155,7 @@ int pa_run(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, ui
            uint8_t *evt_glitch, uint8_t *evt_state_before);
 
 /* pa_run plus every gate's own energies, the per-gate power the paper ranks
- * hotspots by (its spatial-accuracy evaluation, Sec. 5):
+ * hotspots by (its spatial-accuracy evaluation, Fig. 10, Table 3):
  *   gate_J[G][4]   device: per gate (caller's order) the internal, switching,
  *                  glitch and leakage energy over [0, t_max), J; overwritten.
  * The gate rows add up to the totals (up to fp64 summation order).  This
@@ -186,13 +190,16 @@ typedef struct {
                                  that pad windows to even lengths and lanes to their wave's longest */
   int32_t wave_steps_max;     /* steps (event pairs) of the pass's longest wave */
   float wave_steps_mean;      /* steps of a wave, averaged over the waves with work */
+  int32_t tables_in_lds;      /* 1: every block of the pass stages the per-cell tables (axes,
+                                 slew thresholds, leakage) in LDS; 0: they are read through the
+                                 caches (libraries too large for the LDS next to the bins) */
 } pa_info;
 int pa_get_info(pa_ctx *ctx, pa_info *info);
 
 /* ---- Activity text: host-side event packing, overlapped with the GPU ----
  * The paper's GPU flow packs the events of its activity files on host
  * threads while the GPU computes, so that packing hides behind the power
- * computation (its Sec. 5, end-to-end runtime breakdown, Fig. 13).  The text
+ * computation (its end-to-end runtime breakdown, Fig. 13).  The text
  * read here is a subset of VCD with one slew per value change (the paper
  * does not print its input format; slews come from timing analysis there):
  *   - "$var <type> 1 <id> <name> [<more>] $end" declares one variable per

@@ -6,8 +6,8 @@ import this module; the product library never loads it.
 
 The paper's GPU flow packs the events of its activity files on the host
 while the GPU computes ("GPU-Accelerated Gate-Level Time-Based Power Analysis
-via Event-Density-Aware Partitioning and Kernel Fusion", Sec. 5, end-to-end
-runtime breakdown, Fig. 13).  It does not print the file format, so the
+via Event-Density-Aware Partitioning and Kernel Fusion", end-to-end runtime
+breakdown, Fig. 13).  It does not print the file format, so the
 format is a reading: a subset of VCD with one slew per value change,
 
     $var <type> 1 <id> <name> [...] $end    one pin, pins in declaration order

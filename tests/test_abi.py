@@ -1,6 +1,7 @@
-"""CPU checks of the C-ABI library: it loads, exports every entry point that
-include/pa.h declares, and its exact cycle division (Granlund-Montgomery
-multiply-high) equals plain integer division bit for bit."""
+"""CPU checks of the C-ABI library: it loads and exports every entry point
+that include/pa.h declares, the Python binding keeps the header's names, a
+context cannot be created without a GPU, and the fp32 slew thresholds the
+pass compares against pick the same LUT segment as fp64 compares."""
 import ctypes
 import os
 import re

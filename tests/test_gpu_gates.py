@@ -1,8 +1,8 @@
 """GPU per-gate power output (pa_run_gates) against the oracle's per-gate
 energies, and hotspot ranking on the full-size workloads.
 
-The paper ranks gates by power to judge spatial accuracy (its Sec. 5: rank
-correlation and the overlap of the top hotspots).  Here the reference ranking
+The paper ranks gates by power to judge spatial accuracy (its Fig. 10 and
+Table 3: rank correlation and the overlap of the top hotspots).  Here the reference ranking
 is the oracle's; both sides compute every gate's internal, switching, glitch
 and leakage energy in fp64, so the per-gate values must agree within the
 energy bar (1e-9 relative) and the rankings must coincide.
@@ -104,8 +104,9 @@ def test_hotspot_ranking_full_size(name):
 
 
 def test_large_full_size_sampled():
-    """The 200M-event, 2M-gate workload at full size, in the pass the bench
-    times, checked where a full oracle run would take too long:
+    """The 200M-event, 2M-gate workload at full size through pa_run_gates
+    (the diagnostic kernel template, which also adds every gate's own
+    energies), checked against definitions and a sample of gates:
       - per-cycle event counts against a histogram of the event cycles;
       - glitch flags per cycle against the definition (an event whose pin has
         an earlier event in the same clock cycle);

@@ -2,7 +2,7 @@
 text segment by segment while the GPU loads and computes the previous
 segment (the paper's CPU-side event packing overlapped with the GPU,
 "GPU-Accelerated Gate-Level Time-Based Power Analysis via Event-Density-
-Aware Partitioning and Kernel Fusion", Sec. 5, Fig. 13).
+Aware Partitioning and Kernel Fusion", Fig. 13).
 
 The oracle side reads the same text with the plain reader (oracle.vcd_text)
 and runs the CPU oracle on the result; the totals, waveform and counts must

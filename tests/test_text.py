@@ -3,7 +3,7 @@ packer (pa_pack_text, host code only, no GPU) against it.
 
 The paper packs the events of its activity files on host threads while the
 GPU computes ("GPU-Accelerated Gate-Level Time-Based Power Analysis via
-Event-Density-Aware Partitioning and Kernel Fusion", Sec. 5, Fig. 13).  The
+Event-Density-Aware Partitioning and Kernel Fusion", Fig. 13).  The
 text here is the library's reading of such files: a VCD subset with one slew
 per value change.  What pins the oracle reader:
   - a hand-worked golden text (tests/golden/text_small.*);

@@ -7,8 +7,8 @@ and benchmark take their inputs from.
 
 The workloads stand in for the designs and activity traces that "GPU-
 Accelerated Gate-Level Time-Based Power Analysis via Event-Density-Aware
-Partitioning and Kernel Fusion" (arXiv 2609.05960) evaluates on (its Sec. 5
-benchmarks, which are not available here).  Their shapes follow the paper's
+Partitioning and Kernel Fusion" (arXiv 2609.05960) evaluates on (the benchmark
+designs and traces of its Table 2, which are not available here).  Their shapes follow the paper's
 problem statement: gates with k input pins and one output pin, per-pin
 sorted event streams (Sec. 2.4.1/2.4.2), state-indexed internal-power LUTs
 per input pin and state-indexed leakage (Figs. 2-3), and the skewed per-gate
@@ -323,7 +323,8 @@ def contention(m: int, seed: int = 0, G: int = 32, C: int = 100_000) -> Workload
     76.8M events, 96 m events in every waveform bin).  Every event of a cycle lands in the same waveform bin and
     every toggle after a pin's first in a cycle is a glitch, so this is the
     worst case for the per-bin accumulation (the paper's atomic stress test
-    on high-activity synthetic waveforms, Sec. 5)."""
+    on high-activity synthetic waveforms, in its evaluation of the
+    waveform-bin atomic overhead)."""
     rng = np.random.default_rng(seed)
     lib = make_library(rng, [2])
     des = assign_gates(rng, lib, np.full(G, 2, np.int64), 1.0, 50.0)

@@ -5,7 +5,7 @@ into the text that the library's event packer reads, and holds none of the
 power arithmetic.  The paper's GPU flow packs events on the host from
 activity files while the GPU computes ("GPU-Accelerated Gate-Level Time-
 Based Power Analysis via Event-Density-Aware Partitioning and Kernel Fusion",
-Sec. 5, end-to-end runtime breakdown, Fig. 13); its activity files are not
+end-to-end runtime breakdown, Fig. 13); its activity files are not
 available, so this text stands in for them.
 
 Format (a subset of VCD, plus one slew per value change):
