@@ -163,10 +163,12 @@ def _need(t, n: int, name: str, exact: bool = True) -> None:
 
 def _design_sizes(cell_n_in, n_slew: int, n_cap: int):
     """LUT and leakage entries the cell library needs: sum over cells of
-    2^k * k * n_slew * n_cap and of 2^k (k = input count, 1..8)."""
-    k = cell_n_in.detach().to("cpu").to(dtype=cell_n_in.dtype).tolist()
+    2^k * k * n_slew * n_cap and of 2^k (k = input count, 1..8).  None when
+    an input count is outside 1..8: the library then rejects the design
+    (PA_EDATA) before it reads any table."""
+    k = cell_n_in.detach().to("cpu").tolist()
     if any((not isinstance(x, int)) or x < 1 or x > 8 for x in k):
-        raise ValueError("cell_n_in: input counts must be 1..8")
+        return None
     return sum((1 << x) * x * n_slew * n_cap for x in k), sum(1 << x for x in k)
 
 
@@ -221,9 +223,10 @@ def pa_load_design(ctx, gate_cell, gate_cap_F, cell_n_in, n_slew: int, n_cap: in
     _need(slew_axis, nc * int(n_slew), "slew_axis")
     _need(cap_axis, nc * int(n_cap), "cap_axis")
     if nc and 2 <= int(n_slew) <= 16 and 2 <= int(n_cap) <= 16:
-        n_lut, n_leak = _design_sizes(cell_n_in, int(n_slew), int(n_cap))
-        _need(lut_J, n_lut, "lut_J")
-        _need(leak_W, n_leak, "leak_W")
+        sizes = _design_sizes(cell_n_in, int(n_slew), int(n_cap))
+        if sizes is not None:
+            _need(lut_J, sizes[0], "lut_J")
+            _need(leak_W, sizes[1], "leak_W")
     _check(lib().pa_load_design(ctx, int(gate_cell.numel()), _ptr(gate_cell, torch.int32, name="gate_cell"),
                                 _ptr(gate_cap_F, torch.float64, name="gate_cap_F"), int(cell_n_in.numel()),
                                 _ptr(cell_n_in, torch.int32, name="cell_n_in"), int(n_slew), int(n_cap),
