@@ -15,8 +15,14 @@ host side of each call).  The fused kernel's algorithmic bytes per launch
 (12 B per event, 9 B per pin, 12 B per gate, the tables once) over its own
 device time give roofline.achieved.
 
-The CPU baseline is the oracle (single-threaded C) timed on this host on the
-same workload.
+"configs" repeats the measurement for the other workloads (Tiny, Skewed,
+Glitch-heavy and the 200M-event one), each loaded, warmed up and timed the
+same way; the headline value stays the 10M-event workload's.
+
+The CPU baseline is the C oracle timed on this host on the same workload:
+whole passes on one core, then on all the cores this process may use (at
+most 16), the gates cut into contiguous ranges, one per thread; the line
+gives both, the thread count and the CPU model.
 """
 import argparse
 import json
@@ -182,7 +188,9 @@ def main():
     ap.add_argument("--grid-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--quick", action="store_true", help="no 2 s clock warm-up and no CPU baseline (profiling runs)")
+    ap.add_argument("--quick", action="store_true",
+                    help="no 2 s clock warm-up, no CPU baseline and no other configurations (profiling runs)")
+    ap.add_argument("--no-configs", action="store_true", help="time the chosen workload only")
     ap.add_argument("--window-ablation", action="store_true",
                     help="time the pass with density-aware windows and with fixed windows of 1..32 cycles "
                          "(one JSON line each, with the events-per-window distribution)")
@@ -226,56 +234,14 @@ def main():
     if args.text:
         text_pipeline(args, w, dev)
         return
-    d, tr = w.design, w.trace
     gen_s = time.time() - t0
+    head = measure(args, w, dev, gen_s, flush_gib=1)
+    info, tot = head.pop("_info"), head.pop("_totals")
+    d, tr = w.design, w.trace
     E, G, P, C = tr.n_events, d.n_gates, tr.n_pins, tr.n_cycles
-    print(f"[bench] workload {w.name}: {G} gates, {P} pins, {E} events, {C} cycles (gen {gen_s:.1f}s)",
-          file=sys.stderr, flush=True)
-
-    an = pa.PowerAnalysis(0, torch.cuda.current_stream(dev), chunk_cycles=args.chunk_cycles,
-                          grid_blocks=args.grid_blocks, time_kernels=True)
-    t0 = time.time()
-    an.load(d, tr)
-    torch.cuda.synchronize()
-    load_s = time.time() - t0
-    outs = an.alloc_outputs(per_event=False)
-    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
-
-    clk_before = clocks()
-    for _ in range(args.warmup):
-        an.run(outs)
-    t_end = time.time() + (0.0 if args.quick else 2.0)
-    while time.time() < t_end:
-        an.run(outs)
-    # warm (back-to-back, no flush) device times, for reference
-    warm = []
-    for _ in range(10):
-        an.run(outs)
-        warm.append(an.info()["kernel_ms"])
-
-    # the fused kernel's device time (events around it), then the whole pass
-    # with events only before the fused kernel and after the finalize
-    fused_ms, pass_ms = [], []
-    for _ in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(1.0)
-        an.run(outs)
-        fused_ms.append(an.info()["kernel_ms"][0])
-    an.set_timing(2)
-    torch.cuda.synchronize()
-    tb0 = time.perf_counter()
-    for _ in range(args.steps):
-        if not args.no_flush:
-            flush.fill_(1.0)
-        tot = an.run(outs)["totals"]
-        pass_ms.append(an.info()["kernel_ms"][3])
-    torch.cuda.synchronize()
-    tb1 = time.perf_counter()
-    an.set_timing(1)
-    clk_after = clocks()
-    info = an.info()
 
     # plain device copy in the same session: the HBM rate a streaming kernel reaches here
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
     src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     copy_ms = []
     for i in range(12):
@@ -287,36 +253,30 @@ def main():
         if i >= 2:
             copy_ms.append(e0.elapsed_time(e1))
     copy_gbs = 2 * src.numel() * 4 / (statistics.median(copy_ms) * 1e-3) / 1e9
-    del src
-
-    ms_step = statistics.median(pass_ms)
-    ms_fused = statistics.median(fused_ms)
-    tables = d.lut_J.nbytes + d.leak_W.nbytes + d.slew_axis.nbytes + d.cap_axis.nbytes
-    alg_bytes = 12 * E + 9 * P + 12 * G + tables
-    achieved = alg_bytes / (ms_fused * 1e-3) / 1e9
-    value = E / (ms_step * 1e-3)
+    del src, flush
 
     cpu = None
     if not (args.no_cpu_baseline or args.quick):
-        import oracle
+        cpu = cpu_baseline(w, tot)
 
-        oracle.build()
-        # whole passes of the single-threaded oracle until about 10 s of CPU time
-        runs = []
-        while sum(runs) < 10.0 and len(runs) < 20:
-            t0 = time.perf_counter()
-            o = oracle.run(d, tr, per_event=False)
-            runs.append(time.perf_counter() - t0)
-        cpu_s = statistics.median(runs)
-        rel = abs(o["e_int_J"] - tot["e_int_J"]) / abs(o["e_int_J"])
-        cpu = {"value": E / cpu_s, "unit": "events/s", "cores": 1, "kind": "oracle",
-               "sample": f"{len(runs)} whole passes of the {w.name} workload ({E} events each) by the "
-                         f"single-threaded C oracle, median {cpu_s:.2f} s per pass; its e_int agrees with "
-                         f"the GPU to {rel:.1e}"}
+    # every other configuration: the same measurement, one line each in "configs"
+    configs = {w.name: {k: head[k] for k in ("events", "fused_ms", "pass_ms", "events_per_s", "frac", "traffic")}}
+    if not (args.quick or args.no_configs):
+        del w, d, tr
+        for name in ("tiny", "skewed", "glitch_heavy", "large"):
+            if name in configs:
+                continue
+            t0 = time.time()
+            wc = synth.make(name)
+            r = measure(args, wc, dev, time.time() - t0, flush_gib=1, steps=max(10, args.steps // 3))
+            configs[name] = {k: r[k] for k in ("events", "fused_ms", "pass_ms", "events_per_s", "frac", "traffic")}
+            del wc, r
+            torch.cuda.empty_cache()
 
+    ms_step, ms_fused = head["pass_ms"], head["fused_ms"]
     line = {
         "metric": "events/sec and gate-cycles/sec (fused power pass), % of HBM roofline",
-        "value": value,
+        "value": E / (ms_step * 1e-3),
         "unit": "events/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -327,27 +287,133 @@ def main():
         "vs_baseline": None,
         "dtype": "f64",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {G} gates (inputs {int(d.cell_n_in.min())}-{int(d.cell_n_in.max())}, "
-                               f"{d.n_slew}x{d.n_cap} fp64 LUTs), {C} cycles of {tr.t_clk} fs, {E} events, seed 0",
-                   "gates": G, "pins": P, "events": E, "cycles": C,
+        "config": {"workload": head["workload"], "gates": G, "pins": P, "events": E, "cycles": C,
                    "chunk_cycles": info["chunk_cycles"], "grid_blocks": info["grid_blocks"],
                    "block_threads": info["block_threads"], "windows": info["n_windows"],
                    "stream_slots": info["n_slots"], "wave_steps_max": info["wave_steps_max"],
                    "wave_steps_mean": round(info["wave_steps_mean"], 2)},
         "gate_cycles_per_s": G * C / (ms_step * 1e-3),
         "fused_ms": ms_fused,
-        "pass_ms_p10_p90": [float(np.percentile(pass_ms, 10)), float(np.percentile(pass_ms, 90))],
-        "warm_pass_ms_median": statistics.median(x[3] for x in warm),
-        "wall_ms_per_step": (tb1 - tb0) * 1e3 / args.steps,
-        "load_s": load_s,
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(w.name),
-                     "alg_bytes_per_launch": alg_bytes, "copy_GBs": copy_gbs, "frac_of_copy": achieved / copy_gbs},
+        "pass_ms_p10_p90": head["pass_ms_p10_p90"],
+        "warm_pass_ms_median": head["warm_pass_ms"],
+        "wall_ms_per_step": head["wall_ms_per_step"],
+        "load_s": head["load_s"],
+        "load_plus_pass_events_per_s": E / (head["load_s"] + ms_step * 1e-3),
+        "roofline": {"bound": "hbm", "achieved": head["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": head["frac"], "traffic": head["traffic"], "alg_bytes_per_launch": head["alg_bytes"],
+                     "copy_GBs": copy_gbs, "frac_of_copy": head["achieved"] / copy_gbs},
+        "configs": configs,
         "cpu_baseline": cpu,
-        "clocks": {"before": clk_before, "after": clk_after},
+        "clocks": head["clocks"],
         "device_bytes": info["device_bytes"],
     }
     print(json.dumps(line), flush=True)
+
+
+def measure(args, w, dev, gen_s, flush_gib=1, steps=None):
+    """Load one workload and time its pass: W warm-up passes plus >= 2 s of
+    passes for steady clocks, then K cold passes (a 1 GiB write before each
+    evicts the L2s and the Infinity Cache), timed by the library's HIP events
+    on its stream: the fused kernel alone, then the whole pass."""
+    import numpy as np
+    import torch
+
+    import eda_gate_level_amd as pa
+
+    steps = steps or args.steps
+    d, tr = w.design, w.trace
+    E, G, P, C = tr.n_events, d.n_gates, tr.n_pins, tr.n_cycles
+    print(f"[bench] workload {w.name}: {G} gates, {P} pins, {E} events, {C} cycles (gen {gen_s:.1f}s)",
+          file=sys.stderr, flush=True)
+    an = pa.PowerAnalysis(0, torch.cuda.current_stream(dev), chunk_cycles=args.chunk_cycles,
+                          grid_blocks=args.grid_blocks, time_kernels=True)
+    t0 = time.time()
+    an.load(d, tr)
+    torch.cuda.synchronize()
+    load_s = time.time() - t0
+    outs = an.alloc_outputs(per_event=False)
+    flush = torch.empty(flush_gib << 28, dtype=torch.float32, device=dev)
+
+    clk_before = clocks()
+    for _ in range(args.warmup):
+        an.run(outs)
+    t_end = time.time() + (0.0 if args.quick else 2.0)
+    while time.time() < t_end:
+        an.run(outs)
+    warm = []
+    for _ in range(10):
+        an.run(outs)
+        warm.append(an.info()["kernel_ms"])
+    fused_ms, pass_ms = [], []
+    for _ in range(steps):
+        if not args.no_flush:
+            flush.fill_(1.0)
+        an.run(outs)
+        fused_ms.append(an.info()["kernel_ms"][0])
+    an.set_timing(2)
+    torch.cuda.synchronize()
+    tb0 = time.perf_counter()
+    for _ in range(steps):
+        if not args.no_flush:
+            flush.fill_(1.0)
+        tot = an.run(outs)["totals"]
+        pass_ms.append(an.info()["kernel_ms"][3])
+    torch.cuda.synchronize()
+    tb1 = time.perf_counter()
+    an.set_timing(1)
+    clk_after = clocks()
+    info = an.info()
+    an.close()
+    del flush, outs
+    ms_step = statistics.median(pass_ms)
+    ms_fused = statistics.median(fused_ms)
+    tables = d.lut_J.nbytes + d.leak_W.nbytes + d.slew_axis.nbytes + d.cap_axis.nbytes
+    alg_bytes = 12 * E + 9 * P + 12 * G + tables
+    achieved = alg_bytes / (ms_fused * 1e-3) / 1e9
+    return {
+        "workload": f"{w.name}: {G} gates (inputs {int(d.cell_n_in.min())}-{int(d.cell_n_in.max())}, "
+                    f"{d.n_slew}x{d.n_cap} fp64 LUTs), {C} cycles of {tr.t_clk} fs, {E} events, seed 0",
+        "events": E, "fused_ms": ms_fused, "pass_ms": ms_step, "events_per_s": E / (ms_step * 1e-3),
+        "achieved": achieved, "frac": achieved / HBM_PEAK_GBS, "alg_bytes": alg_bytes,
+        "traffic": profiled_traffic(w.name),
+        "pass_ms_p10_p90": [float(np.percentile(pass_ms, 10)), float(np.percentile(pass_ms, 90))],
+        "warm_pass_ms": statistics.median(x[3] for x in warm),
+        "wall_ms_per_step": (tb1 - tb0) * 1e3 / steps, "load_s": load_s,
+        "clocks": {"before": clk_before, "after": clk_after}, "_info": info, "_totals": tot,
+    }
+
+
+def cpu_baseline(w, tot):
+    """The oracle as it stands, on this host: whole passes of the workload on
+    one core until about 10 s have run, then on all the host cores this
+    process may use (at most 16, the CPU share of one GPU) until about 5 s
+    have run; the medians per pass."""
+    import oracle
+
+    oracle.build()
+    d, tr = w.design, w.trace
+    E = tr.n_events
+    one = []
+    while sum(one) < 10.0 and len(one) < 20:
+        t0 = time.perf_counter()
+        o = oracle.run(d, tr, per_event=False)
+        one.append(time.perf_counter() - t0)
+    n = oracle.host_threads()
+    many = []
+    while sum(many) < 5.0 and len(many) < 40:
+        t0 = time.perf_counter()
+        om = oracle.run(d, tr, per_event=False, threads=n)
+        many.append(time.perf_counter() - t0)
+    s1, sn = statistics.median(one), statistics.median(many)
+    rel = max(abs(o["e_int_J"] - tot["e_int_J"]) / abs(o["e_int_J"]),
+              abs(om["e_leak_J"] - tot["e_leak_J"]) / abs(om["e_leak_J"]))
+    return {"value": E / sn, "unit": "events/s", "cores": n, "kind": "oracle",
+            "cpu_model": oracle.cpu_model(),
+            "single_core": {"value": E / s1, "unit": "events/s", "cores": 1, "s_per_pass": s1, "passes": len(one)},
+            "all_core": {"s_per_pass": sn, "passes": len(many), "threads": n},
+            "sample": f"whole passes of the {w.name} workload ({E} events each) by the C oracle: {len(one)} on one "
+                      f"core (median {s1:.2f} s), then {len(many)} on {n} threads (gate ranges, median "
+                      f"{sn:.3f} s); its e_int and e_leak agree with the GPU to {rel:.1e}"}
 
 
 if __name__ == "__main__":
