@@ -42,19 +42,25 @@ def build(verbose: bool = False) -> str:
                "-c", "-o", obj, os.path.join(CSRC, src)]
         procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(obj)
-    for cmd, p in procs:
-        out, _ = p.communicate()
-        if p.returncode != 0:
-            sys.stderr.write(out)
-            raise RuntimeError(f"hipcc failed: {' '.join(cmd)}")
-        if verbose and out:
-            sys.stderr.write(out)
-    tmp = LIB + ".tmp"
-    link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs]
-    subprocess.run(link, check=True)
-    os.replace(tmp, LIB)
-    for o in objs:
-        os.remove(o)
+    try:
+        failed = None
+        for cmd, p in procs:
+            out, _ = p.communicate()
+            if p.returncode != 0:
+                sys.stderr.write(out)
+                failed = failed or cmd
+            elif verbose and out:
+                sys.stderr.write(out)
+        if failed:
+            raise RuntimeError(f"hipcc failed: {' '.join(failed)}")
+        tmp = LIB + ".tmp"
+        link = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs]
+        subprocess.run(link, check=True)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 

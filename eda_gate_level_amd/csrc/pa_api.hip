@@ -138,12 +138,15 @@ struct Events {
   DBuf wdesc, wlen, l0;            // every wave's (first slot, events per lane); events per window; leakage at t = 0
   DBuf lplan;                      // per block, the cells whose LUTs it copies into LDS
   int32_t lut_lds = 0;             // LDS doubles of a block for those copies (0: none)
+  uint64_t pad_key = 0;            // key of an empty slot of the lane streams
+  DBuf blk_lut;                    // walk kernel: every block's LUT range (first entry, entries)
+  int32_t walk_lut = 0;            // walk kernel: LDS doubles for the largest range (0: not used)
   int32_t n_ranges = 0, grid = 1;
   DBuf blk_wave, blk_cnt, blk_part, res;
   int64_t bytes() const {
     return (int64_t)(key.bytes + slew.bytes + orig.bytes + pin_init.bytes + rstart.bytes + rchunk.bytes +
                      chunk_blk.bytes + wdesc.bytes + wlen.bytes + l0.bytes + lplan.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
-                     res.bytes);
+                     res.bytes + blk_lut.bytes);
   }
 };
 
@@ -532,13 +535,13 @@ static int build_ranges(pa_ctx *c, Events &v) {
                 (unsigned long long)slots);
   v.slots = (int64_t)slots;
   HIPCHK(hipMemcpyAsync(v.wdesc.p, wd.data(), sizeof(uint2) * wd.size(), hipMemcpyHostToDevice, s));
-  // ---- the streams: keys and slews, the caller's index of every event; empty slots hold key 0
+  // ---- the streams: keys and slews, the caller's index of every event; empty slots hold the pad key
   const int64_t Sa = (int64_t)slots + 2;  // two zeroed entries past the streams
   HIPCHK(v.key.ensure(sizeof(uint64_t) * Sa));
   HIPCHK(v.slew.ensure(sizeof(float) * Sa));
   HIPCHK(v.orig.ensure(sizeof(uint32_t) * Sa));
-  HIPCHK(hipMemsetAsync(v.key.p, 0, sizeof(uint64_t) * Sa, s));
-  HIPCHK(hipMemsetAsync(v.slew.p, 0, sizeof(float) * Sa, s));
+  HIPCHK(pa::launch_fill_u64(Sa, v.pad_key, v.key.as<uint64_t>(), s));
+  HIPCHK(hipMemsetD32Async((hipDeviceptr_t)v.slew.p, 0x3F800000, Sa, s));  // 1.0f: a pad slot's slew
   HIPCHK(hipMemsetAsync(v.orig.p, 0xFF, sizeof(uint32_t) * Sa, s));
   if (W > 0)
     HIPCHK(pa::launch_scatter(E, ls.skey.as<uint64_t>(), ls.sslew.as<float>(), ls.sorig.as<uint32_t>(),
@@ -555,6 +558,21 @@ static int build_ranges(pa_ctx *c, Events &v) {
                                v.lplan.as<uint2>(), s));
   } else {
     v.lut_lds = 0;
+  }
+  // the walk kernel: every block's LUT range, used when each fits in a block's LDS
+  v.walk_lut = 0;
+  if (nr > 0 && W > 0 && v.pad_key != 0 && c->tun.lut_lds_kib == 0 && pa::walk_supported(d.n_slew, d.n_cap)) {
+    const int32_t room = pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax);
+    HIPCHK(v.blk_lut.ensure(sizeof(uint2) * (size_t)nr));
+    HIPCHK(pa::launch_block_luts(nr, ls.skey.as<uint64_t>(), ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(),
+                                 d.gate_rec.as<uint4>(), d.cell_meta.as<uint2>(), v.gb, d.n_slew, d.n_cap,
+                                 v.blk_lut.as<uint2>(), s));
+    std::vector<uint2> hl((size_t)nr);
+    HIPCHK(hipMemcpyAsync(hl.data(), v.blk_lut.p, sizeof(uint2) * hl.size(), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    uint32_t most = 0;
+    for (const uint2 &r : hl) most = std::max(most, r.y);
+    if ((int64_t)most <= (int64_t)room) v.walk_lut = (int32_t)std::max<uint32_t>(most, 2);
   }
   // leakage power at t = 0, from the initial pin values
   DBuf &part = ls.part;
@@ -655,16 +673,27 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   // the cycle in the chunk has the low word's bits above pin code and tic, and
   // the bits the gate id leaves free in the high word
   const uint32_t gb = bits_for((uint64_t)std::max<int64_t>(G - 1, 0));
+  // and one cycle value more than the chunk needs is kept for the pad slots'
+  // dummy bin (cycle Cc), where the key has the bits
   const uint32_t lc_max = (32 - v.pb - v.tb) + (22 - gb);
   int64_t Cc_want = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : pa::pass_max_chunk_cycles();
   Cc_want = std::min<int64_t>(Cc_want, (int64_t)pa::pass_max_chunk_cycles());
-  if (lc_max < 31) Cc_want = std::min<int64_t>(Cc_want, int64_t(1) << lc_max);
+  const uint32_t lc_use = lc_max > 0 ? lc_max - 1 : 0;
+  if (lc_use < 31) Cc_want = std::min<int64_t>(Cc_want, int64_t(1) << lc_use);
   int64_t Cc = 1;
   while (Cc * 2 <= Cc_want) Cc *= 2;
   uint32_t lc = 0;
   while ((int64_t(1) << lc) < Cc) ++lc;
   v.Cc = (int32_t)Cc;
   v.Q = (int32_t)((v.C + Cc - 1) / Cc);
+  // the pad key: an output-pin 1->0 event at time 0 of cycle Cc (no event's
+  // cycle in its chunk reaches Cc); without a spare cycle bit empty slots are
+  // key 0 (no event has it: an event at a window start is a head)
+  v.pad_key = 0;
+  if (lc + 1 <= lc_max) {
+    const uint64_t lk = ((uint64_t)Cc << (v.pb + v.tb)) | pa::out_code(v.pb);
+    v.pad_key = ((lk >> 32) << (pa::kKeyGateShift + gb)) | (lk & 0xFFFFFFFFull);
+  }
   v.chunk_ticks = Cc * t_clk;
   pa::LayoutFmt f{};
   f.T = t_clk;
@@ -799,6 +828,9 @@ static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_eve
   a.kmax = d.kmax;
   a.lut_plan = v.lut_lds > 0 ? v.lplan.as<uint2>() : nullptr;
   a.lut_lds = v.lut_lds;
+  a.pad_key = v.pad_key;
+  a.blk_lut = v.walk_lut > 0 ? v.blk_lut.as<uint2>() : nullptr;
+  a.walk_lut = v.walk_lut;
   a.blk_wave = v.blk_wave.as<double>();
   a.blk_cnt = v.blk_cnt.as<unsigned long long>();
   a.blk_part = v.blk_part.as<double>();
@@ -915,8 +947,8 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
   std::memset(info, 0, sizeof *info);
   info->n_gates = c->d.G;
   info->n_pins = c->d.P;
-  info->n_events = c->ev.E;
-  info->n_cycles = c->ev.C;
+  info->n_events = c->has_events ? c->ev.E : 0;  // nothing loaded: nothing for a pass
+  info->n_cycles = c->has_events ? c->ev.C : 0;
   info->chunk_cycles = c->ev.Cc;
   info->n_chunks = c->ev.Q;
   info->grid_blocks = c->has_events ? c->ev.grid : 0;

@@ -60,6 +60,7 @@ struct PassArgs {
   const uint64_t *key;
   const float *slew;
   const uint32_t *orig;    // caller's CSR index of each laid-out event (~0 in empty slots)
+  uint64_t pad_key;        // key of an empty slot (no event has it)
   const uint2 *wdesc;      // [n_ranges][waves] every wave's (first slot, events per lane)
   const uint32_t *rchunk;  // [n_ranges] chunk of each range
   int32_t n_ranges;
@@ -91,6 +92,9 @@ struct PassArgs {
   // cells whose LUTs every block copies into LDS (see launch_lut_plan)
   const uint2 *lut_plan;      // [n_ranges][pass_lut_plan_slots()] (cell, LDS offset in doubles), cell ~0 = none
   int32_t lut_lds;            // LDS reserved for them, doubles (0: none)
+  // the walk kernel: every block's LUT range [x, x + y) in doubles, all of it in the block's LDS
+  const uint2 *blk_lut;
+  int32_t walk_lut;           // LDS doubles reserved for the largest range (0: the walk kernel is not used)
   // per-block results, reduced by the finalize kernel
   double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
   unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32
@@ -135,6 +139,15 @@ hipError_t launch_lut_plan(const uint64_t *skey, const uint32_t *ws, const uint3
                            const uint4 *gate_rec, const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap,
                            int32_t lut_lds, uint2 *plan, hipStream_t s);
 int pass_lut_plan_slots();
+// The walk kernel (one template per supported axis size): every block's LUT
+// range (first entry, entries) from its first and last window's gates; the
+// LDS doubles left for a block's LUT range beside its bins, pin records and
+// cell tables (0: none).
+hipError_t launch_block_luts(int32_t nr, const uint64_t *skey, const uint32_t *ws, const uint32_t *bwin,
+                             const uint4 *gate_rec, const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap,
+                             uint2 *out, hipStream_t s);
+bool walk_supported(int n_slew, int n_cap);
+int32_t walk_lut_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax);
 int32_t pass_lut_lds_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax);
 int pass_block_threads();
 int pass_blocks_per_cu();       // blocks of the pass resident on one compute unit

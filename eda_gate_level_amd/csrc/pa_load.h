@@ -82,6 +82,7 @@ hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, c
                           const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
                           uint64_t *key, float *slew, uint32_t *orig, hipStream_t s);
 int lane_plan_lanes();  // lanes of a block of the pass
+hipError_t launch_fill_u64(int64_t n, uint64_t v, uint64_t *out, hipStream_t s);
 hipError_t scan_inclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
                               hipStream_t s);
 hipError_t sort_pairs_u64(const uint64_t *kin, uint64_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,

@@ -538,6 +538,19 @@ hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, c
 }
 int lane_plan_lanes() { return kLaneNT; }
 
+namespace {
+__global__ void k_fill_u64(int64_t n, uint64_t v, uint64_t *out) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = v;
+}
+}  // namespace
+
+hipError_t launch_fill_u64(int64_t n, uint64_t v, uint64_t *out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(n)), dim3(kLT), 0, s, n, v, out);
+  return hipGetLastError();
+}
+
 hipError_t scan_inclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
                               hipStream_t s) {
   return hipcub::DeviceScan::InclusiveSum(tmp, *tmp_bytes, in, out, (int)n, s);

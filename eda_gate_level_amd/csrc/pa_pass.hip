@@ -244,8 +244,8 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       if (j + 2 < len) load_pair(j + 2);
       const uint32_t h0 = (uint32_t)(K0 >> 32);
       // a window head: windows have even lengths in the lane's stream, so a
-      // head is always the first of a pair (an empty slot has key 0)
-      if (K0 != 0ull && ((h0 >> 9) & 1u)) {
+      // head is always the first of a pair (an empty slot holds the pad key)
+      if (K0 != a.pad_key && ((h0 >> 9) & 1u)) {
         gate = (h0 >> 10) & gmask;
         const uint4 rec = a.gate_rec[gate];
         const double cap = __hiloint2double((int)rec.y, (int)rec.x);
@@ -280,15 +280,15 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
       // the state before each event (all events of one timestamp see the
       // state before the first of them, Sec. 2.4.2), the glitch flags (the pin
       // already switched in this clock cycle, Sec. 2.4.1, Fig. 7), the slew
-      // segment and the LUT row.  An empty slot (key 0, a short lane stream
-      // or an odd window) changes no state and adds nothing.
+      // segment and the LUT row.  An empty slot (the pad key: a short lane
+      // stream or an odd window) changes no state and adds nothing.
       uint32_t code[2], tic[2], cyc[2], Sm[2], Sa[2], si[2], lo[2];
       bool act[2], input[2], glitch[2], rise[2];
       float sl[2] = {s0, s1};
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
         const uint64_t K = r ? K1 : K0;
-        act[r] = K != 0ull;
+        act[r] = K != a.pad_key;
         const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
         code[r] = lk & outc;                   // pin code
         tic[r] = (lk >> pb) & tmask;           // time inside the cycle
@@ -505,6 +505,392 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
 }
 
 
+// ---------------------------------------------------------------------------
+// The walk kernel: the same pass for the common case -- the cell tables and
+// every LUT the block's gates use fit in its LDS, the slew and cap axes have
+// NS and NC points, no per-event or per-gate outputs -- written for latency
+// hiding and few instructions per event:
+//   * a four-deep ring of lane-stream pairs in registers, one load per step
+//     into the slot the step has just consumed, so every pair is fetched four
+//     steps before it is used; the gate record of the next pair's window head
+//     is gathered one step ahead; no register moves between steps, so no load
+//     is waited for before its time;
+//   * all LUT reads from the block's LDS copy of the contiguous LUT range of
+//     its cells (gates are numbered in cell order, so a block's gates use a
+//     contiguous range of cells);
+//   * empty slots carry a pad key -- an output-pin 1->0 event in the dummy
+//     cycle Cc -- that changes no state, adds no energy and lands in a bin the
+//     block never writes out, so no event is predicated on being real;
+//   * the energies go to their components with multiply-adds by 0/1 masks,
+//     and leakage changes are binned as (change at the bin start, minus the
+//     change times its time in the bin), which needs no partial-bin fix-up.
+
+struct WalkBin {
+  double w;                // energy: dynamic, minus leakage change x time in the bin
+  double d;                // leakage power changes in the bin
+  unsigned long long c;    // events | glitches << 32
+};
+
+typedef double f64x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) f64x2 lds_f64x2;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) WalkBin lds_bin;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+
+// LDS pointers (32-bit addresses)
+struct WalkLds {
+  lds_f64x2 *axw, *caxw;
+  lds_f32 *thr;
+  lds_bin *bins;      // [Cc + 1]: bin Cc takes the pad slots
+  lds_u32 *prec;      // [waves][pin slots][64][2]: a pin's last (time in cycle, slew bits) per lane
+  lds_f64 *leak;
+  lds_u32x2 *meta;
+  lds_f64 *lut;       // the block's LUT range, 16-byte aligned
+};
+
+__host__ __device__ inline size_t walk_fixed_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr,
+                                                   int64_t n_leak, int kmax) {
+  const size_t b = 16 * (size_t)n_cells * (n_slew - 1 + n_cap - 1) + 4 * (size_t)n_cells * n_thr +
+                   24 * ((size_t)Cc + 1) + prec_bytes(kmax) + 8 * (size_t)n_leak + 8 * (size_t)n_cells;
+  return (b + 15) & ~size_t(15);
+}
+
+__device__ __forceinline__ WalkLds walk_carve(unsigned char *s, int Cc, int n_cells, int n_slew, int n_cap,
+                                              int n_thr, int64_t n_leak, int kmax) {
+  typedef __attribute__((address_space(3))) unsigned char lds_u8;
+  lds_u8 *b = (lds_u8 *)s;
+  WalkLds L;
+  L.axw = (lds_f64x2 *)b;
+  L.caxw = L.axw + n_cells * (n_slew - 1);
+  L.thr = (lds_f32 *)(L.caxw + n_cells * (n_cap - 1));
+  L.bins = (lds_bin *)(L.thr + n_cells * n_thr);
+  L.prec = (lds_u32 *)(L.bins + Cc + 1);
+  L.leak = (lds_f64 *)(L.prec + kNW * (kmax + 1) * 64 * 2);
+  L.meta = (lds_u32x2 *)(L.leak + (int)n_leak);
+  L.lut = (lds_f64 *)(b + walk_fixed_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, kmax));
+  return L;
+}
+
+// 24-bit multiply-add (full rate; every operand here is far below 2^24)
+__device__ __forceinline__ uint32_t mad24(uint32_t x, uint32_t y, uint32_t z) {
+  return (x & 0xFFFFFFu) * (y & 0xFFFFFFu) + z;
+}
+
+template <int NS, int NC>
+__global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
+  constexpr int NIN = NS - 2;  // inner slew-axis points: the segment is the count at or below the slew
+#ifndef PA_WALK_GROUP
+#define PA_WALK_GROUP 2
+#endif
+  constexpr int GP = PA_WALK_GROUP;  // pairs per group of the stream
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  __shared__ double s_red[kNW][8];
+  __shared__ double s_scan[kNW];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int b = blockIdx.x;
+  const int Cc = a.Cc, nthr = a.n_thr;
+  const WalkLds L = walk_carve(s_dyn, Cc, a.n_cells, NS, NC, nthr, a.n_leak, a.kmax);
+  const bool has_range = b < a.n_ranges;
+
+  int base = 0, len = 0, q = 0;
+  if (has_range) {
+    q = (int)a.rchunk[b];
+    const uint2 d = a.wdesc[b * kNW + wid];
+    base = __builtin_amdgcn_readfirstlane((int)d.x);
+    len = __builtin_amdgcn_readfirstlane((int)d.y);
+  }
+  const int npair = len >> 1;  // lane streams have even lengths
+  // The stream in groups of GP pairs.  At the start of group g the lane
+  // issues the gate-record gathers of group g + 1's window heads (its keys
+  // arrived during group g - 1) and the loads of group g + 2's pairs; both are
+  // first needed one group later, so every load has the same lead and a wait
+  // for one never holds up a younger one (loads complete in order).
+  u64x2 k0[GP], k1[GP], k2[GP];  // groups g, g + 1, g + 2
+  f32x2 s0[GP], s1[GP], s2[GP];
+  auto load_pair = [&](int p, u64x2 &k, f32x2 &sl) {
+    const int x = base + p * 128 + 2 * lane;
+    k = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x));
+    sl = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x));
+  };
+#pragma unroll
+  for (int i = 0; i < GP; ++i) {
+    k0[i] = k1[i] = k2[i] = u64x2{a.pad_key, a.pad_key};
+    s0[i] = s1[i] = s2[i] = f32x2{1.f, 1.f};
+    if (npair > 0) {
+      load_pair(min(i, npair - 1), k0[i], s0[i]);
+      load_pair(min(GP + i, npair - 1), k1[i], s1[i]);
+    }
+  }
+
+  // block set-up: bins, cell tables and the LUT range, while the ring fills
+  for (int c = tid; c <= Cc; c += kNT) {
+    L.bins[c].w = 0.0;
+    L.bins[c].d = 0.0;
+    L.bins[c].c = 0ull;
+  }
+  {
+    const f64x2 *ax = reinterpret_cast<const f64x2 *>(a.cell_axw), *cx = reinterpret_cast<const f64x2 *>(a.cell_caxw);
+    const u32x2 *me = reinterpret_cast<const u32x2 *>(a.cell_meta);
+    for (int j = tid; j < a.n_cells * (NS - 1); j += kNT) L.axw[j] = ax[j];
+    for (int j = tid; j < a.n_cells * (NC - 1); j += kNT) L.caxw[j] = cx[j];
+    for (int j = tid; j < a.n_cells * nthr; j += kNT) L.thr[j] = a.cell_thr[j];
+    for (int j = tid; j < a.n_leak; j += kNT) L.leak[j] = a.leak[j];
+    for (int j = tid; j < a.n_cells; j += kNT) L.meta[j] = me[j];
+  }
+  uint32_t lut_lo = 0;
+  if (has_range) {
+    const uint2 r = a.blk_lut[b];
+    lut_lo = r.x;
+    // cell LUT sizes 2^k k NS NC are even, so the range starts 16-byte aligned
+    const f64x2 *src = reinterpret_cast<const f64x2 *>(a.lut + r.x);
+    lds_f64x2 *dst = (lds_f64x2 *)L.lut;
+#pragma unroll 4
+    for (int j = tid; j < (int)(r.y >> 1); j += kNT) dst[j] = src[j];
+  }
+  __syncthreads();
+
+  double e_int = 0.0, e_sw = 0.0, e_gl = 0.0, e_lkt = 0.0;  // e_lkt: sum of leakage change x time in its bin (ticks)
+  const int64_t cstart = (int64_t)q * a.chunk_ticks;
+  const int64_t clen = min(a.chunk_ticks, a.t_max - cstart);
+  const int ncyc = (int)((clen + a.T - 1) / a.T);
+  const bool last_chunk = (q == a.Q - 1);
+  const uint32_t lastc = (uint32_t)(ncyc - 1);
+  const double Td = (double)a.T;
+  const double tail = (double)(a.t_max - cstart);
+  const double tick = a.tick_s;
+  const uint32_t pb = a.pb, tb = a.tb, cs = tb + pb;
+  const uint32_t gmask = (1u << a.gb) - 1u, ysh = 10u + a.gb;
+  const uint32_t tmask = (1u << tb) - 1u;
+  const uint32_t outc = (1u << pb) - 1u;
+  const uint32_t kmax = (uint32_t)a.kmax;
+  constexpr uint32_t PSZ = NS * NC;  // LUT entries per (state, pin)
+
+  if (npair > 0) {
+    auto head_gate = [&](uint64_t K, uint32_t fallback) -> uint32_t {
+      const uint32_t h = (uint32_t)(K >> 32);
+      return ((h >> 9) & 1u) ? ((h >> 10) & gmask) : fallback;
+    };
+    // the gate record's first three words (load, cell and cap segment); the
+    // fourth is not read, so no half-dead load result is waited for
+    auto gather = [&](uint32_t g) -> uint3 { return *reinterpret_cast<const uint3 *>(a.gate_rec + g); };
+    // gate records of group g's and group g + 1's pairs (a window head is
+    // always the first event of a pair; other pairs gather a valid record)
+    uint3 r0[GP], r1[GP];
+#pragma unroll
+    for (int i = 0; i < GP; ++i) r0[i] = gather(head_gate(k0[i].x, 0u));
+    // the lane's window: gate, LUT row base in the LDS copy, state stride,
+    // axis-table and leakage bases, load position on the cap segment,
+    // switching energy, slew thresholds
+    uint32_t gate = 0, wbase = 0, kpsz = 0, axb = 0, lb = 0;
+    double fc = 0.0, esw = 0.0;
+    float th[NIN];
+#pragma unroll
+    for (int j = 0; j < NIN; ++j) th[j] = __builtin_inff();
+    // running state: inputs after the last event, at the start of the current
+    // timestamp, pins switched in the current cycle, last cycle and time,
+    // leakage power of the current state
+    uint32_t S = 0, St = 0, seen = 0, pcyc = ~0u, ptic = 0;
+    double lkS = L.leak[0];
+    lds_u32 *prec = L.prec + (wid * (kmax + 1) * 64 + lane) * 2;
+
+    auto window_head = [&](uint64_t K, const uint3 &rec) {
+      const uint32_t h = (uint32_t)(K >> 32);
+      gate = (h >> 10) & gmask;
+      const double cap = __hiloint2double((int)rec.y, (int)rec.x);
+      const uint32_t cell = rec.z & 0xFFFFFFu, cseg = rec.z >> 24;
+      const u32x2 m = L.meta[cell];
+      lb = m.x >> 4;
+      kpsz = (m.x & 15u) * PSZ;
+      wbase = m.y - lut_lo + cseg;
+      axb = mad24(cell, NS - 1, 0u);
+      const f64x2 cx = L.caxw[mad24(cell, NC - 1, cseg)];
+      fc = (cap - cx.x) * cx.y;  // position on the gate's cap segment (Sec. 2.4.1, Fig. 2)
+      esw = a.hv2 * cap;         // Eq. 1
+#pragma unroll
+      for (int i = 0; i < NIN; i += 4) {
+        const f32x4 t4 = *(const lds_f32x4 *)(L.thr + mad24(cell, nthr, i));
+        th[i] = t4.x;
+        if (i + 1 < NIN) th[i + 1] = t4.y;
+        if (i + 2 < NIN) th[i + 2] = t4.z;
+        if (i + 3 < NIN) th[i + 3] = t4.w;
+      }
+      S = h & 0xFFu;  // input state at the window start
+      St = S;
+      seen = 0;
+      pcyc = ~0u;
+      lkS = L.leak[lb + S];
+    };
+
+    // one event of the lane's walk (Sec. 2.4.1-2.4.2, Fig. 7)
+    auto event = [&](uint64_t K, float sl) {
+      const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
+      const uint32_t code = lk & outc;                                     // pin code
+      const uint32_t tic = (lk >> pb) & tmask;                             // time inside the cycle
+      const uint32_t cyc = (uint32_t)((((uint64_t)(hw >> ysh)) << 32 | lk) >> cs);  // cycle in the chunk
+      const bool rise = (hw >> 8) & 1u;                                    // the pin's value after the event
+      const bool input = code != outc;
+      const bool newcyc = cyc != pcyc;
+      // events of one timestamp all see the state before the first of them (Sec. 2.4.2)
+      if (newcyc || tic != ptic) St = S;
+      if (newcyc) seen = 0u;
+      const uint32_t bit = 1u << code;
+      const bool glitch = (seen & bit) != 0u;  // the pin already switched in this cycle (Fig. 7)
+      seen |= bit;
+      pcyc = cyc;
+      ptic = tic;
+      const uint32_t Sm = St;
+      if (input) S ^= bit;
+      // the slew segment: inner axis points at or below the slew (Sec. 2.4.1, Fig. 2)
+      uint32_t n = 0;
+#pragma unroll
+      for (int i = 0; i < NIN; ++i) n += sl >= th[i] ? 1u : 0u;
+      const uint32_t cl = input ? code : 0u;
+      // (state, pin) row, then the slew segment and the cap segment: every factor is small
+      // kpsz is a loop-carried value whose small range the instruction
+      // selector cannot see: an empty asm hides it from the optimizer too, so
+      // the explicit 24-bit masks stay and the multiply is a full-rate mad24
+      uint32_t kp = kpsz;
+      asm volatile("" : "+v"(kp));
+      const uint32_t lo = mad24(Sm, kp, mad24(cl, PSZ, mad24(n, NC, wbase)));
+      const lds_f64 *Lp = L.lut + lo;
+      const double L00 = Lp[0], L01 = Lp[1], L10 = Lp[NC], L11 = Lp[NC + 1];
+      const f64x2 aw = L.axw[axb + n];
+      const double lkn = L.leak[lb + (S & 0xFFu)];  // leakage of the state after the event (Eq. 4)
+      const double fa = ((double)sl - aw.x) * aw.y;
+      const double v0 = L00 + fc * (L01 - L00);
+      const double v1 = L10 + fc * (L11 - L10);
+      const double Eint = v0 + fa * (v1 - v0);
+      double E = input ? Eint : (rise ? esw : 0.0);  // Eq. 1: 0->1 output events only
+      const double dp = lkn - lkS;  // the input toggle moves the leakage power
+      lkS = lkn;
+      const double ct = dp * (double)tic;
+      e_lkt += ct;
+      lds_u32 *pr = prec + min(code, kmax) * 128;
+      if (glitch) {
+        // Eq. 2 (reading): pulse width and the slews of the pin's previous event in the cycle and this one
+        const uint32_t ptic_pin = pr[0], pslew = pr[1];
+        const double pw = (double)(tic - ptic_pin);
+        const double rr = pw / (0.5 * ((double)sl + (double)__uint_as_float(pslew)));
+        E *= rr > 1.0 ? 1.0 : rr;
+        e_gl += E;
+      }
+      pr[0] = tic;
+      pr[1] = __float_as_uint(sl);
+      e_int = fma(E, (input && !glitch) ? 1.0 : 0.0, e_int);
+      e_sw = fma(E, (!input && !glitch) ? 1.0 : 0.0, e_sw);
+      if (cyc < (uint32_t)Cc) {  // a pad slot adds nothing (its lanes would all hit one bin)
+        lds_bin *bp = L.bins + (cyc & 0xFFFu);
+        __hip_atomic_fetch_add(&bp->w, fma(ct, -tick, E), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&bp->d, dp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&bp->c, 1ull | ((unsigned long long)glitch << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    };
+
+#pragma unroll 1
+    for (int p0 = 0; p0 < npair; p0 += GP) {
+      // group g + 1's gathers, then group g + 2's loads (past the end: the last pair again)
+#pragma unroll
+      for (int i = 0; i < GP; ++i) r1[i] = gather(head_gate(k1[i].x, gate));
+#pragma unroll
+      for (int i = 0; i < GP; ++i) load_pair(min(p0 + 2 * GP + i, npair - 1), k2[i], s2[i]);
+#pragma unroll
+      for (int i = 0; i < GP; ++i) {
+        if (p0 + i >= npair) break;
+        const uint64_t K0 = k0[i].x, K1 = k0[i].y;
+        if ((uint32_t)(K0 >> 41) & 1u) window_head(K0, r0[i]);
+        event(K0, s0[i].x);
+        event(K1, s0[i].y);
+      }
+#pragma unroll
+      for (int i = 0; i < GP; ++i) {
+        k0[i] = k1[i];
+        s0[i] = s1[i];
+        k1[i] = k2[i];
+        s1[i] = s2[i];
+        r0[i] = r1[i];
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- the block's bins: the leakage changes' in-chunk prefix, then its own slots
+  double dsum = 0.0, lkc = 0.0;
+  unsigned long long ngl = 0;
+  {
+    constexpr int PER = (kCCMAX + kNT - 1) / kNT;
+    double loc[PER];
+    double sum = 0.0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid * PER + u;
+      loc[u] = (has_range && c < ncyc) ? L.bins[c].d : 0.0;
+      sum += loc[u];
+    }
+    double incl = sum;
+    for (int o = 1; o < 64; o <<= 1) {
+      const double v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    if (lane == 63) s_scan[wid] = incl;
+    __syncthreads();
+    double wbase_sum = 0.0;
+    for (int w = 0; w < kNW; ++w) {
+      const double v = s_scan[w];
+      if (w < wid) wbase_sum += v;
+      dsum += v;
+    }
+    double run = wbase_sum + incl - sum;  // changes of the chunk's earlier bins in this block
+    double *ow = a.blk_wave + (size_t)b * Cc;
+    unsigned long long *oc = a.blk_cnt + (size_t)b * Cc;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid * PER + u;
+      if (c < Cc) {
+        double v = 0.0;
+        unsigned long long cn = 0ull;
+        if (has_range && c < ncyc) {
+          run += loc[u];  // the bin's own changes count from the bin start; the bin corrects for their times
+          const double blen = (last_chunk && c == (int)lastc) ? (double)a.last_len : Td;
+          v = L.bins[c].w + run * blen * tick;
+          lkc += loc[u] * (tail - Td * (double)c);
+          cn = L.bins[c].c;
+          ngl += cn >> 32;
+        }
+        ow[c] = v;
+        oc[c] = cn;
+      }
+    }
+  }
+
+  // ---- block totals
+  {
+    double v[5] = {e_int, e_sw, e_gl, lkc * tick - e_lkt * tick, (double)ngl};
+#pragma unroll
+    for (int u = 0; u < 5; ++u) v[u] = wave_sum(v[u]);
+    if (lane == 0) {
+#pragma unroll
+      for (int u = 0; u < 5; ++u) s_red[wid][u] = v[u];
+    }
+    __syncthreads();
+    if (tid < 8) {
+      double t = 0.0;
+      if (tid < 4) {
+        for (int w = 0; w < kNW; ++w) t += s_red[w][tid];
+      } else if (tid == 5) {
+        t = dsum;
+      } else if (tid == 6) {
+        for (int w = 0; w < kNW; ++w) t += s_red[w][4];
+      }
+      a.blk_part[(size_t)b * 8 + tid] = t;
+    }
+  }
+}
+
 // One wave per block: 64 windows sampled at the midpoints of 64 equal slices
 // of the block's window range (windows in gate order, gates numbered in cell
 // order, so the cells come out nondecreasing) give the cells present and each
@@ -710,9 +1096,60 @@ int32_t pass_lut_lds_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_t
   return used < kLdsMax ? (int32_t)((kLdsMax - used) / 16 * 2) : 0;
 }
 
+namespace {
+
+// Every block's LUT range: the LUTs of the cells from its first window's gate's
+// cell to its last window's (gates are numbered in cell order, and a block's
+// windows are in gate order), as (first entry, entries).
+__global__ void k_block_luts(int32_t nr, const uint64_t *skey, const uint32_t *ws, const uint32_t *bwin,
+                             const uint4 *gate_rec, const uint2 *cell_meta, uint32_t gb, uint32_t psz, uint2 *out) {
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < nr; b += gridDim.x * blockDim.x) {
+    const uint32_t w0 = bwin[b], w1 = bwin[b + 1];
+    uint2 r = make_uint2(0u, 0u);
+    if (w1 > w0) {
+      const uint32_t gmask = (1u << gb) - 1u;
+      const uint32_t g0 = (uint32_t)(skey[ws[w0]] >> 42) & gmask, g1 = (uint32_t)(skey[ws[w1 - 1]] >> 42) & gmask;
+      const uint32_t c0 = gate_rec[g0].z & 0xFFFFFFu, c1 = gate_rec[g1].z & 0xFFFFFFu;
+      const uint2 m0 = cell_meta[c0], m1 = cell_meta[c1];
+      const uint32_t k1 = m1.x & 15u;
+      r = make_uint2(m0.y, m1.y + ((1u << k1) * k1) * psz - m0.y);
+    }
+    out[b] = r;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_block_luts(int32_t nr, const uint64_t *skey, const uint32_t *ws, const uint32_t *bwin,
+                             const uint4 *gate_rec, const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap,
+                             uint2 *out, hipStream_t s) {
+  if (nr <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_block_luts, dim3((nr + 255) / 256), dim3(256), 0, s, nr, skey, ws, bwin, gate_rec, cell_meta,
+                     gb, (uint32_t)(n_slew * n_cap), out);
+  return hipGetLastError();
+}
+
+bool walk_supported(int n_slew, int n_cap) { return (n_slew == 7 && n_cap == 7) || (n_slew == 8 && n_cap == 8); }
+
+int32_t walk_lut_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, int64_t n_leak, int kmax) {
+  const size_t fixed = walk_fixed_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, kmax) + pass_static_lds_bytes();
+  return fixed < kLdsMax ? (int32_t)((kLdsMax - fixed) / 16 * 2) : 0;
+}
+
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
   const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax);
   const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
+  if (a.walk_lut > 0 && !diag) {
+    // the walk kernel: every block's LUT range in its LDS (at least the four entries a pad slot reads)
+    const size_t dyn = walk_fixed_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax) +
+                       8 * (size_t)max(a.walk_lut, 32);
+    if (!a.blk_lut || a.pad_key == 0 || dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
+    const dim3 g(grid_blocks), t(kNT);
+    if (a.n_slew == 7 && a.n_cap == 7) hipLaunchKernelGGL((k_walk<7, 7>), g, t, dyn, s, a);
+    else if (a.n_slew == 8 && a.n_cap == 8) hipLaunchKernelGGL((k_walk<8, 8>), g, t, dyn, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+  }
   size_t dyn = pass_lds_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax, cells);
   if (cells && a.lut_lds > 0) {
     if (!a.lut_plan) return hipErrorInvalidValue;

@@ -52,8 +52,9 @@ def test_large_bench_configuration_full_size():
     d, t = w.design, w.trace
     _print_case(f"large bench config E={t.n_events}")
     g = pu.gpu_run(d, t, per_event=False)
-    assert d.n_slew == 8 and g["_info"]["chunk_cycles"] == 2048
-    print(f"[large] gpu done, oracle on {__import__('oracle').host_threads()} threads", flush=True)
+    assert d.n_slew == 8
+    print(f"[large] gpu done (chunks of {g['_info']['chunk_cycles']} cycles), oracle on "
+          f"{__import__('oracle').host_threads()} threads", flush=True)
     o = _oracle(d, t)
     pu.assert_parity(g, o, per_event=False, label="large bench config")
     print(f"[large] {t.n_events} events, {int(o['n_glitches'])} glitches, {t.n_cycles} bins checked", flush=True)
@@ -83,7 +84,7 @@ def test_large_shaped_reduced(per_event):
 
     o = oracle.run(d, t, per_event=per_event, threads=oracle.host_threads())
     g = pu.gpu_run(d, t, per_event=per_event)
-    assert g["_info"]["n_chunks"] == 4
+    assert g["_info"]["n_chunks"] >= 4
     pu.assert_parity(g, o, per_event=per_event, label=f"large-shaped per_event {per_event}")
 
 
