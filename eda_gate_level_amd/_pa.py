@@ -16,12 +16,13 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa.so")
 
 PA_OK, PA_EINVAL, PA_EDATA, PA_ENOMEM, PA_EHIP, PA_ESTATE = 0, -1, -2, -3, -4, -5
+PA_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024  # the fixed device scratch of pa_run_noalloc
 _NAMES = {PA_EINVAL: "PA_EINVAL", PA_EDATA: "PA_EDATA", PA_ENOMEM: "PA_ENOMEM", PA_EHIP: "PA_EHIP",
           PA_ESTATE: "PA_ESTATE"}
 
 EXPORTS = ("pa_create", "pa_destroy", "pa_set_stream", "pa_set_timing", "pa_last_error", "pa_load_design",
-           "pa_load_events", "pa_run", "pa_run_gates", "pa_get_info", "pa_get_window_stats", "pa_pack_text",
-           "pa_run_text")
+           "pa_load_events", "pa_run", "pa_run_noalloc", "pa_run_gates", "pa_get_info", "pa_get_window_stats",
+           "pa_pack_text", "pa_run_text")
 
 
 class PaError(RuntimeError):
@@ -97,6 +98,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.pa_load_design.argtypes = [P, i64, P, P, i32, P, i32, i32, P, P, P, P, dbl]
     L.pa_load_events.argtypes = [P, i64, i64, P, P, P, P, P, i64, i64, dbl]
     L.pa_run.argtypes = [P, C.POINTER(pa_totals), P, P, P, P, P]
+    L.pa_run_noalloc.argtypes = [P, C.POINTER(pa_totals), P, P, P, P, P]
     L.pa_run_gates.argtypes = [P, C.POINTER(pa_totals), P, P, P, P]
     L.pa_get_info.argtypes = [P, C.POINTER(pa_info)]
     L.pa_get_window_stats.argtypes = [P, C.POINTER(pa_window_stats)]
@@ -104,7 +106,7 @@ def load_library(path: str = LIB_PATH) -> C.CDLL:
     L.pa_run_text.argtypes = [P, P, i64, i64, i64, dbl, C.POINTER(pa_text_opts), C.POINTER(pa_totals), P, P, P,
                               C.POINTER(pa_text_stats)]
     for name in ("pa_create", "pa_set_stream", "pa_set_timing", "pa_load_design", "pa_load_events", "pa_run",
-                 "pa_run_gates", "pa_get_info", "pa_get_window_stats", "pa_pack_text", "pa_run_text"):
+                 "pa_run_noalloc", "pa_run_gates", "pa_get_info", "pa_get_window_stats", "pa_pack_text", "pa_run_text"):
         getattr(L, name).restype = C.c_int
     return L
 
@@ -265,6 +267,23 @@ def pa_run(ctx, wave_J, cyc_events, cyc_glitches, evt_glitch=None, evt_state_bef
                         _ptr(cyc_glitches, torch.uint64, name="cyc_glitches"),
                         _ptr(evt_glitch, torch.uint8, name="evt_glitch"),
                         _ptr(evt_state_before, torch.uint8, name="evt_state_before")))
+    return tot.as_dict()
+
+
+def pa_run_noalloc(ctx, wave_J, cyc_events, cyc_glitches, evt_glitch=None, evt_state_before=None) -> dict:
+    import torch
+
+    Cn, E, _ = _outputs_for(ctx)
+    for t, name in ((wave_J, "wave_J"), (cyc_events, "cyc_events"), (cyc_glitches, "cyc_glitches")):
+        _need(t, Cn, name, exact=False)
+    for t, name in ((evt_glitch, "evt_glitch"), (evt_state_before, "evt_state_before")):
+        _need(t, E, name, exact=False)
+    tot = pa_totals()
+    _check(lib().pa_run_noalloc(ctx, C.byref(tot), _ptr(wave_J, torch.float64, name="wave_J"),
+                                _ptr(cyc_events, torch.uint64, name="cyc_events"),
+                                _ptr(cyc_glitches, torch.uint64, name="cyc_glitches"),
+                                _ptr(evt_glitch, torch.uint8, name="evt_glitch"),
+                                _ptr(evt_state_before, torch.uint8, name="evt_state_before")))
     return tot.as_dict()
 
 

@@ -23,6 +23,14 @@
 #include "pa_load.h"
 #include "pa_text.h"
 
+// Device memory of pa_run_noalloc: the pass's per-block partial results (cycle
+// bins, cycle counts, block totals) and the finalize's result slots, in one
+// array of fixed size instead of buffers the library allocates.  Every device
+// the library runs on holds its own copy until the process ends.  Host code
+// never uses the name below as an address: each device's address is looked up
+// once (scratch_address) and passed to the kernels.
+static __device__ __align__(256) unsigned char scratch[PA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
@@ -51,6 +59,29 @@ int fail(int code, const char *fmt, ...) {
   va_end(ap);
   g_err = buf;
   return code;
+}
+
+// The address of `scratch` on every device, looked up once per device (with
+// that device current) by the first pa_create on it.
+struct ScratchAddr {
+  bool looked_up = false;
+  hipError_t err = hipSuccess;
+  void *p = nullptr;
+};
+std::mutex g_scratch_mu;
+std::vector<ScratchAddr> g_scratch_addr;
+
+// called with `device` current
+ScratchAddr scratch_address(int device) {
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch_addr.size() <= device) g_scratch_addr.resize((size_t)device + 1);
+  ScratchAddr &a = g_scratch_addr[(size_t)device];
+  if (!a.looked_up) {
+    a.err = hipGetSymbolAddress(&a.p, HIP_SYMBOL(scratch));
+    if (a.err != hipSuccess) a.p = nullptr;
+    a.looked_up = true;
+  }
+  return a;
 }
 
 // owning device buffer
@@ -201,6 +232,7 @@ struct pa_ctx {
   PinnedBuf text_host[2];  // pa_run_text: packed segments on the host, and their device copy
   DBuf text_dev;
   double *h_res = nullptr;
+  ScratchAddr scratch;  // this device's copy of the fixed scratch of pa_run_noalloc
   hipEvent_t tev[3] = {nullptr, nullptr, nullptr};
   float kernel_ms[4] = {0, 0, 0, 0};
 };
@@ -238,6 +270,7 @@ int pa_create(pa_ctx **out, int hip_device, void *hip_stream, const pa_tunables 
   if (t) c->tun = *t;
   c->mem.cap = (int64_t)c->tun.device_mib_cap << 20;
   c->n_cu = prop.multiProcessorCount;
+  c->scratch = scratch_address(hip_device);  // checked by pa_run_noalloc, the only user
   if (hipHostMalloc((void **)&c->h_res, 16 * sizeof(double), hipHostMallocDefault) != hipSuccess) {
     delete c;
     return fail(PA_ENOMEM, "pa_create: pinned host buffer");
@@ -780,8 +813,37 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   return PA_OK;
 }
 
-static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
-                    uint8_t *evt_glitch, uint8_t *evt_state_before, double *gate_J) {
+// Where the pass puts its per-block partial results and the finalize its
+// result slots: [grid][Cc] bins, [grid][Cc] counts, [grid][8] totals, [16].
+struct PassScratch {
+  double *blk_wave = nullptr;
+  unsigned long long *blk_cnt = nullptr;
+  double *blk_part = nullptr;
+  double *res = nullptr;
+};
+
+static PassScratch loaded_scratch(Events &v) {
+  return PassScratch{v.blk_wave.as<double>(), v.blk_cnt.as<unsigned long long>(), v.blk_part.as<double>(),
+                     v.res.as<double>()};
+}
+
+// the same four pieces carved from one block at base (256-byte aligned pieces);
+// returns the bytes they take
+static size_t carve_scratch(const Events &v, void *base, PassScratch *out) {
+  auto al = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t n = (size_t)v.grid * (size_t)v.Cc;
+  const size_t o_cnt = al(sizeof(double) * n), o_part = o_cnt + al(sizeof(unsigned long long) * n),
+               o_res = o_part + al(sizeof(double) * 8 * (size_t)v.grid), end = o_res + al(sizeof(double) * 16);
+  if (out) {
+    char *b = static_cast<char *>(base);
+    *out = PassScratch{reinterpret_cast<double *>(b), reinterpret_cast<unsigned long long *>(b + o_cnt),
+                       reinterpret_cast<double *>(b + o_part), reinterpret_cast<double *>(b + o_res)};
+  }
+  return end;
+}
+
+static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wave_J, uint64_t *cyc_events,
+                    uint64_t *cyc_glitches, uint8_t *evt_glitch, uint8_t *evt_state_before, double *gate_J) {
   const Design &d = c->d;
   Events &v = c->ev;
   hipStream_t s = c->stream;
@@ -831,9 +893,9 @@ static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_eve
   a.pad_key = v.pad_key;
   a.blk_lut = v.walk_lut > 0 ? v.blk_lut.as<uint2>() : nullptr;
   a.walk_lut = v.walk_lut;
-  a.blk_wave = v.blk_wave.as<double>();
-  a.blk_cnt = v.blk_cnt.as<unsigned long long>();
-  a.blk_part = v.blk_part.as<double>();
+  a.blk_wave = sc.blk_wave;
+  a.blk_cnt = sc.blk_cnt;
+  a.blk_part = sc.blk_part;
   a.evt_glitch = evt_glitch;
   a.gate_J = gate_J;
   a.gate_perm = d.perm.as<int32_t>();
@@ -856,7 +918,7 @@ static int run_pass(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_eve
   f.wave_out = wave_J;
   f.cyc_events = cyc_events;
   f.cyc_glitches = cyc_glitches;
-  f.res = v.res.as<double>();
+  f.res = sc.res;
 
   const bool timed = c->tun.time_kernels != 0, per_kernel = c->tun.time_kernels == 1;
   if (timed) HIPCHK(hipEventRecord(c->tev[0], s));
@@ -900,7 +962,29 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   if (!out || !wave_J || !cyc_events || !cyc_glitches) return fail(PA_EINVAL, "pa_run: NULL output");
   BudgetScope bs(&c->mem);
   HIPCHK(hipSetDevice(c->device));
-  return run_pass(c, out, wave_J, cyc_events, cyc_glitches, evt_glitch, evt_state_before, nullptr);
+  return run_pass(c, loaded_scratch(c->ev), out, wave_J, cyc_events, cyc_glitches, evt_glitch, evt_state_before,
+                  nullptr);
+}
+
+int pa_run_noalloc(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
+                   uint8_t *evt_glitch, uint8_t *evt_state_before) {
+  if (!c) return fail(PA_EINVAL, "pa_run_noalloc: NULL context");
+  if (!c->has_design || !c->has_events)
+    return fail(PA_ESTATE, "pa_run_noalloc: design and events must be loaded first");
+  if (!out || !wave_J || !cyc_events || !cyc_glitches) return fail(PA_EINVAL, "pa_run_noalloc: NULL output");
+  if (!c->scratch.p)
+    return fail(PA_EHIP, "pa_run_noalloc: no address for the fixed scratch on device %d (%s)", c->device,
+                hipGetErrorString(c->scratch.err));
+  const size_t need = carve_scratch(c->ev, nullptr, nullptr);
+  if (need > (size_t)PA_NOALLOC_SCRATCH_BYTES)
+    return fail(PA_EINVAL,
+                "pa_run_noalloc: the loaded events need %zu bytes of pass scratch (%d blocks x %d cycles), "
+                "more than the fixed %zu; use pa_run",
+                need, c->ev.grid, c->ev.Cc, (size_t)PA_NOALLOC_SCRATCH_BYTES);
+  HIPCHK(hipSetDevice(c->device));
+  PassScratch sc;
+  carve_scratch(c->ev, c->scratch.p, &sc);
+  return run_pass(c, sc, out, wave_J, cyc_events, cyc_glitches, evt_glitch, evt_state_before, nullptr);
 }
 
 int pa_run_gates(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
@@ -912,7 +996,7 @@ int pa_run_gates(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events
     return fail(PA_EINVAL, "pa_run_gates: NULL output");
   BudgetScope bs(&c->mem);
   HIPCHK(hipSetDevice(c->device));
-  return run_pass(c, out, wave_J, cyc_events, cyc_glitches, nullptr, nullptr, gate_J);
+  return run_pass(c, loaded_scratch(c->ev), out, wave_J, cyc_events, cyc_glitches, nullptr, nullptr, gate_J);
 }
 
 int pa_get_window_stats(pa_ctx *c, pa_window_stats *out) {
@@ -1152,7 +1236,8 @@ int pa_run_text(pa_ctx *c, const char *text, int64_t text_len, int64_t t_clk, in
     if (rc != PA_OK) return rc;
     if (se != hipSuccess) return fail(PA_EHIP, "pa_run_text: HIP error %s", hipGetErrorString(se));
     pa_totals t{};
-    rc = run_pass(c, &t, wave_J + c0, cyc_events + c0, cyc_glitches + c0, nullptr, nullptr, nullptr);
+    rc = run_pass(c, loaded_scratch(c->ev), &t, wave_J + c0, cyc_events + c0, cyc_glitches + c0, nullptr, nullptr,
+                  nullptr);
     if (rc != PA_OK) return rc;
     acc[0] += t.e_int_J;
     acc[1] += t.e_sw_J;

@@ -154,6 +154,25 @@ typedef struct {
 int pa_run(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
            uint8_t *evt_glitch, uint8_t *evt_state_before);
 
+/* pa_run for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments, kernels and results, but the pass's own device scratch -- the
+ * per-block cycle bins, cycle counts and block totals and the finalize's
+ * result slots -- lives in one array of PA_NOALLOC_SCRATCH_BYTES that the
+ * library holds per device for the life of the process, and the call
+ * allocates nothing (no hipMalloc, no hipFree, no allocating library call).
+ * The loaded events need 2 * blocks * chunk_cycles * 8 + blocks * 64 + 128
+ * bytes of it (pieces rounded up to 256 bytes; blocks and chunk_cycles as
+ * pa_get_info reports them); more is PA_EINVAL (pa_run has no such limit).
+ * Every call on a device shares that device's array: calls that overlap in
+ * time on one device (two contexts on two streams, or two threads) race and
+ * give wrong results; calls that follow one another are safe (every call
+ * rewrites all of the array it reads).  PA_EHIP if the array's device
+ * address could not be looked up when the context was created. */
+#define PA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int pa_run_noalloc(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
+                   uint8_t *evt_glitch, uint8_t *evt_state_before);
+
 /* pa_run plus every gate's own energies, the per-gate power the paper ranks
  * hotspots by (its spatial-accuracy evaluation, Fig. 10, Table 3):
  *   gate_J[G][4]   device: per gate (caller's order) the internal, switching,

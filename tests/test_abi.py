@@ -106,3 +106,14 @@ def test_fp32_slew_thresholds_match_fp64_compares(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True)
     bad, n = map(int, out.stdout.split())
     assert out.returncode == 0 and bad == 0 and n > 1_000_000
+
+def test_noalloc_scratch_size_matches_header():
+    from eda_gate_level_amd import _pa
+
+    hdr = open(os.path.join(ROOT, "include", "pa.h")).read()
+    m = re.search(r"#define PA_NOALLOC_SCRATCH_BYTES \(([0-9 *]+)\)", hdr)
+    assert m, "PA_NOALLOC_SCRATCH_BYTES not in pa.h"
+    size = 1
+    for f in m.group(1).split("*"):
+        size *= int(f)
+    assert size == _pa.PA_NOALLOC_SCRATCH_BYTES
