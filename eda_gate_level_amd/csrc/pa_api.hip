@@ -212,7 +212,7 @@ struct PinnedBuf {
 struct LoadScratch {
   DBuf err, ev_pin, chunk_sorted, cbase, level, k0, k1, idx, perm, chunk, tmp, part;
   DBuf skey, sslew, sorig;            // the events in window order
-  DBuf winc, ws, bwin, wkey0, wkey1, widx, worder, wlane, lane_len, wave_len;  // lane streams
+  DBuf winc, ws, bwin, wkey0, wkey1, widx, worder, wlane, phase, wave_len;  // lane streams
 };
 
 }  // namespace
@@ -531,8 +531,9 @@ static int build_ranges(pa_ctx *c, Events &v) {
     HIPCHK(ls.wkey0.ensure(sizeof(uint64_t) * W));
     HIPCHK(ls.wkey1.ensure(sizeof(uint64_t) * W));
     HIPCHK(ls.worder.ensure(sizeof(uint32_t) * W));
-    HIPCHK(pa::launch_win_keys(W, ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(), nr, ls.wkey0.as<uint64_t>(),
-                               ls.widx.as<uint32_t>(), v.wlen.as<uint32_t>(), s));
+    HIPCHK(pa::launch_win_keys(W, ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(), nr, ls.skey.as<uint64_t>(),
+                               pa::out_code(v.pb), ls.wkey0.as<uint64_t>(), ls.widx.as<uint32_t>(),
+                               v.wlen.as<uint32_t>(), s));
     const int end_bit = 32 + (int)bits_for((uint64_t)std::max(nr - 1, 0));
     size_t tb = 0;
     HIPCHK(pa::sort_pairs_u64(ls.wkey0.as<uint64_t>(), ls.wkey1.as<uint64_t>(), ls.widx.as<uint32_t>(),
@@ -540,13 +541,13 @@ static int build_ranges(pa_ctx *c, Events &v) {
     HIPCHK(ls.tmp.ensure(tb));
     HIPCHK(pa::sort_pairs_u64(ls.wkey0.as<uint64_t>(), ls.wkey1.as<uint64_t>(), ls.widx.as<uint32_t>(),
                               ls.worder.as<uint32_t>(), W, end_bit, ls.tmp.p, &tb, s));
-    // ---- lanes: every window's place in its lane's stream, every wave's longest stream
+    // ---- phases: every window's place in its lane's stream, every wave's stream length
     HIPCHK(ls.wlane.ensure(sizeof(uint2) * W));
-    HIPCHK(ls.lane_len.ensure(sizeof(uint32_t) * (size_t)nr * pa::lane_plan_lanes()));
+    HIPCHK(ls.phase.ensure(sizeof(uint2) * pa::phase_plan_entries(W, nr)));
     HIPCHK(ls.wave_len.ensure(sizeof(uint32_t) * (size_t)nr * NW));
-    HIPCHK(pa::launch_lane_plan(nr, ls.bwin.as<uint32_t>(), ls.worder.as<uint32_t>(), v.wlen.as<uint32_t>(),
-                                ls.wlane.as<uint2>(), ls.lane_len.as<uint32_t>(), s));
-    HIPCHK(pa::launch_wave_len((int64_t)nr * NW, ls.lane_len.as<uint32_t>(), ls.wave_len.as<uint32_t>(), s));
+    HIPCHK(pa::launch_phase_plan(nr, ls.bwin.as<uint32_t>(), ls.worder.as<uint32_t>(), ls.wkey1.as<uint64_t>(),
+                                 v.wlen.as<uint32_t>(), ls.phase.as<uint2>(), ls.wlane.as<uint2>(),
+                                 ls.wave_len.as<uint32_t>(), s));
     HIPCHK(hipMemcpyAsync(wave_len.data(), ls.wave_len.p, sizeof(uint32_t) * wave_len.size(), hipMemcpyDeviceToHost,
                           s));
     HIPCHK(hipStreamSynchronize(s));
@@ -736,7 +737,7 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   f.tb = v.tb;
   f.gb = gb;
   v.gb = gb;
-  const uint32_t lkb = lc + v.pb + v.tb;
+  const uint32_t lkb = lc + v.pb + v.tb + 1;  // (kind, cycle, time, pin): kind 1 = the output pin
   const uint32_t qbits = bits_for((uint64_t)std::max<int32_t>(v.Q - 1, 0));
   const int32_t Q = v.Q;
 
@@ -762,7 +763,7 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
     }
     HIPCHK(pa::launch_gate_levels(G, d.pin_base.as<int64_t>(), d.gate_k.as<int32_t>(), pin_ptr, v.C, (int32_t)Cc,
                                   (int32_t)lc, kWindowEvents, fixed_level, level.as<uint8_t>(), s));
-    // ---- order (chunk, gate, cycle, pin, time) by radix sort
+    // ---- order (chunk, gate, kind, cycle, time, pin) by radix sort
     DBuf &k0 = c->ls.k0, &k1 = c->ls.k1, &idx = c->ls.idx, &perm = c->ls.perm, &tmp = c->ls.tmp;
     size_t tmp_bytes = 0;
     HIPCHK(k0.ensure(sizeof(uint64_t) * E));
@@ -1046,7 +1047,7 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
                                  ls.chunk.bytes + ls.tmp.bytes + ls.part.bytes + ls.skey.bytes + ls.sslew.bytes +
                                  ls.sorig.bytes + ls.winc.bytes + ls.ws.bytes + ls.bwin.bytes + ls.wkey0.bytes +
                                  ls.wkey1.bytes + ls.widx.bytes + ls.worder.bytes + ls.wlane.bytes +
-                                 ls.lane_len.bytes + ls.wave_len.bytes);
+                                 ls.phase.bytes + ls.wave_len.bytes);
   for (int k = 0; k < 4; ++k) info->kernel_ms[k] = c->kernel_ms[k];
   info->n_windows = c->has_events ? c->ev.n_windows : 0;
   info->n_slots = c->has_events ? c->ev.slots : 0;

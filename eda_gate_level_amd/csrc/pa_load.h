@@ -66,18 +66,19 @@ hipError_t launch_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, 
                          hipStream_t s);
 hipError_t launch_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted, uint32_t *cb, hipStream_t s);
 // lane streams of the pass (see pa_load.hip): head flags; window starts
-// (ws[W] = E); every block's first window; window sort keys, indices and
-// lengths; per (block, lane) the windows' places and the stream length; per
-// wave the longest stream; the scatter of the sorted events into the streams
+// (ws[W] = E); every block's first window; window sort keys (block, kind,
+// length), indices and lengths; the phase plan: every window's place in its
+// lane's stream and every wave's stream length (ph: phase_plan_entries(W, nr)
+// entries of scratch); the scatter of the sorted events into the streams
 hipError_t launch_head_flags(int64_t E, const uint64_t *skey, uint32_t *flag, hipStream_t s);
 hipError_t launch_win_starts(int64_t E, const uint64_t *skey, const uint32_t *winc, uint32_t *ws, hipStream_t s);
 hipError_t launch_block_windows(int32_t nr, int64_t E, const uint32_t *rstart, const uint64_t *skey,
                                 const uint32_t *winc, uint32_t W, uint32_t *bwin, hipStream_t s);
-hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, uint64_t *wkey,
-                           uint32_t *widx, uint32_t *wlen, hipStream_t s);
-hipError_t launch_lane_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint32_t *wlen,
-                            uint2 *wlane, uint32_t *lane_len, hipStream_t s);
-hipError_t launch_wave_len(int64_t n_waves, const uint32_t *lane_len, uint32_t *wave_len, hipStream_t s);
+hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, const uint64_t *skey,
+                           uint32_t outc, uint64_t *wkey, uint32_t *widx, uint32_t *wlen, hipStream_t s);
+size_t phase_plan_entries(uint32_t W, int32_t nr);
+hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint64_t *wkey,
+                             const uint32_t *wlen, uint2 *ph, uint2 *wlane, uint32_t *wave_len, hipStream_t s);
 hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
                           const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
                           uint64_t *key, float *slew, uint32_t *orig, hipStream_t s);

@@ -8,13 +8,16 @@
 //
 // The event load validates the per-pin streams (sorted, alternating values,
 // inside the window, positive slews) and lays them out: a radix sort puts
-// the events in (time chunk, gate, clock cycle, pin, time) order, and every
+// the events in (time chunk, gate, pin kind, clock cycle, time, pin) order,
+// the kind telling the gate's input pins from its output pin, and every
 // gate's part of a chunk is cut into windows whose length follows the gate's
 // event density (the paper's event-density-aware per-gate cycle
-// partitioning).  The first event of a window carries the gate's input state
-// at the window start, found from per-pin event-count parities (the state
-// reconstruction at a window start of Sec. 2.4.2).  Windows start on cycle
-// boundaries, so the per-pin glitch counter never crosses one.
+// partitioning), the input and the output events of a gate in windows of
+// their own.  The first event of an input window carries the gate's input
+// state at the window start, found from per-pin event-count parities (the
+// state reconstruction at a window start of Sec. 2.4.2); output events need
+// no state.  Windows start on cycle boundaries, so the per-pin glitch
+// counter never crosses one.
 #include <hip/hip_runtime.h>
 
 #include <hipcub/hipcub.hpp>
@@ -155,14 +158,16 @@ __device__ __forceinline__ uint64_t lk_of(const EvPos &p, const LayoutFmt &f) {
   return ((uint64_t)p.cyc << (f.pb + f.tb)) | ((uint64_t)p.tic << f.pb) | p.code;
 }
 
-// sort keys: (chunk, gate, lk) in one word, or (gate, lk) with the chunk apart
+// sort keys: (chunk, gate, kind, lk) in one word, or (gate, kind, lk) with the
+// chunk apart; kind = 1 for the output pin
 __global__ void k_sort_keys(int64_t E, const int64_t *evt_t, const uint32_t *ev_pin, const int32_t *pin_gate,
                             const uint8_t *pin_local, const int32_t *gate_k, LayoutFmt f, uint64_t *key,
                             uint32_t *chunk, uint32_t *idx) {
-  const uint32_t lkb = f.lc + f.pb + f.tb;
+  const uint32_t lkb = f.lc + f.pb + f.tb + 1;
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
     const EvPos p = ev_pos(e, evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
-    const uint64_t low = ((uint64_t)p.g << lkb) | lk_of(p, f);
+    const uint64_t kind = p.code == out_code(f.pb) ? 1u : 0u;
+    const uint64_t low = ((uint64_t)p.g << lkb) | (kind << (lkb - 1)) | lk_of(p, f);
     if (chunk) {
       key[e] = low;
       chunk[e] = (uint32_t)p.q;
@@ -190,13 +195,14 @@ __global__ void k_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, 
     const EvPos p = ev_pos(e, evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
     const uint32_t sl = level[p.g];
     const uint32_t w = p.cyc >> (f.lc - sl);
+    const uint32_t outc = out_code(f.pb);
     bool head = true;
     if (x > 0) {
       const EvPos pp = ev_pos(perm[x - 1], evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
-      head = !(pp.q == p.q && pp.g == p.g && (pp.cyc >> (f.lc - sl)) == w);
+      head = !(pp.q == p.q && pp.g == p.g && (pp.code == outc) == (p.code == outc) && (pp.cyc >> (f.lc - sl)) == w);
     }
     uint64_t S0 = 0;
-    if (head) {
+    if (head && p.code != outc) {
       // input state at the window start: pin value = init XOR parity of its earlier events
       const int64_t tw = ((int64_t)p.q * f.Cc + ((int64_t)w << (f.lc - sl))) * f.T;
       const int64_t pb = pin_base[p.g];
@@ -233,15 +239,21 @@ __global__ void k_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted,
 
 // ------------------------------------------------------ lane streams of the pass
 //
-// The sorted events (window order) are dealt to the pass's lanes: every block
-// owns a range of whole windows of one chunk; its windows, longest first, are
-// dealt to its 1024 lanes, each to one of the lanes with the shortest stream
-// so far (k_lane_plan), so that the lanes' event counts come out nearly equal.
-// A lane's windows follow one another in its stream, each padded to an even
-// length, and a wave's 64 streams are interleaved in pairs.
+// The sorted events (window order) are dealt to the pass's lanes in phases:
+// every block owns a range of whole windows of one chunk; its input windows,
+// longest first, are cut into groups of 64, and so are its output windows; a
+// group is a phase, in which each of a wave's 64 lanes walks one window of
+// the group (lane i the group's i-th window), all starting at the phase's
+// first slot, and the phase lasts as long as its longest window (rounded up
+// to an even count).  So every lane of a wave meets a window start at the same
+// step and walks windows of one kind.  The phases, longest first, go to the
+// block's 16 waves, each to the wave with the least work so far (the
+// longest-processing-time rule); a wave's phases follow one another in its
+// stream, and a wave's 64 streams are interleaved in pairs.
 
 constexpr int kLaneNT = 1024;  // lanes of a block of the pass
 constexpr int kLaneNW = kLaneNT / 64;
+constexpr int kPlanNT = 256;   // threads of a block of the phase plan
 
 __global__ void k_head_flags(int64_t E, const uint64_t *skey, uint32_t *flag) {
   for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x)
@@ -266,10 +278,11 @@ __global__ void k_block_windows(int32_t nr, int64_t E, const uint32_t *rstart, c
   }
 }
 
-// per window: (block << 32 | ~(even length)), so a stable sort orders every
-// block's windows longest first; wlen = the window's event count
-__global__ void k_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, uint64_t *wkey,
-                           uint32_t *widx, uint32_t *wlen) {
+// per window: (block << 32 | kind << 31 | ~length), so a stable sort orders
+// every block's input windows longest first, then its output windows
+// longest first; wlen = the window's event count
+__global__ void k_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, const uint64_t *skey,
+                           uint32_t outc, uint64_t *wkey, uint32_t *widx, uint32_t *wlen) {
   for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < W; w += (int64_t)gridDim.x * blockDim.x) {
     int lo = 0, hi = nr;  // last block with bwin[b] <= w
     while (hi - lo > 1) {
@@ -277,67 +290,60 @@ __global__ void k_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin,
       if (bwin[mid] <= (uint32_t)w) lo = mid; else hi = mid;
     }
     const uint32_t n = ws[w + 1] - ws[w];
+    const uint64_t kind = ((uint32_t)skey[ws[w]] & outc) == outc ? 1u : 0u;
     wlen[w] = n;
-    wkey[w] = ((uint64_t)lo << 32) | (uint64_t)(0xFFFFFFFFu - ((n + 1u) & ~1u));
+    wkey[w] = ((uint64_t)lo << 32) | (kind << 31) | (uint64_t)(0x7FFFFFFFu - n);
     widx[w] = (uint32_t)w;
   }
 }
 
-// One block of kLaneNT threads per block of the pass, one thread per lane:
-// the block's windows, longest first, are dealt in rounds of kLaneNT, each
-// round giving its windows to the lanes in order of their current length,
-// shortest first (the longest-processing-time rule, applied a round at a
-// time), so that the lanes' stream lengths come out nearly equal.  Every
-// window's place in its lane's stream goes to wlane[w] = (global wave << 6 |
-// lane, first slot), and every lane's stream length to lane_len.
-__global__ __launch_bounds__(kLaneNT) void k_lane_plan(const uint32_t *bwin, const uint32_t *worder,
-                                                       const uint32_t *wlen, uint2 *wlane, uint32_t *lane_len) {
-  __shared__ unsigned long long sk[kLaneNT];
-  __shared__ uint32_t snew[kLaneNT];
+// One block per block of the pass.  Its windows come in worder (input
+// windows longest first, then output windows longest first; sorted keys in
+// wkey); phase i of a kind is that kind's windows 64 i .. 64 i + 63.  One
+// thread deals the phases, longest first, to the waves (ph: the phase's
+// wave and first slot, in this block's part [floor(w0 / 64) + 2 b, ...) of
+// the array, which holds at least its phases); then every window gets its
+// place: wlane[w] = (global wave << 6 | lane, first slot).  wave_len = the
+// slots of every wave's stream.
+__global__ __launch_bounds__(kPlanNT) void k_phase_plan(const uint32_t *bwin, const uint32_t *worder,
+                                                        const uint64_t *wkey, const uint32_t *wlen, uint2 *ph,
+                                                        uint2 *wlane, uint32_t *wave_len) {
+  __shared__ uint32_t s_nin;
   const int b = blockIdx.x, u = threadIdx.x;
   const uint32_t w0 = bwin[b], nb = bwin[b + 1] - w0;
-  uint32_t len = 0;  // this lane's stream so far
-  for (uint32_t r0 = 0; r0 < nb; r0 += kLaneNT) {
-    // the lanes sorted by (length, lane): a bitonic sort over the block
-    sk[u] = ((unsigned long long)len << 16) | (unsigned)u;
-    __syncthreads();
-    for (int k = 2; k <= kLaneNT; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        const int ixj = u ^ j;
-        if (ixj > u) {
-          const unsigned long long x = sk[u], y = sk[ixj];
-          if (((u & k) == 0) ? (x > y) : (x < y)) {
-            sk[u] = y;
-            sk[ixj] = x;
-          }
-        }
-        __syncthreads();
-      }
+  uint2 *php = ph + (w0 >> 6) + 2u * (uint32_t)b;
+  if (u == 0) {
+    // input windows: those before the first key with the kind bit
+    uint32_t lo = 0, hi = nb;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if ((wkey[w0 + mid] >> 31) & 1u) hi = mid; else lo = mid + 1;
     }
-    // the round's window of rank r0 + u goes to the u-th shortest lane
-    const unsigned long long e = sk[u];
-    const uint32_t lane = (uint32_t)(e & 0xFFFFu), off = (uint32_t)(e >> 16);
-    uint32_t nl = off;
-    if (r0 + u < nb) {
-      const uint32_t w = worder[w0 + r0 + u];
-      wlane[w] = make_uint2(((uint32_t)(b * kLaneNW) + lane / 64u) << 6 | (lane % 64u), off);
-      nl = off + ((wlen[w] + 1u) & ~1u);  // the window's events padded to an even count
+    const uint32_t nin = lo, nout = nb - nin;
+    const uint32_t pin_ = (nin + 63) >> 6, pout = (nout + 63) >> 6;
+    auto plen = [&](uint32_t first) { return (wlen[worder[w0 + first]] + 1u) & ~1u; };
+    uint32_t load[kLaneNW];
+    for (int v = 0; v < kLaneNW; ++v) load[v] = 0;
+    uint32_t i = 0, o = 0;
+    while (i < pin_ || o < pout) {
+      const uint32_t li = i < pin_ ? plen(i * 64) : 0u, lo2 = o < pout ? plen(nin + o * 64) : 0u;
+      const bool take_in = i < pin_ && (o >= pout || li >= lo2);
+      int v = 0;
+      for (int x = 1; x < kLaneNW; ++x)
+        if (load[x] < load[v]) v = x;
+      php[take_in ? i : pin_ + o] = make_uint2((uint32_t)v, load[v]);
+      load[v] += take_in ? li : lo2;
+      if (take_in) ++i; else ++o;
     }
-    snew[lane] = nl;
-    __syncthreads();
-    len = snew[u];
-    __syncthreads();
+    for (int v = 0; v < kLaneNW; ++v) wave_len[(size_t)b * kLaneNW + v] = load[v];
+    s_nin = nin;
   }
-  lane_len[(size_t)b * kLaneNT + u] = len;
-}
-
-// events per lane of every wave: the longest of its 64 lane streams
-__global__ void k_wave_len(int64_t n_waves, const uint32_t *lane_len, uint32_t *wave_len) {
-  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < n_waves;
-       w += (int64_t)gridDim.x * blockDim.x) {
-    uint32_t m = 0;
-    for (int l = 0; l < 64; ++l) m = max(m, lane_len[w * 64 + l]);
-    wave_len[w] = m;
+  __syncthreads();
+  const uint32_t nin = s_nin, pin_ = (nin + 63) >> 6;
+  for (uint32_t r = u; r < nb; r += kPlanNT) {
+    const uint32_t i = r < nin ? r : r - nin;
+    const uint2 p = php[(r < nin ? 0u : pin_) + (i >> 6)];
+    wlane[worder[w0 + r]] = make_uint2(((uint32_t)b * kLaneNW + p.x) << 6 | (i & 63u), p.y);
   }
 }
 
@@ -512,21 +518,18 @@ hipError_t launch_block_windows(int32_t nr, int64_t E, const uint32_t *rstart, c
   hipLaunchKernelGGL(k_block_windows, dim3(grid_for(nr + 1)), dim3(kLT), 0, s, nr, E, rstart, skey, winc, W, bwin);
   return hipGetLastError();
 }
-hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, uint64_t *wkey,
-                           uint32_t *widx, uint32_t *wlen, hipStream_t s) {
+hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, const uint64_t *skey,
+                           uint32_t outc, uint64_t *wkey, uint32_t *widx, uint32_t *wlen, hipStream_t s) {
   if (W == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_win_keys, dim3(grid_for(W)), dim3(kLT), 0, s, W, ws, bwin, nr, wkey, widx, wlen);
+  hipLaunchKernelGGL(k_win_keys, dim3(grid_for(W)), dim3(kLT), 0, s, W, ws, bwin, nr, skey, outc, wkey, widx, wlen);
   return hipGetLastError();
 }
-hipError_t launch_lane_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint32_t *wlen,
-                            uint2 *wlane, uint32_t *lane_len, hipStream_t s) {
+size_t phase_plan_entries(uint32_t W, int32_t nr) { return (size_t)(W >> 6) + 2 * (size_t)nr + 2; }
+hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint64_t *wkey,
+                             const uint32_t *wlen, uint2 *ph, uint2 *wlane, uint32_t *wave_len, hipStream_t s) {
   if (nr <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lane_plan, dim3((unsigned)nr), dim3(kLaneNT), 0, s, bwin, worder, wlen, wlane, lane_len);
-  return hipGetLastError();
-}
-hipError_t launch_wave_len(int64_t n_waves, const uint32_t *lane_len, uint32_t *wave_len, hipStream_t s) {
-  if (n_waves == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_wave_len, dim3(grid_for(n_waves)), dim3(kLT), 0, s, n_waves, lane_len, wave_len);
+  hipLaunchKernelGGL(k_phase_plan, dim3((unsigned)nr), dim3(kPlanNT), 0, s, bwin, worder, wkey, wlen, ph, wlane,
+                     wave_len);
   return hipGetLastError();
 }
 hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,

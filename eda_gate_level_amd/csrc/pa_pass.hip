@@ -691,13 +691,17 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
 #pragma unroll
     for (int j = 0; j < NIN; ++j) th[j] = __builtin_inff();
     // running state: inputs after the last event, at the start of the current
-    // timestamp, pins switched in the current cycle, last cycle and time,
-    // leakage power of the current state
+    // timestamp, pins switched in the current cycle, last cycle, time and
+    // slew, leakage power of the current state
     uint32_t S = 0, St = 0, seen = 0, pcyc = ~0u, ptic = 0;
+    float pslew = 1.f;
     double lkS = L.leak[0];
+    bool out_phase = false;  // the kind of the current phase's windows (wave-uniform)
     lds_u32 *prec = L.prec + (wid * (kmax + 1) * 64 + lane) * 2;
 
-    auto window_head = [&](uint64_t K, const uint3 &rec) {
+    // a phase of input windows starts: every lane sets up its window (a lane
+    // without one gets a valid, unused set-up from the pad key)
+    auto head_in = [&](uint64_t K, const uint3 &rec) {
       const uint32_t h = (uint32_t)(K >> 32);
       gate = (h >> 10) & gmask;
       const double cap = __hiloint2double((int)rec.y, (int)rec.x);
@@ -709,7 +713,6 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
       axb = mad24(cell, NS - 1, 0u);
       const f64x2 cx = L.caxw[mad24(cell, NC - 1, cseg)];
       fc = (cap - cx.x) * cx.y;  // position on the gate's cap segment (Sec. 2.4.1, Fig. 2)
-      esw = a.hv2 * cap;         // Eq. 1
 #pragma unroll
       for (int i = 0; i < NIN; i += 4) {
         const f32x4 t4 = *(const lds_f32x4 *)(L.thr + mad24(cell, nthr, i));
@@ -724,31 +727,37 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
       pcyc = ~0u;
       lkS = L.leak[lb + S];
     };
+    // a phase of output windows starts: only the switching energy of the gate's load
+    auto head_out = [&](uint64_t K, const uint3 &rec) {
+      gate = ((uint32_t)(K >> 32) >> 10) & gmask;
+      esw = a.hv2 * __hiloint2double((int)rec.y, (int)rec.x);  // Eq. 1
+      pcyc = ~0u;
+    };
 
-    // one event of the lane's walk (Sec. 2.4.1-2.4.2, Fig. 7)
-    auto event = [&](uint64_t K, float sl) {
+    // one input-pin event (Sec. 2.4.1-2.4.2, Fig. 7); a pad slot (dummy cycle
+    // Cc) toggles nothing, so its leakage change is zero, and adds nothing
+    auto event_in = [&](uint64_t K, float sl) {
       const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
       const uint32_t code = lk & outc;                                     // pin code
       const uint32_t tic = (lk >> pb) & tmask;                             // time inside the cycle
       const uint32_t cyc = (uint32_t)((((uint64_t)(hw >> ysh)) << 32 | lk) >> cs);  // cycle in the chunk
-      const bool rise = (hw >> 8) & 1u;                                    // the pin's value after the event
-      const bool input = code != outc;
+      const bool real = cyc < (uint32_t)Cc;
       const bool newcyc = cyc != pcyc;
       // events of one timestamp all see the state before the first of them (Sec. 2.4.2)
       if (newcyc || tic != ptic) St = S;
       if (newcyc) seen = 0u;
-      const uint32_t bit = 1u << code;
+      const uint32_t cl = real ? code : 0u;
+      const uint32_t bit = real ? 1u << code : 0u;
       const bool glitch = (seen & bit) != 0u;  // the pin already switched in this cycle (Fig. 7)
       seen |= bit;
       pcyc = cyc;
       ptic = tic;
       const uint32_t Sm = St;
-      if (input) S ^= bit;
+      S ^= bit;
       // the slew segment: inner axis points at or below the slew (Sec. 2.4.1, Fig. 2)
       uint32_t n = 0;
 #pragma unroll
       for (int i = 0; i < NIN; ++i) n += sl >= th[i] ? 1u : 0u;
-      const uint32_t cl = input ? code : 0u;
       // (state, pin) row, then the slew segment and the cap segment: every factor is small
       // kpsz is a loop-carried value whose small range the instruction
       // selector cannot see: an empty asm hides it from the optimizer too, so
@@ -759,33 +768,61 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
       const lds_f64 *Lp = L.lut + lo;
       const double L00 = Lp[0], L01 = Lp[1], L10 = Lp[NC], L11 = Lp[NC + 1];
       const f64x2 aw = L.axw[axb + n];
-      const double lkn = L.leak[lb + (S & 0xFFu)];  // leakage of the state after the event (Eq. 4)
+      const double lkn = L.leak[lb + S];  // leakage of the state after the event (Eq. 4)
       const double fa = ((double)sl - aw.x) * aw.y;
       const double v0 = L00 + fc * (L01 - L00);
       const double v1 = L10 + fc * (L11 - L10);
-      const double Eint = v0 + fa * (v1 - v0);
-      double E = input ? Eint : (rise ? esw : 0.0);  // Eq. 1: 0->1 output events only
+      double E = v0 + fa * (v1 - v0);
       const double dp = lkn - lkS;  // the input toggle moves the leakage power
       lkS = lkn;
       const double ct = dp * (double)tic;
       e_lkt += ct;
-      lds_u32 *pr = prec + min(code, kmax) * 128;
+      lds_u32 *pr = prec + cl * 128;
       if (glitch) {
         // Eq. 2 (reading): pulse width and the slews of the pin's previous event in the cycle and this one
-        const uint32_t ptic_pin = pr[0], pslew = pr[1];
+        const uint32_t ptic_pin = pr[0], pslew_pin = pr[1];
         const double pw = (double)(tic - ptic_pin);
-        const double rr = pw / (0.5 * ((double)sl + (double)__uint_as_float(pslew)));
+        const double rr = pw / (0.5 * ((double)sl + (double)__uint_as_float(pslew_pin)));
         E *= rr > 1.0 ? 1.0 : rr;
         e_gl += E;
       }
       pr[0] = tic;
       pr[1] = __float_as_uint(sl);
-      e_int = fma(E, (input && !glitch) ? 1.0 : 0.0, e_int);
-      e_sw = fma(E, (!input && !glitch) ? 1.0 : 0.0, e_sw);
-      if (cyc < (uint32_t)Cc) {  // a pad slot adds nothing (its lanes would all hit one bin)
+      if (real) {  // a pad slot adds nothing (its lanes would all hit one bin)
+        e_int += glitch ? 0.0 : E;
         lds_bin *bp = L.bins + (cyc & 0xFFFu);
         __hip_atomic_fetch_add(&bp->w, fma(ct, -tick, E), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         __hip_atomic_fetch_add(&bp->d, dp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_fetch_add(&bp->c, 1ull | ((unsigned long long)glitch << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+    };
+
+    // one output-pin event: 1/2 c Vdd^2 for 0->1 (Eq. 1), scaled by r_gl when
+    // the pin already switched in this cycle (Eq. 2, Fig. 7); the window's only
+    // pin is the output, so its previous event is the lane's previous event.
+    // A pad slot (dummy cycle Cc, value 0) adds nothing.
+    auto event_out = [&](uint64_t K, float sl) {
+      const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
+      const uint32_t tic = (lk >> pb) & tmask;
+      const uint32_t cyc = (uint32_t)((((uint64_t)(hw >> ysh)) << 32 | lk) >> cs);
+      const bool rise = (hw >> 8) & 1u;
+      const bool real = cyc < (uint32_t)Cc;
+      const bool glitch = real && cyc == pcyc;
+      double E = rise ? esw : 0.0;
+      if (glitch) {
+        const double pw = (double)(tic - ptic);
+        const double rr = pw / (0.5 * ((double)sl + (double)pslew));
+        E *= rr > 1.0 ? 1.0 : rr;
+        e_gl += E;
+      }
+      pcyc = cyc;
+      ptic = tic;
+      pslew = sl;
+      if (real) {
+        e_sw += glitch ? 0.0 : E;
+        lds_bin *bp = L.bins + (cyc & 0xFFFu);
+        __hip_atomic_fetch_add(&bp->w, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         __hip_atomic_fetch_add(&bp->c, 1ull | ((unsigned long long)glitch << 32), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_WORKGROUP);
       }
@@ -802,9 +839,21 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
       for (int i = 0; i < GP; ++i) {
         if (p0 + i >= npair) break;
         const uint64_t K0 = k0[i].x, K1 = k0[i].y;
-        if ((uint32_t)(K0 >> 41) & 1u) window_head(K0, r0[i]);
-        event(K0, s0[i].x);
-        event(K1, s0[i].y);
+        // windows start only at phase starts, where every lane with a window
+        // has its head: one wave-uniform test, and the phase's kind from the heads
+        const bool head = ((uint32_t)(K0 >> 41) & 1u) != 0u;
+        if (__ballot(head) != 0ull) {
+          out_phase = __ballot(head && ((uint32_t)K0 & outc) == outc) != 0ull;
+          if (out_phase) head_out(K0, r0[i]);
+          else head_in(K0, r0[i]);
+        }
+        if (out_phase) {
+          event_out(K0, s0[i].x);
+          event_out(K1, s0[i].y);
+        } else {
+          event_in(K0, s0[i].x);
+          event_in(K1, s0[i].y);
+        }
       }
 #pragma unroll
       for (int i = 0; i < GP; ++i) {

@@ -97,7 +97,9 @@ def test_launch_grid_does_not_change_results(grid):
 def test_fixed_windows_do_not_change_results(n_fix):
     """Fixed-length windows (the layout the paper's density-aware windows
     replace) give the same results; with one-cycle windows every (gate,
-    cycle) run is a window, so the window count is the number of such runs."""
+    cycle, pin kind) run is a window (a gate's input events and its output
+    events go to windows of their own), so the window count is the number of
+    such runs."""
     import eda_gate_level_amd as pa
 
     d, t = _random(seed=9, G=400, C=120, rate=0.3)
@@ -111,7 +113,9 @@ def test_fixed_windows_do_not_change_results(n_fix):
         an.close()
     pb = d.pin_base()
     gate = np.repeat(np.repeat(np.arange(d.n_gates), np.diff(pb)), np.diff(t.pin_ptr))
-    run = gate.astype(np.int64) * t.n_cycles + t.evt_t // t.t_clk
+    pin = np.repeat(np.arange(t.n_pins), np.diff(t.pin_ptr))
+    is_out = (pin == pb[1:][gate] - 1).astype(np.int64)  # the gate's last pin is its output
+    run = (gate.astype(np.int64) * t.n_cycles + t.evt_t // t.t_clk) * 2 + is_out
     if n_fix == 1:
         assert st["n_windows"] == np.unique(run).shape[0]
         assert st["max"] == np.bincount(np.unique(run, return_inverse=True)[1]).max()
