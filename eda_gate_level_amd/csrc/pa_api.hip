@@ -172,12 +172,17 @@ struct Events {
   uint64_t pad_key = 0;            // key of an empty slot of the lane streams
   DBuf blk_lut;                    // walk kernel: every block's LUT range (first entry, entries)
   int32_t walk_lut = 0;            // walk kernel: LDS doubles for the largest range (0: not used)
+  // walk kernel: the 8-byte-slot stream (keys, slews with a code or value bit) with a
+  // header pair in front of every phase; tbc = tic bits, ck = pin-code bits in the key
+  bool compact_ok = false;         // the chunk leaves the compact key its bits
+  DBuf ckey, cslew;
+  uint32_t tbc = 0, ck = 0;
   int32_t n_ranges = 0, grid = 1;
   DBuf blk_wave, blk_cnt, blk_part, res;
   int64_t bytes() const {
     return (int64_t)(key.bytes + slew.bytes + orig.bytes + pin_init.bytes + rstart.bytes + rchunk.bytes +
                      chunk_blk.bytes + wdesc.bytes + wlen.bytes + l0.bytes + lplan.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
-                     res.bytes + blk_lut.bytes);
+                     res.bytes + blk_lut.bytes + ckey.bytes + cslew.bytes);
   }
 };
 
@@ -456,6 +461,13 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
 #define PA_WINDOW_EVENTS 32.0
 #endif
 static constexpr double kWindowEvents = PA_WINDOW_EVENTS;
+#ifndef PA_WALK_COST_IN
+#define PA_WALK_COST_IN 5
+#endif
+#ifndef PA_WALK_COST_OUT
+#define PA_WALK_COST_OUT 2
+#endif
+static constexpr uint32_t kWalkCostIn = PA_WALK_COST_IN, kWalkCostOut = PA_WALK_COST_OUT;
 
 // Block ranges of the pass and the lane streams.  Every chunk's events are cut
 // into pieces of about E / target events (never across a chunk, so a block's
@@ -523,10 +535,27 @@ static int build_ranges(pa_ctx *c, Events &v) {
   HIPCHK(ls.bwin.ensure(sizeof(uint32_t) * ((size_t)nr + 1)));
   HIPCHK(v.wlen.ensure(sizeof(uint32_t) * std::max<size_t>(W, 1)));
   std::vector<uint32_t> wave_len((size_t)nr * NW, 0);
+  v.walk_lut = 0;
   if (W > 0) {
     HIPCHK(pa::launch_win_starts(E, ls.skey.as<uint64_t>(), ls.winc.as<uint32_t>(), ls.ws.as<uint32_t>(), s));
     HIPCHK(pa::launch_block_windows(nr, E, v.rstart.as<uint32_t>(), ls.skey.as<uint64_t>(), ls.winc.as<uint32_t>(), W,
                                     ls.bwin.as<uint32_t>(), s));
+    // ---- the walk kernel: every block's LUT range, used when each fits in a block's LDS
+    if (v.pad_key != 0 && v.compact_ok) {
+      const int32_t room = pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax);
+      HIPCHK(v.blk_lut.ensure(sizeof(uint2) * (size_t)nr));
+      HIPCHK(pa::launch_block_luts(nr, ls.skey.as<uint64_t>(), ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(),
+                                   d.gate_rec.as<uint4>(), d.cell_meta.as<uint2>(), v.gb, d.n_slew, d.n_cap,
+                                   v.blk_lut.as<uint2>(), s));
+      std::vector<uint2> hl((size_t)nr);
+      HIPCHK(hipMemcpyAsync(hl.data(), v.blk_lut.p, sizeof(uint2) * hl.size(), hipMemcpyDeviceToHost, s));
+      HIPCHK(hipStreamSynchronize(s));
+      uint32_t most = 0;
+      for (const uint2 &r : hl) most = std::max(most, r.y);
+      // at least the entries a lane without a window reads (its row 0, segment n, cap segment 0)
+      most = std::max<uint32_t>(most, 2u * (uint32_t)(d.n_slew * d.n_cap));
+      if ((int64_t)most <= (int64_t)room) v.walk_lut = (int32_t)most;
+    }
     // ---- every block's windows, longest first (a stable sort keeps gate order among equals)
     HIPCHK(ls.wkey0.ensure(sizeof(uint64_t) * W));
     HIPCHK(ls.wkey1.ensure(sizeof(uint64_t) * W));
@@ -545,8 +574,12 @@ static int build_ranges(pa_ctx *c, Events &v) {
     HIPCHK(ls.wlane.ensure(sizeof(uint2) * W));
     HIPCHK(ls.phase.ensure(sizeof(uint2) * pa::phase_plan_entries(W, nr)));
     HIPCHK(ls.wave_len.ensure(sizeof(uint32_t) * (size_t)nr * NW));
+    // the walk kernel's slots of an input phase cost about 2.5 times those of
+    // an output phase (no table reads, leakage or pin records there)
+    const bool walk = v.walk_lut > 0;
     HIPCHK(pa::launch_phase_plan(nr, ls.bwin.as<uint32_t>(), ls.worder.as<uint32_t>(), ls.wkey1.as<uint64_t>(),
-                                 v.wlen.as<uint32_t>(), ls.phase.as<uint2>(), ls.wlane.as<uint2>(),
+                                 v.wlen.as<uint32_t>(), walk ? 2u : 0u, walk ? kWalkCostIn : 1u,
+                                 walk ? kWalkCostOut : 1u, ls.phase.as<uint2>(), ls.wlane.as<uint2>(),
                                  ls.wave_len.as<uint32_t>(), s));
     HIPCHK(hipMemcpyAsync(wave_len.data(), ls.wave_len.p, sizeof(uint32_t) * wave_len.size(), hipMemcpyDeviceToHost,
                           s));
@@ -581,6 +614,17 @@ static int build_ranges(pa_ctx *c, Events &v) {
     HIPCHK(pa::launch_scatter(E, ls.skey.as<uint64_t>(), ls.sslew.as<float>(), ls.sorig.as<uint32_t>(),
                               ls.winc.as<uint32_t>(), ls.ws.as<uint32_t>(), ls.wlane.as<uint2>(), v.wdesc.as<uint2>(),
                               v.key.as<uint64_t>(), v.slew.as<float>(), v.orig.as<uint32_t>(), s));
+  // the walk kernel's compact stream and the phases' header pairs
+  if (v.walk_lut > 0) {
+    HIPCHK(v.ckey.ensure(sizeof(uint32_t) * Sa));
+    HIPCHK(v.cslew.ensure(sizeof(uint32_t) * Sa));
+    HIPCHK(pa::launch_compact(Sa, v.key.as<uint64_t>(), v.slew.as<float>(), v.pad_key, v.pb, v.tb, v.gb, v.tbc, v.ck,
+                              v.ckey.as<uint32_t>(), v.cslew.as<uint32_t>(), s));
+    const uint32_t hdr = ((1u << v.tbc) - 1u) << v.ck;
+    HIPCHK(pa::launch_headers(W, ls.wlane.as<uint2>(), v.wdesc.as<uint2>(), ls.ws.as<uint32_t>(),
+                              ls.skey.as<uint64_t>(), d.gate_rec.as<uint4>(), v.gb, pa::out_code(v.pb), hdr,
+                              1u << (v.tbc + v.ck), v.ckey.as<uint32_t>(), v.cslew.as<uint32_t>(), s));
+  }
   // the cells whose LUTs every block copies into its spare LDS
   v.lut_lds = pa::pass_lut_lds_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax);
   if (c->tun.lut_lds_kib < 0) v.lut_lds = 0;
@@ -592,21 +636,6 @@ static int build_ranges(pa_ctx *c, Events &v) {
                                v.lplan.as<uint2>(), s));
   } else {
     v.lut_lds = 0;
-  }
-  // the walk kernel: every block's LUT range, used when each fits in a block's LDS
-  v.walk_lut = 0;
-  if (nr > 0 && W > 0 && v.pad_key != 0 && c->tun.lut_lds_kib == 0 && pa::walk_supported(d.n_slew, d.n_cap)) {
-    const int32_t room = pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax);
-    HIPCHK(v.blk_lut.ensure(sizeof(uint2) * (size_t)nr));
-    HIPCHK(pa::launch_block_luts(nr, ls.skey.as<uint64_t>(), ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(),
-                                 d.gate_rec.as<uint4>(), d.cell_meta.as<uint2>(), v.gb, d.n_slew, d.n_cap,
-                                 v.blk_lut.as<uint2>(), s));
-    std::vector<uint2> hl((size_t)nr);
-    HIPCHK(hipMemcpyAsync(hl.data(), v.blk_lut.p, sizeof(uint2) * hl.size(), hipMemcpyDeviceToHost, s));
-    HIPCHK(hipStreamSynchronize(s));
-    uint32_t most = 0;
-    for (const uint2 &r : hl) most = std::max(most, r.y);
-    if ((int64_t)most <= (int64_t)room) v.walk_lut = (int32_t)std::max<uint32_t>(most, 2);
   }
   // leakage power at t = 0, from the initial pin values
   DBuf &part = ls.part;
@@ -714,10 +743,20 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   Cc_want = std::min<int64_t>(Cc_want, (int64_t)pa::pass_max_chunk_cycles());
   const uint32_t lc_use = lc_max > 0 ? lc_max - 1 : 0;
   if (lc_use < 31) Cc_want = std::min<int64_t>(Cc_want, int64_t(1) << lc_use);
+  // the walk kernel's 32-bit key: cycle, tic (bits of t_clk itself, so the
+  // tic field is never all ones in an event) and the pin code's high bits;
+  // unless the caller fixed the chunk, it is cut to what that key holds
+  v.tbc = bits_for((uint64_t)t_clk);
+  v.ck = d.kmax > 2 ? bits_for((uint64_t)((d.kmax - 1) >> 1)) : 0;
+  const bool compact_want = pa::walk_supported(d.n_slew, d.n_cap) && c->tun.lut_lds_kib == 0 &&
+                            d.n_cells < (1 << 20) && v.tbc + v.ck + 6 <= 32;
+  if (compact_want && c->tun.chunk_cycles == 0)
+    Cc_want = std::min<int64_t>(Cc_want, int64_t(1) << (32 - v.tbc - v.ck));
   int64_t Cc = 1;
   while (Cc * 2 <= Cc_want) Cc *= 2;
   uint32_t lc = 0;
   while ((int64_t(1) << lc) < Cc) ++lc;
+  v.compact_ok = compact_want && lc + v.tbc + v.ck <= 32;
   v.Cc = (int32_t)Cc;
   v.Q = (int32_t)((v.C + Cc - 1) / Cc);
   // the pad key: an output-pin 1->0 event at time 0 of cycle Cc (no event's
@@ -894,6 +933,10 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   a.pad_key = v.pad_key;
   a.blk_lut = v.walk_lut > 0 ? v.blk_lut.as<uint2>() : nullptr;
   a.walk_lut = v.walk_lut;
+  a.ckey = v.walk_lut > 0 ? v.ckey.as<uint32_t>() : nullptr;
+  a.cslew = v.walk_lut > 0 ? v.cslew.as<uint32_t>() : nullptr;
+  a.tbc = v.tbc;
+  a.ck = v.ck;
   a.blk_wave = sc.blk_wave;
   a.blk_cnt = sc.blk_cnt;
   a.blk_part = sc.blk_part;

@@ -95,6 +95,12 @@ struct PassArgs {
   // the walk kernel: every block's LUT range [x, x + y) in doubles, all of it in the block's LDS
   const uint2 *blk_lut;
   int32_t walk_lut;           // LDS doubles reserved for the largest range (0: the walk kernel is not used)
+  // the walk kernel's stream, slot for slot with key/slew: 32-bit keys (cycle << (tbc + ck) | tic << ck |
+  // pin code >> 1; ~0 = empty; an all-ones tic field = a phase's header pair) and slews whose sign bit
+  // holds the pin code's low bit (input pins) or the new value (output pin)
+  const uint32_t *ckey;
+  const uint32_t *cslew;
+  uint32_t tbc, ck;
   // per-block results, reduced by the finalize kernel
   double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
   unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32

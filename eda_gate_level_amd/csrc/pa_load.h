@@ -77,8 +77,18 @@ hipError_t launch_block_windows(int32_t nr, int64_t E, const uint32_t *rstart, c
 hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin, int32_t nr, const uint64_t *skey,
                            uint32_t outc, uint64_t *wkey, uint32_t *widx, uint32_t *wlen, hipStream_t s);
 size_t phase_plan_entries(uint32_t W, int32_t nr);
+// hp: slots of a header pair in front of every phase (2) or none (0); w_in,
+// w_out: relative cost of a slot of an input or an output phase
 hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint64_t *wkey,
-                             const uint32_t *wlen, uint2 *ph, uint2 *wlane, uint32_t *wave_len, hipStream_t s);
+                             const uint32_t *wlen, uint32_t hp, uint32_t w_in, uint32_t w_out, uint2 *ph,
+                             uint2 *wlane, uint32_t *wave_len, hipStream_t s);
+// the walk kernel's 8-byte-slot stream from the 16-byte one, then every window's header pair
+hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,
+                          uint32_t tb, uint32_t gb, uint32_t tbc, uint32_t ck, uint32_t *ckey, uint32_t *cslew,
+                          hipStream_t s);
+hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
+                          const uint4 *gate_rec, uint32_t gb, uint32_t outc, uint32_t hdr, uint32_t out_bit,
+                          uint32_t *ckey, uint32_t *cslew, hipStream_t s);
 hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
                           const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
                           uint64_t *key, float *slew, uint32_t *orig, hipStream_t s);

@@ -300,14 +300,17 @@ __global__ void k_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin,
 // One block per block of the pass.  Its windows come in worder (input
 // windows longest first, then output windows longest first; sorted keys in
 // wkey); phase i of a kind is that kind's windows 64 i .. 64 i + 63.  One
-// thread deals the phases, longest first, to the waves (ph: the phase's
+// thread deals the phases, costliest first, to the waves, each to the wave
+// with the least cost so far (a phase costs its slots times w_in or w_out,
+// the relative cost of a slot of its kind in the pass); ph gets the phase's
 // wave and first slot, in this block's part [floor(w0 / 64) + 2 b, ...) of
-// the array, which holds at least its phases); then every window gets its
+// the array, which holds at least its phases.  Then every window gets its
 // place: wlane[w] = (global wave << 6 | lane, first slot).  wave_len = the
 // slots of every wave's stream.
 __global__ __launch_bounds__(kPlanNT) void k_phase_plan(const uint32_t *bwin, const uint32_t *worder,
-                                                        const uint64_t *wkey, const uint32_t *wlen, uint2 *ph,
-                                                        uint2 *wlane, uint32_t *wave_len) {
+                                                        const uint64_t *wkey, const uint32_t *wlen, uint32_t hp,
+                                                        uint32_t w_in, uint32_t w_out, uint2 *ph, uint2 *wlane,
+                                                        uint32_t *wave_len) {
   __shared__ uint32_t s_nin;
   const int b = blockIdx.x, u = threadIdx.x;
   const uint32_t w0 = bwin[b], nb = bwin[b + 1] - w0;
@@ -321,18 +324,21 @@ __global__ __launch_bounds__(kPlanNT) void k_phase_plan(const uint32_t *bwin, co
     }
     const uint32_t nin = lo, nout = nb - nin;
     const uint32_t pin_ = (nin + 63) >> 6, pout = (nout + 63) >> 6;
-    auto plen = [&](uint32_t first) { return (wlen[worder[w0 + first]] + 1u) & ~1u; };
+    auto plen = [&](uint32_t first) { return hp + ((wlen[worder[w0 + first]] + 1u) & ~1u); };
     uint32_t load[kLaneNW];
-    for (int v = 0; v < kLaneNW; ++v) load[v] = 0;
+    uint64_t cost[kLaneNW];
+    for (int v = 0; v < kLaneNW; ++v) load[v] = 0, cost[v] = 0;
     uint32_t i = 0, o = 0;
     while (i < pin_ || o < pout) {
       const uint32_t li = i < pin_ ? plen(i * 64) : 0u, lo2 = o < pout ? plen(nin + o * 64) : 0u;
-      const bool take_in = i < pin_ && (o >= pout || li >= lo2);
+      const uint64_t ci = (uint64_t)li * w_in, co = (uint64_t)lo2 * w_out;
+      const bool take_in = i < pin_ && (o >= pout || ci >= co);
       int v = 0;
       for (int x = 1; x < kLaneNW; ++x)
-        if (load[x] < load[v]) v = x;
+        if (cost[x] < cost[v]) v = x;
       php[take_in ? i : pin_ + o] = make_uint2((uint32_t)v, load[v]);
       load[v] += take_in ? li : lo2;
+      cost[v] += take_in ? ci : co;
       if (take_in) ++i; else ++o;
     }
     for (int v = 0; v < kLaneNW; ++v) wave_len[(size_t)b * kLaneNW + v] = load[v];
@@ -343,7 +349,57 @@ __global__ __launch_bounds__(kPlanNT) void k_phase_plan(const uint32_t *bwin, co
   for (uint32_t r = u; r < nb; r += kPlanNT) {
     const uint32_t i = r < nin ? r : r - nin;
     const uint2 p = php[(r < nin ? 0u : pin_) + (i >> 6)];
-    wlane[worder[w0 + r]] = make_uint2(((uint32_t)b * kLaneNW + p.x) << 6 | (i & 63u), p.y);
+    wlane[worder[w0 + r]] = make_uint2(((uint32_t)b * kLaneNW + p.x) << 6 | (i & 63u), p.y + hp);
+  }
+}
+
+// The walk kernel's stream, 8 bytes a slot (the lane streams above, slot for
+// slot).  An event: key = cycle << (tbc + ck) | tic << ck | pin code >> 1, and
+// the slew's bits with the sign bit (always 0 in a slew) holding the pin
+// code's low bit (input pins) or the pin's new value (output pin).  tbc =
+// bits of the clock period, so the tic field is never all ones in an event.
+// An empty slot: key ~0, slew 1.0.
+__global__ void k_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,
+                          uint32_t tb, uint32_t gb, uint32_t tbc, uint32_t ck, uint32_t *ckey, uint32_t *cslew) {
+  const uint32_t outc = out_code(pb), cs = pb + tb, ysh = 10u + gb;
+  const uint32_t tmask = (1u << tb) - 1u;
+  for (int64_t y = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; y < n; y += (int64_t)gridDim.x * blockDim.x) {
+    const uint64_t K = key[y];
+    uint32_t kw = 0xFFFFFFFFu, sw = 0x3F800000u;
+    if (K != pad_key) {
+      const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
+      const uint32_t code = lk & outc;
+      const uint32_t tic = (lk >> pb) & tmask;
+      const uint32_t cyc = (uint32_t)((((uint64_t)(hw >> ysh)) << 32 | lk) >> cs);
+      const bool out = code == outc;
+      kw = (cyc << (tbc + ck)) | (tic << ck) | (out ? 0u : (code >> 1));
+      sw = __float_as_uint(slew[y]) | ((out ? ((hw >> 8) & 1u) : (code & 1u)) << 31);
+    }
+    ckey[y] = kw;
+    cslew[y] = sw;
+  }
+}
+
+// Every window's header pair, the two slots in front of its first event in
+// the compact stream: keys (hdr | output << (tbc + ck), cell | cap segment <<
+// 20 | start state << 24 for an input window, 0 for an output window), slews
+// the gate's load (fp64 bits, low word first).  hdr has an all-ones tic field.
+__global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
+                          const uint4 *gate_rec, uint32_t gb, uint32_t outc, uint32_t hdr, uint32_t out_bit,
+                          uint32_t *ckey, uint32_t *cslew) {
+  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < W; w += (int64_t)gridDim.x * blockDim.x) {
+    const uint2 wl = wlane[w];
+    const uint32_t j = wl.y - 2u;  // the header pair: an even slot of the lane's stream
+    const uint32_t y = wdesc[wl.x >> 6].x + (j >> 1) * 128u + 2u * (wl.x & 63u);
+    const uint64_t K = skey[ws[w]];
+    const uint32_t hw = (uint32_t)(K >> 32);
+    const uint32_t g = (hw >> 10) & ((1u << gb) - 1u);
+    const bool out = ((uint32_t)K & outc) == outc;
+    const uint4 r = gate_rec[g];
+    ckey[y] = hdr | (out ? out_bit : 0u);
+    ckey[y + 1] = out ? 0u : ((r.z & 0xFFFFFu) | ((r.z >> 24) << 20) | ((hw & 0xFFu) << 24));
+    cslew[y] = r.x;
+    cslew[y + 1] = r.y;
   }
 }
 
@@ -526,10 +582,27 @@ hipError_t launch_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin,
 }
 size_t phase_plan_entries(uint32_t W, int32_t nr) { return (size_t)(W >> 6) + 2 * (size_t)nr + 2; }
 hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint64_t *wkey,
-                             const uint32_t *wlen, uint2 *ph, uint2 *wlane, uint32_t *wave_len, hipStream_t s) {
+                             const uint32_t *wlen, uint32_t hp, uint32_t w_in, uint32_t w_out, uint2 *ph,
+                             uint2 *wlane, uint32_t *wave_len, hipStream_t s) {
   if (nr <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_phase_plan, dim3((unsigned)nr), dim3(kPlanNT), 0, s, bwin, worder, wkey, wlen, ph, wlane,
-                     wave_len);
+  hipLaunchKernelGGL(k_phase_plan, dim3((unsigned)nr), dim3(kPlanNT), 0, s, bwin, worder, wkey, wlen, hp, w_in, w_out,
+                     ph, wlane, wave_len);
+  return hipGetLastError();
+}
+hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,
+                          uint32_t tb, uint32_t gb, uint32_t tbc, uint32_t ck, uint32_t *ckey, uint32_t *cslew,
+                          hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_compact, dim3(grid_for(n)), dim3(kLT), 0, s, n, key, slew, pad_key, pb, tb, gb, tbc, ck, ckey,
+                     cslew);
+  return hipGetLastError();
+}
+hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
+                          const uint4 *gate_rec, uint32_t gb, uint32_t outc, uint32_t hdr, uint32_t out_bit,
+                          uint32_t *ckey, uint32_t *cslew, hipStream_t s) {
+  if (W == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_headers, dim3(grid_for(W)), dim3(kLT), 0, s, W, wlane, wdesc, ws, skey, gate_rec, gb, outc, hdr,
+                     out_bit, ckey, cslew);
   return hipGetLastError();
 }
 hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,

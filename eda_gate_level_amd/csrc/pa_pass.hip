@@ -510,25 +510,26 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
 // every LUT the block's gates use fit in its LDS, the slew and cap axes have
 // NS and NC points, no per-event or per-gate outputs -- written for latency
 // hiding and few instructions per event:
-//   * a four-deep ring of lane-stream pairs in registers, one load per step
-//     into the slot the step has just consumed, so every pair is fetched four
-//     steps before it is used; the gate record of the next pair's window head
-//     is gathered one step ahead; no register moves between steps, so no load
-//     is waited for before its time;
+//   * the compact stream, 8 bytes a slot: a 32-bit key (cycle, tic, the pin
+//     code's high bits) and the slew with the code's low bit (input pins) or
+//     the new value (output pin) in its sign bit;
+//   * windows start only at phase starts, all lanes of a wave together, each
+//     phase behind a header pair that carries every lane's gate data (cell,
+//     cap segment, start state, load), so the walk reads nothing but its
+//     stream: one ring of stream pairs in registers, loaded a fixed number of
+//     steps ahead, and no load depends on another;
+//   * a phase walks the input-pin path or the output-pin path, never both;
 //   * all LUT reads from the block's LDS copy of the contiguous LUT range of
 //     its cells (gates are numbered in cell order, so a block's gates use a
 //     contiguous range of cells);
-//   * empty slots carry a pad key -- an output-pin 1->0 event in the dummy
-//     cycle Cc -- that changes no state, adds no energy and lands in a bin the
-//     block never writes out, so no event is predicated on being real;
-//   * the energies go to their components with multiply-adds by 0/1 masks,
-//     and leakage changes are binned as (change at the bin start, minus the
+//   * leakage changes are binned as (change at the bin start, minus the
 //     change times its time in the bin), which needs no partial-bin fix-up.
 
 struct WalkBin {
-  double w;                // energy: dynamic, minus leakage change x time in the bin
-  double d;                // leakage power changes in the bin
-  unsigned long long c;    // events | glitches << 32
+  double w;    // energy: dynamic, minus leakage change x time in the bin
+  double d;    // leakage power changes in the bin
+  uint32_t n;  // events
+  uint32_t g;  // glitches
 };
 
 typedef double f64x2 __attribute__((ext_vector_type(2)));
@@ -586,7 +587,11 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
 #ifndef PA_WALK_GROUP
 #define PA_WALK_GROUP 2
 #endif
+#ifndef PA_WALK_LEAD
+#define PA_WALK_LEAD 2
+#endif
   constexpr int GP = PA_WALK_GROUP;  // pairs per group of the stream
+  constexpr int LD = PA_WALK_LEAD;   // groups a load runs ahead of its use
   extern __shared__ __align__(16) unsigned char s_dyn[];
   __shared__ double s_red[kNW][8];
   __shared__ double s_scan[kNW];
@@ -597,63 +602,81 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   const bool has_range = b < a.n_ranges;
 
   int base = 0, len = 0, q = 0;
+  uint2 lut_range = make_uint2(0u, 0u);  // the block's LUT range (first entry, entries)
   if (has_range) {
     q = (int)a.rchunk[b];
     const uint2 d = a.wdesc[b * kNW + wid];
+    lut_range = a.blk_lut[b];
     base = __builtin_amdgcn_readfirstlane((int)d.x);
     len = __builtin_amdgcn_readfirstlane((int)d.y);
   }
   const int npair = len >> 1;  // lane streams have even lengths
-  // The stream in groups of GP pairs.  At the start of group g the lane
-  // issues the gate-record gathers of group g + 1's window heads (its keys
-  // arrived during group g - 1) and the loads of group g + 2's pairs; both are
-  // first needed one group later, so every load has the same lead and a wait
-  // for one never holds up a younger one (loads complete in order).
-  u64x2 k0[GP], k1[GP], k2[GP];  // groups g, g + 1, g + 2
-  f32x2 s0[GP], s1[GP], s2[GP];
-  auto load_pair = [&](int p, u64x2 &k, f32x2 &sl) {
+  // the ring: R = LD + 1 groups of GP pairs; before group g is walked, the
+  // loads of group g + LD go into the slots group g - 1 has freed.  The walk
+  // loop is unrolled R times, so every slot keeps its registers and no load
+  // in flight is ever copied (a copy would have to wait for it).
+  constexpr int R = LD + 1;
+  u32x2 kr[R][GP], sr[R][GP];
+  auto load_pair = [&](int p, u32x2 &k, u32x2 &sl) {
     const int x = base + p * 128 + 2 * lane;
-    k = __builtin_nontemporal_load(reinterpret_cast<const u64x2 *>(a.key + x));
-    sl = __builtin_nontemporal_load(reinterpret_cast<const f32x2 *>(a.slew + x));
+    k = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(a.ckey + x));
+    sl = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(a.cslew + x));
   };
 #pragma unroll
-  for (int i = 0; i < GP; ++i) {
-    k0[i] = k1[i] = k2[i] = u64x2{a.pad_key, a.pad_key};
-    s0[i] = s1[i] = s2[i] = f32x2{1.f, 1.f};
-    if (npair > 0) {
-      load_pair(min(i, npair - 1), k0[i], s0[i]);
-      load_pair(min(GP + i, npair - 1), k1[i], s1[i]);
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < GP; ++i) {
+      kr[r][i] = u32x2{~0u, ~0u};
+      sr[r][i] = u32x2{0x3F800000u, 0x3F800000u};
+      if (r < LD && npair > 0) load_pair(min(r * GP + i, npair - 1), kr[r][i], sr[r][i]);
     }
-  }
 
-  // block set-up: bins, cell tables and the LUT range, while the ring fills
+  // block set-up, while the ring fills: bins, cell tables and the LUT range.
+  // The first element of every table per thread and up to KU LUT pairs per
+  // thread are loaded before the first store, so the set-up waits for
+  // memory once (larger tables and ranges loop on).
+  constexpr int KU = 6;
+  const uint32_t lut_lo = lut_range.x;
+  const int n2 = (int)(lut_range.y >> 1);  // cell LUT sizes 2^k k NS NC are even: the range is 16-byte aligned
+  const f64x2 *lsrc = reinterpret_cast<const f64x2 *>(a.lut + lut_lo);
+  lds_f64x2 *ldst = (lds_f64x2 *)L.lut;
+  f64x2 lv[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u)
+    if (u * kNT < n2) lv[u] = lsrc[min(u * kNT + tid, n2 - 1)];
+  const f64x2 *ax = reinterpret_cast<const f64x2 *>(a.cell_axw), *cx = reinterpret_cast<const f64x2 *>(a.cell_caxw);
+  const u32x2 *me = reinterpret_cast<const u32x2 *>(a.cell_meta);
+  const int nax = a.n_cells * (NS - 1), ncx = a.n_cells * (NC - 1), nth = a.n_cells * nthr, nlk = (int)a.n_leak,
+            nme = a.n_cells;
+  const f64x2 vax = ax[min(tid, nax - 1)], vcx = cx[min(tid, ncx - 1)];
+  const float vth = a.cell_thr[min(tid, nth - 1)];
+  const double vlk = a.leak[min(tid, nlk - 1)];
+  const u32x2 vme = me[min(tid, nme - 1)];
   for (int c = tid; c <= Cc; c += kNT) {
     L.bins[c].w = 0.0;
     L.bins[c].d = 0.0;
-    L.bins[c].c = 0ull;
+    L.bins[c].n = 0u;
+    L.bins[c].g = 0u;
   }
-  {
-    const f64x2 *ax = reinterpret_cast<const f64x2 *>(a.cell_axw), *cx = reinterpret_cast<const f64x2 *>(a.cell_caxw);
-    const u32x2 *me = reinterpret_cast<const u32x2 *>(a.cell_meta);
-    for (int j = tid; j < a.n_cells * (NS - 1); j += kNT) L.axw[j] = ax[j];
-    for (int j = tid; j < a.n_cells * (NC - 1); j += kNT) L.caxw[j] = cx[j];
-    for (int j = tid; j < a.n_cells * nthr; j += kNT) L.thr[j] = a.cell_thr[j];
-    for (int j = tid; j < a.n_leak; j += kNT) L.leak[j] = a.leak[j];
-    for (int j = tid; j < a.n_cells; j += kNT) L.meta[j] = me[j];
-  }
-  uint32_t lut_lo = 0;
-  if (has_range) {
-    const uint2 r = a.blk_lut[b];
-    lut_lo = r.x;
-    // cell LUT sizes 2^k k NS NC are even, so the range starts 16-byte aligned
-    const f64x2 *src = reinterpret_cast<const f64x2 *>(a.lut + r.x);
-    lds_f64x2 *dst = (lds_f64x2 *)L.lut;
-#pragma unroll 4
-    for (int j = tid; j < (int)(r.y >> 1); j += kNT) dst[j] = src[j];
-  }
+  if (tid < nax) L.axw[tid] = vax;
+  if (tid < ncx) L.caxw[tid] = vcx;
+  if (tid < nth) L.thr[tid] = vth;
+  if (tid < nlk) L.leak[tid] = vlk;
+  if (tid < nme) L.meta[tid] = vme;
+#pragma unroll
+  for (int u = 0; u < KU; ++u)
+    if (u * kNT + tid < n2) ldst[u * kNT + tid] = lv[u];
+  for (int j = tid + kNT; j < nax; j += kNT) L.axw[j] = ax[j];
+  for (int j = tid + kNT; j < ncx; j += kNT) L.caxw[j] = cx[j];
+  for (int j = tid + kNT; j < nth; j += kNT) L.thr[j] = a.cell_thr[j];
+  for (int j = tid + kNT; j < nlk; j += kNT) L.leak[j] = a.leak[j];
+  for (int j = tid + kNT; j < nme; j += kNT) L.meta[j] = me[j];
+  for (int j = KU * kNT + tid; j < n2; j += kNT) ldst[j] = lsrc[j];
   __syncthreads();
 
-  double e_int = 0.0, e_sw = 0.0, e_gl = 0.0, e_lkt = 0.0;  // e_lkt: sum of leakage change x time in its bin (ticks)
+  // the leakage changes' times in their bins are not summed here: the bins
+  // hold the energies minus them, so the flush gets their sum from the bins
+  double e_int = 0.0, e_sw = 0.0, e_gl = 0.0;
   const int64_t cstart = (int64_t)q * a.chunk_ticks;
   const int64_t clen = min(a.chunk_ticks, a.t_max - cstart);
   const int ncyc = (int)((clen + a.T - 1) / a.T);
@@ -662,30 +685,22 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   const double Td = (double)a.T;
   const double tail = (double)(a.t_max - cstart);
   const double tick = a.tick_s;
-  const uint32_t pb = a.pb, tb = a.tb, cs = tb + pb;
-  const uint32_t gmask = (1u << a.gb) - 1u, ysh = 10u + a.gb;
-  const uint32_t tmask = (1u << tb) - 1u;
-  const uint32_t outc = (1u << pb) - 1u;
-  const uint32_t kmax = (uint32_t)a.kmax;
+  const uint32_t ck = a.ck, tsh = a.tbc + a.ck;
+  const uint32_t tmask = (1u << a.tbc) - 1u, ckmask = (1u << ck) - 1u;
+  const uint32_t hdr = tmask << ck, out_bit = 1u << tsh;
+  const uint32_t cmask = (uint32_t)Cc - 1u;
+  constexpr uint32_t kPad = ~0u;
   constexpr uint32_t PSZ = NS * NC;  // LUT entries per (state, pin)
+  // a bin by cycle: a full-rate 24-bit offset (a bin is 24 bytes)
+  auto bin_at = [&](uint32_t cyc) -> lds_bin * {
+    return (lds_bin *)((__attribute__((address_space(3))) unsigned char *)L.bins + mad24(cyc & cmask, 24u, 0u));
+  };
 
   if (npair > 0) {
-    auto head_gate = [&](uint64_t K, uint32_t fallback) -> uint32_t {
-      const uint32_t h = (uint32_t)(K >> 32);
-      return ((h >> 9) & 1u) ? ((h >> 10) & gmask) : fallback;
-    };
-    // the gate record's first three words (load, cell and cap segment); the
-    // fourth is not read, so no half-dead load result is waited for
-    auto gather = [&](uint32_t g) -> uint3 { return *reinterpret_cast<const uint3 *>(a.gate_rec + g); };
-    // gate records of group g's and group g + 1's pairs (a window head is
-    // always the first event of a pair; other pairs gather a valid record)
-    uint3 r0[GP], r1[GP];
-#pragma unroll
-    for (int i = 0; i < GP; ++i) r0[i] = gather(head_gate(k0[i].x, 0u));
-    // the lane's window: gate, LUT row base in the LDS copy, state stride,
-    // axis-table and leakage bases, load position on the cap segment,
-    // switching energy, slew thresholds
-    uint32_t gate = 0, wbase = 0, kpsz = 0, axb = 0, lb = 0;
+    // the lane's window: LUT row base in the LDS copy, state stride, axis-table
+    // and leakage bases, load position on the cap segment, switching energy,
+    // slew thresholds
+    uint32_t wbase = 0, kpsz = 0, axb = 0, lb = 0;
     double fc = 0.0, esw = 0.0;
     float th[NIN];
 #pragma unroll
@@ -695,21 +710,24 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     // slew, leakage power of the current state
     uint32_t S = 0, St = 0, seen = 0, pcyc = ~0u, ptic = 0;
     float pslew = 1.f;
-    double lkS = L.leak[0];
     bool out_phase = false;  // the kind of the current phase's windows (wave-uniform)
-    lds_u32 *prec = L.prec + (wid * (kmax + 1) * 64 + lane) * 2;
+    lds_u32 *prec = L.prec + (wid * (a.kmax + 1) * 64 + lane) * 2;
 
-    // a phase of input windows starts: every lane sets up its window (a lane
-    // without one gets a valid, unused set-up from the pad key)
-    auto head_in = [&](uint64_t K, const uint3 &rec) {
-      const uint32_t h = (uint32_t)(K >> 32);
-      gate = (h >> 10) & gmask;
-      const double cap = __hiloint2double((int)rec.y, (int)rec.x);
-      const uint32_t cell = rec.z & 0xFFFFFFu, cseg = rec.z >> 24;
+    // a header pair: every lane with a window in the new phase sets it up (a
+    // lane without one sets up cell 0 with load 0, and walks empty slots)
+    auto header = [&](const u32x2 &k, const u32x2 &sw, bool own) {
+      const double cap = own ? __hiloint2double((int)sw.y, (int)sw.x) : 0.0;
+      if (out_phase) {
+        esw = a.hv2 * cap;  // Eq. 1
+        pcyc = ~0u;
+        return;
+      }
+      // a lane without a window reads the first entries of the LDS range
+      const uint32_t cell = own ? (k.y & 0xFFFFFu) : 0u, cseg = own ? ((k.y >> 20) & 15u) : 0u;
       const u32x2 m = L.meta[cell];
       lb = m.x >> 4;
-      kpsz = (m.x & 15u) * PSZ;
-      wbase = m.y - lut_lo + cseg;
+      kpsz = own ? (m.x & 15u) * PSZ : 0u;
+      wbase = own ? m.y - lut_lo + cseg : 0u;
       axb = mad24(cell, NS - 1, 0u);
       const f64x2 cx = L.caxw[mad24(cell, NC - 1, cseg)];
       fc = (cap - cx.x) * cx.y;  // position on the gate's cap segment (Sec. 2.4.1, Fig. 2)
@@ -721,154 +739,203 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
         if (i + 2 < NIN) th[i + 2] = t4.z;
         if (i + 3 < NIN) th[i + 3] = t4.w;
       }
-      S = h & 0xFFu;  // input state at the window start
+      S = own ? k.y >> 24 : 0u;  // input state at the window start
       St = S;
       seen = 0;
       pcyc = ~0u;
-      lkS = L.leak[lb + S];
-    };
-    // a phase of output windows starts: only the switching energy of the gate's load
-    auto head_out = [&](uint64_t K, const uint3 &rec) {
-      gate = ((uint32_t)(K >> 32) >> 10) & gmask;
-      esw = a.hv2 * __hiloint2double((int)rec.y, (int)rec.x);  // Eq. 1
-      pcyc = ~0u;
     };
 
-    // one input-pin event (Sec. 2.4.1-2.4.2, Fig. 7); a pad slot (dummy cycle
-    // Cc) toggles nothing, so its leakage change is zero, and adds nothing
-    auto event_in = [&](uint64_t K, float sl) {
-      const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
-      const uint32_t code = lk & outc;                                     // pin code
-      const uint32_t tic = (lk >> pb) & tmask;                             // time inside the cycle
-      const uint32_t cyc = (uint32_t)((((uint64_t)(hw >> ysh)) << 32 | lk) >> cs);  // cycle in the chunk
-      const bool real = cyc < (uint32_t)Cc;
-      const bool newcyc = cyc != pcyc;
-      // events of one timestamp all see the state before the first of them (Sec. 2.4.2)
-      if (newcyc || tic != ptic) St = S;
-      if (newcyc) seen = 0u;
-      const uint32_t cl = real ? code : 0u;
-      const uint32_t bit = real ? 1u << code : 0u;
-      const bool glitch = (seen & bit) != 0u;  // the pin already switched in this cycle (Fig. 7)
-      seen |= bit;
-      pcyc = cyc;
-      ptic = tic;
-      const uint32_t Sm = St;
-      S ^= bit;
-      // the slew segment: inner axis points at or below the slew (Sec. 2.4.1, Fig. 2)
-      uint32_t n = 0;
+    // the two input-pin events of a pair (Sec. 2.4.1-2.4.2, Fig. 7), in
+    // phases so that both events' table reads are in flight together and
+    // their arithmetic interleaves; an empty slot toggles nothing, so its
+    // leakage change is zero, and adds nothing
+    auto pair_in = [&](const u32x2 &K, const u32x2 &SW) {
+      bool real[2], glitch[2];
+      uint32_t tic[2], cyc[2], cl[2], lo[2], li[2], nseg[2];
+      float sl[2];
+      // the leakage power before the pair is read again rather than carried
+      // from the previous pair, so no LDS result lives across the loop's joins
+      const uint32_t l0 = lb + S;
+      // integer work: fields, the state before each event (all events of one
+      // timestamp see the state before the first of them, Sec. 2.4.2), the
+      // glitch flags (the pin already switched in this cycle, Fig. 7), the
+      // slew segment (inner axis points at or below the slew, Fig. 2), the
+      // LUT row and the leakage entry of the state after the event
 #pragma unroll
-      for (int i = 0; i < NIN; ++i) n += sl >= th[i] ? 1u : 0u;
-      // (state, pin) row, then the slew segment and the cap segment: every factor is small
-      // kpsz is a loop-carried value whose small range the instruction
-      // selector cannot see: an empty asm hides it from the optimizer too, so
-      // the explicit 24-bit masks stay and the multiply is a full-rate mad24
-      uint32_t kp = kpsz;
-      asm volatile("" : "+v"(kp));
-      const uint32_t lo = mad24(Sm, kp, mad24(cl, PSZ, mad24(n, NC, wbase)));
-      const lds_f64 *Lp = L.lut + lo;
-      const double L00 = Lp[0], L01 = Lp[1], L10 = Lp[NC], L11 = Lp[NC + 1];
-      const f64x2 aw = L.axw[axb + n];
-      const double lkn = L.leak[lb + S];  // leakage of the state after the event (Eq. 4)
-      const double fa = ((double)sl - aw.x) * aw.y;
-      const double v0 = L00 + fc * (L01 - L00);
-      const double v1 = L10 + fc * (L11 - L10);
-      double E = v0 + fa * (v1 - v0);
-      const double dp = lkn - lkS;  // the input toggle moves the leakage power
-      lkS = lkn;
-      const double ct = dp * (double)tic;
-      e_lkt += ct;
-      lds_u32 *pr = prec + cl * 128;
-      if (glitch) {
-        // Eq. 2 (reading): pulse width and the slews of the pin's previous event in the cycle and this one
-        const uint32_t ptic_pin = pr[0], pslew_pin = pr[1];
-        const double pw = (double)(tic - ptic_pin);
-        const double rr = pw / (0.5 * ((double)sl + (double)__uint_as_float(pslew_pin)));
-        E *= rr > 1.0 ? 1.0 : rr;
-        e_gl += E;
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t k = r ? K.y : K.x, sw = r ? SW.y : SW.x;
+        real[r] = k != kPad;
+        const uint32_t code = ((k & ckmask) << 1) | (sw >> 31);
+        sl[r] = __uint_as_float(sw & 0x7FFFFFFFu);
+        tic[r] = (k >> ck) & tmask;
+        cyc[r] = k >> tsh;
+        const bool newcyc = cyc[r] != pcyc;
+        if (newcyc || tic[r] != ptic) St = S;
+        if (newcyc) seen = 0u;
+        cl[r] = real[r] ? code : 0u;
+        const uint32_t bit = real[r] ? 1u << code : 0u;
+        glitch[r] = (seen & bit) != 0u;
+        seen |= bit;
+        pcyc = cyc[r];
+        ptic = tic[r];
+        const uint32_t Sm = St;
+        S ^= bit;
+        uint32_t n = 0;
+#pragma unroll
+        for (int i = 0; i < NIN; ++i) n += sl[r] >= th[i] ? 1u : 0u;
+        nseg[r] = n;
+        // every factor is small; kpsz is a loop-carried value whose small
+        // range the instruction selector cannot see: an empty asm hides it
+        // from the optimizer too, so the multiply is a full-rate mad24
+        uint32_t kp = kpsz;
+        asm volatile("" : "+v"(kp));
+        lo[r] = mad24(Sm, kp, mad24(cl[r], PSZ, mad24(n, NC, wbase)));
+        li[r] = lb + S;
       }
-      pr[0] = tic;
-      pr[1] = __float_as_uint(sl);
-      if (real) {  // a pad slot adds nothing (its lanes would all hit one bin)
-        e_int += glitch ? 0.0 : E;
-        lds_bin *bp = L.bins + (cyc & 0xFFFu);
-        __hip_atomic_fetch_add(&bp->w, fma(ct, -tick, E), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_add(&bp->d, dp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_add(&bp->c, 1ull | ((unsigned long long)glitch << 32), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      // every table read of both events
+      double L00[2], L01[2], L10[2], L11[2], lkn[2];
+      f64x2 aw[2];
+      const double lkS = L.leak[l0];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const lds_f64 *Lp = L.lut + lo[r];
+        L00[r] = Lp[0];
+        L01[r] = Lp[1];
+        L10[r] = Lp[NC];
+        L11[r] = Lp[NC + 1];
+        aw[r] = L.axw[axb + nseg[r]];
+        lkn[r] = L.leak[li[r]];
+      }
+      // energies (bilinear on slew and load, Fig. 2) and leakage changes (Eq. 4)
+      double E[2], dp[2], ct[2];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const double fa = ((double)sl[r] - aw[r].x) * aw[r].y;
+        const double v0 = L00[r] + fc * (L01[r] - L00[r]);
+        const double v1 = L10[r] + fc * (L11[r] - L10[r]);
+        E[r] = v0 + fa * (v1 - v0);
+      }
+      dp[0] = lkn[0] - lkS;
+      dp[1] = lkn[1] - lkn[0];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) ct[r] = dp[r] * (double)tic[r];
+      // rarely, a glitch: Eq. 2 (reading), the pulse width and the slews of
+      // the pin's previous event in the cycle and this one; the pin records
+      // are read and written in event order (both events may be one pin's)
+      lds_u32 *pr0 = prec + cl[0] * 128, *pr1 = prec + cl[1] * 128;
+      if (glitch[0] || glitch[1]) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          lds_u32 *pr = r ? pr1 : pr0;
+          if (glitch[r]) {
+            const uint32_t ptic_pin = pr[0], pslew_pin = pr[1];
+            const double pw = (double)(tic[r] - ptic_pin);
+            const double rr = pw / (0.5 * ((double)sl[r] + (double)__uint_as_float(pslew_pin)));
+            E[r] *= rr > 1.0 ? 1.0 : rr;
+            e_gl += E[r];
+          }
+          pr[0] = tic[r];
+          pr[1] = __float_as_uint(sl[r]);
+        }
+      } else {
+        pr0[0] = tic[0];
+        pr0[1] = __float_as_uint(sl[0]);
+        pr1[0] = tic[1];
+        pr1[1] = __float_as_uint(sl[1]);
+      }
+      // the components and the bins; an empty slot adds nothing
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (real[r]) {
+          e_int += glitch[r] ? 0.0 : E[r];
+          lds_bin *bp = bin_at(cyc[r]);
+          __hip_atomic_fetch_add(&bp->w, fma(ct[r], -tick, E[r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(&bp->d, dp[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(&bp->n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          if (glitch[r]) __hip_atomic_fetch_add(&bp->g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
       }
     };
 
-    // one output-pin event: 1/2 c Vdd^2 for 0->1 (Eq. 1), scaled by r_gl when
-    // the pin already switched in this cycle (Eq. 2, Fig. 7); the window's only
-    // pin is the output, so its previous event is the lane's previous event.
-    // A pad slot (dummy cycle Cc, value 0) adds nothing.
-    auto event_out = [&](uint64_t K, float sl) {
-      const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
-      const uint32_t tic = (lk >> pb) & tmask;
-      const uint32_t cyc = (uint32_t)((((uint64_t)(hw >> ysh)) << 32 | lk) >> cs);
-      const bool rise = (hw >> 8) & 1u;
-      const bool real = cyc < (uint32_t)Cc;
-      const bool glitch = real && cyc == pcyc;
-      double E = rise ? esw : 0.0;
-      if (glitch) {
-        const double pw = (double)(tic - ptic);
-        const double rr = pw / (0.5 * ((double)sl + (double)pslew));
-        E *= rr > 1.0 ? 1.0 : rr;
-        e_gl += E;
+    // the two output-pin events of a pair: 1/2 c Vdd^2 for 0->1 (Eq. 1),
+    // scaled by r_gl when the pin already switched in this cycle (Eq. 2,
+    // Fig. 7); the window's only pin is the output, so its previous event is
+    // the lane's previous event.  An empty slot (value bit 0) adds nothing.
+    auto pair_out = [&](const u32x2 &K, const u32x2 &SW) {
+      bool real[2], glitch[2];
+      uint32_t tic[2], cyc[2];
+      float sl[2];
+      double E[2];
+      uint32_t pt = ptic;
+      float ps = pslew;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const uint32_t k = r ? K.y : K.x, sw = r ? SW.y : SW.x;
+        real[r] = k != kPad;
+        sl[r] = __uint_as_float(sw & 0x7FFFFFFFu);
+        tic[r] = (k >> ck) & tmask;
+        cyc[r] = k >> tsh;
+        glitch[r] = real[r] && cyc[r] == pcyc;
+        E[r] = (sw >> 31) ? esw : 0.0;
+        pcyc = cyc[r];
       }
-      pcyc = cyc;
-      ptic = tic;
-      pslew = sl;
-      if (real) {
-        e_sw += glitch ? 0.0 : E;
-        lds_bin *bp = L.bins + (cyc & 0xFFFu);
-        __hip_atomic_fetch_add(&bp->w, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-        __hip_atomic_fetch_add(&bp->c, 1ull | ((unsigned long long)glitch << 32), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_WORKGROUP);
+      if (glitch[0] || glitch[1]) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          if (glitch[r]) {
+            const double pw = (double)(tic[r] - (r ? tic[0] : pt));
+            const double rr = pw / (0.5 * ((double)sl[r] + (double)(r ? sl[0] : ps)));
+            E[r] *= rr > 1.0 ? 1.0 : rr;
+            e_gl += E[r];
+          }
+        }
+      }
+      ptic = tic[1];
+      pslew = sl[1];
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (real[r]) {
+          e_sw += glitch[r] ? 0.0 : E[r];
+          lds_bin *bp = bin_at(cyc[r]);
+          __hip_atomic_fetch_add(&bp->w, E[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          __hip_atomic_fetch_add(&bp->n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          if (glitch[r]) __hip_atomic_fetch_add(&bp->g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
       }
     };
 
 #pragma unroll 1
-    for (int p0 = 0; p0 < npair; p0 += GP) {
-      // group g + 1's gathers, then group g + 2's loads (past the end: the last pair again)
+    for (int p0 = 0; p0 < npair; p0 += GP * R) {
 #pragma unroll
-      for (int i = 0; i < GP; ++i) r1[i] = gather(head_gate(k1[i].x, gate));
+      for (int u = 0; u < R; ++u) {
+        const int pg = p0 + u * GP;  // the group's first pair
+        if (pg >= npair) break;
+        // group g + LD's loads (past the end: the last pair again)
 #pragma unroll
-      for (int i = 0; i < GP; ++i) load_pair(min(p0 + 2 * GP + i, npair - 1), k2[i], s2[i]);
+        for (int i = 0; i < GP; ++i)
+          load_pair(min(pg + LD * GP + i, npair - 1), kr[(u + LD) % R][i], sr[(u + LD) % R][i]);
 #pragma unroll
-      for (int i = 0; i < GP; ++i) {
-        if (p0 + i >= npair) break;
-        const uint64_t K0 = k0[i].x, K1 = k0[i].y;
-        // windows start only at phase starts, where every lane with a window
-        // has its head: one wave-uniform test, and the phase's kind from the heads
-        const bool head = ((uint32_t)(K0 >> 41) & 1u) != 0u;
-        if (__ballot(head) != 0ull) {
-          out_phase = __ballot(head && ((uint32_t)K0 & outc) == outc) != 0ull;
-          if (out_phase) head_out(K0, r0[i]);
-          else head_in(K0, r0[i]);
+        for (int i = 0; i < GP; ++i) {
+          if (pg + i >= npair) break;
+          const u32x2 k = kr[u][i], sw = sr[u][i];
+          // a header pair starts a phase in every lane at once: one wave-uniform
+          // test, the phase's kind from the headers
+          const bool own = (k.x & ~out_bit) == hdr;
+          if (__ballot(own) != 0ull) {
+            out_phase = __ballot(own && (k.x & out_bit)) != 0ull;
+            header(k, sw, own);
+            continue;
+          }
+          if (out_phase) pair_out(k, sw);
+          else pair_in(k, sw);
         }
-        if (out_phase) {
-          event_out(K0, s0[i].x);
-          event_out(K1, s0[i].y);
-        } else {
-          event_in(K0, s0[i].x);
-          event_in(K1, s0[i].y);
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < GP; ++i) {
-        k0[i] = k1[i];
-        s0[i] = s1[i];
-        k1[i] = k2[i];
-        s1[i] = s2[i];
-        r0[i] = r1[i];
       }
     }
   }
   __syncthreads();
 
   // ---- the block's bins: the leakage changes' in-chunk prefix, then its own slots
-  double dsum = 0.0, lkc = 0.0;
+  double dsum = 0.0, lkc = 0.0, wsum = 0.0;
   unsigned long long ngl = 0;
   {
     constexpr int PER = (kCCMAX + kNT - 1) / kNT;
@@ -905,10 +972,13 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
         if (has_range && c < ncyc) {
           run += loc[u];  // the bin's own changes count from the bin start; the bin corrects for their times
           const double blen = (last_chunk && c == (int)lastc) ? (double)a.last_len : Td;
-          v = L.bins[c].w + run * blen * tick;
+          const double w = L.bins[c].w;
+          wsum += w;
+          v = w + run * blen * tick;
           lkc += loc[u] * (tail - Td * (double)c);
-          cn = L.bins[c].c;
-          ngl += cn >> 32;
+          const uint32_t ng = L.bins[c].g;
+          cn = (unsigned long long)L.bins[c].n | ((unsigned long long)ng << 32);
+          ngl += ng;
         }
         ow[c] = v;
         oc[c] = cn;
@@ -918,7 +988,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
 
   // ---- block totals
   {
-    double v[5] = {e_int, e_sw, e_gl, lkc * tick - e_lkt * tick, (double)ngl};
+    // leakage: the changes' energy to t_max from their bins' starts, minus
+    // their times in their bins (the bins' sum less the dynamic energies)
+    double v[5] = {e_int, e_sw, e_gl, lkc * tick - ((e_int + e_sw + e_gl) - wsum), (double)ngl};
 #pragma unroll
     for (int u = 0; u < 5; ++u) v[u] = wave_sum(v[u]);
     if (lane == 0) {
@@ -1189,10 +1261,10 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
   const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax);
   const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
   if (a.walk_lut > 0 && !diag) {
-    // the walk kernel: every block's LUT range in its LDS (at least the four entries a pad slot reads)
+    // the walk kernel: every block's LUT range in its LDS (at least the entries a lane without a window reads)
     const size_t dyn = walk_fixed_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax) +
-                       8 * (size_t)max(a.walk_lut, 32);
-    if (!a.blk_lut || a.pad_key == 0 || dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
+                       8 * (size_t)max(a.walk_lut, 2 * a.n_slew * a.n_cap);
+    if (!a.blk_lut || !a.ckey || !a.cslew || dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
     const dim3 g(grid_blocks), t(kNT);
     if (a.n_slew == 7 && a.n_cap == 7) hipLaunchKernelGGL((k_walk<7, 7>), g, t, dyn, s, a);
     else if (a.n_slew == 8 && a.n_cap == 8) hipLaunchKernelGGL((k_walk<8, 8>), g, t, dyn, s, a);

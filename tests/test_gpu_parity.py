@@ -145,11 +145,14 @@ def test_lut_copies_in_lds(name):
     """Each block copies the LUTs of the cells most of its events use into
     LDS and reads the rest through the caches.  With no copies, with room for
     the smallest tables only, and with all the spare LDS, the results must
-    meet the parity bar, in both the plain and the per-event kernels, and the
-    event energies must be bit for bit the same (same arithmetic on the same
-    table values, summed in a fixed order).  The bins and the leakage built
-    from them are LDS atomics, whose order between waves is free, so they
-    match to rounding."""
+    meet the parity bar, in both the plain and the per-event kernels.  The
+    event energies are the same arithmetic on the same table values; where
+    two settings share the lane layout (the cached and the partly copied
+    tables) they are summed in the same order and agree bit for bit, and the
+    default setting (the walk kernel, whose layout deals the windows to the
+    lanes by its own cost) agrees to rounding.  The bins and the leakage
+    built from them are LDS atomics, whose order between waves is free, so
+    they match to rounding."""
     d, t = LUT_CASES[name]()
     _print_case(f"lut copies {name}")
     o = _oracle(d, t)
@@ -161,11 +164,40 @@ def test_lut_copies_in_lds(name):
             if ref is None:
                 ref = g
                 continue
-            for key in ("e_int_J", "e_sw_J", "e_gl_J", "n_glitches"):
-                assert g[key] == ref[key], (key, kib, per_event)
+            same_layout = kib != 0
+            for key in ("e_int_J", "e_sw_J", "e_gl_J"):
+                if same_layout:
+                    assert g[key] == ref[key], (key, kib, per_event)
+                else:
+                    assert pu.rel_err(g[key], ref[key]) <= 1e-13, (key, kib, per_event)
+            assert g["n_glitches"] == ref["n_glitches"]
             assert pu.rel_err(g["e_leak_J"], ref["e_leak_J"]) <= 1e-13, (kib, per_event)
             np.testing.assert_allclose(g["wave_J"], ref["wave_J"], rtol=1e-13, atol=0)
             assert np.array_equal(g["cyc_events"], ref["cyc_events"])
+
+
+@pytest.mark.parametrize("name", ["tiny-7x7", "eight-cells"])
+def test_event_energies_repeat_bit_for_bit(name):
+    """The internal, switching and glitch energies are summed in a fixed
+    order (per lane in stream order, then fixed-order reductions), so runs of
+    one configuration on the loaded data repeat them bit for bit, as they do
+    the integer outputs; the bins and the leakage match to rounding."""
+    import eda_gate_level_amd as pa
+
+    d, t = LUT_CASES[name]()
+    _print_case(f"repeat {name}")
+    an = pa.PowerAnalysis()
+    try:
+        an.load(d, t)
+        r = [an.run() for _ in range(3)]
+    finally:
+        an.close()
+    for x in r[1:]:
+        for key in ("e_int_J", "e_sw_J", "e_gl_J", "n_glitches", "n_events"):
+            assert x["totals"][key] == r[0]["totals"][key], key
+        assert np.array_equal(x["cyc_events"].cpu().numpy(), r[0]["cyc_events"].cpu().numpy())
+        assert np.array_equal(x["cyc_glitches"].cpu().numpy(), r[0]["cyc_glitches"].cpu().numpy())
+        np.testing.assert_allclose(x["wave_J"].cpu().numpy(), r[0]["wave_J"].cpu().numpy(), rtol=1e-13, atol=0)
 
 
 def test_load_frees_its_scratch():
