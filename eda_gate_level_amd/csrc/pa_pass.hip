@@ -75,6 +75,29 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// A double moved between lanes by a DPP control (both halves; lanes whose
+// source is out of range or whose row is masked off get 0).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xf, true);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xf, true);
+  return __hiloint2double(hi, lo);
+}
+
+// Inclusive sum over the lanes of a wave up to this one, in a fixed order,
+// with DPP lane moves (no LDS): a scan within every row of 16 lanes (shifts
+// by 1, 2, 4, 8), then the rows' totals carried on by the row broadcasts of
+// lane 15 and lane 31.  Lane 63 holds the wave's total.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xf>(v);  // row_shr:8
+  v += dpp_f64<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_f64<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
+}
+
 struct CellLds {
   double2 *axw, *caxw;
   float *thr;
@@ -594,7 +617,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   constexpr int LD = PA_WALK_LEAD;   // groups a load runs ahead of its use
   extern __shared__ __align__(16) unsigned char s_dyn[];
   __shared__ double s_red[kNW][8];
-  __shared__ double s_scan[kNW];
+  __shared__ double s_scan[((kCCMAX + kNT - 1) / kNT) * kNW];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x;
   const int Cc = a.Cc, nthr = a.n_thr;
@@ -934,43 +957,41 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   }
   __syncthreads();
 
-  // ---- the block's bins: the leakage changes' in-chunk prefix, then its own slots
+  // ---- the block's bins: the leakage changes' in-chunk prefix, then its own
+  // slots.  Thread t owns bins t, t + kNT, ..., so the stores coalesce; the
+  // prefix runs over the bins in cycle order: a DPP scan within every wave,
+  // then the waves' totals, one row of bins after the other.
+  constexpr int PER = (kCCMAX + kNT - 1) / kNT;
   double dsum = 0.0, lkc = 0.0, wsum = 0.0;
   unsigned long long ngl = 0;
   {
-    constexpr int PER = (kCCMAX + kNT - 1) / kNT;
-    double loc[PER];
-    double sum = 0.0;
+    double loc[PER], incl[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int c = tid * PER + u;
+      const int c = u * kNT + tid;
       loc[u] = (has_range && c < ncyc) ? L.bins[c].d : 0.0;
-      sum += loc[u];
+      incl[u] = wave_incl_scan(loc[u]);
+      if (lane == 63) s_scan[u * kNW + wid] = incl[u];
     }
-    double incl = sum;
-    for (int o = 1; o < 64; o <<= 1) {
-      const double v = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += v;
-    }
-    if (lane == 63) s_scan[wid] = incl;
     __syncthreads();
-    double wbase_sum = 0.0;
-    for (int w = 0; w < kNW; ++w) {
-      const double v = s_scan[w];
-      if (w < wid) wbase_sum += v;
-      dsum += v;
-    }
-    double run = wbase_sum + incl - sum;  // changes of the chunk's earlier bins in this block
     double *ow = a.blk_wave + (size_t)b * Cc;
     unsigned long long *oc = a.blk_cnt + (size_t)b * Cc;
+    double before = 0.0;  // changes of all earlier rows of bins
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int c = tid * PER + u;
+      double row = 0.0, wb = 0.0;
+      for (int w = 0; w < kNW; ++w) {
+        const double v = s_scan[u * kNW + w];
+        if (w < wid) wb += v;
+        row += v;
+      }
+      const int c = u * kNT + tid;
       if (c < Cc) {
         double v = 0.0;
         unsigned long long cn = 0ull;
         if (has_range && c < ncyc) {
-          run += loc[u];  // the bin's own changes count from the bin start; the bin corrects for their times
+          // the bin's own changes count from the bin start; the bin corrects for their times
+          const double run = before + wb + incl[u];
           const double blen = (last_chunk && c == (int)lastc) ? (double)a.last_len : Td;
           const double w = L.bins[c].w;
           wsum += w;
@@ -983,17 +1004,19 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
         ow[c] = v;
         oc[c] = cn;
       }
+      before += row;
     }
+    dsum = before;
   }
 
-  // ---- block totals
+  // ---- block totals: DPP sums within the waves, then over the waves in order
   {
     // leakage: the changes' energy to t_max from their bins' starts, minus
     // their times in their bins (the bins' sum less the dynamic energies)
     double v[5] = {e_int, e_sw, e_gl, lkc * tick - ((e_int + e_sw + e_gl) - wsum), (double)ngl};
 #pragma unroll
-    for (int u = 0; u < 5; ++u) v[u] = wave_sum(v[u]);
-    if (lane == 0) {
+    for (int u = 0; u < 5; ++u) v[u] = wave_incl_scan(v[u]);
+    if (lane == 63) {
 #pragma unroll
       for (int u = 0; u < 5; ++u) s_red[wid][u] = v[u];
     }
@@ -1185,7 +1208,11 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
 int pass_block_threads() { return kNT; }
 int pass_blocks_per_cu() { return kBPC; }
 int pass_waves_per_block() { return kNW; }
-size_t pass_static_lds_bytes() { return (size_t)kNW * 9 * sizeof(double); }
+// static LDS of the pass kernels: s_red [kNW][8] and s_scan (the walk kernel's
+// holds a row of wave totals for every kNT bins of a chunk)
+size_t pass_static_lds_bytes() {
+  return (size_t)kNW * 8 * sizeof(double) + (size_t)((kCCMAX + kNT - 1) / kNT) * kNW * sizeof(double);
+}
 
 hipError_t launch_lut_plan(const uint64_t *skey, const uint32_t *ws, const uint32_t *bwin, int32_t n_ranges,
                            const uint4 *gate_rec, const uint2 *cell_meta, uint32_t gb, int n_slew, int n_cap,
