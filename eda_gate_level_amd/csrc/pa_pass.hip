@@ -645,16 +645,8 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     k = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(a.ckey + x));
     sl = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(a.cslew + x));
   };
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int i = 0; i < GP; ++i) {
-      kr[r][i] = u32x2{~0u, ~0u};
-      sr[r][i] = u32x2{0x3F800000u, 0x3F800000u};
-      if (r < LD && npair > 0) load_pair(min(r * GP + i, npair - 1), kr[r][i], sr[r][i]);
-    }
 
-  // block set-up, while the ring fills: bins, cell tables and the LUT range.
+  // block set-up: bins, cell tables and the LUT range.
   // The first element of every table per thread and up to KU LUT pairs per
   // thread are loaded before the first store, so the set-up waits for
   // memory once (larger tables and ranges loop on).
@@ -675,6 +667,16 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   const float vth = a.cell_thr[min(tid, nth - 1)];
   const double vlk = a.leak[min(tid, nlk - 1)];
   const u32x2 vme = me[min(tid, nme - 1)];
+  // the ring's first groups, issued after the tables so that waiting for the
+  // tables does not wait for them (loads complete in order)
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int i = 0; i < GP; ++i) {
+      kr[r][i] = u32x2{~0u, ~0u};
+      sr[r][i] = u32x2{0x3F800000u, 0x3F800000u};
+      if (r < LD && npair > 0) load_pair(min(r * GP + i, npair - 1), kr[r][i], sr[r][i]);
+    }
   for (int c = tid; c <= Cc; c += kNT) {
     L.bins[c].w = 0.0;
     L.bins[c].d = 0.0;
