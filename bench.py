@@ -114,6 +114,39 @@ def window_ablation(args, w, dev):
         an.close()
 
 
+def atomic_ablation(args, dev):
+    """The paper's waveform-bin atomic stress test: 32 two-input gates, 100,000
+    cycles, every pin toggling m = 1, 2, 4, 8 times per cycle (every event of
+    a cycle lands in one bin), the pass with its LDS bin atomics against the
+    same pass with plain loads, adds and stores and with plain stores alone
+    (plain_bins 1 and 2: timing only, their bins are wrong)."""
+    import torch
+
+    import eda_gate_level_amd as pa
+    from workloads import synth
+
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    for m in (1, 2, 4, 8):
+        w = synth.contention(m)
+        row = {"workload": w.name, "events": w.trace.n_events, "toggles_per_cycle": m}
+        for plain in (0, 1, 2):
+            an = pa.PowerAnalysis(0, torch.cuda.current_stream(dev), time_kernels=1, plain_bins=plain)
+            an.load(w.design, w.trace)
+            outs = an.alloc_outputs()
+            for _ in range(max(3, args.warmup // 4)):
+                an.run(outs)
+            fused = []
+            for _ in range(max(5, args.steps // 2)):
+                flush.fill_(1.0)
+                an.run(outs)
+                fused.append(an.info()["kernel_ms"][0])
+            row[("atomic_fused_ms", "plain_add_fused_ms", "plain_store_fused_ms")[plain]] = statistics.median(fused)
+            an.close()
+        for k in ("plain_add", "plain_store"):
+            row[f"atomic_overhead_vs_{k}_pct"] = round(100.0 * (row["atomic_fused_ms"] / row[f"{k}_fused_ms"] - 1.0), 2)
+        print(json.dumps(row), flush=True)
+
+
 def text_pipeline(args, w, dev):
     """Activity text through the host packer: the whole text packed on host
     threads alone, then the text's power analysis with packing and GPU work
@@ -194,6 +227,9 @@ def main():
     ap.add_argument("--window-ablation", action="store_true",
                     help="time the pass with density-aware windows and with fixed windows of 1..32 cycles "
                          "(one JSON line each, with the events-per-window distribution)")
+    ap.add_argument("--atomic-ablation", action="store_true",
+                    help="the waveform-bin stress workloads (m = 1, 2, 4, 8 toggles per pin and cycle), bin "
+                         "atomics against plain loads and stores, one JSON line each")
     ap.add_argument("--text", action="store_true",
                     help="write the workload as activity text and time its host packing and the overlapped "
                          "text pipeline (one JSON line)")
@@ -226,6 +262,9 @@ def main():
 
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.atomic_ablation:
+        atomic_ablation(args, dev)
+        return
     t0 = time.time()
     w = synth.make(args.workload)
     if args.window_ablation:

@@ -36,14 +36,15 @@ class PowerAnalysis:
     output tensors."""
 
     def __init__(self, device: int = 0, stream=None, chunk_cycles: int = 0, grid_blocks: int = 0,
-                 time_kernels=0, fixed_window_cycles: int = 0, lut_lds_kib: int = 0, device_mib_cap: int = 0):
+                 time_kernels=0, fixed_window_cycles: int = 0, lut_lds_kib: int = 0, device_mib_cap: int = 0,
+                 plain_bins: int = 0):
         import torch
 
         self.device = torch.device("cuda", device)
         if stream is None:
             stream = torch.cuda.current_stream(self.device)
         self.ctx = pa_create(device, stream, chunk_cycles, grid_blocks, time_kernels, fixed_window_cycles,
-                             lut_lds_kib, device_mib_cap)
+                             lut_lds_kib, device_mib_cap, plain_bins)
         self.n_cycles = 0
         self.n_events = 0
         self.n_gates = 0

@@ -33,7 +33,8 @@ class PaError(RuntimeError):
 
 class pa_tunables(C.Structure):
     _fields_ = [("chunk_cycles", C.c_int32), ("grid_blocks", C.c_int32), ("time_kernels", C.c_int32),
-                ("fixed_window_cycles", C.c_int32), ("lut_lds_kib", C.c_int32), ("device_mib_cap", C.c_int32)]
+                ("fixed_window_cycles", C.c_int32), ("lut_lds_kib", C.c_int32), ("device_mib_cap", C.c_int32),
+                ("plain_bins", C.c_int32)]
 
 
 class pa_totals(C.Structure):
@@ -191,9 +192,9 @@ def _stream_handle(stream) -> C.c_void_p:
 
 def pa_create(device: int = 0, stream=None, chunk_cycles: int = 0, grid_blocks: int = 0,
               time_kernels=0, fixed_window_cycles: int = 0, lut_lds_kib: int = 0,
-              device_mib_cap: int = 0) -> C.c_void_p:
+              device_mib_cap: int = 0, plain_bins: int = 0) -> C.c_void_p:
     t = pa_tunables(chunk_cycles, grid_blocks, int(time_kernels), int(fixed_window_cycles), int(lut_lds_kib),
-                    int(device_mib_cap))
+                    int(device_mib_cap), int(plain_bins))
     h = C.c_void_p()
     _check(lib().pa_create(C.byref(h), int(device), _stream_handle(stream), C.byref(t)))
     return h

@@ -262,6 +262,8 @@ int pa_create(pa_ctx **out, int hip_device, void *hip_stream, const pa_tunables 
   if (t && (t->time_kernels < 0 || t->time_kernels > 2))
     return fail(PA_EINVAL, "pa_create: time_kernels must be 0, 1 or 2");
   if (t && t->device_mib_cap < 0) return fail(PA_EINVAL, "pa_create: device_mib_cap must be >= 0");
+  if (t && (t->plain_bins < 0 || t->plain_bins > 2))
+    return fail(PA_EINVAL, "pa_create: plain_bins must be 0, 1 or 2");
   int ndev = 0;
   HIPCHK(hipGetDeviceCount(&ndev));
   if (hip_device < 0 || hip_device >= ndev) return fail(PA_EINVAL, "pa_create: device %d of %d", hip_device, ndev);
@@ -937,6 +939,7 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   a.cslew = v.walk_lut > 0 ? v.cslew.as<uint32_t>() : nullptr;
   a.tbc = v.tbc;
   a.ck = v.ck;
+  a.plain_bins = c->tun.plain_bins;
   a.blk_wave = sc.blk_wave;
   a.blk_cnt = sc.blk_cnt;
   a.blk_part = sc.blk_part;

@@ -101,6 +101,7 @@ struct PassArgs {
   const uint32_t *ckey;
   const uint32_t *cslew;
   uint32_t tbc, ck;
+  int32_t plain_bins;         // timing aid: 1 plain adds, 2 plain stores to the bins (results wrong)
   // per-block results, reduced by the finalize kernel
   double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
   unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32

@@ -604,7 +604,17 @@ __device__ __forceinline__ uint32_t mad24(uint32_t x, uint32_t y, uint32_t z) {
   return (x & 0xFFFFFFu) * (y & 0xFFFFFFu) + z;
 }
 
-template <int NS, int NC>
+// Add to a bin: an LDS atomic (PLAIN 0), or, as timing aids whose results
+// are wrong, a plain load, add and store that loses an update meeting another
+// on the same address (1), or a plain store of the contribution alone (2).
+template <int PLAIN, class T, class P>
+__device__ __forceinline__ void bin_add(P *p, T v) {
+  if constexpr (PLAIN == 1) *p += v;
+  else if constexpr (PLAIN == 2) *p = v;
+  else __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+template <int NS, int NC, int PLAIN>
 __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   constexpr int NIN = NS - 2;  // inner slew-axis points: the segment is the count at or below the slew
 #ifndef PA_WALK_GROUP
@@ -874,10 +884,10 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
         if (real[r]) {
           e_int += glitch[r] ? 0.0 : E[r];
           lds_bin *bp = bin_at(cyc[r]);
-          __hip_atomic_fetch_add(&bp->w, fma(ct[r], -tick, E[r]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          __hip_atomic_fetch_add(&bp->d, dp[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          __hip_atomic_fetch_add(&bp->n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          if (glitch[r]) __hip_atomic_fetch_add(&bp->g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          bin_add<PLAIN>(&bp->w, fma(ct[r], -tick, E[r]));
+          bin_add<PLAIN>(&bp->d, dp[r]);
+          bin_add<PLAIN>(&bp->n, 1u);
+          if (glitch[r]) bin_add<PLAIN>(&bp->g, 1u);
         }
       }
     };
@@ -922,9 +932,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
         if (real[r]) {
           e_sw += glitch[r] ? 0.0 : E[r];
           lds_bin *bp = bin_at(cyc[r]);
-          __hip_atomic_fetch_add(&bp->w, E[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          __hip_atomic_fetch_add(&bp->n, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          if (glitch[r]) __hip_atomic_fetch_add(&bp->g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          bin_add<PLAIN>(&bp->w, E[r]);
+          bin_add<PLAIN>(&bp->n, 1u);
+          if (glitch[r]) bin_add<PLAIN>(&bp->g, 1u);
         }
       }
     };
@@ -1295,8 +1305,15 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
                        8 * (size_t)max(a.walk_lut, 2 * a.n_slew * a.n_cap);
     if (!a.blk_lut || !a.ckey || !a.cslew || dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
     const dim3 g(grid_blocks), t(kNT);
-    if (a.n_slew == 7 && a.n_cap == 7) hipLaunchKernelGGL((k_walk<7, 7>), g, t, dyn, s, a);
-    else if (a.n_slew == 8 && a.n_cap == 8) hipLaunchKernelGGL((k_walk<8, 8>), g, t, dyn, s, a);
+    if (a.n_slew == 7 && a.n_cap == 7) {
+      if (a.plain_bins == 1) hipLaunchKernelGGL((k_walk<7, 7, 1>), g, t, dyn, s, a);
+      else if (a.plain_bins == 2) hipLaunchKernelGGL((k_walk<7, 7, 2>), g, t, dyn, s, a);
+      else hipLaunchKernelGGL((k_walk<7, 7, 0>), g, t, dyn, s, a);
+    } else if (a.n_slew == 8 && a.n_cap == 8) {
+      if (a.plain_bins == 1) hipLaunchKernelGGL((k_walk<8, 8, 1>), g, t, dyn, s, a);
+      else if (a.plain_bins == 2) hipLaunchKernelGGL((k_walk<8, 8, 2>), g, t, dyn, s, a);
+      else hipLaunchKernelGGL((k_walk<8, 8, 0>), g, t, dyn, s, a);
+    }
     else return hipErrorInvalidValue;
     return hipGetLastError();
   }

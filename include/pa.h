@@ -78,6 +78,14 @@ typedef struct {
                              at most n MiB together, and an allocation past that fails with
                              PA_ENOMEM as a real out-of-memory would (for testing the
                              out-of-memory paths; a failed load keeps the loaded data) */
+  int32_t plain_bins;     /* timing aid for the paper's waveform-bin atomic stress test (its
+                             high-activity synthetic waveforms with 1-8 toggles per cycle),
+                             0, 1 or 2: 0 = atomic adds to the pass's per-cycle bins; 1 = plain
+                             loads, adds and stores; 2 = plain stores of each contribution (the
+                             no-atomic variant "regular writes" read literally).  With 1 or 2
+                             the waveform, counts and leakage are wrong (updates are lost or
+                             overwritten), so results are for timing only.  Used by the walk
+                             kernel; the other kernels ignore it */
 } pa_tunables;
 
 /* Create a context on HIP device `hip_device`, launching on `hip_stream`

@@ -358,3 +358,38 @@ def test_workload_full_size(name):
     o = _oracle(w.design, w.trace)
     g = pu.gpu_run(w.design, w.trace)
     pu.assert_parity(g, o, label=name)
+
+
+@pytest.mark.parametrize("m", [1, 8])
+def test_contention_full_size(m):
+    """The waveform-bin stress workload at the shape the bench times (32
+    two-input gates, 100,000 cycles, m toggles per pin and cycle: every event
+    of a cycle in one bin, every toggle after a pin's first in a cycle a
+    glitch) through the bench's pass: every total, bin and count against the
+    threaded oracle."""
+    import oracle
+
+    w = synth.contention(m)
+    _print_case(f"contention full size m={m} events={w.trace.n_events}")
+    o = oracle.run(w.design, w.trace, per_event=False, threads=oracle.host_threads())
+    g = pu.gpu_run(w.design, w.trace, per_event=False)
+    pu.assert_parity(g, o, per_event=False, label=f"contention {m} full")
+
+
+def test_plain_bins_is_a_timing_aid():
+    """plain_bins = 1 or 2 swaps the bin atomics for plain adds or plain
+    stores (the no-atomic variants of the stress test): the per-lane energy
+    sums do not touch the bins, so they stay exact; 3 is refused."""
+    import eda_gate_level_amd as pa
+
+    d, t = LUT_CASES["tiny-7x7"]()
+    _print_case("plain bins")
+    ref = pu.gpu_run(d, t, per_event=False)
+    for mode in (1, 2):
+        g = pu.gpu_run(d, t, per_event=False, plain_bins=mode)
+        for key in ("e_int_J", "e_sw_J", "e_gl_J", "n_events"):
+            assert g[key] == ref[key], (mode, key)
+        assert np.isfinite(g["wave_J"]).all()
+    with pytest.raises(pa.PaError) as ei:
+        pa.PowerAnalysis(plain_bins=3)
+    assert ei.value.code == pa.PA_EINVAL
