@@ -66,12 +66,12 @@ def kernel_text(src):
 
 
 def profiled_traffic(workload):
-    """HBM bytes per launch of the fused kernel from the committed rocprofv3
-    counter summary, or None when the kernel source changed since."""
+    """HBM bytes per launch of the pass kernel (k_walk) from the committed
+    rocprofv3 counter summary, or None when the kernel source changed since."""
     import hashlib
     import re
 
-    path = os.path.join(ROOT, "profiles", f"k_fused_{workload}.md")
+    path = os.path.join(ROOT, "profiles", f"k_walk_{workload}.md")
     try:
         text = open(path).read()
     except OSError:

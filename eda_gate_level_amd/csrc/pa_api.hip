@@ -477,6 +477,9 @@ static constexpr uint32_t kWalkCostIn = PA_WALK_COST_IN, kWalkCostOut = PA_WALK_
 // windows are then dealt to its lanes (pa_load.hip) and scattered into the
 // interleaved streams.  Also the first block of every chunk, for the
 // finalize kernel.  The sorted events are in c->ls.skey / sslew / sorig.
+// When the walk kernel can run but some block's LUT range does not fit in
+// its LDS, the target doubles (smaller blocks span fewer cells), a few times
+// at most.
 static int build_ranges(pa_ctx *c, Events &v) {
   const Design &d = c->d;
   hipStream_t s = c->stream;
@@ -484,41 +487,11 @@ static int build_ranges(pa_ctx *c, Events &v) {
   if (pa::pass_block_threads() != pa::lane_plan_lanes())
     return fail(PA_EINVAL, "pa_load_events: lane plan and pass disagree on the block size");
   const int NW = pa::pass_waves_per_block();
-  const int64_t target_blocks =
+  int64_t target_blocks =
       c->tun.grid_blocks > 0 ? c->tun.grid_blocks : (int64_t)pa::pass_blocks_per_cu() * c->n_cu;
   const int64_t min_events = 4 * (int64_t)pa::pass_wave_batch() * NW;
-  const int64_t per = std::max<int64_t>(min_events, (v.E + target_blocks - 1) / std::max<int64_t>(1, target_blocks));
-  std::vector<uint32_t> rs, rq, cb(v.Q + 1);
-  for (int32_t q = 0; q < v.Q; ++q) {
-    cb[q] = (uint32_t)rs.size();
-    const int64_t a = v.h_chunk_base[q], b = v.h_chunk_base[q + 1];
-    if (b <= a) continue;
-    const int64_t n = std::max<int64_t>(1, (b - a) / per);  // never more blocks than the target
-    for (int64_t i = 0; i < n; ++i) {
-      rs.push_back((uint32_t)(a + (b - a) * i / n));
-      rq.push_back((uint32_t)q);
-    }
-  }
-  cb[v.Q] = (uint32_t)rs.size();
-  const int32_t nr = (int32_t)rs.size();
-  v.n_ranges = nr;
-  v.grid = std::max(1, nr);
-  rs.push_back((uint32_t)v.E);
-  rq.push_back(0);
-  HIPCHK(v.rstart.ensure(sizeof(uint32_t) * rs.size()));
-  HIPCHK(v.rchunk.ensure(sizeof(uint32_t) * rq.size()));
-  HIPCHK(v.chunk_blk.ensure(sizeof(uint32_t) * cb.size()));
-  HIPCHK(v.blk_wave.ensure(sizeof(double) * (size_t)v.grid * v.Cc));
-  HIPCHK(v.blk_cnt.ensure(sizeof(unsigned long long) * (size_t)v.grid * v.Cc));
-  HIPCHK(v.blk_part.ensure(sizeof(double) * 8 * (size_t)v.grid));
-  HIPCHK(v.res.ensure(sizeof(double) * 16));
-  HIPCHK(hipMemcpyAsync(v.rstart.p, rs.data(), sizeof(uint32_t) * rs.size(), hipMemcpyHostToDevice, s));
-  HIPCHK(hipMemcpyAsync(v.rchunk.p, rq.data(), sizeof(uint32_t) * rq.size(), hipMemcpyHostToDevice, s));
-  HIPCHK(hipMemcpyAsync(v.chunk_blk.p, cb.data(), sizeof(uint32_t) * cb.size(), hipMemcpyHostToDevice, s));
-  HIPCHK(v.wdesc.ensure(sizeof(uint2) * (size_t)v.grid * NW));
-  HIPCHK(hipMemsetAsync(v.wdesc.p, 0, sizeof(uint2) * (size_t)v.grid * NW, s));
 
-  // ---- windows: starts, each block's first window, lengths
+  // ---- windows: starts and lengths
   const int64_t E = v.E;
   uint32_t W = 0;
   if (E > 0) {
@@ -534,30 +507,76 @@ static int build_ranges(pa_ctx *c, Events &v) {
   }
   v.n_windows = W;
   HIPCHK(ls.ws.ensure(sizeof(uint32_t) * ((size_t)W + 1)));
-  HIPCHK(ls.bwin.ensure(sizeof(uint32_t) * ((size_t)nr + 1)));
   HIPCHK(v.wlen.ensure(sizeof(uint32_t) * std::max<size_t>(W, 1)));
-  std::vector<uint32_t> wave_len((size_t)nr * NW, 0);
-  v.walk_lut = 0;
-  if (W > 0) {
+  if (W > 0)
     HIPCHK(pa::launch_win_starts(E, ls.skey.as<uint64_t>(), ls.winc.as<uint32_t>(), ls.ws.as<uint32_t>(), s));
+
+  // ---- block ranges; with windows, every block's first window and LUT range
+  const bool try_walk = W > 0 && v.pad_key != 0 && v.compact_ok;
+  const int32_t room =
+      try_walk ? pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax) : 0;
+  int32_t nr = 0;
+  std::vector<uint32_t> rs, rq, cb(v.Q + 1);
+  v.walk_lut = 0;
+  for (int attempt = 0;; ++attempt) {
+    const int64_t per =
+        std::max<int64_t>(min_events, (v.E + target_blocks - 1) / std::max<int64_t>(1, target_blocks));
+    rs.clear();
+    rq.clear();
+    for (int32_t q = 0; q < v.Q; ++q) {
+      cb[q] = (uint32_t)rs.size();
+      const int64_t a = v.h_chunk_base[q], b = v.h_chunk_base[q + 1];
+      if (b <= a) continue;
+      const int64_t n = std::max<int64_t>(1, (b - a) / per);  // never more blocks than the target
+      for (int64_t i = 0; i < n; ++i) {
+        rs.push_back((uint32_t)(a + (b - a) * i / n));
+        rq.push_back((uint32_t)q);
+      }
+    }
+    cb[v.Q] = (uint32_t)rs.size();
+    nr = (int32_t)rs.size();
+    rs.push_back((uint32_t)v.E);
+    rq.push_back(0);
+    HIPCHK(v.rstart.ensure(sizeof(uint32_t) * rs.size()));
+    HIPCHK(hipMemcpyAsync(v.rstart.p, rs.data(), sizeof(uint32_t) * rs.size(), hipMemcpyHostToDevice, s));
+    if (W == 0) break;
+    HIPCHK(ls.bwin.ensure(sizeof(uint32_t) * ((size_t)nr + 1)));
     HIPCHK(pa::launch_block_windows(nr, E, v.rstart.as<uint32_t>(), ls.skey.as<uint64_t>(), ls.winc.as<uint32_t>(), W,
                                     ls.bwin.as<uint32_t>(), s));
-    // ---- the walk kernel: every block's LUT range, used when each fits in a block's LDS
-    if (v.pad_key != 0 && v.compact_ok) {
-      const int32_t room = pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax);
-      HIPCHK(v.blk_lut.ensure(sizeof(uint2) * (size_t)nr));
-      HIPCHK(pa::launch_block_luts(nr, ls.skey.as<uint64_t>(), ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(),
-                                   d.gate_rec.as<uint4>(), d.cell_meta.as<uint2>(), v.gb, d.n_slew, d.n_cap,
-                                   v.blk_lut.as<uint2>(), s));
-      std::vector<uint2> hl((size_t)nr);
-      HIPCHK(hipMemcpyAsync(hl.data(), v.blk_lut.p, sizeof(uint2) * hl.size(), hipMemcpyDeviceToHost, s));
-      HIPCHK(hipStreamSynchronize(s));
-      uint32_t most = 0;
-      for (const uint2 &r : hl) most = std::max(most, r.y);
-      // at least the entries a lane without a window reads (its row 0, segment n, cap segment 0)
-      most = std::max<uint32_t>(most, 2u * (uint32_t)(d.n_slew * d.n_cap));
-      if ((int64_t)most <= (int64_t)room) v.walk_lut = (int32_t)most;
+    if (!try_walk) break;
+    // the walk kernel: every block's LUT range, used when each fits in a block's LDS
+    HIPCHK(v.blk_lut.ensure(sizeof(uint2) * (size_t)nr));
+    HIPCHK(pa::launch_block_luts(nr, ls.skey.as<uint64_t>(), ls.ws.as<uint32_t>(), ls.bwin.as<uint32_t>(),
+                                 d.gate_rec.as<uint4>(), d.cell_meta.as<uint2>(), v.gb, d.n_slew, d.n_cap,
+                                 v.blk_lut.as<uint2>(), s));
+    std::vector<uint2> hl((size_t)nr);
+    HIPCHK(hipMemcpyAsync(hl.data(), v.blk_lut.p, sizeof(uint2) * hl.size(), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    uint32_t most = 0;
+    for (const uint2 &r : hl) most = std::max(most, r.y);
+    // at least the entries a lane without a window reads (its row 0, segment n, cap segment 0)
+    most = std::max<uint32_t>(most, 2u * (uint32_t)(d.n_slew * d.n_cap));
+    if ((int64_t)most <= (int64_t)room) {
+      v.walk_lut = (int32_t)most;
+      break;
     }
+    if (c->tun.grid_blocks > 0 || attempt >= 3 || per <= min_events) break;
+    target_blocks *= 2;
+  }
+  v.n_ranges = nr;
+  v.grid = std::max(1, nr);
+  HIPCHK(v.rchunk.ensure(sizeof(uint32_t) * rq.size()));
+  HIPCHK(v.chunk_blk.ensure(sizeof(uint32_t) * cb.size()));
+  HIPCHK(v.blk_wave.ensure(sizeof(double) * (size_t)v.grid * v.Cc));
+  HIPCHK(v.blk_cnt.ensure(sizeof(unsigned long long) * (size_t)v.grid * v.Cc));
+  HIPCHK(v.blk_part.ensure(sizeof(double) * 8 * (size_t)v.grid));
+  HIPCHK(v.res.ensure(sizeof(double) * 16));
+  HIPCHK(hipMemcpyAsync(v.rchunk.p, rq.data(), sizeof(uint32_t) * rq.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(hipMemcpyAsync(v.chunk_blk.p, cb.data(), sizeof(uint32_t) * cb.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(v.wdesc.ensure(sizeof(uint2) * (size_t)v.grid * NW));
+  HIPCHK(hipMemsetAsync(v.wdesc.p, 0, sizeof(uint2) * (size_t)v.grid * NW, s));
+  std::vector<uint32_t> wave_len((size_t)nr * NW, 0);
+  if (W > 0) {
     // ---- every block's windows, longest first (a stable sort keeps gate order among equals)
     HIPCHK(ls.wkey0.ensure(sizeof(uint64_t) * W));
     HIPCHK(ls.wkey1.ensure(sizeof(uint64_t) * W));

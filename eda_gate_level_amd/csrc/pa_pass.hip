@@ -570,7 +570,7 @@ struct WalkLds {
   lds_f64x2 *axw, *caxw;
   lds_f32 *thr;
   lds_bin *bins;      // [Cc + 1]: bin Cc takes the pad slots
-  lds_u32 *prec;      // [waves][pin slots][64][2]: a pin's last (time in cycle, slew bits) per lane
+  lds_u32 *prec;      // [waves][input pins][64][2]: a pin's last (time in cycle, slew bits) per lane
   lds_f64 *leak;
   lds_u32x2 *meta;
   lds_f64 *lut;       // the block's LUT range, 16-byte aligned
@@ -578,8 +578,9 @@ struct WalkLds {
 
 __host__ __device__ inline size_t walk_fixed_bytes(int Cc, int n_cells, int n_slew, int n_cap, int n_thr,
                                                    int64_t n_leak, int kmax) {
+  // pin records for the input pins only: output events walk windows of their own
   const size_t b = 16 * (size_t)n_cells * (n_slew - 1 + n_cap - 1) + 4 * (size_t)n_cells * n_thr +
-                   24 * ((size_t)Cc + 1) + prec_bytes(kmax) + 8 * (size_t)n_leak + 8 * (size_t)n_cells;
+                   24 * ((size_t)Cc + 1) + (size_t)kNW * kmax * 64 * 8 + 8 * (size_t)n_leak + 8 * (size_t)n_cells;
   return (b + 15) & ~size_t(15);
 }
 
@@ -593,7 +594,7 @@ __device__ __forceinline__ WalkLds walk_carve(unsigned char *s, int Cc, int n_ce
   L.thr = (lds_f32 *)(L.caxw + n_cells * (n_cap - 1));
   L.bins = (lds_bin *)(L.thr + n_cells * n_thr);
   L.prec = (lds_u32 *)(L.bins + Cc + 1);
-  L.leak = (lds_f64 *)(L.prec + kNW * (kmax + 1) * 64 * 2);
+  L.leak = (lds_f64 *)(L.prec + kNW * kmax * 64 * 2);
   L.meta = (lds_u32x2 *)(L.leak + (int)n_leak);
   L.lut = (lds_f64 *)(b + walk_fixed_bytes(Cc, n_cells, n_slew, n_cap, n_thr, n_leak, kmax));
   return L;
@@ -746,7 +747,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     uint32_t S = 0, St = 0, seen = 0, pcyc = ~0u, ptic = 0;
     float pslew = 1.f;
     bool out_phase = false;  // the kind of the current phase's windows (wave-uniform)
-    lds_u32 *prec = L.prec + (wid * (a.kmax + 1) * 64 + lane) * 2;
+    lds_u32 *prec = L.prec + (wid * a.kmax * 64 + lane) * 2;
 
     // a header pair: every lane with a window in the new phase sets it up (a
     // lane without one sets up cell 0 with load 0, and walks empty slots)
