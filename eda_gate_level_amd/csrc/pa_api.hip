@@ -469,11 +469,17 @@ static constexpr double kWindowEvents = PA_WINDOW_EVENTS;
 #ifndef PA_WALK_COST_OUT
 #define PA_WALK_COST_OUT 2
 #endif
-static constexpr uint32_t kWalkCostIn = PA_WALK_COST_IN, kWalkCostOut = PA_WALK_COST_OUT;
+#ifndef PA_WALK_COST_HEAD
+#define PA_WALK_COST_HEAD 8
+#endif
+static constexpr uint32_t kWalkCostIn = PA_WALK_COST_IN, kWalkCostOut = PA_WALK_COST_OUT,
+                          kWalkCostHead = PA_WALK_COST_HEAD;
 
 // Block ranges of the pass and the lane streams.  Every chunk's events are cut
-// into pieces of about E / target events (never across a chunk, so a block's
-// bins cover one chunk), each cut moved to the next window start; a block's
+// into pieces of about 1 / target of the total cost of the pass (the walk
+// kernel's relative costs of its events and window set-ups; never across a
+// chunk, so a block's bins cover one chunk), each cut moved to the next
+// window start; a block's
 // windows are then dealt to its lanes (pa_load.hip) and scattered into the
 // interleaved streams.  Also the first block of every chunk, for the
 // finalize kernel.  The sorted events are in c->ls.skey / sslew / sorig.
@@ -511,27 +517,70 @@ static int build_ranges(pa_ctx *c, Events &v) {
   if (W > 0)
     HIPCHK(pa::launch_win_starts(E, ls.skey.as<uint64_t>(), ls.winc.as<uint32_t>(), ls.ws.as<uint32_t>(), s));
 
-  // ---- block ranges; with windows, every block's first window and LUT range
+  // ---- every sorted event's cost in the pass (the walk kernel's relative
+  // costs of input-pin and output-pin events and of a window's set-up, else
+  // one per event), and the cost before every chunk: blocks get equal costs
   const bool try_walk = W > 0 && v.pad_key != 0 && v.compact_ok;
   const int32_t room =
       try_walk ? pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax) : 0;
+  std::vector<uint64_t> cpre((size_t)v.Q + 1, 0);
+  if (E > 0) {
+    HIPCHK(ls.k0.ensure(sizeof(uint64_t) * E));  // the sort's buffers, free again here
+    HIPCHK(ls.k1.ensure(sizeof(uint64_t) * E));
+    HIPCHK(pa::launch_event_cost(E, ls.skey.as<uint64_t>(), pa::out_code(v.pb), try_walk ? kWalkCostIn : 1u,
+                                 try_walk ? kWalkCostOut : 1u, try_walk ? kWalkCostHead : 0u, ls.k0.as<uint64_t>(),
+                                 s));
+    size_t tb = 0;
+    HIPCHK(pa::scan_inclusive_u64(ls.k0.as<uint64_t>(), ls.k1.as<uint64_t>(), E, nullptr, &tb, s));
+    HIPCHK(ls.tmp.ensure(tb));
+    HIPCHK(pa::scan_inclusive_u64(ls.k0.as<uint64_t>(), ls.k1.as<uint64_t>(), E, ls.tmp.p, &tb, s));
+    HIPCHK(ls.wkey0.ensure(sizeof(uint64_t) * ((size_t)v.Q + 1)));
+    HIPCHK(pa::launch_gather_prefix(v.Q + 1, ls.cbase.as<uint32_t>(), ls.k1.as<uint64_t>(), ls.wkey0.as<uint64_t>(),
+                                    s));
+    HIPCHK(hipMemcpyAsync(cpre.data(), ls.wkey0.p, sizeof(uint64_t) * cpre.size(), hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+  }
+  const uint64_t total = cpre[v.Q];
+
+  // ---- block ranges; with windows, every block's first window and LUT range
   int32_t nr = 0;
   std::vector<uint32_t> rs, rq, cb(v.Q + 1);
+  std::vector<uint64_t> tgt;
+  std::vector<size_t> tgt_at;
   v.walk_lut = 0;
   for (int attempt = 0;; ++attempt) {
-    const int64_t per =
-        std::max<int64_t>(min_events, (v.E + target_blocks - 1) / std::max<int64_t>(1, target_blocks));
+    const uint64_t per_cost = std::max<uint64_t>(1, (total + target_blocks - 1) / std::max<int64_t>(1, target_blocks));
     rs.clear();
     rq.clear();
+    tgt.clear();
+    tgt_at.clear();
     for (int32_t q = 0; q < v.Q; ++q) {
       cb[q] = (uint32_t)rs.size();
       const int64_t a = v.h_chunk_base[q], b = v.h_chunk_base[q + 1];
       if (b <= a) continue;
-      const int64_t n = std::max<int64_t>(1, (b - a) / per);  // never more blocks than the target
+      // never more blocks than the target, nor blocks of fewer than min_events events
+      const uint64_t cq = cpre[q + 1] - cpre[q];
+      const int64_t n = std::max<int64_t>(1, std::min<int64_t>((int64_t)(cq / per_cost), (b - a) / min_events));
       for (int64_t i = 0; i < n; ++i) {
-        rs.push_back((uint32_t)(a + (b - a) * i / n));
+        if (i > 0) {
+          tgt.push_back(cpre[q] + cq * (uint64_t)i / (uint64_t)n);
+          tgt_at.push_back(rs.size());
+        }
+        rs.push_back((uint32_t)a);
         rq.push_back((uint32_t)q);
       }
+    }
+    if (!tgt.empty()) {
+      // every inner cut: the first event past its share of the chunk's cost
+      HIPCHK(ls.wkey1.ensure(sizeof(uint64_t) * tgt.size()));
+      HIPCHK(ls.worder.ensure(sizeof(uint32_t) * tgt.size()));
+      HIPCHK(hipMemcpyAsync(ls.wkey1.p, tgt.data(), sizeof(uint64_t) * tgt.size(), hipMemcpyHostToDevice, s));
+      HIPCHK(pa::launch_cost_cuts((int32_t)tgt.size(), ls.wkey1.as<uint64_t>(), ls.k1.as<uint64_t>(), E,
+                                  ls.worder.as<uint32_t>(), s));
+      std::vector<uint32_t> pos(tgt.size());
+      HIPCHK(hipMemcpyAsync(pos.data(), ls.worder.p, sizeof(uint32_t) * pos.size(), hipMemcpyDeviceToHost, s));
+      HIPCHK(hipStreamSynchronize(s));
+      for (size_t i = 0; i < pos.size(); ++i) rs[tgt_at[i]] = pos[i];
     }
     cb[v.Q] = (uint32_t)rs.size();
     nr = (int32_t)rs.size();
@@ -560,7 +609,7 @@ static int build_ranges(pa_ctx *c, Events &v) {
       v.walk_lut = (int32_t)most;
       break;
     }
-    if (c->tun.grid_blocks > 0 || attempt >= 3 || per <= min_events) break;
+    if (c->tun.grid_blocks > 0 || attempt >= 3) break;
     target_blocks *= 2;
   }
   v.n_ranges = nr;

@@ -94,6 +94,15 @@ hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, c
                           uint64_t *key, float *slew, uint32_t *orig, hipStream_t s);
 int lane_plan_lanes();  // lanes of a block of the pass
 hipError_t launch_fill_u64(int64_t n, uint64_t v, uint64_t *out, hipStream_t s);
+// the cost of every sorted event in the pass (kind weight plus a window head's
+// weight); the first event past each cost target; the cost before given events
+hipError_t launch_event_cost(int64_t E, const uint64_t *skey, uint32_t outc, uint32_t w_in, uint32_t w_out,
+                             uint32_t w_head, uint64_t *cost, hipStream_t s);
+hipError_t launch_cost_cuts(int32_t n, const uint64_t *target, const uint64_t *pref, int64_t E, uint32_t *pos,
+                            hipStream_t s);
+hipError_t launch_gather_prefix(int32_t n, const uint32_t *at, const uint64_t *pref, uint64_t *out, hipStream_t s);
+hipError_t scan_inclusive_u64(const uint64_t *in, uint64_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
+                              hipStream_t s);
 hipError_t scan_inclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
                               hipStream_t s);
 hipError_t sort_pairs_u64(const uint64_t *kin, uint64_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,

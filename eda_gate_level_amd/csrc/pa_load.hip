@@ -403,6 +403,38 @@ __global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, co
   }
 }
 
+// Every sorted event's cost in the pass, for cutting the chunks into blocks
+// of equal cost: w_in for an input-pin event, w_out for an output-pin
+// event, plus w_head for the first event of a window (its set-up).
+__global__ void k_event_cost(int64_t E, const uint64_t *skey, uint32_t outc, uint32_t w_in, uint32_t w_out,
+                             uint32_t w_head, uint64_t *cost) {
+  for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
+    const uint64_t K = skey[x];
+    const bool out = ((uint32_t)K & outc) == outc;
+    cost[x] = (out ? w_out : w_in) + (((K >> kKeyHeadShift) & 1ull) ? w_head : 0u);
+  }
+}
+
+// pos[i] = the first sorted event whose inclusive cost prefix exceeds
+// target[i] (E if none); pref is nondecreasing
+__global__ void k_cost_cuts(int32_t n, const uint64_t *target, const uint64_t *pref, int64_t E, uint32_t *pos) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    const uint64_t t = target[i];
+    int64_t lo = 0, hi = E;
+    while (lo < hi) {
+      const int64_t mid = (lo + hi) >> 1;
+      if (pref[mid] <= t) lo = mid + 1; else hi = mid;
+    }
+    pos[i] = (uint32_t)lo;
+  }
+}
+
+// out[i] = inclusive prefix before sorted event at[i] (0 for event 0)
+__global__ void k_gather_prefix(int32_t n, const uint32_t *at, const uint64_t *pref, uint64_t *out) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    out[i] = at[i] > 0 ? pref[at[i] - 1] : 0ull;
+}
+
 // every sorted event to its slot in its lane's stream
 __global__ void k_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
                           const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
@@ -625,6 +657,28 @@ hipError_t launch_fill_u64(int64_t n, uint64_t v, uint64_t *out, hipStream_t s) 
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_u64, dim3(grid_for(n)), dim3(kLT), 0, s, n, v, out);
   return hipGetLastError();
+}
+
+hipError_t launch_event_cost(int64_t E, const uint64_t *skey, uint32_t outc, uint32_t w_in, uint32_t w_out,
+                             uint32_t w_head, uint64_t *cost, hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_event_cost, dim3(grid_for(E)), dim3(kLT), 0, s, E, skey, outc, w_in, w_out, w_head, cost);
+  return hipGetLastError();
+}
+hipError_t launch_cost_cuts(int32_t n, const uint64_t *target, const uint64_t *pref, int64_t E, uint32_t *pos,
+                            hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_cost_cuts, dim3(grid_for(n)), dim3(kLT), 0, s, n, target, pref, E, pos);
+  return hipGetLastError();
+}
+hipError_t launch_gather_prefix(int32_t n, const uint32_t *at, const uint64_t *pref, uint64_t *out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather_prefix, dim3(grid_for(n)), dim3(kLT), 0, s, n, at, pref, out);
+  return hipGetLastError();
+}
+hipError_t scan_inclusive_u64(const uint64_t *in, uint64_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
+                              hipStream_t s) {
+  return hipcub::DeviceScan::InclusiveSum(tmp, *tmp_bytes, in, out, (int)n, s);
 }
 
 hipError_t scan_inclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
