@@ -67,7 +67,8 @@ def kernel_text(src):
 
 def profiled_traffic(workload):
     """HBM bytes per launch of the pass kernel (k_walk) from the committed
-    rocprofv3 counter summary, or None when the kernel source changed since."""
+    rocprofv3 counter summary, or None when the kernel or the layout code
+    changed since."""
     import hashlib
     import re
 
@@ -77,7 +78,8 @@ def profiled_traffic(workload):
     except OSError:
         return None
     h = hashlib.sha256()
-    for f in ("pa_pass.hip", "pa_common.h"):
+    # the kernel and the layout code (the stream's slots are the traffic)
+    for f in ("pa_pass.hip", "pa_common.h", "pa_api.hip", "pa_load.hip"):
         with open(os.path.join(ROOT, "eda_gate_level_amd", "csrc", f)) as fh:
             h.update(kernel_text(fh.read()).encode())
     m_sha = re.search(r"fused_source_sha256: ([0-9a-f]{64})", text)

@@ -520,7 +520,7 @@ static int build_ranges(pa_ctx *c, Events &v) {
   // ---- every sorted event's cost in the pass (the walk kernel's relative
   // costs of input-pin and output-pin events and of a window's set-up, else
   // one per event), and the cost before every chunk: blocks get equal costs
-  const bool try_walk = W > 0 && v.pad_key != 0 && v.compact_ok;
+  const bool try_walk = W > 0 && v.compact_ok;
   const int32_t room =
       try_walk ? pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax) : 0;
   std::vector<uint64_t> cpre((size_t)v.Q + 1, 0);
@@ -806,13 +806,10 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   // the cycle in the chunk has the low word's bits above pin code and tic, and
   // the bits the gate id leaves free in the high word
   const uint32_t gb = bits_for((uint64_t)std::max<int64_t>(G - 1, 0));
-  // and one cycle value more than the chunk needs is kept for the pad slots'
-  // dummy bin (cycle Cc), where the key has the bits
   const uint32_t lc_max = (32 - v.pb - v.tb) + (22 - gb);
   int64_t Cc_want = c->tun.chunk_cycles > 0 ? c->tun.chunk_cycles : pa::pass_max_chunk_cycles();
   Cc_want = std::min<int64_t>(Cc_want, (int64_t)pa::pass_max_chunk_cycles());
-  const uint32_t lc_use = lc_max > 0 ? lc_max - 1 : 0;
-  if (lc_use < 31) Cc_want = std::min<int64_t>(Cc_want, int64_t(1) << lc_use);
+  if (lc_max < 31) Cc_want = std::min<int64_t>(Cc_want, int64_t(1) << lc_max);
   // the walk kernel's 32-bit key: cycle, tic (bits of t_clk itself, so the
   // tic field is never all ones in an event) and the pin code's high bits;
   // unless the caller fixed the chunk, it is cut to what that key holds
