@@ -135,10 +135,15 @@ int pa_load_design(pa_ctx *ctx, int64_t n_gates, const int32_t *gate_cell, const
  * previously loaded events stay usable) and re-laid out into library-owned
  * memory: time chunks of chunk_cycles cycles; every gate's part of a chunk
  * is cut into 2^s equal windows sized from the gate's event density (the
- * paper's event-density-aware per-gate cycle partitioning), the events of a
- * window in clock cycle, time and pin order; the windows of a block of the
- * pass are dealt to its lanes by length, and every lane walks its windows
- * event by event. */
+ * paper's event-density-aware per-gate cycle partitioning), a gate's input
+ * events and its output events in windows of their own, the events of a
+ * window in clock cycle, time and pin order.  The pass's blocks are cut so
+ * that each carries about the same walk cost (events and window heads);
+ * a block's windows go in phases of up to 64 windows of one pin kind, dealt
+ * to its waves by cost, one window per lane, and every lane walks its window
+ * event by event.  Besides the 16-byte event records the layout keeps an
+ * 8-byte record per slot (cycle, tick and pin packed into 32 bits, the slew
+ * as float32) that the pass streams when the sizes allow. */
 int pa_load_events(pa_ctx *ctx, int64_t n_pins, int64_t n_events, const int64_t *pin_ptr,
                    const uint8_t *pin_init, const int64_t *evt_t, const uint8_t *evt_val,
                    const float *evt_slew, int64_t t_clk, int64_t t_max, double tick_s);
@@ -213,8 +218,9 @@ typedef struct {
                                  scratch is freed when pa_load_events returns) */
   float kernel_ms[4];         /* last timed pa_run: fused, finalize, (unused), whole pass; mode 2 fills only the last */
   int64_t n_windows;          /* density-aware windows of the layout */
-  int64_t n_slots;            /* slots of the pass's lane streams: the events plus the empty slots
-                                 that pad windows to even lengths and lanes to their wave's longest */
+  int64_t n_slots;            /* slots of the pass's lane streams: the events, two header slots per
+                                 window (walk kernel), and the empty slots that pad a phase's lanes to even
+                                 lengths and to the phase's longest */
   int32_t wave_steps_max;     /* steps (event pairs) of the pass's longest wave */
   float wave_steps_mean;      /* steps of a wave, averaged over the waves with work */
   int32_t tables_in_lds;      /* 1: every block of the pass stages the per-cell tables (axes,

@@ -393,3 +393,34 @@ def test_plain_bins_is_a_timing_aid():
     with pytest.raises(pa.PaError) as ei:
         pa.PowerAnalysis(plain_bins=3)
     assert ei.value.code == pa.PA_EINVAL
+
+
+@pytest.mark.parametrize("name", ["medium", "skewed"])
+def test_window_count_against_the_additive_law(name):
+    """The paper sizes a gate's work items by an additive law, about
+    events / target + a floor.  The library's windows, 2^s per (gate, time
+    chunk) with s the smallest level whose expected events per window are
+    at most 32, split by pin kind, must land between half the law's count
+    (target 32, floor one per (gate, chunk)) and four times it (twice for
+    the power of two, twice for the two kinds)."""
+    import eda_gate_level_amd as pa
+
+    w = synth.make(name)
+    d, t = w.design, w.trace
+    _print_case(f"window law {name}")
+    an = pa.PowerAnalysis()
+    try:
+        an.load(d, t)
+        st = an.window_stats()
+        info = an.info()
+    finally:
+        an.close()
+    Cc = info["chunk_cycles"]
+    pb = d.pin_base()
+    gate = np.repeat(np.repeat(np.arange(d.n_gates), np.diff(pb)), np.diff(t.pin_ptr))
+    chunk = (t.evt_t // t.t_clk) // Cc
+    per = np.bincount(gate.astype(np.int64) * info["n_chunks"] + chunk)
+    per = per[per > 0]
+    law = float(np.sum(per / 32.0 + 1.0))
+    print(f"windows {st['n_windows']} law {law:.0f} ratio {st['n_windows'] / law:.3f}", flush=True)
+    assert 0.5 * law <= st["n_windows"] <= 4.0 * law
