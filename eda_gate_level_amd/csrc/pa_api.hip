@@ -464,14 +464,20 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
 #endif
 static constexpr double kWindowEvents = PA_WINDOW_EVENTS;
 #ifndef PA_WALK_COST_IN
-#define PA_WALK_COST_IN 5
+#define PA_WALK_COST_IN 10
 #endif
 #ifndef PA_WALK_COST_OUT
-#define PA_WALK_COST_OUT 2
+#define PA_WALK_COST_OUT 3
 #endif
 #ifndef PA_WALK_COST_HEAD
-#define PA_WALK_COST_HEAD 8
+#define PA_WALK_COST_HEAD 5
 #endif
+// The walk kernel's relative costs of an input-pin event (three LDS atomics,
+// four LUT reads and the table reads; a gate with one or two inputs costs 2
+// or 1 less, one with five or more 1 more), an output-pin event (two
+// atomics) and a window's set-up: a least-squares fit of the blocks' walk
+// times to their event and window counts on the 10M-event, skewed,
+// glitch-heavy and 200M-event workloads
 static constexpr uint32_t kWalkCostIn = PA_WALK_COST_IN, kWalkCostOut = PA_WALK_COST_OUT,
                           kWalkCostHead = PA_WALK_COST_HEAD;
 
@@ -528,7 +534,8 @@ static int build_ranges(pa_ctx *c, Events &v) {
     HIPCHK(ls.k0.ensure(sizeof(uint64_t) * E));  // the sort's buffers, free again here
     HIPCHK(ls.k1.ensure(sizeof(uint64_t) * E));
     HIPCHK(pa::launch_event_cost(E, ls.skey.as<uint64_t>(), pa::out_code(v.pb), try_walk ? kWalkCostIn : 1u,
-                                 try_walk ? kWalkCostOut : 1u, try_walk ? kWalkCostHead : 0u, ls.k0.as<uint64_t>(),
+                                 try_walk ? kWalkCostOut : 1u, try_walk ? kWalkCostHead : 0u,
+                                 try_walk ? d.gate_k.as<int32_t>() : nullptr, v.gb, ls.k0.as<uint64_t>(),
                                  s));
     size_t tb = 0;
     HIPCHK(pa::scan_inclusive_u64(ls.k0.as<uint64_t>(), ls.k1.as<uint64_t>(), E, nullptr, &tb, s));
@@ -644,7 +651,7 @@ static int build_ranges(pa_ctx *c, Events &v) {
     HIPCHK(ls.wlane.ensure(sizeof(uint2) * W));
     HIPCHK(ls.phase.ensure(sizeof(uint2) * pa::phase_plan_entries(W, nr)));
     HIPCHK(ls.wave_len.ensure(sizeof(uint32_t) * (size_t)nr * NW));
-    // the walk kernel's slots of an input phase cost about 2.5 times those of
+    // the walk kernel's slots of an input phase cost about 3.3 times those of
     // an output phase (no table reads, leakage or pin records there)
     const bool walk = v.walk_lut > 0;
     HIPCHK(pa::launch_phase_plan(nr, ls.bwin.as<uint32_t>(), ls.worder.as<uint32_t>(), ls.wkey1.as<uint64_t>(),

@@ -97,7 +97,7 @@ hipError_t launch_fill_u64(int64_t n, uint64_t v, uint64_t *out, hipStream_t s);
 // the cost of every sorted event in the pass (kind weight plus a window head's
 // weight); the first event past each cost target; the cost before given events
 hipError_t launch_event_cost(int64_t E, const uint64_t *skey, uint32_t outc, uint32_t w_in, uint32_t w_out,
-                             uint32_t w_head, uint64_t *cost, hipStream_t s);
+                             uint32_t w_head, const int32_t *gate_k, uint32_t gb, uint64_t *cost, hipStream_t s);
 hipError_t launch_cost_cuts(int32_t n, const uint64_t *target, const uint64_t *pref, int64_t E, uint32_t *pos,
                             hipStream_t s);
 hipError_t launch_gather_prefix(int32_t n, const uint32_t *at, const uint64_t *pref, uint64_t *out, hipStream_t s);

@@ -297,16 +297,23 @@ __global__ void k_win_keys(uint32_t W, const uint32_t *ws, const uint32_t *bwin,
   }
 }
 
+// Relative walk times of a block's waves 4 i .. 4 i + 3 given equal work,
+// measured on the 10M-event, skewed and 200M-event workloads: the i-th oldest
+// wave of every SIMD issues after the older ones
+__constant__ uint32_t kWaveSlow[4] = {72u, 92u, 110u, 126u};
+
 // One block per block of the pass.  Its windows come in worder (input
 // windows longest first, then output windows longest first; sorted keys in
 // wkey); phase i of a kind is that kind's windows 64 i .. 64 i + 63.  One
 // thread deals the phases, costliest first, to the waves, each to the wave
-// with the least cost so far (a phase costs its slots times w_in or w_out,
-// the relative cost of a slot of its kind in the pass); ph gets the phase's
+// that would finish it first (its cost so far plus the phase's, times its
+// relative walk time; a phase costs its slots times w_in or w_out, the
+// relative cost of a slot of its kind in the pass); ph gets the phase's
 // wave and first slot, in this block's part [floor(w0 / 64) + 2 b, ...) of
 // the array, which holds at least its phases.  Then every window gets its
 // place: wlane[w] = (global wave << 6 | lane, first slot).  wave_len = the
 // slots of every wave's stream.
+
 __global__ __launch_bounds__(kPlanNT) void k_phase_plan(const uint32_t *bwin, const uint32_t *worder,
                                                         const uint64_t *wkey, const uint32_t *wlen, uint32_t hp,
                                                         uint32_t w_in, uint32_t w_out, uint2 *ph, uint2 *wlane,
@@ -333,9 +340,13 @@ __global__ __launch_bounds__(kPlanNT) void k_phase_plan(const uint32_t *bwin, co
       const uint32_t li = i < pin_ ? plen(i * 64) : 0u, lo2 = o < pout ? plen(nin + o * 64) : 0u;
       const uint64_t ci = (uint64_t)li * w_in, co = (uint64_t)lo2 * w_out;
       const bool take_in = i < pin_ && (o >= pout || ci >= co);
+      const uint64_t cc = take_in ? ci : co;
       int v = 0;
-      for (int x = 1; x < kLaneNW; ++x)
-        if (cost[x] < cost[v]) v = x;
+      uint64_t best = (cost[0] + cc) * kWaveSlow[0];
+      for (int x = 1; x < kLaneNW; ++x) {
+        const uint64_t f = (cost[x] + cc) * kWaveSlow[x >> 2];
+        if (f < best) best = f, v = x;
+      }
       php[take_in ? i : pin_ + o] = make_uint2((uint32_t)v, load[v]);
       load[v] += take_in ? li : lo2;
       cost[v] += take_in ? ci : co;
@@ -407,11 +418,19 @@ __global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, co
 // of equal cost: w_in for an input-pin event, w_out for an output-pin
 // event, plus w_head for the first event of a window (its set-up).
 __global__ void k_event_cost(int64_t E, const uint64_t *skey, uint32_t outc, uint32_t w_in, uint32_t w_out,
-                             uint32_t w_head, uint64_t *cost) {
+                             uint32_t w_head, const int32_t *gate_k, uint32_t gb, uint64_t *cost) {
   for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
     const uint64_t K = skey[x];
     const bool out = ((uint32_t)K & outc) == outc;
-    cost[x] = (out ? w_out : w_in) + (((K >> kKeyHeadShift) & 1ull) ? w_head : 0u);
+    uint32_t wi = w_in;
+    if (gate_k != nullptr && !out) {
+      // an input event of a gate with few inputs costs less (its LUT rows
+      // spread over fewer LDS banks): w_in - 2 for one input, - 1 for two,
+      // + 1 from five
+      const int k = gate_k[(uint32_t)(K >> 42) & ((1u << gb) - 1u)];
+      wi = (uint32_t)max(1, (int)w_in + (k < 3 ? k - 3 : 0) + (k >= 5 ? 1 : 0));
+    }
+    cost[x] = (out ? w_out : wi) + (((K >> kKeyHeadShift) & 1ull) ? w_head : 0u);
   }
 }
 
@@ -660,9 +679,10 @@ hipError_t launch_fill_u64(int64_t n, uint64_t v, uint64_t *out, hipStream_t s) 
 }
 
 hipError_t launch_event_cost(int64_t E, const uint64_t *skey, uint32_t outc, uint32_t w_in, uint32_t w_out,
-                             uint32_t w_head, uint64_t *cost, hipStream_t s) {
+                             uint32_t w_head, const int32_t *gate_k, uint32_t gb, uint64_t *cost, hipStream_t s) {
   if (E <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_event_cost, dim3(grid_for(E)), dim3(kLT), 0, s, E, skey, outc, w_in, w_out, w_head, cost);
+  hipLaunchKernelGGL(k_event_cost, dim3(grid_for(E)), dim3(kLT), 0, s, E, skey, outc, w_in, w_out, w_head, gate_k, gb,
+                     cost);
   return hipGetLastError();
 }
 hipError_t launch_cost_cuts(int32_t n, const uint64_t *target, const uint64_t *pref, int64_t E, uint32_t *pos,

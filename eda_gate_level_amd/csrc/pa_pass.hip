@@ -942,6 +942,17 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
 
 #pragma unroll 1
     for (int p0 = 0; p0 < npair; p0 += GP * R) {
+      // issue priority by the share of the wave's stream still to walk (the
+      // quarter: 3 for the first, 0 for the last): a SIMD issues oldest wave
+      // first among equals, and a wave that falls behind the others of its
+      // block catches up instead of finishing last
+      {
+        const int quarter = (4 * (npair - p0) - 1) / npair;
+        if (quarter >= 3) __builtin_amdgcn_s_setprio(3);
+        else if (quarter == 2) __builtin_amdgcn_s_setprio(2);
+        else if (quarter == 1) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+      }
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         const int pg = p0 + u * GP;  // the group's first pair
@@ -967,6 +978,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
         }
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   }
   __syncthreads();
 
