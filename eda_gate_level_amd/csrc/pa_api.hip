@@ -166,6 +166,8 @@ struct Events {
   int32_t wave_steps_max = 0;       // steps of the longest wave, and the mean over waves with work
   float wave_steps_mean = 0.f;
   DBuf rstart, rchunk, chunk_blk;  // block ranges of the pass, first block of every chunk
+  std::vector<uint32_t> chunk_blk_host;
+  double l0_host = 0.0;            // the leakage power at t = 0 (the value in l0)
   DBuf wdesc, wlen, l0;            // every wave's (first slot, events per lane); events per window; leakage at t = 0
   DBuf lplan;                      // per block, the cells whose LUTs it copies into LDS
   int32_t lut_lds = 0;             // LDS doubles of a block for those copies (0: none)
@@ -629,6 +631,7 @@ static int build_ranges(pa_ctx *c, Events &v) {
   HIPCHK(v.res.ensure(sizeof(double) * 16));
   HIPCHK(hipMemcpyAsync(v.rchunk.p, rq.data(), sizeof(uint32_t) * rq.size(), hipMemcpyHostToDevice, s));
   HIPCHK(hipMemcpyAsync(v.chunk_blk.p, cb.data(), sizeof(uint32_t) * cb.size(), hipMemcpyHostToDevice, s));
+  v.chunk_blk_host = cb;
   HIPCHK(v.wdesc.ensure(sizeof(uint2) * (size_t)v.grid * NW));
   HIPCHK(hipMemsetAsync(v.wdesc.p, 0, sizeof(uint2) * (size_t)v.grid * NW, s));
   std::vector<uint32_t> wave_len((size_t)nr * NW, 0);
@@ -720,6 +723,7 @@ static int build_ranges(pa_ctx *c, Events &v) {
   HIPCHK(v.l0.ensure(sizeof(double)));
   HIPCHK(pa::launch_leak0(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
                           d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), part.as<double>(), v.l0.as<double>(), s));
+  HIPCHK(hipMemcpyAsync(&v.l0_host, v.l0.p, sizeof(double), hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
   return PA_OK;
 }
@@ -1030,7 +1034,9 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   f.tick_s = v.tick_s;
   f.grid = v.grid;
   f.chunk_blk = v.chunk_blk.as<uint32_t>();
-  f.l0 = v.l0.as<double>();
+  if (v.Q < 64)
+    for (int i = 0; i <= v.Q; ++i) f.cblk[i] = v.chunk_blk_host[i];
+  f.l0 = v.l0_host;
   f.blk_wave = a.blk_wave;
   f.blk_cnt = a.blk_cnt;
   f.blk_part = a.blk_part;

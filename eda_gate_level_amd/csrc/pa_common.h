@@ -122,10 +122,11 @@ struct FinalArgs {
   double tick_s;
   int32_t grid;
   const uint32_t *chunk_blk;  // [Q+1] first block of every chunk (blocks are in chunk order)
+  uint32_t cblk[64];          // the same values when Q < 64, passed by value (no dependent load)
   const double *blk_wave;
   const unsigned long long *blk_cnt;
   const double *blk_part;
-  const double *l0;           // leakage power at t = 0, summed at load
+  double l0;                  // leakage power at t = 0, summed at load
   double *wave_out;
   uint64_t *cyc_events;
   uint64_t *cyc_glitches;

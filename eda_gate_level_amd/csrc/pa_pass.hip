@@ -548,6 +548,10 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
 //   * leakage changes are binned as (change at the bin start, minus the
 //     change times its time in the bin), which needs no partial-bin fix-up.
 
+// the walk kernel keeps the pin records of gates with at most this many
+// inputs in registers
+constexpr int kWalkRegPins = 4;
+
 struct WalkBin {
   double w;    // energy: dynamic, minus leakage change x time in the bin
   double d;    // leakage power changes in the bin
@@ -615,7 +619,7 @@ __device__ __forceinline__ void bin_add(P *p, T v) {
   else __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <int NS, int NC, int PLAIN>
+template <int NS, int NC, int PLAIN, int KREG>
 __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   constexpr int NIN = NS - 2;  // inner slew-axis points: the segment is the count at or below the slew
 #ifndef PA_WALK_GROUP
@@ -748,6 +752,13 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     float pslew = 1.f;
     bool out_phase = false;  // the kind of the current phase's windows (wave-uniform)
     lds_u32 *prec = L.prec + (wid * a.kmax * 64 + lane) * 2;
+    // with at most KREG = 4 input pins per gate, the pin records (last time
+    // in the cycle, slew bits) live in registers instead: two 4-vectors whose
+    // elements a per-lane pin selects (selects, not an indexed array, which
+    // would go to scratch memory)
+    static_assert(KREG == 0 || KREG == 4, "register pin records hold four pins");
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 rtic = {0u, 0u, 0u, 0u}, rslw = {0u, 0u, 0u, 0u};
 
     // a header pair: every lane with a window in the new phase sets it up (a
     // lane without one sets up cell 0 with load 0, and walks empty slots)
@@ -858,26 +869,49 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
       // rarely, a glitch: Eq. 2 (reading), the pulse width and the slews of
       // the pin's previous event in the cycle and this one; the pin records
       // are read and written in event order (both events may be one pin's)
-      lds_u32 *pr0 = prec + cl[0] * 128, *pr1 = prec + cl[1] * 128;
-      if (glitch[0] || glitch[1]) {
+      if constexpr (KREG > 0) {
+        if (glitch[0] || glitch[1]) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          lds_u32 *pr = r ? pr1 : pr0;
-          if (glitch[r]) {
-            const uint32_t ptic_pin = pr[0], pslew_pin = pr[1];
-            const double pw = (double)(tic[r] - ptic_pin);
-            const double rr = pw / (0.5 * ((double)sl[r] + (double)__uint_as_float(pslew_pin)));
-            E[r] *= rr > 1.0 ? 1.0 : rr;
-            e_gl += E[r];
+          for (int r = 0; r < 2; ++r) {
+            if (glitch[r]) {
+              const uint32_t ptic_pin = rtic[cl[r] & 3u], pslew_pin = rslw[cl[r] & 3u];
+              const double pw = (double)(tic[r] - ptic_pin);
+              const double rr = pw / (0.5 * ((double)sl[r] + (double)__uint_as_float(pslew_pin)));
+              E[r] *= rr > 1.0 ? 1.0 : rr;
+              e_gl += E[r];
+            }
+            rtic[cl[r] & 3u] = tic[r];
+            rslw[cl[r] & 3u] = __float_as_uint(sl[r]);
           }
-          pr[0] = tic[r];
-          pr[1] = __float_as_uint(sl[r]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            rtic[cl[r] & 3u] = tic[r];
+            rslw[cl[r] & 3u] = __float_as_uint(sl[r]);
+          }
         }
       } else {
-        pr0[0] = tic[0];
-        pr0[1] = __float_as_uint(sl[0]);
-        pr1[0] = tic[1];
-        pr1[1] = __float_as_uint(sl[1]);
+        lds_u32 *pr0 = prec + cl[0] * 128, *pr1 = prec + cl[1] * 128;
+        if (glitch[0] || glitch[1]) {
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            lds_u32 *pr = r ? pr1 : pr0;
+            if (glitch[r]) {
+              const uint32_t ptic_pin = pr[0], pslew_pin = pr[1];
+              const double pw = (double)(tic[r] - ptic_pin);
+              const double rr = pw / (0.5 * ((double)sl[r] + (double)__uint_as_float(pslew_pin)));
+              E[r] *= rr > 1.0 ? 1.0 : rr;
+              e_gl += E[r];
+            }
+            pr[0] = tic[r];
+            pr[1] = __float_as_uint(sl[r]);
+          }
+        } else {
+          pr0[0] = tic[0];
+          pr0[1] = __float_as_uint(sl[0]);
+          pr1[0] = tic[1];
+          pr1[1] = __float_as_uint(sl[1]);
+        }
       }
       // the components and the bins; an empty slot adds nothing
 #pragma unroll
@@ -1110,28 +1144,33 @@ constexpr int kFC = 64;             // finalize: cycles per block (one per lane)
 constexpr int kFP = 8;              // finalize: waves per block, each adding up a share of the blocks
 constexpr int kFT = kFC * kFP;
 
-// Lane l of wave p adds up, for cycle l of the block's 64, the bins of the
-// p-th share of the cycle's chunk's blocks; the waves also share the sums over
-// all blocks' totals.  Wave 0 then adds the shares in order after the leakage
-// carried into the chunk (L0 plus the changes of earlier chunks); block 0 also
-// writes the totals (Eq. 3).  Every sum runs in a fixed order, and every loop
-// keeps eight independent loads in flight.
+// Lane l of wave p < 7 adds up, for cycle l of the block's 64, the bins of
+// the p-th seventh of the cycle's chunk's blocks; wave 7 adds up the blocks'
+// totals (so no wave waits for two rounds of loads).  Wave 0 then adds the
+// shares in order after the leakage carried into the chunk (L0 plus the
+// changes of earlier chunks); block 0 also writes the totals (Eq. 3).  Every
+// sum runs in a fixed order.  L0 and the chunks' first blocks (fewer than 64
+// chunks) come by value, and the loads of a loop step are issued
+// unconditionally (an index past the end is clamped and its value dropped),
+// so they go out together and wait once.
 __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
   __shared__ double s_w[kFP][kFC];
   __shared__ unsigned long long s_n[kFP][kFC];
-  __shared__ double s_t[kFP][8];
+  __shared__ double s_t[8];
   const int lane = threadIdx.x & 63, wp = threadIdx.x >> 6;
   const int64_t c0 = (int64_t)blockIdx.x * kFC;
   const int64_t chi = min(c0 + kFC, f.C) - 1;
   const int64_t c = c0 + lane;
   const int qa = (int)(c0 / f.Cc), qb = (int)(chi / f.Cc);
   const int q = (int)(min(c, chi) / f.Cc);
-  const uint32_t ba = f.chunk_blk[qa];
+  const bool inl = f.Q < 64;
+  auto cblk = [&](int i) -> uint32_t { return inl ? f.cblk[i] : f.chunk_blk[i]; };
   const bool totals = blockIdx.x == 0;
-  {
+  constexpr int kBW = kFP - 1;  // waves adding up bins
+  if (wp < kBW) {
     // this wave's share of the cycle's chunk's blocks
-    const uint32_t b0 = f.chunk_blk[q], b1 = f.chunk_blk[q + 1];
-    const uint32_t n = b1 - b0, s0 = b0 + n * wp / kFP, s1 = b0 + n * (wp + 1) / kFP;
+    const uint32_t b0 = cblk(q), b1 = cblk(q + 1);
+    const uint32_t n = b1 - b0, s0 = b0 + n * wp / kBW, s1 = b0 + n * (wp + 1) / kBW;
     const int cin = (int)(min(c, chi) - (int64_t)q * f.Cc);
     double w = 0.0;
     unsigned long long cnt = 0;
@@ -1140,34 +1179,44 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
       unsigned long long m[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const bool ok = bb + u < s1;
-        v[u] = ok ? f.blk_wave[(size_t)(bb + u) * f.Cc + cin] : 0.0;
-        m[u] = ok ? f.blk_cnt[(size_t)(bb + u) * f.Cc + cin] : 0ull;
+        const uint32_t bi = min(bb + u, s1 - 1);
+        v[u] = f.blk_wave[(size_t)bi * f.Cc + cin];
+        m[u] = f.blk_cnt[(size_t)bi * f.Cc + cin];
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        w += v[u];
-        cnt += m[u];
+        const bool ok = bb + u < s1;
+        w += ok ? v[u] : 0.0;
+        cnt += ok ? m[u] : 0ull;
       }
     }
     s_w[wp][lane] = w;
     s_n[wp][lane] = cnt;
-    // this wave's share of the blocks' totals: L0, the changes before chunk qa, and (block 0) the energies
+  } else {
+    // the blocks' totals: the changes before chunk qa, and (block 0) the energies
+    const uint32_t ba = cblk(qa);
     double t[7] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
-    for (int b8 = wp * 64 * 8; b8 < f.grid; b8 += kFT * 8) {
+    for (int b8 = 0; b8 < f.grid; b8 += 64 * 8) {
+      double d5[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) d5[u] = f.blk_part[(size_t)min(b8 + u * 64 + lane, f.grid - 1) * 8 + 5];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         const int bb = b8 + u * 64 + lane;
-        if (bb < f.grid) {
-          const double *pp = f.blk_part + (size_t)bb * 8;
-          if ((uint32_t)bb < ba) t[1] += pp[5];
-          if (totals) {
-            t[2] += pp[0];
-            t[3] += pp[1];
-            t[4] += pp[2];
-            t[5] += pp[3];
-            t[6] += pp[6];
-          }
+        t[1] += (bb < f.grid && (uint32_t)bb < ba) ? d5[u] : 0.0;
+      }
+      if (totals) {
+        double pp[8][5];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const double *p = f.blk_part + (size_t)min(b8 + u * 64 + lane, f.grid - 1) * 8;
+          pp[u][0] = p[0], pp[u][1] = p[1], pp[u][2] = p[2], pp[u][3] = p[3], pp[u][4] = p[6];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const bool ok = b8 + u * 64 + lane < f.grid;
+#pragma unroll
+          for (int x = 0; x < 5; ++x) t[2 + x] += ok ? pp[u][x] : 0.0;
         }
       }
     }
@@ -1175,19 +1224,19 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
     for (int u = 0; u < 7; ++u) t[u] = wave_sum(t[u]);
     if (lane == 0) {
 #pragma unroll
-      for (int u = 0; u < 7; ++u) s_t[wp][u] = t[u];
+      for (int u = 0; u < 7; ++u) s_t[u] = t[u];
     }
+    s_w[wp][lane] = 0.0;
+    s_n[wp][lane] = 0ull;
   }
   __syncthreads();
   if (wp != 0) return;
-  const double l0 = *f.l0;
-  double pre = 0.0;
-#pragma unroll
-  for (int p = 0; p < kFP; ++p) pre += s_t[p][1];
+  const double l0 = f.l0;
+  const double pre = s_t[1];
   // the changes inside chunks qa .. qb-1 (qb - qa < 64), then their exclusive prefix
   double dq = 0.0;
   if (lane < qb - qa) {
-    const uint32_t b0 = f.chunk_blk[qa + lane], b1 = f.chunk_blk[qa + lane + 1];
+    const uint32_t b0 = cblk(qa + lane), b1 = cblk(qa + lane + 1);
     for (uint32_t bb = b0; bb < b1; ++bb) dq += f.blk_part[(size_t)bb * 8 + 5];
   }
   double incl = dq;
@@ -1211,9 +1260,8 @@ __global__ __launch_bounds__(kFT) void k_finalize(FinalArgs f) {
     f.cyc_glitches[c] = cnt >> 32;
   }
   if (totals && lane == 0) {
-    double t[5] = {0.0, 0.0, 0.0, 0.0, 0.0};
-    for (int p = 0; p < kFP; ++p)
-      for (int u = 0; u < 5; ++u) t[u] += s_t[p][2 + u];
+    double t[5];
+    for (int u = 0; u < 5; ++u) t[u] = s_t[2 + u];
     const double window = (double)f.t_max * f.tick_s;
     const double e_leak = l0 * window + t[3];
     f.res[0] = t[0];
@@ -1318,14 +1366,17 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
                        8 * (size_t)max(a.walk_lut, 2 * a.n_slew * a.n_cap);
     if (!a.blk_lut || !a.ckey || !a.cslew || dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
     const dim3 g(grid_blocks), t(kNT);
+    const bool kreg = a.kmax <= kWalkRegPins;
     if (a.n_slew == 7 && a.n_cap == 7) {
-      if (a.plain_bins == 1) hipLaunchKernelGGL((k_walk<7, 7, 1>), g, t, dyn, s, a);
-      else if (a.plain_bins == 2) hipLaunchKernelGGL((k_walk<7, 7, 2>), g, t, dyn, s, a);
-      else hipLaunchKernelGGL((k_walk<7, 7, 0>), g, t, dyn, s, a);
+      if (a.plain_bins == 1) hipLaunchKernelGGL((k_walk<7, 7, 1, 0>), g, t, dyn, s, a);
+      else if (a.plain_bins == 2) hipLaunchKernelGGL((k_walk<7, 7, 2, 0>), g, t, dyn, s, a);
+      else if (kreg) hipLaunchKernelGGL((k_walk<7, 7, 0, kWalkRegPins>), g, t, dyn, s, a);
+      else hipLaunchKernelGGL((k_walk<7, 7, 0, 0>), g, t, dyn, s, a);
     } else if (a.n_slew == 8 && a.n_cap == 8) {
-      if (a.plain_bins == 1) hipLaunchKernelGGL((k_walk<8, 8, 1>), g, t, dyn, s, a);
-      else if (a.plain_bins == 2) hipLaunchKernelGGL((k_walk<8, 8, 2>), g, t, dyn, s, a);
-      else hipLaunchKernelGGL((k_walk<8, 8, 0>), g, t, dyn, s, a);
+      if (a.plain_bins == 1) hipLaunchKernelGGL((k_walk<8, 8, 1, 0>), g, t, dyn, s, a);
+      else if (a.plain_bins == 2) hipLaunchKernelGGL((k_walk<8, 8, 2, 0>), g, t, dyn, s, a);
+      else if (kreg) hipLaunchKernelGGL((k_walk<8, 8, 0, kWalkRegPins>), g, t, dyn, s, a);
+      else hipLaunchKernelGGL((k_walk<8, 8, 0, 0>), g, t, dyn, s, a);
     }
     else return hipErrorInvalidValue;
     return hipGetLastError();
