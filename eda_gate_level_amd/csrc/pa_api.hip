@@ -350,7 +350,8 @@ int pa_load_design(pa_ctx *c, int64_t n_gates, const int32_t *gate_cell, const d
   int32_t kmax = 0;
   for (int32_t i = 0; i < n_cells; ++i) {
     const int32_t k = hk[i];
-    if (k < 1 || k > 8) return fail(PA_EDATA, "pa_load_design: cell %d has %d inputs (1..8 allowed)", i, k);
+    if (k < 1 || k > pa::kMaxInputs)
+      return fail(PA_EDATA, "pa_load_design: cell %d has %d inputs (1..%d allowed)", i, k, pa::kMaxInputs);
     kmax = std::max(kmax, k);
     meta[2 * i] = (uint32_t)k | (uint32_t)(kb << 4);
     meta[2 * i + 1] = (uint32_t)lb;
@@ -483,6 +484,30 @@ static constexpr double kWindowEvents = PA_WINDOW_EVENTS;
 static constexpr uint32_t kWalkCostIn = PA_WALK_COST_IN, kWalkCostOut = PA_WALK_COST_OUT,
                           kWalkCostHead = PA_WALK_COST_HEAD;
 
+static void swap_bufs(DBuf &a, DBuf &b) {
+  std::swap(a.p, b.p);
+  std::swap(a.bytes, b.bytes);
+}
+
+// Radix sort of (k_in, v_in) pairs by the key's low end_bit bits, stable;
+// the sorted pairs end in (k_out, v_out), the inputs are overwritten.
+static hipError_t sort_pairs64(DBuf &k_in, DBuf &k_out, DBuf &v_in, DBuf &v_out, int64_t n, int end_bit, DBuf &tmp,
+                               hipStream_t s) {
+  uint64_t *ka = k_in.as<uint64_t>(), *kb = k_out.as<uint64_t>();
+  uint32_t *va = v_in.as<uint32_t>(), *vb = v_out.as<uint32_t>();
+  size_t tb = 0;
+  hipError_t e = pa::sort_pairs_u64(&ka, &kb, &va, &vb, n, end_bit, nullptr, &tb, s);
+  if (e == hipSuccess) e = tmp.ensure(tb);
+  if (e == hipSuccess) e = pa::sort_pairs_u64(&ka, &kb, &va, &vb, n, end_bit, tmp.p, &tb, s);
+  if (e != hipSuccess) return e;
+  // the result is in (ka, va): k_in's buffer unless the passes ended in k_out's
+  if (ka == k_in.p) {
+    swap_bufs(k_in, k_out);
+    swap_bufs(v_in, v_out);
+  }
+  return hipSuccess;
+}
+
 // Block ranges of the pass and the lane streams.  Every chunk's events are cut
 // into pieces of about 1 / target of the total cost of the pass (the walk
 // kernel's relative costs of its events and window set-ups; never across a
@@ -494,7 +519,7 @@ static constexpr uint32_t kWalkCostIn = PA_WALK_COST_IN, kWalkCostOut = PA_WALK_
 // When the walk kernel can run but some block's LUT range does not fit in
 // its LDS, the target doubles (smaller blocks span fewer cells), a few times
 // at most.
-static int build_ranges(pa_ctx *c, Events &v) {
+static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t) {
   const Design &d = c->d;
   hipStream_t s = c->stream;
   LoadScratch &ls = c->ls;
@@ -522,8 +547,20 @@ static int build_ranges(pa_ctx *c, Events &v) {
   v.n_windows = W;
   HIPCHK(ls.ws.ensure(sizeof(uint32_t) * ((size_t)W + 1)));
   HIPCHK(v.wlen.ensure(sizeof(uint32_t) * std::max<size_t>(W, 1)));
-  if (W > 0)
+  if (W > 0) {
     HIPCHK(pa::launch_win_starts(E, ls.skey.as<uint64_t>(), ls.winc.as<uint32_t>(), ls.ws.as<uint32_t>(), s));
+    // the input windows' start states, into their first events' keys
+    pa::LayoutFmt f{};
+    f.T = v.T;
+    f.Cc = v.Cc;
+    f.lc = bits_for((uint64_t)v.Cc) - 1;
+    f.pb = v.pb;
+    f.tb = v.tb;
+    f.gb = v.gb;
+    HIPCHK(pa::launch_window_s0(W, ls.ws.as<uint32_t>(), ls.chunk_sorted.as<uint32_t>(), ls.level.as<uint8_t>(),
+                                d.gate_k.as<int32_t>(), d.pin_base.as<int64_t>(), pin_ptr, pin_init, evt_t, f,
+                                ls.skey.as<uint64_t>(), s));
+  }
 
   // ---- every sorted event's cost in the pass (the walk kernel's relative
   // costs of input-pin and output-pin events and of a window's set-up, else
@@ -644,12 +681,7 @@ static int build_ranges(pa_ctx *c, Events &v) {
                                pa::out_code(v.pb), ls.wkey0.as<uint64_t>(), ls.widx.as<uint32_t>(),
                                v.wlen.as<uint32_t>(), s));
     const int end_bit = 32 + (int)bits_for((uint64_t)std::max(nr - 1, 0));
-    size_t tb = 0;
-    HIPCHK(pa::sort_pairs_u64(ls.wkey0.as<uint64_t>(), ls.wkey1.as<uint64_t>(), ls.widx.as<uint32_t>(),
-                              ls.worder.as<uint32_t>(), W, end_bit, nullptr, &tb, s));
-    HIPCHK(ls.tmp.ensure(tb));
-    HIPCHK(pa::sort_pairs_u64(ls.wkey0.as<uint64_t>(), ls.wkey1.as<uint64_t>(), ls.widx.as<uint32_t>(),
-                              ls.worder.as<uint32_t>(), W, end_bit, ls.tmp.p, &tb, s));
+    HIPCHK(sort_pairs64(ls.wkey0, ls.wkey1, ls.widx, ls.worder, W, end_bit, ls.tmp, s));
     // ---- phases: every window's place in its lane's stream, every wave's stream length
     HIPCHK(ls.wlane.ensure(sizeof(uint2) * W));
     HIPCHK(ls.phase.ensure(sizeof(uint2) * pa::phase_plan_entries(W, nr)));
@@ -787,8 +819,18 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   HIPCHK(hipStreamSynchronize(s));
   if (herr & pa::ERR_PIN_PTR) return fail(PA_EDATA, "pa_load_events: pin_ptr decreases");
   if (herr & pa::ERR_INIT) return fail(PA_EDATA, "pa_load_events: pin_init not in {0,1}");
-  if (E > 0) HIPCHK(pa::launch_event_check(E, P, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_max,
-                                           ev_pin.as<uint32_t>(), err.as<uint32_t>(), s));
+  if (E > 0) {
+    // owning pins (a scatter of every pin's index at its first event and a
+    // running maximum), then the checks
+    DBuf &mark = c->ls.idx, &tmp = c->ls.tmp;
+    HIPCHK(mark.ensure(sizeof(uint32_t) * E));
+    size_t tb = 0;
+    HIPCHK(pa::launch_event_check(E, P, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_max, mark.as<uint32_t>(),
+                                  ev_pin.as<uint32_t>(), err.as<uint32_t>(), nullptr, &tb, s));
+    HIPCHK(tmp.ensure(tb));
+    HIPCHK(pa::launch_event_check(E, P, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_max, mark.as<uint32_t>(),
+                                  ev_pin.as<uint32_t>(), err.as<uint32_t>(), tmp.p, &tb, s));
+  }
   HIPCHK(hipMemcpyAsync(&herr, err.p, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
   if (herr & pa::ERR_TIME_RANGE) return fail(PA_EDATA, "pa_load_events: event time outside [0, t_max)");
@@ -894,25 +936,22 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
                                 d.gate_k.as<int32_t>(), f, k0.as<uint64_t>(),
                                 one_key ? nullptr : chunk.as<uint32_t>(), idx.as<uint32_t>(), s));
     const int end_bit = (int)(one_key ? qbits + f.gb + lkb : f.gb + lkb);
-    HIPCHK(pa::sort_pairs_u64(k0.as<uint64_t>(), k1.as<uint64_t>(), idx.as<uint32_t>(), perm.as<uint32_t>(), E,
-                              end_bit, nullptr, &tmp_bytes, s));
-    HIPCHK(tmp.ensure(tmp_bytes));
-    HIPCHK(pa::sort_pairs_u64(k0.as<uint64_t>(), k1.as<uint64_t>(), idx.as<uint32_t>(), perm.as<uint32_t>(), E,
-                              end_bit, tmp.p, &tmp_bytes, s));
+    HIPCHK(sort_pairs64(k0, k1, idx, perm, E, end_bit, tmp, s));  // sorted keys in k1, permutation in perm
     if (!one_key) {
-      // stable second pass by chunk
-      uint32_t *qk = reinterpret_cast<uint32_t *>(k0.p), *qs = reinterpret_cast<uint32_t *>(k1.p);
+      // stable second pass by chunk (the keys in k0's buffer as 32-bit words)
+      uint32_t *qk = reinterpret_cast<uint32_t *>(k0.p), *qs = qk + E;
       HIPCHK(pa::launch_chunk_of(E, perm.as<uint32_t>(), chunk.as<uint32_t>(), qk, s));
+      uint32_t *pa_ = perm.as<uint32_t>(), *pb_ = idx.as<uint32_t>();
       tmp_bytes = 0;
-      HIPCHK(pa::sort_pairs_u32(qk, qs, perm.as<uint32_t>(), idx.as<uint32_t>(), E, (int)qbits, nullptr, &tmp_bytes, s));
+      HIPCHK(pa::sort_pairs_u32(&qk, &qs, &pa_, &pb_, E, (int)qbits, nullptr, &tmp_bytes, s));
       HIPCHK(tmp.ensure(tmp_bytes));
-      HIPCHK(pa::sort_pairs_u32(qk, qs, perm.as<uint32_t>(), idx.as<uint32_t>(), E, (int)qbits, tmp.p, &tmp_bytes, s));
-      std::swap(perm.p, idx.p);
-      std::swap(perm.bytes, idx.bytes);
+      HIPCHK(pa::sort_pairs_u32(&qk, &qs, &pa_, &pb_, E, (int)qbits, tmp.p, &tmp_bytes, s));
+      if (pa_ != perm.p) swap_bufs(perm, idx);  // the permutation ended in idx's buffer
     }
     // ---- packed keys, window heads and start states
     HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
-    HIPCHK(pa::launch_layout(E, perm.as<uint32_t>(), evt_t, evt_slew, evt_val, ev_pin.as<uint32_t>(),
+    HIPCHK(pa::launch_layout(E, perm.as<uint32_t>(), one_key ? k1.as<uint64_t>() : nullptr, evt_t, evt_slew, evt_val,
+                             ev_pin.as<uint32_t>(),
                              d.pin_gate.as<int32_t>(), d.pin_local.as<uint8_t>(), d.gate_k.as<int32_t>(),
                              level.as<uint8_t>(), d.pin_base.as<int64_t>(), pin_ptr, pin_init, f, skey.as<uint64_t>(),
                              sslew.as<float>(), sorig.as<uint32_t>(), chunk_sorted.as<uint32_t>(), err.as<uint32_t>(),
@@ -923,7 +962,7 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   v.h_chunk_base.resize(Q + 1);
   HIPCHK(hipMemcpyAsync(v.h_chunk_base.data(), cbase.p, sizeof(uint32_t) * (Q + 1), hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
-  int rc = build_ranges(c, v);
+  int rc = build_ranges(c, v, pin_ptr, pin_init, evt_t);
   if (rc != PA_OK) return rc;
   c->ev_spare = std::move(c->ev);
   c->ev = std::move(v);

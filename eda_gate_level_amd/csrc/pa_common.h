@@ -9,6 +9,8 @@
 
 namespace pa {
 
+constexpr int kMaxInputs = 8;  // inputs of a cell (pa_load_design rejects more)
+
 // ---------------------------------------------------------------------------
 // Event layout.  Time is cut into chunks of Cc clock cycles (a power of two);
 // inside a chunk every gate's cycles are cut into 2^s equal windows, s chosen

@@ -47,7 +47,8 @@ hipError_t launch_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pi
                             hipStream_t s);
 hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init,
                               const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_max,
-                              uint32_t *ev_pin, uint32_t *err, hipStream_t s);
+                              uint32_t *mark, uint32_t *ev_pin, uint32_t *err, void *tmp, size_t *tmp_bytes,
+                              hipStream_t s);
 // per-gate window level: fixed_level >= 0 gives every gate that level, else density-aware
 hipError_t launch_gate_levels(int64_t G, const int64_t *pin_base, const int32_t *gate_k, const int64_t *pin_ptr,
                               int64_t C, int32_t Cc, int32_t lc, double target, int32_t fixed_level,
@@ -58,12 +59,17 @@ hipError_t launch_sort_keys(int64_t E, const int64_t *evt_t, const uint32_t *ev_
                             uint32_t *chunk, uint32_t *idx, hipStream_t s);
 hipError_t launch_chunk_of(int64_t E, const uint32_t *perm, const uint32_t *chunk, uint32_t *chunk_sorted,
                            hipStream_t s);
-hipError_t launch_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, const float *evt_slew,
-                         const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
-                         const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
-                         const int64_t *pin_base, const int64_t *pin_ptr, const uint8_t *pin_init, const LayoutFmt &f,
-                         uint64_t *key_out, float *slew_out, uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err,
-                         hipStream_t s);
+hipError_t launch_layout(int64_t E, const uint32_t *perm, const uint64_t *skey, const int64_t *evt_t,
+                         const float *evt_slew, const uint8_t *evt_val, const uint32_t *ev_pin,
+                         const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
+                         const uint8_t *level, const int64_t *pin_base, const int64_t *pin_ptr,
+                         const uint8_t *pin_init, const LayoutFmt &f, uint64_t *key_out, float *slew_out,
+                         uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err, hipStream_t s);
+// the start state of every input window into its first event's key (after the windows are known)
+hipError_t launch_window_s0(uint32_t W, const uint32_t *ws, const uint32_t *chunk_sorted, const uint8_t *level,
+                            const int32_t *gate_k, const int64_t *pin_base, const int64_t *pin_ptr,
+                            const uint8_t *pin_init, const int64_t *evt_t, const LayoutFmt &f, uint64_t *skey,
+                            hipStream_t s);
 hipError_t launch_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted, uint32_t *cb, hipStream_t s);
 // lane streams of the pass (see pa_load.hip): head flags; window starts
 // (ws[W] = E); every block's first window; window sort keys (block, kind,
@@ -105,9 +111,9 @@ hipError_t scan_inclusive_u64(const uint64_t *in, uint64_t *out, int64_t n, void
                               hipStream_t s);
 hipError_t scan_inclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
                               hipStream_t s);
-hipError_t sort_pairs_u64(const uint64_t *kin, uint64_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,
-                          int end_bit, void *tmp, size_t *tmp_bytes, hipStream_t s);
-hipError_t sort_pairs_u32(const uint32_t *kin, uint32_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,
-                          int end_bit, void *tmp, size_t *tmp_bytes, hipStream_t s);
+hipError_t sort_pairs_u64(uint64_t **k0, uint64_t **k1, uint32_t **v0, uint32_t **v1, int64_t n, int end_bit,
+                          void *tmp, size_t *tmp_bytes, hipStream_t s);
+hipError_t sort_pairs_u32(uint32_t **k0, uint32_t **k1, uint32_t **v0, uint32_t **v1, int64_t n, int end_bit,
+                          void *tmp, size_t *tmp_bytes, hipStream_t s);
 
 }  // namespace pa

@@ -20,7 +20,11 @@
 // counter never crosses one.
 #include <hip/hip_runtime.h>
 
-#include <hipcub/hipcub.hpp>
+#include <cstring>
+#include <utility>
+
+#include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_scan.hpp>
 
 #include "pa_common.h"
 #include "pa_load.h"
@@ -83,17 +87,21 @@ __global__ void k_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pi
   }
 }
 
-// owning pin of every event (last p with pin_ptr[p] <= e) and validation
-__global__ void k_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init,
-                              const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_max,
-                              uint32_t *ev_pin, uint32_t *err) {
+// Owning pin of every event, the last p with pin_ptr[p] <= e: every pin with
+// events writes its index at its first event (those positions are distinct),
+// the rest of the array holding 0, and a running maximum over the events
+// spreads each index over its pin's range.
+__global__ void k_pin_starts(int64_t P, const int64_t *pin_ptr, uint32_t *mark) {
+  for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x)
+    if (pin_ptr[p] < pin_ptr[p + 1]) mark[pin_ptr[p]] = (uint32_t)p;
+}
+
+// validation of every event against its pin
+__global__ void k_event_check(int64_t E, const int64_t *pin_ptr, const uint8_t *pin_init, const int64_t *evt_t,
+                              const uint8_t *evt_val, const float *evt_slew, int64_t t_max, const uint32_t *ev_pin,
+                              uint32_t *err) {
   for (int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; e < E; e += (int64_t)gridDim.x * blockDim.x) {
-    int64_t lo = 0, hi = P;  // pin_ptr[lo] <= e < pin_ptr[hi]
-    while (hi - lo > 1) {
-      const int64_t mid = (lo + hi) >> 1;
-      if (pin_ptr[mid] <= e) lo = mid; else hi = mid;
-    }
-    ev_pin[e] = (uint32_t)lo;
+    const uint32_t lo = ev_pin[e];
     const int64_t idx = e - pin_ptr[lo];
     const int64_t t = evt_t[e];
     uint32_t bad = 0;
@@ -184,46 +192,101 @@ __global__ void k_chunk_of(int64_t E, const uint32_t *perm, const uint32_t *chun
     chunk_sorted[x] = chunk[perm[x]];
 }
 
+// an event's fields from its sort key (chunk, gate, kind, cycle, time, pin code)
+__device__ __forceinline__ EvPos key_pos(uint64_t K, const LayoutFmt &f) {
+  const uint32_t lkb = f.lc + f.pb + f.tb + 1;
+  EvPos r;
+  r.q = K >> (f.gb + lkb);
+  r.g = (uint32_t)(K >> lkb) & ((1u << f.gb) - 1u);
+  const uint64_t lk = K & ((uint64_t(1) << (lkb - 1)) - 1u);
+  r.code = (uint32_t)lk & ((1u << f.pb) - 1u);
+  r.tic = (uint32_t)(lk >> f.pb) & (uint32_t)((uint64_t(1) << f.tb) - 1u);
+  r.cyc = (uint32_t)(lk >> (f.pb + f.tb));
+  return r;
+}
+
 // Packed keys of the sorted events, window heads and their start states.
-__global__ void k_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, const float *evt_slew,
-                         const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
-                         const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
-                         const int64_t *pin_base, const int64_t *pin_ptr, const uint8_t *pin_init, LayoutFmt f,
-                         uint64_t *key_out, float *slew_out, uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err) {
+// With skey (the sorted one-word keys) an event's fields and its
+// predecessor's come from the keys; without, from the caller's arrays.
+__global__ void k_layout(int64_t E, const uint32_t *perm, const uint64_t *skey, const int64_t *evt_t,
+                         const float *evt_slew, const uint8_t *evt_val, const uint32_t *ev_pin,
+                         const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
+                         const uint8_t *level, const int64_t *pin_base, const int64_t *pin_ptr,
+                         const uint8_t *pin_init, LayoutFmt f, uint64_t *key_out, float *slew_out, uint32_t *orig_out,
+                         uint32_t *chunk_out, uint32_t *err) {
   for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = perm[x];
-    const EvPos p = ev_pos(e, evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
+    const EvPos p = skey ? key_pos(skey[x], f) : ev_pos(e, evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
     const uint32_t sl = level[p.g];
     const uint32_t w = p.cyc >> (f.lc - sl);
     const uint32_t outc = out_code(f.pb);
     bool head = true;
     if (x > 0) {
-      const EvPos pp = ev_pos(perm[x - 1], evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
+      const EvPos pp = skey ? key_pos(skey[x - 1], f) : ev_pos(perm[x - 1], evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
       head = !(pp.q == p.q && pp.g == p.g && (pp.code == outc) == (p.code == outc) && (pp.cyc >> (f.lc - sl)) == w);
     }
-    uint64_t S0 = 0;
-    if (head && p.code != outc) {
-      // input state at the window start: pin value = init XOR parity of its earlier events
-      const int64_t tw = ((int64_t)p.q * f.Cc + ((int64_t)w << (f.lc - sl))) * f.T;
-      const int64_t pb = pin_base[p.g];
-      const int32_t k = gate_k[p.g];
-      for (int32_t j = 0; j < k; ++j) {
-        int64_t lo = pin_ptr[pb + j], hi = pin_ptr[pb + j + 1];
-        const int64_t base = lo;
-        while (lo < hi) {  // first event at or after tw
-          const int64_t mid = (lo + hi) >> 1;
-          if (evt_t[mid] < tw) lo = mid + 1; else hi = mid;
-        }
-        S0 |= (uint64_t)((pin_init[pb + j] ^ (uint8_t)((lo - base) & 1)) & 1u) << j;
-      }
-    }
+    // an input window's start state is added by k_window_s0, once the windows are known
     const uint64_t lk = lk_of(p, f);
-    key_out[x] = ((lk >> 32) << (kKeyGateShift + f.gb)) | ((uint64_t)p.g << kKeyGateShift) |
+    const uint32_t hs = kKeyGateShift + f.gb;  // the cycle's high bits go above the gate id (none at hs = 64)
+    key_out[x] = (hs < 64 ? (lk >> 32) << hs : 0ull) | ((uint64_t)p.g << kKeyGateShift) |
                  ((uint64_t)head << kKeyHeadShift) | ((uint64_t)(evt_val[e] & 1u) << kKeyValShift) |
-                 (S0 << kKeyS0Shift) | (lk & 0xFFFFFFFFull);
+                 (lk & 0xFFFFFFFFull);
     slew_out[x] = evt_slew[e];
     orig_out[x] = (uint32_t)e;
     chunk_out[x] = (uint32_t)p.q;
+  }
+}
+
+// The input state at the start of every input window, into its first
+// event's key: a pin's value there is its initial value XOR the parity of
+// its events before the window start (a binary search in the pin's events).
+// One thread per window, after the windows' first events are known.
+__global__ void k_window_s0(uint32_t W, const uint32_t *ws, const uint32_t *chunk_sorted, const uint8_t *level,
+                            const int32_t *gate_k, const int64_t *pin_base, const int64_t *pin_ptr,
+                            const uint8_t *pin_init, const int64_t *evt_t, LayoutFmt f, uint64_t *skey) {
+  const uint32_t outc = out_code(f.pb);
+  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < W; w += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t x = ws[w];
+    const uint64_t K = skey[x];
+    const uint32_t g = (uint32_t)(K >> kKeyGateShift) & ((1u << f.gb) - 1u);
+    // the cycle's high bits above the gate id (none when the gate id fills the word)
+    const uint32_t hs = kKeyGateShift + f.gb;
+    const uint64_t lk = (K & 0xFFFFFFFFull) | (hs < 64 ? (K >> hs) << 32 : 0ull);
+    if (((uint32_t)lk & outc) == outc) continue;  // an output window needs no state
+    const uint32_t cyc = (uint32_t)(lk >> (f.pb + f.tb));
+    const uint32_t sh = f.lc - level[g];
+    const int64_t tw = ((int64_t)chunk_sorted[x] * f.Cc + (int64_t)((cyc >> sh) << sh)) * f.T;
+    const int64_t pb = pin_base[g];
+    const int32_t k = gate_k[g];
+    // the pins' binary searches (first event at or after tw) step together,
+    // so their loads go out side by side
+    int64_t lo[kMaxInputs], hi[kMaxInputs], base[kMaxInputs];
+#pragma unroll
+    for (int j = 0; j < kMaxInputs; ++j) {
+      base[j] = j < k ? pin_ptr[pb + j] : 0;
+      hi[j] = j < k ? pin_ptr[pb + j + 1] : 0;
+      lo[j] = base[j];
+    }
+    bool more = true;
+    while (more) {
+      more = false;
+      int64_t t[kMaxInputs];
+#pragma unroll
+      for (int j = 0; j < kMaxInputs; ++j) t[j] = lo[j] < hi[j] ? evt_t[(lo[j] + hi[j]) >> 1] : 0;
+#pragma unroll
+      for (int j = 0; j < kMaxInputs; ++j) {
+        if (lo[j] < hi[j]) {
+          const int64_t mid = (lo[j] + hi[j]) >> 1;
+          if (t[j] < tw) lo[j] = mid + 1; else hi[j] = mid;
+          more |= lo[j] < hi[j];
+        }
+      }
+    }
+    uint64_t S0 = 0;
+#pragma unroll
+    for (int j = 0; j < kMaxInputs; ++j)
+      if (j < k) S0 |= (uint64_t)((pin_init[pb + j] ^ (uint8_t)((lo[j] - base[j]) & 1)) & 1u) << j;
+    skey[x] = K | (S0 << kKeyS0Shift);
   }
 }
 
@@ -253,7 +316,7 @@ __global__ void k_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted,
 
 constexpr int kLaneNT = 1024;  // lanes of a block of the pass
 constexpr int kLaneNW = kLaneNT / 64;
-constexpr int kPlanNT = 256;   // threads of a block of the phase plan
+constexpr int kPlanNT = 1024;  // threads of a block of the phase plan
 
 __global__ void k_head_flags(int64_t E, const uint64_t *skey, uint32_t *flag) {
   for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x)
@@ -305,62 +368,103 @@ __constant__ uint32_t kWaveSlow[4] = {72u, 92u, 110u, 126u};
 // One block per block of the pass.  Its windows come in worder (input
 // windows longest first, then output windows longest first; sorted keys in
 // wkey); phase i of a kind is that kind's windows 64 i .. 64 i + 63.  One
-// thread deals the phases, costliest first, to the waves, each to the wave
+// wave deals the phases, costliest first, to the waves, each to the wave
 // that would finish it first (its cost so far plus the phase's, times its
 // relative walk time; a phase costs its slots times w_in or w_out, the
 // relative cost of a slot of its kind in the pass); ph gets the phase's
 // wave and first slot, in this block's part [floor(w0 / 64) + 2 b, ...) of
-// the array, which holds at least its phases.  Then every window gets its
-// place: wlane[w] = (global wave << 6 | lane, first slot).  wave_len = the
-// slots of every wave's stream.
+// the array, which holds at least its phases.  Before that all threads count
+// the input windows and read the phases' lengths into LDS.  Then every window
+// gets its place: wlane[w] = (global wave << 6 | lane, first slot).  wave_len
+// = the slots of every wave's stream.
+
+constexpr int kPlanLen = 4096;  // phases whose lengths the phase plan keeps in LDS
 
 __global__ __launch_bounds__(kPlanNT) void k_phase_plan(const uint32_t *bwin, const uint32_t *worder,
                                                         const uint64_t *wkey, const uint32_t *wlen, uint32_t hp,
                                                         uint32_t w_in, uint32_t w_out, uint2 *ph, uint2 *wlane,
                                                         uint32_t *wave_len) {
-  __shared__ uint32_t s_nin;
+  __shared__ uint32_t s_cnt[kPlanNT / 64];
+  __shared__ uint32_t s_len[kPlanLen];
   const int b = blockIdx.x, u = threadIdx.x;
   const uint32_t w0 = bwin[b], nb = bwin[b + 1] - w0;
   uint2 *php = ph + (w0 >> 6) + 2u * (uint32_t)b;
-  if (u == 0) {
-    // input windows: those before the first key with the kind bit
-    uint32_t lo = 0, hi = nb;
-    while (lo < hi) {
-      const uint32_t mid = (lo + hi) >> 1;
-      if ((wkey[w0 + mid] >> 31) & 1u) hi = mid; else lo = mid + 1;
+  // input windows: the keys without the kind bit (they come first), counted by all threads
+  uint32_t cnt = 0;
+  for (uint32_t r0 = 0; r0 < nb; r0 += 4 * kPlanNT) {
+    uint64_t kk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t r = r0 + t * kPlanNT + u;
+      kk[t] = r < nb ? wkey[w0 + r] : (1ull << 31);
     }
-    const uint32_t nin = lo, nout = nb - nin;
-    const uint32_t pin_ = (nin + 63) >> 6, pout = (nout + 63) >> 6;
-    auto plen = [&](uint32_t first) { return hp + ((wlen[worder[w0 + first]] + 1u) & ~1u); };
-    uint32_t load[kLaneNW];
-    uint64_t cost[kLaneNW];
-    for (int v = 0; v < kLaneNW; ++v) load[v] = 0, cost[v] = 0;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cnt += ((kk[t] >> 31) & 1u) ? 0u : 1u;
+  }
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+  if ((u & 63) == 0) s_cnt[u >> 6] = cnt;
+  __syncthreads();
+  uint32_t nin = 0;
+  for (int i = 0; i < kPlanNT / 64; ++i) nin += s_cnt[i];
+  const uint32_t nout = nb - nin;
+  const uint32_t pin_ = (nin + 63) >> 6, pout = (nout + 63) >> 6, np = pin_ + pout;
+  // a phase's slots: the header pair and its longest (first) window rounded up to even
+  auto plen = [&](uint32_t i) {
+    const uint32_t first = i < pin_ ? i * 64 : nin + (i - pin_) * 64;
+    return hp + ((wlen[worder[w0 + first]] + 1u) & ~1u);
+  };
+  for (uint32_t i = u; i < np && i < (uint32_t)kPlanLen; i += kPlanNT) s_len[i] = plen(i);
+  __syncthreads();
+  if (u < 64) {
+    // wave 0 deals: lane v < 16 holds wave v's slots and cost; each phase goes
+    // to the lane with the least (cost + the phase's) x slowness, the lowest
+    // such lane on ties, found by a butterfly over the 16 lanes
+    const int lane = u;
+    uint32_t load = 0;
+    uint64_t cost = 0;
+    const uint64_t slow = kWaveSlow[(lane & (kLaneNW - 1)) >> 2];
     uint32_t i = 0, o = 0;
     while (i < pin_ || o < pout) {
-      const uint32_t li = i < pin_ ? plen(i * 64) : 0u, lo2 = o < pout ? plen(nin + o * 64) : 0u;
+      const uint32_t xi = i, xo = pin_ + o;
+      const uint32_t li = i < pin_ ? (xi < (uint32_t)kPlanLen ? s_len[xi] : plen(xi)) : 0u;
+      const uint32_t lo2 = o < pout ? (xo < (uint32_t)kPlanLen ? s_len[xo] : plen(xo)) : 0u;
       const uint64_t ci = (uint64_t)li * w_in, co = (uint64_t)lo2 * w_out;
       const bool take_in = i < pin_ && (o >= pout || ci >= co);
       const uint64_t cc = take_in ? ci : co;
-      int v = 0;
-      uint64_t best = (cost[0] + cc) * kWaveSlow[0];
-      for (int x = 1; x < kLaneNW; ++x) {
-        const uint64_t f = (cost[x] + cc) * kWaveSlow[x >> 2];
-        if (f < best) best = f, v = x;
+      uint64_t f = lane < kLaneNW ? (cost + cc) * slow : ~0ull;
+      uint32_t v = (uint32_t)lane;
+      for (int off = kLaneNW / 2; off > 0; off >>= 1) {
+        const uint64_t f2 = __shfl_xor(f, off, kLaneNW);
+        const uint32_t v2 = __shfl_xor(v, off, kLaneNW);
+        if (f2 < f || (f2 == f && v2 < v)) f = f2, v = v2;
       }
-      php[take_in ? i : pin_ + o] = make_uint2((uint32_t)v, load[v]);
-      load[v] += take_in ? li : lo2;
-      cost[v] += take_in ? ci : co;
+      const uint32_t lv = __shfl(load, (int)v);
+      if (lane == 0) php[take_in ? i : pin_ + o] = make_uint2(v, lv);
+      if ((uint32_t)lane == v) {
+        load += take_in ? li : lo2;
+        cost += cc;
+      }
       if (take_in) ++i; else ++o;
     }
-    for (int v = 0; v < kLaneNW; ++v) wave_len[(size_t)b * kLaneNW + v] = load[v];
-    s_nin = nin;
+    if (lane < kLaneNW) wave_len[(size_t)b * kLaneNW + lane] = load;
   }
   __syncthreads();
-  const uint32_t nin = s_nin, pin_ = (nin + 63) >> 6;
-  for (uint32_t r = u; r < nb; r += kPlanNT) {
-    const uint32_t i = r < nin ? r : r - nin;
-    const uint2 p = php[(r < nin ? 0u : pin_) + (i >> 6)];
-    wlane[worder[w0 + r]] = make_uint2(((uint32_t)b * kLaneNW + p.x) << 6 | (i & 63u), p.y + hp);
+  for (uint32_t r0 = 0; r0 < nb; r0 += 4 * kPlanNT) {
+    uint2 p[4];
+    uint32_t wo[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t r = min(r0 + t * kPlanNT + u, nb - 1);
+      const uint32_t i = r < nin ? r : r - nin;
+      p[t] = php[(r < nin ? 0u : pin_) + (i >> 6)];
+      wo[t] = worder[w0 + r];
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t r = r0 + t * kPlanNT + u;
+      const uint32_t i = r < nin ? r : r - nin;
+      if (r < nb) wlane[wo[t]] = make_uint2(((uint32_t)b * kLaneNW + p[t].x) << 6 | (i & 63u), p[t].y + hp);
+    }
   }
 }
 
@@ -381,7 +485,8 @@ __global__ void k_compact(int64_t n, const uint64_t *key, const float *slew, uin
       const uint32_t lk = (uint32_t)K, hw = (uint32_t)(K >> 32);
       const uint32_t code = lk & outc;
       const uint32_t tic = (lk >> pb) & tmask;
-      const uint32_t cyc = (uint32_t)((((uint64_t)(hw >> ysh)) << 32 | lk) >> cs);
+      const uint32_t hi = ysh < 32 ? hw >> ysh : 0u;  // the cycle's bits above the gate id
+      const uint32_t cyc = (uint32_t)((((uint64_t)hi) << 32 | lk) >> cs);
       const bool out = code == outc;
       kw = (cyc << (tbc + ck)) | (tic << ck) | (out ? 0u : (code >> 1));
       sw = __float_as_uint(slew[y]) | ((out ? ((hw >> 8) & 1u) : (code & 1u)) << 31);
@@ -567,9 +672,17 @@ hipError_t launch_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pi
 
 hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init,
                               const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_max,
-                              uint32_t *ev_pin, uint32_t *err, hipStream_t s) {
-  hipLaunchKernelGGL(k_event_check, dim3(grid_for(E)), dim3(kLT), 0, s, E, P, pin_ptr, pin_init, evt_t, evt_val,
-                     evt_slew, t_max, ev_pin, err);
+                              uint32_t *mark, uint32_t *ev_pin, uint32_t *err, void *tmp, size_t *tmp_bytes,
+                              hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  if (!tmp) return rocprim::inclusive_scan(nullptr, *tmp_bytes, mark, ev_pin, (size_t)E, rocprim::maximum<uint32_t>(), s);
+  hipError_t e = hipMemsetAsync(mark, 0, sizeof(uint32_t) * E, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_pin_starts, dim3(grid_for(P)), dim3(kLT), 0, s, P, pin_ptr, mark);
+  e = rocprim::inclusive_scan(tmp, *tmp_bytes, mark, ev_pin, (size_t)E, rocprim::maximum<uint32_t>(), s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_event_check, dim3(grid_for(E)), dim3(kLT), 0, s, E, pin_ptr, pin_init, evt_t, evt_val, evt_slew,
+                     t_max, ev_pin, err);
   return hipGetLastError();
 }
 
@@ -595,15 +708,25 @@ hipError_t launch_chunk_of(int64_t E, const uint32_t *perm, const uint32_t *chun
   return hipGetLastError();
 }
 
-hipError_t launch_layout(int64_t E, const uint32_t *perm, const int64_t *evt_t, const float *evt_slew,
-                         const uint8_t *evt_val, const uint32_t *ev_pin, const int32_t *pin_gate,
-                         const uint8_t *pin_local, const int32_t *gate_k, const uint8_t *level,
-                         const int64_t *pin_base, const int64_t *pin_ptr, const uint8_t *pin_init, const LayoutFmt &f,
-                         uint64_t *key_out, float *slew_out, uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(k_layout, dim3(grid_for(E)), dim3(kLT), 0, s, E, perm, evt_t, evt_slew, evt_val, ev_pin, pin_gate,
-                     pin_local, gate_k, level, pin_base, pin_ptr, pin_init, f, key_out, slew_out, orig_out, chunk_out,
-                     err);
+hipError_t launch_layout(int64_t E, const uint32_t *perm, const uint64_t *skey, const int64_t *evt_t,
+                         const float *evt_slew, const uint8_t *evt_val, const uint32_t *ev_pin,
+                         const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
+                         const uint8_t *level, const int64_t *pin_base, const int64_t *pin_ptr,
+                         const uint8_t *pin_init, const LayoutFmt &f, uint64_t *key_out, float *slew_out,
+                         uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err, hipStream_t s) {
+  hipLaunchKernelGGL(k_layout, dim3(grid_for(E)), dim3(kLT), 0, s, E, perm, skey, evt_t, evt_slew, evt_val, ev_pin,
+                     pin_gate, pin_local, gate_k, level, pin_base, pin_ptr, pin_init, f, key_out, slew_out, orig_out,
+                     chunk_out, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_s0(uint32_t W, const uint32_t *ws, const uint32_t *chunk_sorted, const uint8_t *level,
+                            const int32_t *gate_k, const int64_t *pin_base, const int64_t *pin_ptr,
+                            const uint8_t *pin_init, const int64_t *evt_t, const LayoutFmt &f, uint64_t *skey,
+                            hipStream_t s) {
+  if (W == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_window_s0, dim3(grid_for(W)), dim3(kLT), 0, s, W, ws, chunk_sorted, level, gate_k, pin_base,
+                     pin_ptr, pin_init, evt_t, f, skey);
   return hipGetLastError();
 }
 
@@ -640,20 +763,20 @@ hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *w
                      ph, wlane, wave_len);
   return hipGetLastError();
 }
-hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,
-                          uint32_t tb, uint32_t gb, uint32_t tbc, uint32_t ck, uint32_t *ckey, uint32_t *cslew,
-                          hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_compact, dim3(grid_for(n)), dim3(kLT), 0, s, n, key, slew, pad_key, pb, tb, gb, tbc, ck, ckey,
-                     cslew);
-  return hipGetLastError();
-}
 hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
                           const uint4 *gate_rec, uint32_t gb, uint32_t outc, uint32_t hdr, uint32_t out_bit,
                           uint32_t *ckey, uint32_t *cslew, hipStream_t s) {
   if (W == 0) return hipSuccess;
   hipLaunchKernelGGL(k_headers, dim3(grid_for(W)), dim3(kLT), 0, s, W, wlane, wdesc, ws, skey, gate_rec, gb, outc, hdr,
                      out_bit, ckey, cslew);
+  return hipGetLastError();
+}
+hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,
+                          uint32_t tb, uint32_t gb, uint32_t tbc, uint32_t ck, uint32_t *ckey, uint32_t *cslew,
+                          hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_compact, dim3(grid_for(n)), dim3(kLT), 0, s, n, key, slew, pad_key, pb, tb, gb, tbc, ck, ckey,
+                     cslew);
   return hipGetLastError();
 }
 hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
@@ -698,22 +821,39 @@ hipError_t launch_gather_prefix(int32_t n, const uint32_t *at, const uint64_t *p
 }
 hipError_t scan_inclusive_u64(const uint64_t *in, uint64_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
                               hipStream_t s) {
-  return hipcub::DeviceScan::InclusiveSum(tmp, *tmp_bytes, in, out, (int)n, s);
+  return rocprim::inclusive_scan(tmp, *tmp_bytes, in, out, (size_t)n, rocprim::plus<uint64_t>(), s);
 }
 
 hipError_t scan_inclusive_u32(const uint32_t *in, uint32_t *out, int64_t n, void *tmp, size_t *tmp_bytes,
                               hipStream_t s) {
-  return hipcub::DeviceScan::InclusiveSum(tmp, *tmp_bytes, in, out, (int)n, s);
+  return rocprim::inclusive_scan(tmp, *tmp_bytes, in, out, (size_t)n, rocprim::plus<uint32_t>(), s);
 }
 
-hipError_t sort_pairs_u64(const uint64_t *kin, uint64_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,
-                          int end_bit, void *tmp, size_t *tmp_bytes, hipStream_t s) {
-  return hipcub::DeviceRadixSort::SortPairs(tmp, *tmp_bytes, kin, kout, vin, vout, (int)n, 0, end_bit, s);
+// radix sorts that ping-pong between the two buffers given (no copy back):
+// the sorted keys and values end in (*k0, *v0) or (*k1, *v1), and the
+// pointers are swapped so that *k0 and *v0 hold them
+hipError_t sort_pairs_u64(uint64_t **k0, uint64_t **k1, uint32_t **v0, uint32_t **v1, int64_t n, int end_bit,
+                          void *tmp, size_t *tmp_bytes, hipStream_t s) {
+  rocprim::double_buffer<uint64_t> kb(*k0, *k1);
+  rocprim::double_buffer<uint32_t> vb(*v0, *v1);
+  const hipError_t e = rocprim::radix_sort_pairs(tmp, *tmp_bytes, kb, vb, (size_t)n, 0u, (unsigned)end_bit, s);
+  if (tmp && e == hipSuccess && kb.current() != *k0) {
+    std::swap(*k0, *k1);
+    std::swap(*v0, *v1);
+  }
+  return e;
 }
 
-hipError_t sort_pairs_u32(const uint32_t *kin, uint32_t *kout, const uint32_t *vin, uint32_t *vout, int64_t n,
-                          int end_bit, void *tmp, size_t *tmp_bytes, hipStream_t s) {
-  return hipcub::DeviceRadixSort::SortPairs(tmp, *tmp_bytes, kin, kout, vin, vout, (int)n, 0, end_bit, s);
+hipError_t sort_pairs_u32(uint32_t **k0, uint32_t **k1, uint32_t **v0, uint32_t **v1, int64_t n, int end_bit,
+                          void *tmp, size_t *tmp_bytes, hipStream_t s) {
+  rocprim::double_buffer<uint32_t> kb(*k0, *k1);
+  rocprim::double_buffer<uint32_t> vb(*v0, *v1);
+  const hipError_t e = rocprim::radix_sort_pairs(tmp, *tmp_bytes, kb, vb, (size_t)n, 0u, (unsigned)end_bit, s);
+  if (tmp && e == hipSuccess && kb.current() != *k0) {
+    std::swap(*k0, *k1);
+    std::swap(*v0, *v1);
+  }
+  return e;
 }
 
 }  // namespace pa
