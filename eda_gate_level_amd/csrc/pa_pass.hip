@@ -98,6 +98,21 @@ __device__ __forceinline__ double wave_incl_scan(double v) {
   return v;
 }
 
+// Inclusive sum within every row of 16 lanes, in a fixed order.
+__device__ __forceinline__ double row_incl_scan(double v) {
+  v += dpp_f64<0x111, 0xf>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xf>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xf>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xf>(v);  // row_shr:8
+  return v;
+}
+
+// lane l's double, l wave-uniform
+__device__ __forceinline__ double lane_f64(double v, int l) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
+                          __builtin_amdgcn_readlane(__double2loint(v), l));
+}
+
 struct CellLds {
   double2 *axw, *caxw;
   float *thr;
@@ -1035,15 +1050,16 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     __syncthreads();
     double *ow = a.blk_wave + (size_t)b * Cc;
     unsigned long long *oc = a.blk_cnt + (size_t)b * Cc;
+    // the waves' totals of row u sit in lanes 16 u .. 16 u + 15 (one row of
+    // lanes per row of bins): a scan within the rows of lanes gives every
+    // wave the changes of the waves before it and every row's total
+    static_assert(kNW == 16 && PER <= 4, "one row of 16 lanes per row of bins");
+    const double tw = row_incl_scan(lane < PER * kNW ? s_scan[lane] : 0.0);
     double before = 0.0;  // changes of all earlier rows of bins
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      double row = 0.0, wb = 0.0;
-      for (int w = 0; w < kNW; ++w) {
-        const double v = s_scan[u * kNW + w];
-        if (w < wid) wb += v;
-        row += v;
-      }
+      const double row = lane_f64(tw, u * kNW + kNW - 1);
+      const double wb = wid > 0 ? lane_f64(tw, u * kNW + wid - 1) : 0.0;
       const int c = u * kNT + tid;
       if (c < Cc) {
         double v = 0.0;
