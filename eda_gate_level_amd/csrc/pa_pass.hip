@@ -697,15 +697,18 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   const float vth = a.cell_thr[min(tid, nth - 1)];
   const double vlk = a.leak[min(tid, nlk - 1)];
   const u32x2 vme = me[min(tid, nme - 1)];
-  // the ring's first groups, issued after the tables so that waiting for the
-  // tables does not wait for them (loads complete in order)
+  // the ring's first group, issued after the tables so that waiting for the
+  // tables does not wait for it (loads complete in order); the next groups
+  // after the set-up barrier: every wave of the chip asks for its first
+  // stream bytes at once, and asking for one group instead of LD halves that
+  // burst, so the first group arrives sooner
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int i = 0; i < GP; ++i) {
       kr[r][i] = u32x2{~0u, ~0u};
       sr[r][i] = u32x2{0x3F800000u, 0x3F800000u};
-      if (r < LD && npair > 0) load_pair(min(r * GP + i, npair - 1), kr[r][i], sr[r][i]);
+      if (r == 0 && npair > 0) load_pair(min(i, npair - 1), kr[r][i], sr[r][i]);
     }
   for (int c = tid; c <= Cc; c += kNT) {
     L.bins[c].w = 0.0;
@@ -728,6 +731,11 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   for (int j = tid + kNT; j < nme; j += kNT) L.meta[j] = me[j];
   for (int j = KU * kNT + tid; j < n2; j += kNT) ldst[j] = lsrc[j];
   __syncthreads();
+#pragma unroll
+  for (int r = 1; r < LD; ++r)
+#pragma unroll
+    for (int i = 0; i < GP; ++i)
+      if (npair > 0) load_pair(min(r * GP + i, npair - 1), kr[r][i], sr[r][i]);
 
   // the leakage changes' times in their bins are not summed here: the bins
   // hold the energies minus them, so the flush gets their sum from the bins
