@@ -802,23 +802,14 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   HIPCHK(hipSetDevice(c->device));
   hipStream_t s = c->stream;
   const int64_t P = n_pins, E = n_events, G = d.G;
-  int64_t ends[2] = {0, 0};
-  HIPCHK(hipMemcpyAsync(&ends[0], pin_ptr, sizeof(int64_t), hipMemcpyDeviceToHost, s));
-  HIPCHK(hipMemcpyAsync(&ends[1], pin_ptr + P, sizeof(int64_t), hipMemcpyDeviceToHost, s));
-  HIPCHK(hipStreamSynchronize(s));
-  if (ends[0] != 0 || ends[1] != E) return fail(PA_EDATA, "pa_load_events: pin_ptr[0] must be 0 and pin_ptr[P] = n_events");
-
-  // ---- validation
+  // ---- validation: the pin checks and the event checks run back to back
+  // (the event kernels stay in bounds whatever pin_ptr holds) and are read
+  // back once, reported in order
   DBuf &err = c->ls.err, &ev_pin = c->ls.ev_pin;
   HIPCHK(err.ensure(sizeof(uint32_t)));
   HIPCHK(ev_pin.ensure(sizeof(uint32_t) * std::max<int64_t>(E, 1)));
   HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
-  if (P > 0) HIPCHK(pa::launch_pin_check(P, pin_ptr, pin_init, err.as<uint32_t>(), s));
-  uint32_t herr = 0;
-  HIPCHK(hipMemcpyAsync(&herr, err.p, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-  HIPCHK(hipStreamSynchronize(s));
-  if (herr & pa::ERR_PIN_PTR) return fail(PA_EDATA, "pa_load_events: pin_ptr decreases");
-  if (herr & pa::ERR_INIT) return fail(PA_EDATA, "pa_load_events: pin_init not in {0,1}");
+  HIPCHK(pa::launch_pin_check(P, E, pin_ptr, pin_init, err.as<uint32_t>(), s));
   if (E > 0) {
     // owning pins (a scatter of every pin's index at its first event and a
     // running maximum), then the checks
@@ -831,8 +822,12 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
     HIPCHK(pa::launch_event_check(E, P, pin_ptr, pin_init, evt_t, evt_val, evt_slew, t_max, mark.as<uint32_t>(),
                                   ev_pin.as<uint32_t>(), err.as<uint32_t>(), tmp.p, &tb, s));
   }
+  uint32_t herr = 0;
   HIPCHK(hipMemcpyAsync(&herr, err.p, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
+  if (herr & pa::ERR_ENDS) return fail(PA_EDATA, "pa_load_events: pin_ptr[0] must be 0 and pin_ptr[P] = n_events");
+  if (herr & pa::ERR_PIN_PTR) return fail(PA_EDATA, "pa_load_events: pin_ptr decreases");
+  if (herr & pa::ERR_INIT) return fail(PA_EDATA, "pa_load_events: pin_init not in {0,1}");
   if (herr & pa::ERR_TIME_RANGE) return fail(PA_EDATA, "pa_load_events: event time outside [0, t_max)");
   if (herr & pa::ERR_TIME_ORDER) return fail(PA_EDATA, "pa_load_events: timestamps not strictly increasing on a pin");
   if (herr & pa::ERR_VALUE) return fail(PA_EDATA, "pa_load_events: values do not alternate starting from !init");
@@ -948,14 +943,11 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
       HIPCHK(pa::sort_pairs_u32(&qk, &qs, &pa_, &pb_, E, (int)qbits, tmp.p, &tmp_bytes, s));
       if (pa_ != perm.p) swap_bufs(perm, idx);  // the permutation ended in idx's buffer
     }
-    // ---- packed keys, window heads and start states
-    HIPCHK(hipMemsetAsync(err.p, 0, sizeof(uint32_t), s));
+    // ---- packed keys and window heads (the start states come with the windows)
     HIPCHK(pa::launch_layout(E, perm.as<uint32_t>(), one_key ? k1.as<uint64_t>() : nullptr, evt_t, evt_slew, evt_val,
-                             ev_pin.as<uint32_t>(),
-                             d.pin_gate.as<int32_t>(), d.pin_local.as<uint8_t>(), d.gate_k.as<int32_t>(),
-                             level.as<uint8_t>(), d.pin_base.as<int64_t>(), pin_ptr, pin_init, f, skey.as<uint64_t>(),
-                             sslew.as<float>(), sorig.as<uint32_t>(), chunk_sorted.as<uint32_t>(), err.as<uint32_t>(),
-                             s));
+                             ev_pin.as<uint32_t>(), d.pin_gate.as<int32_t>(), d.pin_local.as<uint8_t>(),
+                             d.gate_k.as<int32_t>(), level.as<uint8_t>(), f, skey.as<uint64_t>(), sslew.as<float>(),
+                             sorig.as<uint32_t>(), chunk_sorted.as<uint32_t>(), s));
   }
   HIPCHK(pa::launch_chunk_base(E, Q, chunk_sorted.as<uint32_t>(), cbase.as<uint32_t>(), s));
   if (P > 0) HIPCHK(hipMemcpyAsync(v.pin_init.p, pin_init, P, hipMemcpyDeviceToDevice, s));

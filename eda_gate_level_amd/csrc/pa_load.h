@@ -18,6 +18,7 @@ enum : uint32_t {
   ERR_TIME_ORDER = 1u << 5,  // timestamps not strictly increasing on a pin
   ERR_VALUE = 1u << 6,       // values do not alternate starting from !init
   ERR_SLEW = 1u << 7,        // slew not finite and > 0
+  ERR_ENDS = 1u << 8,        // pin_ptr[0] != 0 or pin_ptr[P] != n_events
 };
 
 // bit widths of the event layout
@@ -43,7 +44,7 @@ hipError_t launch_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *c
                             double *gate_J, hipStream_t s);
 hipError_t launch_pin_owner(int64_t G, const int64_t *pin_base, const int32_t *gate_k, int32_t *pin_gate,
                             uint8_t *pin_local, hipStream_t s);
-hipError_t launch_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err,
+hipError_t launch_pin_check(int64_t P, int64_t E, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err,
                             hipStream_t s);
 hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init,
                               const int64_t *evt_t, const uint8_t *evt_val, const float *evt_slew, int64_t t_max,
@@ -62,9 +63,8 @@ hipError_t launch_chunk_of(int64_t E, const uint32_t *perm, const uint32_t *chun
 hipError_t launch_layout(int64_t E, const uint32_t *perm, const uint64_t *skey, const int64_t *evt_t,
                          const float *evt_slew, const uint8_t *evt_val, const uint32_t *ev_pin,
                          const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
-                         const uint8_t *level, const int64_t *pin_base, const int64_t *pin_ptr,
-                         const uint8_t *pin_init, const LayoutFmt &f, uint64_t *key_out, float *slew_out,
-                         uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err, hipStream_t s);
+                         const uint8_t *level, const LayoutFmt &f, uint64_t *key_out, float *slew_out,
+                         uint32_t *orig_out, uint32_t *chunk_out, hipStream_t s);
 // the start state of every input window into its first event's key (after the windows are known)
 hipError_t launch_window_s0(uint32_t W, const uint32_t *ws, const uint32_t *chunk_sorted, const uint8_t *level,
                             const int32_t *gate_k, const int64_t *pin_base, const int64_t *pin_ptr,

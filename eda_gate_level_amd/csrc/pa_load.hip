@@ -80,7 +80,8 @@ __global__ void k_pin_owner(int64_t G, const int64_t *pin_base, const int32_t *g
 
 // ------------------------------------------------------------------ events
 
-__global__ void k_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err) {
+__global__ void k_pin_check(int64_t P, int64_t E, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err) {
+  if (blockIdx.x == 0 && threadIdx.x == 0 && (pin_ptr[0] != 0 || pin_ptr[P] != E)) atomicOr(err, ERR_ENDS);
   for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x) {
     if (pin_ptr[p + 1] < pin_ptr[p]) atomicOr(err, ERR_PIN_PTR);
     if (pin_init[p] > 1) atomicOr(err, ERR_INIT);
@@ -90,10 +91,14 @@ __global__ void k_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pi
 // Owning pin of every event, the last p with pin_ptr[p] <= e: every pin with
 // events writes its index at its first event (those positions are distinct),
 // the rest of the array holding 0, and a running maximum over the events
-// spreads each index over its pin's range.
-__global__ void k_pin_starts(int64_t P, const int64_t *pin_ptr, uint32_t *mark) {
-  for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x)
-    if (pin_ptr[p] < pin_ptr[p + 1]) mark[pin_ptr[p]] = (uint32_t)p;
+// spreads each index over its pin's range.  This runs before the pin checks
+// are read back, so a position outside [0, E) is skipped (the load then
+// fails on those checks).
+__global__ void k_pin_starts(int64_t P, int64_t E, const int64_t *pin_ptr, uint32_t *mark) {
+  for (int64_t p = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; p < P; p += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t a = pin_ptr[p];
+    if (a < pin_ptr[p + 1] && a >= 0 && a < E) mark[a] = (uint32_t)p;
+  }
 }
 
 // validation of every event against its pin
@@ -106,7 +111,7 @@ __global__ void k_event_check(int64_t E, const int64_t *pin_ptr, const uint8_t *
     const int64_t t = evt_t[e];
     uint32_t bad = 0;
     if (t < 0 || t >= t_max) bad |= ERR_TIME_RANGE;
-    if (idx > 0 && !(t > evt_t[e - 1])) bad |= ERR_TIME_ORDER;
+    if (idx > 0 && e > 0 && !(t > evt_t[e - 1])) bad |= ERR_TIME_ORDER;
     const uint8_t init = pin_init[lo] & 1u;
     if (evt_val[e] != (uint8_t)(init ^ ((idx + 1) & 1))) bad |= ERR_VALUE;
     const float s = evt_slew[e];
@@ -211,9 +216,8 @@ __device__ __forceinline__ EvPos key_pos(uint64_t K, const LayoutFmt &f) {
 __global__ void k_layout(int64_t E, const uint32_t *perm, const uint64_t *skey, const int64_t *evt_t,
                          const float *evt_slew, const uint8_t *evt_val, const uint32_t *ev_pin,
                          const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
-                         const uint8_t *level, const int64_t *pin_base, const int64_t *pin_ptr,
-                         const uint8_t *pin_init, LayoutFmt f, uint64_t *key_out, float *slew_out, uint32_t *orig_out,
-                         uint32_t *chunk_out, uint32_t *err) {
+                         const uint8_t *level, LayoutFmt f, uint64_t *key_out, float *slew_out, uint32_t *orig_out,
+                         uint32_t *chunk_out) {
   for (int64_t x = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; x < E; x += (int64_t)gridDim.x * blockDim.x) {
     const int64_t e = perm[x];
     const EvPos p = skey ? key_pos(skey[x], f) : ev_pos(e, evt_t, ev_pin, pin_gate, pin_local, gate_k, f);
@@ -664,9 +668,9 @@ hipError_t launch_pin_owner(int64_t G, const int64_t *pin_base, const int32_t *g
   return hipGetLastError();
 }
 
-hipError_t launch_pin_check(int64_t P, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err,
+hipError_t launch_pin_check(int64_t P, int64_t E, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err,
                             hipStream_t s) {
-  hipLaunchKernelGGL(k_pin_check, dim3(grid_for(P)), dim3(kLT), 0, s, P, pin_ptr, pin_init, err);
+  hipLaunchKernelGGL(k_pin_check, dim3(grid_for(P)), dim3(kLT), 0, s, P, E, pin_ptr, pin_init, err);
   return hipGetLastError();
 }
 
@@ -678,7 +682,7 @@ hipError_t launch_event_check(int64_t E, int64_t P, const int64_t *pin_ptr, cons
   if (!tmp) return rocprim::inclusive_scan(nullptr, *tmp_bytes, mark, ev_pin, (size_t)E, rocprim::maximum<uint32_t>(), s);
   hipError_t e = hipMemsetAsync(mark, 0, sizeof(uint32_t) * E, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_pin_starts, dim3(grid_for(P)), dim3(kLT), 0, s, P, pin_ptr, mark);
+  hipLaunchKernelGGL(k_pin_starts, dim3(grid_for(P)), dim3(kLT), 0, s, P, E, pin_ptr, mark);
   e = rocprim::inclusive_scan(tmp, *tmp_bytes, mark, ev_pin, (size_t)E, rocprim::maximum<uint32_t>(), s);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_event_check, dim3(grid_for(E)), dim3(kLT), 0, s, E, pin_ptr, pin_init, evt_t, evt_val, evt_slew,
@@ -711,12 +715,10 @@ hipError_t launch_chunk_of(int64_t E, const uint32_t *perm, const uint32_t *chun
 hipError_t launch_layout(int64_t E, const uint32_t *perm, const uint64_t *skey, const int64_t *evt_t,
                          const float *evt_slew, const uint8_t *evt_val, const uint32_t *ev_pin,
                          const int32_t *pin_gate, const uint8_t *pin_local, const int32_t *gate_k,
-                         const uint8_t *level, const int64_t *pin_base, const int64_t *pin_ptr,
-                         const uint8_t *pin_init, const LayoutFmt &f, uint64_t *key_out, float *slew_out,
-                         uint32_t *orig_out, uint32_t *chunk_out, uint32_t *err, hipStream_t s) {
+                         const uint8_t *level, const LayoutFmt &f, uint64_t *key_out, float *slew_out,
+                         uint32_t *orig_out, uint32_t *chunk_out, hipStream_t s) {
   hipLaunchKernelGGL(k_layout, dim3(grid_for(E)), dim3(kLT), 0, s, E, perm, skey, evt_t, evt_slew, evt_val, ev_pin,
-                     pin_gate, pin_local, gate_k, level, pin_base, pin_ptr, pin_init, f, key_out, slew_out, orig_out,
-                     chunk_out, err);
+                     pin_gate, pin_local, gate_k, level, f, key_out, slew_out, orig_out, chunk_out);
   return hipGetLastError();
 }
 
