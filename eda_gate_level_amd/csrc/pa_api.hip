@@ -237,6 +237,7 @@ struct pa_ctx {
   LoadScratch ls;
   bool keep_load_buffers = false;  // pa_run_text: ev_spare and ls live until the text is done
   PinnedBuf text_host[2];  // pa_run_text: packed segments on the host, and their device copy
+  PinnedBuf readback;      // the load's small device-to-host reads, gathered for one synchronisation
   DBuf text_dev;
   double *h_res = nullptr;
   ScratchAddr scratch;  // this device's copy of the fixed scratch of pa_run_noalloc
@@ -530,9 +531,17 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
       c->tun.grid_blocks > 0 ? c->tun.grid_blocks : (int64_t)pa::pass_blocks_per_cu() * c->n_cu;
   const int64_t min_events = 4 * (int64_t)pa::pass_wave_batch() * NW;
 
-  // ---- windows: starts and lengths
+  // ---- device work that needs no host decision, read back in one go: the
+  // window count (a scan of the head flags), every sorted event's cost in
+  // the pass (the walk kernel's relative costs of input-pin and output-pin
+  // events and of a window's set-up, else one per event) and the cost before
+  // every chunk, the chunks' first events, and the leakage power at t = 0
   const int64_t E = v.E;
-  uint32_t W = 0;
+  const bool try_walk = E > 0 && v.compact_ok;  // with events there is a window
+  const int32_t room =
+      try_walk ? pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax) : 0;
+  const size_t nq = (size_t)v.Q + 1;
+  HIPCHK(ls.wkey0.ensure(sizeof(uint64_t) * nq));
   if (E > 0) {
     HIPCHK(ls.winc.ensure(sizeof(uint32_t) * E));
     HIPCHK(ls.widx.ensure(sizeof(uint32_t) * E));  // head flags first, window indices later
@@ -541,9 +550,46 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
     HIPCHK(pa::scan_inclusive_u32(ls.widx.as<uint32_t>(), ls.winc.as<uint32_t>(), E, nullptr, &tb, s));
     HIPCHK(ls.tmp.ensure(tb));
     HIPCHK(pa::scan_inclusive_u32(ls.widx.as<uint32_t>(), ls.winc.as<uint32_t>(), E, ls.tmp.p, &tb, s));
-    HIPCHK(hipMemcpyAsync(&W, ls.winc.as<uint32_t>() + (E - 1), sizeof(uint32_t), hipMemcpyDeviceToHost, s));
-    HIPCHK(hipStreamSynchronize(s));
+    HIPCHK(ls.k0.ensure(sizeof(uint64_t) * E));  // the sort's buffers, free again here
+    HIPCHK(ls.k1.ensure(sizeof(uint64_t) * E));
+    HIPCHK(pa::launch_event_cost(E, ls.skey.as<uint64_t>(), pa::out_code(v.pb), try_walk ? kWalkCostIn : 1u,
+                                 try_walk ? kWalkCostOut : 1u, try_walk ? kWalkCostHead : 0u,
+                                 try_walk ? d.gate_k.as<int32_t>() : nullptr, v.gb, ls.k0.as<uint64_t>(),
+                                 s));
+    tb = 0;
+    HIPCHK(pa::scan_inclusive_u64(ls.k0.as<uint64_t>(), ls.k1.as<uint64_t>(), E, nullptr, &tb, s));
+    HIPCHK(ls.tmp.ensure(tb));
+    HIPCHK(pa::scan_inclusive_u64(ls.k0.as<uint64_t>(), ls.k1.as<uint64_t>(), E, ls.tmp.p, &tb, s));
+    HIPCHK(pa::launch_gather_prefix(v.Q + 1, ls.cbase.as<uint32_t>(), ls.k1.as<uint64_t>(), ls.wkey0.as<uint64_t>(),
+                                    s));
+  } else {
+    HIPCHK(hipMemsetAsync(ls.wkey0.p, 0, sizeof(uint64_t) * nq, s));
   }
+  DBuf &part = ls.part;
+  HIPCHK(part.ensure(sizeof(double) * pa::leak0_parts()));
+  HIPCHK(v.l0.ensure(sizeof(double)));
+  HIPCHK(pa::launch_leak0(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
+                          d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), part.as<double>(), v.l0.as<double>(), s));
+  // pinned: [l0][cpre Q+1][W][chunk bases Q+1]
+  const size_t rb_bytes = sizeof(double) + sizeof(uint64_t) * nq + sizeof(uint32_t) * (1 + nq);
+  HIPCHK(c->readback.ensure(rb_bytes));
+  unsigned char *rb = static_cast<unsigned char *>(c->readback.p);
+  double *rb_l0 = reinterpret_cast<double *>(rb);
+  uint64_t *rb_cpre = reinterpret_cast<uint64_t *>(rb + sizeof(double));
+  uint32_t *rb_w = reinterpret_cast<uint32_t *>(rb_cpre + nq);
+  uint32_t *rb_cb = rb_w + 1;
+  *rb_w = 0;
+  HIPCHK(hipMemcpyAsync(rb_l0, v.l0.p, sizeof(double), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(rb_cpre, ls.wkey0.p, sizeof(uint64_t) * nq, hipMemcpyDeviceToHost, s));
+  if (E > 0) HIPCHK(hipMemcpyAsync(rb_w, ls.winc.as<uint32_t>() + (E - 1), sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+  HIPCHK(hipMemcpyAsync(rb_cb, ls.cbase.p, sizeof(uint32_t) * nq, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  v.l0_host = *rb_l0;
+  std::vector<uint64_t> cpre(rb_cpre, rb_cpre + nq);
+  const uint32_t W = *rb_w;
+  v.h_chunk_base.assign(rb_cb, rb_cb + nq);
+
+  // ---- windows: starts and lengths
   v.n_windows = W;
   HIPCHK(ls.ws.ensure(sizeof(uint32_t) * ((size_t)W + 1)));
   HIPCHK(v.wlen.ensure(sizeof(uint32_t) * std::max<size_t>(W, 1)));
@@ -560,31 +606,6 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
     HIPCHK(pa::launch_window_s0(W, ls.ws.as<uint32_t>(), ls.chunk_sorted.as<uint32_t>(), ls.level.as<uint8_t>(),
                                 d.gate_k.as<int32_t>(), d.pin_base.as<int64_t>(), pin_ptr, pin_init, evt_t, f,
                                 ls.skey.as<uint64_t>(), s));
-  }
-
-  // ---- every sorted event's cost in the pass (the walk kernel's relative
-  // costs of input-pin and output-pin events and of a window's set-up, else
-  // one per event), and the cost before every chunk: blocks get equal costs
-  const bool try_walk = W > 0 && v.compact_ok;
-  const int32_t room =
-      try_walk ? pa::walk_lut_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax) : 0;
-  std::vector<uint64_t> cpre((size_t)v.Q + 1, 0);
-  if (E > 0) {
-    HIPCHK(ls.k0.ensure(sizeof(uint64_t) * E));  // the sort's buffers, free again here
-    HIPCHK(ls.k1.ensure(sizeof(uint64_t) * E));
-    HIPCHK(pa::launch_event_cost(E, ls.skey.as<uint64_t>(), pa::out_code(v.pb), try_walk ? kWalkCostIn : 1u,
-                                 try_walk ? kWalkCostOut : 1u, try_walk ? kWalkCostHead : 0u,
-                                 try_walk ? d.gate_k.as<int32_t>() : nullptr, v.gb, ls.k0.as<uint64_t>(),
-                                 s));
-    size_t tb = 0;
-    HIPCHK(pa::scan_inclusive_u64(ls.k0.as<uint64_t>(), ls.k1.as<uint64_t>(), E, nullptr, &tb, s));
-    HIPCHK(ls.tmp.ensure(tb));
-    HIPCHK(pa::scan_inclusive_u64(ls.k0.as<uint64_t>(), ls.k1.as<uint64_t>(), E, ls.tmp.p, &tb, s));
-    HIPCHK(ls.wkey0.ensure(sizeof(uint64_t) * ((size_t)v.Q + 1)));
-    HIPCHK(pa::launch_gather_prefix(v.Q + 1, ls.cbase.as<uint32_t>(), ls.k1.as<uint64_t>(), ls.wkey0.as<uint64_t>(),
-                                    s));
-    HIPCHK(hipMemcpyAsync(cpre.data(), ls.wkey0.p, sizeof(uint64_t) * cpre.size(), hipMemcpyDeviceToHost, s));
-    HIPCHK(hipStreamSynchronize(s));
   }
   const uint64_t total = cpre[v.Q];
 
@@ -749,13 +770,6 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
   } else {
     v.lut_lds = 0;
   }
-  // leakage power at t = 0, from the initial pin values
-  DBuf &part = ls.part;
-  HIPCHK(part.ensure(sizeof(double) * pa::leak0_parts()));
-  HIPCHK(v.l0.ensure(sizeof(double)));
-  HIPCHK(pa::launch_leak0(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
-                          d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), part.as<double>(), v.l0.as<double>(), s));
-  HIPCHK(hipMemcpyAsync(&v.l0_host, v.l0.p, sizeof(double), hipMemcpyDeviceToHost, s));
   HIPCHK(hipStreamSynchronize(s));
   return PA_OK;
 }
@@ -951,9 +965,6 @@ static int load_events(pa_ctx *c, int64_t n_pins, int64_t n_events, const int64_
   }
   HIPCHK(pa::launch_chunk_base(E, Q, chunk_sorted.as<uint32_t>(), cbase.as<uint32_t>(), s));
   if (P > 0) HIPCHK(hipMemcpyAsync(v.pin_init.p, pin_init, P, hipMemcpyDeviceToDevice, s));
-  v.h_chunk_base.resize(Q + 1);
-  HIPCHK(hipMemcpyAsync(v.h_chunk_base.data(), cbase.p, sizeof(uint32_t) * (Q + 1), hipMemcpyDeviceToHost, s));
-  HIPCHK(hipStreamSynchronize(s));
   int rc = build_ranges(c, v, pin_ptr, pin_init, evt_t);
   if (rc != PA_OK) return rc;
   c->ev_spare = std::move(c->ev);
