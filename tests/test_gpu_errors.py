@@ -59,11 +59,20 @@ def _mut(t, kind):
         if pp[3] == pp[4]:
             pp[3] += 1
         return dataclasses.replace(t, pin_ptr=pp)
+    if kind == "ptr_first":  # pin_ptr[0] != 0
+        pp = t.pin_ptr.copy(); pp[0] = 1
+        return dataclasses.replace(t, pin_ptr=pp)
+    if kind == "ptr_last":  # pin_ptr[P] != n_events
+        pp = t.pin_ptr.copy(); pp[-1] -= 1
+        return dataclasses.replace(t, pin_ptr=pp)
+    if kind == "ptr_far":  # offsets far outside the events: the owner scatter must skip them
+        pp = t.pin_ptr.copy(); pp[5] = 1 << 40; pp[7] = -7
+        return dataclasses.replace(t, pin_ptr=pp)
     raise ValueError(kind)
 
 
 @pytest.mark.parametrize("kind", ["unsorted", "value", "value2", "t_max", "negative", "slew", "slew_nan", "init",
-                                  "pin_ptr"])
+                                  "pin_ptr", "ptr_first", "ptr_last", "ptr_far"])
 def test_bad_events_rejected_and_previous_data_kept(kind):
     import eda_gate_level_amd as pa
     import oracle
