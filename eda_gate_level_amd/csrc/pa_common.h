@@ -15,15 +15,17 @@ constexpr int kMaxInputs = 8;  // inputs of a cell (pa_load_design rejects more)
 // Event layout.  Time is cut into chunks of Cc clock cycles (a power of two);
 // inside a chunk every gate's cycles are cut into 2^s equal windows, s chosen
 // per gate from its event density (the paper's event-density-aware per-gate
-// cycle partitioning).  Inside a window the events are in
+// cycle partitioning); a gate's input-pin events and its output-pin events go
+// to windows of their own.  Inside a window the events are in
 //   (cycle, time, pin code)
 // order: the events of one clock cycle form one run in time order, events of
 // one timestamp ordered by pin code.  Every block of the pass owns a range of
-// whole windows of one chunk; its windows are dealt to its lanes, and each
-// lane walks its windows one after the other (each padded to an even length).
-// A wave's 64 lane streams are interleaved in pairs: event j of lane l sits at
-// slot base + (j / 2) * 128 + 2 l + j % 2.  Empty slots hold key 0, which no
-// event has (an event at the start of a window is a head, so bit 41 is set).
+// whole windows of one chunk; its windows go in phases of up to 64 windows of
+// one kind to its waves, one window per lane, each lane's window padded to
+// an even length and to the phase's longest.  A wave's 64 lane streams are
+// interleaved in pairs: slot j of lane l sits at base + (j / 2) * 128 + 2 l +
+// j % 2.  Empty slots hold the pad key (an output-pin 1->0 event in cycle Cc,
+// or key 0 when the chunk leaves no spare cycle bit), which no event has.
 //
 // Packed 64-bit key of an event (gb = bits of the largest gate id, cs = pb + tb):
 //   bits [42 + gb, 64)  the high bits of the cycle in the chunk (22 - gb of them)
