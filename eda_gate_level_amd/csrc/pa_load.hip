@@ -313,10 +313,11 @@ __global__ void k_chunk_base(int64_t E, int32_t Q, const uint32_t *chunk_sorted,
 // the group (lane i the group's i-th window), all starting at the phase's
 // first slot, and the phase lasts as long as its longest window (rounded up
 // to an even count).  So every lane of a wave meets a window start at the same
-// step and walks windows of one kind.  The phases, longest first, go to the
-// block's 16 waves, each to the wave with the least work so far (the
-// longest-processing-time rule); a wave's phases follow one another in its
-// stream, and a wave's 64 streams are interleaved in pairs.
+// step and walks windows of one kind.  The phases, costliest first, go to the
+// block's 16 waves, each to the wave that would finish it first given the
+// work it holds and its measured relative speed (the longest-processing-time
+// rule); a wave's phases follow one another in its stream, and a wave's 64
+// streams are interleaved in pairs.
 
 constexpr int kLaneNT = 1024;  // lanes of a block of the pass
 constexpr int kLaneNW = kLaneNT / 64;
