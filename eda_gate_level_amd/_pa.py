@@ -60,7 +60,7 @@ class pa_info(C.Structure):
                 ("block_threads", C.c_int32), ("batch_events", C.c_int32), ("max_segment_events", C.c_int32),
                 ("device_bytes", C.c_int64), ("kernel_ms", C.c_float * 4), ("n_windows", C.c_int64),
                 ("n_slots", C.c_int64), ("wave_steps_max", C.c_int32), ("wave_steps_mean", C.c_float),
-                ("tables_in_lds", C.c_int32)]
+                ("tables_in_lds", C.c_int32), ("walk_kernel", C.c_int32)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_ if f != "kernel_ms"}

@@ -1224,6 +1224,7 @@ int pa_get_info(pa_ctx *c, pa_info *info) {
                                                 c->d.n_leak, c->d.kmax))
                             ? 1
                             : 0;
+  info->walk_kernel = c->has_events && c->ev.walk_lut > 0 ? 1 : 0;
   return PA_OK;
 }
 

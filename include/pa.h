@@ -226,6 +226,10 @@ typedef struct {
   int32_t tables_in_lds;      /* 1: every block of the pass stages the per-cell tables (axes,
                                  slew thresholds, leakage) in LDS; 0: they are read through the
                                  caches (libraries too large for the LDS next to the bins) */
+  int32_t walk_kernel;        /* 1: a pass over the loaded events without per-event or per-gate outputs
+                                 (pa_run without them, pa_run_noalloc) runs the walk kernel (7- or
+                                 8-point axes, every block's LUT range fits its LDS); 0: it runs the
+                                 general pass kernel */
 } pa_info;
 int pa_get_info(pa_ctx *ctx, pa_info *info);
 
