@@ -70,6 +70,18 @@ constexpr size_t kLdsMax = 160 * 1024 / kBPC;  // LDS of a block (gfx950: 160 KB
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
+// r_gl (Eq. 2 as read): the pulse width over the mean of the two slews, at
+// most 1.  The reciprocal of the mean is the hardware estimate refined by
+// two Newton steps (each doubles its correct bits), a few ulp from the
+// quotient instead of the exact division's dozen instructions.
+__device__ __forceinline__ double glitch_ratio(double pw, double s0, double s1) {
+  const double m = 0.5 * (s0 + s1);
+  double x = __builtin_amdgcn_rcp(m);
+  x = fma(fma(-m, x, 1.0), x, x);
+  x = fma(fma(-m, x, 1.0), x, x);
+  return fmin(pw * x, 1.0);
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
@@ -410,9 +422,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_fused(PassArgs a) {
           uint2 *pr = prec + (size_t)min(code[r], kmax) * 64;
           if (glitch[r]) {
             const uint2 prev = *pr;  // the pin's previous event in this cycle
-            const double pw = (double)(tic[r] - prev.x);
-            const double rr = pw / (0.5 * ((double)sl[r] + (double)__uint_as_float(prev.y)));  // Eq. 2 (reading)
-            scale[r] = rr > 1.0 ? 1.0 : rr;
+            scale[r] = glitch_ratio((double)(tic[r] - prev.x), (double)sl[r], (double)__uint_as_float(prev.y));
           }
           if (act[r]) *pr = make_uint2(tic[r], __float_as_uint(sl[r]));
         }
@@ -894,24 +904,24 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
       // are read and written in event order (both events may be one pin's)
       if constexpr (KREG > 0) {
         if (glitch[0] || glitch[1]) {
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            if (glitch[r]) {
-              const uint32_t ptic_pin = rtic[cl[r] & 3u], pslew_pin = rslw[cl[r] & 3u];
-              const double pw = (double)(tic[r] - ptic_pin);
-              const double rr = pw / (0.5 * ((double)sl[r] + (double)__uint_as_float(pslew_pin)));
-              E[r] *= rr > 1.0 ? 1.0 : rr;
-              e_gl += E[r];
-            }
-            rtic[cl[r] & 3u] = tic[r];
-            rslw[cl[r] & 3u] = __float_as_uint(sl[r]);
+          // the second event's pin record is the first event itself when both are one pin's
+          const bool same = cl[1] == cl[0];
+          const uint32_t pt0 = rtic[cl[0] & 3u], ps0 = rslw[cl[0] & 3u];
+          const uint32_t pt1 = same ? tic[0] : rtic[cl[1] & 3u];
+          const uint32_t ps1 = same ? __float_as_uint(sl[0]) : rslw[cl[1] & 3u];
+          if (glitch[0]) {
+            E[0] *= glitch_ratio((double)(tic[0] - pt0), (double)sl[0], (double)__uint_as_float(ps0));
+            e_gl += E[0];
           }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 2; ++r) {
-            rtic[cl[r] & 3u] = tic[r];
-            rslw[cl[r] & 3u] = __float_as_uint(sl[r]);
+          if (glitch[1]) {
+            E[1] *= glitch_ratio((double)(tic[1] - pt1), (double)sl[1], (double)__uint_as_float(ps1));
+            e_gl += E[1];
           }
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          rtic[cl[r] & 3u] = tic[r];
+          rslw[cl[r] & 3u] = __float_as_uint(sl[r]);
         }
       } else {
         lds_u32 *pr0 = prec + cl[0] * 128, *pr1 = prec + cl[1] * 128;
@@ -921,9 +931,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
             lds_u32 *pr = r ? pr1 : pr0;
             if (glitch[r]) {
               const uint32_t ptic_pin = pr[0], pslew_pin = pr[1];
-              const double pw = (double)(tic[r] - ptic_pin);
-              const double rr = pw / (0.5 * ((double)sl[r] + (double)__uint_as_float(pslew_pin)));
-              E[r] *= rr > 1.0 ? 1.0 : rr;
+              E[r] *= glitch_ratio((double)(tic[r] - ptic_pin), (double)sl[r], (double)__uint_as_float(pslew_pin));
               e_gl += E[r];
             }
             pr[0] = tic[r];
@@ -976,9 +984,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           if (glitch[r]) {
-            const double pw = (double)(tic[r] - (r ? tic[0] : pt));
-            const double rr = pw / (0.5 * ((double)sl[r] + (double)(r ? sl[0] : ps)));
-            E[r] *= rr > 1.0 ? 1.0 : rr;
+            E[r] *= glitch_ratio((double)(tic[r] - (r ? tic[0] : pt)), (double)sl[r], (double)(r ? sl[0] : ps));
             e_gl += E[r];
           }
         }
