@@ -9,11 +9,13 @@ Timing: W untimed warm-up passes plus >= 2 s of passes to reach steady
 clocks; then K passes, each preceded by a 1 GiB write that evicts the L2s
 and the 256 MB Infinity Cache (so the events come from HBM), all bracketed
 by torch.cuda.synchronize().  ms_per_step is the median device time of the
-pass (HIP events recorded by the library around its kernels, on its stream);
-wall_ms_per_step is the bracket divided by K (includes the flushes and the
-host side of each call).  The fused kernel's algorithmic bytes per launch
-(12 B per event, 9 B per pin, 12 B per gate, the tables once) over its own
-device time give roofline.achieved.
+pass (HIP events recorded by the library on its stream before the first
+kernel and after the last); wall_ms_per_step is the bracket divided by K
+(includes the flushes and the host side of each call).  The fused kernel's
+algorithmic bytes per launch (12 B per event, 9 B per pin, 12 B per gate,
+the tables once) over its own device time (HIP events attached to its
+dispatch, which time the kernel's execution as the profiler's kernel trace
+does) give roofline.achieved.
 
 "configs" repeats the measurement for the other workloads (Tiny, Skewed,
 Glitch-heavy and the 200M-event one), each loaded, warmed up and timed the
@@ -382,9 +384,11 @@ def measure(args, w, dev, gen_s, flush_gib=1, steps=None):
     while time.time() < t_end:
         an.run(outs)
     warm = []
+    an.set_timing(2)
     for _ in range(10):
         an.run(outs)
         warm.append(an.info()["kernel_ms"])
+    an.set_timing(1)
     fused_ms, pass_ms = [], []
     for _ in range(steps):
         if not args.no_flush:

@@ -241,7 +241,7 @@ struct pa_ctx {
   DBuf text_dev;
   double *h_res = nullptr;
   ScratchAddr scratch;  // this device's copy of the fixed scratch of pa_run_noalloc
-  hipEvent_t tev[3] = {nullptr, nullptr, nullptr};
+  hipEvent_t tev[6] = {nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};  // pass start, end; walk, finalize
   float kernel_ms[4] = {0, 0, 0, 0};
 };
 
@@ -1088,11 +1088,13 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   f.res = sc.res;
 
   const bool timed = c->tun.time_kernels != 0, per_kernel = c->tun.time_kernels == 1;
+  // mode 1 times each kernel by events attached to its dispatch, mode 2 the
+  // whole pass by events recorded before the first and after the last
   if (timed) HIPCHK(hipEventRecord(c->tev[0], s));
-  hipError_t e1 = pa::launch_pass(a, v.grid, s);
-  if (per_kernel && e1 == hipSuccess) e1 = hipEventRecord(c->tev[1], s);
-  if (e1 == hipSuccess) e1 = pa::launch_finalize(f, s);
-  if (timed && e1 == hipSuccess) e1 = hipEventRecord(c->tev[2], s);
+  hipError_t e1 = per_kernel ? pa::launch_pass(a, v.grid, s, c->tev[2], c->tev[3]) : pa::launch_pass(a, v.grid, s);
+  if (e1 == hipSuccess)
+    e1 = per_kernel ? pa::launch_finalize(f, s, c->tev[4], c->tev[5]) : pa::launch_finalize(f, s);
+  if (timed && e1 == hipSuccess) e1 = hipEventRecord(c->tev[1], s);
   if (e1 == hipSuccess) e1 = hipMemcpyAsync(c->h_res, f.res, sizeof(double) * 16, hipMemcpyDeviceToHost, s);
   if (e1 == hipSuccess) e1 = hipStreamSynchronize(s);
   if (e1 != hipSuccess) {
@@ -1100,13 +1102,12 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
     return fail(PA_EHIP, "pa_run: HIP error %s", hipGetErrorString(e1));
   }
   if (per_kernel) {
-    (void)hipEventElapsedTime(&c->kernel_ms[0], c->tev[0], c->tev[1]);
-    (void)hipEventElapsedTime(&c->kernel_ms[1], c->tev[1], c->tev[2]);
-    c->kernel_ms[3] = c->kernel_ms[0] + c->kernel_ms[1];
+    (void)hipEventElapsedTime(&c->kernel_ms[0], c->tev[2], c->tev[3]);
+    (void)hipEventElapsedTime(&c->kernel_ms[1], c->tev[4], c->tev[5]);
   } else if (timed) {
     c->kernel_ms[0] = c->kernel_ms[1] = 0.0f;
-    (void)hipEventElapsedTime(&c->kernel_ms[3], c->tev[0], c->tev[2]);
   }
+  if (timed) (void)hipEventElapsedTime(&c->kernel_ms[3], c->tev[0], c->tev[1]);
   const double *r = c->h_res;
   out->e_int_J = r[0];
   out->e_sw_J = r[1];

@@ -137,9 +137,11 @@ struct FinalArgs {
   double *res;                // [16] results for the host
 };
 
-// Launchers (defined in pa_pass.hip).
-hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s);
-hipError_t launch_finalize(const FinalArgs &a, hipStream_t s);
+// Launchers (defined in pa_pass.hip).  Given two events, they time the
+// kernel's own execution (events attached to its dispatch).
+hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s, hipEvent_t e0 = nullptr,
+                       hipEvent_t e1 = nullptr);
+hipError_t launch_finalize(const FinalArgs &a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
 // Per block, the cells whose LUTs it copies into the LDS left over by its bins,
 // pin records and cell tables (lut_lds doubles, from pass_lut_lds_doubles): 64
 // windows sampled evenly over the block's window range [bwin[b], bwin[b+1])

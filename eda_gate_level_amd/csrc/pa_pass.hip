@@ -43,6 +43,7 @@
 //     split (Sec. 2.4.2, Eq. 4) summed in another order;
 //   * every block writes its bins and totals to its own slots; the finalize
 //     kernel adds them up in a fixed order (no global atomics).
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "pa_common.h"
@@ -1387,7 +1388,16 @@ int32_t walk_lut_doubles(int Cc, int n_cells, int n_slew, int n_cap, int n_thr, 
   return fixed < kLdsMax ? (int32_t)((kLdsMax - fixed) / 16 * 2) : 0;
 }
 
-hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
+// A launch; with events, they are attached to the kernel's dispatch and
+// time the kernel's own execution (not the dispatch and completion around it).
+template <class K, class A>
+static void launch_timed(K kernel, dim3 g, dim3 t, size_t dyn, hipStream_t s, hipEvent_t e0, hipEvent_t e1,
+                         const A &a) {
+  if (e0 && e1) hipExtLaunchKernelGGL(kernel, g, t, (uint32_t)dyn, s, e0, e1, 0, a);
+  else hipLaunchKernelGGL(kernel, g, t, dyn, s, a);
+}
+
+hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax);
   const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
   if (a.walk_lut > 0 && !diag) {
@@ -1398,15 +1408,15 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
     const dim3 g(grid_blocks), t(kNT);
     const bool kreg = a.kmax <= kWalkRegPins;
     if (a.n_slew == 7 && a.n_cap == 7) {
-      if (a.plain_bins == 1) hipLaunchKernelGGL((k_walk<7, 7, 1, 0>), g, t, dyn, s, a);
-      else if (a.plain_bins == 2) hipLaunchKernelGGL((k_walk<7, 7, 2, 0>), g, t, dyn, s, a);
-      else if (kreg) hipLaunchKernelGGL((k_walk<7, 7, 0, kWalkRegPins>), g, t, dyn, s, a);
-      else hipLaunchKernelGGL((k_walk<7, 7, 0, 0>), g, t, dyn, s, a);
+      if (a.plain_bins == 1) launch_timed(k_walk<7, 7, 1, 0>, g, t, dyn, s, e0, e1, a);
+      else if (a.plain_bins == 2) launch_timed(k_walk<7, 7, 2, 0>, g, t, dyn, s, e0, e1, a);
+      else if (kreg) launch_timed(k_walk<7, 7, 0, kWalkRegPins>, g, t, dyn, s, e0, e1, a);
+      else launch_timed(k_walk<7, 7, 0, 0>, g, t, dyn, s, e0, e1, a);
     } else if (a.n_slew == 8 && a.n_cap == 8) {
-      if (a.plain_bins == 1) hipLaunchKernelGGL((k_walk<8, 8, 1, 0>), g, t, dyn, s, a);
-      else if (a.plain_bins == 2) hipLaunchKernelGGL((k_walk<8, 8, 2, 0>), g, t, dyn, s, a);
-      else if (kreg) hipLaunchKernelGGL((k_walk<8, 8, 0, kWalkRegPins>), g, t, dyn, s, a);
-      else hipLaunchKernelGGL((k_walk<8, 8, 0, 0>), g, t, dyn, s, a);
+      if (a.plain_bins == 1) launch_timed(k_walk<8, 8, 1, 0>, g, t, dyn, s, e0, e1, a);
+      else if (a.plain_bins == 2) launch_timed(k_walk<8, 8, 2, 0>, g, t, dyn, s, e0, e1, a);
+      else if (kreg) launch_timed(k_walk<8, 8, 0, kWalkRegPins>, g, t, dyn, s, e0, e1, a);
+      else launch_timed(k_walk<8, 8, 0, 0>, g, t, dyn, s, e0, e1, a);
     }
     else return hipErrorInvalidValue;
     return hipGetLastError();
@@ -1419,22 +1429,22 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s) {
   if (dyn + pass_static_lds_bytes() > kLdsMax) return hipErrorInvalidValue;
   const dim3 g(grid_blocks), t(kNT);
   if (cells && !diag) {
-    if (a.n_slew == 7) hipLaunchKernelGGL((k_fused<true, false, 5>), g, t, dyn, s, a);
-    else if (a.n_slew == 8) hipLaunchKernelGGL((k_fused<true, false, 6>), g, t, dyn, s, a);
-    else hipLaunchKernelGGL((k_fused<true, false, -1>), g, t, dyn, s, a);
+    if (a.n_slew == 7) launch_timed(k_fused<true, false, 5>, g, t, dyn, s, e0, e1, a);
+    else if (a.n_slew == 8) launch_timed(k_fused<true, false, 6>, g, t, dyn, s, e0, e1, a);
+    else launch_timed(k_fused<true, false, -1>, g, t, dyn, s, e0, e1, a);
   } else if (cells) {
-    hipLaunchKernelGGL((k_fused<true, true, -1>), g, t, dyn, s, a);
+    launch_timed(k_fused<true, true, -1>, g, t, dyn, s, e0, e1, a);
   } else if (!diag) {
-    hipLaunchKernelGGL((k_fused<false, false, -1>), g, t, dyn, s, a);
+    launch_timed(k_fused<false, false, -1>, g, t, dyn, s, e0, e1, a);
   } else {
-    hipLaunchKernelGGL((k_fused<false, true, -1>), g, t, dyn, s, a);
+    launch_timed(k_fused<false, true, -1>, g, t, dyn, s, e0, e1, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_finalize(const FinalArgs &f, hipStream_t s) {
+hipError_t launch_finalize(const FinalArgs &f, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const int grid = (int)((f.C + kFC - 1) / kFC);
-  hipLaunchKernelGGL(k_finalize, dim3(grid), dim3(kFT), 0, s, f);
+  launch_timed(k_finalize, dim3(grid), dim3(kFT), 0, s, e0, e1, f);
   return hipGetLastError();
 }
 

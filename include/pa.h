@@ -64,9 +64,10 @@ typedef struct {
   int32_t grid_blocks;    /* target block count of the fused pass (0 = one 1024-thread block
                              per compute unit);
                              the pass cuts the events into about this many ranges */
-  int32_t time_kernels;   /* 0: no timing; 1: device times of the fused kernel, the finalize
-                             kernel and the whole pass (three events on the stream);
-                             2: the whole pass only (two events, none between the kernels) */
+  int32_t time_kernels;   /* 0: no timing; 1: device times of the fused kernel and of the
+                             finalize kernel (events attached to each kernel's dispatch: the
+                             kernel's own execution) and of the whole pass; 2: the whole pass
+                             only (events recorded before the first kernel and after the last) */
   int32_t fixed_window_cycles; /* 0: density-aware windows (below); n > 0: every gate's
                              windows are n cycles (rounded down to a power of two, at most the
                              chunk) -- the fixed-window layout the paper compares against */

@@ -126,7 +126,8 @@ def test_bad_arguments():
             pa.pa_run(an.ctx, None, torch.empty(t.n_cycles, dtype=torch.uint64, device=dev),
                       torch.empty(t.n_cycles, dtype=torch.uint64, device=dev))
         assert ei.value.code == pa.PA_EINVAL
-        # timing modes: 0..2 only; the pass-only mode fills the whole-pass time alone
+        # timing modes: 0..2 only; the pass-only mode fills the whole-pass time alone; the
+        # per-kernel mode times each kernel's own execution, inside the whole pass
         for mode in (-1, 3):
             with pytest.raises(pa.PaError) as ei:
                 an.set_timing(mode)
@@ -139,7 +140,7 @@ def test_bad_arguments():
         an.set_timing(1)
         an.run(outs)
         km = an.info()["kernel_ms"]
-        assert km[0] > 0.0 and km[1] > 0.0 and abs(km[3] - km[0] - km[1]) < 1e-6
+        assert km[0] > 0.0 and km[1] > 0.0 and km[3] >= km[0] + km[1]
     finally:
         an.close()
     with pytest.raises(pa.PaError) as ei:
