@@ -120,6 +120,28 @@ __device__ __forceinline__ double row_incl_scan(double v) {
   return v;
 }
 
+// The same two scans of 32-bit integers.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, true);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_u32<0x111, 0xf>(v);
+  v += dpp_u32<0x112, 0xf>(v);
+  v += dpp_u32<0x114, 0xf>(v);
+  v += dpp_u32<0x118, 0xf>(v);
+  v += dpp_u32<0x142, 0xa>(v);
+  v += dpp_u32<0x143, 0xc>(v);
+  return v;
+}
+__device__ __forceinline__ uint32_t row_incl_scan_u32(uint32_t v) {
+  v += dpp_u32<0x111, 0xf>(v);
+  v += dpp_u32<0x112, 0xf>(v);
+  v += dpp_u32<0x114, 0xf>(v);
+  v += dpp_u32<0x118, 0xf>(v);
+  return v;
+}
+
 // lane l's double, l wave-uniform
 __device__ __forceinline__ double lane_f64(double v, int l) {
   return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
@@ -658,7 +680,8 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   constexpr int LD = PA_WALK_LEAD;   // groups a load runs ahead of its use
   extern __shared__ __align__(16) unsigned char s_dyn[];
   __shared__ double s_red[kNW][8];
-  __shared__ double s_scan[((kCCMAX + kNT - 1) / kNT) * kNW];
+  __shared__ double s_scan[kNW];
+  __shared__ uint32_t s_redu[kNW];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int b = blockIdx.x;
   const int Cc = a.Cc, nthr = a.n_thr;
@@ -1044,83 +1067,93 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
   }
+  // the walk's energies, summed within the wave as soon as it ends its walk
+  // (a wave that ends early does it while the others still walk)
+  {
+    const double t0 = wave_incl_scan(e_int), t1 = wave_incl_scan(e_sw), t2 = wave_incl_scan(e_gl);
+    if (lane == 63) {
+      s_red[wid][0] = t0;
+      s_red[wid][1] = t1;
+      s_red[wid][2] = t2;
+    }
+  }
   __syncthreads();
 
-  // ---- the block's bins: the leakage changes' in-chunk prefix, then its own
-  // slots.  Thread t owns bins t, t + kNT, ..., so the stores coalesce; the
-  // prefix runs over the bins in cycle order: a DPP scan within every wave,
-  // then the waves' totals, one row of bins after the other.
-  constexpr int PER = (kCCMAX + kNT - 1) / kNT;
-  double dsum = 0.0, lkc = 0.0, wsum = 0.0;
-  unsigned long long ngl = 0;
+  // ---- the block's bins: thread t owns bins 2t and 2t + 1.  The leakage
+  // changes' in-chunk prefix: a DPP scan of the threads' pairs within every
+  // wave, then the waves' totals over one row of 16 lanes; every thread
+  // stores its two bins with one 16-byte store per array.
+  static_assert(kCCMAX <= 2 * kNT && kNW == 16, "two bins per thread; one row of lanes for the waves");
+  double xs = 0.0;   // the thread's share of the leakage part: changes' energy to t_max plus its bins' sum
+  uint32_t ngl = 0;  // glitches in the thread's bins
+  double dsum = 0.0;
   {
-    double loc[PER], incl[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int c = u * kNT + tid;
-      loc[u] = (has_range && c < ncyc) ? L.bins[c].d : 0.0;
-      incl[u] = wave_incl_scan(loc[u]);
-      if (lane == 63) s_scan[u * kNW + wid] = incl[u];
-    }
+    const int c0 = 2 * tid;
+    const bool in0 = has_range && c0 < ncyc, in1 = has_range && c0 + 1 < ncyc;
+    const double d0 = in0 ? L.bins[c0].d : 0.0, d1 = in1 ? L.bins[c0 + 1].d : 0.0;
+    const double incl = wave_incl_scan(d0 + d1);  // the wave's changes up to bin 2t + 1
+    if (lane == 63) s_scan[wid] = incl;
+    const double excl = dpp_f64<0x138, 0xf>(incl);  // wave_shr:1, lane 0 gets 0: up to bin 2t - 1
     __syncthreads();
+    const double tw = row_incl_scan(lane < kNW ? s_scan[lane] : 0.0);
+    const double wb = wid > 0 ? lane_f64(tw, wid - 1) : 0.0;  // changes of the earlier waves' bins
+    dsum = lane_f64(tw, kNW - 1);
+    // the bins' own changes count from the bin start; the bin corrects for their times
+    const double r0 = (wb + excl) + d0, r1 = r0 + d1;
+    double v0 = 0.0, v1 = 0.0;
+    unsigned long long n0 = 0ull, n1 = 0ull;
+    if (in0) {
+      const double blen = (last_chunk && c0 == (int)lastc) ? (double)a.last_len : Td;
+      const double w = L.bins[c0].w;
+      const uint32_t g = L.bins[c0].g;
+      v0 = w + r0 * blen * tick;
+      xs += w + d0 * (tail - Td * (double)c0) * tick;
+      n0 = (unsigned long long)L.bins[c0].n | ((unsigned long long)g << 32);
+      ngl += g;
+    }
+    if (in1) {
+      const double blen = (last_chunk && c0 + 1 == (int)lastc) ? (double)a.last_len : Td;
+      const double w = L.bins[c0 + 1].w;
+      const uint32_t g = L.bins[c0 + 1].g;
+      v1 = w + r1 * blen * tick;
+      xs += w + d1 * (tail - Td * (double)(c0 + 1)) * tick;
+      n1 = (unsigned long long)L.bins[c0 + 1].n | ((unsigned long long)g << 32);
+      ngl += g;
+    }
     double *ow = a.blk_wave + (size_t)b * Cc;
     unsigned long long *oc = a.blk_cnt + (size_t)b * Cc;
-    // the waves' totals of row u sit in lanes 16 u .. 16 u + 15 (one row of
-    // lanes per row of bins): a scan within the rows of lanes gives every
-    // wave the changes of the waves before it and every row's total
-    static_assert(kNW == 16 && PER <= 4, "one row of 16 lanes per row of bins");
-    const double tw = row_incl_scan(lane < PER * kNW ? s_scan[lane] : 0.0);
-    double before = 0.0;  // changes of all earlier rows of bins
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const double row = lane_f64(tw, u * kNW + kNW - 1);
-      const double wb = wid > 0 ? lane_f64(tw, u * kNW + wid - 1) : 0.0;
-      const int c = u * kNT + tid;
-      if (c < Cc) {
-        double v = 0.0;
-        unsigned long long cn = 0ull;
-        if (has_range && c < ncyc) {
-          // the bin's own changes count from the bin start; the bin corrects for their times
-          const double run = before + wb + incl[u];
-          const double blen = (last_chunk && c == (int)lastc) ? (double)a.last_len : Td;
-          const double w = L.bins[c].w;
-          wsum += w;
-          v = w + run * blen * tick;
-          lkc += loc[u] * (tail - Td * (double)c);
-          const uint32_t ng = L.bins[c].g;
-          cn = (unsigned long long)L.bins[c].n | ((unsigned long long)ng << 32);
-          ngl += ng;
-        }
-        ow[c] = v;
-        oc[c] = cn;
-      }
-      before += row;
+    if (c0 + 1 < Cc) {  // Cc is a power of two, so here Cc is even and both stores are 16-byte aligned
+      *reinterpret_cast<double2 *>(ow + c0) = make_double2(v0, v1);
+      *reinterpret_cast<ulonglong2 *>(oc + c0) = make_ulonglong2(n0, n1);
+    } else if (c0 < Cc) {
+      ow[c0] = v0;
+      oc[c0] = n0;
     }
-    dsum = before;
   }
 
-  // ---- block totals: DPP sums within the waves, then over the waves in order
+  // ---- block totals: the leakage part and the glitches within the waves,
+  // then every quantity over the waves with one row scan
   {
-    // leakage: the changes' energy to t_max from their bins' starts, minus
-    // their times in their bins (the bins' sum less the dynamic energies)
-    double v[5] = {e_int, e_sw, e_gl, lkc * tick - ((e_int + e_sw + e_gl) - wsum), (double)ngl};
-#pragma unroll
-    for (int u = 0; u < 5; ++u) v[u] = wave_incl_scan(v[u]);
+    const double xw = wave_incl_scan(xs);
+    const uint32_t gw = wave_incl_scan_u32(ngl);
     if (lane == 63) {
-#pragma unroll
-      for (int u = 0; u < 5; ++u) s_red[wid][u] = v[u];
+      s_red[wid][3] = xw;
+      s_redu[wid] = gw;
     }
     __syncthreads();
-    if (tid < 8) {
-      double t = 0.0;
-      if (tid < 4) {
-        for (int w = 0; w < kNW; ++w) t += s_red[w][tid];
-      } else if (tid == 5) {
-        t = dsum;
-      } else if (tid == 6) {
-        for (int w = 0; w < kNW; ++w) t += s_red[w][4];
+    if (wid == 0) {
+      // row q of the wave's lanes holds the waves' totals of quantity q: e_int, e_sw, e_gl, leakage part
+      const double t = row_incl_scan(s_red[lane & 15][lane >> 4]);
+      const uint32_t gt = row_incl_scan_u32(lane < kNW ? s_redu[lane] : 0u);
+      const double T0 = lane_f64(t, 15), T1 = lane_f64(t, 31), T2 = lane_f64(t, 47), X = lane_f64(t, 63);
+      const uint32_t G = __builtin_amdgcn_readlane(gt, 15);
+      // the leakage: the changes' energy to t_max from their bins' starts, minus their times
+      // in their bins (the bins' sum less the dynamic energies)
+      if (lane < 8) {
+        const double val = lane == 0 ? T0 : lane == 1 ? T1 : lane == 2 ? T2 : lane == 3 ? X - ((T0 + T1) + T2)
+                         : lane == 5 ? dsum : lane == 6 ? (double)G : 0.0;
+        a.blk_part[(size_t)b * 8 + lane] = val;
       }
-      a.blk_part[(size_t)b * 8 + tid] = t;
     }
   }
 }
