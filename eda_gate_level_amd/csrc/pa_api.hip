@@ -471,17 +471,19 @@ static constexpr double kWindowEvents = PA_WINDOW_EVENTS;
 #define PA_WALK_COST_IN 10
 #endif
 #ifndef PA_WALK_COST_OUT
-#define PA_WALK_COST_OUT 3
+#define PA_WALK_COST_OUT 4
 #endif
 #ifndef PA_WALK_COST_HEAD
-#define PA_WALK_COST_HEAD 5
+#define PA_WALK_COST_HEAD 4
 #endif
 // The walk kernel's relative costs of an input-pin event (three LDS atomics,
 // four LUT reads and the table reads; a gate with one or two inputs costs 2
 // or 1 less, one with five or more 1 more), an output-pin event (two
 // atomics) and a window's set-up: a least-squares fit of the blocks' walk
 // times to their event and window counts on the 10M-event, skewed,
-// glitch-heavy and 200M-event workloads
+// glitch-heavy and 200M-event workloads, then the output and window weights
+// moved from 3 and 5 to 4 and 4 by timing weight variants on the same
+// workloads (the skewed one 1.9% faster, the others unchanged)
 static constexpr uint32_t kWalkCostIn = PA_WALK_COST_IN, kWalkCostOut = PA_WALK_COST_OUT,
                           kWalkCostHead = PA_WALK_COST_HEAD;
 
@@ -707,7 +709,7 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
     HIPCHK(ls.wlane.ensure(sizeof(uint2) * W));
     HIPCHK(ls.phase.ensure(sizeof(uint2) * pa::phase_plan_entries(W, nr)));
     HIPCHK(ls.wave_len.ensure(sizeof(uint32_t) * (size_t)nr * NW));
-    // the walk kernel's slots of an input phase cost about 3.3 times those of
+    // the walk kernel's slots of an input phase cost about 2.5 times those of
     // an output phase (no table reads, leakage or pin records there)
     const bool walk = v.walk_lut > 0;
     HIPCHK(pa::launch_phase_plan(nr, ls.bwin.as<uint32_t>(), ls.worder.as<uint32_t>(), ls.wkey1.as<uint64_t>(),
