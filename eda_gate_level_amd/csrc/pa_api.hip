@@ -179,12 +179,17 @@ struct Events {
   bool compact_ok = false;         // the chunk leaves the compact key its bits
   DBuf ckey, cslew;
   uint32_t tbc = 0, ck = 0;
+  // per-event outputs from the walk kernel: every event's slot by its caller
+  // index, and the kernel's 16-bit values in stream order; built by the first
+  // pa_run that asks for per-event outputs, dropped by the next load
+  DBuf slot_of, evs;
+  bool ev_map = false;
   int32_t n_ranges = 0, grid = 1;
   DBuf blk_wave, blk_cnt, blk_part, res;
   int64_t bytes() const {
     return (int64_t)(key.bytes + slew.bytes + orig.bytes + pin_init.bytes + rstart.bytes + rchunk.bytes +
                      chunk_blk.bytes + wdesc.bytes + wlen.bytes + l0.bytes + lplan.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
-                     res.bytes + blk_lut.bytes + ckey.bytes + cslew.bytes);
+                     res.bytes + blk_lut.bytes + ckey.bytes + cslew.bytes + slot_of.bytes + evs.bytes);
   }
 };
 
@@ -736,6 +741,7 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
     return fail(PA_EINVAL, "pa_load_events: the lane streams need %llu slots (2^31 allowed)",
                 (unsigned long long)slots);
   v.slots = (int64_t)slots;
+  v.ev_map = false;  // the slots moved: the per-event map is built again when asked for
   HIPCHK(hipMemcpyAsync(v.wdesc.p, wd.data(), sizeof(uint2) * wd.size(), hipMemcpyHostToDevice, s));
   // ---- the streams: keys and slews, the caller's index of every event; empty slots hold the pad key
   const int64_t Sa = (int64_t)slots + 2;  // two zeroed entries past the streams
@@ -1067,6 +1073,15 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   a.gate_J = gate_J;
   a.gate_perm = d.perm.as<int32_t>();
   a.evt_state = evt_state_before;
+  // per-event outputs from the walk kernel (in stream order, then into the
+  // caller's order) once the slot map is built; else the general kernel
+  const bool ev_walk = (evt_glitch || evt_state_before) && !gate_J && v.walk_lut > 0 && c->tun.plain_bins == 0 &&
+                       v.ev_map;
+  if (ev_walk) {
+    a.evt_glitch = nullptr;
+    a.evt_state = nullptr;
+    a.evs = v.evs.as<uint32_t>();
+  }
 
   pa::FinalArgs f{};
   f.C = v.C;
@@ -1094,6 +1109,8 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   // whole pass by events recorded before the first and after the last
   if (timed) HIPCHK(hipEventRecord(c->tev[0], s));
   hipError_t e1 = per_kernel ? pa::launch_pass(a, v.grid, s, c->tev[2], c->tev[3]) : pa::launch_pass(a, v.grid, s);
+  if (e1 == hipSuccess && ev_walk)
+    e1 = pa::launch_event_out(v.E, v.slot_of.as<uint32_t>(), v.evs.as<uint32_t>(), evt_glitch, evt_state_before, s);
   if (e1 == hipSuccess)
     e1 = per_kernel ? pa::launch_finalize(f, s, c->tev[4], c->tev[5]) : pa::launch_finalize(f, s);
   if (timed && e1 == hipSuccess) e1 = hipEventRecord(c->tev[1], s);
@@ -1132,6 +1149,16 @@ int pa_run(pa_ctx *c, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint
   if (!out || !wave_J || !cyc_events || !cyc_glitches) return fail(PA_EINVAL, "pa_run: NULL output");
   BudgetScope bs(&c->mem);
   HIPCHK(hipSetDevice(c->device));
+  Events &v = c->ev;
+  if ((evt_glitch || evt_state_before) && v.walk_lut > 0 && c->tun.plain_bins == 0 && v.E > 0 && !v.ev_map) {
+    // the walk kernel's per-event outputs: every event's slot (the inverse of the
+    // stream's caller-index array), and room for the values in stream order
+    const int64_t Sa = v.slots + 2;
+    HIPCHK(v.slot_of.ensure(sizeof(uint32_t) * (size_t)v.E));
+    HIPCHK(v.evs.ensure(sizeof(uint32_t) * (size_t)((Sa + 1) / 2)));
+    HIPCHK(pa::launch_slot_of(Sa, v.orig.as<uint32_t>(), v.slot_of.as<uint32_t>(), c->stream));
+    v.ev_map = true;
+  }
   return run_pass(c, loaded_scratch(c->ev), out, wave_J, cyc_events, cyc_glitches, evt_glitch, evt_state_before,
                   nullptr);
 }

@@ -106,6 +106,9 @@ struct PassArgs {
   const uint32_t *cslew;
   uint32_t tbc, ck;
   int32_t plain_bins;         // timing aid: 1 plain adds, 2 plain stores to the bins (results wrong)
+  // the walk kernel's per-event outputs, in stream order: 16 bits a slot (state before | glitch << 8),
+  // two slots per 32-bit word (null: none)
+  uint32_t *evs;
   // per-block results, reduced by the finalize kernel
   double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
   unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32
@@ -142,6 +145,12 @@ struct FinalArgs {
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s, hipEvent_t e0 = nullptr,
                        hipEvent_t e1 = nullptr);
 hipError_t launch_finalize(const FinalArgs &a, hipStream_t s, hipEvent_t e0 = nullptr, hipEvent_t e1 = nullptr);
+// Per-event outputs of the walk kernel: every event's slot by its caller
+// index (n slots of the caller-index array); the 16-bit slot values into
+// the caller's order (either output may be null).
+hipError_t launch_slot_of(int64_t n, const uint32_t *orig, uint32_t *slot_of, hipStream_t s);
+hipError_t launch_event_out(int64_t E, const uint32_t *slot_of, const uint32_t *evs, uint8_t *glitch,
+                            uint8_t *state, hipStream_t s);
 // Per block, the cells whose LUTs it copies into the LDS left over by its bins,
 // pin records and cell tables (lut_lds doubles, from pass_lut_lds_doubles): 64
 // windows sampled evenly over the block's window range [bwin[b], bwin[b+1])

@@ -667,7 +667,7 @@ __device__ __forceinline__ void bin_add(P *p, T v) {
   else __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
-template <int NS, int NC, int PLAIN, int KREG>
+template <int NS, int NC, int PLAIN, int KREG, bool EV>
 __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
   constexpr int NIN = NS - 2;  // inner slew-axis points: the segment is the count at or below the slew
 #ifndef PA_WALK_GROUP
@@ -853,7 +853,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     // phases so that both events' table reads are in flight together and
     // their arithmetic interleaves; an empty slot toggles nothing, so its
     // leakage change is zero, and adds nothing
-    auto pair_in = [&](const u32x2 &K, const u32x2 &SW) {
+    auto pair_in = [&](const u32x2 &K, const u32x2 &SW, uint32_t &ev) {
       bool real[2], glitch[2];
       uint32_t tic[2], cyc[2], cl[2], lo[2], li[2], nseg[2];
       float sl[2];
@@ -884,6 +884,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
         ptic = tic[r];
         const uint32_t Sm = St;
         S ^= bit;
+        if constexpr (EV) ev |= (Sm | (glitch[r] ? 256u : 0u)) << (16 * r);
         uint32_t n = 0;
 #pragma unroll
         for (int i = 0; i < NIN; ++i) n += sl[r] >= th[i] ? 1u : 0u;
@@ -986,7 +987,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     // scaled by r_gl when the pin already switched in this cycle (Eq. 2,
     // Fig. 7); the window's only pin is the output, so its previous event is
     // the lane's previous event.  An empty slot (value bit 0) adds nothing.
-    auto pair_out = [&](const u32x2 &K, const u32x2 &SW) {
+    auto pair_out = [&](const u32x2 &K, const u32x2 &SW, uint32_t &ev) {
       bool real[2], glitch[2];
       uint32_t tic[2], cyc[2];
       float sl[2];
@@ -1001,6 +1002,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
         tic[r] = (k >> ck) & tmask;
         cyc[r] = k >> tsh;
         glitch[r] = real[r] && cyc[r] == pcyc;
+        if constexpr (EV) ev |= (glitch[r] ? 256u : 0u) << (16 * r);  // an output event's state is 0
         E[r] = (sw >> 31) ? esw : 0.0;
         pcyc = cyc[r];
       }
@@ -1060,8 +1062,11 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
             header(k, sw, own);
             continue;
           }
-          if (out_phase) pair_out(k, sw);
-          else pair_in(k, sw);
+          uint32_t ev = 0;  // the pair's per-event outputs: state before | glitch << 8, per slot
+          if (out_phase) pair_out(k, sw, ev);
+          else pair_in(k, sw, ev);
+          // in stream order: the wave's 64 lanes store 256 contiguous bytes
+          if constexpr (EV) a.evs[((uint32_t)base >> 1) + (uint32_t)(pg + i) * 64u + lane] = ev;
         }
       }
     }
@@ -1441,15 +1446,19 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s, hipEve
     const dim3 g(grid_blocks), t(kNT);
     const bool kreg = a.kmax <= kWalkRegPins;
     if (a.n_slew == 7 && a.n_cap == 7) {
-      if (a.plain_bins == 1) launch_timed(k_walk<7, 7, 1, 0>, g, t, dyn, s, e0, e1, a);
-      else if (a.plain_bins == 2) launch_timed(k_walk<7, 7, 2, 0>, g, t, dyn, s, e0, e1, a);
-      else if (kreg) launch_timed(k_walk<7, 7, 0, kWalkRegPins>, g, t, dyn, s, e0, e1, a);
-      else launch_timed(k_walk<7, 7, 0, 0>, g, t, dyn, s, e0, e1, a);
+      if (a.plain_bins == 1) launch_timed(k_walk<7, 7, 1, 0, false>, g, t, dyn, s, e0, e1, a);
+      else if (a.plain_bins == 2) launch_timed(k_walk<7, 7, 2, 0, false>, g, t, dyn, s, e0, e1, a);
+      else if (a.evs && kreg) launch_timed(k_walk<7, 7, 0, kWalkRegPins, true>, g, t, dyn, s, e0, e1, a);
+      else if (a.evs) launch_timed(k_walk<7, 7, 0, 0, true>, g, t, dyn, s, e0, e1, a);
+      else if (kreg) launch_timed(k_walk<7, 7, 0, kWalkRegPins, false>, g, t, dyn, s, e0, e1, a);
+      else launch_timed(k_walk<7, 7, 0, 0, false>, g, t, dyn, s, e0, e1, a);
     } else if (a.n_slew == 8 && a.n_cap == 8) {
-      if (a.plain_bins == 1) launch_timed(k_walk<8, 8, 1, 0>, g, t, dyn, s, e0, e1, a);
-      else if (a.plain_bins == 2) launch_timed(k_walk<8, 8, 2, 0>, g, t, dyn, s, e0, e1, a);
-      else if (kreg) launch_timed(k_walk<8, 8, 0, kWalkRegPins>, g, t, dyn, s, e0, e1, a);
-      else launch_timed(k_walk<8, 8, 0, 0>, g, t, dyn, s, e0, e1, a);
+      if (a.plain_bins == 1) launch_timed(k_walk<8, 8, 1, 0, false>, g, t, dyn, s, e0, e1, a);
+      else if (a.plain_bins == 2) launch_timed(k_walk<8, 8, 2, 0, false>, g, t, dyn, s, e0, e1, a);
+      else if (a.evs && kreg) launch_timed(k_walk<8, 8, 0, kWalkRegPins, true>, g, t, dyn, s, e0, e1, a);
+      else if (a.evs) launch_timed(k_walk<8, 8, 0, 0, true>, g, t, dyn, s, e0, e1, a);
+      else if (kreg) launch_timed(k_walk<8, 8, 0, kWalkRegPins, false>, g, t, dyn, s, e0, e1, a);
+      else launch_timed(k_walk<8, 8, 0, 0, false>, g, t, dyn, s, e0, e1, a);
     }
     else return hipErrorInvalidValue;
     return hipGetLastError();
@@ -1472,6 +1481,40 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s, hipEve
   } else {
     launch_timed(k_fused<false, true, -1>, g, t, dyn, s, e0, e1, a);
   }
+  return hipGetLastError();
+}
+
+// Every laid-out event's slot, by the caller's event index (the inverse of
+// the stream's caller-index array; empty slots hold ~0 there).
+__global__ void k_slot_of(int64_t n, const uint32_t *orig, uint32_t *slot_of) {
+  const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (x >= n) return;
+  const uint32_t o = orig[x];
+  if (o != ~0u) slot_of[o] = (uint32_t)x;
+}
+
+// The walk's per-event outputs (state before | glitch << 8, 16 bits a slot,
+// in stream order) into the caller's event order.
+__global__ void k_event_out(int64_t E, const uint32_t *slot_of, const uint16_t *evs, uint8_t *glitch,
+                            uint8_t *state) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= E) return;
+  const uint32_t v = evs[slot_of[e]];
+  if (glitch) glitch[e] = (uint8_t)(v >> 8);
+  if (state) state[e] = (uint8_t)(v & 0xFFu);
+}
+
+hipError_t launch_slot_of(int64_t n, const uint32_t *orig, uint32_t *slot_of, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_slot_of, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, n, orig, slot_of);
+  return hipGetLastError();
+}
+
+hipError_t launch_event_out(int64_t E, const uint32_t *slot_of, const uint32_t *evs, uint8_t *glitch,
+                            uint8_t *state, hipStream_t s) {
+  if (E <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_event_out, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, s, E, slot_of,
+                     reinterpret_cast<const uint16_t *>(evs), glitch, state);
   return hipGetLastError();
 }
 

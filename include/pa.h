@@ -164,7 +164,12 @@ typedef struct {
  *   evt_glitch[E]  device or NULL: 1 if the event is a glitch (caller's CSR order)
  *   evt_state_before[E] device or NULL: S(t-) of input-pin events, 0 for output
  *                  events (caller's CSR order)
- * C = n_cycles = ceil(t_max / t_clk).  The output arrays must not overlap. */
+ * C = n_cycles = ceil(t_max / t_clk).  The output arrays must not overlap.
+ * With per-event outputs and the walk kernel (pa_info.walk_kernel), the kernel
+ * writes them in its stream's order and a small kernel moves them into the
+ * caller's order through every event's slot; the first such call builds that
+ * map (4 bytes per event and 2 per stream slot of device memory, kept until
+ * the next pa_load_events). */
 int pa_run(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
            uint8_t *evt_glitch, uint8_t *evt_state_before);
 
@@ -182,7 +187,9 @@ int pa_run(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, ui
  * time on one device (two contexts on two streams, or two threads) race and
  * give wrong results; calls that follow one another are safe (every call
  * rewrites all of the array it reads).  PA_EHIP if the array's device
- * address could not be looked up when the context was created. */
+ * address could not be looked up when the context was created.  Per-event
+ * outputs take the walk kernel only when a pa_run with per-event outputs
+ * has built its map for the loaded events; otherwise the general kernel. */
 #define PA_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
 int pa_run_noalloc(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
                    uint8_t *evt_glitch, uint8_t *evt_state_before);

@@ -200,17 +200,18 @@ def test_walk_contention_small(m):
     pu.assert_parity(_walk_run(w.design, w.trace, label), _oracle(w.design, w.trace), per_event=False, label=label)
 
 
-def test_walk_matches_the_per_event_kernel():
-    """The walk kernel and the per-event kernel agree: integer outputs bit for
+def test_walk_matches_the_general_kernel():
+    """The walk kernel and the general kernel agree: integer outputs bit for
     bit, energies and bins to rounding (they sum in different orders).  The
     walk kernel takes the leakage's in-bin time corrections from the bins'
     sum less the dynamic energies, so its leakage total carries a rounding
     error of about 1e-16 times the dynamic energy: the bar for the leakage
     is 1e-15 of the dynamic energy, not of the leakage itself."""
     d, t = _case(seed=16, G=1500, C=100, rate=0.3, ks=(1, 2, 5), cpk=1)
-    _print_case("walk vs per-event kernel")
-    a = _walk_run(d, t, "walk vs per-event")
-    b = pu.gpu_run(d, t, per_event=True)
+    _print_case("walk vs general kernel")
+    a = _walk_run(d, t, "walk vs general")
+    b = pu.gpu_run(d, t, per_event=True, lut_lds_kib=-1)  # no LUT copies: the general kernel
+    assert b["_info"]["walk_kernel"] == 0
     for key in ("n_events", "n_glitches"):
         assert a[key] == b[key], key
     assert np.array_equal(a["cyc_events"], b["cyc_events"])
@@ -221,3 +222,25 @@ def test_walk_matches_the_per_event_kernel():
     assert abs(a["e_leak_J"] - b["e_leak_J"]) <= 1e-15 * e_dyn, (a["e_leak_J"], b["e_leak_J"], e_dyn)
     assert pu.rel_err(a["p_leak_W"], b["p_leak_W"]) <= 1e-15 * e_dyn / b["e_leak_J"] + 1e-15
     np.testing.assert_allclose(a["wave_J"], b["wave_J"], rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("case", [dict(seed=1), dict(seed=2, ks=(1, 5), cpk=1, G=60, rate=0.2),
+                                  dict(seed=3, collide=50, rate=0.8, G=120), dict(seed=14, ks=(2, 3), G=150, n_axis=8)],
+                         ids=["k1-4", "k1-5", "collide", "8x8"])
+@pytest.mark.parametrize("chunk", [0, 1])
+def test_walk_per_event_outputs(case, chunk):
+    """Per-event outputs from the walk kernel (written in stream order, moved
+    into the caller's order through every event's slot): the glitch flags and
+    the states before every event bit for bit against the oracle and against
+    the general kernel, with every total, bin and count."""
+    d, t = _case(**case)
+    label = f"walk per-event {case} chunk {chunk}"
+    _print_case(label)
+    g = pu.gpu_run(d, t, per_event=True, chunk_cycles=chunk)
+    assert g["_info"]["walk_kernel"] == 1, label
+    import oracle
+
+    pu.assert_parity(g, oracle.run(d, t), per_event=True, label=label)
+    ref = pu.gpu_run(d, t, per_event=True, chunk_cycles=chunk, lut_lds_kib=-1)
+    np.testing.assert_array_equal(g["evt_glitch"], ref["evt_glitch"])
+    np.testing.assert_array_equal(g["evt_state_before"], ref["evt_state_before"])
