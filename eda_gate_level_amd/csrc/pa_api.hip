@@ -763,8 +763,9 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
                               v.ckey.as<uint32_t>(), v.cslew.as<uint32_t>(), s));
     const uint32_t hdr = ((1u << v.tbc) - 1u) << v.ck;
     HIPCHK(pa::launch_headers(W, ls.wlane.as<uint2>(), v.wdesc.as<uint2>(), ls.ws.as<uint32_t>(),
-                              ls.skey.as<uint64_t>(), d.gate_rec.as<uint4>(), v.gb, pa::out_code(v.pb), hdr,
-                              1u << (v.tbc + v.ck), v.ckey.as<uint32_t>(), v.cslew.as<uint32_t>(), s));
+                              ls.skey.as<uint64_t>(), d.gate_rec.as<uint4>(), d.perm.as<int32_t>(), v.gb,
+                              pa::out_code(v.pb), hdr, 1u << (v.tbc + v.ck), v.ckey.as<uint32_t>(),
+                              v.cslew.as<uint32_t>(), v.orig.as<uint32_t>(), s));
   }
   // the cells whose LUTs every block copies into its spare LDS
   v.lut_lds = pa::pass_lut_lds_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax);
@@ -1077,6 +1078,9 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   // caller's order) once the slot map is built; else the general kernel
   const bool ev_walk = (evt_glitch || evt_state_before) && !gate_J && v.walk_lut > 0 && c->tun.plain_bins == 0 &&
                        v.ev_map;
+  // per-gate rows from the walk kernel: every window's energies and leakage
+  // added to its gate's row when the window ends
+  a.gate_walk = (gate_J && !evt_glitch && !evt_state_before && v.walk_lut > 0 && c->tun.plain_bins == 0) ? 1 : 0;
   if (ev_walk) {
     a.evt_glitch = nullptr;
     a.evt_state = nullptr;

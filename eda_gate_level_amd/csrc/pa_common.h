@@ -63,7 +63,8 @@ struct PassArgs {
   // events
   const uint64_t *key;
   const float *slew;
-  const uint32_t *orig;    // caller's CSR index of each laid-out event (~0 in empty slots)
+  const uint32_t *orig;    // caller's CSR index of each laid-out event (~0 in empty slots; at a window's
+                           // header, with the walk kernel: its gate in the caller's order | 1 << 31)
   uint64_t pad_key;        // key of an empty slot (no event has it)
   const uint2 *wdesc;      // [n_ranges][waves] every wave's (first slot, events per lane)
   const uint32_t *rchunk;  // [n_ranges] chunk of each range
@@ -109,6 +110,7 @@ struct PassArgs {
   // the walk kernel's per-event outputs, in stream order: 16 bits a slot (state before | glitch << 8),
   // two slots per 32-bit word (null: none)
   uint32_t *evs;
+  int32_t gate_walk;          // 1: the walk kernel adds each window's energies to its gate's row of gate_J
   // per-block results, reduced by the finalize kernel
   double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
   unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32

@@ -88,13 +88,15 @@ size_t phase_plan_entries(uint32_t W, int32_t nr);
 hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint64_t *wkey,
                              const uint32_t *wlen, uint32_t hp, uint32_t w_in, uint32_t w_out, uint2 *ph,
                              uint2 *wlane, uint32_t *wave_len, hipStream_t s);
-// the walk kernel's 8-byte-slot stream from the 16-byte one, then every window's header pair
+// the walk kernel's 8-byte-slot stream from the 16-byte one, then every window's header pair (and
+// the window's gate, caller's order, flagged by the high bit, in the 16-byte stream's caller-index slot
+// of the header: no event is there)
 hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,
                           uint32_t tb, uint32_t gb, uint32_t tbc, uint32_t ck, uint32_t *ckey, uint32_t *cslew,
                           hipStream_t s);
 hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
-                          const uint4 *gate_rec, uint32_t gb, uint32_t outc, uint32_t hdr, uint32_t out_bit,
-                          uint32_t *ckey, uint32_t *cslew, hipStream_t s);
+                          const uint4 *gate_rec, const int32_t *perm, uint32_t gb, uint32_t outc, uint32_t hdr,
+                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig, hipStream_t s);
 hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
                           const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
                           uint64_t *key, float *slew, uint32_t *orig, hipStream_t s);

@@ -506,8 +506,8 @@ __global__ void k_compact(int64_t n, const uint64_t *key, const float *slew, uin
 // 20 | start state << 24 for an input window, 0 for an output window), slews
 // the gate's load (fp64 bits, low word first).  hdr has an all-ones tic field.
 __global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
-                          const uint4 *gate_rec, uint32_t gb, uint32_t outc, uint32_t hdr, uint32_t out_bit,
-                          uint32_t *ckey, uint32_t *cslew) {
+                          const uint4 *gate_rec, const int32_t *perm, uint32_t gb, uint32_t outc, uint32_t hdr,
+                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig) {
   for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < W; w += (int64_t)gridDim.x * blockDim.x) {
     const uint2 wl = wlane[w];
     const uint32_t j = wl.y - 2u;  // the header pair: an even slot of the lane's stream
@@ -521,6 +521,7 @@ __global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, co
     ckey[y + 1] = out ? 0u : ((r.z & 0xFFFFFu) | ((r.z >> 24) << 20) | ((hw & 0xFFu) << 24));
     cslew[y] = r.x;
     cslew[y + 1] = r.y;
+    orig[y] = 0x80000000u | (uint32_t)perm[g];  // the window's gate (caller's order), flagged: no event
   }
 }
 
@@ -767,11 +768,11 @@ hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *w
   return hipGetLastError();
 }
 hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
-                          const uint4 *gate_rec, uint32_t gb, uint32_t outc, uint32_t hdr, uint32_t out_bit,
-                          uint32_t *ckey, uint32_t *cslew, hipStream_t s) {
+                          const uint4 *gate_rec, const int32_t *perm, uint32_t gb, uint32_t outc, uint32_t hdr,
+                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig, hipStream_t s) {
   if (W == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_headers, dim3(grid_for(W)), dim3(kLT), 0, s, W, wlane, wdesc, ws, skey, gate_rec, gb, outc, hdr,
-                     out_bit, ckey, cslew);
+  hipLaunchKernelGGL(k_headers, dim3(grid_for(W)), dim3(kLT), 0, s, W, wlane, wdesc, ws, skey, gate_rec, perm, gb, outc,
+                     hdr, out_bit, ckey, cslew, orig);
   return hipGetLastError();
 }
 hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,

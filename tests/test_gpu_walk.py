@@ -244,3 +244,44 @@ def test_walk_per_event_outputs(case, chunk):
     ref = pu.gpu_run(d, t, per_event=True, chunk_cycles=chunk, lut_lds_kib=-1)
     np.testing.assert_array_equal(g["evt_glitch"], ref["evt_glitch"])
     np.testing.assert_array_equal(g["evt_state_before"], ref["evt_state_before"])
+
+
+def _walk_gates(d, t, **kw):
+    import eda_gate_level_amd as pa
+
+    an = pa.PowerAnalysis(**kw)
+    try:
+        an.load(d, t)
+        outs = an.alloc_outputs(per_gate=True)
+        r = an.run(outs)
+        g = dict(r["totals"])
+        g["gate_J"] = r["gate_J"][:d.n_gates].cpu().numpy()
+        g["wave_J"] = r["wave_J"].cpu().numpy()
+        g["cyc_events"] = r["cyc_events"].cpu().numpy().astype(np.uint64)
+        g["cyc_glitches"] = r["cyc_glitches"].cpu().numpy().astype(np.uint64)
+        g["_info"] = an.info()
+        return g
+    finally:
+        an.close()
+
+
+@pytest.mark.parametrize("case", [dict(seed=1), dict(seed=2, ks=(1, 5), cpk=1, G=60, rate=0.2),
+                                  dict(seed=4, collide=1000, rate=0.6, G=80), dict(seed=14, ks=(2, 3), G=150, n_axis=8)],
+                         ids=["k1-4", "k1-5", "cycle-edges", "8x8"])
+@pytest.mark.parametrize("chunk", [0, 3])
+def test_walk_per_gate_rows(case, chunk):
+    """Per-gate rows from the walk kernel (each window's energies and the
+    leakage of its power changes to t_max, added to its gate's row when the
+    window ends): every entry within 1e-9 of the oracle's per-gate energies,
+    the rows adding up to the totals, and every total, bin and count."""
+    import oracle
+    from test_gpu_gates import _assert_gates
+
+    d, t = _case(**case)
+    label = f"walk per-gate {case} chunk {chunk}"
+    _print_case(label)
+    g = _walk_gates(d, t, chunk_cycles=chunk)
+    assert g["_info"]["walk_kernel"] == 1, label
+    o = oracle.run(d, t, per_event=False, per_gate=True)
+    pu.assert_parity(g, o, per_event=False, label=label)
+    _assert_gates(g, o, label)
