@@ -198,10 +198,12 @@ int pa_run_noalloc(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_ev
  * hotspots by (its spatial-accuracy evaluation, Fig. 10, Table 3):
  *   gate_J[G][4]   device: per gate (caller's order) the internal, switching,
  *                  glitch and leakage energy over [0, t_max), J; overwritten.
- * The gate rows add up to the totals (up to fp64 summation order).  This
- * pass takes the diagnostic kernel variant and adds the per-gate energies
- * with device atomics, so its row sums may differ between runs in the last
- * bits; the totals and the waveform do not. */
+ * The gate rows add up to the totals (up to fp64 summation order).  With
+ * the walk kernel (pa_info.walk_kernel) every window's energies and the
+ * leakage of its power changes go to its gate's row when the window ends;
+ * otherwise the diagnostic variant of the general kernel adds them event by
+ * event.  Either way with device atomics, so the rows may differ between
+ * runs in the last bits; the totals and the waveform do not. */
 int pa_run_gates(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
                  double *gate_J);
 
