@@ -17,6 +17,10 @@ the tables once) over its own device time (HIP events attached to its
 dispatch, which time the kernel's execution as the profiler's kernel trace
 does) give roofline.achieved.
 
+"per_event_and_per_gate" times the headline workload's pass with per-event
+outputs and its per-gate pass (pa_run_gates), whole passes and the walk
+kernel alone.
+
 "configs" repeats the measurement for the other workloads (Tiny, Skewed,
 Glitch-heavy and the 200M-event one), each loaded, warmed up and timed the
 same way; the headline value stays the 10M-event workload's.
@@ -301,6 +305,7 @@ def main():
     cpu = None
     if not (args.no_cpu_baseline or args.quick):
         cpu = cpu_baseline(w, tot)
+    diag = None if args.quick else diag_passes(w, dev)
 
     # every other configuration: the same measurement, one line each in "configs"
     configs = {w.name: {k: head[k] for k in ("events", "fused_ms", "pass_ms", "events_per_s", "frac", "traffic")}}
@@ -346,11 +351,44 @@ def main():
                      "frac": head["frac"], "traffic": head["traffic"], "alg_bytes_per_launch": head["alg_bytes"],
                      "copy_GBs": copy_gbs, "frac_of_copy": head["achieved"] / copy_gbs},
         "configs": configs,
+        "per_event_and_per_gate": diag,
         "cpu_baseline": cpu,
         "clocks": head["clocks"],
         "device_bytes": info["device_bytes"],
     }
     print(json.dumps(line), flush=True)
+
+
+def diag_passes(w, dev, steps=10):
+    """The headline workload's pass with per-event outputs (glitch flags and
+    states in the caller's order) and its per-gate pass (pa_run_gates): the
+    median device time of each over cold passes, and of the walk kernel alone."""
+    import torch
+
+    import eda_gate_level_amd as pa
+
+    out = {}
+    flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    an = pa.PowerAnalysis(0, torch.cuda.current_stream(dev), time_kernels=1)
+    try:
+        an.load(w.design, w.trace)
+        for name, outs in (("per_event", an.alloc_outputs(per_event=True)), ("per_gate", an.alloc_outputs(per_gate=True))):
+            for _ in range(3):
+                an.run(outs)
+            kern, whole = [], []
+            for mode in (1, 2):
+                an.set_timing(mode)
+                for _ in range(steps):
+                    flush.fill_(1.0)
+                    an.run(outs)
+                    (kern if mode == 1 else whole).append(an.info()["kernel_ms"][0 if mode == 1 else 3])
+            an.set_timing(1)
+            out[name] = {"walk_kernel_ms": statistics.median(kern), "pass_ms": statistics.median(whole)}
+            del outs
+    finally:
+        an.close()
+    del flush
+    return out
 
 
 def measure(args, w, dev, gen_s, flush_gib=1, steps=None):
