@@ -27,8 +27,16 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-pthread", "-ffp-contract=off"
 
 
 def build(extra_flags=(), out=LIB) -> str:
-    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", out, SRC, "-lm"]
-    subprocess.run(cmd, check=True)
+    # compiled under a private name and renamed into place, so that a process
+    # loading the library never sees a half-written file
+    tmp = f"{out}.{os.getpid()}.tmp"
+    cmd = ["gcc", *CFLAGS, *extra_flags, "-o", tmp, SRC, "-lm"]
+    try:
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
     return out
 
 
