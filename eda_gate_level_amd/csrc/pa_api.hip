@@ -184,12 +184,22 @@ struct Events {
   // pa_run that asks for per-event outputs, dropped by the next load
   DBuf slot_of, evs;
   bool ev_map = false;
+  // per-gate rows from the walk kernel: the windows ranked gate-major, every
+  // gate's first rank and first piece (G + 1 entries each; a gate of many
+  // windows is summed in pieces by whole blocks first); made by the first
+  // pa_run_gates: every window's four sums by rank, every piece's sums and
+  // gate, every gate's leakage at its initial state over the window
+  DBuf goff, pfirst, wrec, wpart, pgate, gleak;
+  uint32_t n_pieces = 0;
+  bool gate_prep = false;
   int32_t n_ranges = 0, grid = 1;
   DBuf blk_wave, blk_cnt, blk_part, res;
   int64_t bytes() const {
     return (int64_t)(key.bytes + slew.bytes + orig.bytes + pin_init.bytes + rstart.bytes + rchunk.bytes +
                      chunk_blk.bytes + wdesc.bytes + wlen.bytes + l0.bytes + lplan.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
-                     res.bytes + blk_lut.bytes + ckey.bytes + cslew.bytes + slot_of.bytes + evs.bytes);
+                     res.bytes + blk_lut.bytes + ckey.bytes + cslew.bytes + slot_of.bytes + evs.bytes +
+                     goff.bytes + pfirst.bytes + wrec.bytes + wpart.bytes + pgate.bytes +
+                     gleak.bytes);
   }
 };
 
@@ -761,9 +771,39 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
     HIPCHK(v.cslew.ensure(sizeof(uint32_t) * Sa));
     HIPCHK(pa::launch_compact(Sa, v.key.as<uint64_t>(), v.slew.as<float>(), v.pad_key, v.pb, v.tb, v.gb, v.tbc, v.ck,
                               v.ckey.as<uint32_t>(), v.cslew.as<uint32_t>(), s));
+    // the windows ranked gate-major (a stable sort keeps a gate's windows in
+    // time order), every gate's first rank and its pieces for the row sums
+    HIPCHK(v.goff.ensure(sizeof(uint32_t) * (size_t)(d.G + 1)));
+    HIPCHK(v.pfirst.ensure(sizeof(uint32_t) * (size_t)(d.G + 1)));
+    HIPCHK(hipMemsetAsync(v.pfirst.p, 0, sizeof(uint32_t) * (size_t)(d.G + 1), s));
+    v.n_pieces = 0;
+    v.gate_prep = false;
+    if (W > 0) {
+      HIPCHK(ls.wkey0.ensure(sizeof(uint32_t) * 2 * (size_t)W));
+      // the values' two buffers: either ends up free after the sort, and holds the gates' pieces
+      HIPCHK(ls.widx.ensure(sizeof(uint32_t) * (size_t)std::max<int64_t>(W, d.G)));
+      HIPCHK(ls.worder.ensure(sizeof(uint32_t) * (size_t)std::max<int64_t>(W, d.G)));
+      HIPCHK(ls.wkey1.ensure(sizeof(uint32_t) * (size_t)W));
+      uint32_t *qk = ls.wkey0.as<uint32_t>(), *qs = qk + W, *qv = ls.widx.as<uint32_t>(),
+               *qw = ls.worder.as<uint32_t>();
+      HIPCHK(pa::launch_win_gates(W, ls.ws.as<uint32_t>(), ls.skey.as<uint64_t>(), v.gb, qk, qv, s));
+      const int gbits = (int)bits_for((uint64_t)std::max<int64_t>(d.G - 1, 0));
+      size_t tb = 0;
+      HIPCHK(pa::sort_pairs_u32(&qk, &qs, &qv, &qw, W, gbits, nullptr, &tb, s));
+      HIPCHK(ls.tmp.ensure(tb));
+      HIPCHK(pa::sort_pairs_u32(&qk, &qs, &qv, &qw, W, gbits, ls.tmp.p, &tb, s));
+      // the pieces per gate, their prefix after pfirst[0] = 0
+      uint32_t *npiece = qw;
+      HIPCHK(pa::launch_win_ranks(W, d.G, qk, qv, ls.wkey1.as<uint32_t>(), v.goff.as<uint32_t>(), npiece, s));
+      tb = 0;
+      HIPCHK(pa::scan_inclusive_u32(npiece, v.pfirst.as<uint32_t>() + 1, d.G, nullptr, &tb, s));
+      HIPCHK(ls.tmp.ensure(tb));
+      HIPCHK(pa::scan_inclusive_u32(npiece, v.pfirst.as<uint32_t>() + 1, d.G, ls.tmp.p, &tb, s));
+      HIPCHK(hipMemcpyAsync(&v.n_pieces, v.pfirst.as<uint32_t>() + d.G, sizeof(uint32_t), hipMemcpyDeviceToHost, s));
+    }
     const uint32_t hdr = ((1u << v.tbc) - 1u) << v.ck;
     HIPCHK(pa::launch_headers(W, ls.wlane.as<uint2>(), v.wdesc.as<uint2>(), ls.ws.as<uint32_t>(),
-                              ls.skey.as<uint64_t>(), d.gate_rec.as<uint4>(), d.perm.as<int32_t>(), v.gb,
+                              ls.skey.as<uint64_t>(), d.gate_rec.as<uint4>(), ls.wkey1.as<uint32_t>(), v.gb,
                               pa::out_code(v.pb), hdr, 1u << (v.tbc + v.ck), v.ckey.as<uint32_t>(),
                               v.cslew.as<uint32_t>(), v.orig.as<uint32_t>(), s));
   }
@@ -1016,7 +1056,22 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   const Design &d = c->d;
   Events &v = c->ev;
   hipStream_t s = c->stream;
-  if (gate_J)
+  // per-gate rows from the walk kernel: every window's sums stored at its
+  // rank, the rows made from them after the pass; else the general kernel,
+  // which adds to rows set up before it
+  const bool gate_walk = gate_J && !evt_glitch && !evt_state_before && v.walk_lut > 0 && c->tun.plain_bins == 0 &&
+                         v.n_windows > 0;
+  if (gate_walk && !v.gate_prep) {
+    HIPCHK(v.wrec.ensure(sizeof(double) * 4 * (size_t)v.n_windows));
+    HIPCHK(v.wpart.ensure(sizeof(double) * 4 * (size_t)std::max<uint32_t>(v.n_pieces, 1)));
+    HIPCHK(v.pgate.ensure(sizeof(uint32_t) * (size_t)std::max<uint32_t>(v.n_pieces, 1)));
+    HIPCHK(v.gleak.ensure(sizeof(double) * (size_t)d.G));
+    HIPCHK(pa::launch_gate_prep(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
+                                d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), (double)v.t_max * v.tick_s,
+                                v.pfirst.as<uint32_t>(), v.gleak.as<double>(), v.pgate.as<uint32_t>(), s));
+    v.gate_prep = true;
+  }
+  if (gate_J && !gate_walk)
     HIPCHK(pa::launch_gate_rows(d.G, d.gate_info.as<uint32_t>(), d.cell_meta.as<uint2>(), d.leak.as<double>(),
                                 d.pin_base.as<int64_t>(), v.pin_init.as<uint8_t>(), d.perm.as<int32_t>(),
                                 (double)v.t_max * v.tick_s, gate_J, s));
@@ -1071,16 +1126,14 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   a.blk_cnt = sc.blk_cnt;
   a.blk_part = sc.blk_part;
   a.evt_glitch = evt_glitch;
-  a.gate_J = gate_J;
+  a.gate_J = gate_walk ? nullptr : gate_J;
+  a.wrec = gate_walk ? v.wrec.as<double>() : nullptr;
   a.gate_perm = d.perm.as<int32_t>();
   a.evt_state = evt_state_before;
   // per-event outputs from the walk kernel (in stream order, then into the
   // caller's order) once the slot map is built; else the general kernel
   const bool ev_walk = (evt_glitch || evt_state_before) && !gate_J && v.walk_lut > 0 && c->tun.plain_bins == 0 &&
                        v.ev_map;
-  // per-gate rows from the walk kernel: every window's energies and leakage
-  // added to its gate's row when the window ends
-  a.gate_walk = (gate_J && !evt_glitch && !evt_state_before && v.walk_lut > 0 && c->tun.plain_bins == 0) ? 1 : 0;
   if (ev_walk) {
     a.evt_glitch = nullptr;
     a.evt_state = nullptr;
@@ -1115,6 +1168,10 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   hipError_t e1 = per_kernel ? pa::launch_pass(a, v.grid, s, c->tev[2], c->tev[3]) : pa::launch_pass(a, v.grid, s);
   if (e1 == hipSuccess && ev_walk)
     e1 = pa::launch_event_out(v.E, v.slot_of.as<uint32_t>(), v.evs.as<uint32_t>(), evt_glitch, evt_state_before, s);
+  if (e1 == hipSuccess && gate_walk)
+    e1 = pa::launch_gate_sums(d.G, v.n_pieces, v.goff.as<uint32_t>(), v.pfirst.as<uint32_t>(),
+                              v.pgate.as<uint32_t>(), v.gleak.as<double>(), d.perm.as<int32_t>(),
+                              v.wrec.as<double>(), v.wpart.as<double>(), gate_J, s);
   if (e1 == hipSuccess)
     e1 = per_kernel ? pa::launch_finalize(f, s, c->tev[4], c->tev[5]) : pa::launch_finalize(f, s);
   if (timed && e1 == hipSuccess) e1 = hipEventRecord(c->tev[1], s);

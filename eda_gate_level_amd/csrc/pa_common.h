@@ -110,7 +110,8 @@ struct PassArgs {
   // the walk kernel's per-event outputs, in stream order: 16 bits a slot (state before | glitch << 8),
   // two slots per 32-bit word (null: none)
   uint32_t *evs;
-  int32_t gate_walk;          // 1: the walk kernel adds each window's energies to its gate's row of gate_J
+  double *wrec;               // walk kernel: [windows][4] every window's sums (internal, switching, glitch,
+                              // leakage to t_max) at its rank in gate order (the header's caller-index slot)
   // per-block results, reduced by the finalize kernel
   double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
   unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32

@@ -42,6 +42,24 @@ int leak0_parts();
 hipError_t launch_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
                             const int64_t *pin_base, const uint8_t *pin_init, const int32_t *perm, double window,
                             double *gate_J, hipStream_t s);
+// the windows ranked gate-major (internal gate order): every window's gate (key) and index (value); after a
+// stable sort by key, every window's rank, every gate's first rank (goff[G + 1]) and its pieces for the
+// row sums (npiece[G]; their exclusive prefix is pfirst[G + 1])
+hipError_t launch_win_gates(uint32_t W, const uint32_t *ws, const uint64_t *skey, uint32_t gb, uint32_t *key,
+                            uint32_t *val, hipStream_t s);
+hipError_t launch_win_ranks(uint32_t W, int64_t G, const uint32_t *key, const uint32_t *val, uint32_t *rank,
+                            uint32_t *goff, uint32_t *npiece, hipStream_t s);
+// per-gate output rows (caller's gate order) from the walk kernel's window sums (rec[W][4], by rank): the
+// gate's windows (or, for a larger gate, its pieces, part[n_pieces][4], summed first) added in a fixed
+// order, plus the leakage at the initial state over the window (gleak[G])
+hipError_t launch_gate_sums(int64_t G, uint32_t n_pieces, const uint32_t *goff, const uint32_t *pfirst,
+                            const uint32_t *pgate, const double *gleak, const int32_t *perm, const double *rec,
+                            double *part, double *gate_J, hipStream_t s);
+// once per event load, for the row sums: every gate's leakage at its initial state over the window
+// (gleak[G], internal order) and every piece's gate (pgate[n_pieces])
+hipError_t launch_gate_prep(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
+                            const int64_t *pin_base, const uint8_t *pin_init, double window, const uint32_t *pfirst,
+                            double *gleak, uint32_t *pgate, hipStream_t s);
 hipError_t launch_pin_owner(int64_t G, const int64_t *pin_base, const int32_t *gate_k, int32_t *pin_gate,
                             uint8_t *pin_local, hipStream_t s);
 hipError_t launch_pin_check(int64_t P, int64_t E, const int64_t *pin_ptr, const uint8_t *pin_init, uint32_t *err,
@@ -89,13 +107,13 @@ hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *w
                              const uint32_t *wlen, uint32_t hp, uint32_t w_in, uint32_t w_out, uint2 *ph,
                              uint2 *wlane, uint32_t *wave_len, hipStream_t s);
 // the walk kernel's 8-byte-slot stream from the 16-byte one, then every window's header pair (and
-// the window's gate, caller's order, flagged by the high bit, in the 16-byte stream's caller-index slot
+// the window's rank in gate order, flagged by the high bit, in the 16-byte stream's caller-index slot
 // of the header: no event is there)
 hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,
                           uint32_t tb, uint32_t gb, uint32_t tbc, uint32_t ck, uint32_t *ckey, uint32_t *cslew,
                           hipStream_t s);
 hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
-                          const uint4 *gate_rec, const int32_t *perm, uint32_t gb, uint32_t outc, uint32_t hdr,
+                          const uint4 *gate_rec, const uint32_t *rank, uint32_t gb, uint32_t outc, uint32_t hdr,
                           uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig, hipStream_t s);
 hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
                           const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,

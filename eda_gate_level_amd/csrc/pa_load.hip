@@ -33,6 +33,10 @@ namespace pa {
 namespace {
 
 constexpr int kLT = 256;
+// per-gate rows from the walk kernel's window sums: kRowLanes lanes add a
+// gate's windows, or, for a gate of more than kRowSmall windows, its pieces
+// of kRowPiece windows, each summed by a block first
+constexpr uint32_t kRowLanes = 8, kRowSmall = 64, kRowPiece = 1024;
 
 inline int grid_for(int64_t n) {
   int64_t g = (n + kLT - 1) / kLT;
@@ -506,7 +510,7 @@ __global__ void k_compact(int64_t n, const uint64_t *key, const float *slew, uin
 // 20 | start state << 24 for an input window, 0 for an output window), slews
 // the gate's load (fp64 bits, low word first).  hdr has an all-ones tic field.
 __global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
-                          const uint4 *gate_rec, const int32_t *perm, uint32_t gb, uint32_t outc, uint32_t hdr,
+                          const uint4 *gate_rec, const uint32_t *rank, uint32_t gb, uint32_t outc, uint32_t hdr,
                           uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig) {
   for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < W; w += (int64_t)gridDim.x * blockDim.x) {
     const uint2 wl = wlane[w];
@@ -521,7 +525,7 @@ __global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, co
     ckey[y + 1] = out ? 0u : ((r.z & 0xFFFFFu) | ((r.z >> 24) << 20) | ((hw & 0xFFu) << 24));
     cslew[y] = r.x;
     cslew[y + 1] = r.y;
-    orig[y] = 0x80000000u | (uint32_t)perm[g];  // the window's gate (caller's order), flagged: no event
+    orig[y] = 0x80000000u | rank[w];  // the window's place in gate order, flagged: no event there
   }
 }
 
@@ -630,20 +634,29 @@ int leak0_parts() { return kL0B; }
 
 // Per-gate output start: row perm[g] = (0, 0, 0, leak[S0] * window), the
 // gate's leakage before any power change.
+// A gate's leakage energy at its initial state over the window (internal gate g).
+__device__ __forceinline__ double gate_leak_window(int64_t g, const uint32_t *gate_info, const uint2 *cell_meta,
+                                                   const double *leak, const int64_t *pin_base,
+                                                   const uint8_t *pin_init, double window) {
+  const uint2 m = cell_meta[gate_info[g] & 0xFFFFFFu];
+  const int k = (int)(m.x & 15u);
+  const int64_t p0 = pin_base[g];
+  uint32_t S = 0;
+  for (int j = 0; j < k; ++j) S |= uint32_t(pin_init[p0 + j]) << j;
+  return leak[(m.x >> 4) + S] * window;
+}
+
+// Every gate's row (caller's order): zero dynamic parts and the leakage at the
+// initial state over the window (the general kernel adds the rest).
 __global__ void k_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
                             const int64_t *pin_base, const uint8_t *pin_init, const int32_t *perm, double window,
                             double *gate_J) {
   for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
-    const uint2 m = cell_meta[gate_info[g] & 0xFFFFFFu];
-    const int k = (int)(m.x & 15u);
-    const int64_t p0 = pin_base[g];
-    uint32_t S = 0;
-    for (int j = 0; j < k; ++j) S |= uint32_t(pin_init[p0 + j]) << j;
     double *row = gate_J + 4 * (size_t)perm[g];
     row[0] = 0.0;
     row[1] = 0.0;
     row[2] = 0.0;
-    row[3] = leak[(m.x >> 4) + S] * window;
+    row[3] = gate_leak_window(g, gate_info, cell_meta, leak, pin_base, pin_init, window);
   }
 }
 
@@ -653,6 +666,177 @@ hipError_t launch_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *c
   if (G <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_gate_rows, dim3(grid_for(G)), dim3(kLT), 0, s, G, gate_info, cell_meta, leak, pin_base,
                      pin_init, perm, window, gate_J);
+  return hipGetLastError();
+}
+
+// The pieces of the larger gates' rows (see k_gate_sums): block p sums piece
+// p, kRowPiece ranks of gate pgate[p], in a fixed order.
+__global__ __launch_bounds__(kLT) void k_piece_sums(const uint32_t *goff, const uint32_t *pfirst,
+                                                     const uint32_t *pgate, const double4 *rec, double4 *part) {
+  const uint32_t p = blockIdx.x, g = pgate[p];
+  const uint32_t r0 = goff[g] + (p - pfirst[g]) * kRowPiece, r1 = min(goff[g + 1], r0 + kRowPiece);
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
+  for (uint32_t r = r0 + threadIdx.x; r < r1; r += kLT) {
+    const double4 x = rec[r];
+    s0 += x.x;
+    s1 += x.y;
+    s2 += x.z;
+    s3 += x.w;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    s0 += __shfl_down(s0, off);
+    s1 += __shfl_down(s1, off);
+    s2 += __shfl_down(s2, off);
+    s3 += __shfl_down(s3, off);
+  }
+  __shared__ double4 sw[kLT / 64];
+  if ((threadIdx.x & 63) == 0) sw[threadIdx.x >> 6] = make_double4(s0, s1, s2, s3);
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  double4 t = sw[0];
+  for (int w = 1; w < kLT / 64; ++w) {
+    t.x += sw[w].x;
+    t.y += sw[w].y;
+    t.z += sw[w].z;
+    t.w += sw[w].w;
+  }
+  part[p] = t;
+}
+
+// Per-gate rows from the walk kernel's window sums, stored by rank (the
+// windows ranked gate-major, internal gate order; goff[g] the first rank of
+// gate g).  kRowLanes lanes take one gate: each adds every kRowLanes-th of
+// the gate's window sums (at most kRowSmall windows), or of its pieces
+// (k_piece_sums, before), and a fixed tree adds the lanes' sums.  So a row
+// repeats bit for bit from run to run, and no gate waits on one lane walking
+// all of its windows.
+__global__ __launch_bounds__(kLT) void k_gate_sums(int64_t G, const uint32_t *goff, const uint32_t *pfirst,
+                                                    const double *gleak, const int32_t *perm, const double4 *rec,
+                                                    const double4 *part, double *gate_J) {
+  const int64_t g = (blockIdx.x * (int64_t)kLT + threadIdx.x) / kRowLanes;  // wave-aligned groups of lanes
+  const uint32_t j = threadIdx.x % kRowLanes;
+  double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0, lk = 0.0;
+  int32_t c = 0;
+  if (g < G) {
+    if (j == 0) {
+      lk = gleak[g];
+      c = perm[g];
+    }
+    const uint32_t r0 = goff[g], r1 = goff[g + 1];
+    const double4 *src = rec;
+    uint32_t a = r0, b = r1;
+    if (r1 - r0 > kRowSmall) {
+      src = part;
+      a = pfirst[g];
+      b = pfirst[g + 1];
+    }
+#pragma unroll 4
+    for (uint32_t r = a + j; r < b; r += kRowLanes) {
+      const double4 x = src[r];
+      s0 += x.x;
+      s1 += x.y;
+      s2 += x.z;
+      s3 += x.w;
+    }
+  }
+  for (int off = kRowLanes / 2; off > 0; off >>= 1) {
+    s0 += __shfl_xor(s0, off);
+    s1 += __shfl_xor(s1, off);
+    s2 += __shfl_xor(s2, off);
+    s3 += __shfl_xor(s3, off);
+  }
+  if (g >= G || j != 0) return;
+  s3 += lk;
+  double2 *row = reinterpret_cast<double2 *>(gate_J + 4 * (size_t)c);
+  row[0] = make_double2(s0, s1);
+  row[1] = make_double2(s2, s3);
+}
+
+hipError_t launch_gate_sums(int64_t G, uint32_t n_pieces, const uint32_t *goff, const uint32_t *pfirst,
+                            const uint32_t *pgate, const double *gleak, const int32_t *perm, const double *rec,
+                            double *part, double *gate_J, hipStream_t s) {
+  if (G <= 0) return hipSuccess;
+  const double4 *r4 = reinterpret_cast<const double4 *>(rec);
+  double4 *p4 = reinterpret_cast<double4 *>(part);
+  if (n_pieces > 0) hipLaunchKernelGGL(k_piece_sums, dim3(n_pieces), dim3(kLT), 0, s, goff, pfirst, pgate, r4, p4);
+  const int64_t nb = (G * kRowLanes + kLT - 1) / kLT;
+  hipLaunchKernelGGL(k_gate_sums, dim3((uint32_t)nb), dim3(kLT), 0, s, G, goff, pfirst, gleak, perm, r4, p4, gate_J);
+  return hipGetLastError();
+}
+
+// What the row sums read besides the window sums, once per event load: every
+// gate's leakage energy at its initial state over the window, and every
+// piece's gate.
+__global__ void k_gate_prep(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
+                            const int64_t *pin_base, const uint8_t *pin_init, double window, const uint32_t *pfirst,
+                            double *gleak, uint32_t *pgate) {
+  for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g < G; g += (int64_t)gridDim.x * blockDim.x) {
+    gleak[g] = gate_leak_window(g, gate_info, cell_meta, leak, pin_base, pin_init, window);
+    for (uint32_t q = pfirst[g]; q < pfirst[g + 1]; ++q) pgate[q] = (uint32_t)g;
+  }
+}
+
+hipError_t launch_gate_prep(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
+                            const int64_t *pin_base, const uint8_t *pin_init, double window, const uint32_t *pfirst,
+                            double *gleak, uint32_t *pgate, hipStream_t s) {
+  if (G <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gate_prep, dim3(grid_for(G)), dim3(kLT), 0, s, G, gate_info, cell_meta, leak, pin_base,
+                     pin_init, window, pfirst, gleak, pgate);
+  return hipGetLastError();
+}
+
+// Every window's internal gate (the sort key) and index (the value), for
+// ranking the windows gate-major.
+__global__ void k_win_gates(uint32_t W, const uint32_t *ws, const uint64_t *skey, uint32_t gb, uint32_t *key,
+                            uint32_t *val) {
+  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < W; w += (int64_t)gridDim.x * blockDim.x) {
+    key[w] = (uint32_t)(skey[ws[w]] >> 32 >> 10) & ((1u << gb) - 1u);
+    val[w] = (uint32_t)w;
+  }
+}
+
+// From the windows sorted by gate (stable: window order within a gate):
+// every window's rank.
+__global__ void k_win_ranks(uint32_t W, const uint32_t *val, uint32_t *rank) {
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < W; r += (int64_t)gridDim.x * blockDim.x)
+    rank[val[r]] = (uint32_t)r;
+}
+
+// Every gate's first rank, the first sorted key not below the gate (a gate
+// without windows gets the next gate's first rank; goff[G] = W), and its
+// pieces for the row sums: none up to kRowSmall windows, else one per
+// kRowPiece windows.
+__global__ void k_gate_first(uint32_t W, int64_t G, const uint32_t *key, uint32_t *goff, uint32_t *npiece) {
+  for (int64_t g = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; g <= G; g += (int64_t)gridDim.x * blockDim.x) {
+    auto first = [&](int64_t x) {
+      uint32_t lo = 0, hi = W;
+      while (lo < hi) {
+        const uint32_t mid = lo + (hi - lo) / 2;
+        if ((int64_t)key[mid] < x) lo = mid + 1;
+        else hi = mid;
+      }
+      return lo;
+    };
+    const uint32_t a = first(g);
+    goff[g] = a;
+    if (g < G) {
+      const uint32_t n = first(g + 1) - a;
+      npiece[g] = n > kRowSmall ? (n + kRowPiece - 1) / kRowPiece : 0u;
+    }
+  }
+}
+
+hipError_t launch_win_gates(uint32_t W, const uint32_t *ws, const uint64_t *skey, uint32_t gb, uint32_t *key,
+                            uint32_t *val, hipStream_t s) {
+  if (W == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_win_gates, dim3(grid_for(W)), dim3(kLT), 0, s, W, ws, skey, gb, key, val);
+  return hipGetLastError();
+}
+
+hipError_t launch_win_ranks(uint32_t W, int64_t G, const uint32_t *key, const uint32_t *val, uint32_t *rank,
+                            uint32_t *goff, uint32_t *npiece, hipStream_t s) {
+  if (W > 0) hipLaunchKernelGGL(k_win_ranks, dim3(grid_for(W)), dim3(kLT), 0, s, W, val, rank);
+  hipLaunchKernelGGL(k_gate_first, dim3(grid_for(G + 1)), dim3(kLT), 0, s, W, G, key, goff, npiece);
   return hipGetLastError();
 }
 
@@ -768,10 +952,10 @@ hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *w
   return hipGetLastError();
 }
 hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
-                          const uint4 *gate_rec, const int32_t *perm, uint32_t gb, uint32_t outc, uint32_t hdr,
+                          const uint4 *gate_rec, const uint32_t *rank, uint32_t gb, uint32_t outc, uint32_t hdr,
                           uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig, hipStream_t s) {
   if (W == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_headers, dim3(grid_for(W)), dim3(kLT), 0, s, W, wlane, wdesc, ws, skey, gate_rec, perm, gb, outc,
+  hipLaunchKernelGGL(k_headers, dim3(grid_for(W)), dim3(kLT), 0, s, W, wlane, wdesc, ws, skey, gate_rec, rank, gb, outc,
                      hdr, out_bit, ckey, cslew, orig);
   return hipGetLastError();
 }

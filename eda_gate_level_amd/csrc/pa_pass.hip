@@ -142,31 +142,6 @@ __device__ __forceinline__ uint32_t row_incl_scan_u32(uint32_t v) {
   return v;
 }
 
-// Inclusive sums over runs of lanes (a run starts at every lane whose head
-// flag is set, and at lane 0), in a fixed order: the same DPP steps as
-// wave_incl_scan, each adding only while no run start lies between, so the
-// last lane of a run holds the run's exact sum.
-__device__ __forceinline__ void wave_seg_scan4(double (&v)[4], bool head) {
-  uint32_t f = head ? 1u : 0u;
-#define PA_SEG_STEP(CTRL, ROWS)                                   \
-  {                                                               \
-    double u[4];                                                  \
-    for (int q = 0; q < 4; ++q) u[q] = dpp_f64<CTRL, ROWS>(v[q]); \
-    const uint32_t fu = dpp_u32<CTRL, ROWS>(f);                   \
-    if (!f) {                                                     \
-      for (int q = 0; q < 4; ++q) v[q] += u[q];                   \
-      f |= fu;                                                    \
-    }                                                             \
-  }
-  PA_SEG_STEP(0x111, 0xf)
-  PA_SEG_STEP(0x112, 0xf)
-  PA_SEG_STEP(0x114, 0xf)
-  PA_SEG_STEP(0x118, 0xf)
-  PA_SEG_STEP(0x142, 0xa)
-  PA_SEG_STEP(0x143, 0xc)
-#undef PA_SEG_STEP
-}
-
 // lane l's double, l wave-uniform
 __device__ __forceinline__ double lane_f64(double v, int l) {
   return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), l),
@@ -833,27 +808,16 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     uint32_t S = 0, St = 0, seen = 0, pcyc = ~0u, ptic = 0;
     float pslew = 1.f;
     bool out_phase = false;  // the kind of the current phase's windows (wave-uniform)
-    // per-gate rows (MODE 2): the window's gate (caller's order), the lane's
+    // per-gate rows (MODE 2): the window's rank in gate order, the lane's
     // energy sums at the window start, the window's leakage to t_max
     uint32_t gid = ~0u;
     double g_int0 = 0.0, g_sw0 = 0.0, g_gl0 = 0.0, g_lk = 0.0;
-    // The wave's lanes hold windows of one kind; windows of one gate sit in
-    // neighbouring lanes (a busy gate's many windows have like lengths), so
-    // runs of lanes with the same gate are summed first and the run's last
-    // lane adds the sums.  An input window has no switching energy, an output
-    // window no internal energy or leakage change, and most have no glitch:
-    // only the nonzero parts go out, so a run costs one or two device atomics.
+    // the window's four sums, stored at its rank (every window once a pass)
     auto flush_gate = [&]() {
-      double v[4] = {e_int - g_int0, e_sw - g_sw0, e_gl - g_gl0, g_lk * tick};
-      const uint32_t gprev = (uint32_t)__builtin_amdgcn_update_dpp((int)~0u, (int)gid, 0x138, 0xf, 0xf, false);
-      const uint32_t gnext = (uint32_t)__builtin_amdgcn_update_dpp((int)~0u, (int)gid, 0x130, 0xf, 0xf, false);
-      wave_seg_scan4(v, lane == 0 || gid != gprev || gid == ~0u);
-      if (gid != ~0u && (lane == 63 || gnext != gid)) {
-        double *row = a.gate_J + 4 * (size_t)gid;
-        if (v[0] != 0.0) atomicAdd(row + 0, v[0]);
-        if (v[1] != 0.0) atomicAdd(row + 1, v[1]);
-        if (v[2] != 0.0) atomicAdd(row + 2, v[2]);
-        if (v[3] != 0.0) atomicAdd(row + 3, v[3]);
+      if (gid != ~0u) {
+        double2 *r = reinterpret_cast<double2 *>(a.wrec) + 2 * (size_t)gid;
+        r[0] = make_double2(e_int - g_int0, e_sw - g_sw0);
+        r[1] = make_double2(e_gl - g_gl0, g_lk * tick);
       }
     };
     lds_u32 *prec = L.prec + (wid * a.kmax * 64 + lane) * 2;
@@ -1111,7 +1075,7 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
           if (__ballot(own) != 0ull) {
             out_phase = __ballot(own && (k.x & out_bit)) != 0ull;
             if constexpr (MODE == 2) {
-              // the previous window's row; the new window's gate from the caller-index
+              // the previous window's sums; the new window's rank from the caller-index
               // slot of its header (flagged by the high bit)
               flush_gate();
               gid = own ? (a.orig[(uint32_t)base + (uint32_t)(pg + i) * 128u + 2u * lane] & 0x7FFFFFFFu) : ~0u;
@@ -1499,7 +1463,7 @@ static void launch_timed(K kernel, dim3 g, dim3 t, size_t dyn, hipStream_t s, hi
 
 hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   const bool cells = pass_cells_fit_lds(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax);
-  const bool diag = a.evt_glitch || a.evt_state || (a.gate_J && !a.gate_walk);
+  const bool diag = a.evt_glitch || a.evt_state || a.gate_J;
   if (a.walk_lut > 0 && !diag) {
     // the walk kernel: every block's LUT range in its LDS (at least the entries a lane without a window reads)
     const size_t dyn = walk_fixed_bytes(a.Cc, a.n_cells, a.n_slew, a.n_cap, a.n_thr, a.n_leak, a.kmax) +
@@ -1510,8 +1474,8 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s, hipEve
     if (a.n_slew == 7 && a.n_cap == 7) {
       if (a.plain_bins == 1) launch_timed(k_walk<7, 7, 1, 0, 0>, g, t, dyn, s, e0, e1, a);
       else if (a.plain_bins == 2) launch_timed(k_walk<7, 7, 2, 0, 0>, g, t, dyn, s, e0, e1, a);
-      else if (a.gate_J && kreg) launch_timed(k_walk<7, 7, 0, kWalkRegPins, 2>, g, t, dyn, s, e0, e1, a);
-      else if (a.gate_J) launch_timed(k_walk<7, 7, 0, 0, 2>, g, t, dyn, s, e0, e1, a);
+      else if (a.wrec && kreg) launch_timed(k_walk<7, 7, 0, kWalkRegPins, 2>, g, t, dyn, s, e0, e1, a);
+      else if (a.wrec) launch_timed(k_walk<7, 7, 0, 0, 2>, g, t, dyn, s, e0, e1, a);
       else if (a.evs && kreg) launch_timed(k_walk<7, 7, 0, kWalkRegPins, 1>, g, t, dyn, s, e0, e1, a);
       else if (a.evs) launch_timed(k_walk<7, 7, 0, 0, 1>, g, t, dyn, s, e0, e1, a);
       else if (kreg) launch_timed(k_walk<7, 7, 0, kWalkRegPins, 0>, g, t, dyn, s, e0, e1, a);
@@ -1519,8 +1483,8 @@ hipError_t launch_pass(const PassArgs &a, int grid_blocks, hipStream_t s, hipEve
     } else if (a.n_slew == 8 && a.n_cap == 8) {
       if (a.plain_bins == 1) launch_timed(k_walk<8, 8, 1, 0, 0>, g, t, dyn, s, e0, e1, a);
       else if (a.plain_bins == 2) launch_timed(k_walk<8, 8, 2, 0, 0>, g, t, dyn, s, e0, e1, a);
-      else if (a.gate_J && kreg) launch_timed(k_walk<8, 8, 0, kWalkRegPins, 2>, g, t, dyn, s, e0, e1, a);
-      else if (a.gate_J) launch_timed(k_walk<8, 8, 0, 0, 2>, g, t, dyn, s, e0, e1, a);
+      else if (a.wrec && kreg) launch_timed(k_walk<8, 8, 0, kWalkRegPins, 2>, g, t, dyn, s, e0, e1, a);
+      else if (a.wrec) launch_timed(k_walk<8, 8, 0, 0, 2>, g, t, dyn, s, e0, e1, a);
       else if (a.evs && kreg) launch_timed(k_walk<8, 8, 0, kWalkRegPins, 1>, g, t, dyn, s, e0, e1, a);
       else if (a.evs) launch_timed(k_walk<8, 8, 0, 0, 1>, g, t, dyn, s, e0, e1, a);
       else if (kreg) launch_timed(k_walk<8, 8, 0, kWalkRegPins, 0>, g, t, dyn, s, e0, e1, a);

@@ -40,13 +40,19 @@ def _slews(rng, n):
     return np.exp(rng.uniform(np.log(50.0), np.log(300_000.0), n)).astype(np.float32)
 
 
-def _case(seed, G=200, C=40, T=1000, rate=0.3, ks=(1, 2, 3, 4), collide=0, t_max=None, n_axis=7, cpk=2):
+def _case(seed, G=200, C=40, T=1000, rate=0.3, ks=(1, 2, 3, 4), collide=0, t_max=None, n_axis=7, cpk=2, hot=()):
+    """A random design and Poisson trace; hot = ((gate, rate), ...) gives those
+    gates' pins their own rate (events per pin per cycle)."""
     rng = np.random.default_rng(seed)
     lib = synth.make_library(rng, ks, cells_per_k=cpk, n_axis=n_axis)
     k = rng.choice(np.array(ks), size=G)
     des = synth.assign_gates(rng, lib, k, 1.0, 50.0)
-    P = int(des.pin_base()[-1])
-    tr = synth.poisson_trace(rng, np.full(P, rate), C, T)
+    pb = des.pin_base()
+    P = int(pb[-1])
+    rates = np.full(P, rate)
+    for g, r in hot:
+        rates[pb[g]:pb[g + 1]] = r
+    tr = synth.poisson_trace(rng, rates, C, T)
     pin = np.repeat(np.arange(P), np.diff(tr.pin_ptr))
     tt = tr.evt_t
     if collide:
@@ -256,6 +262,9 @@ def _walk_gates(d, t, **kw):
         r = an.run(outs)
         g = dict(r["totals"])
         g["gate_J"] = r["gate_J"][:d.n_gates].cpu().numpy()
+        # a second run into rows filled with NaN: every row rewritten, the same bits
+        outs["gate_J"].fill_(float("nan"))
+        g["gate_J_again"] = an.run(outs)["gate_J"][:d.n_gates].cpu().numpy()
         g["wave_J"] = r["wave_J"].cpu().numpy()
         g["cyc_events"] = r["cyc_events"].cpu().numpy().astype(np.uint64)
         g["cyc_glitches"] = r["cyc_glitches"].cpu().numpy().astype(np.uint64)
@@ -266,14 +275,17 @@ def _walk_gates(d, t, **kw):
 
 
 @pytest.mark.parametrize("case", [dict(seed=1), dict(seed=2, ks=(1, 5), cpk=1, G=60, rate=0.2),
-                                  dict(seed=4, collide=1000, rate=0.6, G=80), dict(seed=14, ks=(2, 3), G=150, n_axis=8)],
-                         ids=["k1-4", "k1-5", "cycle-edges", "8x8"])
+                                  dict(seed=4, collide=1000, rate=0.6, G=80), dict(seed=14, ks=(2, 3), G=150, n_axis=8),
+                                  dict(seed=21, G=40, C=600, rate=0.2, hot=((7, 40.0), (8, 3.0), (30, 12.0)))],
+                         ids=["k1-4", "k1-5", "cycle-edges", "8x8", "hot-gates"])
 @pytest.mark.parametrize("chunk", [0, 3])
 def test_walk_per_gate_rows(case, chunk):
     """Per-gate rows from the walk kernel (each window's energies and the
-    leakage of its power changes to t_max, added to its gate's row when the
-    window ends): every entry within 1e-9 of the oracle's per-gate energies,
-    the rows adding up to the totals, and every total, bin and count."""
+    leakage of its power changes to t_max, stored at the window's rank in
+    gate order and added up per gate after the walk): every entry within
+    1e-9 of the oracle's per-gate energies, the rows adding up to the
+    totals, every total, bin and count, and a second run giving the same
+    rows bit for bit."""
     import oracle
     from test_gpu_gates import _assert_gates
 
@@ -285,3 +297,4 @@ def test_walk_per_gate_rows(case, chunk):
     o = oracle.run(d, t, per_event=False, per_gate=True)
     pu.assert_parity(g, o, per_event=False, label=label)
     _assert_gates(g, o, label)
+    assert np.array_equal(g["gate_J"], g["gate_J_again"]), label
