@@ -186,10 +186,12 @@ struct Events {
   bool ev_map = false;
   // per-gate rows from the walk kernel: the windows ranked gate-major, every
   // gate's first rank and first piece (G + 1 entries each; a gate of many
-  // windows is summed in pieces by whole blocks first); made by the first
-  // pa_run_gates: every window's four sums by rank, every piece's sums and
-  // gate, every gate's leakage at its initial state over the window
-  DBuf goff, pfirst, wrec, wpart, pgate, gleak;
+  // windows is summed in pieces by whole blocks first), every window's
+  // header pair by rank; made by the first pa_run_gates: room for four sums
+  // at every pair of the lane streams (the walk kernel stores a window's at
+  // its header pair), every piece's sums and gate, every gate's leakage at
+  // its initial state over the window
+  DBuf goff, pfirst, wpos, wrec, wpart, pgate, gleak;
   uint32_t n_pieces = 0;
   bool gate_prep = false;
   int32_t n_ranges = 0, grid = 1;
@@ -198,7 +200,7 @@ struct Events {
     return (int64_t)(key.bytes + slew.bytes + orig.bytes + pin_init.bytes + rstart.bytes + rchunk.bytes +
                      chunk_blk.bytes + wdesc.bytes + wlen.bytes + l0.bytes + lplan.bytes + blk_wave.bytes + blk_cnt.bytes + blk_part.bytes +
                      res.bytes + blk_lut.bytes + ckey.bytes + cslew.bytes + slot_of.bytes + evs.bytes +
-                     goff.bytes + pfirst.bytes + wrec.bytes + wpart.bytes + pgate.bytes +
+                     goff.bytes + pfirst.bytes + wpos.bytes + wrec.bytes + wpart.bytes + pgate.bytes +
                      gleak.bytes);
   }
 };
@@ -775,6 +777,7 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
     // time order), every gate's first rank and its pieces for the row sums
     HIPCHK(v.goff.ensure(sizeof(uint32_t) * (size_t)(d.G + 1)));
     HIPCHK(v.pfirst.ensure(sizeof(uint32_t) * (size_t)(d.G + 1)));
+    HIPCHK(v.wpos.ensure(sizeof(uint32_t) * (size_t)std::max<int64_t>(W, 1)));
     HIPCHK(hipMemsetAsync(v.pfirst.p, 0, sizeof(uint32_t) * (size_t)(d.G + 1), s));
     v.n_pieces = 0;
     v.gate_prep = false;
@@ -805,7 +808,7 @@ static int build_ranges(pa_ctx *c, Events &v, const int64_t *pin_ptr, const uint
     HIPCHK(pa::launch_headers(W, ls.wlane.as<uint2>(), v.wdesc.as<uint2>(), ls.ws.as<uint32_t>(),
                               ls.skey.as<uint64_t>(), d.gate_rec.as<uint4>(), ls.wkey1.as<uint32_t>(), v.gb,
                               pa::out_code(v.pb), hdr, 1u << (v.tbc + v.ck), v.ckey.as<uint32_t>(),
-                              v.cslew.as<uint32_t>(), v.orig.as<uint32_t>(), s));
+                              v.cslew.as<uint32_t>(), v.wpos.as<uint32_t>(), s));
   }
   // the cells whose LUTs every block copies into its spare LDS
   v.lut_lds = pa::pass_lut_lds_doubles(v.Cc, d.n_cells, d.n_slew, d.n_cap, d.n_thr, d.n_leak, d.kmax);
@@ -1062,7 +1065,7 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   const bool gate_walk = gate_J && !evt_glitch && !evt_state_before && v.walk_lut > 0 && c->tun.plain_bins == 0 &&
                          v.n_windows > 0;
   if (gate_walk && !v.gate_prep) {
-    HIPCHK(v.wrec.ensure(sizeof(double) * 4 * (size_t)v.n_windows));
+    HIPCHK(v.wrec.ensure(sizeof(double) * 4 * (size_t)((v.slots + 3) / 2)));
     HIPCHK(v.wpart.ensure(sizeof(double) * 4 * (size_t)std::max<uint32_t>(v.n_pieces, 1)));
     HIPCHK(v.pgate.ensure(sizeof(uint32_t) * (size_t)std::max<uint32_t>(v.n_pieces, 1)));
     HIPCHK(v.gleak.ensure(sizeof(double) * (size_t)d.G));
@@ -1171,7 +1174,7 @@ static int run_pass(pa_ctx *c, const PassScratch &sc, pa_totals *out, double *wa
   if (e1 == hipSuccess && gate_walk)
     e1 = pa::launch_gate_sums(d.G, v.n_pieces, v.goff.as<uint32_t>(), v.pfirst.as<uint32_t>(),
                               v.pgate.as<uint32_t>(), v.gleak.as<double>(), d.perm.as<int32_t>(),
-                              v.wrec.as<double>(), v.wpart.as<double>(), gate_J, s);
+                              v.wpos.as<uint32_t>(), v.wrec.as<double>(), v.wpart.as<double>(), gate_J, s);
   if (e1 == hipSuccess)
     e1 = per_kernel ? pa::launch_finalize(f, s, c->tev[4], c->tev[5]) : pa::launch_finalize(f, s);
   if (timed && e1 == hipSuccess) e1 = hipEventRecord(c->tev[1], s);

@@ -63,8 +63,7 @@ struct PassArgs {
   // events
   const uint64_t *key;
   const float *slew;
-  const uint32_t *orig;    // caller's CSR index of each laid-out event (~0 in empty slots; at a window's
-                           // header, with the walk kernel: its gate in the caller's order | 1 << 31)
+  const uint32_t *orig;    // caller's CSR index of each laid-out event (~0 in empty slots and headers)
   uint64_t pad_key;        // key of an empty slot (no event has it)
   const uint2 *wdesc;      // [n_ranges][waves] every wave's (first slot, events per lane)
   const uint32_t *rchunk;  // [n_ranges] chunk of each range
@@ -110,8 +109,8 @@ struct PassArgs {
   // the walk kernel's per-event outputs, in stream order: 16 bits a slot (state before | glitch << 8),
   // two slots per 32-bit word (null: none)
   uint32_t *evs;
-  double *wrec;               // walk kernel: [windows][4] every window's sums (internal, switching, glitch,
-                              // leakage to t_max) at its rank in gate order (the header's caller-index slot)
+  double *wrec;               // walk kernel: [pairs][4] every window's sums (internal, switching, glitch,
+                              // leakage to t_max) at its header's pair of the lane streams
   // per-block results, reduced by the finalize kernel
   double *blk_wave;              // [grid][Cc] energy per cycle of the block's chunk
   unsigned long long *blk_cnt;   // [grid][Cc] events | glitches << 32

@@ -49,12 +49,12 @@ hipError_t launch_win_gates(uint32_t W, const uint32_t *ws, const uint64_t *skey
                             uint32_t *val, hipStream_t s);
 hipError_t launch_win_ranks(uint32_t W, int64_t G, const uint32_t *key, const uint32_t *val, uint32_t *rank,
                             uint32_t *goff, uint32_t *npiece, hipStream_t s);
-// per-gate output rows (caller's gate order) from the walk kernel's window sums (rec[W][4], by rank): the
-// gate's windows (or, for a larger gate, its pieces, part[n_pieces][4], summed first) added in a fixed
-// order, plus the leakage at the initial state over the window (gleak[G])
+// per-gate output rows (caller's gate order) from the walk kernel's window sums (rec[pairs][4], the window
+// of rank r at pair wpos[r]): the gate's windows (or, for a larger gate, its pieces, part[n_pieces][4],
+// summed first) added in a fixed order, plus the leakage at the initial state over the window (gleak[G])
 hipError_t launch_gate_sums(int64_t G, uint32_t n_pieces, const uint32_t *goff, const uint32_t *pfirst,
-                            const uint32_t *pgate, const double *gleak, const int32_t *perm, const double *rec,
-                            double *part, double *gate_J, hipStream_t s);
+                            const uint32_t *pgate, const double *gleak, const int32_t *perm, const uint32_t *wpos,
+                            const double *rec, double *part, double *gate_J, hipStream_t s);
 // once per event load, for the row sums: every gate's leakage at its initial state over the window
 // (gleak[G], internal order) and every piece's gate (pgate[n_pieces])
 hipError_t launch_gate_prep(int64_t G, const uint32_t *gate_info, const uint2 *cell_meta, const double *leak,
@@ -106,15 +106,14 @@ size_t phase_plan_entries(uint32_t W, int32_t nr);
 hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *worder, const uint64_t *wkey,
                              const uint32_t *wlen, uint32_t hp, uint32_t w_in, uint32_t w_out, uint2 *ph,
                              uint2 *wlane, uint32_t *wave_len, hipStream_t s);
-// the walk kernel's 8-byte-slot stream from the 16-byte one, then every window's header pair (and
-// the window's rank in gate order, flagged by the high bit, in the 16-byte stream's caller-index slot
-// of the header: no event is there)
+// the walk kernel's 8-byte-slot stream from the 16-byte one, then every window's header pair (and,
+// by the window's rank in gate order, the header's pair index: wpos[rank[w]])
 hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,
                           uint32_t tb, uint32_t gb, uint32_t tbc, uint32_t ck, uint32_t *ckey, uint32_t *cslew,
                           hipStream_t s);
 hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
                           const uint4 *gate_rec, const uint32_t *rank, uint32_t gb, uint32_t outc, uint32_t hdr,
-                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig, hipStream_t s);
+                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *wpos, hipStream_t s);
 hipError_t launch_scatter(int64_t E, const uint64_t *skey, const float *sslew, const uint32_t *sorig,
                           const uint32_t *winc, const uint32_t *ws, const uint2 *wlane, const uint2 *wdesc,
                           uint64_t *key, float *slew, uint32_t *orig, hipStream_t s);

@@ -511,7 +511,7 @@ __global__ void k_compact(int64_t n, const uint64_t *key, const float *slew, uin
 // the gate's load (fp64 bits, low word first).  hdr has an all-ones tic field.
 __global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
                           const uint4 *gate_rec, const uint32_t *rank, uint32_t gb, uint32_t outc, uint32_t hdr,
-                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig) {
+                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *wpos) {
   for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < W; w += (int64_t)gridDim.x * blockDim.x) {
     const uint2 wl = wlane[w];
     const uint32_t j = wl.y - 2u;  // the header pair: an even slot of the lane's stream
@@ -525,7 +525,7 @@ __global__ void k_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, co
     ckey[y + 1] = out ? 0u : ((r.z & 0xFFFFFu) | ((r.z >> 24) << 20) | ((hw & 0xFFu) << 24));
     cslew[y] = r.x;
     cslew[y + 1] = r.y;
-    orig[y] = 0x80000000u | rank[w];  // the window's place in gate order, flagged: no event there
+    wpos[rank[w]] = y >> 1;  // the header's pair: where the walk kernel stores the window's sums
   }
 }
 
@@ -672,12 +672,13 @@ hipError_t launch_gate_rows(int64_t G, const uint32_t *gate_info, const uint2 *c
 // The pieces of the larger gates' rows (see k_gate_sums): block p sums piece
 // p, kRowPiece ranks of gate pgate[p], in a fixed order.
 __global__ __launch_bounds__(kLT) void k_piece_sums(const uint32_t *goff, const uint32_t *pfirst,
-                                                     const uint32_t *pgate, const double4 *rec, double4 *part) {
+                                                     const uint32_t *pgate, const uint32_t *wpos, const double4 *rec,
+                                                     double4 *part) {
   const uint32_t p = blockIdx.x, g = pgate[p];
   const uint32_t r0 = goff[g] + (p - pfirst[g]) * kRowPiece, r1 = min(goff[g + 1], r0 + kRowPiece);
   double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0;
   for (uint32_t r = r0 + threadIdx.x; r < r1; r += kLT) {
-    const double4 x = rec[r];
+    const double4 x = rec[wpos[r]];
     s0 += x.x;
     s1 += x.y;
     s2 += x.z;
@@ -703,16 +704,16 @@ __global__ __launch_bounds__(kLT) void k_piece_sums(const uint32_t *goff, const 
   part[p] = t;
 }
 
-// Per-gate rows from the walk kernel's window sums, stored by rank (the
-// windows ranked gate-major, internal gate order; goff[g] the first rank of
-// gate g).  kRowLanes lanes take one gate: each adds every kRowLanes-th of
+// Per-gate rows from the walk kernel's window sums (stored at each window's
+// header pair, wpos[r] for the window of rank r: the windows ranked
+// gate-major, internal gate order; goff[g] the first rank of gate g).  kRowLanes lanes take one gate: each adds every kRowLanes-th of
 // the gate's window sums (at most kRowSmall windows), or of its pieces
 // (k_piece_sums, before), and a fixed tree adds the lanes' sums.  So a row
 // repeats bit for bit from run to run, and no gate waits on one lane walking
 // all of its windows.
 __global__ __launch_bounds__(kLT) void k_gate_sums(int64_t G, const uint32_t *goff, const uint32_t *pfirst,
-                                                    const double *gleak, const int32_t *perm, const double4 *rec,
-                                                    const double4 *part, double *gate_J) {
+                                                    const double *gleak, const int32_t *perm, const uint32_t *wpos,
+                                                    const double4 *rec, const double4 *part, double *gate_J) {
   const int64_t g = (blockIdx.x * (int64_t)kLT + threadIdx.x) / kRowLanes;  // wave-aligned groups of lanes
   const uint32_t j = threadIdx.x % kRowLanes;
   double s0 = 0.0, s1 = 0.0, s2 = 0.0, s3 = 0.0, lk = 0.0;
@@ -723,20 +724,24 @@ __global__ __launch_bounds__(kLT) void k_gate_sums(int64_t G, const uint32_t *go
       c = perm[g];
     }
     const uint32_t r0 = goff[g], r1 = goff[g + 1];
-    const double4 *src = rec;
-    uint32_t a = r0, b = r1;
     if (r1 - r0 > kRowSmall) {
-      src = part;
-      a = pfirst[g];
-      b = pfirst[g + 1];
-    }
 #pragma unroll 4
-    for (uint32_t r = a + j; r < b; r += kRowLanes) {
-      const double4 x = src[r];
-      s0 += x.x;
-      s1 += x.y;
-      s2 += x.z;
-      s3 += x.w;
+      for (uint32_t q = pfirst[g] + j; q < pfirst[g + 1]; q += kRowLanes) {
+        const double4 x = part[q];
+        s0 += x.x;
+        s1 += x.y;
+        s2 += x.z;
+        s3 += x.w;
+      }
+    } else {
+#pragma unroll 4
+      for (uint32_t r = r0 + j; r < r1; r += kRowLanes) {
+        const double4 x = rec[wpos[r]];
+        s0 += x.x;
+        s1 += x.y;
+        s2 += x.z;
+        s3 += x.w;
+      }
     }
   }
   for (int off = kRowLanes / 2; off > 0; off >>= 1) {
@@ -753,14 +758,16 @@ __global__ __launch_bounds__(kLT) void k_gate_sums(int64_t G, const uint32_t *go
 }
 
 hipError_t launch_gate_sums(int64_t G, uint32_t n_pieces, const uint32_t *goff, const uint32_t *pfirst,
-                            const uint32_t *pgate, const double *gleak, const int32_t *perm, const double *rec,
-                            double *part, double *gate_J, hipStream_t s) {
+                            const uint32_t *pgate, const double *gleak, const int32_t *perm, const uint32_t *wpos,
+                            const double *rec, double *part, double *gate_J, hipStream_t s) {
   if (G <= 0) return hipSuccess;
   const double4 *r4 = reinterpret_cast<const double4 *>(rec);
   double4 *p4 = reinterpret_cast<double4 *>(part);
-  if (n_pieces > 0) hipLaunchKernelGGL(k_piece_sums, dim3(n_pieces), dim3(kLT), 0, s, goff, pfirst, pgate, r4, p4);
+  if (n_pieces > 0)
+    hipLaunchKernelGGL(k_piece_sums, dim3(n_pieces), dim3(kLT), 0, s, goff, pfirst, pgate, wpos, r4, p4);
   const int64_t nb = (G * kRowLanes + kLT - 1) / kLT;
-  hipLaunchKernelGGL(k_gate_sums, dim3((uint32_t)nb), dim3(kLT), 0, s, G, goff, pfirst, gleak, perm, r4, p4, gate_J);
+  hipLaunchKernelGGL(k_gate_sums, dim3((uint32_t)nb), dim3(kLT), 0, s, G, goff, pfirst, gleak, perm, wpos, r4, p4,
+                     gate_J);
   return hipGetLastError();
 }
 
@@ -953,10 +960,10 @@ hipError_t launch_phase_plan(int32_t nr, const uint32_t *bwin, const uint32_t *w
 }
 hipError_t launch_headers(uint32_t W, const uint2 *wlane, const uint2 *wdesc, const uint32_t *ws, const uint64_t *skey,
                           const uint4 *gate_rec, const uint32_t *rank, uint32_t gb, uint32_t outc, uint32_t hdr,
-                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *orig, hipStream_t s) {
+                          uint32_t out_bit, uint32_t *ckey, uint32_t *cslew, uint32_t *wpos, hipStream_t s) {
   if (W == 0) return hipSuccess;
   hipLaunchKernelGGL(k_headers, dim3(grid_for(W)), dim3(kLT), 0, s, W, wlane, wdesc, ws, skey, gate_rec, rank, gb, outc,
-                     hdr, out_bit, ckey, cslew, orig);
+                     hdr, out_bit, ckey, cslew, wpos);
   return hipGetLastError();
 }
 hipError_t launch_compact(int64_t n, const uint64_t *key, const float *slew, uint64_t pad_key, uint32_t pb,

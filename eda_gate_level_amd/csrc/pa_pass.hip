@@ -808,11 +808,12 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
     uint32_t S = 0, St = 0, seen = 0, pcyc = ~0u, ptic = 0;
     float pslew = 1.f;
     bool out_phase = false;  // the kind of the current phase's windows (wave-uniform)
-    // per-gate rows (MODE 2): the window's rank in gate order, the lane's
-    // energy sums at the window start, the window's leakage to t_max
+    // per-gate rows (MODE 2): the window's header pair, the lane's energy
+    // sums at the window start, the window's leakage to t_max
     uint32_t gid = ~0u;
     double g_int0 = 0.0, g_sw0 = 0.0, g_gl0 = 0.0, g_lk = 0.0;
-    // the window's four sums, stored at its rank (every window once a pass)
+    // the window's four sums, stored at its header pair (every window once a
+    // pass): the wave's lanes store 2 KB in one piece
     auto flush_gate = [&]() {
       if (gid != ~0u) {
         double2 *r = reinterpret_cast<double2 *>(a.wrec) + 2 * (size_t)gid;
@@ -1075,10 +1076,9 @@ __global__ __launch_bounds__(kNT) PA_FUSED_ATTR void k_walk(PassArgs a) {
           if (__ballot(own) != 0ull) {
             out_phase = __ballot(own && (k.x & out_bit)) != 0ull;
             if constexpr (MODE == 2) {
-              // the previous window's sums; the new window's rank from the caller-index
-              // slot of its header (flagged by the high bit)
+              // the previous window's sums; the new window's header pair
               flush_gate();
-              gid = own ? (a.orig[(uint32_t)base + (uint32_t)(pg + i) * 128u + 2u * lane] & 0x7FFFFFFFu) : ~0u;
+              gid = own ? ((uint32_t)base >> 1) + (uint32_t)(pg + i) * 64u + lane : ~0u;
               g_int0 = e_int;
               g_sw0 = e_sw;
               g_gl0 = e_gl;
@@ -1520,7 +1520,7 @@ __global__ void k_slot_of(int64_t n, const uint32_t *orig, uint32_t *slot_of) {
   const int64_t x = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (x >= n) return;
   const uint32_t o = orig[x];
-  if (o < 0x80000000u) slot_of[o] = (uint32_t)x;  // ~0: an empty slot; high bit: a header's gate
+  if (o < 0x80000000u) slot_of[o] = (uint32_t)x;  // ~0: an empty slot or a header
 }
 
 // The walk's per-event outputs (state before | glitch << 8, 16 bits a slot,

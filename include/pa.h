@@ -200,10 +200,11 @@ int pa_run_noalloc(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_ev
  *                  glitch and leakage energy over [0, t_max), J; overwritten.
  * The gate rows add up to the totals (up to fp64 summation order).  With
  * the walk kernel (pa_info.walk_kernel) every window's energies and the
- * leakage of its power changes are stored at the window's rank in gate
- * order (the load ranks the windows), and a second kernel adds each gate's
- * windows in rank order: the rows repeat bit for bit from run to run.  The
- * first such call allocates the per-window sums (32 bytes a window, kept
+ * leakage of its power changes are stored at the window's header in the
+ * lane streams, and kernels after the walk add each gate's windows in a
+ * fixed order (the load ranks the windows gate-major): the rows repeat bit
+ * for bit from run to run.  The first such call allocates room for the
+ * window sums (16 bytes a slot of the lane streams, pa_info.n_slots; kept
  * until the next load).  Otherwise the diagnostic variant of the general
  * kernel adds them event by event with device atomics, so the rows may
  * differ between runs in the last bits; the totals and the waveform never
