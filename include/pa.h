@@ -207,8 +207,9 @@ int pa_run_noalloc(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_ev
  * window sums (16 bytes a slot of the lane streams, pa_info.n_slots; kept
  * until the next load).  Otherwise the diagnostic variant of the general
  * kernel adds them event by event with device atomics, so the rows may
- * differ between runs in the last bits; the totals and the waveform never
- * do. */
+ * differ between runs in the last bits.  The totals and the waveform
+ * behave as in pa_run either way (dynamic energies and counts bit for bit,
+ * the waveform bins and the leakage total to rounding). */
 int pa_run_gates(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
                  double *gate_J);
 
