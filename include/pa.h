@@ -169,7 +169,11 @@ typedef struct {
  * writes them in its stream's order and a small kernel moves them into the
  * caller's order through every event's slot; the first such call builds that
  * map (4 bytes per event and 2 per stream slot of device memory, kept until
- * the next pa_load_events). */
+ * the next pa_load_events).  From run to run of one loaded layout, the
+ * dynamic energies, every count and the per-event outputs repeat bit for bit;
+ * the waveform bins and the leakage total, built with atomic adds in LDS
+ * whose order between waves is free, repeat to rounding (about 1e-16
+ * relative). */
 int pa_run(pa_ctx *ctx, pa_totals *out, double *wave_J, uint64_t *cyc_events, uint64_t *cyc_glitches,
            uint8_t *evt_glitch, uint8_t *evt_state_before);
 
