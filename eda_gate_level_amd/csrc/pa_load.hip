@@ -36,7 +36,7 @@ constexpr int kLT = 256;
 // per-gate rows from the walk kernel's window sums: kRowLanes lanes add a
 // gate's windows, or, for a gate of more than kRowSmall windows, its pieces
 // of kRowPiece windows, each summed by a block first
-constexpr uint32_t kRowLanes = 8, kRowSmall = 64, kRowPiece = 1024;
+constexpr uint32_t kRowLanes = 2, kRowSmall = 64, kRowPiece = 1024;
 
 inline int grid_for(int64_t n) {
   int64_t g = (n + kLT - 1) / kLT;
