@@ -276,7 +276,8 @@ def _walk_gates(d, t, **kw):
 
 @pytest.mark.parametrize("case", [dict(seed=1), dict(seed=2, ks=(1, 5), cpk=1, G=60, rate=0.2),
                                   dict(seed=4, collide=1000, rate=0.6, G=80), dict(seed=14, ks=(2, 3), G=150, n_axis=8),
-                                  dict(seed=21, G=40, C=600, rate=0.2, hot=((7, 40.0), (8, 3.0), (30, 12.0)))],
+                                  dict(seed=21, G=40, C=600, rate=0.2,
+                                       hot=((0, 0.0), (7, 40.0), (8, 3.0), (20, 0.0), (30, 12.0), (39, 0.0)))],
                          ids=["k1-4", "k1-5", "cycle-edges", "8x8", "hot-gates"])
 @pytest.mark.parametrize("chunk", [0, 3])
 def test_walk_per_gate_rows(case, chunk):
